@@ -1,0 +1,193 @@
+"""Python binding of libmuir: channel-wise gated delta-rule linear attention with
+matched-filter readout (Muir), hand-written HIP kernels for AMD CDNA4 (gfx950).
+
+The binding only marshals arguments: it checks tensor dtypes, shapes and devices,
+allocates outputs and the workspace with PyTorch, passes raw device pointers and the
+current HIP stream to the C ABI declared in ``include/muir.h``, and raises
+``MuirError`` with the library's message on a non-zero status. Every step of the
+computation runs in the library's kernels; there is no fallback. Importing works
+without a GPU (argument validation can be exercised on the CPU), but the library
+itself must be built (``python -m gated_delta_rule_06_amd._build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "decode_step",
+    "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuir.so")
+
+MUIR_F32, MUIR_BF16 = 0, 1
+STATUS = {0: "MUIR_OK", 1: "MUIR_ERR_NULL", 2: "MUIR_ERR_SHAPE", 3: "MUIR_ERR_UNSUPPORTED",
+          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIAS", 6: "MUIR_ERR_HIP"}
+
+
+class MuirError(RuntimeError):
+    """A libmuir call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libmuir.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_delta_rule_06_amd._build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.muir_chunk_fwd_workspace_size.argtypes = [i] * 6 + [i]
+        L.muir_chunk_fwd_workspace_size.restype = sz
+        L.muir_chunk_fwd.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd.restype = i
+        L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
+        L.muir_decode_step.restype = i
+        L.muir_status_string.argtypes = [i]
+        L.muir_status_string.restype = ctypes.c_char_p
+        L.muir_last_error.argtypes = []
+        L.muir_last_error.restype = ctypes.c_char_p
+        L.muir_version.argtypes = []
+        L.muir_version.restype = i
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().muir_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().muir_last_error().decode()
+
+
+def version() -> int:
+    return int(lib().muir_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise MuirError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    if device.type != "cuda":
+        return None
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MUIR_F32
+    if t.dtype == torch.bfloat16:
+        return MUIR_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _require(t, name, dtype=None, shape=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (the library has no host path)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, chunk: int,
+                             dtype_code: int) -> int:
+    return int(lib().muir_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, dtype_code))
+
+
+def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out=None,
+              return_state: bool = True, workspace=None):
+    """Chunkwise forward over whole sequences (``muir_chunk_fwd``).
+
+    q, k [B,T,H,dk] and v [B,T,H,dv] in float32 or bfloat16 (same dtype); a, g
+    [B,T,H,dk], e, w [B,T,H,dv] and r [H,dk] float32; s0 [B,H,dk,dv] float32 or None.
+    Returns (o, s_out): o [B,T,H,dv] in the q/k/v dtype and the final state (or None
+    with ``return_state=False``). ``s_out`` may be passed (it may be ``s0`` itself for
+    an in-place update); ``workspace`` may be a pre-allocated uint8 device tensor.
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, q.dtype, (B, T, H, dk if name != "v" else dv), dev)
+    for name, t, d in (("a", a, dk), ("g", g, dk), ("e", e, dv), ("w", w, dv)):
+        _require(t, name, torch.float32, (B, T, H, d), dev)
+    _require(r, "r", torch.float32, (H, dk), dev)
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", q.dtype, (B, T, H, dv), dev)
+    if s_out is None and return_state:
+        s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif s_out is not None:
+        _require(s_out, "s_out", torch.float32, (B, H, dk, dv), dev)
+    need = chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", torch.uint8, None, dev)
+    status = lib().muir_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(r), _ptr(s0),
+        _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, code, _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(status)
+    return o, s_out
+
+
+def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):
+    """One recurrent step per (batch, head), updating ``state`` in place.
+
+    q, k [B,H,dk], v [B,H,dv] (float32 or bfloat16); a, g [B,H,dk], e, w [B,H,dv],
+    r [H,dk] float32; state [B,H,dk,dv] float32. Returns o [B,H,dv] (q/k/v dtype).
+    """
+    import torch
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    code = _dtype_code(q)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("v", v, dv)):
+        _require(t, name, q.dtype, (B, H, d), dev)
+    for name, t, d in (("a", a, dk), ("g", g, dk), ("e", e, dv), ("w", w, dv)):
+        _require(t, name, torch.float32, (B, H, d), dev)
+    _require(r, "r", torch.float32, (H, dk), dev)
+    _require(state, "state", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", q.dtype, (B, H, dv), dev)
+    status = lib().muir_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(r),
+        _ptr(state), _ptr(o), B, H, dk, dv, code, _stream(dev))
+    _check(status)
+    return o

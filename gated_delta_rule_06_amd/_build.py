@@ -1,0 +1,58 @@
+"""Build libmuir.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in-tree.
+
+Usage: ``python -m gated_delta_rule_06_amd._build``. The library lands in this package
+directory; the public header is ``include/muir.h`` at the repository root.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmuir.so")
+SOURCES = ["api.cpp", "decode.hip", "chunk_fwd.hip"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU instructions are kept out of every kernel.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libmuir")
+    return exe
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source into ``libmuir.so`` (always recompiles); returns its path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *HIP_FLAGS,
+           *extra_flags, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    t0 = time.time()
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless.
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,89 @@
+// gfx950 matrix-core (MFMA) helpers for the chunk kernels.
+//
+// Every contraction in the chunk forward is D[16x16] += A[16xK] * B[Kx16] with the
+// operands held as "row x contraction" matrices on both sides: A rows are output rows,
+// B "rows" are output columns. Both operands therefore use the same fragment layout.
+//
+//   bf16 operands: v_mfma_f32_16x16x32_bf16. Per instruction K = 32; lane l holds
+//                  row (l % 16) and contraction indices 8*(l / 16) + [0, 8).
+//   fp32 operands: v_mfma_f32_16x16x4_f32.   Per instruction K = 4; lane l holds
+//                  row (l % 16) and contraction index (l / 16).
+//   Accumulator (both): 16x16 fp32, lane l holds column (l % 16), rows 4*(l/16)+[0,4).
+//
+// Accumulation is always fp32.
+#pragma once
+
+#include "common.hpp"
+
+namespace muir {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+
+template <typename OpT> struct Mma;
+
+template <> struct Mma<bf16_t> {
+    static constexpr int KSTEP = 32;  // contraction length per instruction
+    static constexpr int VALS = 8;    // contraction values per lane
+    using frag = bf16x8_t;
+
+    // Contraction index (within one KSTEP block) of element j held by lane l.
+    static __device__ __forceinline__ int kidx(int lane, int j) { return (lane >> 4) * 8 + j; }
+
+    static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Round 8 floats to bf16 (nearest even) into one fragment.
+    static __device__ __forceinline__ frag pack(const float (&x)[8]) {
+        u16x8_t u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = f32_to_bf16(x[j]);
+        return __builtin_bit_cast(frag, u);
+    }
+    // Fragment from 8 consecutive stored operands (16-byte aligned).
+    static __device__ __forceinline__ frag load(const bf16_t *p) {
+        return __builtin_bit_cast(frag, *reinterpret_cast<const u16x8_t *>(p));
+    }
+    static __device__ __forceinline__ frag zero() {
+        u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
+        return __builtin_bit_cast(frag, u);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const float (&x)[8]) {
+        u16x8_t u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = f32_to_bf16(x[j]);
+        *reinterpret_cast<u16x8_t *>(p) = u;
+    }
+    static __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+    static __device__ __forceinline__ bf16_t from_f32(float x) { return bf16_t{f32_to_bf16(x)}; }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KSTEP = 4;
+    static constexpr int VALS = 1;
+    using frag = float;
+
+    static __device__ __forceinline__ int kidx(int lane, int) { return lane >> 4; }
+
+    static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag pack(const float (&x)[1]) { return x[0]; }
+    static __device__ __forceinline__ frag load(const float *p) { return *p; }
+    static __device__ __forceinline__ frag zero() { return 0.f; }
+    static __device__ __forceinline__ void store(float *p, const float (&x)[1]) { *p = x[0]; }
+    static __device__ __forceinline__ float to_f32(float x) { return x; }
+    static __device__ __forceinline__ float from_f32(float x) { return x; }
+};
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Order this wave's LDS writes before its following LDS reads from other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace muir

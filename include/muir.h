@@ -1,0 +1,148 @@
+/*
+ * muir.h -- C ABI of libmuir: channel-wise gated delta-rule linear attention with
+ * matched-filter readout (Muir), hand-written HIP kernels for AMD CDNA4 (gfx950).
+ *
+ * The method (sources are the pages on "Muir: Linear Attention with Sensitivity-
+ * Allocated Gating and Matched-Filter Readout", arXiv 2611.08376):
+ *   per head, a dk x dv fp32 state S (rows = key channels). For each token t:
+ *     S <- Diag(a_t) S                  channel-wise (per-row) decay, a_t in [0, 1]
+ *     p <- S^T k_t                      prediction of the decayed state for k_t
+ *     S <- S + k_t (w_t * v_t - e_t * p)^T   erase under the value-channel erase
+ *                                       gate e_t, then write under the write gate w_t
+ *     o_t <- S^T (r * g_t * q_t)        matched-filter readout: static row scale r
+ *                                       times the dynamic query gate g_t
+ *   Update order: the Muir abstract ("Full text" on the Astral Feed page): gated
+ *   delta-rule models decay the state and erase its prediction for an incoming key
+ *   before writing a new value, with channel-wise decay and decoupled erase and write
+ *   gates. Readout: openai-hub news page, section on matched-filter readout (a static
+ *   per-row scale from each row's expected energy plus per-token query modulation),
+ *   and the liuch.name summary, first bullet (inverse fractional power law plus
+ *   per-token query modulation).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a caller-owned DEVICE buffer, contiguous, row-major,
+ *     16-byte aligned. The library never allocates or frees device memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     Buffers must stay live until the stream reaches the call.
+ *   - Argument errors are detected on the host, before any launch, and return a
+ *     status; nothing is launched then. A failed launch returns MUIR_ERR_HIP.
+ *     muir_last_error() gives a human-readable detail for the calling thread.
+ *   - No exceptions cross the ABI. Values are not checked for NaN/Inf; non-finite
+ *     inputs propagate. Gates are expected in [0, 1] (a), (0, 1) (e, w, g).
+ *   - Results are deterministic: reductions use no atomics.
+ *   - The library keeps no state across calls and is safe to call from several
+ *     threads (the error detail is thread-local).
+ */
+#ifndef MUIR_H
+#define MUIR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t passed as a plain pointer. */
+typedef void *muir_stream_t;
+
+typedef enum {
+    MUIR_OK = 0,
+    MUIR_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    MUIR_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
+    MUIR_ERR_UNSUPPORTED = 3, /* a valid but unimplemented combination           */
+    MUIR_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned      */
+    MUIR_ERR_ALIAS = 5,       /* an output overlaps an input it must not alias   */
+    MUIR_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+} muir_status_t;
+
+typedef enum {
+    MUIR_F32 = 0,             /* q, k, v and o are float32                       */
+    MUIR_BF16 = 1             /* q, k, v and o are bfloat16                      */
+} muir_dtype_t;
+
+/*
+ * Workspace bytes needed by muir_chunk_fwd for these sizes (0 for invalid sizes).
+ * The workspace holds, per (batch, head, chunk), the chunk's lower-triangular
+ * intra-chunk matrices (the decayed key-key Gram M and query-key Gram P) in fp32,
+ * 16x16 blocks, so its size is 2 * B * H * ceil(T/chunk) * (chunk/16)(chunk/16+1)/2
+ * * 1 KiB. It must be 256-byte aligned. Its contents are scratch: nothing is
+ * expected in it on entry or kept from it on return.
+ */
+size_t muir_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int chunk,
+                                     muir_dtype_t qkv);
+
+/*
+ * Chunkwise-parallel forward over a whole sequence (training / prefill).
+ *
+ * The pages' stable large-chunk scheme (liuch.name summary, third bullet; openai-hub
+ * page, section on rewriting the long-sequence parallel algorithm for TPU): decays
+ * that cross a block boundary are split into two running products pivoted at that
+ * boundary, both in (0, 1], so nothing is divided by a cumulative decay; the
+ * intra-chunk unit lower-triangular system is solved by recursive block-Neumann
+ * halving whose off-diagonal products run on the matrix cores; chunks are chained by
+ * carrying the state. With a value-channel erase gate every value column has its own
+ * triangular system, so the recursion is applied to each right-hand side.
+ *
+ *   q, k    [B, T, H, dk]  dtype `qkv`      keys should be L2-normalised by the caller
+ *   v       [B, T, H, dv]  dtype `qkv`
+ *   a, g    [B, T, H, dk]  float32          per-row decay in [0, 1], query gate
+ *   e, w    [B, T, H, dv]  float32          erase and write gates (value channels)
+ *   r       [H, dk]        float32          static readout row scale
+ *   s0      [B, H, dk, dv] float32 or NULL  initial state (NULL = zeros)
+ *   o       [B, T, H, dv]  dtype `qkv`      output, o_t read after token t's update
+ *   s_out   [B, H, dk, dv] float32 or NULL  final state; may equal s0 (in place)
+ *   chunk   64, 128 or 256; T need not be a multiple (the last chunk is partial)
+ *   dk, dv  dk == dv, 64 or 128
+ *   T       >= 0 (T == 0 copies s0, or zeros, into s_out and writes no o)
+ *   workspace / workspace_bytes: at least muir_chunk_fwd_workspace_size(...) bytes
+ *
+ * Errors: MUIR_ERR_NULL for a missing q/k/v/a/g/e/w/r/o (when T > 0) or workspace;
+ * MUIR_ERR_SHAPE for B < 1, T < 0, H < 1 or size overflow; MUIR_ERR_UNSUPPORTED for
+ * dk != dv, d not in {64, 128} or chunk not in {64, 128, 256}; MUIR_ERR_WORKSPACE for
+ * a short or misaligned workspace; MUIR_ERR_ALIAS when o overlaps an input or s_out
+ * overlaps an input other than s0 (or s0 partially).
+ */
+muir_status_t muir_chunk_fwd(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *r,
+    const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
+ * One recurrent step per (batch, head), updating the state in place (decode).
+ * Constant-memory inference against the fixed state (Muir abstract, "Full text";
+ * openai-hub page, opening section: the history lives in a fixed 2-D state, so
+ * memory does not grow with context).
+ *
+ *   q, k    [B, H, dk] dtype `qkv`;  v [B, H, dv] dtype `qkv`
+ *   a, g    [B, H, dk] float32;      e, w [B, H, dv] float32;  r [H, dk] float32
+ *   state   [B, H, dk, dv] float32, read and written in place
+ *   o       [B, H, dv] dtype `qkv`
+ *   dk, dv  dk == dv, 64 or 128
+ *
+ * Errors: MUIR_ERR_NULL for any missing pointer; MUIR_ERR_SHAPE for B < 1, H < 1;
+ * MUIR_ERR_UNSUPPORTED for other d; MUIR_ERR_ALIAS when o or state overlaps an input
+ * or each other.
+ */
+muir_status_t muir_decode_step(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *r,
+    float *state, void *o,
+    int B, int H, int dk, int dv, muir_dtype_t qkv, muir_stream_t stream);
+
+/* Static, never-NULL name of a status code ("MUIR_OK", ...). */
+const char *muir_status_string(muir_status_t s);
+
+/* Detail of the calling thread's last failed call ("" if none). Valid until the next
+ * call on this thread. */
+const char *muir_last_error(void);
+
+/* Version of the library as major*10000 + minor*100 + patch. */
+int muir_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUIR_H */

@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every function the public header
+declares, and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_06_amd as muir
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "muir.h")
+
+# Fake, 256-byte aligned, non-overlapping "device" addresses. They are only ever
+# passed in calls that fail validation, so nothing dereferences them.
+BASE = 1 << 40
+STRIDE = 1 << 32
+
+
+def fake(i):
+    return ctypes.c_void_p(BASE + i * STRIDE)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muir_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("muir_chunk_fwd", "muir_chunk_fwd_workspace_size", "muir_decode_step",
+                     "muir_status_string", "muir_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = muir.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings():
+    for code, name in muir.STATUS.items():
+        assert muir.status_string(code) == name
+    assert muir.status_string(99) == "MUIR_STATUS_UNKNOWN"
+    assert muir.version() >= 10000
+
+
+def test_workspace_size():
+    ws = muir.chunk_fwd_workspace_size
+    a = ws(2, 1000, 3, 64, 64, 64, muir.MUIR_BF16)
+    b = ws(2, 1024, 3, 64, 64, 64, muir.MUIR_BF16)
+    assert a == b > 0                      # ceil(T / chunk) slots
+    assert ws(2, 1025, 3, 64, 64, 64, muir.MUIR_BF16) > b
+    assert ws(1, 64, 1, 64, 64, 64, muir.MUIR_F32) > ws(1, 64, 1, 64, 64, 64, muir.MUIR_BF16)
+    assert ws(1, 0, 1, 64, 64, 64, muir.MUIR_BF16) == 0
+    for bad in [(0, 64, 1, 64, 64, 64), (1, 64, 1, 64, 128, 64), (1, 64, 1, 32, 32, 64),
+                (1, 64, 1, 64, 64, 32), (1, -1, 1, 64, 64, 64)]:
+        assert ws(*bad, muir.MUIR_BF16) == 0
+    assert ws(1, 64, 1, 64, 64, 64, 7) == 0
+
+
+def _chunk_call(**over):
+    lib = muir.lib()
+    args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),
+                r=fake(7), s0=fake(8), o=fake(9), s_out=fake(10), B=2, T=100, H=3, dk=64,
+                dv=64, chunk=64, qkv=muir.MUIR_BF16, ws=fake(11),
+                wsb=muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16),
+                stream=None)
+    args.update(over)
+    st = lib.muir_chunk_fwd(args["q"], args["k"], args["v"], args["a"], args["g"], args["e"],
+                            args["w"], args["r"], args["s0"], args["o"], args["s_out"],
+                            args["B"], args["T"], args["H"], args["dk"], args["dv"],
+                            args["chunk"], args["qkv"], args["ws"], args["wsb"], args["stream"])
+    return st, muir.last_error()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(dk=0), 2),
+    (dict(dk=64, dv=128), 3), (dict(dk=32, dv=32), 3), (dict(chunk=32), 3),
+    (dict(qkv=5), 3),
+    (dict(q=None), 1), (dict(a=None), 1), (dict(o=None), 1), (dict(r=None), 1),
+    (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=ctypes.c_void_p(BASE + 11 * STRIDE + 16)), 4),
+    (dict(q=ctypes.c_void_p(BASE + 8)), 2),
+    (dict(o=fake(2)), 5), (dict(s_out=fake(3)), 5),
+    (dict(o=ctypes.c_void_p(BASE + 2 * STRIDE + 4096)), 5),
+    (dict(s_out=ctypes.c_void_p(BASE + 8 * STRIDE + 256)), 5),
+    (dict(o=fake(10)), 5), (dict(ws=fake(9)), 5),
+])
+def test_chunk_fwd_rejects_bad_arguments(over, status):
+    st, msg = _chunk_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def _decode_call(**over):
+    lib = muir.lib()
+    args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),
+                r=fake(7), state=fake(8), o=fake(9), B=4, H=2, dk=128, dv=128,
+                qkv=muir.MUIR_BF16, stream=None)
+    args.update(over)
+    st = lib.muir_decode_step(args["q"], args["k"], args["v"], args["a"], args["g"], args["e"],
+                              args["w"], args["r"], args["state"], args["o"], args["B"],
+                              args["H"], args["dk"], args["dv"], args["qkv"], args["stream"])
+    return st, muir.last_error()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(dk=96, dv=96), 3), (dict(dk=128, dv=64), 3),
+    (dict(qkv=2), 3), (dict(state=None), 1), (dict(r=None), 1), (dict(v=None), 1),
+    (dict(o=fake(1)), 5), (dict(state=fake(3)), 5), (dict(o=fake(8)), 5),
+    (dict(e=ctypes.c_void_p(BASE + 5 * STRIDE + 4)), 2),
+])
+def test_decode_step_rejects_bad_arguments(over, status):
+    st, msg = _decode_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_python_binding_validates_before_calling():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(TypeError):
+        muir.chunk_fwd(x.double(), x, x, x, x, x, x, torch.zeros(1, 64))
+    # host tensors never reach the library
+    with pytest.raises(ValueError):
+        muir.chunk_fwd(x, x, x, x, x, x, x, torch.zeros(1, 64))
+    with pytest.raises(ValueError):
+        muir.decode_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0],
+                         torch.zeros(1, 64), torch.zeros(1, 1, 64, 64))

@@ -1,0 +1,178 @@
+"""GPU parity of muir_chunk_fwd against the fp64 CPU oracle (token recurrence).
+
+Bar: per-head max relative error (max |x - ref| / max |ref| over the head's slice,
+separately for o and the final state) <= 1e-4 for fp32 q/k/v and <= 2e-2 for bf16,
+with every value finite. Calls go through the C ABI via the Python binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_06_amd as muir
+import oracle
+import workloads
+from parity import NAMES, o_err, s_err, to_device, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def gpu_fwd(inp, device, chunk, s0=None, qkv=None):
+    qkv = qkv or inp["qkv"]
+    t = to_device(inp, device, qkv)
+    s0t = None if s0 is None else torch.from_numpy(np.asarray(s0, np.float32)).to(device)
+    o, s = muir.chunk_fwd(*[t[n] for n in NAMES], s0=s0t, chunk=chunk)
+    torch.cuda.synchronize()
+    return to_numpy(o), to_numpy(s)
+
+
+def ref_fwd(inp, s0=None):
+    return oracle.recurrent(*[inp[n] for n in NAMES], s0=s0)
+
+
+def assert_parity(o, s, o_ref, s_ref, tol, what):
+    eo, es = o_err(o, o_ref), s_err(s, s_ref)
+    worst = max(eo.max(), es.max())
+    print(f"{what}: max head err o={eo.max():.3e} state={es.max():.3e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all(), f"{what}: non-finite output"
+    assert worst <= tol, (f"{what}: o err per head {np.round(eo, 6).tolist()}, "
+                          f"state err per head {np.round(es, 6).tolist()}")
+
+
+def state_like(rng, B, H, d, scale=0.3):
+    return (rng.standard_normal((B, H, d, d)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("T", [1, 15, 64, 65, 300])
+def test_small_shapes(device, qkv, d, chunk, T):
+    """Every (d, chunk, dtype) at lengths that exercise one token, a partial leaf, an
+    exact chunk, one token past it and several chunks with a ragged tail."""
+    inp = workloads.chunk_inputs(0, B=2, T=T, H=2, d=d, qkv=qkv, seed=1000 + T)
+    s0 = state_like(np.random.default_rng(T), 2, 2, d) if T % 2 else None
+    o, s = gpu_fwd(inp, device, chunk, s0)
+    o_ref, s_ref = ref_fwd(inp, s0)
+    assert_parity(o, s, o_ref, s_ref, TOL[qkv], f"T={T} d={d} C={chunk} {qkv}")
+
+
+def test_config0_tiny_fp32(device):
+    inp = workloads.chunk_inputs(0)
+    o, s = gpu_fwd(inp, device, 64)
+    assert_parity(o, s, *ref_fwd(inp), 1e-4, "config0")
+
+
+def test_config1_166m_shape(device):
+    inp = workloads.chunk_inputs(1)
+    o, s = gpu_fwd(inp, device, 64)
+    assert_parity(o, s, *ref_fwd(inp), 2e-2, "config1 C=64")
+
+
+@pytest.fixture(scope="module")
+def config2():
+    inp = workloads.chunk_inputs(2)
+    return inp, ref_fwd(inp)
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_config2_134b_shape(device, config2, chunk):
+    inp, (o_ref, s_ref) = config2
+    o, s = gpu_fwd(inp, device, chunk)
+    assert_parity(o, s, o_ref, s_ref, 2e-2, f"config2 C={chunk}")
+
+
+def test_config2_slow_rows_carry_more_energy(config2):
+    """Reported statistic: slow rows (long half-life) hold far more state energy than
+    fast rows (the pages' 100x slow-channel glare). Not a pass/fail bound on the ratio."""
+    inp, (_, s_ref) = config2
+    a_mean = inp["a"].mean(axis=(0, 1))                          # [H, d]
+    energy = (s_ref ** 2).sum(axis=-1).mean(axis=0)               # [H, d]
+    ratios = []
+    for h in range(a_mean.shape[0]):
+        order = np.argsort(a_mean[h])
+        q = len(order) // 4
+        ratios.append(np.median(energy[h, order[-q:]]) / np.median(energy[h, order[:q]]))
+    print(f"slow/fast row energy ratio (median over heads): {np.median(ratios):.1f}", flush=True)
+    assert np.median(ratios) > 1.0
+
+
+def test_config3_long_context_stress(device):
+    inp = workloads.chunk_inputs(3)
+    o, s = gpu_fwd(inp, device, 256)
+    nan_heads = [h for h in range(16) if not (np.isfinite(o[:, :, h]).all()
+                                               and np.isfinite(s[:, h]).all())]
+    assert nan_heads == [], f"non-finite heads {nan_heads}"
+    assert_parity(o, s, *ref_fwd(inp), 2e-2, "config3 C=256")
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_chunk_size_invariance(device, qkv):
+    inp = workloads.chunk_inputs(2, B=1, T=777, H=3, qkv=qkv, seed=7)
+    outs = {C: gpu_fwd(inp, device, C) for C in (64, 128, 256)}
+    for C in (128, 256):
+        assert_parity(*outs[C], *outs[64], TOL[qkv], f"C={C} vs C=64 {qkv}")
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_split_sequence_resumes_from_state(device, qkv):
+    inp = workloads.chunk_inputs(1, B=2, T=700, H=2, qkv=qkv, seed=8)
+    o, s = gpu_fwd(inp, device, 64)
+    cut = 333
+    first = {n: (inp[n][:, :cut] if n != "r" else inp[n]) for n in NAMES}
+    second = {n: (inp[n][:, cut:] if n != "r" else inp[n]) for n in NAMES}
+    o1, s1 = gpu_fwd(first, device, 128, qkv=qkv)
+    o2, s2 = gpu_fwd(second, device, 64, s0=s1, qkv=qkv)
+    assert_parity(np.concatenate([o1, o2], axis=1), s2, o, s, TOL[qkv], f"split {qkv}")
+
+
+def test_deterministic(device):
+    inp = workloads.chunk_inputs(2, B=2, T=600, H=4, seed=9)
+    o1, s1 = gpu_fwd(inp, device, 256)
+    o2, s2 = gpu_fwd(inp, device, 256)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def test_in_place_state_and_empty_sequence(device):
+    inp = workloads.chunk_inputs(1, B=1, T=200, H=2, seed=10)
+    t = to_device(inp, device, "bf16")
+    s0 = torch.from_numpy(state_like(np.random.default_rng(3), 1, 2, 64)).to(device)
+    _, s_ref = muir.chunk_fwd(*[t[n] for n in NAMES], s0=s0.clone(), chunk=64)
+    state = s0.clone()
+    muir.chunk_fwd(*[t[n] for n in NAMES], s0=state, s_out=state, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(state, s_ref)
+    empty = {n: (x[:, :0].contiguous() if n != "r" else x) for n, x in t.items()}
+    o, s = muir.chunk_fwd(*[empty[n] for n in NAMES], s0=s0, chunk=64)
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(s, s0)
+    _, z = muir.chunk_fwd(*[empty[n] for n in NAMES], chunk=128)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z) == 0
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_extreme_decays_stay_finite(device, chunk):
+    """Decays of exactly 0, 1e-30 and 1, mixed with U(1e-3, 0.05) stress rows: the
+    pivoted products never divide, so every value stays finite and on the oracle."""
+    inp = workloads.chunk_inputs(3, B=1, T=600, H=4, seed=11)
+    a = inp["a"]
+    rng = np.random.default_rng(12)
+    pick = rng.uniform(size=a.shape)
+    a[pick < 0.05] = 0.0
+    a[(pick >= 0.05) & (pick < 0.1)] = 1e-30
+    a[(pick >= 0.1) & (pick < 0.2)] = 1.0
+    a[:, 100:140, 1, :] = 1.0
+    o, s = gpu_fwd(inp, device, chunk)
+    assert_parity(o, s, *ref_fwd(inp), 2e-2, f"extreme decays C={chunk}")
+
+
+def test_full_erase_and_no_decay_special_cases(device):
+    """e = 1 and a = 1 on some heads (the exact-erase and pure delta-rule corners)."""
+    inp = workloads.chunk_inputs(2, B=1, T=300, H=3, qkv="f32", seed=13)
+    inp["e"][:, :, 0] = 1.0
+    inp["a"][:, :, 1] = 1.0
+    inp["e"][:, :, 2] = 0.0
+    o, s = gpu_fwd(inp, device, 128)
+    assert_parity(o, s, *ref_fwd(inp), 1e-4, "special gates fp32")
