@@ -1,0 +1,239 @@
+"""Benchmark of the chunkwise gated delta rule (Muir) on one MI355X.
+
+Prints ONE JSON line. A step is one pass of the chunk forward over one layer call of
+the long-context workload (B=1, H=16, d=128, T=32768, chunk 256, bf16 q/k/v, fp32
+gates and state): the parallel phase (decay products, pivoted operands, Gram blocks)
+then the sequential phase (block-Neumann solve, readout, state carry). ``value`` is
+tokens/s per layer over the timed steps, with inputs already resident in HBM.
+
+Also measured in the same run and reported as secondary fields: the 1.34B-class
+shape at T=4096 (B=8, chunk 128 and 256), and the decode step (B=256 x H=16 x 128x128
+fp32 states, one layer call) in GB/s. Each kernel's average duration comes from HIP
+events recorded around it on the stream it runs on. ``cpu_baseline`` is the CPU
+oracle's fp32 token recurrence on the same long-context workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only main]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5166e15      # flop/s, dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+NAMES = "q k v a g e w r".split()
+
+
+def algorithmic(d, chunk, qkv_bytes=2):
+    """Per token-head algorithmic bytes and MFMA flops of each phase.
+
+    prepare: reads q, k (qkv dtype) and a, g (fp32); Gram M and P: 2*C*d flops.
+    scan:    reads v (qkv dtype), e, w (fp32), writes o (qkv dtype);
+             H, (Qh*gamma) S0, (K*beta)^T U: 6*d*d flops; solve and P U: 2*C*d flops.
+    """
+    return {
+        "prepare": {"bytes": 2 * d * qkv_bytes + 2 * d * 4, "flops": 2 * chunk * d},
+        "scan": {"bytes": 2 * d * qkv_bytes + 2 * d * 4, "flops": 6 * d * d + 2 * chunk * d},
+    }
+
+
+def to_dev(inp, dev):
+    import numpy as np
+    import torch
+    qdt = torch.bfloat16 if inp["qkv"] == "bf16" else torch.float32
+    return {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to(
+        dev, qdt if n in ("q", "k", "v") else torch.float32) for n in NAMES}
+
+
+def time_chunk(inp, chunk, dev, steps, warmup):
+    """Time `steps` chunk forwards; returns dict of per-step and per-kernel times (ms)."""
+    import torch
+    import gated_delta_rule_06_amd as muir
+    t = to_dev(inp, dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    code = muir.MUIR_BF16 if inp["qkv"] == "bf16" else muir.MUIR_F32
+    ws = torch.empty(muir.chunk_fwd_workspace_size(B, T, H, d, d, chunk, code),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(t["v"])
+    s_out = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        muir.chunk_fwd_prepare(t["q"], t["k"], t["a"], t["g"], t["r"], chunk=chunk, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        muir.chunk_fwd_scan(t["v"], t["e"], t["w"], None, chunk=chunk, workspace=ws, o=o,
+                            s_out=s_out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    prep = [e[0].elapsed_time(e[1]) for e in evs]
+    scan = [e[1].elapsed_time(e[2]) for e in evs]
+    total = evs[0][0].elapsed_time(evs[-1][2])
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s_out).all()
+    return {"ms_per_step": total / steps, "wall_ms_per_step": wall / steps,
+            "prepare_ms": sum(prep) / steps, "scan_ms": sum(scan) / steps}
+
+
+def chunk_report(name, inp, chunk, r):
+    d, tok_heads = inp["d"], inp["B"] * inp["T"] * inp["H"]
+    alg = algorithmic(d, chunk)
+    out = {"workload": name, "chunk": chunk,
+           "tokens_per_s_per_layer": inp["B"] * inp["T"] / (r["ms_per_step"] * 1e-3),
+           "ms_per_call": r["ms_per_step"], "prepare_ms": r["prepare_ms"], "scan_ms": r["scan_ms"]}
+    call_bytes = sum(p["bytes"] for p in alg.values()) * tok_heads
+    call_flops = sum(p["flops"] for p in alg.values()) * tok_heads
+    sec = r["ms_per_step"] * 1e-3
+    out["hbm_frac"] = call_bytes / sec / HBM_PEAK
+    out["mfma_frac"] = call_flops / sec / BF16_PEAK
+    return out
+
+
+def time_decode(dev, steps, warmup):
+    import numpy as np
+    import torch
+    import gated_delta_rule_06_amd as muir
+    import workloads
+    cfg = workloads.DECODE_CONFIG
+    B, H, d = cfg.B, cfg.H, cfg.d
+    u, r = workloads.decode_base(cfg, L=1)
+    u_t = torch.from_numpy(u.astype(np.float32)).to(dev)
+    x = workloads.decode_step_inputs_torch(0, u_t, dev, B=B, cfg=cfg)
+    args = [x[n][0] for n in ("q", "k", "v", "a", "g", "e", "w")]
+    r_t = torch.from_numpy(r[0]).to(dev)
+    state = torch.randn(B, H, d, d, device=dev) * 0.1
+    o = torch.empty(B, H, d, dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        muir.decode_step(*args, r_t, state, o=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        muir.decode_step(*args, r_t, state, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_head = 2 * d * d * 4 + 3 * d * 2 + 4 * d * 4 + d * 2   # 134,144 B at d = 128
+    gbs = per_head * B * H / (ms * 1e-3) / 1e9
+    assert torch.isfinite(state).all()
+    return {"workload": "decode B256 H16 d128 (one layer call)", "ms_per_call": ms,
+            "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / HBM_PEAK, "bytes_per_head_step": per_head}
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    """The CPU oracle (fp32 token recurrence, as it stands) on a bounded sample of the
+    long-context workload: all 16 heads, the first T_s tokens, T_s sized from a short
+    probe so the measured run takes at most ~budget_s."""
+    import oracle
+    threads = oracle.max_threads()
+    T = inp["T"]
+    sl = lambda n, T_s: inp[n][:, :T_s] if n != "r" else inp[n]
+    probe = min(T, 1024)
+    t0 = time.perf_counter()
+    oracle.recurrent(*[sl(n, probe) for n in NAMES], precision="f32", threads=threads)
+    per_tok = (time.perf_counter() - t0) / probe
+    T_s = int(min(T, max(probe, budget_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.recurrent(*[sl(n, T_s) for n in NAMES], precision="f32", threads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": inp["B"] * T_s / sec, "unit": "tokens/s/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp32 token recurrence in C (OpenMP) on the first {T_s} of {T} tokens, "
+                      f"all {inp['H']} heads, B={inp['B']}, d={inp['d']}; {sec:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["all", "main", "t4k", "decode"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the chunk forward shards over (batch, head) with no "
+              f"communication and no multi-GPU path is built; --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    dev = torch.device("cuda", 0)
+    torch.cuda.init()
+
+    result = {"metric": "chunk-fwd tokens/s/layer @H16 d128 T4K/32K; %MFMA peak; "
+                        "decode-step HBM GB/s",
+              "unit": "tokens/s/layer", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    secondary = {}
+    main_inp = None
+    if args.only in ("all", "main"):
+        main_inp = workloads.chunk_inputs(3)
+        name = "chunk_fwd long-context B1 H16 d128 T32768 C256 bf16"
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+        r = time_chunk(main_inp, 256, dev, args.steps, args.warmup)
+        rep = chunk_report(name, main_inp, 256, r)
+        result["value"] = rep["tokens_per_s_per_layer"]
+        result["ms_per_step"] = r["ms_per_step"]
+        result["config"] = {"workload": name, "B": 1, "T": 32768, "H": 16, "d": 128,
+                            "chunk": 256, "qkv": "bf16", "gates": "fp32", "state": "fp32"}
+        alg = algorithmic(128, 256)
+        tok_heads = main_inp["B"] * main_inp["T"] * main_inp["H"]
+        dom = "scan" if r["scan_ms"] >= r["prepare_ms"] else "prepare"
+        dom_ms = r[f"{dom}_ms"]
+        ach = alg[dom]["bytes"] * tok_heads / (dom_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "kernel": f"chunk_{dom}", "achieved": ach,
+                              "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                              "frac": ach * 1e9 / HBM_PEAK, "traffic": None,
+                              "avg_ms": dom_ms}
+        result["phases_ms"] = {"prepare": r["prepare_ms"], "scan": r["scan_ms"]}
+        result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"]}
+    if args.only in ("all", "t4k"):
+        inp = workloads.chunk_inputs(2)
+        for chunk in (128, 256):
+            name = f"chunk_fwd 1.34B-class B8 H16 d128 T4096 C{chunk} bf16"
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            r = time_chunk(inp, chunk, dev, args.steps, args.warmup)
+            secondary[f"t4k_c{chunk}"] = chunk_report(name, inp, chunk, r)
+        del inp
+        if "value" not in result:
+            best = secondary["t4k_c256"]
+            result["value"] = best["tokens_per_s_per_layer"]
+            result["ms_per_step"] = best["ms_per_call"]
+            result["config"] = {"workload": best["workload"]}
+    if args.only in ("all", "decode"):
+        print("bench: decode step B256 H16 d128", file=sys.stderr, flush=True)
+        secondary["decode"] = time_decode(dev, max(50, args.steps * 10), args.warmup * 5)
+        if "value" not in result:
+            result["value"] = secondary["decode"]["GB_per_s"]
+            result["unit"] = "GB/s"
+            result["ms_per_step"] = secondary["decode"]["ms_per_call"]
+            result["config"] = {"workload": secondary["decode"]["workload"]}
+    result["secondary"] = secondary
+    if main_inp is not None and not args.no_cpu:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(main_inp)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

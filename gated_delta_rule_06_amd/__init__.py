@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = [
-    "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "decode_step",
+    "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_prepare",
+    "chunk_fwd_scan", "decode_step",
     "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
 ]
 
@@ -52,6 +53,10 @@ def lib():
         L.muir_chunk_fwd_workspace_size.restype = sz
         L.muir_chunk_fwd.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd.restype = i
+        L.muir_chunk_fwd_prepare.argtypes = [vp] * 5 + [i] * 6 + [vp, sz, vp]
+        L.muir_chunk_fwd_prepare.restype = i
+        L.muir_chunk_fwd_scan.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_scan.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
         L.muir_decode_step.restype = i
         L.muir_status_string.argtypes = [i]
@@ -163,6 +168,42 @@ def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out
         workspace.numel(), _stream(dev))
     _check(status)
     return o, s_out
+
+
+def chunk_fwd_prepare(q, k, a, g, r, *, chunk: int, workspace):
+    """Parallel phase of the chunk forward (``muir_chunk_fwd_prepare``) into ``workspace``."""
+    import torch
+    B, T, H, dk = q.shape
+    dev = q.device
+    code = _dtype_code(q)
+    _require(q, "q", q.dtype, (B, T, H, dk), dev)
+    _require(k, "k", q.dtype, (B, T, H, dk), dev)
+    for name, t in (("a", a), ("g", g)):
+        _require(t, name, torch.float32, (B, T, H, dk), dev)
+    _require(r, "r", torch.float32, (H, dk), dev)
+    _require(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib().muir_chunk_fwd_prepare(
+        _ptr(q), _ptr(k), _ptr(a), _ptr(g), _ptr(r), B, T, H, dk, chunk, code,
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def chunk_fwd_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None):
+    """Sequential phase of the chunk forward (``muir_chunk_fwd_scan``) from ``workspace``."""
+    import torch
+    B, T, H, dv = v.shape
+    dev = v.device
+    code = _dtype_code(v)
+    for name, t in (("e", e), ("w", w)):
+        _require(t, name, torch.float32, (B, T, H, dv), dev)
+    _require(o, "o", v.dtype, (B, T, H, dv), dev)
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, (B, H, dv, dv), dev)
+    if s_out is not None:
+        _require(s_out, "s_out", torch.float32, (B, H, dv, dv), dev)
+    _require(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib().muir_chunk_fwd_scan(
+        _ptr(v), _ptr(e), _ptr(w), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dv, dv, chunk,
+        code, _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

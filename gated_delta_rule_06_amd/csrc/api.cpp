@@ -95,78 +95,148 @@ size_t muir_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int ch
     return muir::chunk_workspace_bytes(B, T, H, dk, chunk, qkv == MUIR_BF16);
 }
 
+}  // extern "C"
+
+namespace {
+
+// One chunk-forward call as seen by the validator. Pointers a phase does not use are
+// NULL; `prep` / `scan` say which phase's inputs and outputs are required.
+struct ChunkCall {
+    const char *fn;
+    const void *q, *k, *v;
+    const float *a, *g, *e, *w, *r, *s0;
+    void *o;
+    float *s_out;
+    int B, T, H, dk, dv, chunk;
+    muir_dtype_t qkv;
+    const void *workspace;
+    size_t workspace_bytes;
+    bool prep, scan;
+};
+
+muir_status_t validate(const ChunkCall &c) {
+    const char *fn = c.fn;
+    if (c.B < 1 || c.T < 0 || c.H < 1)
+        return fail(MUIR_ERR_SHAPE, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn,
+                    c.B, c.T, c.H);
+    if (c.dk < 1 || c.dv < 1)
+        return fail(MUIR_ERR_SHAPE, "%s: dk=%d dv=%d must be positive", fn, c.dk, c.dv);
+    if (c.qkv != MUIR_F32 && c.qkv != MUIR_BF16)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, static_cast<int>(c.qkv));
+    if (c.dk != c.dv || !supported_d(c.dk))
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: need dk == dv in {64, 128} (got %d, %d)", fn,
+                    c.dk, c.dv);
+    if (!supported_chunk(c.chunk))
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: chunk must be 64, 128 or 256 (got %d)", fn,
+                    c.chunk);
+    if (c.T > 0 && c.prep && (!c.q || !c.k || !c.a || !c.g))
+        return fail(MUIR_ERR_NULL, "%s: q, k, a and g are required", fn);
+    if (c.T > 0 && c.scan && (!c.v || !c.e || !c.w || !c.o))
+        return fail(MUIR_ERR_NULL, "%s: v, e, w and o are required", fn);
+    if (c.prep && !c.r) return fail(MUIR_ERR_NULL, "%s: r is required", fn);
+
+    const size_t es = c.qkv == MUIR_BF16 ? 2 : 4;
+    size_t n_tok, n_state;
+    if (!mul_size(n_tok, {static_cast<size_t>(c.B), static_cast<size_t>(c.T),
+                          static_cast<size_t>(c.H), static_cast<size_t>(c.dk)}) ||
+        !mul_size(n_state, {static_cast<size_t>(c.B), static_cast<size_t>(c.H),
+                            static_cast<size_t>(c.dk), static_cast<size_t>(c.dv)}) ||
+        n_tok > SIZE_MAX / 4 || n_state > SIZE_MAX / 4)
+        return fail(MUIR_ERR_SHAPE, "%s: sizes overflow", fn);
+
+    const size_t need =
+        muir::chunk_workspace_bytes(c.B, c.T, c.H, c.dk, c.chunk, c.qkv == MUIR_BF16);
+    if (need == 0 && c.T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (need > 0) {
+        if (!c.workspace)
+            return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+        if (c.workspace_bytes < need)
+            return fail(MUIR_ERR_WORKSPACE, "%s: workspace has %zu bytes, need %zu", fn,
+                        c.workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(c.workspace) % 256 != 0)
+            return fail(MUIR_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    }
+    const void *all[] = {c.q, c.k, c.v, c.a, c.g, c.e, c.w, c.r, c.s0, c.o, c.s_out};
+    for (const void *p : all)
+        if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
+
+    const Range inputs[] = {
+        range("q", c.q, n_tok * es), range("k", c.k, n_tok * es), range("v", c.v, n_tok * es),
+        range("a", c.a, n_tok * 4), range("g", c.g, n_tok * 4), range("e", c.e, n_tok * 4),
+        range("w", c.w, n_tok * 4), range("r", c.r, static_cast<size_t>(c.H) * c.dk * 4),
+        range("s0", c.s0, n_state * 4)};
+    const Range ro = range("o", c.o, n_tok * es);
+    const Range rs = range("s_out", c.s_out, n_state * 4);
+    const Range rw = range("workspace", c.workspace, need);
+    for (const Range &x : inputs) {
+        if (overlaps(ro, x)) return fail(MUIR_ERR_ALIAS, "%s: o overlaps %s", fn, x.name);
+        if (overlaps(rw, x)) return fail(MUIR_ERR_ALIAS, "%s: workspace overlaps %s", fn, x.name);
+        if (overlaps(rs, x) && !(x.lo == rs.lo && x.hi == rs.hi && strcmp(x.name, "s0") == 0))
+            return fail(MUIR_ERR_ALIAS, "%s: s_out overlaps %s", fn, x.name);
+    }
+    if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw))
+        return fail(MUIR_ERR_ALIAS, "%s: o, s_out and workspace must not overlap", fn);
+    return MUIR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 muir_status_t muir_chunk_fwd(const void *q, const void *k, const void *v, const float *a,
                              const float *g, const float *e, const float *w, const float *r,
                              const float *s0, void *o, float *s_out, int B, int T, int H,
                              int dk, int dv, int chunk, muir_dtype_t qkv, void *workspace,
                              size_t workspace_bytes, muir_stream_t stream) {
-    if (B < 1 || T < 0 || H < 1)
-        return fail(MUIR_ERR_SHAPE, "chunk_fwd: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)",
-                    B, T, H);
-    if (dk < 1 || dv < 1)
-        return fail(MUIR_ERR_SHAPE, "chunk_fwd: dk=%d dv=%d must be positive", dk, dv);
-    if (qkv != MUIR_F32 && qkv != MUIR_BF16)
-        return fail(MUIR_ERR_UNSUPPORTED, "chunk_fwd: unknown dtype %d", static_cast<int>(qkv));
-    if (dk != dv || !supported_d(dk))
-        return fail(MUIR_ERR_UNSUPPORTED, "chunk_fwd: need dk == dv in {64, 128} (got %d, %d)",
-                    dk, dv);
-    if (!supported_chunk(chunk))
-        return fail(MUIR_ERR_UNSUPPORTED, "chunk_fwd: chunk must be 64, 128 or 256 (got %d)",
-                    chunk);
-    if (T > 0 && (!q || !k || !v || !a || !g || !e || !w || !o))
-        return fail(MUIR_ERR_NULL, "chunk_fwd: q, k, v, a, g, e, w and o are required");
-    if (!r) return fail(MUIR_ERR_NULL, "chunk_fwd: r is required");
-
-    const size_t es = qkv == MUIR_BF16 ? 2 : 4;
-    size_t n_tok, n_state;
-    if (!mul_size(n_tok, {static_cast<size_t>(B), static_cast<size_t>(T),
-                          static_cast<size_t>(H), static_cast<size_t>(dk)}) ||
-        !mul_size(n_state, {static_cast<size_t>(B), static_cast<size_t>(H),
-                            static_cast<size_t>(dk), static_cast<size_t>(dv)}) ||
-        n_tok > SIZE_MAX / 4 || n_state > SIZE_MAX / 4)
-        return fail(MUIR_ERR_SHAPE, "chunk_fwd: sizes overflow");
-
-    const size_t need = muir::chunk_workspace_bytes(B, T, H, dk, chunk, qkv == MUIR_BF16);
-    if (need == 0 && T > 0) return fail(MUIR_ERR_SHAPE, "chunk_fwd: workspace size overflows");
-    if (need > 0) {
-        if (!workspace)
-            return fail(MUIR_ERR_WORKSPACE, "chunk_fwd: workspace of %zu bytes required", need);
-        if (workspace_bytes < need)
-            return fail(MUIR_ERR_WORKSPACE, "chunk_fwd: workspace has %zu bytes, need %zu",
-                        workspace_bytes, need);
-        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-            return fail(MUIR_ERR_WORKSPACE, "chunk_fwd: workspace must be 256-byte aligned");
+    const ChunkCall c{"chunk_fwd", q, k, v, a, g, e, w, r, s0, o, s_out, B, T, H, dk, dv, chunk,
+                      qkv, workspace, workspace_bytes, true, true};
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    const bool bf16 = qkv == MUIR_BF16;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (T > 0) {
+        const muir_status_t sp = check_hip(
+            muir::launch_chunk_prepare(q, k, a, g, r, B, T, H, dk, chunk, bf16, workspace, hs),
+            "chunk_fwd prepare launch");
+        if (sp != MUIR_OK) return sp;
     }
-    for (const void *p : {q, k, v, static_cast<const void *>(o), static_cast<const void *>(a), static_cast<const void *>(g),
-                          static_cast<const void *>(e), static_cast<const void *>(w),
-                          static_cast<const void *>(r), static_cast<const void *>(s0),
-                          static_cast<const void *>(s_out)})
-        if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
-            return fail(MUIR_ERR_SHAPE, "chunk_fwd: every buffer must be 16-byte aligned");
-
-    const Range inputs[] = {
-        range("q", q, n_tok * es), range("k", k, n_tok * es), range("v", v, n_tok * es),
-        range("a", a, n_tok * 4), range("g", g, n_tok * 4), range("e", e, n_tok * 4),
-        range("w", w, n_tok * 4), range("r", r, static_cast<size_t>(H) * dk * 4),
-        range("s0", s0, n_state * 4)};
-    const Range ro = range("o", o, n_tok * es);
-    const Range rs = range("s_out", s_out, n_state * 4);
-    const Range rw = range("workspace", workspace, need);
-    for (const Range &x : inputs) {
-        if (overlaps(ro, x)) return fail(MUIR_ERR_ALIAS, "chunk_fwd: o overlaps %s", x.name);
-        if (overlaps(rw, x))
-            return fail(MUIR_ERR_ALIAS, "chunk_fwd: workspace overlaps %s", x.name);
-        if (overlaps(rs, x) && !(x.lo == rs.lo && x.hi == rs.hi && strcmp(x.name, "s0") == 0))
-            return fail(MUIR_ERR_ALIAS, "chunk_fwd: s_out overlaps %s", x.name);
-    }
-    if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw))
-        return fail(MUIR_ERR_ALIAS, "chunk_fwd: o, s_out and workspace must not overlap");
-
     if (T == 0 && !s_out) return ok();
-    return check_hip(muir::launch_chunk_fwd(q, k, v, a, g, e, w, r, s0, o, s_out, B, T, H, dk,
-                                            chunk, qkv == MUIR_BF16, workspace,
-                                            static_cast<hipStream_t>(stream)),
-                     "chunk_fwd launch");
+    return check_hip(muir::launch_chunk_scan(v, e, w, s0, o, s_out, B, T, H, dk, chunk, bf16,
+                                             workspace, hs),
+                     "chunk_fwd scan launch");
+}
+
+muir_status_t muir_chunk_fwd_prepare(const void *q, const void *k, const float *a,
+                                     const float *g, const float *r, int B, int T, int H, int dk,
+                                     int chunk, muir_dtype_t qkv, void *workspace,
+                                     size_t workspace_bytes, muir_stream_t stream) {
+    const ChunkCall c{"chunk_fwd_prepare", q, k, nullptr, a, g, nullptr, nullptr, r, nullptr,
+                      nullptr, nullptr, B, T, H, dk, dk, chunk, qkv, workspace, workspace_bytes,
+                      true, false};
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T == 0) return ok();
+    return check_hip(muir::launch_chunk_prepare(q, k, a, g, r, B, T, H, dk, chunk,
+                                                qkv == MUIR_BF16, workspace,
+                                                static_cast<hipStream_t>(stream)),
+                     "chunk_fwd_prepare launch");
+}
+
+muir_status_t muir_chunk_fwd_scan(const void *v, const float *e, const float *w, const float *s0,
+                                  void *o, float *s_out, int B, int T, int H, int dk, int dv,
+                                  int chunk, muir_dtype_t qkv, const void *workspace,
+                                  size_t workspace_bytes, muir_stream_t stream) {
+    const ChunkCall c{"chunk_fwd_scan", nullptr, nullptr, v, nullptr, nullptr, e, w, nullptr, s0,
+                      o, s_out, B, T, H, dk, dv, chunk, qkv, workspace, workspace_bytes, false,
+                      true};
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T == 0 && !s_out) return ok();
+    return check_hip(muir::launch_chunk_scan(v, e, w, s0, o, s_out, B, T, H, dk, chunk,
+                                             qkv == MUIR_BF16, workspace,
+                                             static_cast<hipStream_t>(stream)),
+                     "chunk_fwd_scan launch");
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

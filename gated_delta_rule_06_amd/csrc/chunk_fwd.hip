@@ -568,24 +568,28 @@ size_t slot_bytes_rt(bool bf16, int d, int chunk) {
 }
 
 template <typename QT, typename OpT, int D, int C>
-hipError_t launch_typed(const void *q, const void *k, const void *v, const float *a,
-                        const float *g, const float *e, const float *w, const float *r,
-                        const float *s0, void *o, float *s_out, int B, int T, int H,
-                        void *workspace, hipStream_t stream) {
+hipError_t prepare_typed(const void *q, const void *k, const float *a, const float *g,
+                         const float *r, int B, int T, int H, void *workspace,
+                         hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
-    if (nchunks > 0) {
-        using LDS = GramLds<OpT, D, C>;
-        auto kg = chunk_gram_kernel<QT, OpT, D, C>;
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kg),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(LDS::BYTES));
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(kg, dim3(nchunks, H, B), dim3(kThreads), LDS::BYTES, stream,
-                           static_cast<const QT *>(q), static_cast<const QT *>(k), a, g, r,
-                           static_cast<unsigned char *>(workspace), T, H, nchunks);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
+    if (nchunks == 0) return hipSuccess;
+    using LDS = GramLds<OpT, D, C>;
+    auto kg = chunk_gram_kernel<QT, OpT, D, C>;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kg),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(LDS::BYTES));
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kg, dim3(nchunks, H, B), dim3(kThreads), LDS::BYTES, stream,
+                       static_cast<const QT *>(q), static_cast<const QT *>(k), a, g, r,
+                       static_cast<unsigned char *>(workspace), T, H, nchunks);
+    return hipGetLastError();
+}
+
+template <typename QT, typename OpT, int D, int C>
+hipError_t scan_typed(const void *v, const float *e, const float *w, const float *s0, void *o,
+                      float *s_out, int B, int T, int H, const void *workspace,
+                      hipStream_t stream) {
+    const int nchunks = (T + C - 1) / C;
     hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C>), dim3(B * H, D / 16), dim3(kThreads), 0,
                        stream, static_cast<const QT *>(v), e, w, s0, static_cast<QT *>(o), s_out,
                        static_cast<const unsigned char *>(workspace), T, H, nchunks);
@@ -603,22 +607,32 @@ size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
     return n * slot;
 }
 
-hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *a,
-                            const float *g, const float *e, const float *w, const float *r,
-                            const float *s0, void *o, float *s_out, int B, int T, int H,
-                            int d, int chunk, bool bf16, void *workspace,
-                            hipStream_t stream) {
-#define MUIR_CHUNK(D, C)                                                                      \
-    if (d == D && chunk == C) {                                                               \
-        if (bf16)                                                                             \
-            return launch_typed<bf16_t, bf16_t, D, C>(q, k, v, a, g, e, w, r, s0, o, s_out, B, \
-                                                      T, H, workspace, stream);               \
-        return launch_typed<float, float, D, C>(q, k, v, a, g, e, w, r, s0, o, s_out, B, T, H, \
-                                                workspace, stream);                           \
-    }
-    MUIR_CHUNK(64, 64) MUIR_CHUNK(64, 128) MUIR_CHUNK(64, 256)
-    MUIR_CHUNK(128, 64) MUIR_CHUNK(128, 128) MUIR_CHUNK(128, 256)
-#undef MUIR_CHUNK
+hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, const float *g,
+                                const float *r, int B, int T, int H, int d, int chunk, bool bf16,
+                                void *workspace, hipStream_t stream) {
+#define MUIR_PREP(D, C)                                                                        \
+    if (d == D && chunk == C)                                                                  \
+        return bf16 ? prepare_typed<bf16_t, bf16_t, D, C>(q, k, a, g, r, B, T, H, workspace,    \
+                                                          stream)                              \
+                    : prepare_typed<float, float, D, C>(q, k, a, g, r, B, T, H, workspace, stream);
+    MUIR_PREP(64, 64) MUIR_PREP(64, 128) MUIR_PREP(64, 256)
+    MUIR_PREP(128, 64) MUIR_PREP(128, 128) MUIR_PREP(128, 256)
+#undef MUIR_PREP
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *s0,
+                             void *o, float *s_out, int B, int T, int H, int d, int chunk,
+                             bool bf16, const void *workspace, hipStream_t stream) {
+#define MUIR_SCAN(D, C)                                                                        \
+    if (d == D && chunk == C)                                                                  \
+        return bf16 ? scan_typed<bf16_t, bf16_t, D, C>(v, e, w, s0, o, s_out, B, T, H,          \
+                                                       workspace, stream)                      \
+                    : scan_typed<float, float, D, C>(v, e, w, s0, o, s_out, B, T, H, workspace, \
+                                                     stream);
+    MUIR_SCAN(64, 64) MUIR_SCAN(64, 128) MUIR_SCAN(64, 256)
+    MUIR_SCAN(128, 64) MUIR_SCAN(128, 128) MUIR_SCAN(128, 256)
+#undef MUIR_SCAN
     return hipErrorInvalidValue;
 }
 

@@ -15,10 +15,14 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
 // Bytes of the chunk-forward workspace for these sizes (0 when they overflow).
 size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16);
 
-hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *a,
-                            const float *g, const float *e, const float *w, const float *r,
-                            const float *s0, void *o, float *s_out, int B, int T, int H,
-                            int d, int chunk, bool bf16, void *workspace,
-                            hipStream_t stream);
+// Phase P: decay products, pivoted operands and intra-chunk Gram blocks -> workspace.
+hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, const float *g,
+                                const float *r, int B, int T, int H, int d, int chunk, bool bf16,
+                                void *workspace, hipStream_t stream);
+
+// Phase S: sequential chunk scan (solve, readout, state carry) from the workspace.
+hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *s0,
+                             void *o, float *s_out, int B, int T, int H, int d, int chunk,
+                             bool bf16, const void *workspace, hipStream_t stream);
 
 }  // namespace muir

@@ -62,11 +62,12 @@ typedef enum {
 
 /*
  * Workspace bytes needed by muir_chunk_fwd for these sizes (0 for invalid sizes).
- * The workspace holds, per (batch, head, chunk), the chunk's lower-triangular
- * intra-chunk matrices (the decayed key-key Gram M and query-key Gram P) in fp32,
- * 16x16 blocks, so its size is 2 * B * H * ceil(T/chunk) * (chunk/16)(chunk/16+1)/2
- * * 1 KiB. It must be 256-byte aligned. Its contents are scratch: nothing is
- * expected in it on entry or kept from it on return.
+ * The workspace holds, per (batch, head, chunk), what the parallel phase hands to the
+ * sequential one: the lower-triangular intra-chunk Gram matrices M and P in 16x16
+ * blocks, the decay-scaled operands K*gamma, (r*g*q)*gamma and (K*beta)^T, and the
+ * whole-chunk decay, in the operand precision (bf16 for bf16 q/k/v, fp32 otherwise).
+ * It must be 256-byte aligned. Its contents are scratch: nothing is expected in it
+ * on entry to muir_chunk_fwd or kept from it on return.
  */
 size_t muir_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int chunk,
                                      muir_dtype_t qkv);
@@ -108,6 +109,39 @@ muir_status_t muir_chunk_fwd(
     const float *s0, void *o, float *s_out,
     int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
     void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
+ * The two phases of muir_chunk_fwd as separate calls, for callers that schedule or
+ * time them on their own. muir_chunk_fwd(...) is exactly muir_chunk_fwd_prepare(...)
+ * followed by muir_chunk_fwd_scan(...) on the same stream with the same workspace.
+ *
+ * muir_chunk_fwd_prepare: the parallel phase, one work item per (batch, head, chunk):
+ *   the decay running products pivoted at 16-token block boundaries (every factor in
+ *   [0, 1], no division), the decay-scaled operands K*gamma, (r*g*q)*gamma and
+ *   (K*beta)^T, the whole-chunk decay gamma_C, and the lower-triangular intra-chunk
+ *   Gram matrices M (decayed key-key, strictly lower) and P (decayed query-key,
+ *   inclusive) in 16x16 blocks on the matrix cores. Writes them into `workspace`.
+ *   Arguments as for muir_chunk_fwd (dv is taken equal to dk). T == 0 launches nothing.
+ *
+ * muir_chunk_fwd_scan: the sequential phase, one work item per (batch, head, 16 value
+ *   columns), chunk after chunk: the prediction of the carried state, the recursive
+ *   block-Neumann solve of every value column's triangular system, the readout
+ *   o = (r*g*q*gamma) S0 + P U and the state carry S = Diag(gamma_C) S0 + (K*beta)^T U.
+ *   Reads `workspace` as left by muir_chunk_fwd_prepare for the same sizes and inputs;
+ *   the workspace must not be modified between the two calls. T == 0 copies s0 (or
+ *   zeros) into s_out.
+ *
+ * Errors as for muir_chunk_fwd, restricted to the arguments each phase takes.
+ */
+muir_status_t muir_chunk_fwd_prepare(
+    const void *q, const void *k, const float *a, const float *g, const float *r,
+    int B, int T, int H, int dk, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+muir_status_t muir_chunk_fwd_scan(
+    const void *v, const float *e, const float *w, const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
  * One recurrent step per (batch, head), updating the state in place (decode).
