@@ -16,15 +16,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even float32 -> bfloat16 bits; NaN stays a quiet NaN.
+// Round-to-nearest-even float32 -> bfloat16 bits. The __bf16 conversion lowers to
+// gfx950's v_cvt_pk_bf16_f32 (nearest-even, NaN stays NaN), with no branches.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
-        return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    }
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 
 // Element access for the two q/k/v/o types.
 template <typename T> struct elem;

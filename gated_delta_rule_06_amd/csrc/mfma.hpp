@@ -20,6 +20,8 @@ namespace muir {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename OpT> struct Mma;
 
@@ -57,6 +59,20 @@ template <> struct Mma<bf16_t> {
     }
     static __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
     static __device__ __forceinline__ bf16_t from_f32(float x) { return bf16_t{f32_to_bf16(x)}; }
+
+    // K = 16 step (one v_mfma_f32_16x16x16_bf16): element j of lane l sits at
+    // contraction index 4*(l/16) + j.
+    static __device__ __forceinline__ int k16idx(int lane, int j) { return (lane >> 4) * 4 + j; }
+    static __device__ __forceinline__ f32x4_t mma_k16(const float (&a)[4], const float (&b)[4],
+                                                      f32x4_t c) {
+        s16x4_t ua, ub;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ua[j] = static_cast<short>(f32_to_bf16(a[j]));
+            ub[j] = static_cast<short>(f32_to_bf16(b[j]));
+        }
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua, ub, c, 0, 0, 0);
+    }
 };
 
 template <> struct Mma<float> {
@@ -75,9 +91,66 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ void store(float *p, const float (&x)[1]) { *p = x[0]; }
     static __device__ __forceinline__ float to_f32(float x) { return x; }
     static __device__ __forceinline__ float from_f32(float x) { return x; }
+
+    // K = 16 step (four v_mfma_f32_16x16x4_f32): element j of lane l sits at
+    // contraction index 4*j + l/16.
+    static __device__ __forceinline__ int k16idx(int lane, int j) { return 4 * j + (lane >> 4); }
+    static __device__ __forceinline__ f32x4_t mma_k16(const float (&a)[4], const float (&b)[4],
+                                                      f32x4_t c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
 };
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// N consecutive elements (16-byte aligned for N >= 4) as floats.
+template <int N> __device__ __forceinline__ void load_vec(const float *p, float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const float4 t = reinterpret_cast<const float4 *>(p)[i];
+            x[4 * i] = t.x; x[4 * i + 1] = t.y; x[4 * i + 2] = t.z; x[4 * i + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = p[i];
+    }
+}
+template <int N> __device__ __forceinline__ void load_vec(const bf16_t *p, float (&x)[N]) {
+    if constexpr (N == 8) {
+        const u16x8_t u = *reinterpret_cast<const u16x8_t *>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(u[i]);
+    } else if constexpr (N == 4) {
+        const u16x4_t u = *reinterpret_cast<const u16x4_t *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = bf16_to_f32(u[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = bf16_to_f32(p[i].bits);
+    }
+}
+// Four consecutive elements from an fp32 accumulator.
+__device__ __forceinline__ void store4(float *p, f32x4_t v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16_t *p, f32x4_t v) {
+    u16x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
+    *reinterpret_cast<u16x4_t *>(p) = u;
+}
+
+// Workgroup barrier that orders LDS only. Waves of one workgroup never exchange data
+// through global memory inside these kernels, so global loads issued as prefetches
+// stay in flight across the barrier (a full __syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Order this wave's LDS writes before its following LDS reads from other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
