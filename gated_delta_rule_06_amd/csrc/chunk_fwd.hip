@@ -35,6 +35,9 @@
 //    leaf behind: the readout O_L = (Qh*gamma)_L S0 + P_{L,<=L} U_{<=L} and the state
 //    contribution (K*beta)_L^T U_L, both on MFMA. The chunk's Gram blocks M are copied
 //    into LDS by direct global->LDS loads issued during the previous chunk.
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -50,23 +53,34 @@ constexpr size_t kLdsBudget = 160 * 1024 - 1024;
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace slot of one (batch, head, chunk). M and P blocks are 16x16 row-major
-// (row = later token t, column = earlier token s), lower-triangular block order.
+// (row = later token t, column = earlier token s), lower-triangular block order; the
+// diagonal blocks of M are kept apart in fp32 (MD) for the leaf solve, and the tri slots
+// of M's diagonal blocks are left unused.
+//
+// The matrix-core operands are stored in the order the scan consumes them. Within every
+// group of 32 positions, position 8g + 4h + i holds index 16h + 4g + i of the group
+// (g < 4, h < 2, i < 4): lane group g then finds, in one 8-element load, the indices
+// 4g..4g+3 of both 16-halves. Kg and Qg ([C][D]) are permuted along channels, KbT
+// ([D][C]) along tokens.
 template <typename OpT, int D, int C> struct Slot {
     static constexpr int NB = C / 16;
     static constexpr int NTRI = NB * (NB + 1) / 2;
     static constexpr size_t M_BYTES = size_t(NTRI) * 256 * sizeof(OpT);
     static constexpr size_t M_OFF = 0;
-    // gamma_C sits right after M, inside a 1 KiB window, so one copy brings both into LDS.
-    static constexpr size_t GC_OFF = M_OFF + M_BYTES;
-    static constexpr size_t MG_BYTES = M_BYTES + 1024;
-    static constexpr size_t P_OFF = GC_OFF + 1024;
+    static constexpr size_t GC_OFF = align256(M_OFF + M_BYTES);       // gamma_C, D floats
+    static constexpr size_t P_OFF = align256(GC_OFF + size_t(D) * 4);
     static constexpr size_t KG_OFF = align256(P_OFF + M_BYTES);
     static constexpr size_t QG_OFF = align256(KG_OFF + size_t(C) * D * sizeof(OpT));
     static constexpr size_t KBT_OFF = align256(QG_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t BYTES = align256(KBT_OFF + size_t(C) * D * sizeof(OpT));
-    static_assert(M_BYTES % 1024 == 0 && D * 4 <= 1024, "M + gamma_C copy window");
+    static constexpr size_t MD_OFF = align256(KBT_OFF + size_t(C) * D * sizeof(OpT));
+    static constexpr size_t BYTES = align256(MD_OFF + size_t(NB) * 256 * 4);
     static __host__ __device__ constexpr int tri(int bt, int bs) { return bt * (bt + 1) / 2 + bs; }
 };
+
+// Storage position of index x under the 32-group permutation described above.
+__host__ __device__ constexpr int pair_perm(int x) {
+    return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
 
 // LDS of the prepare kernel: block totals, K*sigma (padded rows), per-wave tables.
 template <typename OpT, int D, int C> struct PrepLds {
@@ -110,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
     OpT *__restrict__ gQg = reinterpret_cast<OpT *>(slot + SL::QG_OFF);
     OpT *__restrict__ gKbT = reinterpret_cast<OpT *>(slot + SL::KBT_OFF);
     float *__restrict__ gGC = reinterpret_cast<float *>(slot + SL::GC_OFF);
+    float *__restrict__ gMD = reinterpret_cast<float *>(slot + SL::MD_OFF);
 
     const int t0 = ci * C;
     const int nreal = min(C, T - t0);
@@ -177,8 +192,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             const int tt = 16 * bb + t;
             pi *= av[t];
             const float gam = G * pi;
-            gKg[size_t(tt) * D + ch] = MM::from_f32(kv[t] * gam);
-            gQg[size_t(tt) * D + ch] = MM::from_f32(qv[t] * gam);
+            gKg[size_t(tt) * D + pair_perm(ch)] = MM::from_f32(kv[t] * gam);
+            gQg[size_t(tt) * D + pair_perm(ch)] = MM::from_f32(qv[t] * gam);
         }
         float kbt[16];
         float sig = 1.f;
@@ -188,10 +203,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             sh_bb[(16 * bb + t) * DB + ch] = MM::from_f32(kv[t] * sig);
             sig *= av[t];
         }
-        OpT *dst = gKbT + size_t(ch) * C + 16 * bb;
+        OpT *dst = gKbT + size_t(ch) * C;
 #pragma unroll
         for (int t = 0; t < 16; t += 4)
-            store4(dst + t, f32x4_t{kbt[t], kbt[t + 1], kbt[t + 2], kbt[t + 3]});
+            store4(dst + pair_perm(16 * bb + t), f32x4_t{kbt[t], kbt[t + 1], kbt[t + 2], kbt[t + 3]});
     }
     lds_barrier();
 
@@ -296,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) leafP[i] += (og + i == tl) ? accD[i] : 0.f;
         }
-        store4(gM + size_t(SL::tri(bt, bt)) * 256 + tl * 16 + og, leafM);
+        store4(gMD + size_t(bt) * 256 + tl * 16 + og, leafM);
         store4(gP + size_t(SL::tri(bt, bt)) * 256 + tl * 16 + og, leafP);
         if (bt == 0) continue;
 
@@ -354,404 +369,451 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 // ---------------------------------------------------------------------------------
 // Phase S: sequential chunk scan.
 // ---------------------------------------------------------------------------------
-// Four (K*beta)^T values of one lane for a K = 16 step, kept packed and unconverted
-// while the load is in flight.
-template <typename OpT> struct KbFrag;
-template <> struct KbFrag<bf16_t> {
-    u16x4_t u;  // contraction indices 4*(lane/16) + [0, 4): one 8-byte load
-    __device__ __forceinline__ void load(const bf16_t *row, int lane) {
-        u = *reinterpret_cast<const u16x4_t *>(row + Mma<bf16_t>::k16idx(lane, 0));
-    }
-    __device__ __forceinline__ void get(float (&x)[4]) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = bf16_to_f32(u[j]);
-    }
-};
-template <> struct KbFrag<float> {
-    float f[4];  // contraction indices 4*j + lane/16
-    __device__ __forceinline__ void load(const float *row, int lane) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f[j] = row[Mma<float>::k16idx(lane, j)];
-    }
-    __device__ __forceinline__ void get(float (&x)[4]) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = f[j];
-    }
-};
-
-template <typename OpT, int D, int C> struct ScanLds {
-    using SL = Slot<OpT, D, C>;
-    static constexpr int CP = C + 4;                                  // padded token row
-    static constexpr size_t TILE = size_t(16) * CP * 4;               // one [column][token] tile
-    static constexpr size_t REST = 2 * TILE + size_t(D) * 16 * 4 + 256 * 4 + size_t(D) * 4;
-    static constexpr bool M_IN_LDS = SL::MG_BYTES + REST <= kLdsBudget;
-    static constexpr size_t M_SZ = M_IN_LDS ? SL::MG_BYTES : 0;   // M blocks + gamma_C window
-    static constexpr size_t U_OFF = M_SZ;
-    static constexpr size_t E_OFF = U_OFF + TILE;
-    static constexpr size_t S_OFF = E_OFF + TILE;
-    static constexpr size_t L_OFF = S_OFF + size_t(D) * 16 * 4;
-    static constexpr size_t G_OFF = L_OFF + 256 * 4;              // gamma_C of this chunk
-    static constexpr size_t BYTES = G_OFF + size_t(D) * 4;
-    static_assert(BYTES <= kLdsBudget, "LDS budget");
-};
-
-typedef __attribute__((address_space(1))) const void gptr_t;
-typedef __attribute__((address_space(3))) void lptr_t;
-
-// Copy `bytes` (a multiple of 1 KiB) from global memory into LDS with direct
-// global->LDS loads: every wave moves 1 KiB per instruction, 16 bytes per lane.
-__device__ __forceinline__ void copy_to_lds(const void *gsrc, void *ldst, size_t bytes, int wave,
-                                            int lane, int nwaves = kWaves) {
-    const int n = static_cast<int>(bytes / 1024);
-    for (int c = wave; c < n; c += nwaves) {
-        const char *src = static_cast<const char *>(gsrc) + size_t(c) * 1024 + lane * 16;
-        char *dst = static_cast<char *>(ldst) + size_t(c) * 1024;
-        __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)dst, 16, 0, 0);
-    }
+// Every product of the scan is D[16x16] += A[16xK] B[16xK]^T on the matrix cores with
+// K = 16 (mma4, four values per lane) or K = 32 (mma8, eight values per lane). Lane l
+// holds row l%16 of each operand; which contraction index its j-th value stands for is
+// chosen by the caller, the same on both sides, so the hardware's own k order never
+// matters. Accumulator: lane l holds column l%16, rows 4(l/16) + i.
+// Buffer resources: every load and store of the scan goes through a descriptor whose
+// base is wave-uniform, with a 32-bit per-lane byte offset and a uniform byte offset.
+// Reads past num_records return zero and writes past it are dropped, which is how the
+// tokens past the end of the sequence are handled.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), 0);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
+}
+__device__ __forceinline__ f32x4_t buf_load_f4(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(f32x4_t, buf_load16(r, voff, soff));
 }
 
-// Leaves are numbered linearly over the whole sequence (leaf lam = chunk lam / NB, row
-// block lam % NB), so every prefetch below may reach into the next chunk.
+template <typename OpT> struct Frag;
+template <> struct Frag<bf16_t> {
+    using f4 = u16x4_t;
+    using f8 = u16x8_t;
+    static __device__ __forceinline__ f4 bload4(rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
+    }
+    static __device__ __forceinline__ f8 bload8(rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(u16x8_t, buf_load16(r, voff, soff));
+    }
+    static __device__ __forceinline__ f4 load4(const bf16_t *p) {
+        return *reinterpret_cast<const u16x4_t *>(p);
+    }
+    static __device__ __forceinline__ f8 load8(const bf16_t *p) {
+        return *reinterpret_cast<const u16x8_t *>(p);
+    }
+    static __device__ __forceinline__ f8 cat(f4 a, f4 b) {
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ f4 pack(f32x4_t v) {
+        u16x4_t u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
+        return u;
+    }
+    // Lane (n, g) of the 16x16 identity as an mma4 operand: value j is I[n][4g + j].
+    static __device__ __forceinline__ f4 unit(int n, int g) {
+        u16x4_t u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = n == 4 * g + j ? 0x3f80 : 0;
+        return u;
+    }
+    // K = 16 products run as the K = 32 instruction with a zero upper half: an
+    // accumulation chain that alternates the 16x16x16 and 16x16x32 bf16 instructions
+    // needs more wait states between them than the compiler inserts on gfx950, so only
+    // one instruction kind is ever used.
+    static __device__ __forceinline__ f32x4_t mma4(f4 a, f4 b, f32x4_t c) {
+        const f4 z = {0, 0, 0, 0};
+        return mma8(cat(a, z), cat(b, z), c);
+    }
+    static __device__ __forceinline__ f32x4_t mma8(f8 a, f8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct Frag<float> {
+    using f4 = f32x4_t;
+    struct f8 {
+        f32x4_t lo, hi;
+    };
+    static __device__ __forceinline__ f4 load4(const float *p) {
+        const float4 t = *reinterpret_cast<const float4 *>(p);
+        return f32x4_t{t.x, t.y, t.z, t.w};
+    }
+    static __device__ __forceinline__ f8 load8(const float *p) { return {load4(p), load4(p + 4)}; }
+    static __device__ __forceinline__ f4 bload4(rsrc_t r, unsigned voff, unsigned soff) {
+        return buf_load_f4(r, voff, soff);
+    }
+    static __device__ __forceinline__ f8 bload8(rsrc_t r, unsigned voff, unsigned soff) {
+        return {buf_load_f4(r, voff, soff), buf_load_f4(r, voff + 16, soff)};
+    }
+    static __device__ __forceinline__ f8 cat(f4 a, f4 b) { return {a, b}; }
+    static __device__ __forceinline__ f4 pack(f32x4_t v) { return v; }
+    static __device__ __forceinline__ f4 unit(int n, int g) {
+        f32x4_t u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = n == 4 * g + j ? 1.f : 0.f;
+        return u;
+    }
+    static __device__ __forceinline__ f32x4_t mma4(f4 a, f4 b, f32x4_t c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f32x4_t mma8(f8 a, f8 b, f32x4_t c) {
+        return mma4(a.hi, b.hi, mma4(a.lo, b.lo, c));
+    }
+};
+
+// One step of the leaf's forward substitution for the four value columns a lane holds:
+// x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
+// broadcast inside the FMA. Within a step the four columns use different registers, so
+// each register is read by DPP at least three instructions after it was written; the
+// first step waits the two states a DPP read needs after a VALU write.
+template <int S>
+__device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, float &x3, float n0,
+                                           float n1, float n2, float n3) {
+#define MUIR_BCAST_FMA(R, N) \
+    "v_fmac_f32_dpp " R ", " R ", " N " row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+    if constexpr (S == 0) {
+        asm("s_nop 1\n\t" MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5")
+                MUIR_BCAST_FMA("%2", "%6") MUIR_BCAST_FMA("%3", "%7")
+            : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+            : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+    } else {
+        asm(MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5") MUIR_BCAST_FMA("%2", "%6")
+                MUIR_BCAST_FMA("%3", "%7")
+            : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+            : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+    }
+#undef MUIR_BCAST_FMA
+}
+
+// Calls fn(std::integral_constant<int, 0>{}) ... fn(std::integral_constant<int, N-1>{}) in
+// order, so that indices into register arrays are compile-time constants.
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn &&fn, std::integer_sequence<int, Is...>) {
+    (fn(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename Fn> __device__ __forceinline__ void static_for(Fn &&fn) {
+    static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
+
+// Four consecutive q/k/v-typed elements through a buffer resource.
+template <typename QT> struct Row4;
+template <> struct Row4<bf16_t> {
+    using raw = u16x4_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
+    }
+    static __device__ __forceinline__ float get(raw v, int i) { return bf16_to_f32(v[i]); }
+    static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
+        u16x4_t u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, int(voff), int(soff), 0);
+    }
+};
+template <> struct Row4<float> {
+    using raw = f32x4_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
+        return buf_load_f4(r, voff, soff);
+    }
+    static __device__ __forceinline__ float get(raw v, int i) { return v[i]; }
+    static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(voff), int(soff), 0);
+    }
+};
+
+// Per-leaf inputs of the serial chain, row layout: lane (t, g) holds token t of the
+// leaf and value columns 4g..4g+3 of the tile.
+template <typename QT> struct LeafIn {
+    f32x4_t ev, wv;
+    typename Row4<QT>::raw vv;
+    f32x4_t md[4];  // row t of the leaf's diagonal M block (fp32)
+};
+
+// The scan: one wavefront per (batch, head, 16 value columns), sequential over chunks
+// and over the 16-token leaves inside each chunk. Value columns are exactly independent,
+// so nothing is shared between wavefronts. For leaf L of a chunk with start state S0:
+//   acc = (K*gamma)_L S0 + sum_{l<L} M_{L,l} U_l          (matrix cores)
+//   (I + Diag(e) M_LL) u = w*v - e*acc                      (forward substitution)
+//   O_L = (Qh*gamma)_L S0 + sum_{l<=L} P_{L,l} U_l          (matrix cores)
+//   S_C = Diag(gamma_C) S0 + sum_L (K*beta)_L^T U_L         (matrix cores)
+// Only M_{L,L-1} U_{L-1}, the substitution and one transpose lie on the serial path; the
+// other products of each leaf are issued while the substitution runs.
+//
+// Layouts: "row layout" (lane (t, g): token t, columns 4g..4g+3) is what the
+// substitution works in, and is the accumulator layout of products whose B operand rows
+// are tokens. U is kept as an operand with rows = value columns and values = tokens
+// 4g..4g+3 of the leaf; an mma4 against the identity turns a row-layout u into it. The
+// state is kept as accumulators with rows = channels, columns = value columns.
 template <typename QT, typename OpT, int D, int C>
-__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
+__global__ __launch_bounds__(64) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ s0, QT *__restrict__ o, float *__restrict__ s_out,
-    const unsigned char *__restrict__ ws, int T, int H, int nchunks) {
+    const unsigned char *__restrict__ ws, int T, int H, int BH, int nchunks) {
     using SL = Slot<OpT, D, C>;
-    using LY = ScanLds<OpT, D, C>;
-    using MM = Mma<OpT>;
-    using frag = typename MM::frag;
-    constexpr int NB = C / 16;            // 16-token leaves per chunk
-    constexpr int NCT = D / 16;           // 16-row channel tiles of the state
-    constexpr int CP = LY::CP;
-    constexpr int NKD = D / MM::KSTEP;
-    constexpr int NKC = C / MM::KSTEP;    // k-steps over a whole chunk
-    constexpr int VALS = MM::VALS;
-    constexpr int CT_PER = (NCT + 2) / 3;  // state tiles per follower wave (waves 1..3)
+    using F = Frag<OpT>;
+    using f4 = typename F::f4;
+    using f8 = typename F::f8;
+    constexpr int NB = C / 16;    // leaves per chunk
+    constexpr int NCT = D / 16;   // 16-channel tiles of the state
+    constexpr int NKD = D / 32;   // K = 32 steps over the channels
+    constexpr int HALF = NCT / 2; // state tiles updated per leaf
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    OpT *__restrict__ sh_M = reinterpret_cast<OpT *>(smem);
-    float *__restrict__ sh_U = reinterpret_cast<float *>(smem + LY::U_OFF);  // [16][CP]
-    float *__restrict__ sh_E = reinterpret_cast<float *>(smem + LY::E_OFF);  // [16][CP]
-    float *__restrict__ sh_S = reinterpret_cast<float *>(smem + LY::S_OFF);  // [D][16]
-    float *__restrict__ sh_L = reinterpret_cast<float *>(smem + LY::L_OFF);  // [16][16]
-    float *__restrict__ sh_G = reinterpret_cast<float *>(smem + LY::G_OFF);  // [D]
-
-    const int bh = blockIdx.x;
+    // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
+    // get ids that are equal mod 8, so they share an XCD and its L2.
+    const int id = blockIdx.x;
+    const int bh = (id >> 3) / NCT * 8 + (id & 7);
+    const int ct = (id >> 3) % NCT;
+    if (bh >= BH) return;
     const int b = bh / H, h = bh % H;
-    const int j0 = 16 * blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int og = (lane >> 4) * 4, c16 = lane & 15;
+    const int j0 = 16 * ct;
+    const int lane = threadIdx.x, x = lane & 15, g = lane >> 4;
     const size_t HD = size_t(H) * D;
-    const size_t sbase = size_t(bh) * D * D;             // state [b,h] offset
-    const size_t tb0 = size_t(b) * T * HD + size_t(h) * D + j0;  // token 0 of this tile
-    const int nleaf = nchunks * NB;
-    auto slot_of = [&](int ci) { return ws + (size_t(bh) * nchunks + ci) * SL::BYTES; };
-    auto kg_of = [&](int ci) { return reinterpret_cast<const OpT *>(slot_of(ci) + SL::KG_OFF); };
-    auto qg_of = [&](int ci) { return reinterpret_cast<const OpT *>(slot_of(ci) + SL::QG_OFF); };
-    auto p_of = [&](int ci) { return reinterpret_cast<const OpT *>(slot_of(ci) + SL::P_OFF); };
-    auto kbt_of = [&](int ci) { return reinterpret_cast<const OpT *>(slot_of(ci) + SL::KBT_OFF); };
+    const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
+    float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
+    const unsigned lo_st = unsigned(4 * g * D + x);  // state [channel 4g][column x]
 
-    // --- prefetch helpers (global -> registers) ---
-    // Every load is unconditional from a clamped, valid address; what lies past the end
-    // of the sequence or outside a triangle is zeroed where it is consumed, so no branch
-    // ever waits on a prefetch.
-    auto leaf_pos = [&](int lam, int &ci, int &rt) {  // only called when nleaf >= 1
-        const int lc = min(lam, nleaf - 1);
-        ci = lc / NB;
-        rt = lc % NB;
-    };
-    // Wave 0: (K*gamma) rows of leaf lam as the A operand, and its raw e, w, v.
-    auto load_leaf = [&](int lam, frag (&kg)[NKD], float (&ee)[4], float (&ww)[4], QT (&vv)[4]) {
-        int ci, rt;
-        leaf_pos(lam, ci, rt);
-        const OpT *src = kg_of(ci) + size_t(16 * rt + c16) * D + MM::kidx(lane, 0);
+    // State: S[c][i] = state[16c + 4g + i][j0 + x].
+    f32x4_t S[NCT];
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) kg[kk] = MM::load(src + kk * MM::KSTEP);
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const size_t idx = tb0 + size_t(min(ci * C + 16 * rt + og + i, T - 1)) * HD + c16;
-            ee[i] = e[idx];
-            ww[i] = w[idx];
-            vv[i] = v[idx];  // converted where it is used, so the load stays in flight
+        for (int i = 0; i < 4; ++i)
+            S[c][i] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+    if (nchunks == 0) {
+        if (south) {
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) south[size_t(16 * c + i) * D + lo_st] = S[c][i];
         }
-    };
-    // Readout owner: P row block of leaf lam (blocks past the diagonal are replaced by
-    // the diagonal block and zeroed at use) and (Qh*gamma) rows of leaf lam.
-    auto load_readout = [&](int lam, frag (&pp)[NKC], frag (&qg)[NKD]) {
-        int ci, rt;
-        leaf_pos(lam, ci, rt);
-        const OpT *P = p_of(ci);
-#pragma unroll
-        for (int ks = 0; ks < NKC; ++ks) {
-            const int s = ks * MM::KSTEP + MM::kidx(lane, 0);
-            pp[ks] = MM::load(P + size_t(SL::tri(rt, min(s >> 4, rt))) * 256 + c16 * 16 + (s & 15));
-        }
-        const OpT *src = qg_of(ci) + size_t(16 * rt + c16) * D + MM::kidx(lane, 0);
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) qg[kk] = MM::load(src + kk * MM::KSTEP);
-    };
-    // State followers: (K*beta)^T columns of leaf lam for the wave's channel tiles.
-    auto load_kb = [&](int lam, KbFrag<OpT> (&dst)[CT_PER]) {
-        int ci, rt;
-        leaf_pos(lam, ci, rt);
-        const OpT *K = kbt_of(ci);
-#pragma unroll
-        for (int x = 0; x < CT_PER; ++x) {
-            const int ct = min(wave - 1 + 3 * x, NCT - 1);
-            dst[x].load(K + size_t(16 * ct + c16) * C + 16 * rt, lane);
-        }
-    };
-
-    // State tiles: waves 1..3 own channel tiles ct = (wave-1) + 3x, fp32, kept on chip.
-    // The fp32 state lives in LDS (sh_S) between chunks; during a chunk the followers
-    // accumulate (K*beta)^T U for their channel tiles in Sacc.
-    f32x4_t Sacc[CT_PER];
-#pragma unroll
-    for (int x = 0; x < CT_PER; ++x) {
-        Sacc[x] = zero4();
-        const int ct = wave - 1 + 3 * x;
-        if (wave > 0 && ct < NCT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = 16 * ct + og + i;
-                sh_S[ch * 16 + c16] = s0 ? s0[sbase + size_t(ch) * D + j0 + c16] : 0.f;
-            }
-        }
+        return;
     }
 
-    // Double-buffered prefetch state: buffer A serves even leaves, B odd leaves (chunks
-    // hold an even number of leaves), so no in-flight register is ever copied.
-    frag kgA[NKD], kgB[NKD];      // wave 0
-    float eA[4], wA[4], eB[4], wB[4];
-    QT vA[4], vB[4];
-    frag pfP[NKC], pfQ[NKD];      // followers: next owned readout leaf
-    KbFrag<OpT> kbA[CT_PER], kbB[CT_PER];
-    // With no chunk (T == 0) nothing may be read: the workspace and the token tensors
-    // are empty, and the clamped indices below would be -1.
-    if (nchunks > 0) {
-        if (wave == 0) {
-            load_leaf(0, kgA, eA, wA, vA);
-            load_leaf(1, kgB, eB, wB, vB);
-        } else {
-            load_readout(wave - 1, pfP, pfQ);
-            load_kb(0, kbA);
-            load_kb(1, kbB);
+    // Per-lane byte offsets (each load adds one to a uniform base and offset).
+    constexpr unsigned OB = sizeof(OpT);
+    const unsigned lo_blk = unsigned(x * 16 + 4 * g) * OB;  // 16x16 block, row x, cols 4g..
+    const unsigned lo_kg = unsigned(x * D + 8 * g) * OB;    // [token x][8g..] of Kg / Qg
+    const unsigned lo_kbt = unsigned(x * C + 8 * g) * OB;   // [channel x][8g..] of KbT
+    const unsigned lo_md = unsigned(x * 16 * 4);
+    const unsigned lo_gc = unsigned(4 * g * 4);
+    const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
+    const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
+
+    const f4 unit = F::unit(x, g);
+    // Workspace slot of chunk ci (clamped to the last chunk: prefetches past the end
+    // read valid, unused data).
+    auto ws_rsrc = [&](int ci) {
+        return make_rsrc(ws + (size_t(bh) * nchunks + min(ci, nchunks - 1)) * SL::BYTES,
+                         unsigned(SL::BYTES));
+    };
+    // Token rows of chunk ci of one [B, T, H, *] tensor, columns j0.. of head h; rows at
+    // or past T lie outside the resource.
+    auto tok_rsrc = [&](const void *base, int ci, unsigned esize) {
+        const int t0 = ci * C;
+        // Uniform by construction; readfirstlane keeps the descriptor in SGPRs (a
+        // min/max pair may otherwise be selected as a vector med3).
+        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(C, T - t0)));
+        const size_t off = ((size_t(b) * T + size_t(min(t0, T))) * HD + size_t(h) * D + j0) * esize;
+        return make_rsrc(static_cast<const unsigned char *>(base) + off, unsigned(rows * HD * esize));
+    };
+
+    auto load_leaf = [&](int ci, int L, LeafIn<QT> &in) {
+        const unsigned so = unsigned(16 * L) * unsigned(HD);  // token offset in the chunk
+        in.ev = buf_load_f4(tok_rsrc(e, ci, 4), lo_f, so * 4u);
+        in.wv = buf_load_f4(tok_rsrc(w, ci, 4), lo_f, so * 4u);
+        in.vv = Row4<QT>::load(tok_rsrc(v, ci, sizeof(QT)), lo_q, so * unsigned(sizeof(QT)));
+        const rsrc_t r = ws_rsrc(ci);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            in.md[q4] = buf_load_f4(r, lo_md, unsigned(SL::MD_OFF + L * 1024 + 16 * q4));
+    };
+    auto load_kg = [&](int ci, int L, size_t OFF, f8 (&dst)[NKD]) {
+        const rsrc_t r = ws_rsrc(ci);
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk)
+            dst[kk] = F::bload8(r, lo_kg, unsigned(OFF + (16 * L * D + 32 * kk) * OB));
+    };
+    auto load_blk = [&](int ci, size_t OFF, int bt, int bs) {
+        return F::bload4(ws_rsrc(ci), lo_blk, unsigned(OFF + SL::tri(bt, bs) * 256 * OB));
+    };
+    auto load_kbt = [&](int ci, int pair, int c) {
+        return F::bload8(ws_rsrc(ci), lo_kbt, unsigned(SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
+    };
+
+    // Matrix-core operands of leaf L's window, loaded during leaf L - 1:
+    //   kg    (K*gamma) of leaf L + 1 (for its H), or of leaf 0 of the next chunk
+    //   qg    (Qh*gamma) of leaf L, and P_{L,l} (l < L), P_{L,L}: the readout of leaf L
+    //   mrow  M_{L+1,l} (l < L) and mnext = M_{L+1,L}: the right-hand side of leaf L + 1
+    //   kbt   (K*beta)^T of leaf pair (L-2, L-1) for half of the state tiles
+    struct Win {
+        f8 kg[NKD], qg[NKD], kbt[HALF];
+        f4 mrow[NB], prow[NB], pdiag, mnext;
+    };
+    auto load_win_a = [&](int ci, int L, Win &wn) {
+        if (L + 1 < NB) load_kg(ci, L + 1, SL::KG_OFF, wn.kg);
+        else load_kg(ci + 1, 0, SL::KG_OFF, wn.kg);
+        load_kg(ci, L, SL::QG_OFF, wn.qg);
+    };
+    auto load_win_b = [&](int ci, int L, Win &wn) {
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            if (L + 1 < NB) wn.mrow[l] = load_blk(ci, SL::M_OFF, L + 1, l);
+            wn.prow[l] = load_blk(ci, SL::P_OFF, L, l);
         }
-        if constexpr (LY::M_IN_LDS) copy_to_lds(slot_of(0) + SL::M_OFF, sh_M, SL::MG_BYTES, wave, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();
+        wn.pdiag = load_blk(ci, SL::P_OFF, L, L);
+        wn.mnext = load_blk(ci, SL::M_OFF, L + 1 < NB ? L + 1 : L, L);
+        if (L >= 2) {
+#pragma unroll
+            for (int c = 0; c < HALF; ++c) wn.kbt[c] = load_kbt(ci, (L - 2) / 2, c + (L & 1) * HALF);
+        }
+    };
+    auto load_gc = [&](int ci, f32x4_t (&gcv)[NCT]) {
+        const rsrc_t r = ws_rsrc(ci);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) gcv[c] = buf_load_f4(r, lo_gc, unsigned(SL::GC_OFF + 64 * c));
+    };
+
+    // Leaf inputs: in[L & 1] holds leaf L and is refilled with leaf L + 2 once leaf L is
+    // solved. Window operands: win[L & 1] (see Win).
+    LeafIn<QT> in[2];
+    load_leaf(0, 0, in[0]);
+    load_leaf(0, 1, in[1]);
+    Win win[2];
+    f8 kgH[NKD];  // (K*gamma) of leaf 0 of the current chunk
+    load_kg(0, 0, SL::KG_OFF, kgH);
+    load_win_a(0, 0, win[0]);
+    load_win_b(0, 0, win[0]);
+    f32x4_t gcv[NCT];  // gamma_C of the current chunk
+    load_gc(0, gcv);
+    f8 kbtLast[NCT];  // (K*beta)^T of the chunk's last leaf pair
 
     for (int ci = 0; ci < nchunks; ++ci) {
-        const unsigned char *slot = slot_of(ci);
-        const OpT *__restrict__ gM = reinterpret_cast<const OpT *>(slot + SL::M_OFF);
-        const float *__restrict__ gGC = reinterpret_cast<const float *>(slot + SL::GC_OFF);
-        // M block (bt, bs), element row `row`, column `col` (the LDS copy when it fits).
-        auto mptr = [&](int bt, int bs, int row, int col) -> const OpT * {
-            const size_t off = size_t(SL::tri(bt, bs)) * 256 + row * 16 + col;
-            if constexpr (LY::M_IN_LDS) return sh_M + off;
-            else return gM + off;
-        };
-
-        // S0 of this chunk as the B operand (contraction = channel, column = value column).
-        frag fS[NKD];
+        // Chunk start: S holds S0. Its operand copy serves the whole chunk; S itself
+        // becomes the accumulator of S_C, starting from Diag(gamma_C) S0.
+        f4 fS[NCT];
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) {
-            float x[VALS];
-#pragma unroll
-            for (int j = 0; j < VALS; ++j)
-                x[j] = sh_S[(kk * MM::KSTEP + MM::kidx(lane, j)) * 16 + c16];
-            fS[kk] = MM::pack(x);
+        for (int c = 0; c < NCT; ++c) {
+            fS[c] = F::pack(S[c]);
+            S[c] *= gcv[c];
         }
+        f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
 #pragma unroll
-        for (int x = 0; x < CT_PER; ++x) Sacc[x] = zero4();
-        // gamma_C of this chunk, kept apart from the copy window that the next chunk's
-        // copy overwrites (read only after the chunk's last barrier).
-        if (tid >= 64 && tid < 64 + D) {
-            if constexpr (LY::M_IN_LDS) {
-                sh_G[tid - 64] = reinterpret_cast<const float *>(smem + SL::GC_OFF)[tid - 64];
+        for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
+
+        f4 Uh[NB];
+        static_for<NB>([&](auto Lc) {
+            constexpr int L = decltype(Lc)::value;
+            constexpr bool more = L + 1 < NB;
+            Win &cw = win[L & 1];
+            Win &nw = win[(L + 1) & 1];
+            LeafIn<QT> &cin = in[L & 1];
+            const int ciN = more ? ci : ci + 1;  // chunk of leaf L + 1
+            constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
+
+            // ---- serial path: last M term and right-hand side ----
+            if constexpr (L > 0) acc = F::mma4(Uh[L - 1], win[(L - 1) & 1].mnext, acc);
+            // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
+            float ne[4];
+            float x0, x1, x2, x3;
+            {
+                float r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ne[i] = -cin.ev[i];
+                    r[i] = fmaf(ne[i], acc[i], cin.wv[i] * Row4<QT>::get(cin.vv, i));
+                }
+                x0 = r[0]; x1 = r[1]; x2 = r[2]; x3 = r[3];
+            }
+            // Coefficients of step s: -e_c * M_LL[t][s], formed just before the step.
+            auto step = [&](auto Sc) {
+                constexpr int St = decltype(Sc)::value;
+                const float m = cin.md[St / 4][St % 4];
+                subst_step<St>(x0, x1, x2, x3, ne[0] * m, ne[1] * m, ne[2] * m, ne[3] * m);
+            };
+
+            static_for<4>([&](auto Sc) { step(std::integral_constant<int, decltype(Sc)::value>{}); });
+
+            // ---- window, part 1: H of the next leaf and S0's share of this readout ----
+            f32x4_t accN = zero4(), ro = zero4();
+            if constexpr (more) {
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk)
+                    accN = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.kg[kk], accN);
             } else {
-                sh_G[tid - 64] = gGC[tid - 64];
-            }
-        }
-        f32x4_t accH = zero4();  // wave 0: (K*gamma)_L S0 of the current leaf
-        if (wave == 0) {
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) accH = MM::mma(kgA[kk], fS[kk], accH);
-        }
+                for (int kk = 0; kk < NKD; ++kk) kgH[kk] = cw.kg[kk];
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+                ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
+            load_win_a(ciN, LN, nw);
 
-        // One leaf. `kg/ee/ww/vv` hold leaf L and are refilled with leaf L + 2; `kgn` holds
-        // leaf L + 1; `kb` holds leaf L's (K*beta)^T and is refilled with leaf L + 2.
-        auto leaf_step = [&](int L, frag (&kg)[NKD], float (&ee)[4], float (&ww)[4],
-                             QT (&vv)[4], const frag (&kgn)[NKD], KbFrag<OpT> (&kb)[CT_PER]) {
-            const int lam = ci * NB + L;
-            if (wave == 0) {
-                // a4, serial chain. R_L = w*v - e * ((K*gamma)_L S0 + M_{L,<L} U_{<L}).
-                // Straight-line over the whole chunk width: steps past 16*L read a valid
-                // block and multiply a zeroed U fragment, so all LDS reads can be batched.
-                f32x4_t acc0 = accH, acc1 = zero4();
-                const int klen = 16 * L;
-#pragma unroll
-                for (int ks = 0; ks < NKC; ++ks) {
-                    const int s = ks * MM::KSTEP + MM::kidx(lane, 0);
-                    const bool in = s < klen;
-                    const int sc = in ? s : 0;
-                    float xa[VALS], xb[VALS];
-                    load_vec<VALS>(mptr(L, sc >> 4, c16, sc & 15), xa);
-                    load_vec<VALS>(sh_U + c16 * CP + sc, xb);
-#pragma unroll
-                    for (int j = 0; j < VALS; ++j) xb[j] = in ? xb[j] : 0.f;
-                    if (ks & 1) acc1 = MM::mma(MM::pack(xa), MM::pack(xb), acc1);
-                    else acc0 = MM::mma(MM::pack(xa), MM::pack(xb), acc0);
-                }
-                const f32x4_t acc = acc0 + acc1;
-                const int cell = c16 * CP + 16 * L + og;
-                float rr[4], er[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool in = ci * C + 16 * L + og + i < T;
-                    er[i] = in ? ee[i] : 0.f;
-                    rr[i] = (in ? ww[i] * to_f32(vv[i]) : 0.f) - er[i] * acc[i];
-                }
-                store4(sh_U + cell, f32x4_t{rr[0], rr[1], rr[2], rr[3]});
-                store4(sh_E + cell, f32x4_t{er[0], er[1], er[2], er[3]});
-                // Refill this buffer two leaves ahead and start the next leaf's
-                // (K*gamma) S0 on the matrix cores while this leaf is substituted.
-                load_leaf(lam + 2, kg, ee, ww, vv);
-                accH = zero4();
-                if (L + 1 < NB) {
-#pragma unroll
-                    for (int kk = 0; kk < NKD; ++kk) accH = MM::mma(kgn[kk], fS[kk], accH);
-                }
-                {   // leaf block of M in fp32, stored transposed: sh_L[s * 16 + t] = M_ts
-                    float x4[4];
-                    load_vec<4>(mptr(L, L, 0, 0) + lane * 4, x4);  // row lane/4, cols 4(lane%4)+i
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sh_L[(4 * (lane & 3) + i) * 16 + (lane >> 2)] = x4[i];
-                }
-                wave_lds_sync();
-                if (lane < 16) {
-                    // (I + Diag(e_j) M_LL) u_j = r_j by forward substitution, column j = lane.
-                    // Column s of the leaf is read as four broadcast 16-byte LDS loads, one
-                    // column ahead of its use.
-                    float rv[16], ev[16], p[16];
-                    const float4 *ru = reinterpret_cast<const float4 *>(sh_U + lane * CP + 16 * L);
-                    const float4 *re = reinterpret_cast<const float4 *>(sh_E + lane * CP + 16 * L);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const float4 a4 = ru[x], b4 = re[x];
-                        rv[4 * x] = a4.x; rv[4 * x + 1] = a4.y; rv[4 * x + 2] = a4.z; rv[4 * x + 3] = a4.w;
-                        ev[4 * x] = b4.x; ev[4 * x + 1] = b4.y; ev[4 * x + 2] = b4.z; ev[4 * x + 3] = b4.w;
-                    }
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) p[t] = 0.f;
-                    const float4 *lt = reinterpret_cast<const float4 *>(sh_L);
-                    float4 col[4], nxt[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) col[x] = lt[x];
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) {
-                        if (s + 1 < 16) {
-#pragma unroll
-                            for (int x = (s + 1) / 4; x < 4; ++x) nxt[x] = lt[(s + 1) * 4 + x];
-                        }
-                        const float u = rv[s] - ev[s] * p[s];
-                        rv[s] = u;
-                        const float *c = reinterpret_cast<const float *>(col);
-#pragma unroll
-                        for (int t = s + 1; t < 16; ++t) p[t] += c[t] * u;
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) col[x] = nxt[x];
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    float4 *wu = reinterpret_cast<float4 *>(sh_U + lane * CP + 16 * L);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        wu[x] = make_float4(rv[4 * x], rv[4 * x + 1], rv[4 * x + 2], rv[4 * x + 3]);
-                }
-            }
-            lds_barrier();
-            if (wave > 0) {
-                // a6: readout of leaf L by its owner: O_L = (Qh*gamma)_L S0 + P_{L,<=L} U.
-                if (wave - 1 == lam % 3) {
-                    f32x4_t acc0 = zero4(), acc1 = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < NKD; ++kk) acc0 = MM::mma(pfQ[kk], fS[kk], acc0);
-                    const int klen = 16 * (L + 1);
-#pragma unroll
-                    for (int ks = 0; ks < NKC; ++ks) {
-                        const int s = ks * MM::KSTEP + MM::kidx(lane, 0);
-                        const bool in = s < klen;
-                        float xb[VALS];
-                        load_vec<VALS>(sh_U + c16 * CP + (in ? s : 0), xb);
-#pragma unroll
-                        for (int j = 0; j < VALS; ++j) xb[j] = in ? xb[j] : 0.f;
-                        const frag fa = in ? pfP[ks] : MM::zero();
-                        if (ks & 1) acc1 = MM::mma(fa, MM::pack(xb), acc1);
-                        else acc0 = MM::mma(fa, MM::pack(xb), acc0);
-                    }
-                    const f32x4_t acc = acc0 + acc1;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = ci * C + 16 * L + og + i;
-                        if (t < T) elem<QT>::store(o, tb0 + size_t(t) * HD + c16, acc[i]);
-                    }
-                    load_readout(lam + 3, pfP, pfQ);
-                }
-                // a5, leaf L's share of the state carry: Sacc += (K*beta)_L^T U_L.
-                float ub[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ub[j] = sh_U[c16 * CP + 16 * L + MM::k16idx(lane, j)];
-#pragma unroll
-                for (int x = 0; x < CT_PER; ++x) {
-                    float ka[4];
-                    kb[x].get(ka);
-                    if (wave - 1 + 3 * x < NCT) Sacc[x] = MM::mma_k16(ka, ub, Sacc[x]);
-                }
-                load_kb(lam + 2, kb);
-            }
-        };
+            static_for<4>([&](auto Sc) { step(std::integral_constant<int, 4 + decltype(Sc)::value>{}); });
 
-        for (int L = 0; L < NB; L += 2) {
-            leaf_step(L, kgA, eA, wA, vA, kgB, kbA);
-            leaf_step(L + 1, kgB, eB, wB, vB, kgA, kbB);
-        }
-        // Wave 0 finished with this chunk's M before the last barrier of the loop: the
-        // next chunk's M (and gamma_C) streams into LDS while the state is finished.
-        if constexpr (LY::M_IN_LDS) {
-            if (ci + 1 < nchunks && wave > 0)
-                copy_to_lds(slot_of(ci + 1) + SL::M_OFF, sh_M, SL::MG_BYTES, wave - 1, lane,
-                            kWaves - 1);
-        }
-        // S_C = Diag(gamma_C) S0 + (K*beta)^T U.
-        if (wave > 0) {
+            // ---- window, part 2: earlier leaves' terms, state carry of a leaf pair ----
 #pragma unroll
-            for (int x = 0; x < CT_PER; ++x) {
-                const int ct = wave - 1 + 3 * x;
-                if (ct >= NCT) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ch = 16 * ct + og + i;
-                    sh_S[ch * 16 + c16] = sh_G[ch] * sh_S[ch * 16 + c16] + Sacc[x][i];
+            for (int l = 0; l < L; l += 2) {
+                if (l + 1 < L) {
+                    const f8 u2 = F::cat(Uh[l], Uh[l + 1]);
+                    if constexpr (more) accN = F::mma8(u2, F::cat(cw.mrow[l], cw.mrow[l + 1]), accN);
+                    ro = F::mma8(u2, F::cat(cw.prow[l], cw.prow[l + 1]), ro);
+                } else {
+                    if constexpr (more) accN = F::mma4(Uh[l], cw.mrow[l], accN);
+                    ro = F::mma4(Uh[l], cw.prow[l], ro);
                 }
             }
+            if constexpr (L >= 2) {
+                constexpr int p0 = (L - 2) & ~1;
+                const f8 u2 = F::cat(Uh[p0], Uh[p0 + 1]);
+#pragma unroll
+                for (int c = 0; c < HALF; ++c) {
+                    constexpr int off = (L & 1) * HALF;
+                    S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off]);
+                }
+            }
+            const f4 pdiag = cw.pdiag;
+            load_win_b(ciN, LN, nw);
+            if constexpr (!more) {
+                load_gc(ci + 1, gcv);
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
+            }
+
+            static_for<8>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
+
+            // ---- u -> U operand (transpose on the matrix cores), readout ----
+            Uh[L] = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
+            if constexpr (more) acc = accN;
+            ro = F::mma4(Uh[L], pdiag, ro);
+            load_leaf(L + 2 < NB ? ci : ci + 1, (L + 2) % NB, cin);  // leaf L + 2
+            Row4<QT>::store(tok_rsrc(o, ci, sizeof(QT)), lo_q,
+                            unsigned(16 * L) * unsigned(HD) * unsigned(sizeof(QT)), ro);
+        });
+        // Chunk end: the last leaf pair's share of the state.
+        {
+            const f8 u2 = F::cat(Uh[NB - 2], Uh[NB - 1]);
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c]);
         }
-        if constexpr (LY::M_IN_LDS) __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier();
     }
 
-    if (s_out && wave > 0) {
+    if (south) {
 #pragma unroll
-        for (int x = 0; x < CT_PER; ++x) {
-            const int ct = wave - 1 + 3 * x;
-            if (ct >= NCT) continue;
+        for (int c = 0; c < NCT; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = 16 * ct + og + i;
-                s_out[sbase + size_t(ch) * D + j0 + c16] = sh_S[ch * 16 + c16];
-            }
-        }
+            for (int i = 0; i < 4; ++i) south[size_t(16 * c + i) * D + lo_st] = S[c][i];
     }
 }
 
@@ -790,15 +852,11 @@ hipError_t scan_typed(const void *v, const float *e, const float *w, const float
                       float *s_out, int B, int T, int H, const void *workspace,
                       hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
-    using LY = ScanLds<OpT, D, C>;
-    auto kern = chunk_scan_kernel<QT, OpT, D, C>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(LY::BYTES));
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(B * H, D / 16), dim3(kThreads), LY::BYTES, stream,
-                       static_cast<const QT *>(v), e, w, s0, static_cast<QT *>(o), s_out,
-                       static_cast<const unsigned char *>(workspace), T, H, nchunks);
+    const int BH = B * H;
+    const int groups = (BH + 7) / 8;
+    hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C>), dim3(groups * 8 * (D / 16)), dim3(64), 0,
+                       stream, static_cast<const QT *>(v), e, w, s0, static_cast<QT *>(o), s_out,
+                       static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
     return hipGetLastError();
 }
 

@@ -59,20 +59,6 @@ template <> struct Mma<bf16_t> {
     }
     static __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
     static __device__ __forceinline__ bf16_t from_f32(float x) { return bf16_t{f32_to_bf16(x)}; }
-
-    // K = 16 step (one v_mfma_f32_16x16x16_bf16): element j of lane l sits at
-    // contraction index 4*(l/16) + j.
-    static __device__ __forceinline__ int k16idx(int lane, int j) { return (lane >> 4) * 4 + j; }
-    static __device__ __forceinline__ f32x4_t mma_k16(const float (&a)[4], const float (&b)[4],
-                                                      f32x4_t c) {
-        s16x4_t ua, ub;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ua[j] = static_cast<short>(f32_to_bf16(a[j]));
-            ub[j] = static_cast<short>(f32_to_bf16(b[j]));
-        }
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua, ub, c, 0, 0, 0);
-    }
 };
 
 template <> struct Mma<float> {
@@ -91,16 +77,6 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ void store(float *p, const float (&x)[1]) { *p = x[0]; }
     static __device__ __forceinline__ float to_f32(float x) { return x; }
     static __device__ __forceinline__ float from_f32(float x) { return x; }
-
-    // K = 16 step (four v_mfma_f32_16x16x4_f32): element j of lane l sits at
-    // contraction index 4*j + l/16.
-    static __device__ __forceinline__ int k16idx(int lane, int j) { return 4 * j + (lane >> 4); }
-    static __device__ __forceinline__ f32x4_t mma_k16(const float (&a)[4], const float (&b)[4],
-                                                      f32x4_t c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
-        return c;
-    }
 };
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
