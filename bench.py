@@ -42,6 +42,26 @@ def algorithmic(d, chunk, qkv_bytes=2):
     }
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` ('prepare' or 'scan') on the long-context workload,
+    from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/ (scaled by the copy
+    calibration recorded there). None when the summary is missing or was taken on a
+    different version of the kernel source."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "chunk_fwd_long_context_hbm_counters.md")
+    src = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc", "chunk_fwd.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(r"traffic sha=(\w+) prepare_bytes=(\d+) scan_bytes=(\d+)", text)
+    if not m or m.group(1) != sha:
+        return None
+    return float(m.group(2) if kernel == "prepare" else m.group(3))
+
+
 def to_dev(inp, dev):
     import numpy as np
     import torch
@@ -164,7 +184,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "main", "t4k", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "copy"], default="all",
+                    help="'copy' times a plain 1 GiB device copy: the known-size kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the chunk forward shards over (batch, head) with no "
@@ -176,6 +198,23 @@ def main():
     import workloads
     dev = torch.device("cuda", 0)
     torch.cuda.init()
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"metric": "device copy GB/s", "value": 2 * n / (ms * 1e-3) / 1e9,
+                          "unit": "GB/s", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "ms_per_launch": ms, "n_gpus": 1, "steps": args.steps}), flush=True)
+        return
 
     result = {"metric": "chunk-fwd tokens/s/layer @H16 d128 T4K/32K; %MFMA peak; "
                         "decode-step HBM GB/s",
@@ -201,7 +240,7 @@ def main():
         ach = alg[dom]["bytes"] * tok_heads / (dom_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "kernel": f"chunk_{dom}", "achieved": ach,
                               "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                              "frac": ach * 1e9 / HBM_PEAK, "traffic": None,
+                              "frac": ach * 1e9 / HBM_PEAK, "traffic": measured_traffic(dom),
                               "avg_ms": dom_ms}
         result["phases_ms"] = {"prepare": r["prepare_ms"], "scan": r["scan_ms"]}
         result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"]}
