@@ -541,15 +541,21 @@ template <typename QT> struct LeafIn {
     f32x4_t md[4];  // row t of the leaf's diagonal M block (fp32)
 };
 
-// The scan: one wavefront per (batch, head, 16 value columns), sequential over chunks
-// and over the 16-token leaves inside each chunk. Value columns are exactly independent,
-// so nothing is shared between wavefronts. For leaf L of a chunk with start state S0:
+// The scan: one workgroup of two wavefronts per (batch, head, 16 value columns),
+// sequential over chunks and over the 16-token leaves inside each chunk. Value columns
+// are exactly independent, so nothing is shared between workgroups. For leaf L of a
+// chunk with start state S0:
 //   acc = (K*gamma)_L S0 + sum_{l<L} M_{L,l} U_l          (matrix cores)
 //   (I + Diag(e) M_LL) u = w*v - e*acc                      (forward substitution)
-//   O_L = (Qh*gamma)_L S0 + sum_{l<=L} P_{L,l} U_l          (matrix cores)
 //   S_C = Diag(gamma_C) S0 + sum_L (K*beta)_L^T U_L         (matrix cores)
-// Only M_{L,L-1} U_{L-1}, the substitution and one transpose lie on the serial path; the
-// other products of each leaf are issued while the substitution runs.
+//   O_L = (Qh*gamma)_L S0 + sum_{l<=L} P_{L,l} U_l          (matrix cores)
+// The chain wavefront (wave 0) computes the first three; only M_{L,L-1} U_{L-1}, the
+// substitution and one transpose lie on its serial path, the other products of each
+// leaf are issued while the substitution runs. The readout wavefront (wave 1) computes
+// O one chunk behind, from the chunk's S0 and U that the chain leaves in LDS; the two
+// meet at one barrier per chunk. Splitting the operand streams between two wavefronts
+// doubles the loads each chain keeps in flight (vector-memory loads return in order, so
+// one wavefront's prefetch depth is bounded by what it can hold).
 //
 // Layouts: "row layout" (lane (t, g): token t, columns 4g..4g+3) is what the
 // substitution works in, and is the accumulator layout of products whose B operand rows
@@ -557,7 +563,7 @@ template <typename QT> struct LeafIn {
 // 4g..4g+3 of the leaf; an mma4 against the identity turns a row-layout u into it. The
 // state is kept as accumulators with rows = channels, columns = value columns.
 template <typename QT, typename OpT, int D, int C>
-__global__ __launch_bounds__(64) void chunk_scan_kernel(
+__global__ __launch_bounds__(128) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ s0, QT *__restrict__ o, float *__restrict__ s_out,
     const unsigned char *__restrict__ ws, int T, int H, int BH, int nchunks) {
@@ -570,6 +576,11 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(
     constexpr int NKD = D / 32;   // K = 32 steps over the channels
     constexpr int HALF = NCT / 2; // state tiles updated per leaf
 
+    // Chunk hand-over from the chain to the readout wavefront, double-buffered by chunk
+    // parity: S0 as operands and every leaf's U, both in the lane order of the operands.
+    __shared__ f4 sh_fS[2][NCT][64];
+    __shared__ f4 sh_U[2][NB][64];
+
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
     const int id = blockIdx.x;
@@ -578,25 +589,20 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(
     if (bh >= BH) return;
     const int b = bh / H, h = bh % H;
     const int j0 = 16 * ct;
-    const int lane = threadIdx.x, x = lane & 15, g = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
     const size_t HD = size_t(H) * D;
+    const unsigned lo_st = unsigned(4 * g * D + x);  // state [channel 4g][column x]
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
-    const unsigned lo_st = unsigned(4 * g * D + x);  // state [channel 4g][column x]
 
-    // State: S[c][i] = state[16c + 4g + i][j0 + x].
-    f32x4_t S[NCT];
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[c][i] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
     if (nchunks == 0) {
-        if (south) {
+        if (wave == 0 && south) {
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) south[size_t(16 * c + i) * D + lo_st] = S[c][i];
+                for (int i = 0; i < 4; ++i)
+                    south[size_t(16 * c + i) * D + lo_st] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
         }
         return;
     }
@@ -611,78 +617,123 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(
     const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
     const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
 
-    const f4 unit = F::unit(x, g);
-    // Workspace slot of chunk ci (clamped to the last chunk: prefetches past the end
-    // read valid, unused data).
-    auto ws_rsrc = [&](int ci) {
-        return make_rsrc(ws + (size_t(bh) * nchunks + min(ci, nchunks - 1)) * SL::BYTES,
-                         unsigned(SL::BYTES));
-    };
-    // Token rows of chunk ci of one [B, T, H, *] tensor, columns j0.. of head h; rows at
-    // or past T lie outside the resource.
-    auto tok_rsrc = [&](const void *base, int ci, unsigned esize) {
-        const int t0 = ci * C;
-        // Uniform by construction; readfirstlane keeps the descriptor in SGPRs (a
-        // min/max pair may otherwise be selected as a vector med3).
-        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(C, T - t0)));
-        const size_t off = ((size_t(b) * T + size_t(min(t0, T))) * HD + size_t(h) * D + j0) * esize;
-        return make_rsrc(static_cast<const unsigned char *>(base) + off, unsigned(rows * HD * esize));
-    };
+    // Descriptors (loop-invariant). The workspace one covers this head's chunk slots;
+    // a chunk index past the end is clamped to the last chunk (prefetches read valid,
+    // unused data). The token ones cover rows 0..T-1 of this head and column tile of one
+    // [B, T, H, *] tensor, from (b, 0, h, j0): the end of row T-1's tile lies inside, row
+    // T starts outside, so tokens at or past T read zero and their stores are dropped.
+    // The bounds check includes the scalar offset, which carries the token row.
+    const rsrc_t rws = make_rsrc(ws + size_t(bh) * nchunks * SL::BYTES, unsigned(size_t(nchunks) * SL::BYTES));
+    auto wsoff = [&](int ci, size_t off) { return unsigned(size_t(min(ci, nchunks - 1)) * SL::BYTES + off); };
+    const size_t tok0 = size_t(b) * T * HD + size_t(h) * D + j0;
+    const unsigned tok_elems = unsigned(size_t(T) * HD - size_t(h) * D - j0);
+    auto trow = [&](int t, unsigned es) { return unsigned(min(t, T)) * unsigned(HD) * es; };
 
-    auto load_leaf = [&](int ci, int L, LeafIn<QT> &in) {
-        const unsigned so = unsigned(16 * L) * unsigned(HD);  // token offset in the chunk
-        in.ev = buf_load_f4(tok_rsrc(e, ci, 4), lo_f, so * 4u);
-        in.wv = buf_load_f4(tok_rsrc(w, ci, 4), lo_f, so * 4u);
-        in.vv = Row4<QT>::load(tok_rsrc(v, ci, sizeof(QT)), lo_q, so * unsigned(sizeof(QT)));
-        const rsrc_t r = ws_rsrc(ci);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            in.md[q4] = buf_load_f4(r, lo_md, unsigned(SL::MD_OFF + L * 1024 + 16 * q4));
-    };
     auto load_kg = [&](int ci, int L, size_t OFF, f8 (&dst)[NKD]) {
-        const rsrc_t r = ws_rsrc(ci);
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk)
-            dst[kk] = F::bload8(r, lo_kg, unsigned(OFF + (16 * L * D + 32 * kk) * OB));
+            dst[kk] = F::bload8(rws, lo_kg, wsoff(ci, OFF + (16 * L * D + 32 * kk) * OB));
     };
     auto load_blk = [&](int ci, size_t OFF, int bt, int bs) {
-        return F::bload4(ws_rsrc(ci), lo_blk, unsigned(OFF + SL::tri(bt, bs) * 256 * OB));
-    };
-    auto load_kbt = [&](int ci, int pair, int c) {
-        return F::bload8(ws_rsrc(ci), lo_kbt, unsigned(SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
+        return F::bload4(rws, lo_blk, wsoff(ci, OFF + SL::tri(bt, bs) * 256 * OB));
     };
 
-    // Matrix-core operands of leaf L's window, loaded during leaf L - 1:
+    if (wave == 1) {
+        // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
+        const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * unsigned(sizeof(QT)));
+        // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L}, loaded one leaf ahead.
+        struct RWin {
+            f8 qg[NKD];
+            f4 prow[NB];
+        };
+        auto load_rwin = [&](int ci, int L, RWin &wn) {
+            load_kg(ci, L, SL::QG_OFF, wn.qg);
+#pragma unroll
+            for (int l = 0; l <= L; ++l) wn.prow[l] = load_blk(ci, SL::P_OFF, L, l);
+        };
+        RWin rw[2];
+        load_rwin(0, 0, rw[0]);
+        for (int p = 0; p <= nchunks; ++p) {
+            if (p >= 1) {
+                const int ci = p - 1;
+                const int buf = ci & 1;
+                f4 fS[NCT];
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) fS[c] = sh_fS[buf][c][lane];
+                f4 Uh[NB];
+                static_for<NB>([&](auto Lc) {
+                    constexpr int L = decltype(Lc)::value;
+                    RWin &cw = rw[L & 1];
+                    // The next leaf's operands (the next chunk's first leaf after the last).
+                    load_rwin(L + 1 < NB ? ci : ci + 1, (L + 1) % NB, rw[(L + 1) & 1]);
+                    Uh[L] = sh_U[buf][L][lane];
+                    f32x4_t ro = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < NKD; ++kk)
+                        ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
+#pragma unroll
+                    for (int l = 0; l <= L; l += 2) {
+                        if (l + 1 <= L) ro = F::mma8(F::cat(Uh[l], Uh[l + 1]), F::cat(cw.prow[l], cw.prow[l + 1]), ro);
+                        else ro = F::mma4(Uh[l], cw.prow[l], ro);
+                    }
+                    Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
+                });
+            }
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---------------- chain wavefront ----------------
+    // State: S[c][i] = state[16c + 4g + i][j0 + x].
+    f32x4_t S[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[c][i] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+
+    const f4 unit = F::unit(x, g);
+    const rsrc_t re = make_rsrc(e + tok0, tok_elems * 4u);
+    const rsrc_t rwt = make_rsrc(w + tok0, tok_elems * 4u);
+    const rsrc_t rv = make_rsrc(v + tok0, tok_elems * unsigned(sizeof(QT)));
+
+    auto load_leaf = [&](int ci, int L, LeafIn<QT> &in) {
+        const unsigned so = trow(ci * C + 16 * L, 4u);
+        in.ev = buf_load_f4(re, lo_f, so);
+        in.wv = buf_load_f4(rwt, lo_f, so);
+        in.vv = Row4<QT>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            in.md[q4] = buf_load_f4(rws, lo_md, wsoff(ci, SL::MD_OFF + L * 1024 + 16 * q4));
+    };
+    auto load_kbt = [&](int ci, int pair, int c) {
+        return F::bload8(rws, lo_kbt, wsoff(ci, SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
+    };
+    auto load_gc = [&](int ci, f32x4_t (&gcv)[NCT]) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) gcv[c] = buf_load_f4(rws, lo_gc, wsoff(ci, SL::GC_OFF + 64 * c));
+    };
+
+    // Matrix-core operands of leaf L's window, loaded at the start of leaf L - 1:
     //   kg    (K*gamma) of leaf L + 1 (for its H), or of leaf 0 of the next chunk
-    //   qg    (Qh*gamma) of leaf L, and P_{L,l} (l < L), P_{L,L}: the readout of leaf L
     //   mrow  M_{L+1,l} (l < L) and mnext = M_{L+1,L}: the right-hand side of leaf L + 1
     //   kbt   (K*beta)^T of leaf pair (L-2, L-1) for half of the state tiles
     struct Win {
-        f8 kg[NKD], qg[NKD], kbt[HALF];
-        f4 mrow[NB], prow[NB], pdiag, mnext;
+        f8 kg[NKD], kbt[HALF];
+        f4 mrow[NB], mnext;
     };
-    auto load_win_a = [&](int ci, int L, Win &wn) {
+    auto load_win = [&](int ci, int L, Win &wn) {
         if (L + 1 < NB) load_kg(ci, L + 1, SL::KG_OFF, wn.kg);
         else load_kg(ci + 1, 0, SL::KG_OFF, wn.kg);
-        load_kg(ci, L, SL::QG_OFF, wn.qg);
-    };
-    auto load_win_b = [&](int ci, int L, Win &wn) {
 #pragma unroll
-        for (int l = 0; l < L; ++l) {
+        for (int l = 0; l < L; ++l)
             if (L + 1 < NB) wn.mrow[l] = load_blk(ci, SL::M_OFF, L + 1, l);
-            wn.prow[l] = load_blk(ci, SL::P_OFF, L, l);
-        }
-        wn.pdiag = load_blk(ci, SL::P_OFF, L, L);
         wn.mnext = load_blk(ci, SL::M_OFF, L + 1 < NB ? L + 1 : L, L);
         if (L >= 2) {
 #pragma unroll
             for (int c = 0; c < HALF; ++c) wn.kbt[c] = load_kbt(ci, (L - 2) / 2, c + (L & 1) * HALF);
         }
-    };
-    auto load_gc = [&](int ci, f32x4_t (&gcv)[NCT]) {
-        const rsrc_t r = ws_rsrc(ci);
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) gcv[c] = buf_load_f4(r, lo_gc, unsigned(SL::GC_OFF + 64 * c));
     };
 
     // Leaf inputs: in[L & 1] holds leaf L and is refilled with leaf L + 2 once leaf L is
@@ -693,120 +744,115 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(
     Win win[2];
     f8 kgH[NKD];  // (K*gamma) of leaf 0 of the current chunk
     load_kg(0, 0, SL::KG_OFF, kgH);
-    load_win_a(0, 0, win[0]);
-    load_win_b(0, 0, win[0]);
+    load_win(0, 0, win[0]);
     f32x4_t gcv[NCT];  // gamma_C of the current chunk
     load_gc(0, gcv);
     f8 kbtLast[NCT];  // (K*beta)^T of the chunk's last leaf pair
 
-    for (int ci = 0; ci < nchunks; ++ci) {
-        // Chunk start: S holds S0. Its operand copy serves the whole chunk; S itself
-        // becomes the accumulator of S_C, starting from Diag(gamma_C) S0.
-        f4 fS[NCT];
+    for (int p = 0; p <= nchunks; ++p) {
+        if (p < nchunks) {
+            const int ci = p;
+            const int buf = ci & 1;
+            // Chunk start: S holds S0. Its operand copy serves the whole chunk (and the
+            // readout, through LDS); S itself becomes the accumulator of S_C, starting
+            // from Diag(gamma_C) S0.
+            f4 fS[NCT];
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-            fS[c] = F::pack(S[c]);
-            S[c] *= gcv[c];
-        }
-        f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
+            for (int c = 0; c < NCT; ++c) {
+                fS[c] = F::pack(S[c]);
+                sh_fS[buf][c][lane] = fS[c];
+                S[c] *= gcv[c];
+            }
+            f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
+            for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
 
-        f4 Uh[NB];
-        static_for<NB>([&](auto Lc) {
-            constexpr int L = decltype(Lc)::value;
-            constexpr bool more = L + 1 < NB;
-            Win &cw = win[L & 1];
-            Win &nw = win[(L + 1) & 1];
-            LeafIn<QT> &cin = in[L & 1];
-            const int ciN = more ? ci : ci + 1;  // chunk of leaf L + 1
-            constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
+            f4 Uh[NB];
+            static_for<NB>([&](auto Lc) {
+                constexpr int L = decltype(Lc)::value;
+                constexpr bool more = L + 1 < NB;
+                Win &cw = win[L & 1];
+                Win &nw = win[(L + 1) & 1];
+                LeafIn<QT> &cin = in[L & 1];
+                const int ciN = more ? ci : ci + 1;  // chunk of leaf L + 1
+                constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
 
-            // ---- serial path: last M term and right-hand side ----
-            if constexpr (L > 0) acc = F::mma4(Uh[L - 1], win[(L - 1) & 1].mnext, acc);
-            // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
-            float ne[4];
-            float x0, x1, x2, x3;
-            {
-                float r[4];
+                // ---- serial path: last M term and right-hand side ----
+                if constexpr (L > 0) acc = F::mma4(Uh[L - 1], win[(L - 1) & 1].mnext, acc);
+                load_win(ciN, LN, nw);
+                // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
+                float ne[4];
+                float x0, x1, x2, x3;
+                {
+                    float r[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ne[i] = -cin.ev[i];
-                    r[i] = fmaf(ne[i], acc[i], cin.wv[i] * Row4<QT>::get(cin.vv, i));
+                    for (int i = 0; i < 4; ++i) {
+                        ne[i] = -cin.ev[i];
+                        r[i] = fmaf(ne[i], acc[i], cin.wv[i] * Row4<QT>::get(cin.vv, i));
+                    }
+                    x0 = r[0]; x1 = r[1]; x2 = r[2]; x3 = r[3];
                 }
-                x0 = r[0]; x1 = r[1]; x2 = r[2]; x3 = r[3];
-            }
-            // Coefficients of step s: -e_c * M_LL[t][s], formed just before the step.
-            auto step = [&](auto Sc) {
-                constexpr int St = decltype(Sc)::value;
-                const float m = cin.md[St / 4][St % 4];
-                subst_step<St>(x0, x1, x2, x3, ne[0] * m, ne[1] * m, ne[2] * m, ne[3] * m);
-            };
+                // Coefficients of step s: -e_c * M_LL[t][s], formed just before the step.
+                auto step = [&](auto Sc) {
+                    constexpr int St = decltype(Sc)::value;
+                    const float m = cin.md[St / 4][St % 4];
+                    subst_step<St>(x0, x1, x2, x3, ne[0] * m, ne[1] * m, ne[2] * m, ne[3] * m);
+                };
 
-            static_for<4>([&](auto Sc) { step(std::integral_constant<int, decltype(Sc)::value>{}); });
+                static_for<4>([&](auto Sc) { step(std::integral_constant<int, decltype(Sc)::value>{}); });
 
-            // ---- window, part 1: H of the next leaf and S0's share of this readout ----
-            f32x4_t accN = zero4(), ro = zero4();
-            if constexpr (more) {
+                // ---- window, part 1: H of the next leaf ----
+                f32x4_t accN = zero4();
+                if constexpr (more) {
 #pragma unroll
-                for (int kk = 0; kk < NKD; ++kk)
-                    accN = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.kg[kk], accN);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) kgH[kk] = cw.kg[kk];
-            }
-#pragma unroll
-            for (int kk = 0; kk < NKD; ++kk)
-                ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
-            load_win_a(ciN, LN, nw);
-
-            static_for<4>([&](auto Sc) { step(std::integral_constant<int, 4 + decltype(Sc)::value>{}); });
-
-            // ---- window, part 2: earlier leaves' terms, state carry of a leaf pair ----
-#pragma unroll
-            for (int l = 0; l < L; l += 2) {
-                if (l + 1 < L) {
-                    const f8 u2 = F::cat(Uh[l], Uh[l + 1]);
-                    if constexpr (more) accN = F::mma8(u2, F::cat(cw.mrow[l], cw.mrow[l + 1]), accN);
-                    ro = F::mma8(u2, F::cat(cw.prow[l], cw.prow[l + 1]), ro);
+                    for (int kk = 0; kk < NKD; ++kk)
+                        accN = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.kg[kk], accN);
                 } else {
-                    if constexpr (more) accN = F::mma4(Uh[l], cw.mrow[l], accN);
-                    ro = F::mma4(Uh[l], cw.prow[l], ro);
+#pragma unroll
+                    for (int kk = 0; kk < NKD; ++kk) kgH[kk] = cw.kg[kk];
                 }
-            }
-            if constexpr (L >= 2) {
-                constexpr int p0 = (L - 2) & ~1;
-                const f8 u2 = F::cat(Uh[p0], Uh[p0 + 1]);
+
+                static_for<4>([&](auto Sc) { step(std::integral_constant<int, 4 + decltype(Sc)::value>{}); });
+
+                // ---- window, part 2: earlier leaves' terms, state carry of a leaf pair ----
+                if constexpr (more) {
 #pragma unroll
-                for (int c = 0; c < HALF; ++c) {
-                    constexpr int off = (L & 1) * HALF;
-                    S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off]);
+                    for (int l = 0; l < L; l += 2) {
+                        if (l + 1 < L) accN = F::mma8(F::cat(Uh[l], Uh[l + 1]), F::cat(cw.mrow[l], cw.mrow[l + 1]), accN);
+                        else accN = F::mma4(Uh[l], cw.mrow[l], accN);
+                    }
                 }
-            }
-            const f4 pdiag = cw.pdiag;
-            load_win_b(ciN, LN, nw);
-            if constexpr (!more) {
-                load_gc(ci + 1, gcv);
+                if constexpr (L >= 2) {
+                    constexpr int p0 = (L - 2) & ~1;
+                    const f8 u2 = F::cat(Uh[p0], Uh[p0 + 1]);
 #pragma unroll
-                for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
-            }
-
-            static_for<8>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
-
-            // ---- u -> U operand (transpose on the matrix cores), readout ----
-            Uh[L] = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
-            if constexpr (more) acc = accN;
-            ro = F::mma4(Uh[L], pdiag, ro);
-            load_leaf(L + 2 < NB ? ci : ci + 1, (L + 2) % NB, cin);  // leaf L + 2
-            Row4<QT>::store(tok_rsrc(o, ci, sizeof(QT)), lo_q,
-                            unsigned(16 * L) * unsigned(HD) * unsigned(sizeof(QT)), ro);
-        });
-        // Chunk end: the last leaf pair's share of the state.
-        {
-            const f8 u2 = F::cat(Uh[NB - 2], Uh[NB - 1]);
+                    for (int c = 0; c < HALF; ++c) {
+                        constexpr int off = (L & 1) * HALF;
+                        S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off]);
+                    }
+                }
+                if constexpr (!more) {
+                    load_gc(ci + 1, gcv);
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c]);
+                    for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
+                }
+
+                static_for<8>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
+
+                // ---- u -> U operand (transpose on the matrix cores), hand-over ----
+                Uh[L] = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
+                sh_U[buf][L][lane] = Uh[L];
+                if constexpr (more) acc = accN;
+                load_leaf(L + 2 < NB ? ci : ci + 1, (L + 2) % NB, cin);  // leaf L + 2
+            });
+            // Chunk end: the last leaf pair's share of the state.
+            {
+                const f8 u2 = F::cat(Uh[NB - 2], Uh[NB - 1]);
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c]);
+            }
         }
+        lds_barrier();
     }
 
     if (south) {
@@ -854,7 +900,7 @@ hipError_t scan_typed(const void *v, const float *e, const float *w, const float
     const int nchunks = (T + C - 1) / C;
     const int BH = B * H;
     const int groups = (BH + 7) / 8;
-    hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C>), dim3(groups * 8 * (D / 16)), dim3(64), 0,
+    hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C>), dim3(groups * 8 * (D / 16)), dim3(128), 0,
                        stream, static_cast<const QT *>(v), e, w, s0, static_cast<QT *>(o), s_out,
                        static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
     return hipGetLastError();
