@@ -67,8 +67,8 @@ template <typename OpT, int D, int C> struct Slot {
     static constexpr int NTRI = NB * (NB + 1) / 2;
     static constexpr size_t M_BYTES = size_t(NTRI) * 256 * sizeof(OpT);
     static constexpr size_t M_OFF = 0;
-    static constexpr size_t GC_OFF = align256(M_OFF + M_BYTES);       // gamma_C, D floats
-    static constexpr size_t P_OFF = align256(GC_OFF + size_t(D) * 4);
+    static constexpr size_t PP_OFF = align256(M_OFF + M_BYTES);       // pair decays [NB/2][D]
+    static constexpr size_t P_OFF = align256(PP_OFF + size_t(NB / 2) * D * 4);
     static constexpr size_t KG_OFF = align256(P_OFF + M_BYTES);
     static constexpr size_t QG_OFF = align256(KG_OFF + size_t(C) * D * sizeof(OpT));
     static constexpr size_t KBT_OFF = align256(QG_OFF + size_t(C) * D * sizeof(OpT));
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
     OpT *__restrict__ gKg = reinterpret_cast<OpT *>(slot + SL::KG_OFF);
     OpT *__restrict__ gQg = reinterpret_cast<OpT *>(slot + SL::QG_OFF);
     OpT *__restrict__ gKbT = reinterpret_cast<OpT *>(slot + SL::KBT_OFF);
-    float *__restrict__ gGC = reinterpret_cast<float *>(slot + SL::GC_OFF);
+    float *__restrict__ gPP = reinterpret_cast<float *>(slot + SL::PP_OFF);
     float *__restrict__ gMD = reinterpret_cast<float *>(slot + SL::MD_OFF);
 
     const int t0 = ci * C;
@@ -182,10 +182,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             kv[t] = in ? kv[t] : 0.f;
             qv[t] = in ? rc * gv[t] * qv[t] : 0.f;
         }
-        float G = 1.f, Gs = 1.f;
+        float G = 1.f;
         for (int x = 0; x < bb; ++x) G *= sh_pi[x * D + ch];
-        for (int x = bb + 1; x < NB; ++x) Gs *= sh_pi[x * D + ch];
-        if (bb == 0) gGC[ch] = sh_pi[ch] * Gs;  // gamma_C
+        // (K*beta)^T is pivoted at the end of the block pair: the second block's product
+        // scales the first block's keys. The pair's whole product is stored for the scan.
+        const float Gp = (bb & 1) ? 1.f : sh_pi[(bb + 1) * D + ch];
+        if (bb & 1) gPP[(bb >> 1) * D + ch] = sh_pi[(bb - 1) * D + ch] * sh_pi[bb * D + ch];
         float pi = 1.f;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
         float sig = 1.f;
 #pragma unroll
         for (int t = 15; t >= 0; --t) {
-            kbt[t] = kv[t] * (sig * Gs);
+            kbt[t] = kv[t] * (sig * Gp);
             sh_bb[(16 * bb + t) * DB + ch] = MM::from_f32(kv[t] * sig);
             sig *= av[t];
         }
@@ -580,6 +582,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     // parity: S0 as operands and every leaf's U, both in the lane order of the operands.
     __shared__ f4 sh_fS[2][NCT][64];
     __shared__ f4 sh_U[2][NB][64];
+    // Decay of every leaf pair of a chunk, per channel, double-buffered by chunk parity;
+    // staged by the readout wavefront one chunk ahead of the chain.
+    constexpr int NP = NB / 2;
+    __shared__ __align__(16) float sh_pp[2][NP][D];
 
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
@@ -613,7 +619,6 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     const unsigned lo_kg = unsigned(x * D + 8 * g) * OB;    // [token x][8g..] of Kg / Qg
     const unsigned lo_kbt = unsigned(x * C + 8 * g) * OB;   // [channel x][8g..] of KbT
     const unsigned lo_md = unsigned(x * 16 * 4);
-    const unsigned lo_gc = unsigned(4 * g * 4);
     const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
     const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
 
@@ -653,7 +658,28 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         };
         RWin rw[2];
         load_rwin(0, 0, rw[0]);
+        // Pair decays of chunk ci into sh_pp[ci & 1] (NP * D floats, four per lane and
+        // step).
+        constexpr int PP4 = NP * D / 4;
+        constexpr int PPN = (PP4 + 63) / 64;
+        auto load_ppt = [&](int ci, f32x4_t (&dst)[PPN]) {
+#pragma unroll
+            for (int n = 0; n < PPN; ++n)
+                if (n * 64 + lane < PP4)
+                    dst[n] = buf_load_f4(rws, unsigned(16 * (n * 64 + lane)), wsoff(ci, SL::PP_OFF));
+        };
+        auto put_ppt = [&](int ci, const f32x4_t (&src)[PPN]) {
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(&sh_pp[ci & 1][0][0]);
+#pragma unroll
+            for (int n = 0; n < PPN; ++n)
+                if (n * 64 + lane < PP4) dst[n * 64 + lane] = src[n];
+        };
+        f32x4_t ppt[PPN];
+        load_ppt(0, ppt);
+        put_ppt(0, ppt);
+        lds_barrier();
         for (int p = 0; p <= nchunks; ++p) {
+            if (p + 1 < nchunks) load_ppt(p + 1, ppt);
             if (p >= 1) {
                 const int ci = p - 1;
                 const int buf = ci & 1;
@@ -679,6 +705,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
             }
+            if (p + 1 < nchunks) put_ppt(p + 1, ppt);
             lds_barrier();
         }
         return;
@@ -710,15 +737,16 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     auto load_kbt = [&](int ci, int pair, int c) {
         return F::bload8(rws, lo_kbt, wsoff(ci, SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
     };
-    auto load_gc = [&](int ci, f32x4_t (&gcv)[NCT]) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) gcv[c] = buf_load_f4(rws, lo_gc, wsoff(ci, SL::GC_OFF + 64 * c));
+    // Decay over leaf pair `pair` of chunk ci of the rows of state tile c.
+    auto lds_pp = [&](int ci, int pair, int c) {
+        return *reinterpret_cast<const f32x4_t *>(&sh_pp[ci & 1][pair][16 * c + 4 * g]);
     };
 
     // Matrix-core operands of leaf L's window, loaded at the start of leaf L - 1:
     //   kg    (K*gamma) of leaf L + 1 (for its H), or of leaf 0 of the next chunk
     //   mrow  M_{L+1,l} (l < L) and mnext = M_{L+1,L}: the right-hand side of leaf L + 1
-    //   kbt   (K*beta)^T of leaf pair (L-2, L-1) for half of the state tiles
+    //   kbt   (K*beta)^T of leaf pair (L-2, L-1) for half of the state tiles, pivoted
+    //         at the pair's end
     struct Win {
         f8 kg[NKD], kbt[HALF];
         f4 mrow[NB], mnext;
@@ -745,23 +773,23 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     f8 kgH[NKD];  // (K*gamma) of leaf 0 of the current chunk
     load_kg(0, 0, SL::KG_OFF, kgH);
     load_win(0, 0, win[0]);
-    f32x4_t gcv[NCT];  // gamma_C of the current chunk
-    load_gc(0, gcv);
     f8 kbtLast[NCT];  // (K*beta)^T of the chunk's last leaf pair
 
+    lds_barrier();  // the first chunk's pair decays are in LDS
     for (int p = 0; p <= nchunks; ++p) {
         if (p < nchunks) {
             const int ci = p;
             const int buf = ci & 1;
             // Chunk start: S holds S0. Its operand copy serves the whole chunk (and the
-            // readout, through LDS); S itself becomes the accumulator of S_C, starting
-            // from Diag(gamma_C) S0.
+            // readout, through LDS); S itself becomes the accumulator of S_C, carried in
+            // Horner form: per leaf pair, S <- Diag(pair decay) S + (K*beta')^T U, with
+            // beta' pivoted at the pair's end, which ends at Diag(gamma_C) S0 +
+            // (K*beta)^T U.
             f4 fS[NCT];
 #pragma unroll
             for (int c = 0; c < NCT; ++c) {
                 fS[c] = F::pack(S[c]);
                 sh_fS[buf][c][lane] = fS[c];
-                S[c] *= gcv[c];
             }
             f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
 #pragma unroll
@@ -828,11 +856,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 #pragma unroll
                     for (int c = 0; c < HALF; ++c) {
                         constexpr int off = (L & 1) * HALF;
-                        S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off]);
+                        S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off] * lds_pp(ci, p0 / 2, c + off));
                     }
                 }
                 if constexpr (!more) {
-                    load_gc(ci + 1, gcv);
 #pragma unroll
                     for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
                 }
@@ -849,7 +876,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
             {
                 const f8 u2 = F::cat(Uh[NB - 2], Uh[NB - 1]);
 #pragma unroll
-                for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c]);
+                for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c] * lds_pp(ci, NP - 1, c));
             }
         }
         lds_barrier();

@@ -122,10 +122,15 @@ __device__ __forceinline__ void store4(bf16_t *p, f32x4_t v) {
 // Workgroup barrier that orders LDS only. Waves of one workgroup never exchange data
 // through global memory inside these kernels, so global loads issued as prefetches
 // stay in flight across the barrier (a full __syncthreads() would wait for them).
+// The scheduling barriers keep every instruction on its side of the barrier: without
+// them the machine scheduler, which sees one region across many unrolled phases, sinks
+// prefetch loads down to their uses to save registers and so undoes the prefetch.
 __device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Order this wave's LDS writes before its following LDS reads from other lanes.
