@@ -535,6 +535,374 @@ template <> struct Row4<float> {
     }
 };
 
+// ---------------------------------------------------------------------------------
+// Phase P for bf16 operands: the same outputs in one streaming pass over the chunk.
+// ---------------------------------------------------------------------------------
+// Row scans over the 16 tokens of a block run on the 16-lane DPP rows. dpp_or_one<CTRL>
+// moves x across lanes with DPP control CTRL; lanes whose source lies outside their row
+// read 1 (the identity of the products).
+template <int CTRL> __device__ __forceinline__ float dpp_or_one(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f),
+                                                                 __builtin_bit_cast(int, x), CTRL,
+                                                                 0xf, 0xf, false));
+}
+constexpr int kRowShl1 = 0x101, kRowShl4 = 0x104, kRowShr1 = 0x111, kRowShr4 = 0x114;
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int row_bcast(int n) { return 0x150 + n; }  // lane n of each row to the whole row
+
+// LDS of the bf16 prepare kernel (bytes).
+template <int D, int C> struct Prep2Lds {
+    static constexpr int NB = C / 16, NG = D / 32;
+    static constexpr size_t BB_OFF = 0;                                  // [C][D] K*sigma
+    static constexpr size_t A_OFF = BB_OFF + size_t(C) * D * 2;          // [2][2][16][D] K*pi, Qh*pi
+    static constexpr size_t KT_OFF = A_OFF + size_t(2) * 2 * 16 * D * 2; // [D][32] (K*beta')^T
+    static constexpr size_t PI_OFF = KT_OFF + size_t(D) * 32 * 2;        // [NB][D] block decays
+    static constexpr size_t FT_OFF = PI_OFF + size_t(NB) * D * 4;        // [NB][D] decay to the pair
+    static constexpr size_t DG_OFF = FT_OFF + size_t(NB) * D * 4;        // [2][NG][2][64] partials
+    static constexpr size_t BYTES = DG_OFF + size_t(2) * NG * 2 * 64 * 16;
+};
+
+// Operand rows in LDS ([row][D] bf16) are stored as D/8 chunks of 16 bytes, chunk c of
+// row r at chunk position c ^ (r mod D/8): a 16-lane read of one chunk column over 16
+// rows then touches 16 different bank groups.
+template <int D> __device__ __forceinline__ int swz(int row, int chunk) {
+    return row * D + 8 * (chunk ^ (row & (D / 8 - 1)));
+}
+
+// One workgroup of 4D threads (8 wavefronts at D = 128) per (chunk, head, batch), walking
+// the chunk one leaf pair (two 16-token blocks) at a time with the next pair's inputs in
+// flight. Wavefront w = h * NG + cg holds block h of the pair and channel group cg (32
+// channels); lane 16 G + t holds token t of the block and channels 32cg + 4G + {0..3}
+// and 32cg + 16 + 4G + {0..3} -- value j is channel 32cg + 4G + (j & 3) + 16 (j >> 2) --
+// which are the operand positions 32cg + 8G .. + 7, so a thread's share of a Kg or Qg row
+// is one 16-byte vector, and its eight values are its lane's share of a K = 32 matrix-core
+// operand over the group's channels.
+//
+// Per pair p (blocks 2p, 2p + 1), for each channel:
+//   pi_t   = prod of a from the block start to t (inclusive)     (row prefix scan)
+//   sigma_s = prod of a after s to the block end                (row suffix scan)
+//   Kg = k * G_b * pi, Qg = qh * G_b * pi with G_b the product of the earlier blocks;
+//   (K*beta')^T = k * sigma * (decay of block 2p + 1 for block 2p), pivoted at the pair end;
+//   the pair's decay; the diagonal blocks of M and P from the recursive pivots inside the
+//   block (the scan's nested levels give every level's running products); the
+//   off-diagonal blocks (bt, bs) against the K*sigma of all earlier blocks kept in LDS,
+//   scaled by the decay of the whole blocks in between.
+template <int D, int C>
+__global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const float *__restrict__ a,
+    const float *__restrict__ g, const float *__restrict__ r, unsigned char *__restrict__ ws,
+    int T, int H, int nchunks) {
+    using SL = Slot<bf16_t, D, C>;
+    using LY = Prep2Lds<D, C>;
+    using F = Frag<bf16_t>;
+    using f4 = F::f4;
+    using f8 = F::f8;
+    constexpr int NB = C / 16, NP = NB / 2, NG = D / 32, NW = 2 * NG, NT = 64 * NW;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    bf16_t *sh_bb = reinterpret_cast<bf16_t *>(smem + LY::BB_OFF);
+    bf16_t *sh_A = reinterpret_cast<bf16_t *>(smem + LY::A_OFF);
+    bf16_t *sh_kt = reinterpret_cast<bf16_t *>(smem + LY::KT_OFF);
+    float *sh_pi = reinterpret_cast<float *>(smem + LY::PI_OFF);
+    float *sh_ft = reinterpret_cast<float *>(smem + LY::FT_OFF);
+    f32x4_t *sh_dg = reinterpret_cast<f32x4_t *>(smem + LY::DG_OFF);
+
+    const int ci = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int hb = wave / NG, cg = wave % NG;  // block of the pair, channel group
+    const int G = lane >> 4, t = lane & 15;
+    const int pos0 = 32 * cg + 8 * G;          // operand positions of the thread
+    const int chl = 32 * cg + 4 * G;           // channels chl + {0..3}, chl + 16 + {0..3}
+
+    unsigned char *slot = ws + ((size_t(b) * H + hh) * nchunks + ci) * SL::BYTES;
+    bf16_t *gM = reinterpret_cast<bf16_t *>(slot + SL::M_OFF);
+    bf16_t *gP = reinterpret_cast<bf16_t *>(slot + SL::P_OFF);
+    bf16_t *gKg = reinterpret_cast<bf16_t *>(slot + SL::KG_OFF);
+    bf16_t *gQg = reinterpret_cast<bf16_t *>(slot + SL::QG_OFF);
+    bf16_t *gKbT = reinterpret_cast<bf16_t *>(slot + SL::KBT_OFF);
+    float *gPP = reinterpret_cast<float *>(slot + SL::PP_OFF);
+    float *gMD = reinterpret_cast<float *>(slot + SL::MD_OFF);
+
+    // Inputs through buffer resources covering tokens t0 .. t0 + nreal - 1 of this head:
+    // padded tokens read zero (k = q = 0); their decay is set to 1 below.
+    const int t0 = ci * C;
+    const int nreal = min(C, T - t0);
+    const size_t HD = size_t(H) * D;
+    const size_t base = (size_t(b) * T + t0) * HD + size_t(hh) * D;
+    const unsigned span = unsigned((size_t(nreal - 1) * HD + D));
+    const rsrc_t ra = make_rsrc(a + base, span * 4u), rg = make_rsrc(g + base, span * 4u);
+    const rsrc_t rk = make_rsrc(k + base, span * 2u), rq = make_rsrc(q + base, span * 2u);
+    const unsigned vo = unsigned(size_t(t) * HD + chl);
+    struct In {
+        f32x4_t a0, a1, g0, g1;
+        u16x4_t k0, k1, q0, q1;
+    };
+    auto load_in = [&](int p, In &in) {
+        const unsigned row = unsigned(32 * p + 16 * hb) * unsigned(HD);
+        in.a0 = buf_load_f4(ra, vo * 4u, row * 4u);
+        in.a1 = buf_load_f4(ra, vo * 4u + 64u, row * 4u);
+        in.g0 = buf_load_f4(rg, vo * 4u, row * 4u);
+        in.g1 = buf_load_f4(rg, vo * 4u + 64u, row * 4u);
+        in.k0 = Row4<bf16_t>::load(rk, vo * 2u, row * 2u);
+        in.k1 = Row4<bf16_t>::load(rk, vo * 2u + 32u, row * 2u);
+        in.q0 = Row4<bf16_t>::load(rq, vo * 2u, row * 2u);
+        in.q1 = Row4<bf16_t>::load(rq, vo * 2u + 32u, row * 2u);
+    };
+    float rr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rr[j] = r[size_t(hh) * D + chl + (j & 3) + 16 * (j >> 2)];
+
+    auto pack8 = [](const float (&x)[8]) {
+        return F::cat(F::pack(f32x4_t{x[0], x[1], x[2], x[3]}), F::pack(f32x4_t{x[4], x[5], x[6], x[7]}));
+    };
+    auto ld8f = [](const float *p, float (&x)[8]) {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(p);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = lo[i]; x[4 + i] = hi[i]; }
+    };
+    auto st8f = [](float *p, const float (&x)[8]) {
+        *reinterpret_cast<f32x4_t *>(p) = f32x4_t{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4_t *>(p + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
+    };
+    // Accumulator layout of the 16x16 products: lane (x = t, G) holds column t (the later
+    // token) and rows s = 4G + i (the earlier token), stored row-major as [t][s].
+    const unsigned blk_lo = unsigned(t * 16 + 4 * G);
+
+    // (K*beta')^T of pair p from LDS to the workspace: thread -> (channel, 8 positions).
+    auto kbt_out = [&](int p) {
+        const int ch = tid >> 2, c4 = tid & 3;
+        const f8 v = *reinterpret_cast<const f8 *>(sh_kt + ch * 32 + 8 * (c4 ^ ((ch >> 2) & 3)));
+        *reinterpret_cast<f8 *>(gKbT + size_t(ch) * C + 32 * p + 8 * c4) = v;
+    };
+    // Decay between block bs and the start of pair p + 1, from the one to pair p.
+    auto ft_update = [&](int p) {
+        constexpr int Q = D / 4;
+        for (int idx = tid; idx < (2 * p + 2) * Q; idx += NT) {
+            const int bs = idx / Q, c4 = 4 * (idx % Q);
+            const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(sh_pi + (2 * p) * D + c4);
+            const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(sh_pi + (2 * p + 1) * D + c4);
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(sh_ft + bs * D + c4);
+            if (bs < 2 * p) *dst = *dst * (p0 * p1);
+            else if (bs == 2 * p) *dst = p1;
+            else *dst = f32x4_t{1.f, 1.f, 1.f, 1.f};
+        }
+    };
+
+    In in;
+    load_in(0, in);
+    float Gp[8];  // product of the blocks before the current pair
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Gp[j] = 1.f;
+
+    for (int p = 0; p < NP; ++p) {
+        const int bt = 2 * p + hb;
+        // ------------------------------ phase 1 ------------------------------
+        if (p > 0) {
+            kbt_out(p - 1);
+            ft_update(p - 1);
+        }
+        float av[8], kv[8], qh[8];
+        {
+            const bool real = 16 * bt + t < nreal;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = real ? in.a0[i] : 1.f;
+                av[4 + i] = real ? in.a1[i] : 1.f;
+                kv[i] = bf16_to_f32(in.k0[i]);
+                kv[4 + i] = bf16_to_f32(in.k1[i]);
+                qh[i] = rr[i] * in.g0[i] * bf16_to_f32(in.q0[i]);
+                qh[4 + i] = rr[4 + i] * in.g1[i] * bf16_to_f32(in.q1[i]);
+            }
+        }
+        if (p + 1 < NP) load_in(p + 1, in);
+
+        // Prefix products inside aligned segments of 2, 4, 8 and 16 tokens (each level
+        // multiplies the upper half of a segment by the last value of its lower half).
+        // Every DPP move runs with all lanes active (a lane can only read a lane that
+        // executes the move), and the lane's choice is a select afterwards.
+        float R2[8], R4[8], R8[8], pi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float x = av[j], y;
+            y = dpp_or_one<kRowShr1>(x);
+            x *= (t & 1) ? y : 1.f;
+            R2[j] = x;
+            y = dpp_or_one<quad_perm(0, 1, 1, 1)>(x);
+            x *= (t & 2) ? y : 1.f;
+            R4[j] = x;
+            y = dpp_or_one<kRowShr4>(dpp_or_one<quad_perm(3, 3, 3, 3)>(x));
+            x *= (t & 4) ? y : 1.f;
+            R8[j] = x;
+            y = dpp_or_one<row_bcast(7)>(x);
+            x *= (t & 8) ? y : 1.f;
+            pi[j] = x;
+        }
+        // Suffix products likewise; the exclusive suffix inside a segment of size n is the
+        // inclusive one of the next token (1 at the segment's last token). Level tables:
+        // f_n(t) = prefix from the segment start (t in an upper half of a 2n-node) or
+        // exclusive suffix to the segment end (t in a lower half).
+        float f8t[8], f4t[8], f2t[8], f1t[8], sig[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float x = av[j], y, l;
+            f1t[j] = (t & 1) ? x : 1.f;
+            y = dpp_or_one<kRowShl1>(x);
+            x *= (t & 1) ? 1.f : y;  // S2
+            l = dpp_or_one<kRowShl1>(x);
+            f2t[j] = (t & 2) ? R2[j] : ((t & 1) ? 1.f : l);
+            y = dpp_or_one<quad_perm(2, 2, 2, 2)>(x);
+            x *= (t & 2) ? 1.f : y;  // S4
+            l = dpp_or_one<kRowShl1>(x);
+            f4t[j] = (t & 4) ? R4[j] : (((t & 3) == 3) ? 1.f : l);
+            y = dpp_or_one<kRowShl4>(dpp_or_one<quad_perm(0, 0, 0, 0)>(x));
+            x *= (t & 4) ? 1.f : y;  // S8
+            l = dpp_or_one<kRowShl1>(x);
+            f8t[j] = (t & 8) ? R8[j] : (((t & 7) == 7) ? 1.f : l);
+            y = dpp_or_one<row_bcast(8)>(x);
+            x *= (t & 8) ? 1.f : y;  // S16
+            sig[j] = dpp_or_one<kRowShl1>(x);  // 1 at t = 15
+        }
+
+        // LDS: K*sigma of the block (all later pairs), K*pi and Qh*pi (this pair's
+        // off-diagonal blocks), the block's decay (lane t = 15 holds it in pi).
+        {
+            float x[8], y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = kv[j] * sig[j];
+            *reinterpret_cast<f8 *>(sh_bb + swz<D>(16 * bt + t, 4 * cg + G)) = pack8(x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { x[j] = kv[j] * pi[j]; y[j] = qh[j] * pi[j]; }
+            *reinterpret_cast<f8 *>(sh_A + (hb * 2 + 0) * 16 * D + swz<D>(t, 4 * cg + G)) = pack8(x);
+            *reinterpret_cast<f8 *>(sh_A + (hb * 2 + 1) * 16 * D + swz<D>(t, 4 * cg + G)) = pack8(y);
+            if (t == 15) st8f(sh_pi + bt * D + pos0, pi);
+        }
+        // This wavefront's share (its 32 channels) of the diagonal blocks of M and P: one
+        // masked product per recursion level, plus the diagonal of P.
+        {
+            f32x4_t lm = zero4(), lp = zero4();
+            auto level = [&](const float (&f)[8], int half) {
+                float x[8], y[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { x[j] = kv[j] * f[j]; y[j] = qh[j] * f[j]; }
+                const f8 fk = pack8(x), fq = pack8(y);
+                const f32x4_t am = F::mma8(fk, fk, zero4());
+                const f32x4_t ap = F::mma8(fk, fq, zero4());
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 4 * G + i;
+                    const bool valid = ((t ^ s) < 2 * half) && (t & half) && !(s & half);
+                    lm[i] += valid ? am[i] : 0.f;
+                    lp[i] += valid ? ap[i] : 0.f;
+                }
+            };
+            level(f8t, 8);
+            level(f4t, 4);
+            level(f2t, 2);
+            level(f1t, 1);
+            const f32x4_t ad = F::mma8(pack8(kv), pack8(qh), zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lp[i] += (4 * G + i == t) ? ad[i] : 0.f;
+            sh_dg[((hb * NG + cg) * 2 + 0) * 64 + lane] = lm;
+            sh_dg[((hb * NG + cg) * 2 + 1) * 64 + lane] = lp;
+        }
+        lds_barrier();
+
+        // ------------------------------ phase 2 ------------------------------
+        float P0[8], P1[8];  // decays of blocks 2p and 2p + 1 at the thread's positions
+        ld8f(sh_pi + (2 * p) * D + pos0, P0);
+        ld8f(sh_pi + (2 * p + 1) * D + pos0, P1);
+        {
+            float x[8], y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gam = Gp[j] * (hb ? P0[j] : 1.f) * pi[j];
+                x[j] = kv[j] * gam;
+                y[j] = qh[j] * gam;
+            }
+            const size_t row = size_t(16 * bt + t) * D + pos0;
+            *reinterpret_cast<f8 *>(gKg + row) = pack8(x);
+            *reinterpret_cast<f8 *>(gQg + row) = pack8(y);
+            // (K*beta')^T into LDS: channel row, position 8 (t / 4) + 4 hb + t % 4 of the
+            // pair (the 32-group order), 16-byte chunks rotated by (channel / 4) mod 4.
+            const int pp = 8 * (t >> 2) + 4 * hb + (t & 3);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int ch = chl + (j & 3) + 16 * (j >> 2);
+                const float kb = kv[j] * sig[j] * (hb ? 1.f : P1[j]);
+                sh_kt[ch * 32 + 8 * ((pp >> 3) ^ ((ch >> 2) & 3)) + (pp & 7)] = bf16_t{f32_to_bf16(kb)};
+            }
+            if (hb == 1 && t == 15) {
+                *reinterpret_cast<f32x4_t *>(gPP + p * D + chl) =
+                    f32x4_t{P0[0] * P1[0], P0[1] * P1[1], P0[2] * P1[2], P0[3] * P1[3]};
+                *reinterpret_cast<f32x4_t *>(gPP + p * D + chl + 16) =
+                    f32x4_t{P0[4] * P1[4], P0[5] * P1[5], P0[6] * P1[6], P0[7] * P1[7]};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Gp[j] *= P0[j] * P1[j];
+        }
+        if (cg == 0) {
+            // Diagonal blocks: sum of the channel groups' shares.
+            f32x4_t lm = zero4(), lp = zero4();
+#pragma unroll
+            for (int c = 0; c < NG; ++c) {
+                lm += sh_dg[((hb * NG + c) * 2 + 0) * 64 + lane];
+                lp += sh_dg[((hb * NG + c) * 2 + 1) * 64 + lane];
+            }
+            *reinterpret_cast<f32x4_t *>(gMD + size_t(bt) * 256 + blk_lo) = lm;
+            store4(gP + size_t(SL::tri(bt, bt)) * 256 + blk_lo, lp);
+        }
+        // Off-diagonal blocks of the pair: (2p, bs < 2p) then (2p + 1, bs <= 2p), dealt to
+        // the wavefronts in turn. Rows s: K*sigma of block bs times the decay of the whole
+        // blocks between bs and bt; columns t: K*pi (Qh*pi) of block bt.
+        const int nblk = 4 * p + 1;
+        if (wave < nblk) {
+            f8 ak[2][NG], aq[2][NG];
+            float pb0[NG][8];  // decay of block 2p at the operand positions of this lane
+#pragma unroll
+            for (int kk = 0; kk < NG; ++kk) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    ak[h2][kk] = *reinterpret_cast<const f8 *>(sh_A + (h2 * 2 + 0) * 16 * D + swz<D>(t, 4 * kk + G));
+                    aq[h2][kk] = *reinterpret_cast<const f8 *>(sh_A + (h2 * 2 + 1) * 16 * D + swz<D>(t, 4 * kk + G));
+                }
+                ld8f(sh_pi + (2 * p) * D + 32 * kk + 8 * G, pb0[kk]);
+            }
+            for (int n = wave; n < nblk; n += NW) {
+                const bool odd = n >= 2 * p;
+                const int bto = odd ? 2 * p + 1 : 2 * p;
+                const int bs = odd ? n - 2 * p : n;
+                f32x4_t am = zero4(), ap = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NG; ++kk) {
+                    const f8 xb = *reinterpret_cast<const f8 *>(sh_bb + swz<D>(16 * bs + t, 4 * kk + G));
+                    float dm[8];
+                    if (bs < 2 * p) {
+                        ld8f(sh_ft + bs * D + 32 * kk + 8 * G, dm);
+                        if (odd) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) dm[j] *= pb0[kk][j];
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) dm[j] = 1.f;
+                    }
+                    float x[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(xb[j]) * dm[j];
+                    const f8 fb = pack8(x);
+                    am = F::mma8(fb, odd ? ak[1][kk] : ak[0][kk], am);
+                    ap = F::mma8(fb, odd ? aq[1][kk] : aq[0][kk], ap);
+                }
+                store4(gM + size_t(SL::tri(bto, bs)) * 256 + blk_lo, am);
+                store4(gP + size_t(SL::tri(bto, bs)) * 256 + blk_lo, ap);
+            }
+        }
+        lds_barrier();
+    }
+    kbt_out(NP - 1);
+}
+
 // Per-leaf inputs of the serial chain, row layout: lane (t, g) holds token t of the
 // leaf and value columns 4g..4g+3 of the tile.
 template <typename QT> struct LeafIn {
@@ -908,16 +1276,29 @@ hipError_t prepare_typed(const void *q, const void *k, const float *a, const flo
                          hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
     if (nchunks == 0) return hipSuccess;
-    using LY = PrepLds<OpT, D, C>;
-    auto kern = chunk_prepare_kernel<QT, OpT, D, C>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(LY::BYTES));
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(kThreads), LY::BYTES, stream,
-                       static_cast<const QT *>(q), static_cast<const QT *>(k), a, g, r,
-                       static_cast<unsigned char *>(workspace), T, H, nchunks);
-    return hipGetLastError();
+    if constexpr (std::is_same_v<OpT, bf16_t>) {
+        using LY = Prep2Lds<D, C>;
+        auto kern = chunk_prepare_bf16_kernel<D, C>;
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(LY::BYTES));
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(4 * D), LY::BYTES, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), a, g,
+                           r, static_cast<unsigned char *>(workspace), T, H, nchunks);
+        return hipGetLastError();
+    } else {
+        using LY = PrepLds<OpT, D, C>;
+        auto kern = chunk_prepare_kernel<QT, OpT, D, C>;
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(LY::BYTES));
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(kThreads), LY::BYTES, stream,
+                           static_cast<const QT *>(q), static_cast<const QT *>(k), a, g, r,
+                           static_cast<unsigned char *>(workspace), T, H, nchunks);
+        return hipGetLastError();
+    }
 }
 
 template <typename QT, typename OpT, int D, int C>
