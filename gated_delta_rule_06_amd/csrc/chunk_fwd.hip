@@ -538,13 +538,12 @@ template <> struct Row4<float> {
 // ---------------------------------------------------------------------------------
 // Phase P for bf16 operands: the same outputs in one streaming pass over the chunk.
 // ---------------------------------------------------------------------------------
-// Row scans over the 16 tokens of a block run on the 16-lane DPP rows. dpp_or_one<CTRL>
+// Row scans over the 16 tokens of a block run on the 16-lane DPP rows. dpp_mv<CTRL>
 // moves x across lanes with DPP control CTRL; lanes whose source lies outside their row
-// read 1 (the identity of the products).
-template <int CTRL> __device__ __forceinline__ float dpp_or_one(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f),
-                                                                 __builtin_bit_cast(int, x), CTRL,
-                                                                 0xf, 0xf, false));
+// read 0, and every use below replaces those lanes' value by a select.
+template <int CTRL> __device__ __forceinline__ float dpp_mv(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                              0xf, 0xf, true));
 }
 constexpr int kRowShl1 = 0x101, kRowShl4 = 0x104, kRowShr1 = 0x111, kRowShr4 = 0x114;
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
@@ -725,16 +724,16 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float x = av[j], y;
-            y = dpp_or_one<kRowShr1>(x);
+            y = dpp_mv<kRowShr1>(x);
             x *= (t & 1) ? y : 1.f;
             R2[j] = x;
-            y = dpp_or_one<quad_perm(0, 1, 1, 1)>(x);
+            y = dpp_mv<quad_perm(0, 1, 1, 1)>(x);
             x *= (t & 2) ? y : 1.f;
             R4[j] = x;
-            y = dpp_or_one<kRowShr4>(dpp_or_one<quad_perm(3, 3, 3, 3)>(x));
+            y = dpp_mv<kRowShr4>(dpp_mv<quad_perm(3, 3, 3, 3)>(x));
             x *= (t & 4) ? y : 1.f;
             R8[j] = x;
-            y = dpp_or_one<row_bcast(7)>(x);
+            y = dpp_mv<row_bcast(7)>(x);
             x *= (t & 8) ? y : 1.f;
             pi[j] = x;
         }
@@ -747,21 +746,22 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
         for (int j = 0; j < 8; ++j) {
             float x = av[j], y, l;
             f1t[j] = (t & 1) ? x : 1.f;
-            y = dpp_or_one<kRowShl1>(x);
+            y = dpp_mv<kRowShl1>(x);
             x *= (t & 1) ? 1.f : y;  // S2
-            l = dpp_or_one<kRowShl1>(x);
+            l = dpp_mv<kRowShl1>(x);
             f2t[j] = (t & 2) ? R2[j] : ((t & 1) ? 1.f : l);
-            y = dpp_or_one<quad_perm(2, 2, 2, 2)>(x);
+            y = dpp_mv<quad_perm(2, 2, 2, 2)>(x);
             x *= (t & 2) ? 1.f : y;  // S4
-            l = dpp_or_one<kRowShl1>(x);
+            l = dpp_mv<kRowShl1>(x);
             f4t[j] = (t & 4) ? R4[j] : (((t & 3) == 3) ? 1.f : l);
-            y = dpp_or_one<kRowShl4>(dpp_or_one<quad_perm(0, 0, 0, 0)>(x));
+            y = dpp_mv<kRowShl4>(dpp_mv<quad_perm(0, 0, 0, 0)>(x));
             x *= (t & 4) ? 1.f : y;  // S8
-            l = dpp_or_one<kRowShl1>(x);
+            l = dpp_mv<kRowShl1>(x);
             f8t[j] = (t & 8) ? R8[j] : (((t & 7) == 7) ? 1.f : l);
-            y = dpp_or_one<row_bcast(8)>(x);
+            y = dpp_mv<row_bcast(8)>(x);
             x *= (t & 8) ? 1.f : y;  // S16
-            sig[j] = dpp_or_one<kRowShl1>(x);  // 1 at t = 15
+            y = dpp_mv<kRowShl1>(x);
+            sig[j] = (t == 15) ? 1.f : y;
         }
 
         // LDS: K*sigma of the block (all later pairs), K*pi and Qh*pi (this pair's
@@ -854,7 +854,9 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
         }
         // Off-diagonal blocks of the pair: (2p, bs < 2p) then (2p + 1, bs <= 2p), dealt to
         // the wavefronts in turn. Rows s: K*sigma of block bs times the decay of the whole
-        // blocks between bs and bt; columns t: K*pi (Qh*pi) of block bt.
+        // blocks between bs and bt; columns t: K*pi (Qh*pi) of block bt. Three cases, each
+        // its own loop: bt = 2p (decay F[bs]), bt = 2p + 1 and bs < 2p (F[bs] times the
+        // decay of block 2p), and (2p + 1, 2p) (no decay in between).
         const int nblk = 4 * p + 1;
         if (wave < nblk) {
             f8 ak[2][NG], aq[2][NG];
@@ -868,35 +870,35 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 }
                 ld8f(sh_pi + (2 * p) * D + 32 * kk + 8 * G, pb0[kk]);
             }
-            for (int n = wave; n < nblk; n += NW) {
-                const bool odd = n >= 2 * p;
-                const int bto = odd ? 2 * p + 1 : 2 * p;
-                const int bs = odd ? n - 2 * p : n;
+            auto block = [&](int bto, int bs, const f8 (&ka)[NG], const f8 (&qa)[NG], auto mode) {
+                constexpr int MODE = decltype(mode)::value;
                 f32x4_t am = zero4(), ap = zero4();
 #pragma unroll
                 for (int kk = 0; kk < NG; ++kk) {
                     const f8 xb = *reinterpret_cast<const f8 *>(sh_bb + swz<D>(16 * bs + t, 4 * kk + G));
-                    float dm[8];
-                    if (bs < 2 * p) {
+                    f8 fb = xb;
+                    if constexpr (MODE != 2) {
+                        float dm[8], x[8];
                         ld8f(sh_ft + bs * D + 32 * kk + 8 * G, dm);
-                        if (odd) {
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) dm[j] *= pb0[kk][j];
+                        for (int j = 0; j < 8; ++j) {
+                            const float d = MODE == 1 ? dm[j] * pb0[kk][j] : dm[j];
+                            x[j] = bf16_to_f32(xb[j]) * d;
                         }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) dm[j] = 1.f;
+                        fb = pack8(x);
                     }
-                    float x[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(xb[j]) * dm[j];
-                    const f8 fb = pack8(x);
-                    am = F::mma8(fb, odd ? ak[1][kk] : ak[0][kk], am);
-                    ap = F::mma8(fb, odd ? aq[1][kk] : aq[0][kk], ap);
+                    am = F::mma8(fb, ka[kk], am);
+                    ap = F::mma8(fb, qa[kk], ap);
                 }
                 store4(gM + size_t(SL::tri(bto, bs)) * 256 + blk_lo, am);
                 store4(gP + size_t(SL::tri(bto, bs)) * 256 + blk_lo, ap);
-            }
+            };
+            for (int n = wave; n < 2 * p; n += NW)
+                block(2 * p, n, ak[0], aq[0], std::integral_constant<int, 0>{});
+            for (int n = 2 * p + ((wave - 2 * p) % NW + NW) % NW; n < 4 * p; n += NW)
+                block(2 * p + 1, n - 2 * p, ak[1], aq[1], std::integral_constant<int, 1>{});
+            if (4 * p % NW == wave)
+                block(2 * p + 1, 2 * p, ak[1], aq[1], std::integral_constant<int, 2>{});
         }
         lds_barrier();
     }
