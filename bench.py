@@ -42,18 +42,29 @@ def algorithmic(d, chunk, qkv_bytes=2):
     }
 
 
+def code_sha(path):
+    """sha256 prefix of a C/HIP source with its comments and whitespace removed, so that
+    it changes with the code but not with its comments."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` ('prepare' or 'scan') on the long-context workload,
     from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/ (scaled by the copy
-    calibration recorded there). None when the summary is missing or was taken on a
-    different version of the kernel source."""
-    import hashlib
+    calibration recorded there). None when the summary is missing or was taken on
+    different code (its code_sha differs from the current source's)."""
     import re
     path = os.path.join(ROOT, "profiles", "chunk_fwd_long_context_hbm_counters.md")
     src = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc", "chunk_fwd.hip")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = code_sha(src)
     except OSError:
         return None
     m = re.search(r"traffic sha=(\w+) prepare_bytes=(\d+) scan_bytes=(\d+)", text)

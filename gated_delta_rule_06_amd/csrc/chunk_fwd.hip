@@ -15,26 +15,28 @@
 //   O = (Qh*gamma) S0 + P U;   S_C = Diag(gamma_C) S0 + (K*beta)^T U
 // where qh = r * g * q. This follows from unrolling the token recurrence (decay, erase
 // the decayed state's prediction for k_t under the value-channel gate e_t, write
-// w_t * v_t, read with r * g_t * q_t).
+// w_t * v_t, read with r * g_t * q_t). The state carry is evaluated in Horner form over
+// 32-token leaf pairs: S <- Diag(pi_p) S + (K*beta')_p^T U_p per pair p, from S0, where
+// pi_p is the pair's whole decay and beta'_s the decay from s to the end of its pair;
+// this ends at the S_C above, with every factor in [0, 1].
 //
 // Two kernels:
-//  * chunk_prepare_kernel (a1-a3), one workgroup per (chunk, head, batch), fully
-//    parallel: decay products, the operands K*gamma, Qh*gamma, (K*beta)^T, gamma_C, and
-//    the lower-triangular M and P in 16x16 blocks. Off-diagonal block (bt, bs) is one
-//    MFMA product (K_bs * sigma_bs * D)(K_bt * pi_bt)^T pivoted at the start of block
-//    bt: pi is the running product inside bt from its start, sigma the running product
-//    inside bs after s, D the product of the whole blocks in between. The 16x16
-//    diagonal blocks recurse further (pivots every 8, 4, 2, 1 tokens), each level one
-//    masked MFMA tile, so the Gram work is all on the matrix cores.
-//  * chunk_scan_kernel (a4-a6), one workgroup per (batch x head, 16 value columns),
-//    sequential over chunks (value columns are exactly independent). Wave 0 carries the
-//    serial chain: for leaf L (16 tokens) it subtracts E_L * (M_{L,<L} U_{<L}) from the
-//    leaf's right-hand side on MFMA -- the off-diagonal products of the block-Neumann
+//  * the parallel phase, one workgroup per (chunk, head, batch): decay products, the
+//    operands K*gamma, Qh*gamma, (K*beta')^T, the pair decays, and the lower-triangular
+//    M and P in 16x16 blocks. Off-diagonal block (bt, bs) is one MFMA product
+//    (K_bs * sigma_bs * D)(K_bt * pi_bt)^T pivoted at the start of block bt: pi is the
+//    running product inside bt from its start, sigma the running product inside bs after
+//    s, D the product of the whole blocks in between. The 16x16 diagonal blocks recurse
+//    further (pivots every 8, 4, 2, 1 tokens), each level one masked MFMA tile, so the
+//    Gram work is all on the matrix cores. chunk_prepare_bf16_kernel streams the chunk
+//    once for bf16 operands; chunk_prepare_kernel serves fp32 operands.
+//  * chunk_scan_kernel, one workgroup per (batch x head, 16 value columns), sequential
+//    over chunks (value columns are exactly independent). Its chain wavefront carries
+//    the serial path: for leaf L (16 tokens) it subtracts E_L * (M_{L,<L} U_{<L}) from
+//    the leaf's right-hand side on MFMA -- the off-diagonal products of the block-Neumann
 //    recursion, grouped by the leaf they update -- then solves the 16x16 unit
-//    lower-triangular leaf of every column by forward substitution. Waves 1-3 follow one
-//    leaf behind: the readout O_L = (Qh*gamma)_L S0 + P_{L,<=L} U_{<=L} and the state
-//    contribution (K*beta)_L^T U_L, both on MFMA. The chunk's Gram blocks M are copied
-//    into LDS by direct global->LDS loads issued during the previous chunk.
+//    lower-triangular leaf of every column by forward substitution, and carries the
+//    state. Its readout wavefront computes O = (Qh*gamma) S0 + P U one chunk behind.
 #include <type_traits>
 #include <utility>
 

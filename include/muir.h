@@ -64,8 +64,9 @@ typedef enum {
  * Workspace bytes needed by muir_chunk_fwd for these sizes (0 for invalid sizes).
  * The workspace holds, per (batch, head, chunk), what the parallel phase hands to the
  * sequential one: the lower-triangular intra-chunk Gram matrices M and P in 16x16
- * blocks, the decay-scaled operands K*gamma, (r*g*q)*gamma and (K*beta)^T, and the
- * whole-chunk decay, in the operand precision (bf16 for bf16 q/k/v, fp32 otherwise).
+ * blocks, the decay-scaled operands K*gamma, (r*g*q)*gamma and (K*beta')^T, in the
+ * operand precision (bf16 for bf16 q/k/v, fp32 otherwise), and the decay of every
+ * 32-token leaf pair in fp32.
  * It must be 256-byte aligned. Its contents are scratch: nothing is expected in it
  * on entry to muir_chunk_fwd or kept from it on return.
  */
@@ -118,7 +119,8 @@ muir_status_t muir_chunk_fwd(
  * muir_chunk_fwd_prepare: the parallel phase, one work item per (batch, head, chunk):
  *   the decay running products pivoted at 16-token block boundaries (every factor in
  *   [0, 1], no division), the decay-scaled operands K*gamma, (r*g*q)*gamma and
- *   (K*beta)^T, the whole-chunk decay gamma_C, and the lower-triangular intra-chunk
+ *   (K*beta')^T (beta' runs to the end of the token's 32-token leaf pair), the decay of
+ *   every leaf pair, and the lower-triangular intra-chunk
  *   Gram matrices M (decayed key-key, strictly lower) and P (decayed query-key,
  *   inclusive) in 16x16 blocks on the matrix cores. Writes them into `workspace`.
  *   Arguments as for muir_chunk_fwd (dv is taken equal to dk). T == 0 launches nothing.
@@ -126,7 +128,8 @@ muir_status_t muir_chunk_fwd(
  * muir_chunk_fwd_scan: the sequential phase, one work item per (batch, head, 16 value
  *   columns), chunk after chunk: the prediction of the carried state, the recursive
  *   block-Neumann solve of every value column's triangular system, the readout
- *   o = (r*g*q*gamma) S0 + P U and the state carry S = Diag(gamma_C) S0 + (K*beta)^T U.
+ *   o = (r*g*q*gamma) S0 + P U and the state carry S = Diag(gamma_C) S0 + (K*beta)^T U,
+ *   evaluated pair by pair as S <- Diag(pair decay) S + (K*beta')^T U.
  *   Reads `workspace` as left by muir_chunk_fwd_prepare for the same sizes and inputs;
  *   the workspace must not be modified between the two calls. T == 0 copies s0 (or
  *   zeros) into s_out.
