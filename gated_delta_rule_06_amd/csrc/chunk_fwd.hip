@@ -596,7 +596,6 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     using SL = Slot<bf16_t, D, C>;
     using LY = Prep2Lds<D, C>;
     using F = Frag<bf16_t>;
-    using f4 = F::f4;
     using f8 = F::f8;
     constexpr int NB = C / 16, NP = NB / 2, NG = D / 32, NW = 2 * NG, NT = 64 * NW;
 
@@ -912,7 +911,6 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 template <typename QT> struct LeafIn {
     f32x4_t ev, wv;
     typename Row4<QT>::raw vv;
-    f32x4_t md[4];  // row t of the leaf's diagonal M block (fp32)
 };
 
 // The scan: one workgroup of two wavefronts per (batch, head, 16 value columns),
@@ -958,6 +956,9 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     // staged by the readout wavefront one chunk ahead of the chain.
     constexpr int NP = NB / 2;
     __shared__ __align__(16) float sh_pp[2][NP][D];
+    // The chunk's fp32 diagonal blocks of M (row-major [t][s] per leaf), staged the same
+    // way: whole 16-byte pieces, so each load of the stager uses full cache lines.
+    __shared__ __align__(16) f32x4_t sh_md[2][NB][64];
 
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
@@ -990,7 +991,6 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     const unsigned lo_blk = unsigned(x * 16 + 4 * g) * OB;  // 16x16 block, row x, cols 4g..
     const unsigned lo_kg = unsigned(x * D + 8 * g) * OB;    // [token x][8g..] of Kg / Qg
     const unsigned lo_kbt = unsigned(x * C + 8 * g) * OB;   // [channel x][8g..] of KbT
-    const unsigned lo_md = unsigned(x * 16 * 4);
     const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
     const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
 
@@ -1049,9 +1049,24 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         f32x4_t ppt[PPN];
         load_ppt(0, ppt);
         put_ppt(0, ppt);
+        // Diagonal blocks of chunk ci (NB KiB): lane l holds floats 4l .. 4l+3 of each leaf.
+        f32x4_t mdt[NB];
+        auto load_mdt = [&](int ci) {
+#pragma unroll
+            for (int L = 0; L < NB; ++L) mdt[L] = buf_load_f4(rws, unsigned(16 * lane), wsoff(ci, SL::MD_OFF + L * 1024));
+        };
+        auto put_mdt = [&](int ci) {
+#pragma unroll
+            for (int L = 0; L < NB; ++L) sh_md[ci & 1][L][lane] = mdt[L];
+        };
+        load_mdt(0);
+        put_mdt(0);
         lds_barrier();
         for (int p = 0; p <= nchunks; ++p) {
-            if (p + 1 < nchunks) load_ppt(p + 1, ppt);
+            if (p + 1 < nchunks) {
+                load_ppt(p + 1, ppt);
+                load_mdt(p + 1);
+            }
             if (p >= 1) {
                 const int ci = p - 1;
                 const int buf = ci & 1;
@@ -1077,7 +1092,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
             }
-            if (p + 1 < nchunks) put_ppt(p + 1, ppt);
+            if (p + 1 < nchunks) {
+                put_ppt(p + 1, ppt);
+                put_mdt(p + 1);
+            }
             lds_barrier();
         }
         return;
@@ -1102,9 +1120,6 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         in.ev = buf_load_f4(re, lo_f, so);
         in.wv = buf_load_f4(rwt, lo_f, so);
         in.vv = Row4<QT>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            in.md[q4] = buf_load_f4(rws, lo_md, wsoff(ci, SL::MD_OFF + L * 1024 + 16 * q4));
     };
     auto load_kbt = [&](int ci, int pair, int c) {
         return F::bload8(rws, lo_kbt, wsoff(ci, SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
@@ -1174,6 +1189,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 Win &cw = win[L & 1];
                 Win &nw = win[(L + 1) & 1];
                 LeafIn<QT> &cin = in[L & 1];
+                // Row t of the leaf's diagonal M block, from LDS (staged a chunk ahead).
+                f32x4_t md[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) md[q4] = sh_md[buf][L][4 * x + q4];
                 const int ciN = more ? ci : ci + 1;  // chunk of leaf L + 1
                 constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
 
@@ -1195,7 +1214,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 // Coefficients of step s: -e_c * M_LL[t][s], formed just before the step.
                 auto step = [&](auto Sc) {
                     constexpr int St = decltype(Sc)::value;
-                    const float m = cin.md[St / 4][St % 4];
+                    const float m = md[St / 4][St % 4];
                     subst_step<St>(x0, x1, x2, x3, ne[0] * m, ne[1] * m, ne[2] * m, ne[3] * m);
                 };
 
