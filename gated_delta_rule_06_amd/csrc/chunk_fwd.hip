@@ -84,6 +84,17 @@ __host__ __device__ constexpr int pair_perm(int x) {
     return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
 }
 
+// Fragment order of the operands Kg, Qg ([C rows][D positions]) and KbT ([D][C]): the
+// operand a lane group needs for one 16-row group and one 32-position group is 64
+// lanes x 8 values, stored contiguously with lane 16G + r holding row r and positions
+// 8G .. 8G + 7 of the group. The scan then reads a whole fragment as one contiguous
+// 16-byte (bf16) load per lane, eight full cache lines per load. Element (row, pos) of
+// an operand with npos positions per row:
+__host__ __device__ constexpr size_t frag_idx(int row, int pos, int npos) {
+    return ((size_t(row >> 4) * (npos >> 5) + (pos >> 5)) * 64 + 16 * ((pos & 31) >> 3) + (row & 15)) * 8 +
+           (pos & 7);
+}
+
 // LDS of the prepare kernel: block totals, K*sigma (padded rows), per-wave tables.
 template <typename OpT, int D, int C> struct PrepLds {
     static constexpr int DP = D + 4;                               // fp32 table row pitch
@@ -196,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             const int tt = 16 * bb + t;
             pi *= av[t];
             const float gam = G * pi;
-            gKg[size_t(tt) * D + pair_perm(ch)] = MM::from_f32(kv[t] * gam);
-            gQg[size_t(tt) * D + pair_perm(ch)] = MM::from_f32(qv[t] * gam);
+            gKg[frag_idx(tt, pair_perm(ch), D)] = MM::from_f32(kv[t] * gam);
+            gQg[frag_idx(tt, pair_perm(ch), D)] = MM::from_f32(qv[t] * gam);
         }
         float kbt[16];
         float sig = 1.f;
@@ -207,10 +218,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             sh_bb[(16 * bb + t) * DB + ch] = MM::from_f32(kv[t] * sig);
             sig *= av[t];
         }
-        OpT *dst = gKbT + size_t(ch) * C;
 #pragma unroll
         for (int t = 0; t < 16; t += 4)
-            store4(dst + pair_perm(16 * bb + t), f32x4_t{kbt[t], kbt[t + 1], kbt[t + 2], kbt[t + 3]});
+            store4(gKbT + frag_idx(ch, pair_perm(16 * bb + t), C),
+                   f32x4_t{kbt[t], kbt[t + 1], kbt[t + 2], kbt[t + 3]});
     }
     lds_barrier();
 
@@ -673,7 +684,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     auto kbt_out = [&](int p) {
         const int ch = tid >> 2, c4 = tid & 3;
         const f8 v = *reinterpret_cast<const f8 *>(sh_kt + ch * 32 + 8 * (c4 ^ ((ch >> 2) & 3)));
-        *reinterpret_cast<f8 *>(gKbT + size_t(ch) * C + 32 * p + 8 * c4) = v;
+        *reinterpret_cast<f8 *>(gKbT + frag_idx(ch, 32 * p + 8 * c4, C)) = v;
     };
     // Decay between block bs and the start of pair p + 1, from the one to pair p.
     auto ft_update = [&](int p) {
@@ -821,7 +832,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 x[j] = kv[j] * gam;
                 y[j] = qh[j] * gam;
             }
-            const size_t row = size_t(16 * bt + t) * D + pos0;
+            const size_t row = frag_idx(16 * bt + t, pos0, D);
             *reinterpret_cast<f8 *>(gKg + row) = pack8(x);
             *reinterpret_cast<f8 *>(gQg + row) = pack8(y);
             // (K*beta')^T into LDS: channel row, position 8 (t / 4) + 4 hb + t % 4 of the
@@ -989,8 +1000,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     // Per-lane byte offsets (each load adds one to a uniform base and offset).
     constexpr unsigned OB = sizeof(OpT);
     const unsigned lo_blk = unsigned(x * 16 + 4 * g) * OB;  // 16x16 block, row x, cols 4g..
-    const unsigned lo_kg = unsigned(x * D + 8 * g) * OB;    // [token x][8g..] of Kg / Qg
-    const unsigned lo_kbt = unsigned(x * C + 8 * g) * OB;   // [channel x][8g..] of KbT
+    const unsigned lo_frag = unsigned(lane * 8) * OB;        // lane's share of an operand fragment
     const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
     const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
 
@@ -1009,7 +1019,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     auto load_kg = [&](int ci, int L, size_t OFF, f8 (&dst)[NKD]) {
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk)
-            dst[kk] = F::bload8(rws, lo_kg, wsoff(ci, OFF + (16 * L * D + 32 * kk) * OB));
+            dst[kk] = F::bload8(rws, lo_frag, wsoff(ci, OFF + frag_idx(16 * L, 32 * kk, D) * OB));
     };
     auto load_blk = [&](int ci, size_t OFF, int bt, int bs) {
         return F::bload4(rws, lo_blk, wsoff(ci, OFF + SL::tri(bt, bs) * 256 * OB));
@@ -1122,7 +1132,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         in.vv = Row4<QT>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
     };
     auto load_kbt = [&](int ci, int pair, int c) {
-        return F::bload8(rws, lo_kbt, wsoff(ci, SL::KBT_OFF + (16 * c * C + 32 * pair) * OB));
+        return F::bload8(rws, lo_frag, wsoff(ci, SL::KBT_OFF + frag_idx(16 * c, 32 * pair, C) * OB));
     };
     // Decay over leaf pair `pair` of chunk ci of the rows of state tile c.
     auto lds_pp = [&](int ci, int pair, int c) {
