@@ -66,8 +66,8 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~si
 // ([D][C]) along tokens.
 template <typename OpT, int D, int C> struct Slot {
     static constexpr int NB = C / 16;
-    static constexpr int NTRI = NB * (NB + 1) / 2;
-    static constexpr size_t M_BYTES = size_t(NTRI) * 256 * sizeof(OpT);
+    static constexpr int NPAIR = (NB / 2) * (NB / 2 + 1);  // block-pair slots of M (and of P)
+    static constexpr size_t M_BYTES = size_t(NPAIR) * 512 * sizeof(OpT);
     static constexpr size_t M_OFF = 0;
     static constexpr size_t PP_OFF = align256(M_OFF + M_BYTES);       // pair decays [NB/2][D]
     static constexpr size_t P_OFF = align256(PP_OFF + size_t(NB / 2) * D * 4);
@@ -76,7 +76,16 @@ template <typename OpT, int D, int C> struct Slot {
     static constexpr size_t KBT_OFF = align256(QG_OFF + size_t(C) * D * sizeof(OpT));
     static constexpr size_t MD_OFF = align256(KBT_OFF + size_t(C) * D * sizeof(OpT));
     static constexpr size_t BYTES = align256(MD_OFF + size_t(NB) * 256 * 4);
-    static __host__ __device__ constexpr int tri(int bt, int bs) { return bt * (bt + 1) / 2 + bs; }
+    // First block-pair slot of block row bt; the row has bt / 2 + 1 of them.
+    static __host__ __device__ constexpr int prow(int bt) {
+        return (bt >> 1) * ((bt >> 1) + 1) + (bt & 1) * ((bt >> 1) + 1);
+    }
+    // Element w = 16 t + s of block (bt, bs). Blocks 2j and 2j + 1 of a row share one
+    // slot, interleaved four elements at a time, so that one 8-element load gives a lane
+    // the same four elements of both (the two halves of a K = 32 operand).
+    static __host__ __device__ constexpr size_t blk(int bt, int bs, int w) {
+        return size_t(prow(bt) + (bs >> 1)) * 512 + ((w >> 2) * 2 + (bs & 1)) * 4 + (w & 3);
+    }
 };
 
 // Storage position of index x under the 32-group permutation described above.
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
             for (int i = 0; i < 4; ++i) leafP[i] += (og + i == tl) ? accD[i] : 0.f;
         }
         store4(gMD + size_t(bt) * 256 + tl * 16 + og, leafM);
-        store4(gP + size_t(SL::tri(bt, bt)) * 256 + tl * 16 + og, leafP);
+        store4(gP + SL::blk(bt, bt, tl * 16 + og), leafP);
         if (bt == 0) continue;
 
         // Off-diagonal blocks (bt, bs), bs < bt, pivot at the start of block bt:
@@ -375,8 +384,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
                 accM = MM::mma(fb, fAk[kk], accM);
                 accP = MM::mma(fb, fAq[kk], accP);
             }
-            store4(gM + size_t(SL::tri(bt, bs)) * 256 + tl * 16 + og, accM);
-            store4(gP + size_t(SL::tri(bt, bs)) * 256 + tl * 16 + og, accP);
+            store4(gM + SL::blk(bt, bs, tl * 16 + og), accM);
+            store4(gP + SL::blk(bt, bs, tl * 16 + og), accP);
         }
     }
 }
@@ -428,6 +437,8 @@ template <> struct Frag<bf16_t> {
     static __device__ __forceinline__ f8 cat(f4 a, f4 b) {
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    static __device__ __forceinline__ f4 lo(f8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+    static __device__ __forceinline__ f4 hi(f8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
     static __device__ __forceinline__ f4 pack(f32x4_t v) {
         u16x4_t u;
 #pragma unroll
@@ -471,6 +482,8 @@ template <> struct Frag<float> {
         return {buf_load_f4(r, voff, soff), buf_load_f4(r, voff + 16, soff)};
     }
     static __device__ __forceinline__ f8 cat(f4 a, f4 b) { return {a, b}; }
+    static __device__ __forceinline__ f4 lo(f8 v) { return v.lo; }
+    static __device__ __forceinline__ f4 hi(f8 v) { return v.hi; }
     static __device__ __forceinline__ f4 pack(f32x4_t v) { return v; }
     static __device__ __forceinline__ f4 unit(int n, int g) {
         f32x4_t u;
@@ -862,7 +875,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 lp += sh_dg[((hb * NG + c) * 2 + 1) * 64 + lane];
             }
             *reinterpret_cast<f32x4_t *>(gMD + size_t(bt) * 256 + blk_lo) = lm;
-            store4(gP + size_t(SL::tri(bt, bt)) * 256 + blk_lo, lp);
+            store4(gP + SL::blk(bt, bt, blk_lo), lp);
         }
         // Off-diagonal blocks of the pair: (2p, bs < 2p) then (2p + 1, bs <= 2p), dealt to
         // the wavefronts in turn. Rows s: K*sigma of block bs times the decay of the whole
@@ -902,8 +915,8 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                     am = F::mma8(fb, ka[kk], am);
                     ap = F::mma8(fb, qa[kk], ap);
                 }
-                store4(gM + size_t(SL::tri(bto, bs)) * 256 + blk_lo, am);
-                store4(gP + size_t(SL::tri(bto, bs)) * 256 + blk_lo, ap);
+                store4(gM + SL::blk(bto, bs, blk_lo), am);
+                store4(gP + SL::blk(bto, bs, blk_lo), ap);
             };
             for (int n = wave; n < 2 * p; n += NW)
                 block(2 * p, n, ak[0], aq[0], std::integral_constant<int, 0>{});
@@ -999,7 +1012,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
     // Per-lane byte offsets (each load adds one to a uniform base and offset).
     constexpr unsigned OB = sizeof(OpT);
-    const unsigned lo_blk = unsigned(x * 16 + 4 * g) * OB;  // 16x16 block, row x, cols 4g..
+    const unsigned lo_pair = unsigned((4 * x + g) * 8) * OB;  // block pair: row x, cols 4g..
     const unsigned lo_frag = unsigned(lane * 8) * OB;        // lane's share of an operand fragment
     const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
     const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
@@ -1021,22 +1034,24 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         for (int kk = 0; kk < NKD; ++kk)
             dst[kk] = F::bload8(rws, lo_frag, wsoff(ci, OFF + frag_idx(16 * L, 32 * kk, D) * OB));
     };
-    auto load_blk = [&](int ci, size_t OFF, int bt, int bs) {
-        return F::bload4(rws, lo_blk, wsoff(ci, OFF + SL::tri(bt, bs) * 256 * OB));
+    // Blocks (bt, 2j) and (bt, 2j + 1) of M or P as one K = 32 operand.
+    auto load_pair = [&](int ci, size_t OFF, int bt, int j) {
+        return F::bload8(rws, lo_pair, wsoff(ci, OFF + size_t(SL::prow(bt) + j) * 512 * OB));
     };
 
     if (wave == 1) {
         // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
         const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * unsigned(sizeof(QT)));
-        // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L}, loaded one leaf ahead.
+        // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L} in block pairs, loaded
+        // one leaf ahead.
         struct RWin {
             f8 qg[NKD];
-            f4 prow[NB];
+            f8 pq[NB / 2];
         };
         auto load_rwin = [&](int ci, int L, RWin &wn) {
             load_kg(ci, L, SL::QG_OFF, wn.qg);
 #pragma unroll
-            for (int l = 0; l <= L; ++l) wn.prow[l] = load_blk(ci, SL::P_OFF, L, l);
+            for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
         };
         RWin rw[2];
         load_rwin(0, 0, rw[0]);
@@ -1096,8 +1111,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                         ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
 #pragma unroll
                     for (int l = 0; l <= L; l += 2) {
-                        if (l + 1 <= L) ro = F::mma8(F::cat(Uh[l], Uh[l + 1]), F::cat(cw.prow[l], cw.prow[l + 1]), ro);
-                        else ro = F::mma4(Uh[l], cw.prow[l], ro);
+                        if (l + 1 <= L) ro = F::mma8(F::cat(Uh[l], Uh[l + 1]), cw.pq[l / 2], ro);
+                        else ro = F::mma4(Uh[l], F::lo(cw.pq[l / 2]), ro);
                     }
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
@@ -1141,20 +1156,20 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
     // Matrix-core operands of leaf L's window, loaded at the start of leaf L - 1:
     //   kg    (K*gamma) of leaf L + 1 (for its H), or of leaf 0 of the next chunk
-    //   mrow  M_{L+1,l} (l < L) and mnext = M_{L+1,L}: the right-hand side of leaf L + 1
+    //   mp    M_{L+1,l} (l <= L) in block pairs: the right-hand side of leaf L + 1
     //   kbt   (K*beta)^T of leaf pair (L-2, L-1) for half of the state tiles, pivoted
     //         at the pair's end
     struct Win {
         f8 kg[NKD], kbt[HALF];
-        f4 mrow[NB], mnext;
+        f8 mp[NB / 2];
     };
     auto load_win = [&](int ci, int L, Win &wn) {
         if (L + 1 < NB) load_kg(ci, L + 1, SL::KG_OFF, wn.kg);
         else load_kg(ci + 1, 0, SL::KG_OFF, wn.kg);
+        if (L + 1 < NB) {
 #pragma unroll
-        for (int l = 0; l < L; ++l)
-            if (L + 1 < NB) wn.mrow[l] = load_blk(ci, SL::M_OFF, L + 1, l);
-        wn.mnext = load_blk(ci, SL::M_OFF, L + 1 < NB ? L + 1 : L, L);
+            for (int j = 0; j <= L / 2; ++j) wn.mp[j] = load_pair(ci, SL::M_OFF, L + 1, j);
+        }
         if (L >= 2) {
 #pragma unroll
             for (int c = 0; c < HALF; ++c) wn.kbt[c] = load_kbt(ci, (L - 2) / 2, c + (L & 1) * HALF);
@@ -1207,7 +1222,12 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
 
                 // ---- serial path: last M term and right-hand side ----
-                if constexpr (L > 0) acc = F::mma4(Uh[L - 1], win[(L - 1) & 1].mnext, acc);
+                if constexpr (L > 0) {
+                    // M_{L,L-1}: half (L - 1) mod 2 of pair (L - 1) / 2 of the window loaded
+                    // for leaf L - 1.
+                    const f8 mpair = win[(L - 1) & 1].mp[(L - 1) / 2];
+                    acc = F::mma4(Uh[L - 1], ((L - 1) & 1) ? F::hi(mpair) : F::lo(mpair), acc);
+                }
                 load_win(ciN, LN, nw);
                 // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
                 float ne[4];
@@ -1247,8 +1267,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 if constexpr (more) {
 #pragma unroll
                     for (int l = 0; l < L; l += 2) {
-                        if (l + 1 < L) accN = F::mma8(F::cat(Uh[l], Uh[l + 1]), F::cat(cw.mrow[l], cw.mrow[l + 1]), accN);
-                        else accN = F::mma4(Uh[l], cw.mrow[l], accN);
+                        if (l + 1 < L) accN = F::mma8(F::cat(Uh[l], Uh[l + 1]), cw.mp[l / 2], accN);
+                        else accN = F::mma4(Uh[l], F::lo(cw.mp[l / 2]), accN);
                     }
                 }
                 if constexpr (L >= 2) {
