@@ -81,11 +81,14 @@ def to_dev(inp, dev):
         dev, qdt if n in ("q", "k", "v") else torch.float32) for n in NAMES}
 
 
-def time_chunk(inp, chunk, dev, steps, warmup):
-    """Time `steps` chunk forwards; returns dict of per-step and per-kernel times (ms)."""
+def time_chunk(inp, chunk, dev, steps, warmup, og=None):
+    """Time `steps` chunk forwards; returns dict of per-step and per-kernel times (ms).
+    With `og` (a numpy [B,T,H,dv] array) the scan runs the output-gate epilogue."""
+    import numpy as np
     import torch
     import gated_delta_rule_06_amd as muir
     t = to_dev(inp, dev)
+    og_t = None if og is None else torch.from_numpy(np.ascontiguousarray(og)).to(dev)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
     code = muir.MUIR_BF16 if inp["qkv"] == "bf16" else muir.MUIR_F32
     ws = torch.empty(muir.chunk_fwd_workspace_size(B, T, H, d, d, chunk, code),
@@ -100,7 +103,7 @@ def time_chunk(inp, chunk, dev, steps, warmup):
         if ev is not None:
             ev[1].record()
         muir.chunk_fwd_scan(t["v"], t["e"], t["w"], None, chunk=chunk, workspace=ws, o=o,
-                            s_out=s_out)
+                            s_out=s_out, og=og_t)
         if ev is not None:
             ev[2].record()
 
@@ -255,6 +258,15 @@ def main():
                               "avg_ms": dom_ms}
         result["phases_ms"] = {"prepare": r["prepare_ms"], "scan": r["scan_ms"]}
         result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"]}
+        # The same call with the output-gate epilogue fused into the readout.
+        og = workloads.output_gate(1, 32768, 16, 128, seed=3)
+        rg = time_chunk(main_inp, 256, dev, args.steps, args.warmup, og=og)
+        del og
+        secondary["long_context_output_gate"] = {
+            "workload": name + " + output-gate epilogue (og fp32)",
+            "tokens_per_s_per_layer": 32768 / (rg["ms_per_step"] * 1e-3),
+            "ms_per_call": rg["ms_per_step"], "prepare_ms": rg["prepare_ms"],
+            "scan_ms": rg["scan_ms"]}
     if args.only in ("all", "t4k"):
         inp = workloads.chunk_inputs(2)
         for chunk in (128, 256):

@@ -57,6 +57,10 @@ def lib():
         L.muir_chunk_fwd_prepare.restype = i
         L.muir_chunk_fwd_scan.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd_scan.restype = i
+        L.muir_chunk_fwd_gated.argtypes = [vp] * 12 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_gated.restype = i
+        L.muir_chunk_fwd_scan_gated.argtypes = [vp] * 7 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_scan_gated.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
         L.muir_decode_step.restype = i
         L.muir_status_string.argtypes = [i]
@@ -128,7 +132,7 @@ def chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, chunk: in
 
 
 def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out=None,
-              return_state: bool = True, workspace=None):
+              return_state: bool = True, workspace=None, og=None):
     """Chunkwise forward over whole sequences (``muir_chunk_fwd``).
 
     q, k [B,T,H,dk] and v [B,T,H,dv] in float32 or bfloat16 (same dtype); a, g
@@ -136,6 +140,8 @@ def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out
     Returns (o, s_out): o [B,T,H,dv] in the q/k/v dtype and the final state (or None
     with ``return_state=False``). ``s_out`` may be passed (it may be ``s0`` itself for
     an in-place update); ``workspace`` may be a pre-allocated uint8 device tensor.
+    With ``og`` ([B,T,H,dv] float32) the output-gate epilogue runs
+    (``muir_chunk_fwd_gated``): o is multiplied by og elementwise as it is stored.
     """
     import torch
     B, T, H, dk = q.shape
@@ -162,10 +168,17 @@ def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _require(workspace, "workspace", torch.uint8, None, dev)
-    status = lib().muir_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(r), _ptr(s0),
-        _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, code, _ptr(workspace),
-        workspace.numel(), _stream(dev))
+    if og is None:
+        status = lib().muir_chunk_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(r), _ptr(s0),
+            _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, code, _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    else:
+        _require(og, "og", torch.float32, (B, T, H, dv), dev)
+        status = lib().muir_chunk_fwd_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(og), _ptr(r),
+            _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, code, _ptr(workspace),
+            workspace.numel(), _stream(dev))
     _check(status)
     return o, s_out
 
@@ -187,8 +200,9 @@ def chunk_fwd_prepare(q, k, a, g, r, *, chunk: int, workspace):
         _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
-def chunk_fwd_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None):
-    """Sequential phase of the chunk forward (``muir_chunk_fwd_scan``) from ``workspace``."""
+def chunk_fwd_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None, og=None):
+    """Sequential phase of the chunk forward (``muir_chunk_fwd_scan``) from ``workspace``;
+    with ``og`` the output-gate epilogue (``muir_chunk_fwd_scan_gated``)."""
     import torch
     B, T, H, dv = v.shape
     dev = v.device
@@ -201,9 +215,15 @@ def chunk_fwd_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None):
     if s_out is not None:
         _require(s_out, "s_out", torch.float32, (B, H, dv, dv), dev)
     _require(workspace, "workspace", torch.uint8, None, dev)
-    _check(lib().muir_chunk_fwd_scan(
-        _ptr(v), _ptr(e), _ptr(w), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dv, dv, chunk,
-        code, _ptr(workspace), workspace.numel(), _stream(dev)))
+    if og is None:
+        _check(lib().muir_chunk_fwd_scan(
+            _ptr(v), _ptr(e), _ptr(w), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dv, dv, chunk,
+            code, _ptr(workspace), workspace.numel(), _stream(dev)))
+    else:
+        _require(og, "og", torch.float32, (B, T, H, dv), dev)
+        _check(lib().muir_chunk_fwd_scan_gated(
+            _ptr(v), _ptr(e), _ptr(w), _ptr(og), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dv,
+            dv, chunk, code, _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

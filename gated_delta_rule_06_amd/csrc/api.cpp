@@ -104,14 +104,14 @@ namespace {
 struct ChunkCall {
     const char *fn;
     const void *q, *k, *v;
-    const float *a, *g, *e, *w, *r, *s0;
+    const float *a, *g, *e, *w, *og, *r, *s0;
     void *o;
     float *s_out;
     int B, T, H, dk, dv, chunk;
     muir_dtype_t qkv;
     const void *workspace;
     size_t workspace_bytes;
-    bool prep, scan;
+    bool prep, scan, gated;
 };
 
 muir_status_t validate(const ChunkCall &c) {
@@ -133,6 +133,7 @@ muir_status_t validate(const ChunkCall &c) {
         return fail(MUIR_ERR_NULL, "%s: q, k, a and g are required", fn);
     if (c.T > 0 && c.scan && (!c.v || !c.e || !c.w || !c.o))
         return fail(MUIR_ERR_NULL, "%s: v, e, w and o are required", fn);
+    if (c.T > 0 && c.gated && !c.og) return fail(MUIR_ERR_NULL, "%s: og is required", fn);
     if (c.prep && !c.r) return fail(MUIR_ERR_NULL, "%s: r is required", fn);
 
     const size_t es = c.qkv == MUIR_BF16 ? 2 : 4;
@@ -156,7 +157,7 @@ muir_status_t validate(const ChunkCall &c) {
         if (reinterpret_cast<uintptr_t>(c.workspace) % 256 != 0)
             return fail(MUIR_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
     }
-    const void *all[] = {c.q, c.k, c.v, c.a, c.g, c.e, c.w, c.r, c.s0, c.o, c.s_out};
+    const void *all[] = {c.q, c.k, c.v, c.a, c.g, c.e, c.w, c.og, c.r, c.s0, c.o, c.s_out};
     for (const void *p : all)
         if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
             return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
@@ -164,7 +165,8 @@ muir_status_t validate(const ChunkCall &c) {
     const Range inputs[] = {
         range("q", c.q, n_tok * es), range("k", c.k, n_tok * es), range("v", c.v, n_tok * es),
         range("a", c.a, n_tok * 4), range("g", c.g, n_tok * 4), range("e", c.e, n_tok * 4),
-        range("w", c.w, n_tok * 4), range("r", c.r, static_cast<size_t>(c.H) * c.dk * 4),
+        range("w", c.w, n_tok * 4), range("og", c.og, n_tok * 4),
+        range("r", c.r, static_cast<size_t>(c.H) * c.dk * 4),
         range("s0", c.s0, n_state * 4)};
     const Range ro = range("o", c.o, n_tok * es);
     const Range rs = range("s_out", c.s_out, n_state * 4);
@@ -180,6 +182,30 @@ muir_status_t validate(const ChunkCall &c) {
     return MUIR_OK;
 }
 
+muir_status_t chunk_scan_impl(const ChunkCall &c, muir_stream_t stream) {
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (c.T == 0 && !c.s_out) return ok();
+    return check_hip(muir::launch_chunk_scan(c.v, c.e, c.w, c.og, c.s0, c.o, c.s_out, c.B, c.T,
+                                             c.H, c.dk, c.chunk, c.qkv == MUIR_BF16,
+                                             c.workspace, static_cast<hipStream_t>(stream)),
+                     c.fn);
+}
+
+muir_status_t chunk_fwd_impl(const ChunkCall &c, muir_stream_t stream) {
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (c.T > 0) {
+        const muir_status_t sp = check_hip(
+            muir::launch_chunk_prepare(c.q, c.k, c.a, c.g, c.r, c.B, c.T, c.H, c.dk, c.chunk,
+                                       c.qkv == MUIR_BF16, const_cast<void *>(c.workspace),
+                                       static_cast<hipStream_t>(stream)),
+            c.fn);
+        if (sp != MUIR_OK) return sp;
+    }
+    return chunk_scan_impl(c, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,31 +215,31 @@ muir_status_t muir_chunk_fwd(const void *q, const void *k, const void *v, const 
                              const float *s0, void *o, float *s_out, int B, int T, int H,
                              int dk, int dv, int chunk, muir_dtype_t qkv, void *workspace,
                              size_t workspace_bytes, muir_stream_t stream) {
-    const ChunkCall c{"chunk_fwd", q, k, v, a, g, e, w, r, s0, o, s_out, B, T, H, dk, dv, chunk,
-                      qkv, workspace, workspace_bytes, true, true};
-    const muir_status_t st = validate(c);
-    if (st != MUIR_OK) return st;
-    const bool bf16 = qkv == MUIR_BF16;
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (T > 0) {
-        const muir_status_t sp = check_hip(
-            muir::launch_chunk_prepare(q, k, a, g, r, B, T, H, dk, chunk, bf16, workspace, hs),
-            "chunk_fwd prepare launch");
-        if (sp != MUIR_OK) return sp;
-    }
-    if (T == 0 && !s_out) return ok();
-    return check_hip(muir::launch_chunk_scan(v, e, w, s0, o, s_out, B, T, H, dk, chunk, bf16,
-                                             workspace, hs),
-                     "chunk_fwd scan launch");
+    return chunk_fwd_impl(ChunkCall{"chunk_fwd", q, k, v, a, g, e, w, nullptr, r, s0, o, s_out,
+                                    B, T, H, dk, dv, chunk, qkv, workspace, workspace_bytes,
+                                    true, true, false},
+                          stream);
+}
+
+muir_status_t muir_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *a,
+                                   const float *g, const float *e, const float *w,
+                                   const float *og, const float *r, const float *s0, void *o,
+                                   float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+                                   muir_dtype_t qkv, void *workspace, size_t workspace_bytes,
+                                   muir_stream_t stream) {
+    return chunk_fwd_impl(ChunkCall{"chunk_fwd_gated", q, k, v, a, g, e, w, og, r, s0, o, s_out,
+                                    B, T, H, dk, dv, chunk, qkv, workspace, workspace_bytes,
+                                    true, true, true},
+                          stream);
 }
 
 muir_status_t muir_chunk_fwd_prepare(const void *q, const void *k, const float *a,
                                      const float *g, const float *r, int B, int T, int H, int dk,
                                      int chunk, muir_dtype_t qkv, void *workspace,
                                      size_t workspace_bytes, muir_stream_t stream) {
-    const ChunkCall c{"chunk_fwd_prepare", q, k, nullptr, a, g, nullptr, nullptr, r, nullptr,
-                      nullptr, nullptr, B, T, H, dk, dk, chunk, qkv, workspace, workspace_bytes,
-                      true, false};
+    const ChunkCall c{"chunk_fwd_prepare", q, k, nullptr, a, g, nullptr, nullptr, nullptr, r,
+                      nullptr, nullptr, nullptr, B, T, H, dk, dk, chunk, qkv, workspace,
+                      workspace_bytes, true, false, false};
     const muir_status_t st = validate(c);
     if (st != MUIR_OK) return st;
     if (T == 0) return ok();
@@ -227,16 +253,21 @@ muir_status_t muir_chunk_fwd_scan(const void *v, const float *e, const float *w,
                                   void *o, float *s_out, int B, int T, int H, int dk, int dv,
                                   int chunk, muir_dtype_t qkv, const void *workspace,
                                   size_t workspace_bytes, muir_stream_t stream) {
-    const ChunkCall c{"chunk_fwd_scan", nullptr, nullptr, v, nullptr, nullptr, e, w, nullptr, s0,
-                      o, s_out, B, T, H, dk, dv, chunk, qkv, workspace, workspace_bytes, false,
-                      true};
-    const muir_status_t st = validate(c);
-    if (st != MUIR_OK) return st;
-    if (T == 0 && !s_out) return ok();
-    return check_hip(muir::launch_chunk_scan(v, e, w, s0, o, s_out, B, T, H, dk, chunk,
-                                             qkv == MUIR_BF16, workspace,
-                                             static_cast<hipStream_t>(stream)),
-                     "chunk_fwd_scan launch");
+    return chunk_scan_impl(ChunkCall{"chunk_fwd_scan", nullptr, nullptr, v, nullptr, nullptr, e,
+                                     w, nullptr, nullptr, s0, o, s_out, B, T, H, dk, dv, chunk,
+                                     qkv, workspace, workspace_bytes, false, true, false},
+                           stream);
+}
+
+muir_status_t muir_chunk_fwd_scan_gated(const void *v, const float *e, const float *w,
+                                        const float *og, const float *s0, void *o, float *s_out,
+                                        int B, int T, int H, int dk, int dv, int chunk,
+                                        muir_dtype_t qkv, const void *workspace,
+                                        size_t workspace_bytes, muir_stream_t stream) {
+    return chunk_scan_impl(ChunkCall{"chunk_fwd_scan_gated", nullptr, nullptr, v, nullptr,
+                                     nullptr, e, w, og, nullptr, s0, o, s_out, B, T, H, dk, dv,
+                                     chunk, qkv, workspace, workspace_bytes, false, true, true},
+                           stream);
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

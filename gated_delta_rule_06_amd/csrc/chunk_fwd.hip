@@ -958,11 +958,15 @@ template <typename QT> struct LeafIn {
 // are tokens. U is kept as an operand with rows = value columns and values = tokens
 // 4g..4g+3 of the leaf; an mma4 against the identity turns a row-layout u into it. The
 // state is kept as accumulators with rows = channels, columns = value columns.
-template <typename QT, typename OpT, int D, int C>
+//
+// GATED: the output-gate epilogue, o <- o * og elementwise with og [B, T, H, dv] fp32 (the
+// output gate of the pages' gate table, applied as the readout is stored).
+template <typename QT, typename OpT, int D, int C, bool GATED>
 __global__ __launch_bounds__(128) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
-    const float *__restrict__ s0, QT *__restrict__ o, float *__restrict__ s_out,
-    const unsigned char *__restrict__ ws, int T, int H, int BH, int nchunks) {
+    const float *__restrict__ og, const float *__restrict__ s0, QT *__restrict__ o,
+    float *__restrict__ s_out, const unsigned char *__restrict__ ws, int T, int H, int BH,
+    int nchunks) {
     using SL = Slot<OpT, D, C>;
     using F = Frag<OpT>;
     using f4 = typename F::f4;
@@ -1042,16 +1046,19 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     if (wave == 1) {
         // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
         const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * unsigned(sizeof(QT)));
-        // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L} in block pairs, loaded
-        // one leaf ahead.
+        const rsrc_t rog = make_rsrc(GATED ? og + tok0 : nullptr, GATED ? tok_elems * 4u : 0u);
+        // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L} in block pairs (and the
+        // output gate rows), loaded one leaf ahead.
         struct RWin {
             f8 qg[NKD];
             f8 pq[NB / 2];
+            f32x4_t og;
         };
         auto load_rwin = [&](int ci, int L, RWin &wn) {
             load_kg(ci, L, SL::QG_OFF, wn.qg);
 #pragma unroll
             for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
+            if constexpr (GATED) wn.og = buf_load_f4(rog, lo_f, trow(ci * C + 16 * L, 4u));
         };
         RWin rw[2];
         load_rwin(0, 0, rw[0]);
@@ -1114,6 +1121,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                         if (l + 1 <= L) ro = F::mma8(F::cat(Uh[l], Uh[l + 1]), cw.pq[l / 2], ro);
                         else ro = F::mma4(Uh[l], F::lo(cw.pq[l / 2]), ro);
                     }
+                    if constexpr (GATED) ro *= cw.og;
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
             }
@@ -1355,15 +1363,21 @@ hipError_t prepare_typed(const void *q, const void *k, const float *a, const flo
 }
 
 template <typename QT, typename OpT, int D, int C>
-hipError_t scan_typed(const void *v, const float *e, const float *w, const float *s0, void *o,
-                      float *s_out, int B, int T, int H, const void *workspace,
-                      hipStream_t stream) {
+hipError_t scan_typed(const void *v, const float *e, const float *w, const float *og,
+                      const float *s0, void *o, float *s_out, int B, int T, int H,
+                      const void *workspace, hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
     const int BH = B * H;
     const int groups = (BH + 7) / 8;
-    hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C>), dim3(groups * 8 * (D / 16)), dim3(128), 0,
-                       stream, static_cast<const QT *>(v), e, w, s0, static_cast<QT *>(o), s_out,
-                       static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+    const dim3 grid(groups * 8 * (D / 16));
+    if (og)
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true>), grid, dim3(128), 0, stream,
+                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
+                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false>), grid, dim3(128), 0, stream,
+                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
+                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
     return hipGetLastError();
 }
 
@@ -1392,15 +1406,15 @@ hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, co
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *s0,
-                             void *o, float *s_out, int B, int T, int H, int d, int chunk,
-                             bool bf16, const void *workspace, hipStream_t stream) {
+hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,
+                             const float *s0, void *o, float *s_out, int B, int T, int H, int d,
+                             int chunk, bool bf16, const void *workspace, hipStream_t stream) {
 #define MUIR_SCAN(D, C)                                                                        \
     if (d == D && chunk == C)                                                                  \
-        return bf16 ? scan_typed<bf16_t, bf16_t, D, C>(v, e, w, s0, o, s_out, B, T, H,          \
+        return bf16 ? scan_typed<bf16_t, bf16_t, D, C>(v, e, w, og, s0, o, s_out, B, T, H,      \
                                                        workspace, stream)                      \
-                    : scan_typed<float, float, D, C>(v, e, w, s0, o, s_out, B, T, H, workspace, \
-                                                     stream);
+                    : scan_typed<float, float, D, C>(v, e, w, og, s0, o, s_out, B, T, H,        \
+                                                     workspace, stream);
     MUIR_SCAN(64, 64) MUIR_SCAN(64, 128) MUIR_SCAN(64, 256)
     MUIR_SCAN(128, 64) MUIR_SCAN(128, 128) MUIR_SCAN(128, 256)
 #undef MUIR_SCAN

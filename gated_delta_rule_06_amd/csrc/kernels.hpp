@@ -20,9 +20,10 @@ hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, co
                                 const float *r, int B, int T, int H, int d, int chunk, bool bf16,
                                 void *workspace, hipStream_t stream);
 
-// Phase S: sequential chunk scan (solve, readout, state carry) from the workspace.
-hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *s0,
-                             void *o, float *s_out, int B, int T, int H, int d, int chunk,
-                             bool bf16, const void *workspace, hipStream_t stream);
+// Phase S: sequential chunk scan (solve, readout, state carry) from the workspace. A
+// non-null og applies the output-gate epilogue o <- o * og.
+hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,
+                             const float *s0, void *o, float *s_out, int B, int T, int H, int d,
+                             int chunk, bool bf16, const void *workspace, hipStream_t stream);
 
 }  // namespace muir

@@ -147,6 +147,31 @@ muir_status_t muir_chunk_fwd_scan(
     const void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
+ * The chunk forward with the output-gate epilogue fused into the readout: the stored
+ * output is o_t * og_t elementwise, og_t being the output gate that sets how much of
+ * the state's readout reaches the network (openai-hub page, section on
+ * sensitivity-allocated gating, gate table: the output gate, rank 128).
+ *
+ *   og: [B, T, H, dv] fp32, the gate values themselves (already through their
+ *       activation, like e, w and g), caller-owned device buffer, 16-byte aligned,
+ *       required when T > 0, must not overlap o, s_out or the workspace.
+ * Everything else is exactly as for muir_chunk_fwd / muir_chunk_fwd_scan; the state and
+ * s_out are unaffected by og. Errors as for those calls, plus MUIR_ERR_NULL for a
+ * missing og.
+ */
+muir_status_t muir_chunk_fwd_gated(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *og,
+    const float *r, const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+muir_status_t muir_chunk_fwd_scan_gated(
+    const void *v, const float *e, const float *w, const float *og, const float *s0,
+    void *o, float *s_out, int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
  * One recurrent step per (batch, head), updating the state in place (decode).
  * Constant-memory inference against the fixed state (Muir abstract, "Full text";
  * openai-hub page, opening section: the history lives in a fixed 2-D state, so

@@ -94,6 +94,42 @@ def test_chunk_fwd_rejects_bad_arguments(over, status):
     assert msg
 
 
+def _gated_call(**over):
+    lib = muir.lib()
+    args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),
+                og=fake(12), r=fake(7), s0=fake(8), o=fake(9), s_out=fake(10), B=2, T=100, H=3,
+                dk=64, dv=64, chunk=64, qkv=muir.MUIR_BF16, ws=fake(11),
+                wsb=muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16),
+                stream=None)
+    args.update(over)
+    st = lib.muir_chunk_fwd_gated(args["q"], args["k"], args["v"], args["a"], args["g"],
+                                  args["e"], args["w"], args["og"], args["r"], args["s0"],
+                                  args["o"], args["s_out"], args["B"], args["T"], args["H"],
+                                  args["dk"], args["dv"], args["chunk"], args["qkv"], args["ws"],
+                                  args["wsb"], args["stream"])
+    return st, muir.last_error()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(og=None), 1), (dict(og=ctypes.c_void_p(BASE + 12 * STRIDE + 8)), 2),
+    (dict(o=fake(12)), 5), (dict(ws=fake(12)), 5), (dict(s_out=fake(12)), 5),
+    (dict(chunk=48), 3), (dict(q=None), 1),
+])
+def test_chunk_fwd_gated_rejects_bad_arguments(over, status):
+    st, msg = _gated_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_scan_gated_requires_the_gate():
+    lib = muir.lib()
+    st = lib.muir_chunk_fwd_scan_gated(fake(2), fake(5), fake(6), None, None, fake(9), None, 2,
+                                       100, 3, 64, 64, 64, muir.MUIR_BF16, fake(11),
+                                       muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64,
+                                                                     muir.MUIR_BF16), None)
+    assert st == 1 and "og" in muir.last_error()
+
+
 def _decode_call(**over):
     lib = muir.lib()
     args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),

@@ -217,6 +217,13 @@ def chunk_inputs(cfg: ChunkConfig | int, *, B=None, T=None, H=None, d=None,
 # on the device with a torch generator seeded from (4, step).
 # ----------------------------------------------------------------------------
 
+def output_gate(B: int, T: int, H: int, d: int, seed: int) -> np.ndarray:
+    """Output-gate values og = sigmoid(N(0,1)) [B,T,H,d] float32, like e, w and g, from a
+    stream of their own (``SeedSequence((seed, 10))``), so the other inputs of the same
+    seed are unchanged."""
+    return _sigmoid(_normal(np.random.SeedSequence((seed, 10)), (B, T, H, d)))
+
+
 def decode_base(cfg: DecodeConfig = DECODE_CONFIG, *, L=None, H=None, d=None):
     """Base log-rate u [L,H,d] (float64) and row scale r [L,H,d] (float32)."""
     L = cfg.L if L is None else L
