@@ -877,13 +877,11 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
             *reinterpret_cast<f32x4_t *>(gMD + size_t(bt) * 256 + blk_lo) = lm;
             store4(gP + SL::blk(bt, bt, blk_lo), lp);
         }
-        // Off-diagonal blocks of the pair: (2p, bs < 2p) then (2p + 1, bs <= 2p), dealt to
-        // the wavefronts in turn. Rows s: K*sigma of block bs times the decay of the whole
-        // blocks between bs and bt; columns t: K*pi (Qh*pi) of block bt. Three cases, each
-        // its own loop: bt = 2p (decay F[bs]), bt = 2p + 1 and bs < 2p (F[bs] times the
-        // decay of block 2p), and (2p + 1, 2p) (no decay in between).
-        const int nblk = 4 * p + 1;
-        if (wave < nblk) {
+        // Off-diagonal blocks of the pair: (2p, bs < 2p) and (2p + 1, bs <= 2p). Rows s:
+        // K*sigma of block bs times the decay of the whole blocks between bs and bt;
+        // columns t: K*pi (Qh*pi) of block bt. The two blocks of one bs < 2p are done
+        // together by one wavefront, bs dealt to the wavefronts in turn.
+        if (wave < 2 * p + 1) {
             f8 ak[2][NG], aq[2][NG];
             float pb0[NG][8];  // decay of block 2p at the operand positions of this lane
 #pragma unroll
@@ -895,35 +893,45 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 }
                 ld8f(sh_pi + (2 * p) * D + 32 * kk + 8 * G, pb0[kk]);
             }
-            auto block = [&](int bto, int bs, const f8 (&ka)[NG], const f8 (&qa)[NG], auto mode) {
-                constexpr int MODE = decltype(mode)::value;
-                f32x4_t am = zero4(), ap = zero4();
+            // Both blocks (2p, bs) and (2p + 1, bs) from one read of block bs's K*sigma:
+            // decay F[bs] for the even row, F[bs] times the decay of block 2p for the odd.
+            auto block_pair = [&](int bs) {
+                f32x4_t am0 = zero4(), ap0 = zero4(), am1 = zero4(), ap1 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < NG; ++kk) {
                     const f8 xb = *reinterpret_cast<const f8 *>(sh_bb + swz<D>(16 * bs + t, 4 * kk + G));
-                    f8 fb = xb;
-                    if constexpr (MODE != 2) {
-                        float dm[8], x[8];
-                        ld8f(sh_ft + bs * D + 32 * kk + 8 * G, dm);
+                    float dm[8], x0[8], x1[8];
+                    ld8f(sh_ft + bs * D + 32 * kk + 8 * G, dm);
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float d = MODE == 1 ? dm[j] * pb0[kk][j] : dm[j];
-                            x[j] = bf16_to_f32(xb[j]) * d;
-                        }
-                        fb = pack8(x);
+                    for (int j = 0; j < 8; ++j) {
+                        x0[j] = bf16_to_f32(xb[j]) * dm[j];
+                        x1[j] = x0[j] * pb0[kk][j];
                     }
-                    am = F::mma8(fb, ka[kk], am);
-                    ap = F::mma8(fb, qa[kk], ap);
+                    const f8 fb0 = pack8(x0), fb1 = pack8(x1);
+                    am0 = F::mma8(fb0, ak[0][kk], am0);
+                    ap0 = F::mma8(fb0, aq[0][kk], ap0);
+                    am1 = F::mma8(fb1, ak[1][kk], am1);
+                    ap1 = F::mma8(fb1, aq[1][kk], ap1);
                 }
-                store4(gM + SL::blk(bto, bs, blk_lo), am);
-                store4(gP + SL::blk(bto, bs, blk_lo), ap);
+                store4(gM + SL::blk(2 * p, bs, blk_lo), am0);
+                store4(gP + SL::blk(2 * p, bs, blk_lo), ap0);
+                store4(gM + SL::blk(2 * p + 1, bs, blk_lo), am1);
+                store4(gP + SL::blk(2 * p + 1, bs, blk_lo), ap1);
             };
-            for (int n = wave; n < 2 * p; n += NW)
-                block(2 * p, n, ak[0], aq[0], std::integral_constant<int, 0>{});
-            for (int n = 2 * p + ((wave - 2 * p) % NW + NW) % NW; n < 4 * p; n += NW)
-                block(2 * p + 1, n - 2 * p, ak[1], aq[1], std::integral_constant<int, 1>{});
-            if (4 * p % NW == wave)
-                block(2 * p + 1, 2 * p, ak[1], aq[1], std::integral_constant<int, 2>{});
+            // Block (2p + 1, 2p): no whole block in between.
+            auto block_adjacent = [&]() {
+                f32x4_t am = zero4(), ap = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NG; ++kk) {
+                    const f8 xb = *reinterpret_cast<const f8 *>(sh_bb + swz<D>(16 * (2 * p) + t, 4 * kk + G));
+                    am = F::mma8(xb, ak[1][kk], am);
+                    ap = F::mma8(xb, aq[1][kk], ap);
+                }
+                store4(gM + SL::blk(2 * p + 1, 2 * p, blk_lo), am);
+                store4(gP + SL::blk(2 * p + 1, 2 * p, blk_lo), ap);
+            };
+            for (int n = wave; n < 2 * p; n += NW) block_pair(n);
+            if (2 * p % NW == wave) block_adjacent();
         }
         lds_barrier();
     }
