@@ -19,8 +19,12 @@ LIB = os.path.join(PKG, "libmuir.so")
 SOURCES = ["api.cpp", "decode.hip", "chunk_fwd.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are kept out of every kernel.
-HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU instructions are kept out of every kernel. MFMA accumulators are kept
+# in ordinary VGPRs: the scan updates its fp32 state accumulators with vector
+# instructions between matrix-core products, and in AGPRs every such update costs a copy
+# out and back.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def hipcc() -> str:

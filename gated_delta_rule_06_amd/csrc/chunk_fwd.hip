@@ -987,7 +987,9 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     // Chunk hand-over from the chain to the readout wavefront, double-buffered by chunk
     // parity: S0 as operands and every leaf's U, both in the lane order of the operands.
     __shared__ f4 sh_fS[2][NCT][64];
-    __shared__ f4 sh_U[2][NB][64];
+    // U of every leaf of the chunk, interleaved by leaf pairs: leaves 2j and 2j + 1 of a
+    // lane are one 8-value K = 32 operand.
+    __shared__ f8 sh_U[2][NB / 2][64];
     // Decay of every leaf pair of a chunk, per channel, double-buffered by chunk parity;
     // staged by the readout wavefront one chunk ahead of the chain.
     constexpr int NP = NB / 2;
@@ -1008,6 +1010,11 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
     const size_t HD = size_t(H) * D;
     const unsigned lo_st = unsigned(4 * g * D + x);  // state [channel 4g][column x]
+    auto u_put = [&](int buf, int L, f4 u) {
+        reinterpret_cast<f4 *>(&sh_U[buf][L >> 1][lane])[L & 1] = u;
+    };
+    auto u_get = [&](int buf, int L) { return reinterpret_cast<const f4 *>(&sh_U[buf][L >> 1][lane])[L & 1]; };
+    auto u_pair = [&](int buf, int j) { return sh_U[buf][j][lane]; };
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
 
@@ -1113,21 +1120,21 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 f4 fS[NCT];
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) fS[c] = sh_fS[buf][c][lane];
-                f4 Uh[NB];
+
                 static_for<NB>([&](auto Lc) {
                     constexpr int L = decltype(Lc)::value;
                     RWin &cw = rw[L & 1];
                     // The next leaf's operands (the next chunk's first leaf after the last).
                     load_rwin(L + 1 < NB ? ci : ci + 1, (L + 1) % NB, rw[(L + 1) & 1]);
-                    Uh[L] = sh_U[buf][L][lane];
+
                     f32x4_t ro = zero4();
 #pragma unroll
                     for (int kk = 0; kk < NKD; ++kk)
                         ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
 #pragma unroll
                     for (int l = 0; l <= L; l += 2) {
-                        if (l + 1 <= L) ro = F::mma8(F::cat(Uh[l], Uh[l + 1]), cw.pq[l / 2], ro);
-                        else ro = F::mma4(Uh[l], F::lo(cw.pq[l / 2]), ro);
+                        if (l + 1 <= L) ro = F::mma8(u_pair(buf, l / 2), cw.pq[l / 2], ro);
+                        else ro = F::mma4(u_get(buf, l), F::lo(cw.pq[l / 2]), ro);
                     }
                     if constexpr (GATED) ro *= cw.og;
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
@@ -1223,7 +1230,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
 
-            f4 Uh[NB];
+            f4 Ulast = F::unit(x, g);  // U of the previous leaf (its pair-mate comes from LDS)
             static_for<NB>([&](auto Lc) {
                 constexpr int L = decltype(Lc)::value;
                 constexpr bool more = L + 1 < NB;
@@ -1242,7 +1249,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     // M_{L,L-1}: half (L - 1) mod 2 of pair (L - 1) / 2 of the window loaded
                     // for leaf L - 1.
                     const f8 mpair = win[(L - 1) & 1].mp[(L - 1) / 2];
-                    acc = F::mma4(Uh[L - 1], ((L - 1) & 1) ? F::hi(mpair) : F::lo(mpair), acc);
+                    acc = F::mma4(Ulast, ((L - 1) & 1) ? F::hi(mpair) : F::lo(mpair), acc);
                 }
                 load_win(ciN, LN, nw);
                 // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
@@ -1283,13 +1290,13 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 if constexpr (more) {
 #pragma unroll
                     for (int l = 0; l < L; l += 2) {
-                        if (l + 1 < L) accN = F::mma8(F::cat(Uh[l], Uh[l + 1]), cw.mp[l / 2], accN);
-                        else accN = F::mma4(Uh[l], F::lo(cw.mp[l / 2]), accN);
+                        if (l + 1 < L) accN = F::mma8(u_pair(buf, l / 2), cw.mp[l / 2], accN);
+                        else accN = F::mma4(l == L - 1 ? Ulast : u_get(buf, l), F::lo(cw.mp[l / 2]), accN);
                     }
                 }
                 if constexpr (L >= 2) {
                     constexpr int p0 = (L - 2) & ~1;
-                    const f8 u2 = F::cat(Uh[p0], Uh[p0 + 1]);
+                    const f8 u2 = u_pair(buf, p0 / 2);
 #pragma unroll
                     for (int c = 0; c < HALF; ++c) {
                         constexpr int off = (L & 1) * HALF;
@@ -1304,14 +1311,14 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 static_for<8>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
 
                 // ---- u -> U operand (transpose on the matrix cores), hand-over ----
-                Uh[L] = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
-                sh_U[buf][L][lane] = Uh[L];
+                Ulast = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
+                u_put(buf, L, Ulast);
                 if constexpr (more) acc = accN;
                 load_leaf(L + 2 < NB ? ci : ci + 1, (L + 2) % NB, cin);  // leaf L + 2
             });
             // Chunk end: the last leaf pair's share of the state.
             {
-                const f8 u2 = F::cat(Uh[NB - 2], Uh[NB - 1]);
+                const f8 u2 = F::cat(u_get(buf, NB - 2), Ulast);
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c] * lds_pp(ci, NP - 1, c));
             }
