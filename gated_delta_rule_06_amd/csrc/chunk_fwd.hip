@@ -337,6 +337,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
         }
         store4(gMD + size_t(bt) * 256 + tl * 16 + og, leafM);
         store4(gP + SL::blk(bt, bt, tl * 16 + og), leafP);
+        store4(gM + SL::blk(bt, bt, tl * 16 + og), zero4());
+        if ((bt & 1) == 0) store4(gP + SL::blk(bt, bt + 1, tl * 16 + og), zero4());
         if (bt == 0) continue;
 
         // Off-diagonal blocks (bt, bs), bs < bt, pivot at the start of block bt:
@@ -464,6 +466,11 @@ template <> struct Frag<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
+    // The 16x16x16 instruction itself, with no accumulator input: nothing to chain with.
+    static __device__ __forceinline__ f32x4_t mma16_fresh(f4 a, f4 b) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                         __builtin_bit_cast(s16x4_t, b), zero4(), 0, 0, 0);
+    }
 };
 template <> struct Frag<float> {
     using f4 = f32x4_t;
@@ -499,6 +506,7 @@ template <> struct Frag<float> {
     static __device__ __forceinline__ f32x4_t mma8(f8 a, f8 b, f32x4_t c) {
         return mma4(a.hi, b.hi, mma4(a.lo, b.lo, c));
     }
+    static __device__ __forceinline__ f32x4_t mma16_fresh(f4 a, f4 b) { return mma4(a, b, zero4()); }
 };
 
 // One step of the leaf's forward substitution for the four value columns a lane holds:
@@ -876,6 +884,11 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
             }
             *reinterpret_cast<f32x4_t *>(gMD + size_t(bt) * 256 + blk_lo) = lm;
             store4(gP + SL::blk(bt, bt, blk_lo), lp);
+            // The pair slots the scan reads whole: M's diagonal block (its products use
+            // the fp32 copy above) and, for even bt, P's block (bt, bt + 1) above the
+            // diagonal hold zeros.
+            store4(gM + SL::blk(bt, bt, blk_lo), zero4());
+            if ((bt & 1) == 0) store4(gP + SL::blk(bt, bt + 1, blk_lo), zero4());
         }
         // Off-diagonal blocks of the pair: (2p, bs < 2p) and (2p + 1, bs <= 2p). Rows s:
         // K*sigma of block bs times the decay of the whole blocks between bs and bt;
@@ -1013,7 +1026,6 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     auto u_put = [&](int buf, int L, f4 u) {
         reinterpret_cast<f4 *>(&sh_U[buf][L >> 1][lane])[L & 1] = u;
     };
-    auto u_get = [&](int buf, int L) { return reinterpret_cast<const f4 *>(&sh_U[buf][L >> 1][lane])[L & 1]; };
     auto u_pair = [&](int buf, int j) { return sh_U[buf][j][lane]; };
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
@@ -1133,8 +1145,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                         ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
 #pragma unroll
                     for (int l = 0; l <= L; l += 2) {
-                        if (l + 1 <= L) ro = F::mma8(u_pair(buf, l / 2), cw.pq[l / 2], ro);
-                        else ro = F::mma4(u_get(buf, l), F::lo(cw.pq[l / 2]), ro);
+                        ro = F::mma8(u_pair(buf, l / 2), cw.pq[l / 2], ro);
                     }
                     if constexpr (GATED) ro *= cw.og;
                     Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
@@ -1230,7 +1241,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
 
-            f4 Ulast = F::unit(x, g);  // U of the previous leaf (its pair-mate comes from LDS)
+            f4 Ulast = F::unit(x, g);  // U of the previous leaf
+            f4 Uprev = Ulast;          // and of the one before
             static_for<NB>([&](auto Lc) {
                 constexpr int L = decltype(Lc)::value;
                 constexpr bool more = L + 1 < NB;
@@ -1246,10 +1258,13 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
                 // ---- serial path: last M term and right-hand side ----
                 if constexpr (L > 0) {
-                    // M_{L,L-1}: half (L - 1) mod 2 of pair (L - 1) / 2 of the window loaded
-                    // for leaf L - 1.
+                    // The block pair of row L that holds M_{L,L-1}, from the window loaded for
+                    // leaf L - 1, as one K = 32 product: for even L it also carries
+                    // M_{L,L-2} U_{L-2} (left out of the precomputed part); for odd L its
+                    // second block is the diagonal block, which is stored as zeros.
                     const f8 mpair = win[(L - 1) & 1].mp[(L - 1) / 2];
-                    acc = F::mma4(Ulast, ((L - 1) & 1) ? F::hi(mpair) : F::lo(mpair), acc);
+                    if constexpr (L % 2 == 0) acc = F::mma8(F::cat(Uprev, Ulast), mpair, acc);
+                    else acc = F::mma8(F::cat(Ulast, Ulast), mpair, acc);
                 }
                 load_win(ciN, LN, nw);
                 // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
@@ -1288,11 +1303,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
                 // ---- window, part 2: earlier leaves' terms, state carry of a leaf pair ----
                 if constexpr (more) {
+                    // Earlier leaves in whole pairs; the pair holding leaf L - 1 (or L alone)
+                    // is the next leaf's serial product.
 #pragma unroll
-                    for (int l = 0; l < L; l += 2) {
-                        if (l + 1 < L) accN = F::mma8(u_pair(buf, l / 2), cw.mp[l / 2], accN);
-                        else accN = F::mma4(l == L - 1 ? Ulast : u_get(buf, l), F::lo(cw.mp[l / 2]), accN);
-                    }
+                    for (int j = 0; j < L / 2; ++j) accN = F::mma8(u_pair(buf, j), cw.mp[j], accN);
                 }
                 if constexpr (L >= 2) {
                     constexpr int p0 = (L - 2) & ~1;
@@ -1308,17 +1322,19 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
                 }
 
-                static_for<8>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
+                // Step 15 would update no token (M is strictly lower triangular): left out.
+                static_for<7>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
 
                 // ---- u -> U operand (transpose on the matrix cores), hand-over ----
-                Ulast = F::pack(F::mma4(F::pack(f32x4_t{x0, x1, x2, x3}), unit, zero4()));
+                Uprev = Ulast;
+                Ulast = F::pack(F::mma16_fresh(F::pack(f32x4_t{x0, x1, x2, x3}), unit));
                 u_put(buf, L, Ulast);
                 if constexpr (more) acc = accN;
                 load_leaf(L + 2 < NB ? ci : ci + 1, (L + 2) % NB, cin);  // leaf L + 2
             });
             // Chunk end: the last leaf pair's share of the state.
             {
-                const f8 u2 = F::cat(u_get(buf, NB - 2), Ulast);
+                const f8 u2 = F::cat(Uprev, Ulast);
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) S[c] = F::mma8(kbtLast[c], u2, S[c] * lds_pp(ci, NP - 1, c));
             }
