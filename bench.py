@@ -42,16 +42,25 @@ def algorithmic(d, chunk, qkv_bytes=2):
     }
 
 
-def code_sha(path):
-    """sha256 prefix of a C/HIP source with its comments and whitespace removed, so that
+CSRC = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc")
+# The sources of the channel-wise chunk kernels: the kernel file and the headers it includes.
+CHUNK_SOURCES = [os.path.join(CSRC, f) for f in
+                 ("chunk_fwd.hip", "chunk_layout.hpp", "mfma.hpp", "common.hpp")]
+
+
+def code_sha(*paths):
+    """sha256 prefix of C/HIP sources with their comments and whitespace removed, so that
     it changes with the code but not with its comments."""
     import hashlib
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = re.sub(r"\s+", "", text)
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", "", text)
+        h.update(text.encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel):
@@ -61,10 +70,9 @@ def measured_traffic(kernel):
     different code (its code_sha differs from the current source's)."""
     import re
     path = os.path.join(ROOT, "profiles", "chunk_fwd_long_context_hbm_counters.md")
-    src = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc", "chunk_fwd.hip")
     try:
         text = open(path).read()
-        sha = code_sha(src)
+        sha = code_sha(*CHUNK_SOURCES)
     except OSError:
         return None
     m = re.search(r"traffic sha=(\w+) prepare_bytes=(\d+) scan_bytes=(\d+)", text)
@@ -123,6 +131,54 @@ def time_chunk(inp, chunk, dev, steps, warmup, og=None):
     assert torch.isfinite(o.float()).all() and torch.isfinite(s_out).all()
     return {"ms_per_step": total / steps, "wall_ms_per_step": wall / steps,
             "prepare_ms": sum(prep) / steps, "scan_ms": sum(scan) / steps}
+
+
+def time_scalar_erase(inp, es, chunk, dev, steps, warmup):
+    """Time `steps` shared-erase forwards (e one value per token and head): the prepare,
+    the chunk-parallel inverse and the scan, each between HIP events on the stream."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_06_amd as muir
+    t = to_dev(inp, dev)
+    e_t = torch.from_numpy(np.ascontiguousarray(es)).to(dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    ws = torch.empty(muir.chunk_fwd_workspace_size(B, T, H, d, d, chunk, muir.MUIR_BF16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(t["v"])
+    s_out = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        muir.chunk_fwd_prepare(t["q"], t["k"], t["a"], t["g"], t["r"], chunk=chunk, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        muir.chunk_fwd_scalar_erase_solve(e_t, dk=d, chunk=chunk, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        muir.chunk_fwd_scalar_erase_scan(t["v"], e_t, t["w"], chunk=chunk, workspace=ws, o=o,
+                                         s_out=s_out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    phase = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / steps
+    total = evs[0][0].elapsed_time(evs[-1][3]) / steps
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s_out).all()
+    tok_heads = B * T * H
+    # Algorithmic bytes per token-head: q, k (bf16), a, g (fp32) | e (one fp32) | v (bf16),
+    # e, w (fp32), o (bf16).
+    nbytes = (2 * d * 2 + 2 * d * 4) + 4 + (d * 2 + 4 + d * 4 + d * 2)
+    sec = total * 1e-3
+    return {"tokens_per_s_per_layer": B * T / sec, "ms_per_call": total,
+            "prepare_ms": phase(0, 1), "solve_ms": phase(1, 2), "scan_ms": phase(2, 3),
+            "hbm_frac": nbytes * tok_heads / sec / HBM_PEAK}
 
 
 def chunk_report(name, inp, chunk, r):
@@ -198,7 +254,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "scalar", "copy"],
+                    default="all",
                     help="'copy' times a plain 1 GiB device copy: the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
@@ -280,6 +337,23 @@ def main():
             result["value"] = best["tokens_per_s_per_layer"]
             result["ms_per_step"] = best["ms_per_call"]
             result["config"] = {"workload": best["workload"]}
+    if args.only in ("all", "scalar"):
+        # The shared-erase variant (one erase strength per token and head), same inputs.
+        for cfg, chunk, key in ((3, 256, "long_context_scalar_erase"),
+                                (2, 128, "t4k_c128_scalar_erase")):
+            inp = main_inp if (cfg == 3 and main_inp is not None) else workloads.chunk_inputs(cfg)
+            es = workloads.scalar_erase(inp["B"], inp["T"], inp["H"], seed=cfg)
+            name = (f"chunk_fwd_scalar_erase B{inp['B']} H{inp['H']} d{inp['d']} T{inp['T']} "
+                    f"C{chunk} bf16, e [B,T,H]")
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            secondary[key] = {"workload": name, "chunk": chunk,
+                              **time_scalar_erase(inp, es, chunk, dev, args.steps, args.warmup)}
+            del inp, es
+        if "value" not in result:
+            first = secondary["long_context_scalar_erase"]
+            result["value"] = first["tokens_per_s_per_layer"]
+            result["ms_per_step"] = first["ms_per_call"]
+            result["config"] = {"workload": first["workload"]}
     if args.only in ("all", "decode"):
         print("bench: decode step B256 H16 d128", file=sys.stderr, flush=True)
         secondary["decode"] = time_decode(dev, max(50, args.steps * 10), args.warmup * 5)

@@ -112,6 +112,7 @@ struct ChunkCall {
     const void *workspace;
     size_t workspace_bytes;
     bool prep, scan, gated;
+    bool scalar_e = false;  // e is [B, T, H] (one erase strength per token): the WY path
 };
 
 muir_status_t validate(const ChunkCall &c) {
@@ -129,6 +130,8 @@ muir_status_t validate(const ChunkCall &c) {
     if (!supported_chunk(c.chunk))
         return fail(MUIR_ERR_UNSUPPORTED, "%s: chunk must be 64, 128 or 256 (got %d)", fn,
                     c.chunk);
+    if (c.scalar_e && c.qkv != MUIR_BF16)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: the shared-erase path needs bf16 q, k, v", fn);
     if (c.T > 0 && c.prep && (!c.q || !c.k || !c.a || !c.g))
         return fail(MUIR_ERR_NULL, "%s: q, k, a and g are required", fn);
     if (c.T > 0 && c.scan && (!c.v || !c.e || !c.w || !c.o))
@@ -144,10 +147,20 @@ muir_status_t validate(const ChunkCall &c) {
                             static_cast<size_t>(c.dk), static_cast<size_t>(c.dv)}) ||
         n_tok > SIZE_MAX / 4 || n_state > SIZE_MAX / 4)
         return fail(MUIR_ERR_SHAPE, "%s: sizes overflow", fn);
+    // The scan addresses one head's tokens and its workspace chunks with 32-bit offsets.
+    const size_t head_span = static_cast<size_t>(c.T) * c.H * c.dk * 4;
+    if (head_span > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED,
+                    "%s: T*H*dv*4 = %zu bytes exceeds 4 GiB; split the sequence over several "
+                    "calls, carrying the state through s0 / s_out", fn, head_span);
 
     const size_t need =
         muir::chunk_workspace_bytes(c.B, c.T, c.H, c.dk, c.chunk, c.qkv == MUIR_BF16);
     if (need == 0 && c.T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (need / (static_cast<size_t>(c.B) * c.H) > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED,
+                    "%s: the workspace of one head exceeds 4 GiB; split the sequence over "
+                    "several calls, carrying the state through s0 / s_out", fn);
     if (need > 0) {
         if (!c.workspace)
             return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
@@ -164,7 +177,8 @@ muir_status_t validate(const ChunkCall &c) {
 
     const Range inputs[] = {
         range("q", c.q, n_tok * es), range("k", c.k, n_tok * es), range("v", c.v, n_tok * es),
-        range("a", c.a, n_tok * 4), range("g", c.g, n_tok * 4), range("e", c.e, n_tok * 4),
+        range("a", c.a, n_tok * 4), range("g", c.g, n_tok * 4),
+        range("e", c.e, c.scalar_e ? n_tok / static_cast<size_t>(c.dk) * 4 : n_tok * 4),
         range("w", c.w, n_tok * 4), range("og", c.og, n_tok * 4),
         range("r", c.r, static_cast<size_t>(c.H) * c.dk * 4),
         range("s0", c.s0, n_state * 4)};
@@ -204,6 +218,13 @@ muir_status_t chunk_fwd_impl(const ChunkCall &c, muir_stream_t stream) {
         if (sp != MUIR_OK) return sp;
     }
     return chunk_scan_impl(c, stream);
+}
+
+muir_status_t wy_scan_impl(const ChunkCall &c, muir_stream_t stream) {
+    if (c.T == 0 && !c.s_out) return ok();
+    return check_hip(muir::launch_wy_scan(c.v, c.e, c.w, c.s0, c.o, c.s_out, c.B, c.T, c.H, c.dk,
+                                          c.chunk, c.workspace, static_cast<hipStream_t>(stream)),
+                     c.fn);
 }
 
 }  // namespace
@@ -268,6 +289,60 @@ muir_status_t muir_chunk_fwd_scan_gated(const void *v, const float *e, const flo
                                      nullptr, e, w, og, nullptr, s0, o, s_out, B, T, H, dk, dv,
                                      chunk, qkv, workspace, workspace_bytes, false, true, true},
                            stream);
+}
+
+muir_status_t muir_chunk_fwd_scalar_erase(const void *q, const void *k, const void *v,
+                                          const float *a, const float *g, const float *e,
+                                          const float *w, const float *r, const float *s0,
+                                          void *o, float *s_out, int B, int T, int H, int dk,
+                                          int dv, int chunk, muir_dtype_t qkv, void *workspace,
+                                          size_t workspace_bytes, muir_stream_t stream) {
+    ChunkCall c{"chunk_fwd_scalar_erase", q, k, v, a, g, e, w, nullptr, r, s0, o, s_out, B, T, H,
+                dk, dv, chunk, qkv, workspace, workspace_bytes, true, true, false};
+    c.scalar_e = true;
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T > 0) {
+        const hipStream_t hs = static_cast<hipStream_t>(stream);
+        muir_status_t sp = check_hip(muir::launch_chunk_prepare(q, k, a, g, r, B, T, H, dk, chunk,
+                                                                true, workspace, hs),
+                                     "chunk_fwd_scalar_erase prepare");
+        if (sp != MUIR_OK) return sp;
+        sp = check_hip(muir::launch_wy_solve(e, B, T, H, dk, chunk, workspace, hs),
+                       "chunk_fwd_scalar_erase solve");
+        if (sp != MUIR_OK) return sp;
+    }
+    return wy_scan_impl(c, stream);
+}
+
+muir_status_t muir_chunk_fwd_scalar_erase_solve(const float *e, int B, int T, int H, int dk,
+                                                int chunk, muir_dtype_t qkv, void *workspace,
+                                                size_t workspace_bytes, muir_stream_t stream) {
+    ChunkCall c{"chunk_fwd_scalar_erase_solve", nullptr, nullptr, nullptr, nullptr, nullptr, e,
+                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, dk, dk, chunk, qkv,
+                workspace, workspace_bytes, false, false, false};
+    c.scalar_e = true;
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T > 0 && !e) return fail(MUIR_ERR_NULL, "chunk_fwd_scalar_erase_solve: e is required");
+    if (T == 0) return ok();
+    return check_hip(muir::launch_wy_solve(e, B, T, H, dk, chunk, workspace,
+                                           static_cast<hipStream_t>(stream)),
+                     "chunk_fwd_scalar_erase_solve launch");
+}
+
+muir_status_t muir_chunk_fwd_scalar_erase_scan(const void *v, const float *e, const float *w,
+                                               const float *s0, void *o, float *s_out, int B,
+                                               int T, int H, int dk, int dv, int chunk,
+                                               muir_dtype_t qkv, const void *workspace,
+                                               size_t workspace_bytes, muir_stream_t stream) {
+    ChunkCall c{"chunk_fwd_scalar_erase_scan", nullptr, nullptr, v, nullptr, nullptr, e, w,
+                nullptr, nullptr, s0, o, s_out, B, T, H, dk, dv, chunk, qkv, workspace,
+                workspace_bytes, false, true, false};
+    c.scalar_e = true;
+    const muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    return wy_scan_impl(c, stream);
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

@@ -40,6 +40,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "chunk_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -51,58 +52,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr size_t kLdsBudget = 160 * 1024 - 1024;
-
-__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Workspace slot of one (batch, head, chunk). M and P blocks are 16x16 row-major
-// (row = later token t, column = earlier token s), lower-triangular block order; the
-// diagonal blocks of M are kept apart in fp32 (MD) for the leaf solve, and the tri slots
-// of M's diagonal blocks are left unused.
-//
-// The matrix-core operands are stored in the order the scan consumes them. Within every
-// group of 32 positions, position 8g + 4h + i holds index 16h + 4g + i of the group
-// (g < 4, h < 2, i < 4): lane group g then finds, in one 8-element load, the indices
-// 4g..4g+3 of both 16-halves. Kg and Qg ([C][D]) are permuted along channels, KbT
-// ([D][C]) along tokens.
-template <typename OpT, int D, int C> struct Slot {
-    static constexpr int NB = C / 16;
-    static constexpr int NPAIR = (NB / 2) * (NB / 2 + 1);  // block-pair slots of M (and of P)
-    static constexpr size_t M_BYTES = size_t(NPAIR) * 512 * sizeof(OpT);
-    static constexpr size_t M_OFF = 0;
-    static constexpr size_t PP_OFF = align256(M_OFF + M_BYTES);       // pair decays [NB/2][D]
-    static constexpr size_t P_OFF = align256(PP_OFF + size_t(NB / 2) * D * 4);
-    static constexpr size_t KG_OFF = align256(P_OFF + M_BYTES);
-    static constexpr size_t QG_OFF = align256(KG_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t KBT_OFF = align256(QG_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t MD_OFF = align256(KBT_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t BYTES = align256(MD_OFF + size_t(NB) * 256 * 4);
-    // First block-pair slot of block row bt; the row has bt / 2 + 1 of them.
-    static __host__ __device__ constexpr int prow(int bt) {
-        return (bt >> 1) * ((bt >> 1) + 1) + (bt & 1) * ((bt >> 1) + 1);
-    }
-    // Element w = 16 t + s of block (bt, bs). Blocks 2j and 2j + 1 of a row share one
-    // slot, interleaved four elements at a time, so that one 8-element load gives a lane
-    // the same four elements of both (the two halves of a K = 32 operand).
-    static __host__ __device__ constexpr size_t blk(int bt, int bs, int w) {
-        return size_t(prow(bt) + (bs >> 1)) * 512 + ((w >> 2) * 2 + (bs & 1)) * 4 + (w & 3);
-    }
-};
-
-// Storage position of index x under the 32-group permutation described above.
-__host__ __device__ constexpr int pair_perm(int x) {
-    return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
-}
-
-// Fragment order of the operands Kg, Qg ([C rows][D positions]) and KbT ([D][C]): the
-// operand a lane group needs for one 16-row group and one 32-position group is 64
-// lanes x 8 values, stored contiguously with lane 16G + r holding row r and positions
-// 8G .. 8G + 7 of the group. The scan then reads a whole fragment as one contiguous
-// 16-byte (bf16) load per lane, eight full cache lines per load. Element (row, pos) of
-// an operand with npos positions per row:
-__host__ __device__ constexpr size_t frag_idx(int row, int pos, int npos) {
-    return ((size_t(row >> 4) * (npos >> 5) + (pos >> 5)) * 64 + 16 * ((pos & 31) >> 3) + (row & 15)) * 8 +
-           (pos & 7);
-}
 
 // LDS of the prepare kernel: block totals, K*sigma (padded rows), per-wave tables.
 template <typename OpT, int D, int C> struct PrepLds {
@@ -395,119 +344,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 // ---------------------------------------------------------------------------------
 // Phase S: sequential chunk scan.
 // ---------------------------------------------------------------------------------
-// Every product of the scan is D[16x16] += A[16xK] B[16xK]^T on the matrix cores with
-// K = 16 (mma4, four values per lane) or K = 32 (mma8, eight values per lane). Lane l
-// holds row l%16 of each operand; which contraction index its j-th value stands for is
-// chosen by the caller, the same on both sides, so the hardware's own k order never
-// matters. Accumulator: lane l holds column l%16, rows 4(l/16) + i.
-// Buffer resources: every load and store of the scan goes through a descriptor whose
-// base is wave-uniform, with a 32-bit per-lane byte offset and a uniform byte offset.
-// Reads past num_records return zero and writes past it are dropped, which is how the
-// tokens past the end of the sequence are handled.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
-}
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), 0);
-}
-__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
-}
-__device__ __forceinline__ f32x4_t buf_load_f4(rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_bit_cast(f32x4_t, buf_load16(r, voff, soff));
-}
-
-template <typename OpT> struct Frag;
-template <> struct Frag<bf16_t> {
-    using f4 = u16x4_t;
-    using f8 = u16x8_t;
-    static __device__ __forceinline__ f4 bload4(rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
-    }
-    static __device__ __forceinline__ f8 bload8(rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(u16x8_t, buf_load16(r, voff, soff));
-    }
-    static __device__ __forceinline__ f4 load4(const bf16_t *p) {
-        return *reinterpret_cast<const u16x4_t *>(p);
-    }
-    static __device__ __forceinline__ f8 load8(const bf16_t *p) {
-        return *reinterpret_cast<const u16x8_t *>(p);
-    }
-    static __device__ __forceinline__ f8 cat(f4 a, f4 b) {
-        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    static __device__ __forceinline__ f4 lo(f8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
-    static __device__ __forceinline__ f4 hi(f8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
-    static __device__ __forceinline__ f4 pack(f32x4_t v) {
-        u16x4_t u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
-        return u;
-    }
-    // Lane (n, g) of the 16x16 identity as an mma4 operand: value j is I[n][4g + j].
-    static __device__ __forceinline__ f4 unit(int n, int g) {
-        u16x4_t u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = n == 4 * g + j ? 0x3f80 : 0;
-        return u;
-    }
-    // K = 16 products run as the K = 32 instruction with a zero upper half: an
-    // accumulation chain that alternates the 16x16x16 and 16x16x32 bf16 instructions
-    // needs more wait states between them than the compiler inserts on gfx950, so only
-    // one instruction kind is ever used.
-    static __device__ __forceinline__ f32x4_t mma4(f4 a, f4 b, f32x4_t c) {
-        const f4 z = {0, 0, 0, 0};
-        return mma8(cat(a, z), cat(b, z), c);
-    }
-    static __device__ __forceinline__ f32x4_t mma8(f8 a, f8 b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    }
-    // The 16x16x16 instruction itself, with no accumulator input: nothing to chain with.
-    static __device__ __forceinline__ f32x4_t mma16_fresh(f4 a, f4 b) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                         __builtin_bit_cast(s16x4_t, b), zero4(), 0, 0, 0);
-    }
-};
-template <> struct Frag<float> {
-    using f4 = f32x4_t;
-    struct f8 {
-        f32x4_t lo, hi;
-    };
-    static __device__ __forceinline__ f4 load4(const float *p) {
-        const float4 t = *reinterpret_cast<const float4 *>(p);
-        return f32x4_t{t.x, t.y, t.z, t.w};
-    }
-    static __device__ __forceinline__ f8 load8(const float *p) { return {load4(p), load4(p + 4)}; }
-    static __device__ __forceinline__ f4 bload4(rsrc_t r, unsigned voff, unsigned soff) {
-        return buf_load_f4(r, voff, soff);
-    }
-    static __device__ __forceinline__ f8 bload8(rsrc_t r, unsigned voff, unsigned soff) {
-        return {buf_load_f4(r, voff, soff), buf_load_f4(r, voff + 16, soff)};
-    }
-    static __device__ __forceinline__ f8 cat(f4 a, f4 b) { return {a, b}; }
-    static __device__ __forceinline__ f4 lo(f8 v) { return v.lo; }
-    static __device__ __forceinline__ f4 hi(f8 v) { return v.hi; }
-    static __device__ __forceinline__ f4 pack(f32x4_t v) { return v; }
-    static __device__ __forceinline__ f4 unit(int n, int g) {
-        f32x4_t u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = n == 4 * g + j ? 1.f : 0.f;
-        return u;
-    }
-    static __device__ __forceinline__ f32x4_t mma4(f4 a, f4 b, f32x4_t c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
-        return c;
-    }
-    static __device__ __forceinline__ f32x4_t mma8(f8 a, f8 b, f32x4_t c) {
-        return mma4(a.hi, b.hi, mma4(a.lo, b.lo, c));
-    }
-    static __device__ __forceinline__ f32x4_t mma16_fresh(f4 a, f4 b) { return mma4(a, b, zero4()); }
-};
 
 // One step of the leaf's forward substitution for the four value columns a lane holds:
 // x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
@@ -533,41 +369,6 @@ __device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, floa
 #undef MUIR_BCAST_FMA
 }
 
-// Calls fn(std::integral_constant<int, 0>{}) ... fn(std::integral_constant<int, N-1>{}) in
-// order, so that indices into register arrays are compile-time constants.
-template <typename Fn, int... Is>
-__device__ __forceinline__ void static_for_impl(Fn &&fn, std::integer_sequence<int, Is...>) {
-    (fn(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename Fn> __device__ __forceinline__ void static_for(Fn &&fn) {
-    static_for_impl(fn, std::make_integer_sequence<int, N>{});
-}
-
-// Four consecutive q/k/v-typed elements through a buffer resource.
-template <typename QT> struct Row4;
-template <> struct Row4<bf16_t> {
-    using raw = u16x4_t;
-    static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
-    }
-    static __device__ __forceinline__ float get(raw v, int i) { return bf16_to_f32(v[i]); }
-    static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
-        u16x4_t u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, int(voff), int(soff), 0);
-    }
-};
-template <> struct Row4<float> {
-    using raw = f32x4_t;
-    static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
-        return buf_load_f4(r, voff, soff);
-    }
-    static __device__ __forceinline__ float get(raw v, int i) { return v[i]; }
-    static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(voff), int(soff), 0);
-    }
-};
 
 // ---------------------------------------------------------------------------------
 // Phase P for bf16 operands: the same outputs in one streaming pass over the chunk.

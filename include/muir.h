@@ -100,8 +100,10 @@ size_t muir_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int ch
  *
  * Errors: MUIR_ERR_NULL for a missing q/k/v/a/g/e/w/r/o (when T > 0) or workspace;
  * MUIR_ERR_SHAPE for B < 1, T < 0, H < 1 or size overflow; MUIR_ERR_UNSUPPORTED for
- * dk != dv, d not in {64, 128} or chunk not in {64, 128, 256}; MUIR_ERR_WORKSPACE for
- * a short or misaligned workspace; MUIR_ERR_ALIAS when o overlaps an input or s_out
+ * dk != dv, d not in {64, 128} or chunk not in {64, 128, 256}, and when one head's
+ * tokens (T*H*dv*4 bytes) or one head's workspace exceed 4 GiB (a longer sequence is
+ * processed in several calls, the state carried through s0 / s_out); MUIR_ERR_WORKSPACE
+ * for a short or misaligned workspace; MUIR_ERR_ALIAS when o overlaps an input or s_out
  * overlaps an input other than s0 (or s0 partially).
  */
 muir_status_t muir_chunk_fwd(
@@ -169,6 +171,51 @@ muir_status_t muir_chunk_fwd_gated(
 muir_status_t muir_chunk_fwd_scan_gated(
     const void *v, const float *e, const float *w, const float *og, const float *s0,
     void *o, float *s_out, int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
+ * The chunk forward with ONE erase strength per token, shared by every value channel:
+ * the plain gated delta rule's erase, which GDN-2 and Muir generalise into decoupled
+ * per-channel erase gates (Muir abstract, "Full text" on the Astral Feed page). The
+ * result is muir_chunk_fwd's with e[b, t, h, j] = e[b, t, h] for every j.
+ *
+ * With a shared erase the intra-chunk unit lower-triangular system I + Diag(e) M is the
+ * same for every value column, so its inverse T is formed once per chunk, in parallel
+ * over chunks, by the block recursion of the stable scheme (liuch.name summary, third
+ * bullet): 16x16 diagonal inverses by forward substitution, off-diagonal blocks on the
+ * matrix cores. The sequential scan then needs only dense products per chunk:
+ * U = T (w*v - e*(K*gamma) S0), o = (r*g*q*gamma) S0 + P U, S_C = Diag(gamma_C) S0 +
+ * (K*beta)^T U.
+ *
+ *   e       [B, T, H]      float32          erase strength per token and head, in (0, 1)
+ *   qkv     MUIR_BF16 only (MUIR_ERR_UNSUPPORTED otherwise)
+ * Every other argument, the workspace size included, as for muir_chunk_fwd.
+ *
+ * The three phases are also separate calls; muir_chunk_fwd_scalar_erase(...) is exactly
+ * muir_chunk_fwd_prepare(...), muir_chunk_fwd_scalar_erase_solve(...) and
+ * muir_chunk_fwd_scalar_erase_scan(...) on one stream with one workspace:
+ *   - solve: the chunk-parallel inverse. It overwrites M in a workspace that
+ *     muir_chunk_fwd_prepare filled with T, so it must run exactly once after each prepare
+ *     (a second run would invert T).
+ *   - scan: the sequential phase. It reads T, P, the operands and the pair decays and
+ *     modifies nothing in the workspace, so it may be repeated.
+ *
+ * Errors as for muir_chunk_fwd, plus MUIR_ERR_UNSUPPORTED for f32 q/k/v.
+ */
+muir_status_t muir_chunk_fwd_scalar_erase(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *r,
+    const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+muir_status_t muir_chunk_fwd_scalar_erase_solve(
+    const float *e, int B, int T, int H, int dk, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+muir_status_t muir_chunk_fwd_scalar_erase_scan(
+    const void *v, const float *e, const float *w, const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
     const void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*

@@ -130,6 +130,70 @@ def test_scan_gated_requires_the_gate():
     assert st == 1 and "og" in muir.last_error()
 
 
+def _scalar_erase_call(**over):
+    lib = muir.lib()
+    args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),
+                r=fake(7), s0=fake(8), o=fake(9), s_out=fake(10), B=2, T=100, H=3, dk=64,
+                dv=64, chunk=64, qkv=muir.MUIR_BF16, ws=fake(11),
+                wsb=muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16),
+                stream=None)
+    args.update(over)
+    st = lib.muir_chunk_fwd_scalar_erase(args["q"], args["k"], args["v"], args["a"], args["g"],
+                                         args["e"], args["w"], args["r"], args["s0"], args["o"],
+                                         args["s_out"], args["B"], args["T"], args["H"],
+                                         args["dk"], args["dv"], args["chunk"], args["qkv"],
+                                         args["ws"], args["wsb"], args["stream"])
+    return st, muir.last_error()
+
+
+# e is [B, T, H] here: 2 * 100 * 3 * 4 = 2400 bytes, so an o starting 4 KiB past e's start
+# does not overlap it, while one 1 KiB past does.
+@pytest.mark.parametrize("over,status", [
+    (dict(qkv=muir.MUIR_F32), 3), (dict(e=None), 1), (dict(w=None), 1), (dict(q=None), 1),
+    (dict(chunk=32), 3), (dict(dk=64, dv=128), 3), (dict(ws=None), 4), (dict(wsb=64), 4),
+    (dict(o=ctypes.c_void_p(BASE + 5 * STRIDE + 1024)), 5),
+    (dict(e=ctypes.c_void_p(BASE + 5 * STRIDE + 8)), 2),
+])
+def test_scalar_erase_rejects_bad_arguments(over, status):
+    st, msg = _scalar_erase_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_scalar_erase_gate_is_one_value_per_token():
+    """An o placed right after a [B, T, H] e does not alias it (a [B, T, H, dv] e would):
+    the call then fails only for the next reason in line, a missing workspace."""
+    st, msg = _scalar_erase_call(o=ctypes.c_void_p(BASE + 5 * STRIDE + 4096), ws=None)
+    assert st == 4, msg
+
+
+def test_scalar_erase_scan_rejects_bad_arguments():
+    lib = muir.lib()
+    wsb = muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16)
+    call = lambda e, qkv, ws: lib.muir_chunk_fwd_scalar_erase_scan(
+        fake(2), e, fake(6), None, fake(9), None, 2, 100, 3, 64, 64, 64, qkv, ws, wsb, None)
+    assert call(None, muir.MUIR_BF16, fake(11)) == 1
+    assert call(fake(5), muir.MUIR_F32, fake(11)) == 3
+    assert call(fake(5), muir.MUIR_BF16, None) == 4
+    solve = lambda e, qkv, ws, T=100: lib.muir_chunk_fwd_scalar_erase_solve(
+        e, 2, T, 3, 64, 64, qkv, ws, wsb, None)
+    assert solve(None, muir.MUIR_BF16, fake(11)) == 1
+    assert solve(fake(5), muir.MUIR_F32, fake(11)) == 3
+    assert solve(fake(5), muir.MUIR_BF16, None) == 4
+    assert solve(fake(5), muir.MUIR_BF16, fake(11), T=-1) == 2
+
+
+@pytest.mark.parametrize("T", [1 << 21, 1 << 23])
+def test_heads_past_32_bit_offsets_are_refused(T):
+    """One head's tokens (T*H*dv*4 bytes) or workspace beyond 4 GiB: both forwards refuse
+    the call instead of wrapping their 32-bit offsets."""
+    wsb = muir.chunk_fwd_workspace_size(1, T, 16, 128, 128, 256, muir.MUIR_BF16)
+    st, msg = _chunk_call(B=1, T=T, H=16, dk=128, dv=128, chunk=256, wsb=wsb)
+    assert st == 3 and "4 GiB" in msg, msg
+    st, msg = _scalar_erase_call(B=1, T=T, H=16, dk=128, dv=128, chunk=256, wsb=wsb)
+    assert st == 3 and "4 GiB" in msg, msg
+
+
 def _decode_call(**over):
     lib = muir.lib()
     args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),

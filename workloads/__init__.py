@@ -34,7 +34,7 @@ import numpy as np
 __all__ = [
     "ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG",
     "round_bf16", "chunk_inputs", "decode_base", "decode_step_inputs_torch",
-    "decode_seed",
+    "decode_seed", "output_gate", "scalar_erase",
 ]
 
 
@@ -222,6 +222,12 @@ def output_gate(B: int, T: int, H: int, d: int, seed: int) -> np.ndarray:
     stream of their own (``SeedSequence((seed, 10))``), so the other inputs of the same
     seed are unchanged."""
     return _sigmoid(_normal(np.random.SeedSequence((seed, 10)), (B, T, H, d)))
+
+
+def scalar_erase(B: int, T: int, H: int, seed: int) -> np.ndarray:
+    """One erase strength per token and head, e = sigmoid(N(0,1)) [B,T,H] float32, like the
+    per-channel e, from a stream of its own (``SeedSequence((seed, 11))``)."""
+    return _sigmoid(_normal(np.random.SeedSequence((seed, 11)), (B, T, H)))
 
 
 def decode_base(cfg: DecodeConfig = DECODE_CONFIG, *, L=None, H=None, d=None):
