@@ -134,15 +134,16 @@ def time_chunk(inp, chunk, dev, steps, warmup, og=None):
 
 
 def time_scalar_erase(inp, es, chunk, dev, steps, warmup):
-    """Time `steps` shared-erase forwards (e one value per token and head): the prepare,
-    the chunk-parallel inverse and the scan, each between HIP events on the stream."""
+    """Time `steps` shared-erase forwards (e one value per token and head): the prepare, the
+    chunk-parallel solve (inverse and per-chunk products) and the scan (state recurrence and
+    readout), each between HIP events on the stream."""
     import numpy as np
     import torch
     import gated_delta_rule_06_amd as muir
     t = to_dev(inp, dev)
     e_t = torch.from_numpy(np.ascontiguousarray(es)).to(dev)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
-    ws = torch.empty(muir.chunk_fwd_workspace_size(B, T, H, d, d, chunk, muir.MUIR_BF16),
+    ws = torch.empty(muir.chunk_fwd_scalar_erase_workspace_size(B, T, H, d, d, chunk),
                      dtype=torch.uint8, device=dev)
     o = torch.empty_like(t["v"])
     s_out = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
@@ -153,10 +154,10 @@ def time_scalar_erase(inp, es, chunk, dev, steps, warmup):
         muir.chunk_fwd_prepare(t["q"], t["k"], t["a"], t["g"], t["r"], chunk=chunk, workspace=ws)
         if ev is not None:
             ev[1].record()
-        muir.chunk_fwd_scalar_erase_solve(e_t, dk=d, chunk=chunk, workspace=ws)
+        muir.chunk_fwd_scalar_erase_solve(t["v"], e_t, t["w"], chunk=chunk, workspace=ws)
         if ev is not None:
             ev[2].record()
-        muir.chunk_fwd_scalar_erase_scan(t["v"], e_t, t["w"], chunk=chunk, workspace=ws, o=o,
+        muir.chunk_fwd_scalar_erase_scan(B=B, T=T, H=H, d=d, chunk=chunk, workspace=ws, o=o,
                                          s_out=s_out)
         if ev is not None:
             ev[3].record()

@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_prepare",
-    "chunk_fwd_scan", "chunk_fwd_scalar_erase", "chunk_fwd_scalar_erase_solve",
+    "chunk_fwd_scan", "chunk_fwd_scalar_erase", "chunk_fwd_scalar_erase_workspace_size",
+    "chunk_fwd_scalar_erase_solve",
     "chunk_fwd_scalar_erase_scan", "decode_step",
     "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
 ]
@@ -64,9 +65,11 @@ def lib():
         L.muir_chunk_fwd_scan_gated.restype = i
         L.muir_chunk_fwd_scalar_erase.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd_scalar_erase.restype = i
-        L.muir_chunk_fwd_scalar_erase_solve.argtypes = [vp] + [i] * 6 + [vp, sz, vp]
+        L.muir_chunk_fwd_scalar_erase_workspace_size.argtypes = [i] * 6
+        L.muir_chunk_fwd_scalar_erase_workspace_size.restype = sz
+        L.muir_chunk_fwd_scalar_erase_solve.argtypes = [vp] * 3 + [i] * 6 + [vp, sz, vp]
         L.muir_chunk_fwd_scalar_erase_solve.restype = i
-        L.muir_chunk_fwd_scalar_erase_scan.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_scalar_erase_scan.argtypes = [vp] * 3 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd_scalar_erase_scan.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
         L.muir_decode_step.restype = i
@@ -233,14 +236,19 @@ def chunk_fwd_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None, og
             dv, chunk, code, _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
+def chunk_fwd_scalar_erase_workspace_size(B: int, T: int, H: int, dk: int, dv: int,
+                                          chunk: int) -> int:
+    return int(lib().muir_chunk_fwd_scalar_erase_workspace_size(B, T, H, dk, dv, chunk))
+
+
 def chunk_fwd_scalar_erase(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 256, o=None,
                            s_out=None, return_state: bool = True, workspace=None):
     """Chunk forward with one erase strength per token (``muir_chunk_fwd_scalar_erase``).
 
     As :func:`chunk_fwd` (bfloat16 q/k/v only) except ``e`` is [B,T,H] float32: the
     result equals the channel-wise forward with e broadcast over the value channels.
-    Returns (o, s_out). The workspace left behind holds the solved operands that
-    :func:`chunk_fwd_scalar_erase_scan` reads.
+    Returns (o, s_out). ``workspace`` (uint8, at least
+    :func:`chunk_fwd_scalar_erase_workspace_size` bytes) may be passed.
     """
     import torch
     B, T, H, dk = q.shape
@@ -263,7 +271,7 @@ def chunk_fwd_scalar_erase(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 256,
         s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif s_out is not None:
         _require(s_out, "s_out", torch.float32, (B, H, dk, dv), dev)
-    need = chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    need = chunk_fwd_scalar_erase_workspace_size(B, T, H, dk, dv, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
@@ -275,38 +283,37 @@ def chunk_fwd_scalar_erase(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 256,
     return o, s_out
 
 
-def chunk_fwd_scalar_erase_solve(e, *, dk: int, chunk: int, workspace):
-    """The chunk-parallel inverse alone (``muir_chunk_fwd_scalar_erase_solve``): turns the M
-    that :func:`chunk_fwd_prepare` (bf16 q/k/v) left in ``workspace`` into T. Run it once
-    per prepare."""
-    import torch
-    B, T, H = e.shape
-    dev = e.device
-    _require(e, "e", torch.float32, (B, T, H), dev)
-    _require(workspace, "workspace", torch.uint8, None, dev)
-    _check(lib().muir_chunk_fwd_scalar_erase_solve(
-        _ptr(e), B, T, H, dk, chunk, MUIR_BF16, _ptr(workspace), workspace.numel(),
-        _stream(dev)))
-
-
-def chunk_fwd_scalar_erase_scan(v, e, w, s0=None, *, chunk: int, workspace, o, s_out=None):
-    """The sequential phase alone (``muir_chunk_fwd_scalar_erase_scan``), from a workspace a
-    :func:`chunk_fwd_scalar_erase` call with the same sizes and inputs left behind."""
+def chunk_fwd_scalar_erase_solve(v, e, w, *, chunk: int, workspace):
+    """The chunk-parallel phase (``muir_chunk_fwd_scalar_erase_solve``) on a workspace that
+    :func:`chunk_fwd_prepare` (bf16 q/k/v) filled: the inverse, then the per-chunk products.
+    Run it once per prepare."""
     import torch
     B, T, H, dv = v.shape
     dev = v.device
-    code = _dtype_code(v)
+    _require(v, "v", torch.bfloat16, (B, T, H, dv), dev)
     _require(e, "e", torch.float32, (B, T, H), dev)
     _require(w, "w", torch.float32, (B, T, H, dv), dev)
-    _require(o, "o", v.dtype, (B, T, H, dv), dev)
+    _require(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib().muir_chunk_fwd_scalar_erase_solve(
+        _ptr(v), _ptr(e), _ptr(w), B, T, H, dv, chunk, MUIR_BF16, _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+
+
+def chunk_fwd_scalar_erase_scan(s0=None, *, B: int, T: int, H: int, d: int, chunk: int,
+                                workspace, o, s_out=None):
+    """The sequential phase and the readout (``muir_chunk_fwd_scalar_erase_scan``) from a
+    solved workspace; o [B,T,H,d] bfloat16 is written."""
+    import torch
+    dev = o.device
+    _require(o, "o", torch.bfloat16, (B, T, H, d), dev)
     if s0 is not None:
-        _require(s0, "s0", torch.float32, (B, H, dv, dv), dev)
+        _require(s0, "s0", torch.float32, (B, H, d, d), dev)
     if s_out is not None:
-        _require(s_out, "s_out", torch.float32, (B, H, dv, dv), dev)
+        _require(s_out, "s_out", torch.float32, (B, H, d, d), dev)
     _require(workspace, "workspace", torch.uint8, None, dev)
     _check(lib().muir_chunk_fwd_scalar_erase_scan(
-        _ptr(v), _ptr(e), _ptr(w), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dv, dv, chunk,
-        code, _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, d, d, chunk, MUIR_BF16, _ptr(workspace),
+        workspace.numel(), _stream(dev)))
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

@@ -154,8 +154,9 @@ muir_status_t validate(const ChunkCall &c) {
                     "%s: T*H*dv*4 = %zu bytes exceeds 4 GiB; split the sequence over several "
                     "calls, carrying the state through s0 / s_out", fn, head_span);
 
-    const size_t need =
-        muir::chunk_workspace_bytes(c.B, c.T, c.H, c.dk, c.chunk, c.qkv == MUIR_BF16);
+    const size_t need = c.scalar_e
+        ? muir::wy_workspace_bytes(c.B, c.T, c.H, c.dk, c.chunk)
+        : muir::chunk_workspace_bytes(c.B, c.T, c.H, c.dk, c.chunk, c.qkv == MUIR_BF16);
     if (need == 0 && c.T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
     if (need / (static_cast<size_t>(c.B) * c.H) > 0xffffffffu)
         return fail(MUIR_ERR_UNSUPPORTED,
@@ -218,13 +219,6 @@ muir_status_t chunk_fwd_impl(const ChunkCall &c, muir_stream_t stream) {
         if (sp != MUIR_OK) return sp;
     }
     return chunk_scan_impl(c, stream);
-}
-
-muir_status_t wy_scan_impl(const ChunkCall &c, muir_stream_t stream) {
-    if (c.T == 0 && !c.s_out) return ok();
-    return check_hip(muir::launch_wy_scan(c.v, c.e, c.w, c.s0, c.o, c.s_out, c.B, c.T, c.H, c.dk,
-                                          c.chunk, c.workspace, static_cast<hipStream_t>(stream)),
-                     c.fn);
 }
 
 }  // namespace
@@ -291,6 +285,13 @@ muir_status_t muir_chunk_fwd_scan_gated(const void *v, const float *e, const flo
                            stream);
 }
 
+size_t muir_chunk_fwd_scalar_erase_workspace_size(int B, int T, int H, int dk, int dv,
+                                                   int chunk) {
+    if (B < 1 || T < 0 || H < 1 || dk != dv || !supported_d(dk) || !supported_chunk(chunk))
+        return 0;
+    return muir::wy_workspace_bytes(B, T, H, dk, chunk);
+}
+
 muir_status_t muir_chunk_fwd_scalar_erase(const void *q, const void *k, const void *v,
                                           const float *a, const float *g, const float *e,
                                           const float *w, const float *r, const float *s0,
@@ -302,47 +303,55 @@ muir_status_t muir_chunk_fwd_scalar_erase(const void *q, const void *k, const vo
     c.scalar_e = true;
     const muir_status_t st = validate(c);
     if (st != MUIR_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (T > 0) {
-        const hipStream_t hs = static_cast<hipStream_t>(stream);
         muir_status_t sp = check_hip(muir::launch_chunk_prepare(q, k, a, g, r, B, T, H, dk, chunk,
                                                                 true, workspace, hs),
                                      "chunk_fwd_scalar_erase prepare");
         if (sp != MUIR_OK) return sp;
-        sp = check_hip(muir::launch_wy_solve(e, B, T, H, dk, chunk, workspace, hs),
+        sp = check_hip(muir::launch_wy_solve(v, e, w, B, T, H, dk, chunk, workspace, hs),
                        "chunk_fwd_scalar_erase solve");
         if (sp != MUIR_OK) return sp;
+    } else if (!s_out) {
+        return ok();
     }
-    return wy_scan_impl(c, stream);
+    return check_hip(muir::launch_wy_scan(s0, o, s_out, B, T, H, dk, chunk, workspace, hs),
+                     "chunk_fwd_scalar_erase scan");
 }
 
-muir_status_t muir_chunk_fwd_scalar_erase_solve(const float *e, int B, int T, int H, int dk,
-                                                int chunk, muir_dtype_t qkv, void *workspace,
+muir_status_t muir_chunk_fwd_scalar_erase_solve(const void *v, const float *e, const float *w,
+                                                int B, int T, int H, int dk, int chunk,
+                                                muir_dtype_t qkv, void *workspace,
                                                 size_t workspace_bytes, muir_stream_t stream) {
-    ChunkCall c{"chunk_fwd_scalar_erase_solve", nullptr, nullptr, nullptr, nullptr, nullptr, e,
-                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, dk, dk, chunk, qkv,
+    ChunkCall c{"chunk_fwd_scalar_erase_solve", nullptr, nullptr, v, nullptr, nullptr, e, w,
+                nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, dk, dk, chunk, qkv,
                 workspace, workspace_bytes, false, false, false};
     c.scalar_e = true;
     const muir_status_t st = validate(c);
     if (st != MUIR_OK) return st;
-    if (T > 0 && !e) return fail(MUIR_ERR_NULL, "chunk_fwd_scalar_erase_solve: e is required");
+    if (T > 0 && (!v || !e || !w))
+        return fail(MUIR_ERR_NULL, "chunk_fwd_scalar_erase_solve: v, e and w are required");
     if (T == 0) return ok();
-    return check_hip(muir::launch_wy_solve(e, B, T, H, dk, chunk, workspace,
+    return check_hip(muir::launch_wy_solve(v, e, w, B, T, H, dk, chunk, workspace,
                                            static_cast<hipStream_t>(stream)),
                      "chunk_fwd_scalar_erase_solve launch");
 }
 
-muir_status_t muir_chunk_fwd_scalar_erase_scan(const void *v, const float *e, const float *w,
-                                               const float *s0, void *o, float *s_out, int B,
+muir_status_t muir_chunk_fwd_scalar_erase_scan(const float *s0, void *o, float *s_out, int B,
                                                int T, int H, int dk, int dv, int chunk,
-                                               muir_dtype_t qkv, const void *workspace,
+                                               muir_dtype_t qkv, void *workspace,
                                                size_t workspace_bytes, muir_stream_t stream) {
-    ChunkCall c{"chunk_fwd_scalar_erase_scan", nullptr, nullptr, v, nullptr, nullptr, e, w,
-                nullptr, nullptr, s0, o, s_out, B, T, H, dk, dv, chunk, qkv, workspace,
-                workspace_bytes, false, true, false};
+    ChunkCall c{"chunk_fwd_scalar_erase_scan", nullptr, nullptr, nullptr, nullptr, nullptr,
+                nullptr, nullptr, nullptr, nullptr, s0, o, s_out, B, T, H, dk, dv, chunk, qkv,
+                workspace, workspace_bytes, false, false, false};
     c.scalar_e = true;
     const muir_status_t st = validate(c);
     if (st != MUIR_OK) return st;
-    return wy_scan_impl(c, stream);
+    if (T > 0 && !o) return fail(MUIR_ERR_NULL, "chunk_fwd_scalar_erase_scan: o is required");
+    if (T == 0 && !s_out) return ok();
+    return check_hip(muir::launch_wy_scan(s0, o, s_out, B, T, H, dk, chunk, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                     "chunk_fwd_scalar_erase_scan launch");
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

@@ -26,13 +26,17 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                              int chunk, bool bf16, const void *workspace, hipStream_t stream);
 
-// Shared-erase variant (one erase strength per token, e [B, T, H]); bf16 operands only.
-// Solve: replaces M in a prepared workspace by T = (I + Diag(e) M)^-1, chunk-parallel.
-hipError_t launch_wy_solve(const float *e, int B, int T, int H, int d, int chunk, void *workspace,
-                           hipStream_t stream);
-// Scan: U = T (w*v - e*(K*gamma) S0), readout and state carry from a solved workspace.
-hipError_t launch_wy_scan(const void *v, const float *e, const float *w, const float *s0, void *o,
-                          float *s_out, int B, int T, int H, int d, int chunk,
-                          const void *workspace, hipStream_t stream);
+// Shared-erase variant (one erase strength per token, e [B, T, H]); bf16 operands only. Its
+// workspace is the prepare kernel's slots followed by one region of per-chunk products per
+// slot.
+size_t wy_workspace_bytes(int B, int T, int H, int d, int chunk);
+// Solve: chunk-parallel. Replaces M in a prepared workspace by T = (I + Diag(e) M)^-1, then
+// forms each chunk's state operator, state increment, readout operator and readout offset.
+hipError_t launch_wy_solve(const void *v, const float *e, const float *w, int B, int T, int H,
+                           int d, int chunk, void *workspace, hipStream_t stream);
+// Scan: the state recurrence over chunks (leaving each chunk's start state in the workspace),
+// then the chunk-parallel readout.
+hipError_t launch_wy_scan(const float *s0, void *o, float *s_out, int B, int T, int H, int d,
+                          int chunk, void *workspace, hipStream_t stream);
 
 }  // namespace muir

@@ -183,25 +183,34 @@ muir_status_t muir_chunk_fwd_scan_gated(
  * same for every value column, so its inverse T is formed once per chunk, in parallel
  * over chunks, by the block recursion of the stable scheme (liuch.name summary, third
  * bullet): 16x16 diagonal inverses by forward substitution, off-diagonal blocks on the
- * matrix cores. The sequential scan then needs only dense products per chunk:
- * U = T (w*v - e*(K*gamma) S0), o = (r*g*q*gamma) S0 + P U, S_C = Diag(gamma_C) S0 +
- * (K*beta)^T U.
+ * matrix cores. Everything that does not depend on the carried state is then formed in
+ * parallel over chunks too (the WY form): with W = T Diag(e) (K*gamma), U~ = T (w*v),
+ *   A = (K*beta)^T W,  Bc = (K*beta)^T U~,  Q~ = (r*g*q*gamma) - P W,  O~ = P U~,
+ * so the sequential part is two d x d products per chunk,
+ *   S_next = Diag(gamma_C) S - A S + Bc,
+ * and the readout o = Q~ S + O~ runs in parallel over chunks afterwards.
  *
  *   e       [B, T, H]      float32          erase strength per token and head, in (0, 1)
  *   qkv     MUIR_BF16 only (MUIR_ERR_UNSUPPORTED otherwise)
- * Every other argument, the workspace size included, as for muir_chunk_fwd.
+ *   workspace / workspace_bytes: at least
+ *           muir_chunk_fwd_scalar_erase_workspace_size(B, T, H, dk, dv, chunk) bytes,
+ *           256-byte aligned: the prepare's workspace followed by the per-chunk products
+ * Every other argument as for muir_chunk_fwd.
  *
  * The three phases are also separate calls; muir_chunk_fwd_scalar_erase(...) is exactly
- * muir_chunk_fwd_prepare(...), muir_chunk_fwd_scalar_erase_solve(...) and
- * muir_chunk_fwd_scalar_erase_scan(...) on one stream with one workspace:
- *   - solve: the chunk-parallel inverse. It overwrites M in a workspace that
- *     muir_chunk_fwd_prepare filled with T, so it must run exactly once after each prepare
- *     (a second run would invert T).
- *   - scan: the sequential phase. It reads T, P, the operands and the pair decays and
- *     modifies nothing in the workspace, so it may be repeated.
+ * muir_chunk_fwd_prepare(...) (into the same workspace), muir_chunk_fwd_scalar_erase_solve(...)
+ * and muir_chunk_fwd_scalar_erase_scan(...) on one stream:
+ *   - solve: chunk-parallel. It overwrites M in the prepared workspace with T, then writes
+ *     the per-chunk products; it must run exactly once after each prepare (a second run
+ *     would invert T).
+ *   - scan: the state recurrence (leaving each chunk's start state in the workspace), then
+ *     the readout. It writes only those start states, the same ones on every run, so it
+ *     may be repeated.
  *
  * Errors as for muir_chunk_fwd, plus MUIR_ERR_UNSUPPORTED for f32 q/k/v.
  */
+size_t muir_chunk_fwd_scalar_erase_workspace_size(int B, int T, int H, int dk, int dv, int chunk);
+
 muir_status_t muir_chunk_fwd_scalar_erase(
     const void *q, const void *k, const void *v,
     const float *a, const float *g, const float *e, const float *w, const float *r,
@@ -210,13 +219,12 @@ muir_status_t muir_chunk_fwd_scalar_erase(
     void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 muir_status_t muir_chunk_fwd_scalar_erase_solve(
-    const float *e, int B, int T, int H, int dk, int chunk, muir_dtype_t qkv,
-    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+    const void *v, const float *e, const float *w, int B, int T, int H, int dk, int chunk,
+    muir_dtype_t qkv, void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 muir_status_t muir_chunk_fwd_scalar_erase_scan(
-    const void *v, const float *e, const float *w, const float *s0, void *o, float *s_out,
-    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
-    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
+    const float *s0, void *o, float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+    muir_dtype_t qkv, void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
  * One recurrent step per (batch, head), updating the state in place (decode).

@@ -135,7 +135,7 @@ def _scalar_erase_call(**over):
     args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),
                 r=fake(7), s0=fake(8), o=fake(9), s_out=fake(10), B=2, T=100, H=3, dk=64,
                 dv=64, chunk=64, qkv=muir.MUIR_BF16, ws=fake(11),
-                wsb=muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16),
+                wsb=muir.chunk_fwd_scalar_erase_workspace_size(2, 100, 3, 64, 64, 64),
                 stream=None)
     args.update(over)
     st = lib.muir_chunk_fwd_scalar_erase(args["q"], args["k"], args["v"], args["a"], args["g"],
@@ -167,20 +167,24 @@ def test_scalar_erase_gate_is_one_value_per_token():
     assert st == 4, msg
 
 
-def test_scalar_erase_scan_rejects_bad_arguments():
+def test_scalar_erase_phases_reject_bad_arguments():
     lib = muir.lib()
-    wsb = muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16)
-    call = lambda e, qkv, ws: lib.muir_chunk_fwd_scalar_erase_scan(
-        fake(2), e, fake(6), None, fake(9), None, 2, 100, 3, 64, 64, 64, qkv, ws, wsb, None)
-    assert call(None, muir.MUIR_BF16, fake(11)) == 1
-    assert call(fake(5), muir.MUIR_F32, fake(11)) == 3
-    assert call(fake(5), muir.MUIR_BF16, None) == 4
-    solve = lambda e, qkv, ws, T=100: lib.muir_chunk_fwd_scalar_erase_solve(
-        e, 2, T, 3, 64, 64, qkv, ws, wsb, None)
-    assert solve(None, muir.MUIR_BF16, fake(11)) == 1
-    assert solve(fake(5), muir.MUIR_F32, fake(11)) == 3
-    assert solve(fake(5), muir.MUIR_BF16, None) == 4
-    assert solve(fake(5), muir.MUIR_BF16, fake(11), T=-1) == 2
+    wsb = muir.chunk_fwd_scalar_erase_workspace_size(2, 100, 3, 64, 64, 64)
+    assert wsb > muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16)
+    solve = lambda v, e, qkv, ws, T=100, n=wsb: lib.muir_chunk_fwd_scalar_erase_solve(
+        v, e, fake(6), 2, T, 3, 64, 64, qkv, ws, n, None)
+    assert solve(fake(2), None, muir.MUIR_BF16, fake(11)) == 1
+    assert solve(None, fake(5), muir.MUIR_BF16, fake(11)) == 1
+    assert solve(fake(2), fake(5), muir.MUIR_F32, fake(11)) == 3
+    assert solve(fake(2), fake(5), muir.MUIR_BF16, None) == 4
+    assert solve(fake(2), fake(5), muir.MUIR_BF16, fake(11), n=wsb - 256) == 4
+    assert solve(fake(2), fake(5), muir.MUIR_BF16, fake(11), T=-1) == 2
+    scan = lambda o, qkv, ws: lib.muir_chunk_fwd_scalar_erase_scan(
+        None, o, None, 2, 100, 3, 64, 64, 64, qkv, ws, wsb, None)
+    assert scan(None, muir.MUIR_BF16, fake(11)) == 1
+    assert scan(fake(9), muir.MUIR_F32, fake(11)) == 3
+    assert scan(fake(9), muir.MUIR_BF16, None) == 4
+    assert muir.chunk_fwd_scalar_erase_workspace_size(1, 64, 1, 64, 128, 64) == 0
 
 
 @pytest.mark.parametrize("T", [1 << 21, 1 << 23])
@@ -190,6 +194,7 @@ def test_heads_past_32_bit_offsets_are_refused(T):
     wsb = muir.chunk_fwd_workspace_size(1, T, 16, 128, 128, 256, muir.MUIR_BF16)
     st, msg = _chunk_call(B=1, T=T, H=16, dk=128, dv=128, chunk=256, wsb=wsb)
     assert st == 3 and "4 GiB" in msg, msg
+    wsb = muir.chunk_fwd_scalar_erase_workspace_size(1, T, 16, 128, 128, 256)
     st, msg = _scalar_erase_call(B=1, T=T, H=16, dk=128, dv=128, chunk=256, wsb=wsb)
     assert st == 3 and "4 GiB" in msg, msg
 
