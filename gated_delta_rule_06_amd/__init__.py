@@ -18,7 +18,7 @@ __all__ = [
     "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_prepare",
     "chunk_fwd_scan", "chunk_fwd_scalar_erase", "chunk_fwd_scalar_erase_workspace_size",
     "chunk_fwd_scalar_erase_solve",
-    "chunk_fwd_scalar_erase_scan", "decode_step",
+    "chunk_fwd_scalar_erase_scan", "lowrank_gates", "decode_step",
     "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
 ]
 
@@ -71,6 +71,8 @@ def lib():
         L.muir_chunk_fwd_scalar_erase_solve.restype = i
         L.muir_chunk_fwd_scalar_erase_scan.argtypes = [vp] * 3 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd_scalar_erase_scan.restype = i
+        L.muir_lowrank_gates.argtypes = [vp] * 13 + [i] * 4 + [vp]
+        L.muir_lowrank_gates.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
         L.muir_decode_step.restype = i
         L.muir_status_string.argtypes = [i]
@@ -314,6 +316,37 @@ def chunk_fwd_scalar_erase_scan(s0=None, *, B: int, T: int, H: int, d: int, chun
     _check(lib().muir_chunk_fwd_scalar_erase_scan(
         _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, d, d, chunk, MUIR_BF16, _ptr(workspace),
         workspace.numel(), _stream(dev)))
+
+
+def lowrank_gates(z, U, c, *, H: int, d: int, which=("a", "e", "w", "g"), out=None):
+    """Gates from the fused low-rank projection (``muir_lowrank_gates``).
+
+    z [B,T,512] bfloat16; U a dict of up-projections {"decay": [H,d,64], "erase": [H,d,64],
+    "write": [H,d,128], "read": [H,d,128]} bfloat16 and c the matching offsets [H,d]
+    float32. Returns a dict of the requested gates among a (decay), e, w, g, each
+    [B,T,H,d] float32 (``out`` may supply them)."""
+    import torch
+    B, T, R = z.shape
+    dev = z.device
+    _require(z, "z", torch.bfloat16, (B, T, 512), dev)
+    names = {"a": ("decay", 64), "e": ("erase", 64), "w": ("write", 128), "g": ("read", 128)}
+    out = dict(out or {})
+    args = []
+    for gname in ("a", "e", "w", "g"):
+        n, r = names[gname]
+        if gname in which:
+            _require(U[n], "U_" + n, torch.bfloat16, (H, d, r), dev)
+            _require(c[n], "c_" + n, torch.float32, (H, d), dev)
+            if gname not in out:
+                out[gname] = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+            _require(out[gname], gname, torch.float32, (B, T, H, d), dev)
+            args.append((U[n], c[n], out[gname]))
+        else:
+            args.append((None, None, None))
+    _check(lib().muir_lowrank_gates(
+        _ptr(z), *[_ptr(x[0]) for x in args], *[_ptr(x[1]) for x in args],
+        *[_ptr(x[2]) for x in args], B, T, H, d, _stream(dev)))
+    return {k: v for k, v in out.items() if k in which}
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

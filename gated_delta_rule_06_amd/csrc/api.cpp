@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <vector>
 
 #include "muir.h"
 #include "kernels.hpp"
@@ -352,6 +353,59 @@ muir_status_t muir_chunk_fwd_scalar_erase_scan(const float *s0, void *o, float *
     return check_hip(muir::launch_wy_scan(s0, o, s_out, B, T, H, dk, chunk, workspace,
                                           static_cast<hipStream_t>(stream)),
                      "chunk_fwd_scalar_erase_scan launch");
+}
+
+muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
+                                const void *Ug, const float *ca, const float *ce, const float *cw,
+                                const float *cg, float *a, float *e, float *w, float *g, int B,
+                                int T, int H, int d, muir_stream_t stream) {
+    const char *fn = "lowrank_gates";
+    if (B < 1 || T < 0 || H < 1)
+        return fail(MUIR_ERR_SHAPE, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
+    if (!supported_d(d)) return fail(MUIR_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    struct Gate {
+        const char *name;
+        const void *U;
+        const float *c;
+        float *out;
+        size_t rank;
+    } gates[] = {{"a", Ua, ca, a, 64}, {"e", Ue, ce, e, 64}, {"w", Uw, cw, w, 128}, {"g", Ug, cg, g, 128}};
+    bool any = false;
+    for (const Gate &gt : gates) {
+        if (!gt.out) continue;
+        any = true;
+        if (!gt.U || !gt.c)
+            return fail(MUIR_ERR_NULL, "%s: gate %s needs its up-projection and offset", fn, gt.name);
+    }
+    if (any && T > 0 && !z) return fail(MUIR_ERR_NULL, "%s: z is required", fn);
+    size_t n_tok, n_z;
+    if (!mul_size(n_tok, {static_cast<size_t>(B), static_cast<size_t>(T), static_cast<size_t>(H),
+                          static_cast<size_t>(d)}) ||
+        !mul_size(n_z, {static_cast<size_t>(B), static_cast<size_t>(T), 512}) || n_tok > SIZE_MAX / 4)
+        return fail(MUIR_ERR_SHAPE, "%s: sizes overflow", fn);
+    if (static_cast<size_t>(T) * H * d * 4 > 0xffffffffu || static_cast<size_t>(T) * 512 * 2 > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: one batch row's gates or z exceed 4 GiB", fn);
+    std::initializer_list<const void *> ptrs = {z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g};
+    for (const void *p : ptrs)
+        if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
+    std::vector<Range> ins = {range("z", z, n_z * 2)};
+    for (const Gate &gt : gates) {
+        ins.push_back(range(gt.name, gt.U, static_cast<size_t>(H) * d * gt.rank * 2));
+        ins.push_back(range(gt.name, gt.c, static_cast<size_t>(H) * d * 4));
+    }
+    for (size_t i = 0; i < 4; ++i) {
+        const Range ro = range(gates[i].name, gates[i].out, n_tok * 4);
+        for (const Range &x : ins)
+            if (overlaps(ro, x)) return fail(MUIR_ERR_ALIAS, "%s: gate %s overlaps an input", fn, gates[i].name);
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlaps(ro, range(gates[j].name, gates[j].out, n_tok * 4)))
+                return fail(MUIR_ERR_ALIAS, "%s: gates %s and %s overlap", fn, gates[i].name, gates[j].name);
+    }
+    if (!any || T == 0) return ok();
+    return check_hip(muir::launch_lowrank_gates(z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g, B,
+                                                T, H, d, static_cast<hipStream_t>(stream)),
+                     "lowrank_gates launch");
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

@@ -39,4 +39,12 @@ hipError_t launch_wy_solve(const void *v, const float *e, const float *w, int B,
 hipError_t launch_wy_scan(const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                           int chunk, void *workspace, hipStream_t stream);
 
+// Gates a, e, w, g [B, T, H, d] fp32 from the fused low-rank gate projection: z [B, T, 512]
+// bf16, up-projections U_n [H, d, r_n] bf16, offsets c_n [H, d] fp32. A null gate output
+// is not computed.
+hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
+                                const void *Ug, const float *ca, const float *ce, const float *cw,
+                                const float *cg, float *a, float *e, float *w, float *g, int B,
+                                int T, int H, int d, hipStream_t stream);
+
 }  // namespace muir

@@ -227,6 +227,34 @@ muir_status_t muir_chunk_fwd_scalar_erase_scan(
     muir_dtype_t qkv, void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
+ * The recurrence's gates from the fused low-rank gate projection. The pages fuse all five
+ * gates into one projection of total rank 512: one shared down-projection, then one
+ * up-projection per gate with its own rank, decay 64, erase 64, output 128, write 128 and
+ * dynamic read 128 (openai-hub page, section on sensitivity-allocated gating, gate table;
+ * liuch.name summary, second bullet). Per gate n:
+ *   y_n = z[b, t, slice_n] . U_n[h, i, :] + c_n[h, i]
+ *   a = exp(-exp(y_decay)) (y is the log decay rate),  e, w, g = sigmoid(y)
+ *
+ *   z        [B, T, 512] bf16: the down-projection's output, rank slices in the table's
+ *            order: decay 0..63, erase 64..127, output 128..255, write 256..383,
+ *            read 384..511 (the output gate's slice is not used here)
+ *   Ua, Ue   [H, d, 64]  bf16;  Uw, Ug [H, d, 128] bf16  (rank contiguous per channel)
+ *   ca .. cg [H, d] fp32 offsets
+ *   a, e, w, g  [B, T, H, d] fp32 outputs; a NULL output is not computed (and its U and c
+ *            may be NULL)
+ *   d        64 or 128
+ *
+ * Errors: MUIR_ERR_NULL for a missing z (T > 0) or a requested gate's U or c;
+ * MUIR_ERR_SHAPE for B < 1, T < 0, H < 1, size overflow or a misaligned buffer;
+ * MUIR_ERR_UNSUPPORTED for other d or a batch row over 4 GiB; MUIR_ERR_ALIAS when an output
+ * overlaps an input or another output.
+ */
+muir_status_t muir_lowrank_gates(
+    const void *z, const void *Ua, const void *Ue, const void *Uw, const void *Ug,
+    const float *ca, const float *ce, const float *cw, const float *cg,
+    float *a, float *e, float *w, float *g, int B, int T, int H, int d, muir_stream_t stream);
+
+/*
  * One recurrent step per (batch, head), updating the state in place (decode).
  * Constant-memory inference against the fixed state (Muir abstract, "Full text";
  * openai-hub page, opening section: the history lives in a fixed 2-D state, so

@@ -25,7 +25,8 @@ Forms provided here:
   * ``bruteforce_np``      the recurrence unrolled into explicit per-column transition
                            products (tiny sizes);
   * ``naive_unpivoted_nonfinite`` the unpivoted fp32 scheme that divides by cumulative
-                           decays, kept only as a negative control (same two passages).
+                           decays, kept only as a negative control (same two passages);
+  * ``lowrank_gates``      (``gates.py``) the four gates from the rank-512 gate projection.
 
 Every form is pinned by tests that do not reuse its own formula: closed forms that
 reduce to textbook linear attention or gated linear attention, the last-write-only
@@ -42,9 +43,11 @@ import numpy as np
 
 from . import build as _build
 
+from .gates import lowrank_gates  # noqa: E402  (the low-rank gate definition)
+
 __all__ = [
     "recurrent", "recurrent_np", "chunked_np", "bruteforce_np",
-    "naive_unpivoted_nonfinite", "pivot_factors", "max_threads", "load",
+    "naive_unpivoted_nonfinite", "pivot_factors", "max_threads", "load", "lowrank_gates",
 ]
 
 _LIB = None

@@ -199,6 +199,38 @@ def test_heads_past_32_bit_offsets_are_refused(T):
     assert st == 3 and "4 GiB" in msg, msg
 
 
+def _gates_call(**over):
+    lib = muir.lib()
+    args = dict(z=fake(0), Ua=fake(1), Ue=fake(2), Uw=fake(3), Ug=fake(4), ca=fake(5), ce=fake(6),
+                cw=fake(7), cg=fake(8), a=fake(9), e=fake(10), w=fake(11), g=fake(12), B=2, T=100,
+                H=3, d=64, stream=None)
+    args.update(over)
+    st = lib.muir_lowrank_gates(*[args[k] for k in ("z", "Ua", "Ue", "Uw", "Ug", "ca", "ce", "cw",
+                                                  "cg", "a", "e", "w", "g", "B", "T", "H", "d",
+                                                  "stream")])
+    return st, muir.last_error()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(d=32), 3),
+    (dict(z=None), 1), (dict(Ua=None), 1), (dict(cg=None), 1),
+    (dict(e=ctypes.c_void_p(BASE + 10 * STRIDE + 8)), 2),
+    (dict(w=fake(0)), 5), (dict(g=fake(11)), 5), (dict(a=fake(5)), 5),
+    (dict(T=1 << 24, H=64, d=128), 3),
+])
+def test_lowrank_gates_rejects_bad_arguments(over, status):
+    st, msg = _gates_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_lowrank_gates_skips_unrequested_gates():
+    # No output requested: nothing to check or launch, even with the weights absent.
+    st, msg = _gates_call(a=None, e=None, w=None, g=None, Ua=None, Ue=None, Uw=None, Ug=None,
+                          ca=None, ce=None, cw=None, cg=None, z=None)
+    assert st == 0, msg
+
+
 def _decode_call(**over):
     lib = muir.lib()
     args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),

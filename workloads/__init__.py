@@ -34,7 +34,7 @@ import numpy as np
 __all__ = [
     "ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG",
     "round_bf16", "chunk_inputs", "decode_base", "decode_step_inputs_torch",
-    "decode_seed", "output_gate", "scalar_erase",
+    "decode_seed", "output_gate", "scalar_erase", "lowrank_gate_inputs", "GATE_RANKS",
 ]
 
 
@@ -228,6 +228,56 @@ def scalar_erase(B: int, T: int, H: int, seed: int) -> np.ndarray:
     """One erase strength per token and head, e = sigmoid(N(0,1)) [B,T,H] float32, like the
     per-channel e, from a stream of its own (``SeedSequence((seed, 11))``)."""
     return _sigmoid(_normal(np.random.SeedSequence((seed, 11)), (B, T, H)))
+
+
+# Rank slices of the fused gate projection's output z, in the gate table's order: decay 64,
+# erase 64, output 128, write 128, read 128.
+GATE_RANKS = (("decay", 64), ("erase", 64), ("output", 128), ("write", 128), ("read", 128))
+
+
+def lowrank_gate_inputs(cfg: ChunkConfig | int, *, B=None, T=None, H=None, d=None,
+                        seed=None) -> dict:
+    """Inputs of the low-rank gate projection for a chunk workload: z [B,T,512] (the shared
+    down-projection's output) and, per gate n in (decay, erase, write, read), an
+    up-projection U_n [H,d,r_n] and an offset c_n [H,d].
+
+    Recipe (one stream each, from ``SeedSequence((seed, 12)).spawn(5)``: z, then U for
+    decay, erase, write, read): z ~ N(0,1); U_decay ~ N(0, 0.1^2/64), so that the decay's
+    log-rate jitter z U has std 0.1 as in the decay recipe, with c_decay = the base log
+    rate u of the configuration; U_erase, U_write, U_read ~ N(0, 1/r), so their
+    pre-activations are N(0,1) as for sigmoid(N(0,1)), with zero offsets. On stress heads
+    (h % 4 == 0 where the configuration has them) c_decay = ln(-ln 0.0255) and U_decay ~
+    N(0, 1/64): decays spread over roughly 1e-4 .. 0.25. z and every U are rounded to bf16.
+    """
+    if isinstance(cfg, int):
+        cfg = CHUNK_CONFIGS[cfg]
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    H = cfg.H if H is None else H
+    d = cfg.d if d is None else d
+    seed = cfg.seed if seed is None else seed
+    seqs = np.random.SeedSequence((seed, 12)).spawn(5)
+    u = _base_u(np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(9)[0])),
+                cfg.decay, cfg.hmax, (H, d))
+    z = round_bf16(_normal(seqs[0], (B, T, 512)))
+    out = {"z": z}
+    ranks = dict(GATE_RANKS)
+    stress = [h for h in range(H) if h % 4 == 0] if cfg.stress else []
+    for i, n in enumerate(("decay", "erase", "write", "read")):
+        r = ranks[n]
+        U = _normal(seqs[1 + i], (H, d, r))
+        if n == "decay":
+            U *= np.float32(0.1 / math.sqrt(r))
+            c = u.astype(np.float32)
+            for h in stress:
+                U[h] *= np.float32(10.0)
+                c[h] = np.float32(math.log(-math.log(0.0255)))
+        else:
+            U *= np.float32(1.0 / math.sqrt(r))
+            c = np.zeros((H, d), np.float32)
+        out["U_" + n] = round_bf16(U)
+        out["c_" + n] = c
+    return out
 
 
 def decode_base(cfg: DecodeConfig = DECODE_CONFIG, *, L=None, H=None, d=None):
