@@ -7,8 +7,9 @@ then the sequential phase (block-Neumann solve, readout, state carry). ``value``
 tokens/s per layer over the timed steps, with inputs already resident in HBM.
 
 Also measured in the same run and reported as secondary fields: the 1.34B-class
-shape at T=4096 (B=8, chunk 128 and 256), and the decode step (B=256 x H=16 x 128x128
-fp32 states, one layer call) in GB/s. Each kernel's average duration comes from HIP
+shape at T=4096 (B=8, chunk 128 and 256), the output-gate epilogue, the shared-erase
+variant, the forward with its gates made from the low-rank gate projection, and the
+decode step (B=256 x H=16 x 128x128 fp32 states, one layer call) in GB/s. Each kernel's average duration comes from HIP
 events recorded around it on the stream it runs on. ``cpu_baseline`` is the CPU
 oracle's fp32 token recurrence on the same long-context workload.
 
@@ -182,6 +183,51 @@ def time_scalar_erase(inp, es, chunk, dev, steps, warmup):
             "hbm_frac": nbytes * tok_heads / sec / HBM_PEAK}
 
 
+def time_lowrank(inp, lr, chunk, dev, steps, warmup):
+    """The forward with its gates from the low-rank gate projection: the fused call
+    (muir_chunk_fwd_lowrank) and, for comparison, the gate kernel writing all four gates
+    followed by the plain forward; each timed with HIP events over `steps` calls."""
+    import torch
+    import gated_delta_rule_06_amd as muir
+    t = to_dev(inp, dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    z = torch.from_numpy(lr["z"]).to(dev, torch.bfloat16)
+    names = ("decay", "erase", "write", "read")
+    U = {n: torch.from_numpy(lr["U_" + n]).to(dev, torch.bfloat16) for n in names}
+    c = {n: torch.from_numpy(lr["c_" + n]).to(dev) for n in names}
+    o = torch.empty_like(t["v"])
+    s_out = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(int(muir.lib().muir_chunk_fwd_lowrank_workspace_size(B, T, H, d, d, chunk)),
+                     dtype=torch.uint8, device=dev)
+    gates = {k: torch.empty((B, T, H, d), dtype=torch.float32, device=dev) for k in "aewg"}
+
+    def fused():
+        muir.chunk_fwd_lowrank(t["q"], t["k"], t["v"], z, U, c, t["r"], chunk=chunk, o=o,
+                               s_out=s_out, workspace=ws)
+
+    def unfused():
+        muir.lowrank_gates(z, U, c, H=H, d=d, out=gates)
+        muir.chunk_fwd(t["q"], t["k"], t["v"], gates["a"], gates["g"], gates["e"], gates["w"],
+                       t["r"], chunk=chunk, o=o, s_out=s_out, workspace=ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    tf, tu = timed(fused), timed(unfused)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s_out).all()
+    return {"tokens_per_s_per_layer": B * T / (tf * 1e-3), "ms_per_call": tf,
+            "unfused_ms_per_call": tu}
+
+
 def chunk_report(name, inp, chunk, r):
     d, tok_heads = inp["d"], inp["B"] * inp["T"] * inp["H"]
     alg = algorithmic(d, chunk)
@@ -255,7 +301,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "scalar", "copy"],
+    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "scalar", "lowrank", "copy"],
                     default="all",
                     help="'copy' times a plain 1 GiB device copy: the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -352,6 +398,23 @@ def main():
             del inp, es
         if "value" not in result:
             first = secondary["long_context_scalar_erase"]
+            result["value"] = first["tokens_per_s_per_layer"]
+            result["ms_per_step"] = first["ms_per_call"]
+            result["config"] = {"workload": first["workload"]}
+    if args.only in ("all", "lowrank"):
+        # Gates from the low-rank gate projection, made inside the call.
+        for cfg, chunk, key in ((3, 256, "long_context_lowrank_gates"),
+                                (2, 128, "t4k_c128_lowrank_gates")):
+            inp = main_inp if (cfg == 3 and main_inp is not None) else workloads.chunk_inputs(cfg)
+            lr = workloads.lowrank_gate_inputs(cfg)
+            name = (f"chunk_fwd_lowrank B{inp['B']} H{inp['H']} d{inp['d']} T{inp['T']} C{chunk} "
+                    f"bf16, gates from z [B,T,512] and rank 64/64/128/128 up-projections")
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            secondary[key] = {"workload": name, "chunk": chunk,
+                              **time_lowrank(inp, lr, chunk, dev, args.steps, args.warmup)}
+            del inp, lr
+        if "value" not in result:
+            first = secondary["long_context_lowrank_gates"]
             result["value"] = first["tokens_per_s_per_layer"]
             result["ms_per_step"] = first["ms_per_call"]
             result["config"] = {"workload": first["workload"]}

@@ -18,7 +18,7 @@ __all__ = [
     "MuirError", "lib", "chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_prepare",
     "chunk_fwd_scan", "chunk_fwd_scalar_erase", "chunk_fwd_scalar_erase_workspace_size",
     "chunk_fwd_scalar_erase_solve",
-    "chunk_fwd_scalar_erase_scan", "lowrank_gates", "decode_step",
+    "chunk_fwd_scalar_erase_scan", "lowrank_gates", "chunk_fwd_lowrank", "decode_step",
     "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
 ]
 
@@ -71,6 +71,10 @@ def lib():
         L.muir_chunk_fwd_scalar_erase_solve.restype = i
         L.muir_chunk_fwd_scalar_erase_scan.argtypes = [vp] * 3 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd_scalar_erase_scan.restype = i
+        L.muir_chunk_fwd_lowrank_workspace_size.argtypes = [i] * 6
+        L.muir_chunk_fwd_lowrank_workspace_size.restype = sz
+        L.muir_chunk_fwd_lowrank.argtypes = [vp] * 16 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_lowrank.restype = i
         L.muir_lowrank_gates.argtypes = [vp] * 13 + [i] * 4 + [vp]
         L.muir_lowrank_gates.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
@@ -347,6 +351,39 @@ def lowrank_gates(z, U, c, *, H: int, d: int, which=("a", "e", "w", "g"), out=No
         _ptr(z), *[_ptr(x[0]) for x in args], *[_ptr(x[1]) for x in args],
         *[_ptr(x[2]) for x in args], B, T, H, d, _stream(dev)))
     return {k: v for k, v in out.items() if k in which}
+
+
+def chunk_fwd_lowrank(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None, s_out=None,
+                      return_state: bool = True, workspace=None):
+    """Chunk forward with the gates made from the low-rank gate projection inside the call
+    (``muir_chunk_fwd_lowrank``). q, k, v bfloat16 as for :func:`chunk_fwd`; z, U, c as for
+    :func:`lowrank_gates` (all four gates). Returns (o, s_out)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, (B, T, H, dk if name != "v" else dv), dev)
+    _require(z, "z", torch.bfloat16, (B, T, 512), dev)
+    for n, rk in (("decay", 64), ("erase", 64), ("write", 128), ("read", 128)):
+        _require(U[n], "U_" + n, torch.bfloat16, (H, dk, rk), dev)
+        _require(c[n], "c_" + n, torch.float32, (H, dk), dev)
+    _require(r, "r", torch.float32, (H, dk), dev)
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if s_out is None and return_state:
+        s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    need = int(lib().muir_chunk_fwd_lowrank_workspace_size(B, T, H, dk, dv, chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().muir_chunk_fwd_lowrank(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(U["decay"]), _ptr(U["erase"]), _ptr(U["write"]),
+        _ptr(U["read"]), _ptr(c["decay"]), _ptr(c["erase"]), _ptr(c["write"]), _ptr(c["read"]),
+        _ptr(r), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, MUIR_BF16,
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, s_out
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

@@ -355,6 +355,83 @@ muir_status_t muir_chunk_fwd_scalar_erase_scan(const float *s0, void *o, float *
                      "chunk_fwd_scalar_erase_scan launch");
 }
 
+size_t muir_chunk_fwd_lowrank_workspace_size(int B, int T, int H, int dk, int dv, int chunk) {
+    const size_t base = muir_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, MUIR_BF16);
+    if (base == 0 && T > 0) return 0;
+    size_t gates;
+    if (!mul_size(gates, {static_cast<size_t>(B), static_cast<size_t>(T), static_cast<size_t>(H),
+                          static_cast<size_t>(dv), 8}))
+        return 0;
+    const size_t aligned = (base + 255) & ~size_t(255);
+    return aligned + gates < aligned ? 0 : aligned + gates;
+}
+
+muir_status_t muir_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const void *z,
+                                     const void *Ua, const void *Ue, const void *Uw,
+                                     const void *Ug, const float *ca, const float *ce,
+                                     const float *cw, const float *cg, const float *r,
+                                     const float *s0, void *o, float *s_out, int B, int T, int H,
+                                     int dk, int dv, int chunk, muir_dtype_t qkv, void *workspace,
+                                     size_t workspace_bytes, muir_stream_t stream) {
+    const char *fn = "chunk_fwd_lowrank";
+    if (qkv != MUIR_BF16)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: the fused low-rank gates need bf16 q, k, v", fn);
+    // Shape, pointer, alignment and aliasing checks of the plain forward, with the gate
+    // tensors standing in as absent: the gates are made inside the call.
+    const size_t base = muir::chunk_workspace_bytes(B, T, H, dk, chunk, true);
+    const size_t ebase = (base + 255) & ~size_t(255);
+    ChunkCall c{fn, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr, r, s0, o, s_out, B, T, H,
+                dk, dv, chunk, qkv, workspace, workspace_bytes, false, false, false};
+    muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T > 0 && (!q || !k || !v || !o || !z)) return fail(MUIR_ERR_NULL, "%s: q, k, v, z and o are required", fn);
+    if (!r || !Ua || !Ue || !Uw || !Ug || !ca || !ce || !cw || !cg)
+        return fail(MUIR_ERR_NULL, "%s: r and every up-projection and offset are required", fn);
+    const size_t need = muir_chunk_fwd_lowrank_workspace_size(B, T, H, dk, dv, chunk);
+    if (need == 0 && T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (T > 0 && (!workspace || workspace_bytes < need))
+        return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+    if (static_cast<size_t>(T) * 512 * 2 > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: one batch row of z exceeds 4 GiB", fn);
+    const size_t n_tok = static_cast<size_t>(B) * T * H * dk;
+    const Range ins[] = {range("q", q, n_tok * 2), range("k", k, n_tok * 2), range("v", v, n_tok * 2),
+                         range("z", z, static_cast<size_t>(B) * T * 512 * 2),
+                         range("Ua", Ua, static_cast<size_t>(H) * dk * 64 * 2),
+                         range("Ue", Ue, static_cast<size_t>(H) * dv * 64 * 2),
+                         range("Uw", Uw, static_cast<size_t>(H) * dv * 128 * 2),
+                         range("Ug", Ug, static_cast<size_t>(H) * dk * 128 * 2),
+                         range("ca", ca, static_cast<size_t>(H) * dk * 4), range("ce", ce, static_cast<size_t>(H) * dv * 4),
+                         range("cw", cw, static_cast<size_t>(H) * dv * 4), range("cg", cg, static_cast<size_t>(H) * dk * 4)};
+    const Range outs[] = {range("o", o, n_tok * 2), range("workspace", workspace, need),
+                          range("s_out", s_out, static_cast<size_t>(B) * H * dk * dv * 4)};
+    for (const Range &x : ins) {
+        if (x.lo % 16 != 0) return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
+        for (const Range &y : outs)
+            if (overlaps(x, y)) return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, y.name, x.name);
+    }
+    if (T == 0) {
+        if (!s_out) return ok();
+        return check_hip(muir::launch_chunk_scan(v, nullptr, nullptr, nullptr, s0, o, s_out, B, T, H,
+                                                 dk, chunk, true, workspace,
+                                                 static_cast<hipStream_t>(stream)),
+                         fn);
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    float *e = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ebase);
+    float *w = e + n_tok;
+    st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, nullptr, ce, cw, nullptr,
+                                              nullptr, e, w, nullptr, B, T, H, dv, hs),
+                   "chunk_fwd_lowrank gates");
+    if (st != MUIR_OK) return st;
+    st = check_hip(muir::launch_chunk_prepare_lowrank(q, k, z, Ua, Ug, ca, cg, r, B, T, H, dk, chunk,
+                                                      workspace, hs),
+                   "chunk_fwd_lowrank prepare");
+    if (st != MUIR_OK) return st;
+    return check_hip(muir::launch_chunk_scan(v, e, w, nullptr, s0, o, s_out, B, T, H, dk, chunk, true,
+                                             workspace, hs),
+                     "chunk_fwd_lowrank scan");
+}
+
 muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
                                 const void *Ug, const float *ca, const float *ce, const float *cw,
                                 const float *cg, float *a, float *e, float *w, float *g, int B,

@@ -421,11 +421,39 @@ template <int D> __device__ __forceinline__ int swz(int row, int chunk) {
 //   block (the scan's nested levels give every level's running products); the
 //   off-diagonal blocks (bt, bs) against the K*sigma of all earlier blocks kept in LDS,
 //   scaled by the decay of the whole blocks in between.
-template <int D, int C>
+//
+// LR: the decay a and the query gate g are not read but formed from the low-rank gate
+// projection (the pages' fused rank-512 gate projection: openai-hub page, section on
+// sensitivity-allocated gating, gate table): a = exp(-exp(z_decay . U_a + c_a)) and
+// g = sigmoid(z_read . U_g + c_g), each a 16-channel x 16-token matrix-core tile per K = 32
+// rank step, whose accumulator is exactly this thread's (token, 8 channels) share. The
+// wavefront's up-projection rows stay in registers for the whole chunk; z rows (shared by
+// every head) replace the fp32 a and g rows in the pair prefetch.
+struct LowRankGates {
+    const bf16_t *z;          // [B, T, 512]
+    const bf16_t *Ua, *Ug;    // [H, D, 64], [H, D, 128]
+    const float *ca, *cg;     // [H, D]
+};
+constexpr int kZRankAll = 512, kZOffDecay = 0, kZOffRead = 384;
+
+// LDS of the LR variant, after the prepare's own: the head's U_g rows (and U_a's when they
+// fit, else each wavefront keeps its four U_a fragments in registers), rows padded against
+// bank conflicts, and the two offset vectors.
+template <int D, int C> struct LrLds {
+    static constexpr int UAP = 64 + 8, UGP = 128 + 8;  // row pitches, elements
+    static constexpr size_t UG_OFF = Prep2Lds<D, C>::BYTES;
+    static constexpr size_t CO_OFF = UG_OFF + size_t(D) * UGP * 2;  // [2][D] fp32: c_a, c_g
+    static constexpr size_t UA_OFF = CO_OFF + size_t(2) * D * 4;
+    static constexpr bool UA_IN_LDS = UA_OFF + size_t(D) * UAP * 2 <= 160 * 1024 - 1024;
+    static constexpr size_t BYTES = UA_IN_LDS ? UA_OFF + size_t(D) * UAP * 2 : UA_OFF;
+    static_assert(UA_OFF <= 160 * 1024 - 1024, "LDS budget");
+};
+
+template <int D, int C, bool LR>
 __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const float *__restrict__ a,
-    const float *__restrict__ g, const float *__restrict__ r, unsigned char *__restrict__ ws,
-    int T, int H, int nchunks) {
+    const float *__restrict__ g, const float *__restrict__ r, LowRankGates lr,
+    unsigned char *__restrict__ ws, int T, int H, int nchunks) {
     using SL = Slot<bf16_t, D, C>;
     using LY = Prep2Lds<D, C>;
     using F = Frag<bf16_t>;
@@ -463,19 +491,38 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     const size_t HD = size_t(H) * D;
     const size_t base = (size_t(b) * T + t0) * HD + size_t(hh) * D;
     const unsigned span = unsigned((size_t(nreal - 1) * HD + D));
-    const rsrc_t ra = make_rsrc(a + base, span * 4u), rg = make_rsrc(g + base, span * 4u);
     const rsrc_t rk = make_rsrc(k + base, span * 2u), rq = make_rsrc(q + base, span * 2u);
     const unsigned vo = unsigned(size_t(t) * HD + chl);
-    struct In {
+    // Gate rows: fp32 a and g, or (LR) the z rows of the decay and read slices, K = 32 rank
+    // steps of 8 values per lane (lane (t, G): token t, ranks 32s + 8G .. + 7).
+    struct GateIn {
         f32x4_t a0, a1, g0, g1;
+    };
+    struct GateInLR {
+        f8 zd[2], zg[4];
+    };
+    struct In : std::conditional_t<LR, GateInLR, GateIn> {
         u16x4_t k0, k1, q0, q1;
     };
+    const rsrc_t ra = make_rsrc(LR ? nullptr : a + base, LR ? 0u : span * 4u);
+    const rsrc_t rg = make_rsrc(LR ? nullptr : g + base, LR ? 0u : span * 4u);
+    const rsrc_t rz = make_rsrc(LR ? lr.z + (size_t(b) * T + t0) * kZRankAll : nullptr,
+                                LR ? unsigned(nreal) * kZRankAll * 2u : 0u);
     auto load_in = [&](int p, In &in) {
         const unsigned row = unsigned(32 * p + 16 * hb) * unsigned(HD);
-        in.a0 = buf_load_f4(ra, vo * 4u, row * 4u);
-        in.a1 = buf_load_f4(ra, vo * 4u + 64u, row * 4u);
-        in.g0 = buf_load_f4(rg, vo * 4u, row * 4u);
-        in.g1 = buf_load_f4(rg, vo * 4u + 64u, row * 4u);
+        if constexpr (LR) {
+            const unsigned zrow = unsigned(32 * p + 16 * hb) * (kZRankAll * 2u);
+            const unsigned zo = unsigned(t) * (kZRankAll * 2u) + unsigned(8 * G) * 2u;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) in.zd[s] = F::bload8(rz, zo + unsigned(kZOffDecay + 32 * s) * 2u, zrow);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) in.zg[s] = F::bload8(rz, zo + unsigned(kZOffRead + 32 * s) * 2u, zrow);
+        } else {
+            in.a0 = buf_load_f4(ra, vo * 4u, row * 4u);
+            in.a1 = buf_load_f4(ra, vo * 4u + 64u, row * 4u);
+            in.g0 = buf_load_f4(rg, vo * 4u, row * 4u);
+            in.g1 = buf_load_f4(rg, vo * 4u + 64u, row * 4u);
+        }
         in.k0 = Row4<bf16_t>::load(rk, vo * 2u, row * 2u);
         in.k1 = Row4<bf16_t>::load(rk, vo * 2u + 32u, row * 2u);
         in.q0 = Row4<bf16_t>::load(rq, vo * 2u, row * 2u);
@@ -484,6 +531,31 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     float rr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) rr[j] = r[size_t(hh) * D + chl + (j & 3) + 16 * (j >> 2)];
+    // LR: the head's up-projection rows and offsets into LDS (U_a, when it does not fit,
+    // is read per pair from the head's rows in memory, which stay in the L1 cache).
+    using LL = LrLds<D, C>;
+    if constexpr (LR) {
+        bf16_t *sh_ug = reinterpret_cast<bf16_t *>(smem + LL::UG_OFF);
+        float *sh_co = reinterpret_cast<float *>(smem + LL::CO_OFF);
+        for (int n = tid; n < D * 16; n += NT) {  // U_g: D rows x 16 chunks of 8
+            const int row = n >> 4, c8 = n & 15;
+            *reinterpret_cast<f8 *>(sh_ug + row * LL::UGP + 8 * c8) =
+                F::load8(lr.Ug + (size_t(hh) * D + row) * 128 + 8 * c8);
+        }
+        for (int n = tid; n < D; n += NT) {
+            sh_co[n] = lr.ca[size_t(hh) * D + n];
+            sh_co[D + n] = lr.cg[size_t(hh) * D + n];
+        }
+        if constexpr (LL::UA_IN_LDS) {
+            bf16_t *sh_ua = reinterpret_cast<bf16_t *>(smem + LL::UA_OFF);
+            for (int n = tid; n < D * 8; n += NT) {
+                const int row = n >> 3, c8 = n & 7;
+                *reinterpret_cast<f8 *>(sh_ua + row * LL::UAP + 8 * c8) =
+                    F::load8(lr.Ua + (size_t(hh) * D + row) * 64 + 8 * c8);
+            }
+        }
+        lds_barrier();
+    }
 
     auto pack8 = [](const float (&x)[8]) {
         return F::cat(F::pack(f32x4_t{x[0], x[1], x[2], x[3]}), F::pack(f32x4_t{x[4], x[5], x[6], x[7]}));
@@ -538,14 +610,49 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
         float av[8], kv[8], qh[8];
         {
             const bool real = 16 * bt + t < nreal;
+            f32x4_t a0, a1, g0, g1;
+            if constexpr (LR) {
+                const bf16_t *sh_ug = reinterpret_cast<const bf16_t *>(smem + LL::UG_OFF);
+                const float *sh_co = reinterpret_cast<const float *>(smem + LL::CO_OFF);
+                f32x4_t y[4];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    y[ct] = *reinterpret_cast<const f32x4_t *>(sh_co + chl + 16 * ct);
+                    y[2 + ct] = *reinterpret_cast<const f32x4_t *>(sh_co + D + chl + 16 * ct);
+                    const int row = 32 * cg + 16 * ct + t;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        f8 ua;
+                        if constexpr (LL::UA_IN_LDS)
+                            ua = *reinterpret_cast<const f8 *>(reinterpret_cast<const bf16_t *>(smem + LL::UA_OFF) +
+                                                               row * LL::UAP + 32 * s + 8 * G);
+                        else
+                            ua = F::load8(lr.Ua + (size_t(hh) * D + row) * 64 + 32 * s + 8 * G);
+                        y[ct] = F::mma8(ua, in.zd[s], y[ct]);
+                    }
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        y[2 + ct] = F::mma8(*reinterpret_cast<const f8 *>(sh_ug + row * LL::UGP + 32 * s + 8 * G),
+                                            in.zg[s], y[2 + ct]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a0[i] = gate_decay(y[0][i]);
+                    a1[i] = gate_decay(y[1][i]);
+                    g0[i] = gate_sigmoid(y[2][i]);
+                    g1[i] = gate_sigmoid(y[3][i]);
+                }
+            } else {
+                a0 = in.a0; a1 = in.a1; g0 = in.g0; g1 = in.g1;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                av[i] = real ? in.a0[i] : 1.f;
-                av[4 + i] = real ? in.a1[i] : 1.f;
+                av[i] = real ? a0[i] : 1.f;
+                av[4 + i] = real ? a1[i] : 1.f;
                 kv[i] = bf16_to_f32(in.k0[i]);
                 kv[4 + i] = bf16_to_f32(in.k1[i]);
-                qh[i] = rr[i] * in.g0[i] * bf16_to_f32(in.q0[i]);
-                qh[4 + i] = rr[4 + i] * in.g1[i] * bf16_to_f32(in.q1[i]);
+                qh[i] = rr[i] * g0[i] * bf16_to_f32(in.q0[i]);
+                qh[4 + i] = rr[4 + i] * g1[i] * bf16_to_f32(in.q1[i]);
             }
         }
         if (p + 1 < NP) load_in(p + 1, in);
@@ -1165,20 +1272,20 @@ size_t slot_bytes_rt(bool bf16, int d, int chunk) {
 
 template <typename QT, typename OpT, int D, int C>
 hipError_t prepare_typed(const void *q, const void *k, const float *a, const float *g,
-                         const float *r, int B, int T, int H, void *workspace,
-                         hipStream_t stream) {
+                         const float *r, const LowRankGates &lr, int B, int T, int H,
+                         void *workspace, hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
     if (nchunks == 0) return hipSuccess;
     if constexpr (std::is_same_v<OpT, bf16_t>) {
-        using LY = Prep2Lds<D, C>;
-        auto kern = chunk_prepare_bf16_kernel<D, C>;
+        const size_t lds = lr.z ? LrLds<D, C>::BYTES : Prep2Lds<D, C>::BYTES;
+        auto kern = lr.z ? chunk_prepare_bf16_kernel<D, C, true> : chunk_prepare_bf16_kernel<D, C, false>;
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(LY::BYTES));
+                                             static_cast<int>(lds));
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(4 * D), LY::BYTES, stream,
+        hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(4 * D), lds, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), a, g,
-                           r, static_cast<unsigned char *>(workspace), T, H, nchunks);
+                           r, lr, static_cast<unsigned char *>(workspace), T, H, nchunks);
         return hipGetLastError();
     } else {
         using LY = PrepLds<OpT, D, C>;
@@ -1227,11 +1334,29 @@ size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
 hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, const float *g,
                                 const float *r, int B, int T, int H, int d, int chunk, bool bf16,
                                 void *workspace, hipStream_t stream) {
+    const LowRankGates none{nullptr, nullptr, nullptr, nullptr, nullptr};
 #define MUIR_PREP(D, C)                                                                        \
     if (d == D && chunk == C)                                                                  \
-        return bf16 ? prepare_typed<bf16_t, bf16_t, D, C>(q, k, a, g, r, B, T, H, workspace,    \
-                                                          stream)                              \
-                    : prepare_typed<float, float, D, C>(q, k, a, g, r, B, T, H, workspace, stream);
+        return bf16 ? prepare_typed<bf16_t, bf16_t, D, C>(q, k, a, g, r, none, B, T, H,         \
+                                                          workspace, stream)                   \
+                    : prepare_typed<float, float, D, C>(q, k, a, g, r, none, B, T, H,           \
+                                                        workspace, stream);
+    MUIR_PREP(64, 64) MUIR_PREP(64, 128) MUIR_PREP(64, 256)
+    MUIR_PREP(128, 64) MUIR_PREP(128, 128) MUIR_PREP(128, 256)
+#undef MUIR_PREP
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_prepare_lowrank(const void *q, const void *k, const void *z,
+                                        const void *Ua, const void *Ug, const float *ca,
+                                        const float *cg, const float *r, int B, int T, int H,
+                                        int d, int chunk, void *workspace, hipStream_t stream) {
+    const LowRankGates lr{static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ua),
+                          static_cast<const bf16_t *>(Ug), ca, cg};
+#define MUIR_PREP(D, C)                                                                        \
+    if (d == D && chunk == C)                                                                  \
+        return prepare_typed<bf16_t, bf16_t, D, C>(q, k, nullptr, nullptr, r, lr, B, T, H,      \
+                                                   workspace, stream);
     MUIR_PREP(64, 64) MUIR_PREP(64, 128) MUIR_PREP(64, 256)
     MUIR_PREP(128, 64) MUIR_PREP(128, 128) MUIR_PREP(128, 256)
 #undef MUIR_PREP

@@ -42,6 +42,11 @@ template <> struct elem<bf16_t> {
     }
 };
 
+// Activations of the low-rank gate projection: the decay from its log rate y, in (0, 1],
+// and the logistic function for the other gates.
+__device__ __forceinline__ float gate_decay(float y) { return __expf(-__expf(y)); }
+__device__ __forceinline__ float gate_sigmoid(float y) { return 1.f / (1.f + __expf(-y)); }
+
 // Sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -13,7 +13,8 @@
 // Each product is a 16-token x 16-channel tile with the rank as the contraction, on the
 // matrix cores: the up-projection's rows (channels) are the A operand and z's rows
 // (tokens) the B operand, so lane (t, G) of the accumulator holds token t and channels
-// 4G .. 4G + 3 of the tile: one 16-byte store of four gate values per lane.
+// 4G .. 4G + 3 of the tile: one 16-byte store of four gate values per lane. The offset
+// c_n is the accumulator's initial value.
 #include "chunk_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -28,114 +29,116 @@ constexpr int kZRank = 512;
 constexpr int kOffDecay = 0, kOffErase = 64, kOffWrite = 256, kOffRead = 384;
 constexpr int kRankDecay = 64, kRankErase = 64, kRankWrite = 128, kRankRead = 128;
 
-__device__ __forceinline__ float decay_of(float y) { return __expf(-__expf(y)); }
-__device__ __forceinline__ float sigmoid_of(float y) { return 1.f / (1.f + __expf(-y)); }
-
-// One gate's up-projection rows for one 16-channel tile, held as A operands: lane (x, G)
-// holds channel 16c + x, ranks 32s + 8G .. + 7 of K-step s.
-template <int R> struct UpRows {
-    Frag<bf16_t>::f8 f[R / 32];
-    f32x4_t off;  // c_n at channels 16c + 4G + r (the accumulator's rows of lane (t, G))
+// LDS of the gate kernel: the head's up-projection rows of the requested gates (row pitch
+// padded by 8 elements against bank conflicts) and their offsets; gate n's region starts at
+// the byte offset the host computes (unrequested gates take no room).
+constexpr int kPad = 8;
+struct GateLds {
+    int u_off[4];   // byte offsets of U_n rows, [D][r_n + kPad] bf16
+    int c_off[4];   // byte offsets of c_n, [D] fp32
+    int bytes;
 };
-
-template <int R>
-__device__ __forceinline__ void load_up(UpRows<R> &u, const bf16_t *U, const float *c, int h,
-                                        int D, int ch0, int lane) {
-    const int x = lane & 15, G = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < R / 32; ++s)
-        u.f[s] = Frag<bf16_t>::load8(U + (size_t(h) * D + ch0 + x) * R + 32 * s + 8 * G);
-    u.off = *reinterpret_cast<const f32x4_t *>(c + size_t(h) * D + ch0 + 4 * G);
+__host__ __device__ constexpr int gate_rank(int n) { return n < 2 ? 64 : 128; }
+__host__ __device__ constexpr int gate_zoff(int n) {
+    return n == 0 ? kOffDecay : n == 1 ? kOffErase : n == 2 ? kOffWrite : kOffRead;
 }
 
-// y (pre-activation) of one gate for the token block whose z rows this lane group loaded.
-template <int R>
-__device__ __forceinline__ f32x4_t preact(const UpRows<R> &u, const Frag<bf16_t>::f8 *zr) {
-    f32x4_t acc = u.off;
-#pragma unroll
-    for (int s = 0; s < R / 32; ++s) acc = Frag<bf16_t>::mma8(u.f[s], zr[s], acc);
-    return acc;
-}
-
-// One wavefront per (head, 16-channel tile, batch, token-block group): the up-projection
-// rows stay in registers while the wavefront walks its token blocks. Gates whose output
-// pointer is null are skipped.
+// One workgroup of four wavefronts per (head, batch, token-block group). The head's
+// up-projection rows sit in LDS, so each z row a wavefront loads serves every channel tile
+// of the head: per token block, z's four slices are loaded once (the next block's while the
+// current one computes), then for each 16-channel tile every requested gate is one short
+// chain of K = 32 products. Gates whose output pointer is null are skipped.
 template <int D>
 __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const bf16_t *__restrict__ z, const bf16_t *__restrict__ Ua, const bf16_t *__restrict__ Ue,
     const bf16_t *__restrict__ Uw, const bf16_t *__restrict__ Ug, const float *__restrict__ ca,
     const float *__restrict__ ce, const float *__restrict__ cw, const float *__restrict__ cg,
     float *__restrict__ a, float *__restrict__ e, float *__restrict__ w, float *__restrict__ g,
-    int T, int H, int nwaves_t) {
+    int T, int H, GateLds lay) {
     using F = Frag<bf16_t>;
     using f8 = F::f8;
     constexpr int NCT = D / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-    const int lane = threadIdx.x & 63, x = lane & 15, G = lane >> 4;
-    const int h = blockIdx.x / NCT, c = blockIdx.x % NCT, b = blockIdx.y;
-    const int tw = blockIdx.z * 4 + wave;  // this wavefront's index along the token blocks
-    const int ch0 = 16 * c;
+    const int tid = threadIdx.x, lane = tid & 63, x = lane & 15, G = lane >> 4;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tw = blockIdx.z * 4 + wave, nw = gridDim.z * 4;
     const int nblk = (T + 15) / 16;
+    const bf16_t *U[4] = {Ua, Ue, Uw, Ug};
+    const float *cc[4] = {ca, ce, cw, cg};
+    float *out[4] = {a, e, w, g};
 
-    UpRows<kRankDecay> ua;
-    UpRows<kRankErase> ue;
-    UpRows<kRankWrite> uw;
-    UpRows<kRankRead> ug;
-    if (a) load_up(ua, Ua, ca, h, D, ch0, lane);
-    if (e) load_up(ue, Ue, ce, h, D, ch0, lane);
-    if (w) load_up(uw, Uw, cw, h, D, ch0, lane);
-    if (g) load_up(ug, Ug, cg, h, D, ch0, lane);
+    // The head's rows of every requested gate into LDS.
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        if (!out[n]) continue;
+        const int R = gate_rank(n), pitch = R + kPad, per_row = R / 8;
+        bf16_t *su = reinterpret_cast<bf16_t *>(smem + lay.u_off[n]);
+        for (int i = tid; i < D * per_row; i += 256) {
+            const int row = i / per_row, c8 = i % per_row;
+            *reinterpret_cast<f8 *>(su + row * pitch + 8 * c8) =
+                F::load8(U[n] + (size_t(h) * D + row) * R + 8 * c8);
+        }
+        float *sc = reinterpret_cast<float *>(smem + lay.c_off[n]);
+        for (int i = tid; i < D; i += 256) sc[i] = cc[n][size_t(h) * D + i];
+    }
+    lds_barrier();
 
-    // z rows of this batch through a descriptor: tokens at or past T read zero. Gate
-    // stores likewise: tokens at or past T are dropped.
     const rsrc_t rz = make_rsrc(z + size_t(b) * T * kZRank, unsigned(size_t(T) * kZRank * 2));
     const size_t HD = size_t(H) * D;
-    const size_t gbase = size_t(b) * T * HD + size_t(h) * D + ch0;  // uniform
-    const unsigned gbytes = unsigned((size_t(T) * HD - size_t(h) * D - ch0) * 4);
-    auto store = [&](float *p, int t, f32x4_t v) {
-        const rsrc_t r = make_rsrc(p + gbase, gbytes);
-        const unsigned off = (unsigned(min(t, T)) * unsigned(HD) + unsigned(4 * G)) * 4u;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(off), 0, 0);
+    const size_t gbase = size_t(b) * T * HD + size_t(h) * D;  // uniform
+    const unsigned gbytes = unsigned((size_t(T) * HD - size_t(h) * D) * 4);
+
+    struct ZRows {
+        f8 r[12];  // decay 2, erase 2, write 4, read 4 K-steps
     };
-    for (int tb = tw; tb < nblk; tb += nwaves_t) {
-        const int t = 16 * tb + x;
-        const unsigned zoff = unsigned(min(t, T)) * unsigned(kZRank) * 2u + unsigned(8 * G) * 2u;
-        auto zrow = [&](int off, f8 *dst, int nsteps) {
+    constexpr int kStep0[4] = {0, 2, 4, 8};
+    auto load_z = [&](int tb, ZRows &zr) {
+        const unsigned t = unsigned(min(16 * tb + x, T));
+        const unsigned zoff = t * unsigned(kZRank) * 2u + unsigned(8 * G) * 2u;
 #pragma unroll
-            for (int s = 0; s < nsteps; ++s)
-                dst[s] = F::bload8(rz, zoff + unsigned(off + 32 * s) * 2u, 0u);
-        };
-        if (a) {
-            f8 zr[kRankDecay / 32];
-            zrow(kOffDecay, zr, kRankDecay / 32);
-            f32x4_t y = preact(ua, zr);
+        for (int n = 0; n < 4; ++n) {
+            if (!out[n]) continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = decay_of(y[r]);
-            store(a, t, y);
+            for (int s = 0; s < gate_rank(n) / 32; ++s)
+                zr.r[kStep0[n] + s] = F::bload8(rz, zoff + unsigned(gate_zoff(n) + 32 * s) * 2u, 0u);
         }
-        if (e) {
-            f8 zr[kRankErase / 32];
-            zrow(kOffErase, zr, kRankErase / 32);
-            f32x4_t y = preact(ue, zr);
+    };
+    auto compute = [&](int tb, const ZRows &zr) {
+        const unsigned t = unsigned(min(16 * tb + x, T));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = sigmoid_of(y[r]);
-            store(e, t, y);
+        for (int n = 0; n < 4; ++n) {
+            if (!out[n]) continue;
+            const int R = gate_rank(n), pitch = R + kPad;
+            const bf16_t *su = reinterpret_cast<const bf16_t *>(smem + lay.u_off[n]);
+            const float *sc = reinterpret_cast<const float *>(smem + lay.c_off[n]);
+            const rsrc_t ro = make_rsrc(out[n] + gbase, gbytes);
+#pragma unroll 2
+            for (int c = 0; c < NCT; ++c) {
+                f32x4_t y = *reinterpret_cast<const f32x4_t *>(sc + 16 * c + 4 * G);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    if (s < R / 32)
+                        y = F::mma8(*reinterpret_cast<const f8 *>(su + (16 * c + x) * pitch + 32 * s + 8 * G),
+                                    zr.r[kStep0[n] + s], y);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] = n == 0 ? gate_decay(y[r]) : gate_sigmoid(y[r]);
+                const unsigned off = (t * unsigned(HD) + unsigned(16 * c + 4 * G)) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, y), ro, int(off), 0, 0);
+            }
         }
-        if (w) {
-            f8 zr[kRankWrite / 32];
-            zrow(kOffWrite, zr, kRankWrite / 32);
-            f32x4_t y = preact(uw, zr);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = sigmoid_of(y[r]);
-            store(w, t, y);
-        }
-        if (g) {
-            f8 zr[kRankRead / 32];
-            zrow(kOffRead, zr, kRankRead / 32);
-            f32x4_t y = preact(ug, zr);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = sigmoid_of(y[r]);
-            store(g, t, y);
+    };
+    // Two z buffers, alternate token blocks (two blocks per iteration keep register indices
+    // static).
+    ZRows z0, z1;
+    if (tw < nblk) load_z(tw, z0);
+    for (int tb = tw; tb < nblk; tb += 2 * nw) {
+        const int tb1 = tb + nw;
+        if (tb1 < nblk) load_z(tb1, z1);
+        compute(tb, z0);
+        if (tb1 < nblk) {
+            if (tb1 + nw < nblk) load_z(tb1 + nw, z0);
+            compute(tb1, z1);
         }
     }
 }
@@ -146,17 +149,32 @@ hipError_t gates_typed(const void *z, const void *Ua, const void *Ue, const void
                        const float *cg, float *a, float *e, float *w, float *g, int B, int T,
                        int H, hipStream_t stream) {
     if (T == 0) return hipSuccess;
+    GateLds lay{};
+    const float *outs[4] = {a, e, w, g};
+    int off = 0;
+    for (int n = 0; n < 4; ++n) {
+        lay.u_off[n] = lay.c_off[n] = 0;
+        if (!outs[n]) continue;
+        lay.u_off[n] = off;
+        off += D * (gate_rank(n) + kPad) * 2;
+        lay.c_off[n] = off;
+        off += D * 4;
+    }
+    lay.bytes = off;
+    if (off == 0) return hipSuccess;
+    auto kern = lowrank_gates_kernel<D>;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, off);
+    if (err != hipSuccess) return err;
+    // Enough workgroups along the tokens to fill the machine, each walking several token
+    // blocks so that loading the head's rows into LDS is amortised.
     const int nblk = (T + 15) / 16;
-    // Enough wavefronts along the tokens to fill the machine about four times over, each
-    // walking at least a few token blocks with its up-projection rows resident.
-    const int tiles = H * (D / 16) * B;
-    int groups = (4 * 256 * 4 + tiles * 4 - 1) / (tiles * 4);
-    groups = max(1, min(groups, (nblk + 3) / 4));
-    hipLaunchKernelGGL((lowrank_gates_kernel<D>), dim3(H * (D / 16), B, groups), dim3(256), 0,
-                       stream, static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ua),
+    int groups = (2 * 256 + H * B - 1) / (H * B);
+    groups = max(1, min(groups, (nblk + 15) / 16));
+    hipLaunchKernelGGL(kern, dim3(H, B, groups), dim3(256), off, stream,
+                       static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ua),
                        static_cast<const bf16_t *>(Ue), static_cast<const bf16_t *>(Uw),
-                       static_cast<const bf16_t *>(Ug), ca, ce, cw, cg, a, e, w, g, T, H,
-                       groups * 4);
+                       static_cast<const bf16_t *>(Ug), ca, ce, cw, cg, a, e, w, g, T, H, lay);
     return hipGetLastError();
 }
 

@@ -20,6 +20,14 @@ hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, co
                                 const float *r, int B, int T, int H, int d, int chunk, bool bf16,
                                 void *workspace, hipStream_t stream);
 
+// Phase P with the decay a and the query gate g formed in the kernel from the low-rank gate
+// projection (z [B, T, 512], U_a [H, d, 64], U_g [H, d, 128] bf16; c_a, c_g [H, d] fp32),
+// bf16 q and k only.
+hipError_t launch_chunk_prepare_lowrank(const void *q, const void *k, const void *z,
+                                        const void *Ua, const void *Ug, const float *ca,
+                                        const float *cg, const float *r, int B, int T, int H,
+                                        int d, int chunk, void *workspace, hipStream_t stream);
+
 // Phase S: sequential chunk scan (solve, readout, state carry) from the workspace. A
 // non-null og applies the output-gate epilogue o <- o * og.
 hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,

@@ -255,6 +255,33 @@ muir_status_t muir_lowrank_gates(
     float *a, float *e, float *w, float *g, int B, int T, int H, int d, muir_stream_t stream);
 
 /*
+ * The chunk forward with its gates made from the fused low-rank gate projection inside the
+ * call (the pages' rank-512 projection; see muir_lowrank_gates for the definition). The
+ * decay a and the query gate g are formed inside the parallel phase's kernel, from z rows
+ * shared by every head, so their fp32 rows are never read from memory; the erase and write
+ * gates e, w are formed by the gate kernel into the workspace and read by the scan.
+ * The result is muir_chunk_fwd's on the gates muir_lowrank_gates makes from the same z, U
+ * and c (bit for bit).
+ *
+ *   q, k, v  as for muir_chunk_fwd, bf16 only (MUIR_ERR_UNSUPPORTED otherwise)
+ *   z, U*, c*  as for muir_lowrank_gates (all four gates' up-projections and offsets)
+ *   r, s0, o, s_out, sizes: as for muir_chunk_fwd
+ *   workspace / workspace_bytes: at least muir_chunk_fwd_lowrank_workspace_size(...) bytes
+ *            (the chunk forward's workspace, then room for e and w)
+ *
+ * Errors as for muir_chunk_fwd and muir_lowrank_gates.
+ */
+size_t muir_chunk_fwd_lowrank_workspace_size(int B, int T, int H, int dk, int dv, int chunk);
+
+muir_status_t muir_chunk_fwd_lowrank(
+    const void *q, const void *k, const void *v, const void *z,
+    const void *Ua, const void *Ue, const void *Uw, const void *Ug,
+    const float *ca, const float *ce, const float *cw, const float *cg, const float *r,
+    const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
  * One recurrent step per (batch, head), updating the state in place (decode).
  * Constant-memory inference against the fixed state (Muir abstract, "Full text";
  * openai-hub page, opening section: the history lives in a fixed 2-D state, so

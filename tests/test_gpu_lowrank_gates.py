@@ -105,3 +105,49 @@ def test_forward_driven_by_lowrank_gates(device, d, chunk):
     eo, es = o_err(to_numpy(o), o_ref), s_err(to_numpy(s), s_ref)
     print(f"low-rank forward d={d} C={chunk}: o={eo.max():.3e} state={es.max():.3e}", flush=True)
     assert max(eo.max(), es.max()) <= 2e-2
+
+
+def lowrank_fwd(inp, lr, device, chunk):
+    t = to_device(inp, device, "bf16")
+    z = torch.from_numpy(lr["z"]).to(device=device, dtype=torch.bfloat16)
+    U, c = dev_weights(lr, device)
+    o, s = muir.chunk_fwd_lowrank(t["q"], t["k"], t["v"], z, U, c, t["r"], chunk=chunk)
+    torch.cuda.synchronize()
+    return to_numpy(o), to_numpy(s)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("T", [15, 300])
+def test_fused_lowrank_forward_parity(device, d, chunk, T):
+    """Gates made inside the call: against the fp64 recurrence on the oracle's gates."""
+    B, H = 2, 2
+    inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv="bf16", seed=700 + T)
+    lr = workloads.lowrank_gate_inputs(0, B=B, T=T, H=H, d=d, seed=700 + T)
+    ref = ref_gates(lr)
+    full = dict(inp)
+    for k in "aewg":
+        full[k] = ref[k]
+    o_ref, s_ref = oracle.recurrent(*[full[n] for n in NAMES])
+    o, s = lowrank_fwd(inp, lr, device, chunk)
+    eo, es = o_err(o, o_ref), s_err(s, s_ref)
+    print(f"fused low-rank T={T} d={d} C={chunk}: o={eo.max():.3e} state={es.max():.3e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert max(eo.max(), es.max()) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg,chunk", [(2, 128), (3, 256)])
+def test_fused_equals_gate_kernel_then_forward(device, cfg, chunk):
+    """At the 1.34B-class and long-context shapes: the fused call is bit for bit the gate
+    kernel's four gates fed to the plain forward (same products, same order)."""
+    inp = workloads.chunk_inputs(cfg)
+    lr = workloads.lowrank_gate_inputs(cfg)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    o1, s1 = lowrank_fwd(inp, lr, device, chunk)
+    gates = gpu_gates(lr, H, d, device)
+    t = to_device(inp, device, "bf16")
+    for k in "aewg":
+        t[k] = torch.from_numpy(gates[k]).to(device)
+    o2, s2 = muir.chunk_fwd(*[t[n] for n in NAMES], chunk=chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, to_numpy(o2)) and np.array_equal(s1, to_numpy(s2))
