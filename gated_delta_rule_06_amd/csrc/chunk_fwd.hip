@@ -30,8 +30,8 @@
 //    further (pivots every 8, 4, 2, 1 tokens), each level one masked MFMA tile, so the
 //    Gram work is all on the matrix cores. chunk_prepare_bf16_kernel streams the chunk
 //    once for bf16 operands; chunk_prepare_kernel serves fp32 operands.
-//  * chunk_scan_kernel, one workgroup per (batch x head, 16 value columns), sequential
-//    over chunks (value columns are exactly independent). Its chain wavefront carries
+//  * chunk_scan_kernel, one workgroup per (batch x head, 16 or 8 value columns),
+//    sequential over chunks (value columns are exactly independent). Its chain wavefront carries
 //    the serial path: for leaf L (16 tokens) it subtracts E_L * (M_{L,<L} U_{<L}) from
 //    the leaf's right-hand side on MFMA -- the off-diagonal products of the block-Neumann
 //    recursion, grouped by the leaf they update -- then solves the 16x16 unit
@@ -345,26 +345,41 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 // Phase S: sequential chunk scan.
 // ---------------------------------------------------------------------------------
 
-// One step of the leaf's forward substitution for the four value columns a lane holds:
-// x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
-// broadcast inside the FMA. Within a step the four columns use different registers, so
-// each register is read by DPP at least three instructions after it was written; the
-// first step waits the two states a DPP read needs after a VALU write.
-template <int S>
+// One step of the leaf's forward substitution for the VC value columns a lane holds (4, 2
+// or 1): x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
+// broadcast inside the FMA. A DPP read needs two wait states after a VALU write of its
+// register. With four columns the other columns' instructions provide them (every
+// register is read three instructions after it was written) and only the first step
+// waits; with two columns one more state is waited each step, with one column two.
+template <int S, int VC>
 __device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, float &x3, float n0,
                                            float n1, float n2, float n3) {
 #define MUIR_BCAST_FMA(R, N) \
     "v_fmac_f32_dpp " R ", " R ", " N " row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
-    if constexpr (S == 0) {
-        asm("s_nop 1\n\t" MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5")
-                MUIR_BCAST_FMA("%2", "%6") MUIR_BCAST_FMA("%3", "%7")
-            : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
-            : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+    if constexpr (VC == 4) {
+        if constexpr (S == 0) {
+            asm("s_nop 1\n\t" MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5")
+                    MUIR_BCAST_FMA("%2", "%6") MUIR_BCAST_FMA("%3", "%7")
+                : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+                : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+        } else {
+            asm(MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5") MUIR_BCAST_FMA("%2", "%6")
+                    MUIR_BCAST_FMA("%3", "%7")
+                : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+                : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+        }
+    } else if constexpr (VC == 2) {
+        asm("s_nop %5\n\t"
+            "v_fmac_f32_dpp %0, %0, %2 row_newbcast:%4 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, %1, %3 row_newbcast:%4 row_mask:0xf bank_mask:0xf"
+            : "+v"(x0), "+v"(x1)
+            : "v"(n0), "v"(n1), "i"(S), "i"(S == 0 ? 1 : 0));
     } else {
-        asm(MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5") MUIR_BCAST_FMA("%2", "%6")
-                MUIR_BCAST_FMA("%3", "%7")
-            : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
-            : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
+        static_assert(VC == 1, "VC is 4, 2 or 1");
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+            : "+v"(x0)
+            : "v"(n0), "i"(S));
     }
 #undef MUIR_BCAST_FMA
 }
@@ -860,13 +875,13 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 }
 
 // Per-leaf inputs of the serial chain, row layout: lane (t, g) holds token t of the
-// leaf and value columns 4g..4g+3 of the tile.
-template <typename QT> struct LeafIn {
+// leaf and the tile's value columns of lane group g (the first VC values).
+template <typename QT, int VC> struct LeafIn {
     f32x4_t ev, wv;
-    typename Row4<QT>::raw vv;
+    typename RowV<QT, VC>::raw vv;
 };
 
-// The scan: one workgroup of two wavefronts per (batch, head, 16 value columns),
+// The scan: one workgroup of two wavefronts per (batch, head, 4 VC value columns),
 // sequential over chunks and over the 16-token leaves inside each chunk. Value columns
 // are exactly independent, so nothing is shared between workgroups. For leaf L of a
 // chunk with start state S0:
@@ -882,15 +897,21 @@ template <typename QT> struct LeafIn {
 // doubles the loads each chain keeps in flight (vector-memory loads return in order, so
 // one wavefront's prefetch depth is bounded by what it can hold).
 //
-// Layouts: "row layout" (lane (t, g): token t, columns 4g..4g+3) is what the
+// Layouts: "row layout" (lane (t, g): token t, tile rows 4g..4g+3) is what the
 // substitution works in, and is the accumulator layout of products whose B operand rows
-// are tokens. U is kept as an operand with rows = value columns and values = tokens
-// 4g..4g+3 of the leaf; an mma4 against the identity turns a row-layout u into it. The
-// state is kept as accumulators with rows = channels, columns = value columns.
+// are tokens. U is kept as an operand with rows = tile rows and values = tokens 4g..4g+3
+// of the leaf; an mma4 against the identity turns a row-layout u into it. The state is
+// kept as accumulators with rows = channels, columns = tile rows.
+//
+// Value columns per workgroup: the matrix-core tiles are 16 rows wide, and tile row
+// 4G + i holds value column j0 + VC G + i for i < VC (VC = 4, 2 or 1). The other tile rows
+// stay exactly zero (zero initial state, zero solution), so each lane's substitution
+// handles only VC columns. Narrower tiles give more workgroups with shorter serial chains
+// for the same products; they pay off when 16-column tiles leave compute units idle.
 //
 // GATED: the output-gate epilogue, o <- o * og elementwise with og [B, T, H, dv] fp32 (the
 // output gate of the pages' gate table, applied as the readout is stored).
-template <typename QT, typename OpT, int D, int C, bool GATED>
+template <typename QT, typename OpT, int D, int C, bool GATED, int VC>
 __global__ __launch_bounds__(128) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ og, const float *__restrict__ s0, QT *__restrict__ o,
@@ -921,16 +942,19 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
+    constexpr int NVT = D / (4 * VC);  // value tiles per head
     const int id = blockIdx.x;
-    const int bh = (id >> 3) / NCT * 8 + (id & 7);
-    const int ct = (id >> 3) % NCT;
+    const int bh = (id >> 3) / NVT * 8 + (id & 7);
+    const int ct = (id >> 3) % NVT;
     if (bh >= BH) return;
     const int b = bh / H, h = bh % H;
-    const int j0 = 16 * ct;
+    const int j0 = 4 * VC * ct;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
     const size_t HD = size_t(H) * D;
-    const unsigned lo_st = unsigned(4 * g * D + x);  // state [channel 4g][column x]
+    // Tile row x of the state holds value column j0 + VC (x / 4) + x % 4, if x % 4 < VC.
+    const bool col_ok = (x & 3) < VC;
+    const unsigned lo_st = unsigned(4 * g * D + VC * (x >> 2) + (x & 3));  // state [4g][column]
     auto u_put = [&](int buf, int L, f4 u) {
         reinterpret_cast<f4 *>(&sh_U[buf][L >> 1][lane])[L & 1] = u;
     };
@@ -939,7 +963,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
 
     if (nchunks == 0) {
-        if (wave == 0 && south) {
+        if (wave == 0 && south && col_ok) {
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
 #pragma unroll
@@ -953,8 +977,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     constexpr unsigned OB = sizeof(OpT);
     const unsigned lo_pair = unsigned((4 * x + g) * 8) * OB;  // block pair: row x, cols 4g..
     const unsigned lo_frag = unsigned(lane * 8) * OB;        // lane's share of an operand fragment
-    const unsigned lo_f = unsigned(x * HD + 4 * g) * 4u;            // e, w: token x, cols 4g..
-    const unsigned lo_q = unsigned(x * HD + 4 * g) * unsigned(sizeof(QT));  // v, o
+    const unsigned lo_f = unsigned(x * HD + VC * g) * 4u;            // e, w: token x, group g
+    const unsigned lo_q = unsigned(x * HD + VC * g) * unsigned(sizeof(QT));  // v, o
 
     // Descriptors (loop-invariant). The workspace one covers this head's chunk slots;
     // a chunk index past the end is clamped to the last chunk (prefetches read valid,
@@ -993,7 +1017,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
             load_kg(ci, L, SL::QG_OFF, wn.qg);
 #pragma unroll
             for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
-            if constexpr (GATED) wn.og = buf_load_f4(rog, lo_f, trow(ci * C + 16 * L, 4u));
+            if constexpr (GATED) wn.og = buf_load_fn<VC>(rog, lo_f, trow(ci * C + 16 * L, 4u));
         };
         RWin rw[2];
         load_rwin(0, 0, rw[0]);
@@ -1056,7 +1080,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                         ro = F::mma8(u_pair(buf, l / 2), cw.pq[l / 2], ro);
                     }
                     if constexpr (GATED) ro *= cw.og;
-                    Row4<QT>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
+                    RowV<QT, VC>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
             }
             if (p + 1 < nchunks) {
@@ -1075,18 +1099,18 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            S[c][i] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+            S[c][i] = s0h && col_ok ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
 
     const f4 unit = F::unit(x, g);
     const rsrc_t re = make_rsrc(e + tok0, tok_elems * 4u);
     const rsrc_t rwt = make_rsrc(w + tok0, tok_elems * 4u);
     const rsrc_t rv = make_rsrc(v + tok0, tok_elems * unsigned(sizeof(QT)));
 
-    auto load_leaf = [&](int ci, int L, LeafIn<QT> &in) {
+    auto load_leaf = [&](int ci, int L, LeafIn<QT, VC> &in) {
         const unsigned so = trow(ci * C + 16 * L, 4u);
-        in.ev = buf_load_f4(re, lo_f, so);
-        in.wv = buf_load_f4(rwt, lo_f, so);
-        in.vv = Row4<QT>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
+        in.ev = buf_load_fn<VC>(re, lo_f, so);
+        in.wv = buf_load_fn<VC>(rwt, lo_f, so);
+        in.vv = RowV<QT, VC>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
     };
     auto load_kbt = [&](int ci, int pair, int c) {
         return F::bload8(rws, lo_frag, wsoff(ci, SL::KBT_OFF + frag_idx(16 * c, 32 * pair, C) * OB));
@@ -1120,7 +1144,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
     // Leaf inputs: in[L & 1] holds leaf L and is refilled with leaf L + 2 once leaf L is
     // solved. Window operands: win[L & 1] (see Win).
-    LeafIn<QT> in[2];
+    LeafIn<QT, VC> in[2];
     load_leaf(0, 0, in[0]);
     load_leaf(0, 1, in[1]);
     Win win[2];
@@ -1156,7 +1180,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 constexpr bool more = L + 1 < NB;
                 Win &cw = win[L & 1];
                 Win &nw = win[(L + 1) & 1];
-                LeafIn<QT> &cin = in[L & 1];
+                LeafIn<QT, VC> &cin = in[L & 1];
                 // Row t of the leaf's diagonal M block, from LDS (staged a chunk ahead).
                 f32x4_t md[4];
 #pragma unroll
@@ -1175,15 +1199,16 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     else acc = F::mma8(F::cat(Ulast, Ulast), mpair, acc);
                 }
                 load_win(ciN, LN, nw);
-                // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0.
-                float ne[4];
+                // Tokens past T read e = w = v = 0 (outside the resource): r = 0, u = 0. Tile
+                // rows past VC in each group hold no column: their u is zero.
+                float ne[4] = {0.f, 0.f, 0.f, 0.f};
                 float x0, x1, x2, x3;
                 {
-                    float r[4];
+                    float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < VC; ++i) {
                         ne[i] = -cin.ev[i];
-                        r[i] = fmaf(ne[i], acc[i], cin.wv[i] * Row4<QT>::get(cin.vv, i));
+                        r[i] = fmaf(ne[i], acc[i], cin.wv[i] * RowV<QT, VC>::get(cin.vv, i));
                     }
                     x0 = r[0]; x1 = r[1]; x2 = r[2]; x3 = r[3];
                 }
@@ -1191,7 +1216,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 auto step = [&](auto Sc) {
                     constexpr int St = decltype(Sc)::value;
                     const float m = md[St / 4][St % 4];
-                    subst_step<St>(x0, x1, x2, x3, ne[0] * m, ne[1] * m, ne[2] * m, ne[3] * m);
+                    float n[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < VC; ++i) n[i] = ne[i] * m;
+                    subst_step<St, VC>(x0, x1, x2, x3, n[0], n[1], n[2], n[3]);
                 };
 
                 static_for<4>([&](auto Sc) { step(std::integral_constant<int, decltype(Sc)::value>{}); });
@@ -1250,7 +1278,7 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
         lds_barrier();
     }
 
-    if (south) {
+    if (south && col_ok) {
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
 #pragma unroll
@@ -1301,23 +1329,38 @@ hipError_t prepare_typed(const void *q, const void *k, const float *a, const flo
     }
 }
 
+template <typename QT, typename OpT, int D, int C, int VC>
+hipError_t scan_vc(const void *v, const float *e, const float *w, const float *og,
+                   const float *s0, void *o, float *s_out, int B, int T, int H,
+                   const void *workspace, hipStream_t stream) {
+    const int nchunks = (T + C - 1) / C;
+    const int BH = B * H;
+    const int groups = (BH + 7) / 8;
+    const dim3 grid(groups * 8 * (D / (4 * VC)));
+    if (og)
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true, VC>), grid, dim3(128), 0, stream,
+                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
+                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false, VC>), grid, dim3(128), 0, stream,
+                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
+                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+    return hipGetLastError();
+}
+
+// Value columns per scan workgroup (4 VC): sixteen when that gives every compute unit a
+// workgroup, else eight (bf16 operands; the fp32 path always takes sixteen). Both give
+// the same results bit for bit: every value column goes through the same operations.
+constexpr int kScanCUs = 256;
 template <typename QT, typename OpT, int D, int C>
 hipError_t scan_typed(const void *v, const float *e, const float *w, const float *og,
                       const float *s0, void *o, float *s_out, int B, int T, int H,
                       const void *workspace, hipStream_t stream) {
-    const int nchunks = (T + C - 1) / C;
-    const int BH = B * H;
-    const int groups = (BH + 7) / 8;
-    const dim3 grid(groups * 8 * (D / 16));
-    if (og)
-        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true>), grid, dim3(128), 0, stream,
-                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
-                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
-    else
-        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false>), grid, dim3(128), 0, stream,
-                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
-                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
-    return hipGetLastError();
+    if constexpr (std::is_same_v<QT, bf16_t>) {
+        if (size_t(B) * H * (D / 16) < size_t(kScanCUs))
+            return scan_vc<QT, OpT, D, C, 2>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
+    }
+    return scan_vc<QT, OpT, D, C, 4>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
 }
 
 }  // namespace

@@ -79,6 +79,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 }
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, unsigned voff, unsigned soff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), 0);
 }
@@ -188,30 +189,72 @@ template <int N, typename Fn> __device__ __forceinline__ void static_for(Fn &&fn
     static_for_impl(fn, std::make_integer_sequence<int, N>{});
 }
 
-// Four consecutive q/k/v-typed elements through a buffer resource.
-template <typename QT> struct Row4;
-template <> struct Row4<bf16_t> {
+// VC (4, 2 or 1) consecutive q/k/v-typed elements through a buffer resource, held as the
+// first VC values of a four-vector; the other values are zero.
+template <int VC> __device__ __forceinline__ f32x4_t buf_load_fn(rsrc_t r, unsigned voff, unsigned soff) {
+    static_assert(VC == 4 || VC == 2 || VC == 1, "VC is 4, 2 or 1");
+    if constexpr (VC == 4) {
+        return buf_load_f4(r, voff, soff);
+    } else if constexpr (VC == 2) {
+        // Whole-vector casts only: this compiler lowers __builtin_bit_cast of a subscripted
+        // vector element as a read of element 0.
+        const f32x2_t f = __builtin_bit_cast(f32x2_t, buf_load8(r, voff, soff));
+        return f32x4_t{f[0], f[1], 0.f, 0.f};
+    } else {
+        const unsigned u = __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), 0);
+        return f32x4_t{__builtin_bit_cast(float, u), 0.f, 0.f, 0.f};
+    }
+}
+template <typename QT, int VC> struct RowV;
+template <int VC> struct RowV<bf16_t, VC> {
+    static_assert(VC == 4 || VC == 2 || VC == 1, "VC is 4, 2 or 1");
     using raw = u16x4_t;
     static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
+        if constexpr (VC == 4) {
+            return __builtin_bit_cast(u16x4_t, buf_load8(r, voff, soff));
+        } else if constexpr (VC == 2) {
+            const unsigned u = __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), 0);
+            return u16x4_t{uint16_t(u & 0xffffu), uint16_t(u >> 16), 0, 0};
+        } else {
+            const uint16_t u = __builtin_amdgcn_raw_buffer_load_b16(r, int(voff), int(soff), 0);
+            return u16x4_t{u, 0, 0, 0};
+        }
     }
     static __device__ __forceinline__ float get(raw v, int i) { return bf16_to_f32(v[i]); }
     static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
-        u16x4_t u;
+        if constexpr (VC == 4) {
+            u16x4_t u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, int(voff), int(soff), 0);
+            for (int i = 0; i < 4; ++i) u[i] = f32_to_bf16(v[i]);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, int(voff), int(soff), 0);
+        } else if constexpr (VC == 2) {
+            const unsigned u = unsigned(f32_to_bf16(v[0])) | (unsigned(f32_to_bf16(v[1])) << 16);
+            __builtin_amdgcn_raw_buffer_store_b32(u, r, int(voff), int(soff), 0);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v[0]), r, int(voff), int(soff), 0);
+        }
     }
 };
-template <> struct Row4<float> {
+template <int VC> struct RowV<float, VC> {
+    static_assert(VC == 4 || VC == 2 || VC == 1, "VC is 4, 2 or 1");
     using raw = f32x4_t;
     static __device__ __forceinline__ raw load(rsrc_t r, unsigned voff, unsigned soff) {
-        return buf_load_f4(r, voff, soff);
+        return buf_load_fn<VC>(r, voff, soff);
     }
     static __device__ __forceinline__ float get(raw v, int i) { return v[i]; }
     static __device__ __forceinline__ void store(rsrc_t r, unsigned voff, unsigned soff, f32x4_t v) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(voff), int(soff), 0);
+        if constexpr (VC == 4) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(voff), int(soff), 0);
+        } else if constexpr (VC == 2) {
+            const f32x2_t f = {v[0], v[1]};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, f), r, int(voff), int(soff), 0);
+        } else {
+            const float f = v[0];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, int(voff), int(soff), 0);
+        }
     }
 };
+// Four consecutive elements.
+template <typename QT> using Row4 = RowV<QT, 4>;
 
 }  // namespace muir

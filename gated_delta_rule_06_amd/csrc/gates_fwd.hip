@@ -24,10 +24,9 @@ namespace muir {
 
 namespace {
 
-// Rank offsets of the four gates' slices of z, and their ranks.
+// Rank offsets of the four gates' slices of z (their ranks: gate_rank below).
 constexpr int kZRank = 512;
 constexpr int kOffDecay = 0, kOffErase = 64, kOffWrite = 256, kOffRead = 384;
-constexpr int kRankDecay = 64, kRankErase = 64, kRankWrite = 128, kRankRead = 128;
 
 // LDS of the gate kernel: the head's up-projection rows of the requested gates (row pitch
 // padded by 8 elements against bank conflicts) and their offsets; gate n's region starts at

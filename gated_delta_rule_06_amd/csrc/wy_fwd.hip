@@ -259,7 +259,6 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
     using f8 = F::f8;
     constexpr int NW = 8, NB = C / 16, NP = NB / 2, NCT = D / 16, NKD = D / 32;
     using BD = BlockDeal<NB, NW>;
-    constexpr unsigned OB = 2;
 
     extern __shared__ __align__(16) unsigned char smem[];
     f8 *sh_b1 = reinterpret_cast<f8 *>(smem + LY::B1_OFF);  // [NP][NCT][64]: e*Kg, then W
