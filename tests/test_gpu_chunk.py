@@ -176,3 +176,23 @@ def test_full_erase_and_no_decay_special_cases(device):
     inp["e"][:, :, 2] = 0.0
     o, s = gpu_fwd(inp, device, 128)
     assert_parity(o, s, *ref_fwd(inp), 1e-4, "special gates fp32")
+
+
+def test_value_tile_widths_agree_bit_for_bit(device):
+    """B*H*d/16 >= 256 runs the scan on 16-column value tiles, fewer heads on 8-column ones.
+    Every value column goes through the same operations either way, so the heads of one
+    call, rerun as two calls of half the heads, give the same bits. The wide call (ragged
+    tail, non-zero initial state) is also checked against the oracle."""
+    B, T, H, d, C = 2, 300, 16, 128, 128
+    inp = workloads.chunk_inputs(2, B=B, T=T, H=H, seed=21)
+    s0 = state_like(np.random.default_rng(21), B, H, d)
+    o, s = gpu_fwd(inp, device, C, s0)
+    assert_parity(o, s, *ref_fwd(inp, s0), TOL["bf16"], "16-column tiles, ragged tail")
+    for h0 in (0, H // 2):
+        part = dict(inp)
+        for n in NAMES:
+            part[n] = np.ascontiguousarray(inp[n][h0:h0 + H // 2] if n == "r"
+                                           else inp[n][:, :, h0:h0 + H // 2])
+        o_h, s_h = gpu_fwd(part, device, C, np.ascontiguousarray(s0[:, h0:h0 + H // 2]))
+        assert np.array_equal(o_h, o[:, :, h0:h0 + H // 2]), f"heads {h0}..: o differs"
+        assert np.array_equal(s_h, s[:, h0:h0 + H // 2]), f"heads {h0}..: state differs"
