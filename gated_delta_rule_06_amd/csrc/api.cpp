@@ -417,16 +417,25 @@ muir_status_t muir_chunk_fwd_lowrank(const void *q, const void *k, const void *v
                          fn);
     }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // e and w: made inside the scan where its LDS allows, else by the gate kernel into the
+    // workspace's tail first.
+    const bool in_scan = muir::scan_gates_in_kernel(B, H, dv, chunk);
     float *e = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ebase);
     float *w = e + n_tok;
-    st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, nullptr, ce, cw, nullptr,
-                                              nullptr, e, w, nullptr, B, T, H, dv, hs),
-                   "chunk_fwd_lowrank gates");
-    if (st != MUIR_OK) return st;
+    if (!in_scan) {
+        st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, nullptr, ce, cw,
+                                                  nullptr, nullptr, e, w, nullptr, B, T, H, dv, hs),
+                       "chunk_fwd_lowrank gates");
+        if (st != MUIR_OK) return st;
+    }
     st = check_hip(muir::launch_chunk_prepare_lowrank(q, k, z, Ua, Ug, ca, cg, r, B, T, H, dk, chunk,
                                                       workspace, hs),
                    "chunk_fwd_lowrank prepare");
     if (st != MUIR_OK) return st;
+    if (in_scan)
+        return check_hip(muir::launch_chunk_scan_lowrank(v, z, Ue, Uw, ce, cw, s0, o, s_out, B, T, H,
+                                                         dk, chunk, workspace, hs),
+                         "chunk_fwd_lowrank scan");
     return check_hip(muir::launch_chunk_scan(v, e, w, nullptr, s0, o, s_out, B, T, H, dk, chunk, true,
                                              workspace, hs),
                      "chunk_fwd_lowrank scan");

@@ -345,12 +345,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 // Phase S: sequential chunk scan.
 // ---------------------------------------------------------------------------------
 
-// One step of the leaf's forward substitution for the VC value columns a lane holds (4, 2
-// or 1): x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
+// One step of the leaf's forward substitution for the VC value columns a lane holds (4 or
+// 2): x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
 // broadcast inside the FMA. A DPP read needs two wait states after a VALU write of its
 // register. With four columns the other columns' instructions provide them (every
 // register is read three instructions after it was written) and only the first step
-// waits; with two columns one more state is waited each step, with one column two.
+// waits; with two columns one more state is waited each step.
 template <int S, int VC>
 __device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, float &x3, float n0,
                                            float n1, float n2, float n3) {
@@ -368,18 +368,13 @@ __device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, floa
                 : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
                 : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
         }
-    } else if constexpr (VC == 2) {
+    } else {
+        static_assert(VC == 2, "VC is 4 or 2");
         asm("s_nop %5\n\t"
             "v_fmac_f32_dpp %0, %0, %2 row_newbcast:%4 row_mask:0xf bank_mask:0xf\n\t"
             "v_fmac_f32_dpp %1, %1, %3 row_newbcast:%4 row_mask:0xf bank_mask:0xf"
             : "+v"(x0), "+v"(x1)
             : "v"(n0), "v"(n1), "i"(S), "i"(S == 0 ? 1 : 0));
-    } else {
-        static_assert(VC == 1, "VC is 4, 2 or 1");
-        asm("s_nop 1\n\t"
-            "v_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
-            : "+v"(x0)
-            : "v"(n0), "i"(S));
     }
 #undef MUIR_BCAST_FMA
 }
@@ -904,19 +899,34 @@ template <typename QT, int VC> struct LeafIn {
 // kept as accumulators with rows = channels, columns = tile rows.
 //
 // Value columns per workgroup: the matrix-core tiles are 16 rows wide, and tile row
-// 4G + i holds value column j0 + VC G + i for i < VC (VC = 4, 2 or 1). The other tile rows
+// 4G + i holds value column j0 + VC G + i for i < VC (VC = 4 or 2). The other tile rows
 // stay exactly zero (zero initial state, zero solution), so each lane's substitution
 // handles only VC columns. Narrower tiles give more workgroups with shorter serial chains
 // for the same products; they pay off when 16-column tiles leave compute units idle.
 //
 // GATED: the output-gate epilogue, o <- o * og elementwise with og [B, T, H, dv] fp32 (the
 // output gate of the pages' gate table, applied as the readout is stored).
-template <typename QT, typename OpT, int D, int C, bool GATED, int VC>
-__global__ __launch_bounds__(128) void chunk_scan_kernel(
+//
+// LRS: e and w are not read but formed inside the kernel from the low-rank gate projection
+// (the pages' fused rank-512 gate projection: openai-hub page, section on
+// sensitivity-allocated gating, gate table): e = sigmoid(z_erase . U_e + c_e) and
+// w = sigmoid(z_write . U_w + c_w). A third wavefront makes them one chunk ahead of the
+// chain into LDS, one matrix-core tile per 16-token leaf and rank step (rows = the tile's
+// value columns, columns = tokens, so its accumulator is the chain's row layout), in the
+// same order of operations as the standalone gate kernel, so the values are the same bits.
+// Built for 16-column tiles only.
+struct ScanGates {
+    const bf16_t *z;          // [B, T, 512]
+    const bf16_t *Ue, *Uw;    // [H, D, 64], [H, D, 128]
+    const float *ce, *cw;     // [H, D]
+};
+constexpr int kZOffErase = 64, kZOffWrite = 256;
+template <typename QT, typename OpT, int D, int C, bool GATED, int VC, bool LRS>
+__global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ og, const float *__restrict__ s0, QT *__restrict__ o,
-    float *__restrict__ s_out, const unsigned char *__restrict__ ws, int T, int H, int BH,
-    int nchunks) {
+    float *__restrict__ s_out, const unsigned char *__restrict__ ws, ScanGates sg, int T, int H,
+    int BH, int nchunks) {
     using SL = Slot<OpT, D, C>;
     using F = Frag<OpT>;
     using f4 = typename F::f4;
@@ -939,6 +949,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     // The chunk's fp32 diagonal blocks of M (row-major [t][s] per leaf), staged the same
     // way: whole 16-byte pieces, so each load of the stager uses full cache lines.
     __shared__ __align__(16) f32x4_t sh_md[2][NB][64];
+    // LRS: e and w of every leaf of a chunk in the chain's row layout, double-buffered by
+    // chunk parity.
+    static_assert(!LRS || VC == 4, "the in-kernel gates run with 16-column tiles");
+    __shared__ __align__(16) f32x4_t sh_ew[LRS ? 2 : 1][LRS ? NB : 1][2][64];
 
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
@@ -1001,6 +1015,81 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
     auto load_pair = [&](int ci, size_t OFF, int bt, int j) {
         return F::bload8(rws, lo_pair, wsoff(ci, OFF + size_t(SL::prow(bt) + j) * 512 * OB));
     };
+
+    if constexpr (LRS) {
+        if (wave == 2) {
+            // ---------------- gate wavefront: e, w of chunk p + 1 in phase p ----------------
+            using F8 = Frag<bf16_t>;
+            using g8 = typename F8::f8;
+            const rsrc_t rz = make_rsrc(sg.z + size_t(b) * T * kZRankAll, unsigned(size_t(T) * kZRankAll * 2));
+            // Up-projection rows as A operands (lane (x, g): column j0 + x, ranks 32s + 8g ..
+            // + 7), and the offsets as the accumulators' start (lane (t, g): columns
+            // j0 + 4g .. + 3).
+            g8 ue[2], uw[4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ue[s] = F8::load8(sg.Ue + (size_t(h) * D + j0 + x) * 64 + 32 * s + 8 * g);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) uw[s] = F8::load8(sg.Uw + (size_t(h) * D + j0 + x) * 128 + 32 * s + 8 * g);
+            f32x4_t ce4, cw4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ce4[i] = sg.ce[size_t(h) * D + j0 + 4 * g + i];
+                cw4[i] = sg.cw[size_t(h) * D + j0 + 4 * g + i];
+            }
+            // z rows of four leaves: erase slice (2 rank steps) and write slice (4).
+            constexpr int NL = NB < 4 ? NB : 4;
+            struct ZGroup {
+                g8 ze[NL][2], zw[NL][4];
+            };
+            auto load_group = [&](int ci, int grp, ZGroup &zg) {
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    const int t = ci * C + 16 * (grp * NL + l) + x;
+                    const unsigned zoff = unsigned(min(t, T)) * (kZRankAll * 2u) + 16u * unsigned(g);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) zg.ze[l][s] = F8::bload8(rz, zoff + unsigned(kZOffErase + 32 * s) * 2u, 0u);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) zg.zw[l][s] = F8::bload8(rz, zoff + unsigned(kZOffWrite + 32 * s) * 2u, 0u);
+                }
+            };
+            auto make_group = [&](int ci, int grp, const ZGroup &zg) {
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    const int L = grp * NL + l;
+                    const bool real = ci * C + 16 * L + x < T;  // tokens past T: e = w = 0
+                    f32x4_t ye = ce4, yw = cw4;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) ye = F8::mma8(ue[s], zg.ze[l][s], ye);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) yw = F8::mma8(uw[s], zg.zw[l][s], yw);
+                    f32x4_t ev, wv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        ev[i] = real ? gate_sigmoid(ye[i]) : 0.f;
+                        wv[i] = real ? gate_sigmoid(yw[i]) : 0.f;
+                    }
+                    sh_ew[ci & 1][L][0][lane] = ev;
+                    sh_ew[ci & 1][L][1][lane] = wv;
+                }
+            };
+            auto make_chunk = [&](int ci) {
+                ZGroup zg[2];
+                load_group(ci, 0, zg[0]);
+                static_for<NB / NL>([&](auto Gc) {
+                    constexpr int grp = decltype(Gc)::value;
+                    if constexpr (grp + 1 < NB / NL) load_group(ci, grp + 1, zg[(grp + 1) & 1]);
+                    make_group(ci, grp, zg[grp & 1]);
+                });
+            };
+            make_chunk(0);
+            lds_barrier();
+            for (int p = 0; p <= nchunks; ++p) {
+                if (p + 1 < nchunks) make_chunk(p + 1);
+                lds_barrier();
+            }
+            return;
+        }
+    }
 
     if (wave == 1) {
         // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
@@ -1108,8 +1197,10 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
 
     auto load_leaf = [&](int ci, int L, LeafIn<QT, VC> &in) {
         const unsigned so = trow(ci * C + 16 * L, 4u);
-        in.ev = buf_load_fn<VC>(re, lo_f, so);
-        in.wv = buf_load_fn<VC>(rwt, lo_f, so);
+        if constexpr (!LRS) {
+            in.ev = buf_load_fn<VC>(re, lo_f, so);
+            in.wv = buf_load_fn<VC>(rwt, lo_f, so);
+        }
         in.vv = RowV<QT, VC>::load(rv, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))));
     };
     auto load_kbt = [&](int ci, int pair, int c) {
@@ -1185,6 +1276,12 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                 f32x4_t md[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) md[q4] = sh_md[buf][L][4 * x + q4];
+                // The leaf's erase and write gates (LRS: from the gate wavefront, in LDS).
+                f32x4_t evv = cin.ev, wvv = cin.wv;
+                if constexpr (LRS) {
+                    evv = sh_ew[buf][L][0][lane];
+                    wvv = sh_ew[buf][L][1][lane];
+                }
                 const int ciN = more ? ci : ci + 1;  // chunk of leaf L + 1
                 constexpr int LN = (L + 1) % NB;     // leaf L + 1 within it
 
@@ -1207,8 +1304,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(
                     float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < VC; ++i) {
-                        ne[i] = -cin.ev[i];
-                        r[i] = fmaf(ne[i], acc[i], cin.wv[i] * RowV<QT, VC>::get(cin.vv, i));
+                        ne[i] = -evv[i];
+                        r[i] = fmaf(ne[i], acc[i], wvv[i] * RowV<QT, VC>::get(cin.vv, i));
                     }
                     x0 = r[0]; x1 = r[1]; x2 = r[2]; x3 = r[3];
                 }
@@ -1329,22 +1426,27 @@ hipError_t prepare_typed(const void *q, const void *k, const float *a, const flo
     }
 }
 
-template <typename QT, typename OpT, int D, int C, int VC>
+template <typename QT, typename OpT, int D, int C, int VC, bool LRS = false>
 hipError_t scan_vc(const void *v, const float *e, const float *w, const float *og,
                    const float *s0, void *o, float *s_out, int B, int T, int H,
-                   const void *workspace, hipStream_t stream) {
+                   const void *workspace, hipStream_t stream, ScanGates sg = {}) {
     const int nchunks = (T + C - 1) / C;
     const int BH = B * H;
     const int groups = (BH + 7) / 8;
     const dim3 grid(groups * 8 * (D / (4 * VC)));
-    if (og)
-        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true, VC>), grid, dim3(128), 0, stream,
-                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
-                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
-    else
-        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false, VC>), grid, dim3(128), 0, stream,
-                           static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
-                           static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+    const dim3 block(LRS ? 192 : 128);
+    if constexpr (!LRS) {  // the in-kernel gates come without the output-gate epilogue
+        if (og) {
+            hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true, VC, false>), grid, block, 0,
+                               stream, static_cast<const QT *>(v), e, w, og, s0,
+                               static_cast<QT *>(o), s_out,
+                               static_cast<const unsigned char *>(workspace), sg, T, H, BH, nchunks);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false, VC, LRS>), grid, block, 0, stream,
+                       static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
+                       static_cast<const unsigned char *>(workspace), sg, T, H, BH, nchunks);
     return hipGetLastError();
 }
 
@@ -1352,12 +1454,14 @@ hipError_t scan_vc(const void *v, const float *e, const float *w, const float *o
 // workgroup, else eight (bf16 operands; the fp32 path always takes sixteen). Both give
 // the same results bit for bit: every value column goes through the same operations.
 constexpr int kScanCUs = 256;
+bool scan_narrow_tiles(int B, int H, int d) { return size_t(B) * H * (d / 16) < size_t(kScanCUs); }
+
 template <typename QT, typename OpT, int D, int C>
 hipError_t scan_typed(const void *v, const float *e, const float *w, const float *og,
                       const float *s0, void *o, float *s_out, int B, int T, int H,
                       const void *workspace, hipStream_t stream) {
     if constexpr (std::is_same_v<QT, bf16_t>) {
-        if (size_t(B) * H * (D / 16) < size_t(kScanCUs))
+        if (scan_narrow_tiles(B, H, D))
             return scan_vc<QT, OpT, D, C, 2>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
     }
     return scan_vc<QT, OpT, D, C, 4>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
@@ -1418,6 +1522,30 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
     MUIR_SCAN(64, 64) MUIR_SCAN(64, 128) MUIR_SCAN(64, 256)
     MUIR_SCAN(128, 64) MUIR_SCAN(128, 128) MUIR_SCAN(128, 256)
 #undef MUIR_SCAN
+    return hipErrorInvalidValue;
+}
+
+// With 16-column tiles and chunks of up to 128 tokens: there the gates' LDS (two chunks of
+// e and w) keeps two workgroups per compute unit, as many as the registers allow. Larger
+// chunks would halve that; with 8-column tiles (one workgroup per compute unit) the gate
+// wavefront's z loads slowed the chain by more than the separate gate pass costs.
+bool scan_gates_in_kernel(int B, int H, int d, int chunk) {
+    return !scan_narrow_tiles(B, H, d) && chunk <= 128;
+}
+
+hipError_t launch_chunk_scan_lowrank(const void *v, const void *z, const void *Ue, const void *Uw,
+                                     const float *ce, const float *cw, const float *s0, void *o,
+                                     float *s_out, int B, int T, int H, int d, int chunk,
+                                     const void *workspace, hipStream_t stream) {
+    if (!scan_gates_in_kernel(B, H, d, chunk)) return hipErrorNotSupported;
+    const ScanGates sg{static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ue),
+                       static_cast<const bf16_t *>(Uw), ce, cw};
+#define MUIR_SCAN_LR(D, C)                                                                        \
+    if (d == D && chunk == C)                                                                     \
+        return scan_vc<bf16_t, bf16_t, D, C, 4, true>(v, nullptr, nullptr, nullptr, s0, o, s_out, \
+                                                      B, T, H, workspace, stream, sg);
+    MUIR_SCAN_LR(64, 64) MUIR_SCAN_LR(64, 128) MUIR_SCAN_LR(128, 64) MUIR_SCAN_LR(128, 128)
+#undef MUIR_SCAN_LR
     return hipErrorInvalidValue;
 }
 

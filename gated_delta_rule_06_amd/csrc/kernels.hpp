@@ -34,6 +34,16 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                              int chunk, bool bf16, const void *workspace, hipStream_t stream);
 
+// Phase S with e and w formed inside the kernel from the low-rank gate projection (z,
+// U_e, U_w, c_e, c_w as for launch_lowrank_gates; bf16 operands), bit-identical to
+// launch_lowrank_gates followed by launch_chunk_scan. Only where scan_gates_in_kernel
+// holds; elsewhere it returns hipErrorNotSupported and the caller makes e and w first.
+bool scan_gates_in_kernel(int B, int H, int d, int chunk);
+hipError_t launch_chunk_scan_lowrank(const void *v, const void *z, const void *Ue, const void *Uw,
+                                     const float *ce, const float *cw, const float *s0, void *o,
+                                     float *s_out, int B, int T, int H, int d, int chunk,
+                                     const void *workspace, hipStream_t stream);
+
 // Shared-erase variant (one erase strength per token, e [B, T, H]); bf16 operands only. Its
 // workspace is the prepare kernel's slots followed by one region of per-chunk products per
 // slot.

@@ -258,16 +258,18 @@ muir_status_t muir_lowrank_gates(
  * The chunk forward with its gates made from the fused low-rank gate projection inside the
  * call (the pages' rank-512 projection; see muir_lowrank_gates for the definition). The
  * decay a and the query gate g are formed inside the parallel phase's kernel, from z rows
- * shared by every head, so their fp32 rows are never read from memory; the erase and write
- * gates e, w are formed by the gate kernel into the workspace and read by the scan.
- * The result is muir_chunk_fwd's on the gates muir_lowrank_gates makes from the same z, U
- * and c (bit for bit).
+ * shared by every head, so their fp32 rows are never read from memory. The erase and write
+ * gates e, w are formed inside the sequential phase's kernel when it runs 16-column value
+ * tiles (B*H*dv/16 >= 256) with chunk <= 128; otherwise the gate kernel writes them into
+ * the workspace and the scan reads them back. Either way the result is muir_chunk_fwd's on
+ * the gates muir_lowrank_gates makes from the same z, U and c (bit for bit).
  *
  *   q, k, v  as for muir_chunk_fwd, bf16 only (MUIR_ERR_UNSUPPORTED otherwise)
  *   z, U*, c*  as for muir_lowrank_gates (all four gates' up-projections and offsets)
  *   r, s0, o, s_out, sizes: as for muir_chunk_fwd
  *   workspace / workspace_bytes: at least muir_chunk_fwd_lowrank_workspace_size(...) bytes
- *            (the chunk forward's workspace, then room for e and w)
+ *            (the chunk forward's workspace, then room for e and w, used only when the
+ *            gate kernel makes them)
  *
  * Errors as for muir_chunk_fwd and muir_lowrank_gates.
  */

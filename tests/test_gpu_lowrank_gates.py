@@ -136,10 +136,31 @@ def test_fused_lowrank_forward_parity(device, d, chunk, T):
     assert max(eo.max(), es.max()) <= 2e-2
 
 
-@pytest.mark.parametrize("cfg,chunk", [(2, 128), (3, 256)])
+@pytest.mark.parametrize("d,B,chunk", [(128, 2, 128), (64, 4, 64)])
+def test_gates_made_inside_the_scan_parity(device, d, B, chunk):
+    """B*H*d/16 = 256 runs 16-column tiles, where e and w are made inside the scan (chunk <=
+    128): against the fp64 recurrence on the oracle's gates, with a ragged tail."""
+    H, T = 16, 300
+    inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv="bf16", seed=760 + d)
+    lr = workloads.lowrank_gate_inputs(0, B=B, T=T, H=H, d=d, seed=760 + d)
+    ref = ref_gates(lr)
+    full = dict(inp)
+    for k in "aewg":
+        full[k] = ref[k]
+    o_ref, s_ref = oracle.recurrent(*[full[n] for n in NAMES])
+    o, s = lowrank_fwd(inp, lr, device, chunk)
+    eo, es = o_err(o, o_ref), s_err(s, s_ref)
+    print(f"gates in the scan d={d} C={chunk}: o={eo.max():.3e} state={es.max():.3e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert max(eo.max(), es.max()) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg,chunk", [(2, 128), (2, 256), (3, 256)])
 def test_fused_equals_gate_kernel_then_forward(device, cfg, chunk):
     """At the 1.34B-class and long-context shapes: the fused call is bit for bit the gate
-    kernel's four gates fed to the plain forward (same products, same order)."""
+    kernel's four gates fed to the plain forward (same products, same order). The cases
+    cover e and w made inside the scan (16-column tiles, C=128) and made by the gate kernel
+    first (16-column tiles at C=256, 8-column tiles on the long-context shape)."""
     inp = workloads.chunk_inputs(cfg)
     lr = workloads.lowrank_gate_inputs(cfg)
     B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
