@@ -13,15 +13,17 @@
 //
 // Layout: state [B,H,dk,dv] fp32 with dv contiguous. A thread owns 4 consecutive
 // columns (one float4) of ROWS rows strided by ROW_GROUPS, so each wave reads whole
-// contiguous rows (coalesced 16-byte loads) and all loads are issued up front.
+// contiguous rows (coalesced 16-byte loads) and all loads are issued up front. The new
+// state is written with non-temporal stores: it is not read again in this step.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace muir {
 
 namespace {
 
-constexpr int kDecodeThreads = 256;
+constexpr int kDecodeThreads = 512;
 
 template <typename QT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
@@ -108,12 +110,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     for (int m = 0; m < ROWS; ++m) {
         const int i = rg + m * ROW_GROUPS;
         const float ai = sh_a[i], ki = sh_k[i];
-        float4 t;
-        t.x = ai * s[m].x + ki * u.x;
-        t.y = ai * s[m].y + ki * u.y;
-        t.z = ai * s[m].z + ki * u.z;
-        t.w = ai * s[m].w + ki * u.w;
-        S4[i * TPR + c4] = t;
+        const f32x4_t t = {ai * s[m].x + ki * u.x, ai * s[m].y + ki * u.y,
+                           ai * s[m].z + ki * u.z, ai * s[m].w + ki * u.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t *>(&S4[i * TPR + c4]));
     }
 }
 

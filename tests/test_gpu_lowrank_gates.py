@@ -107,11 +107,12 @@ def test_forward_driven_by_lowrank_gates(device, d, chunk):
     assert max(eo.max(), es.max()) <= 2e-2
 
 
-def lowrank_fwd(inp, lr, device, chunk):
+def lowrank_fwd(inp, lr, device, chunk, s0=None):
     t = to_device(inp, device, "bf16")
     z = torch.from_numpy(lr["z"]).to(device=device, dtype=torch.bfloat16)
     U, c = dev_weights(lr, device)
-    o, s = muir.chunk_fwd_lowrank(t["q"], t["k"], t["v"], z, U, c, t["r"], chunk=chunk)
+    s0t = None if s0 is None else torch.from_numpy(np.asarray(s0, np.float32)).to(device)
+    o, s = muir.chunk_fwd_lowrank(t["q"], t["k"], t["v"], z, U, c, t["r"], s0t, chunk=chunk)
     torch.cuda.synchronize()
     return to_numpy(o), to_numpy(s)
 
@@ -139,16 +140,18 @@ def test_fused_lowrank_forward_parity(device, d, chunk, T):
 @pytest.mark.parametrize("d,B,chunk", [(128, 2, 128), (64, 4, 64)])
 def test_gates_made_inside_the_scan_parity(device, d, B, chunk):
     """B*H*d/16 = 256 runs 16-column tiles, where e and w are made inside the scan (chunk <=
-    128): against the fp64 recurrence on the oracle's gates, with a ragged tail."""
+    128): against the fp64 recurrence on the oracle's gates, with a ragged tail and a
+    non-zero initial state."""
     H, T = 16, 300
     inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv="bf16", seed=760 + d)
     lr = workloads.lowrank_gate_inputs(0, B=B, T=T, H=H, d=d, seed=760 + d)
+    s0 = (np.random.default_rng(760 + d).standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
     ref = ref_gates(lr)
     full = dict(inp)
     for k in "aewg":
         full[k] = ref[k]
-    o_ref, s_ref = oracle.recurrent(*[full[n] for n in NAMES])
-    o, s = lowrank_fwd(inp, lr, device, chunk)
+    o_ref, s_ref = oracle.recurrent(*[full[n] for n in NAMES], s0=s0)
+    o, s = lowrank_fwd(inp, lr, device, chunk, s0)
     eo, es = o_err(o, o_ref), s_err(s, s_ref)
     print(f"gates in the scan d={d} C={chunk}: o={eo.max():.3e} state={es.max():.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(s).all()
