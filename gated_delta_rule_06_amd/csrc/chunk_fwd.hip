@@ -1182,6 +1182,9 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     }
 
     // ---------------- chain wavefront ----------------
+    // The chain is the critical path: where several workgroups share a SIMD, its wavefront
+    // wins instruction arbitration over the others' readout and gate wavefronts.
+    __builtin_amdgcn_s_setprio(1);
     // State: S[c][i] = state[16c + 4g + i][j0 + x].
     f32x4_t S[NCT];
 #pragma unroll
