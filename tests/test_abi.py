@@ -266,3 +266,49 @@ def test_python_binding_validates_before_calling():
     with pytest.raises(ValueError):
         muir.decode_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0], x[:, 0],
                          torch.zeros(1, 64), torch.zeros(1, 1, 64, 64))
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "muir.h"
+
+int main(void) {
+    /* Host-only calls: sizes, status text, and argument checks that fail before any launch. */
+    const size_t ws = muir_chunk_fwd_workspace_size(1, 256, 2, 64, 64, 64, MUIR_F32);
+    const muir_status_t st = muir_chunk_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                            NULL, NULL, 1, 256, 2, 64, 64, 64, MUIR_F32, NULL, 0,
+                                            NULL);
+    printf("%d %zu %d %s %s\n", muir_version(), ws, (int)st, muir_status_string(st),
+           strlen(muir_last_error()) > 0 ? "detail" : "none");
+    return st == MUIR_ERR_NULL && ws > 0 ? 0 : 1;
+}
+"""
+
+
+def test_c_program_builds_and_calls_the_library(tmp_path):
+    """The public header is plain C11 (and C++): a C caller compiles with warnings as errors,
+    links against libmuir.so and gets sizes and argument errors back without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    lib = muir.lib()  # built, and loadable here
+    libdir = os.path.dirname(muir.LIB_PATH)
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    inc = os.path.dirname(HEADER)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", f"-I{inc}", str(src), "-o", str(exe),
+                    f"-L{libdir}", "-lmuir", f"-Wl,-rpath,{libdir}"], check=True)
+    cxx = shutil.which("g++")
+    if cxx is not None:
+        subprocess.run([cxx, "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", f"-I{inc}", "-x", "c++",
+                        str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    version, ws, status, name, detail = out.stdout.split()
+    assert int(version) == lib.muir_version()
+    assert int(ws) == muir.chunk_fwd_workspace_size(1, 256, 2, 64, 64, 64, 0)
+    assert name == "MUIR_ERR_NULL" and detail == "detail"
