@@ -1453,11 +1453,13 @@ hipError_t scan_vc(const void *v, const float *e, const float *w, const float *o
     return hipGetLastError();
 }
 
-// Value columns per scan workgroup (4 VC): sixteen when that gives every compute unit a
-// workgroup, else eight (bf16 operands; the fp32 path always takes sixteen). Both give
-// the same results bit for bit: every value column goes through the same operations.
+// Value columns per scan workgroup (4 VC): eight when that still gives at most one
+// workgroup per compute unit, else sixteen (bf16 operands; the fp32 path always takes
+// sixteen). A second chain on a compute unit costs more than the narrower tiles save.
+// Both widths give the same results bit for bit: every value column goes through the same
+// operations.
 constexpr int kScanCUs = 256;
-bool scan_narrow_tiles(int B, int H, int d) { return size_t(B) * H * (d / 16) < size_t(kScanCUs); }
+bool scan_narrow_tiles(int B, int H, int d) { return size_t(B) * H * (d / 8) <= size_t(kScanCUs); }
 
 template <typename QT, typename OpT, int D, int C>
 hipError_t scan_typed(const void *v, const float *e, const float *w, const float *og,

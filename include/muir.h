@@ -260,7 +260,7 @@ muir_status_t muir_lowrank_gates(
  * decay a and the query gate g are formed inside the parallel phase's kernel, from z rows
  * shared by every head, so their fp32 rows are never read from memory. The erase and write
  * gates e, w are formed inside the sequential phase's kernel when it runs 16-column value
- * tiles (B*H*dv/16 >= 256) with chunk <= 128; otherwise the gate kernel writes them into
+ * tiles (B*H*dv/8 > 256) with chunk <= 128; otherwise the gate kernel writes them into
  * the workspace and the scan reads them back. Either way the result is muir_chunk_fwd's on
  * the gates muir_lowrank_gates makes from the same z, U and c (bit for bit).
  *

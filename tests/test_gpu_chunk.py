@@ -179,7 +179,7 @@ def test_full_erase_and_no_decay_special_cases(device):
 
 
 def test_value_tile_widths_agree_bit_for_bit(device):
-    """B*H*d/16 >= 256 runs the scan on 16-column value tiles, fewer heads on 8-column ones.
+    """B*H*d/8 > 256 runs the scan on 16-column value tiles, fewer heads on 8-column ones.
     Every value column goes through the same operations either way, so the heads of one
     call, rerun as two calls of half the heads, give the same bits. The wide call (ragged
     tail, non-zero initial state) is also checked against the oracle."""

@@ -139,7 +139,7 @@ def test_fused_lowrank_forward_parity(device, d, chunk, T):
 
 @pytest.mark.parametrize("d,B,chunk", [(128, 2, 128), (64, 4, 64)])
 def test_gates_made_inside_the_scan_parity(device, d, B, chunk):
-    """B*H*d/16 = 256 runs 16-column tiles, where e and w are made inside the scan (chunk <=
+    """B*H*d/8 = 512 runs 16-column tiles, where e and w are made inside the scan (chunk <=
     128): against the fp64 recurrence on the oracle's gates, with a ragged tail and a
     non-zero initial state."""
     H, T = 16, 300
