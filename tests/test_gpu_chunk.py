@@ -196,3 +196,27 @@ def test_value_tile_widths_agree_bit_for_bit(device):
         o_h, s_h = gpu_fwd(part, device, C, np.ascontiguousarray(s0[:, h0:h0 + H // 2]))
         assert np.array_equal(o_h, o[:, :, h0:h0 + H // 2]), f"heads {h0}..: o differs"
         assert np.array_equal(s_h, s[:, h0:h0 + H // 2]), f"heads {h0}..: state differs"
+
+
+def test_head_offsets_past_2_gib(device):
+    """T = 393,216 at H=16, d=128: each fp32 token tensor is 3 GiB, so the byte offsets of the
+    last head's rows pass 2^31 (the scan addresses a head's rows with 32-bit offsets). Inputs
+    follow the decode recipe (base log-rate per head and row, per-token jitter, the same q/k/v
+    and gate draws), drawn on the device with its seeded generator, one token per "layer"
+    slot. The last head is checked against the oracle over the whole sequence."""
+    T, H, d, C = 393216, 16, 128, 256
+    cfg = workloads.DECODE_CONFIG
+    u, r = workloads.decode_base(cfg, L=1, H=H, d=d)
+    u_t = torch.from_numpy(u[0].astype(np.float32)).to(device).expand(T, H, d)
+    x = workloads.decode_step_inputs_torch(0, u_t, device, B=1, cfg=cfg)   # [T, 1, H, d]
+    t = {n: x[n].transpose(0, 1).contiguous() for n in NAMES if n != "r"}   # [1, T, H, d]
+    del x
+    t["r"] = torch.from_numpy(r[0]).to(device)
+    o, s = muir.chunk_fwd(*[t[n] for n in NAMES], chunk=C)
+    torch.cuda.synchronize()
+    h = H - 1
+    head = {n: t[n][:, :, h:h + 1].float().cpu().numpy() for n in NAMES if n != "r"}
+    head["r"] = r[0][h:h + 1]
+    o_ref, s_ref = oracle.recurrent(*[head[n] for n in NAMES])
+    assert_parity(to_numpy(o[:, :, h:h + 1]), to_numpy(s[:, h:h + 1]), o_ref, s_ref, TOL["bf16"],
+                  f"T={T} head {h}")
