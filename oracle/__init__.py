@@ -27,6 +27,8 @@ Forms provided here:
   * ``naive_unpivoted_nonfinite`` the unpivoted fp32 scheme that divides by cumulative
                            decays, kept only as a negative control (same two passages);
   * ``lowrank_gates``      (``gates.py``) the four gates from the rank-512 gate projection.
+  * ``backward``           (``backward.py``) every input's gradient, by autograd, by the
+                           token adjoint and by chunk products (no GPU counterpart yet).
 
 Every form is pinned by tests that do not reuse its own formula: closed forms that
 reduce to textbook linear attention or gated linear attention, the last-write-only
