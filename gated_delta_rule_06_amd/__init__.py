@@ -19,6 +19,7 @@ __all__ = [
     "chunk_fwd_scan", "chunk_fwd_scalar_erase", "chunk_fwd_scalar_erase_workspace_size",
     "chunk_fwd_scalar_erase_solve",
     "chunk_fwd_scalar_erase_scan", "lowrank_gates", "chunk_fwd_lowrank", "decode_step",
+    "chunk_bwd", "chunk_bwd_workspace_size", "BWD_GRADS",
     "status_string", "last_error", "version", "MUIR_F32", "MUIR_BF16", "STATUS",
 ]
 
@@ -77,6 +78,10 @@ def lib():
         L.muir_chunk_fwd_lowrank.restype = i
         L.muir_lowrank_gates.argtypes = [vp] * 13 + [i] * 4 + [vp]
         L.muir_lowrank_gates.restype = i
+        L.muir_chunk_bwd_workspace_size.argtypes = [i] * 7
+        L.muir_chunk_bwd_workspace_size.restype = sz
+        L.muir_chunk_bwd.argtypes = [vp] * 20 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_bwd.restype = i
         L.muir_decode_step.argtypes = [vp] * 10 + [i] * 5 + [vp]
         L.muir_decode_step.restype = i
         L.muir_status_string.argtypes = [i]
@@ -197,6 +202,58 @@ def chunk_fwd(q, k, v, a, g, e, w, r, s0=None, *, chunk: int = 64, o=None, s_out
             workspace.numel(), _stream(dev))
     _check(status)
     return o, s_out
+
+
+def chunk_bwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, chunk: int,
+                            dtype_code: int) -> int:
+    return int(lib().muir_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk, dtype_code))
+
+
+BWD_GRADS = ("q", "k", "v", "la", "g", "e", "w", "r", "s0")
+
+
+def chunk_bwd(q, k, v, a, g, e, w, r, s0=None, *, do, ds_out=None, chunk: int = 64,
+              workspace=None, out=None):
+    """Backward pass of ``chunk_fwd`` (``muir_chunk_bwd``).
+
+    Inputs as for ``chunk_fwd``, plus ``do`` (dL/do, [B,T,H,dv], the q/k/v dtype) and
+    ``ds_out`` (dL/ds_out, [B,H,dk,dv] float32 or None). Returns a dict of float32
+    gradients keyed by ``BWD_GRADS``: "la" is a * dL/da, "r" is [H,dk], "s0" is
+    [B,H,dk,dv]. ``out`` may hold pre-allocated tensors under those keys.
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _require(t, name, q.dtype, (B, T, H, dk if name in ("q", "k") else dv), dev)
+    for name, t, d in (("a", a, dk), ("g", g, dk), ("e", e, dv), ("w", w, dv)):
+        _require(t, name, torch.float32, (B, T, H, d), dev)
+    _require(r, "r", torch.float32, (H, dk), dev)
+    for name, t in (("s0", s0), ("ds_out", ds_out)):
+        if t is not None:
+            _require(t, name, torch.float32, (B, H, dk, dv), dev)
+    shapes = {n: (B, T, H, dk if n in ("q", "k", "la", "g") else dv) for n in BWD_GRADS}
+    shapes["r"] = (H, dk)
+    shapes["s0"] = (B, H, dk, dv)
+    out = dict(out or {})
+    for n, shp in shapes.items():
+        if n in out:
+            _require(out[n], "d" + n, torch.float32, shp, dev)
+        else:
+            out[n] = torch.empty(shp, dtype=torch.float32, device=dev)
+    need = chunk_bwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", torch.uint8, None, dev)
+    status = lib().muir_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(g), _ptr(e), _ptr(w), _ptr(r), _ptr(s0),
+        _ptr(do), _ptr(ds_out), *[_ptr(out[n]) for n in BWD_GRADS],
+        B, T, H, dk, dv, chunk, code, _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(status)
+    return out
 
 
 def chunk_fwd_prepare(q, k, a, g, r, *, chunk: int, workspace):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmuir.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_fwd.hip", "wy_fwd.hip", "gates_fwd.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_fwd.hip", "chunk_bwd.hip", "wy_fwd.hip", "gates_fwd.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of every kernel. MFMA accumulators are kept

@@ -535,4 +535,90 @@ muir_status_t muir_decode_step(const void *q, const void *k, const void *v, cons
                      "decode_step launch");
 }
 
+size_t muir_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int chunk,
+                                     muir_dtype_t qkv) {
+    if (B < 1 || T < 0 || H < 1 || dk != dv || !supported_d(dk) || chunk != 64) return 0;
+    if (qkv != MUIR_F32 && qkv != MUIR_BF16) return 0;
+    return muir::chunk_bwd_workspace_bytes(B, T, H, dk, qkv == MUIR_BF16);
+}
+
+muir_status_t muir_chunk_bwd(const void *q, const void *k, const void *v, const float *a,
+                             const float *g, const float *e, const float *w, const float *r,
+                             const float *s0, const void *dout, const float *ds_out, float *dq,
+                             float *dk, float *dv, float *dla, float *dg, float *de, float *dw,
+                             float *dr, float *ds0, int B, int T, int H, int dk_, int dv_,
+                             int chunk, muir_dtype_t qkv, void *workspace,
+                             size_t workspace_bytes, muir_stream_t stream) {
+    const char *fn = "chunk_bwd";
+    if (B < 1 || T < 0 || H < 1)
+        return fail(MUIR_ERR_SHAPE, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn,
+                    B, T, H);
+    if (qkv != MUIR_F32 && qkv != MUIR_BF16)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, static_cast<int>(qkv));
+    if (dk_ != dv_ || !supported_d(dk_))
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: need dk == dv in {64, 128} (got %d, %d)", fn,
+                    dk_, dv_);
+    if (chunk != 64)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: the backward runs on chunks of 64 (got %d)", fn,
+                    chunk);
+    if (!r || !dr) return fail(MUIR_ERR_NULL, "%s: r and dr are required", fn);
+    if (T > 0 && (!q || !k || !v || !a || !g || !e || !w || !dout || !dq || !dk || !dv ||
+                  !dla || !dg || !de || !dw))
+        return fail(MUIR_ERR_NULL, "%s: every input and gradient pointer except s0, ds_out "
+                    "and ds0 is required", fn);
+    const int d = dk_;
+    const size_t es = qkv == MUIR_BF16 ? 2 : 4;
+    size_t n_tok, n_state;
+    if (!mul_size(n_tok, {static_cast<size_t>(B), static_cast<size_t>(T), static_cast<size_t>(H),
+                          static_cast<size_t>(d)}) ||
+        !mul_size(n_state, {static_cast<size_t>(B), static_cast<size_t>(H), static_cast<size_t>(d),
+                            static_cast<size_t>(d)}) ||
+        n_tok > SIZE_MAX / 4 || n_state > SIZE_MAX / 4)
+        return fail(MUIR_ERR_SHAPE, "%s: sizes overflow", fn);
+    const size_t head_span = static_cast<size_t>(T) * H * d * 4;
+    if (head_span > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: T*H*d*4 = %zu bytes exceeds 4 GiB", fn, head_span);
+    const size_t need = muir::chunk_bwd_workspace_bytes(B, T, H, d, qkv == MUIR_BF16);
+    if (need == 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (muir::chunk_workspace_bytes(B, T, H, d, 64, qkv == MUIR_BF16) /
+            (static_cast<size_t>(B) * H) > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: the forward workspace of one head exceeds 4 GiB",
+                    fn);
+    if (!workspace)
+        return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+    if (workspace_bytes < need)
+        return fail(MUIR_ERR_WORKSPACE, "%s: workspace has %zu bytes, need %zu", fn,
+                    workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(MUIR_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    const void *all[] = {q, k, v, a, g, e, w, r, s0, dout, ds_out, dq, dk, dv, dla, dg, de, dw,
+                         dr, ds0};
+    for (const void *p : all)
+        if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
+    const Range inputs[] = {
+        range("q", q, n_tok * es), range("k", k, n_tok * es), range("v", v, n_tok * es),
+        range("a", a, n_tok * 4), range("g", g, n_tok * 4), range("e", e, n_tok * 4),
+        range("w", w, n_tok * 4), range("r", r, static_cast<size_t>(H) * d * 4),
+        range("s0", s0, n_state * 4), range("dout", dout, n_tok * es),
+        range("ds_out", ds_out, n_state * 4)};
+    const Range outputs[] = {
+        range("dq", dq, n_tok * 4), range("dk", dk, n_tok * 4), range("dv", dv, n_tok * 4),
+        range("dla", dla, n_tok * 4), range("dg", dg, n_tok * 4), range("de", de, n_tok * 4),
+        range("dw", dw, n_tok * 4), range("dr", dr, static_cast<size_t>(H) * d * 4),
+        range("ds0", ds0, n_state * 4), range("workspace", workspace, need)};
+    for (const Range &o : outputs) {
+        for (const Range &x : inputs)
+            if (overlaps(o, x)) return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, x.name);
+        for (const Range &y : outputs)
+            if (&y != &o && overlaps(o, y))
+                return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, y.name);
+    }
+    const muir::ChunkBwdArgs args{q, k, v, a, g, e, w, r, s0, dout, ds_out,
+                                  dq, dk, dv, dla, dg, de, dw, dr, ds0};
+    return check_hip(muir::launch_chunk_bwd(args, B, T, H, d, qkv == MUIR_BF16, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                     fn);
+}
+
 }  // extern "C"

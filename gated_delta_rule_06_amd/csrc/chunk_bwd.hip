@@ -1,0 +1,683 @@
+// Backward pass of the chunkwise gated delta rule with matched-filter readout, for gfx950.
+//
+// Method: Muir abstract (Astral Feed page, "Full text") for the recurrence; liuch.name summary
+// (third bullet) and the openai-hub page (section on the chunkwise algorithm) for the chunk
+// form whose reverse mode this is. Per head, with q_hat = r * g * q, b = w * v, the state S
+// (dk x dv) is decayed per row, the prediction p_t = S^T k_t is erased under the value gate,
+// u_t = b_t - e_t * p_t is written, and o_t = S^T q_hat_t is read. Given dO and dS_T, the
+// adjoint lambda = dL/dS runs backwards. Per chunk of C tokens, with gamma_t the decay product
+// from the chunk start through t, beta_t the product after t to the chunk end, Gamma_ts the
+// product over s < tau <= t, M_ts = sum_i k_ti Gamma_tsi k_si (s < t) and P_ts = sum_i
+// q_hat_ti Gamma_tsi k_si (s <= t):
+//
+//   (I + M^T Diag(e_j)) dU_j = (K*beta) lambda_C + P^T dO        per value column j
+//   dP = -E * dU,   dv = w * dU,   dw = v * dU,   de = -p * dU
+//   lambda_0 = Diag(gamma_C) lambda_C + (Q_hat*gamma)^T dO + (K*gamma)^T dP
+//   dq_hat_t = gamma_t * (S0 do_t) + sum_{s<=t} Gamma_ts * k_s (u_s . do_t)
+//   dk_t     = gamma_t * (S0 dp_t) + sum_{s<t} Gamma_ts * k_s (u_s . dp_t)          (read)
+//            + beta_t * (lambda_C u_t) + sum_{t'>=t} Gamma_t't * q_hat_t' (do_t' . u_t)
+//            + sum_{t'>t} Gamma_t't * k_t' (dp_t' . u_t)                              (write)
+//   a * dL/da at token tau = sum_{t>=tau in chunk} [q_hat*dq_hat + k*dk_read - k*dk_write]_t
+//                            + rowsum(S_C * lambda_C)
+//
+// No decay is ever divided by: cross-block decays are products of factors in (0, 1] split at
+// 16-token block boundaries, and decays inside a block or along one channel are running
+// products.
+//
+// Kernels, in launch order (after the forward's prepare and its scan, which also writes u and
+// the chunk start states):
+//   bwd_prepare_kernel  one workgroup per (b, h, chunk): K*beta, K*gamma, Q_hat*gamma, gamma_C,
+//                       M and P (fp32 matrix cores for the cross-block tiles), and p.
+//   bwd_scan_kernel     one workgroup per (b, h, 8 value columns), chunks in reverse: the
+//                       transposed triangular solve, the adjoint carry, dv, dw, de.
+//   bwd_grads_kernel    one workgroup per (b, h, chunk): dq, dk, dg and a * dL/da.
+//   bwd_dr_kernel       dr summed over batch and chunks.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma.hpp"
+
+namespace muir {
+
+namespace {
+
+constexpr int kC = 64;        // tokens per chunk
+constexpr int kNB = kC / 16;  // 16-token blocks per chunk
+constexpr int kVT = 8;        // value columns per scan workgroup
+constexpr int kBwdThreads = 256;
+
+// D[16x16] += A[16xK] B[Kx16] on the fp32 matrix cores: fa(r, k) = A[r][k], fb(c, k) = B[k][c].
+// Lane l holds output rows 4 (l / 16) .. + 3 of column l % 16.
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4_t mm16(FA fa, FB fb, f32x4_t acc) {
+    const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+#pragma unroll 8
+    for (int m = 0; m < K / 4; ++m) {
+        const int kk = 4 * m + kq;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, kk), fb(r, kk), acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <typename QT> __device__ __forceinline__ float ld(const QT *p, size_t i) { return to_f32(p[i]); }
+
+// ------------------------------------------------------------------------------------------
+// Prepare. LDS: M and P [C][C + 1]; then a union of the pivot pass arrays (per 64-channel
+// pass: a, k, q_hat, in-block prefix F and suffix R [C][65], cross-block products [6][64])
+// and K*gamma [C][D + 4] for the prediction.
+// ------------------------------------------------------------------------------------------
+template <int D> struct PrepBwdLds {
+    static constexpr int LDM = kC + 1;
+    static constexpr int DH = 64;
+    static constexpr int LDH = DH + 1;
+    static constexpr int NPAIR = kNB * (kNB - 1) / 2;
+    static constexpr int MP = 2 * kC * LDM;
+    static constexpr int PASS = 5 * kC * LDH + NPAIR * DH;
+    static constexpr int KGL = kC * (D + 4);
+    static constexpr int FLOATS = MP + (PASS > KGL ? PASS : KGL);
+    static constexpr size_t BYTES = size_t(FLOATS) * 4;
+};
+
+template <typename QT, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
+    const QT *__restrict__ q, const QT *__restrict__ k, const float *__restrict__ a,
+    const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
+    const float *__restrict__ u, float *__restrict__ kb, float *__restrict__ kg,
+    float *__restrict__ qg, float *__restrict__ gC, float *__restrict__ Mw,
+    float *__restrict__ Pw, float *__restrict__ pred, int T, int H, int nchunks) {
+    using L = PrepBwdLds<D>;
+    constexpr int C = kC, LDM = L::LDM, DH = L::DH, LDH = L::LDH;
+    extern __shared__ float lds[];
+    float *sM = lds, *sP = lds + kC * LDM;
+    float *pass = lds + L::MP;
+    float *sA = pass, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH,
+          *sR = sF + C * LDH, *sMid = sR + C * LDH;
+    float *sKG = pass;
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int bh = b * H + h;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t HD = size_t(H) * D;
+    const int c0 = c * C;
+    const int nval = min(C, T - c0);
+    const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
+    const size_t slot = size_t(bh) * nchunks + c;
+    const float *rh = r + size_t(h) * D;
+
+    for (int idx = tid; idx < 2 * C * LDM; idx += kBwdThreads) lds[idx] = 0.f;
+
+    // Cross-block tiles of M and P: pair p = (bt, bs), bs < bt, pair index bt (bt - 1) / 2 + bs;
+    // tile job j < 12: matrix j / 6 (0: M, 1: P), pair j % 6. Wave w owns jobs w, w + 4, w + 8.
+    f32x4_t acc[3] = {zero4(), zero4(), zero4()};
+    // Diagonal-block entries (t, s), s <= t in one block, by pair index: thread tid owns
+    // entries tid, tid + 256, tid + 512 (of 4 * 136).
+    constexpr int NDIAG = kNB * 136;
+    float dM[3] = {0.f, 0.f, 0.f}, dP[3] = {0.f, 0.f, 0.f};
+    int dt[3], ds[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int pi = tid + kBwdThreads * j;
+        int bb = 0, tl = 0, sl = 0;
+        if (pi < NDIAG) {
+            bb = pi / 136;
+            int rem = pi % 136;
+            while (rem > tl) { ++tl; rem -= tl; }
+            sl = rem;
+        }
+        dt[j] = 16 * bb + tl;
+        ds[j] = 16 * bb + sl;
+    }
+
+    for (int p0 = 0; p0 < D; p0 += DH) {
+        __syncthreads();
+        for (int idx = tid; idx < C * DH; idx += kBwdThreads) {
+            const int t = idx / DH, ii = idx % DH;
+            const bool valid = t < nval;
+            const size_t o = tok0 + size_t(t) * HD + p0 + ii;
+            sA[t * LDH + ii] = valid ? a[o] : 1.f;
+            sK[t * LDH + ii] = valid ? ld(k, o) : 0.f;
+            sQ[t * LDH + ii] = valid ? rh[p0 + ii] * g[o] * ld(q, o) : 0.f;
+        }
+        __syncthreads();
+        if (tid < DH) {
+            const int ii = tid;
+            float bp[kNB];
+#pragma unroll
+            for (int bb = 0; bb < kNB; ++bb) {
+                float run = 1.f;
+                for (int tl = 0; tl < 16; ++tl) {
+                    const int t = 16 * bb + tl;
+                    run *= sA[t * LDH + ii];
+                    sF[t * LDH + ii] = run;
+                }
+                run = 1.f;
+                for (int tl = 15; tl >= 0; --tl) {
+                    const int t = 16 * bb + tl;
+                    sR[t * LDH + ii] = run;
+                    run *= sA[t * LDH + ii];
+                }
+                bp[bb] = run;
+            }
+#pragma unroll
+            for (int bt = 1; bt < kNB; ++bt) {
+                float mid = 1.f;
+#pragma unroll
+                for (int bs = bt - 1; bs >= 0; --bs) {
+                    sMid[(bt * (bt - 1) / 2 + bs) * DH + ii] = mid;
+                    mid *= bp[bs];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int job = wave + 4 * j;
+            const int mat = job / 6, pr = job % 6;
+            const int bt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
+            const int bs = pr - bt * (bt - 1) / 2;
+            const float *sX = mat == 0 ? sK : sQ;
+            acc[j] = mm16<DH>(
+                [&](int rr, int kk) { return sX[(16 * bt + rr) * LDH + kk] * sF[(16 * bt + rr) * LDH + kk]; },
+                [&](int cc, int kk) {
+                    return sK[(16 * bs + cc) * LDH + kk] * sR[(16 * bs + cc) * LDH + kk] * sMid[pr * DH + kk];
+                },
+                acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if (tid + kBwdThreads * j >= NDIAG) continue;
+            const int t = dt[j], s = ds[j];
+            float m = 0.f, pp = 0.f;
+            for (int ii = 0; ii < DH; ++ii) {
+                float gm = 1.f;
+                for (int tau = s + 1; tau <= t; ++tau) gm *= sA[tau * LDH + ii];
+                const float ks = gm * sK[s * LDH + ii];
+                m = fmaf(sK[t * LDH + ii], ks, m);
+                pp = fmaf(sQ[t * LDH + ii], ks, pp);
+            }
+            if (s < t) dM[j] += m;
+            dP[j] += pp;
+        }
+    }
+    __syncthreads();
+    // M and P into LDS (the upper parts and M's diagonal stay zero).
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int job = wave + 4 * j;
+        const int mat = job / 6, pr = job % 6;
+        const int bt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
+        const int bs = pr - bt * (bt - 1) / 2;
+        float *dst = mat == 0 ? sM : sP;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * bt + 4 * (lane >> 4) + i) * LDM + 16 * bs + (lane & 15)] = acc[j][i];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        if (tid + kBwdThreads * j >= NDIAG) continue;
+        sM[dt[j] * LDM + ds[j]] = dM[j];
+        sP[dt[j] * LDM + ds[j]] = dP[j];
+    }
+    // Per-channel decay products: K*beta, K*gamma, Q_hat*gamma, gamma_C; K*gamma also to LDS.
+    if (tid < D) {
+        const int i = tid;
+        float gm = 1.f;
+        for (int t = 0; t < C; ++t) {
+            const bool valid = t < nval;
+            const size_t o = tok0 + size_t(t) * HD + i;
+            const float at = valid ? a[o] : 1.f;
+            const float kt = valid ? ld(k, o) : 0.f;
+            const float qh = valid ? rh[i] * g[o] * ld(q, o) : 0.f;
+            gm *= at;
+            kg[(slot * C + t) * D + i] = kt * gm;
+            qg[(slot * C + t) * D + i] = qh * gm;
+            sKG[t * (D + 4) + i] = kt * gm;
+        }
+        gC[slot * D + i] = gm;
+        float bt = 1.f;
+        for (int t = C - 1; t >= 0; --t) {
+            const bool valid = t < nval;
+            const size_t o = tok0 + size_t(t) * HD + i;
+            kb[(slot * C + t) * D + i] = (valid ? ld(k, o) : 0.f) * bt;
+            bt *= valid ? a[o] : 1.f;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+        const int t = idx / C, s = idx % C;
+        Mw[slot * C * C + idx] = sM[t * LDM + s];
+        Pw[slot * C * C + idx] = sP[t * LDM + s];
+    }
+    // p = (K*gamma) S0 + M U, [C x D]: wave w owns value-column tiles w, w + 4, ...
+    const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
+    const float *Ub = u + (size_t(b) * T + c0) * HD + size_t(h) * D;
+    for (int jt = wave; jt < D / 16; jt += 4) {
+#pragma unroll
+        for (int tt = 0; tt < kNB; ++tt) {
+            f32x4_t y = mm16<D>([&](int rr, int kk) { return sKG[(16 * tt + rr) * (D + 4) + kk]; },
+                                [&](int cc, int kk) { return S0[size_t(kk) * D + 16 * jt + cc]; }, zero4());
+            y = mm16<C>([&](int rr, int kk) { return sM[(16 * tt + rr) * LDM + kk]; },
+                        [&](int cc, int kk) { return kk < nval ? Ub[size_t(kk) * HD + 16 * jt + cc] : 0.f; }, y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tt + 4 * (lane >> 4) + i;
+                if (t < nval) pred[tok0 + size_t(t) * HD + 16 * jt + (lane & 15)] = y[i];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Reverse scan over chunks, per (b, h, 8 value columns).
+// ------------------------------------------------------------------------------------------
+template <typename QT, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
+    const QT *__restrict__ dout, const QT *__restrict__ v, const float *__restrict__ e,
+    const float *__restrict__ w, const float *__restrict__ kb, const float *__restrict__ kg,
+    const float *__restrict__ qg, const float *__restrict__ gC, const float *__restrict__ Mw,
+    const float *__restrict__ Pw, const float *__restrict__ pred, const float *__restrict__ dsT,
+    float *__restrict__ dU, float *__restrict__ lamC, float *__restrict__ dv,
+    float *__restrict__ dw, float *__restrict__ de, float *__restrict__ ds0, int T, int H, int BH,
+    int nchunks) {
+    constexpr int C = kC, VT = kVT, NVT = D / VT, LDM = C + 1;
+    __shared__ float sM[C * LDM], sP[C * LDM];
+    __shared__ float sLam[D][VT], sdO[C][VT], sE[C][VT], sdP[C][VT], sRhs[C][VT];
+
+    // The value tiles of one head get ids equal mod 8, so they share an XCD and its L2.
+    const int id = blockIdx.x;
+    const int bh = (id >> 3) / NVT * 8 + (id & 7);
+    const int ct = (id >> 3) % NVT;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh % H;
+    const int j0 = VT * ct;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t HD = size_t(H) * D;
+
+    for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
+        const int i = idx / VT, j = idx % VT;
+        sLam[i][j] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
+    }
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const int c0 = c * C;
+        const int nval = min(C, T - c0);
+        const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D + j0;
+        const size_t slot = size_t(bh) * nchunks + c;
+        __syncthreads();
+        for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
+            const int i = idx / VT, j = idx % VT;
+            lamC[(slot * D + i) * D + j0 + j] = sLam[i][j];
+        }
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+            const int t = idx / C, s = idx % C;
+            sM[t * LDM + s] = Mw[slot * C * C + idx];
+            sP[t * LDM + s] = Pw[slot * C * C + idx];
+        }
+        for (int idx = tid; idx < C * VT; idx += kBwdThreads) {
+            const int t = idx / VT, j = idx % VT;
+            const bool valid = t < nval;
+            const size_t o = tok0 + size_t(t) * HD + j;
+            sdO[t][j] = valid ? ld(dout, o) : 0.f;
+            sE[t][j] = valid ? e[o] : 0.f;
+        }
+        __syncthreads();
+        // Right-hand side: (K*beta) lambda_C + P^T dO, thread (t, column pair).
+        {
+            const int t = tid >> 2, j = 2 * (tid & 3);
+            const float *kbr = kb + (slot * C + t) * D;
+            float r0 = 0.f, r1 = 0.f;
+            for (int i = 0; i < D; ++i) {
+                const float x = kbr[i];
+                r0 = fmaf(x, sLam[i][j], r0);
+                r1 = fmaf(x, sLam[i][j + 1], r1);
+            }
+            for (int tp = t; tp < C; ++tp) {
+                const float p = sP[tp * LDM + t];
+                r0 = fmaf(p, sdO[tp][j], r0);
+                r1 = fmaf(p, sdO[tp][j + 1], r1);
+            }
+            sRhs[t][j] = r0;
+            sRhs[t][j + 1] = r1;
+        }
+        __syncthreads();
+        // Back substitution, wave w: columns 2w, 2w + 1, lane t. With y = e * dU,
+        // dU_t = rhs_t - sum_{s > t} M_st y_s; lanes t >= s read M_st = 0.
+        {
+            const int j = 2 * wave;
+            float x0 = sRhs[lane][j], x1 = sRhs[lane][j + 1];
+            const float e0 = sE[lane][j], e1 = sE[lane][j + 1];
+#pragma unroll
+            for (int s = C - 1; s >= 0; --s) {
+                const float m = sM[s * LDM + lane];
+                const float y0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0 * x0), s));
+                const float y1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1 * x1), s));
+                x0 = fmaf(-m, y0, x0);
+                x1 = fmaf(-m, y1, x1);
+            }
+            sdP[lane][j] = -e0 * x0;
+            sdP[lane][j + 1] = -e1 * x1;
+            if (lane < nval) {
+                const size_t o = tok0 + size_t(lane) * HD + j;
+                dU[o] = x0;
+                dU[o + 1] = x1;
+                dv[o] = w[o] * x0;
+                dv[o + 1] = w[o + 1] * x1;
+                dw[o] = ld(v, o) * x0;
+                dw[o + 1] = ld(v, o + 1) * x1;
+                de[o] = -pred[o] * x0;
+                de[o + 1] = -pred[o + 1] * x1;
+            }
+        }
+        __syncthreads();
+        // lambda <- Diag(gamma_C) lambda + (Q_hat*gamma)^T dO + (K*gamma)^T dP.
+        {
+            constexpr int TPI = kBwdThreads / D;  // threads per channel
+            constexpr int NJ = VT / TPI;
+            const int i = tid % D, jb = (tid / D) * NJ;
+            float acc[NJ];
+            const float gc = gC[slot * D + i];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[j] = gc * sLam[i][jb + j];
+            for (int t = 0; t < C; ++t) {
+                const float xq = qg[(slot * C + t) * D + i], xk = kg[(slot * C + t) * D + i];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[j] = fmaf(xq, sdO[t][jb + j], fmaf(xk, sdP[t][jb + j], acc[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sLam[i][jb + j] = acc[j];
+        }
+    }
+    __syncthreads();
+    if (ds0) {
+        for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
+            const int i = idx / VT, j = idx % VT;
+            ds0[(size_t(bh) * D + i) * D + j0 + j] = sLam[i][j];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Chunk-parallel gradients. LDS: O U^T and dP U^T [C][C + 1]; then a union of U, dO, dP
+// [C][D + 4] (products) and k, a, q_hat channel-major [D][C + 1] (decayed sums).
+// ------------------------------------------------------------------------------------------
+template <int D> struct GradLds {
+    static constexpr int LDM = kC + 1, LDX = D + 4, LDT = kC + 1;
+    static constexpr int OUPU = 2 * kC * LDM;
+    static constexpr int P1 = 3 * kC * LDX, P2 = 3 * D * LDT;
+    static constexpr int FLOATS = OUPU + (P1 > P2 ? P1 : P2);
+    static constexpr size_t BYTES = size_t(FLOATS) * 4;
+};
+
+template <typename QT, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
+    const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ dout,
+    const float *__restrict__ a, const float *__restrict__ g, const float *__restrict__ e,
+    const float *__restrict__ r, const float *__restrict__ U, const float *__restrict__ dU,
+    const float *__restrict__ states, const float *__restrict__ lamC, float *__restrict__ X3,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg,
+    float *__restrict__ dla, float *__restrict__ drp, int T, int H, int nchunks) {
+    using L = GradLds<D>;
+    constexpr int C = kC, LDM = L::LDM, LDX = L::LDX, LDT = L::LDT;
+    extern __shared__ float lds[];
+    float *sOU = lds, *sPU = lds + C * LDM;
+    float *un = lds + L::OUPU;
+    float *sU = un, *sdO = un + C * LDX, *sdP = un + 2 * C * LDX;
+    float *sKT = un, *sAT = un + D * LDT, *sQT = un + 2 * D * LDT;
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int bh = b * H + h;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t HD = size_t(H) * D;
+    const int c0 = c * C;
+    const int nval = min(C, T - c0);
+    const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
+    const size_t slot = size_t(bh) * nchunks + c;
+    const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
+    const float *SC = S0 + size_t(D) * D;
+    const float *lam = lamC + slot * D * D;
+
+    for (int idx = tid; idx < C * D; idx += kBwdThreads) {
+        const int t = idx / D, j = idx % D;
+        const bool valid = t < nval;
+        const size_t o = tok0 + size_t(t) * HD + j;
+        sU[t * LDX + j] = valid ? U[o] : 0.f;
+        sdO[t * LDX + j] = valid ? ld(dout, o) : 0.f;
+        sdP[t * LDX + j] = valid ? -e[o] * dU[o] : 0.f;
+    }
+    __syncthreads();
+    // O U^T (s <= t) and dP U^T (s < t), lower 16x16 tiles; job j < 20: matrix j / 10, tile
+    // j % 10 = bt (bt + 1) / 2 + bs.
+    for (int job = wave; job < 20; job += 4) {
+        const int mat = job / 10, tl = job % 10;
+        const int bt = tl < 1 ? 0 : (tl < 3 ? 1 : (tl < 6 ? 2 : 3));
+        const int bs = tl - bt * (bt + 1) / 2;
+        const float *sX = mat == 0 ? sdO : sdP;
+        const f32x4_t y = mm16<D>([&](int rr, int kk) { return sX[(16 * bt + rr) * LDX + kk]; },
+                                  [&](int cc, int kk) { return sU[(16 * bs + cc) * LDX + kk]; }, zero4());
+        float *dst = mat == 0 ? sOU : sPU;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * bt + 4 * (lane >> 4) + i, s = 16 * bs + (lane & 15);
+            dst[t * LDM + s] = (mat == 0 ? s <= t : s < t) ? y[i] : 0.f;
+        }
+    }
+    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D].
+    for (int it = wave; it < D / 16; it += 4) {
+#pragma unroll
+        for (int tt = 0; tt < kNB; ++tt) {
+            f32x4_t y1 = zero4(), y2 = zero4(), y3 = zero4();
+            const int rr = lane & 15, kq = lane >> 4;
+#pragma unroll 4
+            for (int m = 0; m < D / 4; ++m) {
+                const int kk = 4 * m + kq;
+                const float sb = S0[size_t(16 * it + rr) * D + kk];
+                const float lb = lam[size_t(16 * it + rr) * D + kk];
+                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], sb, y1, 0, 0, 0);
+                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], sb, y2, 0, 0, 0);
+                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + kk], lb, y3, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tt + 4 * (lane >> 4) + i;
+                if (t < nval) {
+                    const size_t o = tok0 + size_t(t) * HD + 16 * it + (lane & 15);
+                    dq[o] = y1[i];
+                    dk[o] = y2[i];
+                    X3[o] = y3[i];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const float *rh = r + size_t(h) * D;
+    for (int idx = tid; idx < C * D; idx += kBwdThreads) {
+        const int t = idx / D, i = idx % D;
+        const bool valid = t < nval;
+        const size_t o = tok0 + size_t(t) * HD + i;
+        sKT[i * LDT + t] = valid ? ld(k, o) : 0.f;
+        sAT[i * LDT + t] = valid ? a[o] : 1.f;
+        sQT[i * LDT + t] = valid ? rh[i] * g[o] * ld(q, o) : 0.f;
+    }
+    __syncthreads();
+    const int i = tid % D, role = tid / D;
+    const float *kT = sKT + i * LDT, *aT = sAT + i * LDT, *qT = sQT + i * LDT;
+    if (role == 0) {
+        // dq_hat and the read part of dk, tokens in order (gamma as a running product).
+        float gm = 1.f, dr_acc = 0.f;
+        for (int t = 0; t < C; ++t) {
+            gm *= aT[t];
+            float sq = 0.f, sr = 0.f, run = 1.f;
+            for (int s = t; s >= 0; --s) {
+                const float ks = run * kT[s];
+                sq = fmaf(sOU[t * LDM + s], ks, sq);
+                sr = fmaf(sPU[t * LDM + s], ks, sr);
+                run *= aT[s];
+            }
+            if (t < nval) {
+                const size_t o = tok0 + size_t(t) * HD + i;
+                const float dqh = fmaf(gm, dq[o], sq);
+                const float dkr = fmaf(gm, dk[o], sr);
+                const float gt = g[o], qt = ld(q, o);
+                dq[o] = rh[i] * gt * dqh;
+                dg[o] = rh[i] * qt * dqh;
+                dr_acc = fmaf(gt * qt, dqh, dr_acc);
+                dk[o] = dkr;
+                dla[o] = fmaf(qT[t], dqh, kT[t] * dkr);
+            }
+        }
+        drp[slot * D + i] = dr_acc;
+    } else if (role == 1) {
+        // Write part of dk, tokens in reverse (beta as a running product).
+        float bt = 1.f;
+        for (int s = C - 1; s >= 0; --s) {
+            float sw = 0.f, run = 1.f;
+            for (int t = s; t < C; ++t) {
+                sw = fmaf(sOU[t * LDM + s], run * qT[t], sw);
+                sw = fmaf(sPU[t * LDM + s], run * kT[t], sw);
+                if (t + 1 < C) run *= aT[t + 1];
+            }
+            if (s < nval) {
+                const size_t o = tok0 + size_t(s) * HD + i;
+                X3[o] = fmaf(bt, X3[o], sw);
+            }
+            bt *= aT[s];
+        }
+    }
+    __syncthreads();
+    if (role == 0) {
+        float rs = 0.f;
+        for (int j = 0; j < D; ++j) rs = fmaf(SC[size_t(i) * D + j], lam[size_t(i) * D + j], rs);
+        float cum = 0.f;
+        for (int t = nval - 1; t >= 0; --t) {
+            const size_t o = tok0 + size_t(t) * HD + i;
+            const float kw = X3[o];
+            cum += dla[o] - kT[t] * kw;
+            dla[o] = cum + rs;
+            dk[o] += kw;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void bwd_dr_kernel(const float *__restrict__ drp, float *__restrict__ dr,
+                                                   int B, int H, int nchunks) {
+    const int h = blockIdx.x, i = threadIdx.x;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < nchunks; ++c) s += drp[((size_t(b) * H + h) * nchunks + c) * D + i];
+    dr[size_t(h) * D + i] = s;
+}
+
+// Workspace regions, each 256-byte aligned.
+struct BwdLayout {
+    size_t fwd, o, u, states, kb, kg, qg, gC, M, P, pred, dU, lamC, X3, drp, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
+    const size_t fwd = chunk_workspace_bytes(B, T, H, d, kC, bf16);
+    if (fwd == 0 && T > 0) return false;
+    const size_t nc = (size_t(T) + kC - 1) / kC;
+    const size_t BH = size_t(B) * H, tok = size_t(B) * T * H * d;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    L.fwd = take(fwd);
+    L.o = take(tok * (bf16 ? 2 : 4));
+    L.u = take(tok * 4);
+    L.states = take(BH * (nc + 1) * d * d * 4);
+    L.kb = take(BH * nc * kC * d * 4);
+    L.kg = take(BH * nc * kC * d * 4);
+    L.qg = take(BH * nc * kC * d * 4);
+    L.gC = take(BH * nc * d * 4);
+    L.M = take(BH * nc * kC * kC * 4);
+    L.P = take(BH * nc * kC * kC * 4);
+    L.pred = take(tok * 4);
+    L.dU = take(tok * 4);
+    L.lamC = take(BH * nc * d * d * 4);
+    L.X3 = take(tok * 4);
+    L.drp = take(BH * nc * d * 4);
+    L.total = off;
+    return true;
+}
+
+template <typename QT, int D>
+hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *ws, const BwdLayout &L,
+                     hipStream_t stream) {
+    const int nchunks = (T + kC - 1) / kC;
+    const int BH = B * H;
+    float *u = reinterpret_cast<float *>(ws + L.u);
+    float *states = reinterpret_cast<float *>(ws + L.states);
+    float *kb = reinterpret_cast<float *>(ws + L.kb), *kg = reinterpret_cast<float *>(ws + L.kg);
+    float *qg = reinterpret_cast<float *>(ws + L.qg), *gC = reinterpret_cast<float *>(ws + L.gC);
+    float *Mw = reinterpret_cast<float *>(ws + L.M), *Pw = reinterpret_cast<float *>(ws + L.P);
+    float *pred = reinterpret_cast<float *>(ws + L.pred), *dUw = reinterpret_cast<float *>(ws + L.dU);
+    float *lamC = reinterpret_cast<float *>(ws + L.lamC), *X3 = reinterpret_cast<float *>(ws + L.X3);
+    float *drp = reinterpret_cast<float *>(ws + L.drp);
+    const bool bf16 = std::is_same_v<QT, bf16_t>;
+    hipError_t err;
+    if (T > 0) {
+        err = launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, kC, bf16, ws + L.fwd, stream);
+        if (err != hipSuccess) return err;
+    }
+    err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, ws + L.o, nullptr, u, states, B, T, H, D, kC, bf16,
+                                 ws + L.fwd, stream);
+    if (err != hipSuccess) return err;
+    const QT *q = static_cast<const QT *>(x.q), *k = static_cast<const QT *>(x.k);
+    const QT *v = static_cast<const QT *>(x.v), *dout = static_cast<const QT *>(x.dout);
+    if (nchunks > 0) {
+        auto kp = bwd_prepare_kernel<QT, D>;
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kp), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  int(PrepBwdLds<D>::BYTES));
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kp, dim3(nchunks, H, B), dim3(kBwdThreads), PrepBwdLds<D>::BYTES, stream, q, k,
+                           x.a, x.g, x.r, states, u, kb, kg, qg, gC, Mw, Pw, pred, T, H, nchunks);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    constexpr int NVT = D / kVT;
+    hipLaunchKernelGGL((bwd_scan_kernel<QT, D>), dim3((BH + 7) / 8 * 8 * NVT), dim3(kBwdThreads), 0, stream,
+                       dout, v, x.e, x.w, kb, kg, qg, gC, Mw, Pw, pred, x.dsT, dUw, lamC, x.dv, x.dw, x.de,
+                       x.ds0, T, H, BH, nchunks);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (nchunks > 0) {
+        auto kgk = bwd_grads_kernel<QT, D>;
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kgk), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  int(GradLds<D>::BYTES));
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kgk, dim3(nchunks, H, B), dim3(kBwdThreads), GradLds<D>::BYTES, stream, q, k, dout,
+                           x.a, x.g, x.e, x.r, u, dUw, states, lamC, X3, x.dq, x.dk, x.dg, x.dla, drp, T, H,
+                           nchunks);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((bwd_dr_kernel<D>), dim3(H), dim3(D), 0, stream, drp, x.dr, B, H, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d, bool bf16) {
+    if (B < 1 || H < 1 || T < 0 || (d != 64 && d != 128)) return 0;
+    BwdLayout L;
+    if (!bwd_layout(B, T, H, d, bf16, L)) return 0;
+    return L.total;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &x, int B, int T, int H, int d, bool bf16, void *workspace,
+                            hipStream_t stream) {
+    BwdLayout L;
+    if (!bwd_layout(B, T, H, d, bf16, L)) return hipErrorInvalidValue;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    if (d == 64) return bf16 ? bwd_typed<bf16_t, 64>(x, B, T, H, ws, L, stream) : bwd_typed<float, 64>(x, B, T, H, ws, L, stream);
+    if (d == 128) return bf16 ? bwd_typed<bf16_t, 128>(x, B, T, H, ws, L, stream) : bwd_typed<float, 128>(x, B, T, H, ws, L, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace muir

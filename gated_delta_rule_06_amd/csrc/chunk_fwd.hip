@@ -921,12 +921,19 @@ struct ScanGates {
     const float *ce, *cw;     // [H, D]
 };
 constexpr int kZOffErase = 64, kZOffWrite = 256;
-template <typename QT, typename OpT, int D, int C, bool GATED, int VC, bool LRS>
+// What the forward keeps for the backward pass (SAVE): u = b - e * p of every token in fp32,
+// [B, T, H, D] like v, and the state at every chunk start and at the end, fp32
+// [B * H][nchunks + 1][D][D].
+struct ScanSave {
+    float *u;
+    float *states;
+};
+template <typename QT, typename OpT, int D, int C, bool GATED, int VC, bool LRS, bool SAVE = false>
 __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     const QT *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ og, const float *__restrict__ s0, QT *__restrict__ o,
     float *__restrict__ s_out, const unsigned char *__restrict__ ws, ScanGates sg, int T, int H,
-    int BH, int nchunks) {
+    int BH, int nchunks, ScanSave sv = {}) {
     using SL = Slot<OpT, D, C>;
     using F = Frag<OpT>;
     using f4 = typename F::f4;
@@ -976,13 +983,18 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
 
+    // SAVE: the state at every chunk start and at the end, [BH][nchunks + 1][D][D].
+    float *svst = SAVE ? sv.states + size_t(bh) * (nchunks + 1) * D * D + j0 : nullptr;
     if (nchunks == 0) {
-        if (wave == 0 && south && col_ok) {
+        if (wave == 0 && col_ok) {
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    south[size_t(16 * c + i) * D + lo_st] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+                    if (south) south[size_t(16 * c + i) * D + lo_st] = x0;
+                    if constexpr (SAVE) svst[size_t(16 * c + i) * D + lo_st] = x0;
+                }
         }
         return;
     }
@@ -1197,6 +1209,16 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     const rsrc_t re = make_rsrc(e + tok0, tok_elems * 4u);
     const rsrc_t rwt = make_rsrc(w + tok0, tok_elems * 4u);
     const rsrc_t rv = make_rsrc(v + tok0, tok_elems * unsigned(sizeof(QT)));
+    const rsrc_t rus = make_rsrc(SAVE ? sv.u + tok0 : nullptr, SAVE ? tok_elems * 4u : 0u);
+    auto save_state = [&](int ci) {
+        if (col_ok) {
+            float *dst = svst + size_t(ci) * D * D;
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[size_t(16 * c + i) * D + lo_st] = S[c][i];
+        }
+    };
 
     auto load_leaf = [&](int ci, int L, LeafIn<QT, VC> &in) {
         const unsigned so = trow(ci * C + 16 * L, 4u);
@@ -1263,6 +1285,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                 fS[c] = F::pack(S[c]);
                 sh_fS[buf][c][lane] = fS[c];
             }
+            if constexpr (SAVE) save_state(ci);
             f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
@@ -1361,6 +1384,8 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                 // Step 15 would update no token (M is strictly lower triangular): left out.
                 static_for<7>([&](auto Sc) { step(std::integral_constant<int, 8 + decltype(Sc)::value>{}); });
 
+                if constexpr (SAVE)
+                    RowV<float, VC>::store(rus, lo_f, trow(ci * C + 16 * L, 4u), f32x4_t{x0, x1, x2, x3});
                 // ---- u -> U operand (transpose on the matrix cores), hand-over ----
                 Uprev = Ulast;
                 Ulast = F::pack(F::mma16_fresh(F::pack(f32x4_t{x0, x1, x2, x3}), unit));
@@ -1384,6 +1409,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) south[size_t(16 * c + i) * D + lo_st] = S[c][i];
     }
+    if constexpr (SAVE) save_state(nchunks);
 }
 
 template <typename OpT, int D, int C>
@@ -1534,6 +1560,42 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
 // e and w) keeps two workgroups per compute unit, as many as the registers allow. Larger
 // chunks would halve that; with 8-column tiles (one workgroup per compute unit) the gate
 // wavefront's z loads slowed the chain by more than the separate gate pass costs.
+template <typename QT, int D, int C>
+hipError_t scan_save_typed(const void *v, const float *e, const float *w, const float *s0,
+                           void *o, float *s_out, const ScanSave &sv, int B, int T, int H,
+                           const void *workspace, hipStream_t stream) {
+    const int nchunks = (T + C - 1) / C;
+    const int BH = B * H;
+    const int groups = (BH + 7) / 8;
+    auto run = [&](auto vc) {
+        constexpr int VC = decltype(vc)::value;
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, QT, D, C, false, VC, false, true>),
+                           dim3(groups * 8 * (D / (4 * VC))), dim3(128), 0, stream,
+                           static_cast<const QT *>(v), e, w, nullptr, s0, static_cast<QT *>(o),
+                           s_out, static_cast<const unsigned char *>(workspace), ScanGates{}, T,
+                           H, BH, nchunks, sv);
+        return hipGetLastError();
+    };
+    if (std::is_same_v<QT, bf16_t> && scan_narrow_tiles(B, H, D)) return run(std::integral_constant<int, 2>{});
+    return run(std::integral_constant<int, 4>{});
+}
+
+hipError_t launch_chunk_scan_save(const void *v, const float *e, const float *w, const float *s0,
+                                  void *o, float *s_out, float *u_out, float *states, int B,
+                                  int T, int H, int d, int chunk, bool bf16,
+                                  const void *workspace, hipStream_t stream) {
+    const ScanSave sv{u_out, states};
+#define MUIR_SCAN_SV(D, C)                                                                        \
+    if (d == D && chunk == C)                                                                     \
+        return bf16 ? scan_save_typed<bf16_t, D, C>(v, e, w, s0, o, s_out, sv, B, T, H, workspace, \
+                                                    stream)                                       \
+                    : scan_save_typed<float, D, C>(v, e, w, s0, o, s_out, sv, B, T, H, workspace,  \
+                                                   stream);
+    MUIR_SCAN_SV(64, 64) MUIR_SCAN_SV(128, 64)
+#undef MUIR_SCAN_SV
+    return hipErrorInvalidValue;
+}
+
 bool scan_gates_in_kernel(int B, int H, int d, int chunk) {
     return !scan_narrow_tiles(B, H, d) && chunk <= 128;
 }

@@ -34,6 +34,14 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                              int chunk, bool bf16, const void *workspace, hipStream_t stream);
 
+// Phase S as above (no output gate), also keeping what the backward pass needs: u_out
+// [B, T, H, d] fp32 (u = w * v - e * p of every token) and states [B * H][nchunks + 1][d][d]
+// fp32 (the state at every chunk start, then the final state). Chunks of 64 only.
+hipError_t launch_chunk_scan_save(const void *v, const float *e, const float *w, const float *s0,
+                                  void *o, float *s_out, float *u_out, float *states, int B,
+                                  int T, int H, int d, int chunk, bool bf16,
+                                  const void *workspace, hipStream_t stream);
+
 // Phase S with e and w formed inside the kernel from the low-rank gate projection (z,
 // U_e, U_w, c_e, c_w as for launch_lowrank_gates; bf16 operands), bit-identical to
 // launch_lowrank_gates followed by launch_chunk_scan. Only where scan_gates_in_kernel
@@ -64,5 +72,19 @@ hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, c
                                 const void *Ug, const float *ca, const float *ce, const float *cw,
                                 const float *cg, float *a, float *e, float *w, float *g, int B,
                                 int T, int H, int d, hipStream_t stream);
+
+// Backward pass of the chunk forward (chunks of 64). Inputs as for the forward, plus dout
+// (dtype of q) and dsT [B, H, d, d] fp32 (NULL: zero); outputs fp32, [B, T, H, d] except
+// dr [H, d] and ds0 [B, H, d, d] (NULL: not written). dla is a * dL/da.
+struct ChunkBwdArgs {
+    const void *q, *k, *v;
+    const float *a, *g, *e, *w, *r, *s0;
+    const void *dout;
+    const float *dsT;
+    float *dq, *dk, *dv, *dla, *dg, *de, *dw, *dr, *ds0;
+};
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d, bool bf16);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &args, int B, int T, int H, int d, bool bf16,
+                            void *workspace, hipStream_t stream);
 
 }  // namespace muir

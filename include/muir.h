@@ -305,6 +305,42 @@ muir_status_t muir_decode_step(
     float *state, void *o,
     int B, int H, int dk, int dv, muir_dtype_t qkv, muir_stream_t stream);
 
+/*
+ * Backward pass of muir_chunk_fwd: every input's gradient of a scalar loss L, given
+ * dL/do and dL/ds_out. Training runs the chunk form in both directions (Muir abstract,
+ * "Full text": chunkwise-parallel training; openai-hub page, section on the chunkwise
+ * algorithm). The gradients are the reverse mode of the same recurrence: per chunk, the
+ * transposed triangular system per value column, the state adjoint carried from the chunk
+ * end to its start, and decayed key/query products for the rest; no decay is divided by.
+ *
+ *   q, k, v, a, g, e, w, r, s0   as for muir_chunk_fwd (s0 may be NULL: zero state)
+ *   dout     [B, T, H, dv] dtype `qkv`: dL/do
+ *   ds_out   [B, H, dk, dv] float32: dL/ds_out, or NULL for zero
+ *   dq, dk, dv, dg, de, dw   [B, T, H, d] float32: dL/dq, dL/dk, ...
+ *   dla      [B, T, H, dk] float32: a * dL/da, the gradient with respect to log a (finite
+ *            where a = 0; callers holding a as a function of its logarithm use it as is)
+ *   dr       [H, dk] float32: dL/dr, summed over batch and tokens
+ *   ds0      [B, H, dk, dv] float32: dL/ds0, or NULL to skip
+ *   chunk    64 (the only chunk size of the backward)
+ *   workspace / workspace_bytes: at least muir_chunk_bwd_workspace_size(...) bytes, 256-byte
+ *            aligned. The call reruns the forward into it (its prepare and scan, keeping u
+ *            and every chunk start state), so no forward result needs to be passed in.
+ *
+ * Every output is written. Errors: as for muir_chunk_fwd; MUIR_ERR_UNSUPPORTED for chunk
+ * != 64; MUIR_ERR_NULL for a missing required pointer; MUIR_ERR_ALIAS when an output
+ * overlaps an input, another output or the workspace.
+ */
+size_t muir_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int chunk,
+                                     muir_dtype_t qkv);
+muir_status_t muir_chunk_bwd(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *r,
+    const float *s0, const void *dout, const float *ds_out,
+    float *dq, float *dk, float *dv, float *dla, float *dg, float *de, float *dw,
+    float *dr, float *ds0,
+    int B, int T, int H, int dk_, int dv_, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
 /* Static, never-NULL name of a status code ("MUIR_OK", ...). */
 const char *muir_status_string(muir_status_t s);
 
