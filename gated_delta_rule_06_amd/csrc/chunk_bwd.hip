@@ -64,10 +64,27 @@ __device__ __forceinline__ f32x4_t mm16(FA fa, FB fb, f32x4_t acc) {
 
 template <typename QT> __device__ __forceinline__ float ld(const QT *p, size_t i) { return to_f32(p[i]); }
 
+// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as floats.
+__device__ __forceinline__ f32x4_t ld4(const float *p, size_t i) {
+    return *reinterpret_cast<const f32x4_t *>(p + i);
+}
+__device__ __forceinline__ f32x4_t ld4(const bf16_t *p, size_t i) {
+    const u16x4_t u = *reinterpret_cast<const u16x4_t *>(p + i);
+    return f32x4_t{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])};
+}
+
 // ------------------------------------------------------------------------------------------
-// Prepare. LDS: M and P [C][C + 1]; then a union of the pivot pass arrays (per 64-channel
-// pass: a, k, q_hat, in-block prefix F and suffix R [C][65], cross-block products [6][64])
-// and K*gamma [C][D + 4] for the prediction.
+// Prepare. LDS: M and P [C][C + 1], K*gamma [C][D + 4] for the prediction, and the pivot
+// pass arrays (per 64-channel pass: a, k, q_hat, prefix F and suffix R [C][65] inside each
+// 16-token block, then inside each 4-token sub-block, and the products of whole blocks,
+// then of whole sub-blocks [16][64]).
+//
+// Pivots. For s < t in different 16-token blocks, Gamma_ts = F_t * (whole blocks between) *
+// R_s, so each cross-block 16x16 tile of M or P is one matrix-core product over channels with
+// the middle factor folded into the s side. Inside a 16-token block the same split at 4-token
+// sub-blocks gives Gamma_ts = F4_t * (whole sub-blocks between) * R4_s; the middle factor
+// depends only on s's sub-block and the gap (1, 2 or 3 sub-blocks), so each gap is one masked
+// product. Pairs inside one sub-block (at most 3 factors) are direct products.
 // ------------------------------------------------------------------------------------------
 template <int D> struct PrepBwdLds {
     static constexpr int LDM = kC + 1;
@@ -75,9 +92,9 @@ template <int D> struct PrepBwdLds {
     static constexpr int LDH = DH + 1;
     static constexpr int NPAIR = kNB * (kNB - 1) / 2;
     static constexpr int MP = 2 * kC * LDM;
-    static constexpr int PASS = 5 * kC * LDH + NPAIR * DH;
+    static constexpr int PASS = 5 * kC * LDH + 16 * DH;
     static constexpr int KGL = kC * (D + 4);
-    static constexpr int FLOATS = MP + (PASS > KGL ? PASS : KGL);
+    static constexpr int FLOATS = MP + KGL + PASS;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -92,10 +109,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     constexpr int C = kC, LDM = L::LDM, DH = L::DH, LDH = L::LDH;
     extern __shared__ float lds[];
     float *sM = lds, *sP = lds + kC * LDM;
-    float *pass = lds + L::MP;
+    float *sKG = lds + L::MP;
+    float *pass = sKG + L::KGL;
     float *sA = pass, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH,
           *sR = sF + C * LDH, *sMid = sR + C * LDH;
-    float *sKG = pass;
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
@@ -112,34 +129,51 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     // Cross-block tiles of M and P: pair p = (bt, bs), bs < bt, pair index bt (bt - 1) / 2 + bs;
     // tile job j < 12: matrix j / 6 (0: M, 1: P), pair j % 6. Wave w owns jobs w, w + 4, w + 8.
     f32x4_t acc[3] = {zero4(), zero4(), zero4()};
-    // Diagonal-block entries (t, s), s <= t in one block, by pair index: thread tid owns
-    // entries tid, tid + 256, tid + 512 (of 4 * 136).
-    constexpr int NDIAG = kNB * 136;
-    float dM[3] = {0.f, 0.f, 0.f}, dP[3] = {0.f, 0.f, 0.f};
-    int dt[3], ds[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int pi = tid + kBwdThreads * j;
-        int bb = 0, tl = 0, sl = 0;
-        if (pi < NDIAG) {
-            bb = pi / 136;
-            int rem = pi % 136;
-            while (rem > tl) { ++tl; rem -= tl; }
-            sl = rem;
-        }
-        dt[j] = 16 * bb + tl;
-        ds[j] = 16 * bb + sl;
+    // Diagonal 16x16 tiles, cross-sub-block entries: wave w owns tile jobs w and w + 4 (job:
+    // matrix j / 4, block j % 4), accumulated over the passes.
+    f32x4_t dacc[2] = {zero4(), zero4()};
+    // Entries (t, s), s <= t, inside one 4-token sub-block: 16 sub-blocks x 10; thread tid < 160
+    // owns one.
+    constexpr int NSUB = (kC / 4) * 10;
+    int st_ = 0, ss_ = 0;
+    if (tid < NSUB) {
+        const int sb = tid / 10;
+        int rem = tid % 10, tl = 0;
+        while (rem > tl) { ++tl; rem -= tl; }
+        st_ = 4 * sb + tl;
+        ss_ = 4 * sb + rem;
     }
+    float sM_ = 0.f, sP_ = 0.f;
 
     for (int p0 = 0; p0 < D; p0 += DH) {
         __syncthreads();
-        for (int idx = tid; idx < C * DH; idx += kBwdThreads) {
-            const int t = idx / DH, ii = idx % DH;
-            const bool valid = t < nval;
-            const size_t o = tok0 + size_t(t) * HD + p0 + ii;
-            sA[t * LDH + ii] = valid ? a[o] : 1.f;
-            sK[t * LDH + ii] = valid ? ld(k, o) : 0.f;
-            sQ[t * LDH + ii] = valid ? rh[p0 + ii] * g[o] * ld(q, o) : 0.f;
+        {
+            // All of the pass's loads are issued before the first LDS store.
+            constexpr int N4 = C * DH / 4 / kBwdThreads;
+            f32x4_t va[N4], vk[N4], vq[N4];
+#pragma unroll
+            for (int j = 0; j < N4; ++j) {
+                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
+                const size_t o = tok0 + size_t(t) * HD + p0 + ii;
+                if (t < nval) {
+                    va[j] = ld4(a, o);
+                    vk[j] = ld4(k, o);
+                    vq[j] = ld4(g, o) * ld4(q, o) * ld4(rh, p0 + ii);
+                } else {
+                    va[j] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+                    vk[j] = vq[j] = zero4();
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < N4; ++j) {
+                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    sA[t * LDH + ii + q4] = va[j][q4];
+                    sK[t * LDH + ii + q4] = vk[j][q4];
+                    sQ[t * LDH + ii + q4] = vq[j][q4];
+                }
+            }
         }
         __syncthreads();
         if (tid < DH) {
@@ -170,6 +204,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
                     mid *= bp[bs];
                 }
             }
+            // K*gamma, Q_hat*gamma (gamma through t), K*beta (beta after t), gamma_C.
+            const int i = p0 + ii;
+            float gm = 1.f;
+            for (int t = 0; t < C; ++t) {
+                gm *= sA[t * LDH + ii];
+                const float kt = sK[t * LDH + ii];
+                kg[(slot * C + t) * D + i] = kt * gm;
+                qg[(slot * C + t) * D + i] = sQ[t * LDH + ii] * gm;
+                sKG[t * (D + 4) + i] = kt * gm;
+            }
+            gC[slot * D + i] = gm;
+            float bt = 1.f;
+            for (int t = C - 1; t >= 0; --t) {
+                kb[(slot * C + t) * D + i] = sK[t * LDH + ii] * bt;
+                bt *= sA[t * LDH + ii];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -186,20 +236,77 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
                 },
                 acc[j]);
         }
+        __syncthreads();
+        // Sub-block pivots (replacing the block ones): F4, R4 and whole-sub-block products B4.
+        float *sB4 = sMid;
+        if (tid < DH) {
+            const int ii = tid;
+            for (int u = 0; u < C / 4; ++u) {
+                float run = 1.f;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            if (tid + kBwdThreads * j >= NDIAG) continue;
-            const int t = dt[j], s = ds[j];
+                for (int tl = 0; tl < 4; ++tl) {
+                    run *= sA[(4 * u + tl) * LDH + ii];
+                    sF[(4 * u + tl) * LDH + ii] = run;
+                }
+                run = 1.f;
+#pragma unroll
+                for (int tl = 3; tl >= 0; --tl) {
+                    sR[(4 * u + tl) * LDH + ii] = run;
+                    run *= sA[(4 * u + tl) * LDH + ii];
+                }
+                sB4[u * DH + ii] = run;
+            }
+        }
+        __syncthreads();
+        // Cross-sub-block entries of the diagonal tiles: for gap g (ut = us + g), the s side
+        // carries K * R4 times the products of the g - 1 whole sub-blocks after s's.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int job = wave + 4 * j;
+            const int mat = job / 4, bb = job % 4;
+            const float *sX = mat == 0 ? sK : sQ;
+            const int rr = lane & 15, kq = lane >> 4;
+            const int us = rr >> 2;  // the B row (column s = 16 bb + rr) sub-block in the block
+            f32x4_t y[3] = {zero4(), zero4(), zero4()};
+#pragma unroll 4
+            for (int m = 0; m < DH / 4; ++m) {
+                const int kk = 4 * m + kq;
+                const int ta = 16 * bb + rr;
+                const float av = sX[ta * LDH + kk] * sF[ta * LDH + kk];
+                const float b1 = sK[ta * LDH + kk] * sR[ta * LDH + kk];
+                const int u0 = 4 * bb + us;  // s's sub-block in the chunk
+                const float m1 = us + 1 < 4 ? sB4[(u0 + 1) * DH + kk] : 0.f;
+                const float m2 = us + 2 < 4 ? sB4[(u0 + 2) * DH + kk] : 0.f;
+                const float b2 = b1 * m1, b3 = b2 * m2;
+                y[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, y[0], 0, 0, 0);
+                y[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b2, y[1], 0, 0, 0);
+                y[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b3, y[2], 0, 0, 0);
+            }
+            // Output lane l: rows 4 (l / 16) + i (sub-block l / 16), column l % 16.
+            const int ut = lane >> 4, usc = (lane & 15) >> 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int gap = ut - usc;
+                dacc[j][i] += gap == 1 ? y[0][i] : (gap == 2 ? y[1][i] : (gap == 3 ? y[2][i] : 0.f));
+            }
+        }
+        // Entries inside one sub-block: decay over s < tau <= t, at most 3 factors.
+        if (tid < NSUB) {
+            const int t = st_, s4 = ss_;
             float m = 0.f, pp = 0.f;
             for (int ii = 0; ii < DH; ++ii) {
                 float gm = 1.f;
-                for (int tau = s + 1; tau <= t; ++tau) gm *= sA[tau * LDH + ii];
-                const float ks = gm * sK[s * LDH + ii];
+#pragma unroll
+                for (int uu = 1; uu < 4; ++uu) {
+                    const float av = sA[((s4 & ~3) + uu) * LDH + ii];
+                    gm *= ((s4 & 3) < uu && uu <= (t & 3)) ? av : 1.f;
+                }
+                const float ks = gm * sK[s4 * LDH + ii];
                 m = fmaf(sK[t * LDH + ii], ks, m);
                 pp = fmaf(sQ[t * LDH + ii], ks, pp);
             }
-            if (s < t) dM[j] += m;
-            dP[j] += pp;
+            if (s4 < t) sM_ += m;
+            sP_ += pp;
         }
     }
     __syncthreads();
@@ -215,34 +322,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
         for (int i = 0; i < 4; ++i) dst[(16 * bt + 4 * (lane >> 4) + i) * LDM + 16 * bs + (lane & 15)] = acc[j][i];
     }
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        if (tid + kBwdThreads * j >= NDIAG) continue;
-        sM[dt[j] * LDM + ds[j]] = dM[j];
-        sP[dt[j] * LDM + ds[j]] = dP[j];
+    for (int j = 0; j < 2; ++j) {
+        const int job = wave + 4 * j;
+        const int mat = job / 4, bb = job % 4;
+        float *dst = mat == 0 ? sM : sP;
+        const int ut = lane >> 4, usc = (lane & 15) >> 2;
+        if (ut > usc) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * bb + 4 * ut + i) * LDM + 16 * bb + (lane & 15)] = dacc[j][i];
+        }
     }
-    // Per-channel decay products: K*beta, K*gamma, Q_hat*gamma, gamma_C; K*gamma also to LDS.
-    if (tid < D) {
-        const int i = tid;
-        float gm = 1.f;
-        for (int t = 0; t < C; ++t) {
-            const bool valid = t < nval;
-            const size_t o = tok0 + size_t(t) * HD + i;
-            const float at = valid ? a[o] : 1.f;
-            const float kt = valid ? ld(k, o) : 0.f;
-            const float qh = valid ? rh[i] * g[o] * ld(q, o) : 0.f;
-            gm *= at;
-            kg[(slot * C + t) * D + i] = kt * gm;
-            qg[(slot * C + t) * D + i] = qh * gm;
-            sKG[t * (D + 4) + i] = kt * gm;
-        }
-        gC[slot * D + i] = gm;
-        float bt = 1.f;
-        for (int t = C - 1; t >= 0; --t) {
-            const bool valid = t < nval;
-            const size_t o = tok0 + size_t(t) * HD + i;
-            kb[(slot * C + t) * D + i] = (valid ? ld(k, o) : 0.f) * bt;
-            bt *= valid ? a[o] : 1.f;
-        }
+    if (tid < NSUB) {
+        if (ss_ < st_) sM[st_ * LDM + ss_] = sM_;
+        sP[st_ * LDM + ss_] = sP_;
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
@@ -254,12 +346,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
     const float *Ub = u + (size_t(b) * T + c0) * HD + size_t(h) * D;
     for (int jt = wave; jt < D / 16; jt += 4) {
+        // This lane's B operands of every contraction step, loaded together.
+        const int cc = lane & 15, kq = lane >> 4;
+        float bS[D / 4], bU[C / 4];
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) bS[m] = S0[size_t(4 * m + kq) * D + 16 * jt + cc];
+#pragma unroll
+        for (int m = 0; m < C / 4; ++m)
+            bU[m] = 4 * m + kq < nval ? Ub[size_t(4 * m + kq) * HD + 16 * jt + cc] : 0.f;
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
-            f32x4_t y = mm16<D>([&](int rr, int kk) { return sKG[(16 * tt + rr) * (D + 4) + kk]; },
-                                [&](int cc, int kk) { return S0[size_t(kk) * D + 16 * jt + cc]; }, zero4());
-            y = mm16<C>([&](int rr, int kk) { return sM[(16 * tt + rr) * LDM + kk]; },
-                        [&](int cc, int kk) { return kk < nval ? Ub[size_t(kk) * HD + 16 * jt + cc] : 0.f; }, y);
+            f32x4_t y = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 4; ++m)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sKG[(16 * tt + cc) * (D + 4) + 4 * m + kq], bS[m], y, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < C / 4; ++m)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * tt + cc) * LDM + 4 * m + kq], bU[m], y, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tt + 4 * (lane >> 4) + i;
@@ -270,8 +373,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// Reverse scan over chunks, per (b, h, 8 value columns).
+// Reverse scan over chunks, per (b, h, 8 value columns). Every operand of a chunk is staged
+// in LDS; the next chunk's operands are loaded into registers while this one is computed,
+// so the loop issues no dependent global loads.
+// LDS: M, P [C][C + 1]; K*beta, Q_hat*gamma, K*gamma [C][D + 1]; lambda [D][8]; gamma_C [D];
+// per-token tiles [C][8] of dO, e, w, v, p, the right-hand side and dP.
 // ------------------------------------------------------------------------------------------
+template <int D> struct ScanBwdLds {
+    static constexpr int LDM = kC + 1, LDK = D + 1;
+    static constexpr int FLOATS = 2 * kC * LDM + 3 * kC * LDK + D * kVT + D + 7 * kC * kVT;
+    static constexpr size_t BYTES = size_t(FLOATS) * 4;
+};
+
 template <typename QT, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     const QT *__restrict__ dout, const QT *__restrict__ v, const float *__restrict__ e,
@@ -281,9 +394,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     float *__restrict__ dU, float *__restrict__ lamC, float *__restrict__ dv,
     float *__restrict__ dw, float *__restrict__ de, float *__restrict__ ds0, int T, int H, int BH,
     int nchunks) {
-    constexpr int C = kC, VT = kVT, NVT = D / VT, LDM = C + 1;
-    __shared__ float sM[C * LDM], sP[C * LDM];
-    __shared__ float sLam[D][VT], sdO[C][VT], sE[C][VT], sdP[C][VT], sRhs[C][VT];
+    using L = ScanBwdLds<D>;
+    constexpr int C = kC, VT = kVT, NVT = D / VT, LDM = L::LDM, LDK = L::LDK;
+    constexpr int NM4 = C * C / 4 / kBwdThreads;  // float4 of M (and of P) per thread
+    constexpr int NK4 = C * D / 4 / kBwdThreads;  // float4 of each [C][D] operand per thread
+    constexpr int NT = C * VT / kBwdThreads;      // tile elements per thread
+    extern __shared__ float lds[];
+    float *sM = lds, *sP = sM + C * LDM;
+    float *sKB = sP + C * LDM, *sQG = sKB + C * LDK, *sKG = sQG + C * LDK;
+    float *sLam = sKG + C * LDK, *sGC = sLam + D * VT;
+    float *sdO = sGC + D, *sE = sdO + C * VT, *sW = sE + C * VT, *sV = sW + C * VT;
+    float *sPr = sV + C * VT, *sRhs = sPr + C * VT, *sdP = sRhs + C * VT;
 
     // The value tiles of one head get ids equal mod 8, so they share an XCD and its L2.
     const int id = blockIdx.x;
@@ -294,59 +415,121 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     const int j0 = VT * ct;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t HD = size_t(H) * D;
+    auto tok_base = [&](int c) { return (size_t(b) * T + size_t(c) * C) * HD + size_t(h) * D + j0; };
+
+    struct Pre {
+        f32x4_t m[NM4], p[NM4], kb[NK4], qg[NK4], kg[NK4];
+        float dO[NT], e[NT], w[NT], v[NT], pr[NT], gc;
+    };
+    auto load_pre = [&](int c, Pre &x) {
+        const size_t slot = size_t(bh) * nchunks + c;
+        const f32x4_t *M4 = reinterpret_cast<const f32x4_t *>(Mw + slot * C * C);
+        const f32x4_t *P4 = reinterpret_cast<const f32x4_t *>(Pw + slot * C * C);
+        const f32x4_t *KB4 = reinterpret_cast<const f32x4_t *>(kb + slot * C * D);
+        const f32x4_t *QG4 = reinterpret_cast<const f32x4_t *>(qg + slot * C * D);
+        const f32x4_t *KG4 = reinterpret_cast<const f32x4_t *>(kg + slot * C * D);
+#pragma unroll
+        for (int j = 0; j < NM4; ++j) {
+            x.m[j] = M4[tid + kBwdThreads * j];
+            x.p[j] = P4[tid + kBwdThreads * j];
+        }
+#pragma unroll
+        for (int j = 0; j < NK4; ++j) {
+            x.kb[j] = KB4[tid + kBwdThreads * j];
+            x.qg[j] = QG4[tid + kBwdThreads * j];
+            x.kg[j] = KG4[tid + kBwdThreads * j];
+        }
+        const int nval = min(C, T - c * C);
+        const size_t t0 = tok_base(c);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int idx = tid + kBwdThreads * j, t = idx / VT;
+            const bool valid = t < nval;
+            const size_t o = t0 + size_t(t) * HD + idx % VT;
+            x.dO[j] = valid ? ld(dout, o) : 0.f;
+            x.e[j] = valid ? e[o] : 0.f;
+            x.w[j] = valid ? w[o] : 0.f;
+            x.v[j] = valid ? ld(v, o) : 0.f;
+            x.pr[j] = valid ? pred[o] : 0.f;
+        }
+        x.gc = tid < D ? gC[slot * D + tid] : 0.f;
+    };
+    auto store_pre = [&](const Pre &x) {
+#pragma unroll
+        for (int j = 0; j < NM4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / C, s = e0 % C;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sM[t * LDM + s + q4] = x.m[j][q4];
+                sP[t * LDM + s + q4] = x.p[j][q4];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NK4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, i = e0 % D;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sKB[t * LDK + i + q4] = x.kb[j][q4];
+                sQG[t * LDK + i + q4] = x.qg[j][q4];
+                sKG[t * LDK + i + q4] = x.kg[j][q4];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int idx = tid + kBwdThreads * j;
+            sdO[idx] = x.dO[j];
+            sE[idx] = x.e[j];
+            sW[idx] = x.w[j];
+            sV[idx] = x.v[j];
+            sPr[idx] = x.pr[j];
+        }
+        if (tid < D) sGC[tid] = x.gc;
+    };
 
     for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
         const int i = idx / VT, j = idx % VT;
-        sLam[i][j] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
+        sLam[idx] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
     }
+    Pre pre;
+    if (nchunks > 0) load_pre(nchunks - 1, pre);
     for (int c = nchunks - 1; c >= 0; --c) {
-        const int c0 = c * C;
-        const int nval = min(C, T - c0);
-        const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D + j0;
+        const int nval = min(C, T - c * C);
+        const size_t tok0 = tok_base(c);
         const size_t slot = size_t(bh) * nchunks + c;
         __syncthreads();
+        store_pre(pre);
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
-            lamC[(slot * D + i) * D + j0 + j] = sLam[i][j];
-        }
-        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-            const int t = idx / C, s = idx % C;
-            sM[t * LDM + s] = Mw[slot * C * C + idx];
-            sP[t * LDM + s] = Pw[slot * C * C + idx];
-        }
-        for (int idx = tid; idx < C * VT; idx += kBwdThreads) {
-            const int t = idx / VT, j = idx % VT;
-            const bool valid = t < nval;
-            const size_t o = tok0 + size_t(t) * HD + j;
-            sdO[t][j] = valid ? ld(dout, o) : 0.f;
-            sE[t][j] = valid ? e[o] : 0.f;
+            lamC[(slot * D + i) * D + j0 + j] = sLam[idx];
         }
         __syncthreads();
+        if (c > 0) load_pre(c - 1, pre);
         // Right-hand side: (K*beta) lambda_C + P^T dO, thread (t, column pair).
         {
             const int t = tid >> 2, j = 2 * (tid & 3);
-            const float *kbr = kb + (slot * C + t) * D;
             float r0 = 0.f, r1 = 0.f;
+#pragma unroll 8
             for (int i = 0; i < D; ++i) {
-                const float x = kbr[i];
-                r0 = fmaf(x, sLam[i][j], r0);
-                r1 = fmaf(x, sLam[i][j + 1], r1);
+                const float x = sKB[t * LDK + i];
+                r0 = fmaf(x, sLam[i * VT + j], r0);
+                r1 = fmaf(x, sLam[i * VT + j + 1], r1);
             }
+#pragma unroll 4
             for (int tp = t; tp < C; ++tp) {
-                const float p = sP[tp * LDM + t];
-                r0 = fmaf(p, sdO[tp][j], r0);
-                r1 = fmaf(p, sdO[tp][j + 1], r1);
+                const float pv = sP[tp * LDM + t];
+                r0 = fmaf(pv, sdO[tp * VT + j], r0);
+                r1 = fmaf(pv, sdO[tp * VT + j + 1], r1);
             }
-            sRhs[t][j] = r0;
-            sRhs[t][j + 1] = r1;
+            sRhs[t * VT + j] = r0;
+            sRhs[t * VT + j + 1] = r1;
         }
         __syncthreads();
         // Back substitution, wave w: columns 2w, 2w + 1, lane t. With y = e * dU,
         // dU_t = rhs_t - sum_{s > t} M_st y_s; lanes t >= s read M_st = 0.
         {
             const int j = 2 * wave;
-            float x0 = sRhs[lane][j], x1 = sRhs[lane][j + 1];
-            const float e0 = sE[lane][j], e1 = sE[lane][j + 1];
+            float x0 = sRhs[lane * VT + j], x1 = sRhs[lane * VT + j + 1];
+            const float e0 = sE[lane * VT + j], e1 = sE[lane * VT + j + 1];
 #pragma unroll
             for (int s = C - 1; s >= 0; --s) {
                 const float m = sM[s * LDM + lane];
@@ -355,18 +538,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
                 x0 = fmaf(-m, y0, x0);
                 x1 = fmaf(-m, y1, x1);
             }
-            sdP[lane][j] = -e0 * x0;
-            sdP[lane][j + 1] = -e1 * x1;
+            sdP[lane * VT + j] = -e0 * x0;
+            sdP[lane * VT + j + 1] = -e1 * x1;
             if (lane < nval) {
                 const size_t o = tok0 + size_t(lane) * HD + j;
+                const int l = lane * VT + j;
                 dU[o] = x0;
                 dU[o + 1] = x1;
-                dv[o] = w[o] * x0;
-                dv[o + 1] = w[o + 1] * x1;
-                dw[o] = ld(v, o) * x0;
-                dw[o + 1] = ld(v, o + 1) * x1;
-                de[o] = -pred[o] * x0;
-                de[o + 1] = -pred[o + 1] * x1;
+                dv[o] = sW[l] * x0;
+                dv[o + 1] = sW[l + 1] * x1;
+                dw[o] = sV[l] * x0;
+                dw[o + 1] = sV[l + 1] * x1;
+                de[o] = -sPr[l] * x0;
+                de[o + 1] = -sPr[l + 1] * x1;
             }
         }
         __syncthreads();
@@ -376,23 +560,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
             constexpr int NJ = VT / TPI;
             const int i = tid % D, jb = (tid / D) * NJ;
             float acc[NJ];
-            const float gc = gC[slot * D + i];
+            const float gc = sGC[i];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[j] = gc * sLam[i][jb + j];
+            for (int j = 0; j < NJ; ++j) acc[j] = gc * sLam[i * VT + jb + j];
+#pragma unroll 4
             for (int t = 0; t < C; ++t) {
-                const float xq = qg[(slot * C + t) * D + i], xk = kg[(slot * C + t) * D + i];
+                const float xq = sQG[t * LDK + i], xk = sKG[t * LDK + i];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[j] = fmaf(xq, sdO[t][jb + j], fmaf(xk, sdP[t][jb + j], acc[j]));
+                for (int j = 0; j < NJ; ++j)
+                    acc[j] = fmaf(xq, sdO[t * VT + jb + j], fmaf(xk, sdP[t * VT + jb + j], acc[j]));
             }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) sLam[i][jb + j] = acc[j];
+            for (int j = 0; j < NJ; ++j) sLam[i * VT + jb + j] = acc[j];
         }
     }
     __syncthreads();
     if (ds0) {
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
-            ds0[(size_t(bh) * D + i) * D + j0 + j] = sLam[i][j];
+            ds0[(size_t(bh) * D + i) * D + j0 + j] = sLam[idx];
         }
     }
 }
@@ -405,7 +591,7 @@ template <int D> struct GradLds {
     static constexpr int LDM = kC + 1, LDX = D + 4, LDT = kC + 1;
     static constexpr int OUPU = 2 * kC * LDM;
     static constexpr int P1 = 3 * kC * LDX, P2 = 3 * D * LDT;
-    static constexpr int FLOATS = OUPU + (P1 > P2 ? P1 : P2);
+    static constexpr int FLOATS = OUPU + D + (P1 > P2 ? P1 : P2);
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -421,7 +607,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     constexpr int C = kC, LDM = L::LDM, LDX = L::LDX, LDT = L::LDT;
     extern __shared__ float lds[];
     float *sOU = lds, *sPU = lds + C * LDM;
-    float *un = lds + L::OUPU;
+    float *sRS = lds + L::OUPU;  // rowsum(S_C * lambda_C) per channel
+    float *un = sRS + D;
     float *sU = un, *sdO = un + C * LDX, *sdP = un + 2 * C * LDX;
     float *sKT = un, *sAT = un + D * LDT, *sQT = un + 2 * D * LDT;
 
@@ -437,13 +624,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     const float *SC = S0 + size_t(D) * D;
     const float *lam = lamC + slot * D * D;
 
-    for (int idx = tid; idx < C * D; idx += kBwdThreads) {
-        const int t = idx / D, j = idx % D;
-        const bool valid = t < nval;
-        const size_t o = tok0 + size_t(t) * HD + j;
-        sU[t * LDX + j] = valid ? U[o] : 0.f;
-        sdO[t * LDX + j] = valid ? ld(dout, o) : 0.f;
-        sdP[t * LDX + j] = valid ? -e[o] * dU[o] : 0.f;
+    {
+        constexpr int N4 = C * D / 4 / kBwdThreads;
+        f32x4_t vu[N4], vo[N4], vp[N4];
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, jj = e0 % D;
+            const size_t o = tok0 + size_t(t) * HD + jj;
+            if (t < nval) {
+                vu[j] = ld4(U, o);
+                vo[j] = ld4(dout, o);
+                vp[j] = -ld4(e, o) * ld4(dU, o);
+            } else {
+                vu[j] = vo[j] = vp[j] = zero4();
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, jj = e0 % D;
+            *reinterpret_cast<f32x4_t *>(&sU[t * LDX + jj]) = vu[j];
+            *reinterpret_cast<f32x4_t *>(&sdO[t * LDX + jj]) = vo[j];
+            *reinterpret_cast<f32x4_t *>(&sdP[t * LDX + jj]) = vp[j];
+        }
+    }
+    // rowsum(S_C * lambda_C), one wave per row.
+    for (int i = wave; i < D; i += 4) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = lane; j < D; j += 64) acc = fmaf(SC[size_t(i) * D + j], lam[size_t(i) * D + j], acc);
+        acc = wave_sum(acc);
+        if (lane == 0) sRS[i] = acc;
     }
     __syncthreads();
     // O U^T (s <= t) and dP U^T (s < t), lower 16x16 tiles; job j < 20: matrix j / 10, tile
@@ -464,18 +674,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     }
     // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D].
     for (int it = wave; it < D / 16; it += 4) {
+        // This lane's B operands (row 16 it + lane % 16 of S0, then of lambda_C), each loaded
+        // in one batch.
+        const int rr = lane & 15, kq = lane >> 4;
+        float bv[D / 4];
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) bv[m] = S0[size_t(16 * it + rr) * D + 4 * m + kq];
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
-            f32x4_t y1 = zero4(), y2 = zero4(), y3 = zero4();
-            const int rr = lane & 15, kq = lane >> 4;
-#pragma unroll 4
+            f32x4_t y1 = zero4(), y2 = zero4();
+#pragma unroll
             for (int m = 0; m < D / 4; ++m) {
                 const int kk = 4 * m + kq;
-                const float sb = S0[size_t(16 * it + rr) * D + kk];
-                const float lb = lam[size_t(16 * it + rr) * D + kk];
-                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], sb, y1, 0, 0, 0);
-                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], sb, y2, 0, 0, 0);
-                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + kk], lb, y3, 0, 0, 0);
+                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], bv[m], y1, 0, 0, 0);
+                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], bv[m], y2, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -484,30 +696,75 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
                     const size_t o = tok0 + size_t(t) * HD + 16 * it + (lane & 15);
                     dq[o] = y1[i];
                     dk[o] = y2[i];
-                    X3[o] = y3[i];
                 }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) bv[m] = lam[size_t(16 * it + rr) * D + 4 * m + kq];
+#pragma unroll
+        for (int tt = 0; tt < kNB; ++tt) {
+            f32x4_t y3 = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 4; ++m)
+                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + 4 * m + kq], bv[m], y3, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tt + 4 * (lane >> 4) + i;
+                if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + (lane & 15)] = y3[i];
             }
         }
     }
     __syncthreads();
     const float *rh = r + size_t(h) * D;
-    for (int idx = tid; idx < C * D; idx += kBwdThreads) {
-        const int t = idx / D, i = idx % D;
-        const bool valid = t < nval;
-        const size_t o = tok0 + size_t(t) * HD + i;
-        sKT[i * LDT + t] = valid ? ld(k, o) : 0.f;
-        sAT[i * LDT + t] = valid ? a[o] : 1.f;
-        sQT[i * LDT + t] = valid ? rh[i] * g[o] * ld(q, o) : 0.f;
+    {
+        constexpr int N4 = C * D / 4 / kBwdThreads;
+        f32x4_t vk[N4], va[N4], vq[N4];
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, ii = e0 % D;
+            const size_t o = tok0 + size_t(t) * HD + ii;
+            if (t < nval) {
+                vk[j] = ld4(k, o);
+                va[j] = ld4(a, o);
+                vq[j] = ld4(g, o) * ld4(q, o) * ld4(rh, ii);
+            } else {
+                vk[j] = vq[j] = zero4();
+                va[j] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, ii = e0 % D;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sKT[(ii + q4) * LDT + t] = vk[j][q4];
+                sAT[(ii + q4) * LDT + t] = va[j][q4];
+                sQT[(ii + q4) * LDT + t] = vq[j][q4];
+            }
+        }
     }
     __syncthreads();
     const int i = tid % D, role = tid / D;
     const float *kT = sKT + i * LDT, *aT = sAT + i * LDT, *qT = sQT + i * LDT;
     if (role == 0) {
-        // dq_hat and the read part of dk, tokens in order (gamma as a running product).
+        // dq_hat and the read part of dk, tokens in order (gamma as a running product). The
+        // token's global operands are loaded one token ahead.
         float gm = 1.f, dr_acc = 0.f;
+        auto fetch = [&](int t, float (&f)[4]) {
+            if (t < nval) {
+                const size_t o = tok0 + size_t(t) * HD + i;
+                f[0] = dq[o]; f[1] = dk[o]; f[2] = g[o]; f[3] = ld(q, o);
+            } else {
+                f[0] = f[1] = f[2] = f[3] = 0.f;
+            }
+        };
+        float cur[4], nxt[4];
+        fetch(0, cur);
         for (int t = 0; t < C; ++t) {
+            fetch(t + 1, nxt);
             gm *= aT[t];
             float sq = 0.f, sr = 0.f, run = 1.f;
+#pragma unroll 4
             for (int s = t; s >= 0; --s) {
                 const float ks = run * kT[s];
                 sq = fmaf(sOU[t * LDM + s], ks, sq);
@@ -516,45 +773,58 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             }
             if (t < nval) {
                 const size_t o = tok0 + size_t(t) * HD + i;
-                const float dqh = fmaf(gm, dq[o], sq);
-                const float dkr = fmaf(gm, dk[o], sr);
-                const float gt = g[o], qt = ld(q, o);
+                const float dqh = fmaf(gm, cur[0], sq);
+                const float dkr = fmaf(gm, cur[1], sr);
+                const float gt = cur[2], qt = cur[3];
                 dq[o] = rh[i] * gt * dqh;
                 dg[o] = rh[i] * qt * dqh;
                 dr_acc = fmaf(gt * qt, dqh, dr_acc);
                 dk[o] = dkr;
                 dla[o] = fmaf(qT[t], dqh, kT[t] * dkr);
             }
+#pragma unroll
+            for (int f = 0; f < 4; ++f) cur[f] = nxt[f];
         }
         drp[slot * D + i] = dr_acc;
     } else if (role == 1) {
         // Write part of dk, tokens in reverse (beta as a running product).
         float bt = 1.f;
+        auto fetch = [&](int s) { return s >= 0 && s < nval ? X3[tok0 + size_t(s) * HD + i] : 0.f; };
+        float cur = fetch(C - 1);
         for (int s = C - 1; s >= 0; --s) {
+            const float nxt = fetch(s - 1);
             float sw = 0.f, run = 1.f;
+#pragma unroll 4
             for (int t = s; t < C; ++t) {
                 sw = fmaf(sOU[t * LDM + s], run * qT[t], sw);
                 sw = fmaf(sPU[t * LDM + s], run * kT[t], sw);
-                if (t + 1 < C) run *= aT[t + 1];
+                run *= aT[t + 1 < C ? t + 1 : t];
             }
-            if (s < nval) {
-                const size_t o = tok0 + size_t(s) * HD + i;
-                X3[o] = fmaf(bt, X3[o], sw);
-            }
+            if (s < nval) X3[tok0 + size_t(s) * HD + i] = fmaf(bt, cur, sw);
             bt *= aT[s];
+            cur = nxt;
         }
     }
     __syncthreads();
     if (role == 0) {
-        float rs = 0.f;
-        for (int j = 0; j < D; ++j) rs = fmaf(SC[size_t(i) * D + j], lam[size_t(i) * D + j], rs);
+        const float rs = sRS[i];
         float cum = 0.f;
+        auto fetch = [&](int t, float (&f)[3]) {
+            if (t >= 0) {
+                const size_t o = tok0 + size_t(t) * HD + i;
+                f[0] = X3[o]; f[1] = dla[o]; f[2] = dk[o];
+            }
+        };
+        float cur[3] = {0.f, 0.f, 0.f}, nxt[3] = {0.f, 0.f, 0.f};
+        fetch(nval - 1, cur);
         for (int t = nval - 1; t >= 0; --t) {
+            fetch(t - 1, nxt);
             const size_t o = tok0 + size_t(t) * HD + i;
-            const float kw = X3[o];
-            cum += dla[o] - kT[t] * kw;
+            cum += cur[1] - kT[t] * cur[0];
             dla[o] = cum + rs;
-            dk[o] += kw;
+            dk[o] = cur[2] + cur[0];
+#pragma unroll
+            for (int f = 0; f < 3; ++f) cur[f] = nxt[f];
         }
     }
 }
@@ -641,7 +911,11 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
         if (err != hipSuccess) return err;
     }
     constexpr int NVT = D / kVT;
-    hipLaunchKernelGGL((bwd_scan_kernel<QT, D>), dim3((BH + 7) / 8 * 8 * NVT), dim3(kBwdThreads), 0, stream,
+    auto ks = bwd_scan_kernel<QT, D>;
+    err = hipFuncSetAttribute(reinterpret_cast<const void *>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              int(ScanBwdLds<D>::BYTES));
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(ks, dim3((BH + 7) / 8 * 8 * NVT), dim3(kBwdThreads), ScanBwdLds<D>::BYTES, stream,
                        dout, v, x.e, x.w, kb, kg, qg, gC, Mw, Pw, pred, x.dsT, dUw, lamC, x.dv, x.dw, x.de,
                        x.ds0, T, H, BH, nchunks);
     err = hipGetLastError();
