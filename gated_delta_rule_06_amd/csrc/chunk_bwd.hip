@@ -28,7 +28,7 @@
 // the chunk start states):
 //   bwd_prepare_kernel  one workgroup per (b, h, chunk): K*beta, K*gamma, Q_hat*gamma, gamma_C,
 //                       M and P (fp32 matrix cores for the cross-block tiles), and p.
-//   bwd_scan_kernel     one workgroup per (b, h, 8 value columns), chunks in reverse: the
+//   bwd_scan_kernel     one workgroup per (b, h, 16 value columns), chunks in reverse: the
 //                       transposed triangular solve, the adjoint carry, dv, dw, de.
 //   bwd_grads_kernel    one workgroup per (b, h, chunk): dq, dk, dg and a * dL/da.
 //   bwd_dr_kernel       dr summed over batch and chunks.
@@ -46,7 +46,6 @@ namespace {
 
 constexpr int kC = 64;        // tokens per chunk
 constexpr int kNB = kC / 16;  // 16-token blocks per chunk
-constexpr int kVT = 8;        // value columns per scan workgroup
 constexpr int kBwdThreads = 256;
 
 // D[16x16] += A[16xK] B[Kx16] on the fp32 matrix cores: fa(r, k) = A[r][k], fb(c, k) = B[k][c].
@@ -373,15 +372,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// Reverse scan over chunks, per (b, h, 8 value columns). Every operand of a chunk is staged
-// in LDS; the next chunk's operands are loaded into registers while this one is computed,
-// so the loop issues no dependent global loads.
-// LDS: M, P [C][C + 1]; K*beta, Q_hat*gamma, K*gamma [C][D + 1]; lambda [D][8]; gamma_C [D];
-// per-token tiles [C][8] of dO, e, w, v, p, the right-hand side and dP.
+// Reverse scan over chunks, per (b, h, 16 value columns); four wavefronts.
+//   right-hand side  (K*beta) lambda_C + P^T dO: fp32 matrix cores, wave w owns tokens
+//                    16w .. 16w + 15; its A operands come straight from memory into registers,
+//                    loaded while the previous chunk is finished.
+//   solve            back substitution, wave w owns columns 4w .. 4w + 3, lane = token.
+//   adjoint carry    lambda <- Diag(gamma_C) lambda + (Q_hat*gamma)^T dO + (K*gamma)^T dP:
+//                    matrix cores, wave w owns channel tiles w, w + 4, ...
+// LDS: lambda [D][16], dO and dP [C][16], M [C][C + 1], per-token tiles [C][17] of e, w, v, p
+// and the right-hand side, gamma_C [D].
 // ------------------------------------------------------------------------------------------
+constexpr int kVTS = 16;  // value columns per scan workgroup
 template <int D> struct ScanBwdLds {
-    static constexpr int LDM = kC + 1, LDK = D + 1;
-    static constexpr int FLOATS = 2 * kC * LDM + 3 * kC * LDK + D * kVT + D + 7 * kC * kVT;
+    static constexpr int LDM = kC + 1, LDT = kVTS + 1;
+    static constexpr int FLOATS = D * kVTS + 2 * kC * kVTS + kC * LDM + 5 * kC * LDT + D;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -395,16 +399,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     float *__restrict__ dw, float *__restrict__ de, float *__restrict__ ds0, int T, int H, int BH,
     int nchunks) {
     using L = ScanBwdLds<D>;
-    constexpr int C = kC, VT = kVT, NVT = D / VT, LDM = L::LDM, LDK = L::LDK;
-    constexpr int NM4 = C * C / 4 / kBwdThreads;  // float4 of M (and of P) per thread
-    constexpr int NK4 = C * D / 4 / kBwdThreads;  // float4 of each [C][D] operand per thread
-    constexpr int NT = C * VT / kBwdThreads;      // tile elements per thread
+    constexpr int C = kC, VT = kVTS, NVT = D / VT, LDM = L::LDM, LDT = L::LDT;
+    constexpr int NIT = D / 64;  // channel tiles per wave in the adjoint carry
     extern __shared__ float lds[];
-    float *sM = lds, *sP = sM + C * LDM;
-    float *sKB = sP + C * LDM, *sQG = sKB + C * LDK, *sKG = sQG + C * LDK;
-    float *sLam = sKG + C * LDK, *sGC = sLam + D * VT;
-    float *sdO = sGC + D, *sE = sdO + C * VT, *sW = sE + C * VT, *sV = sW + C * VT;
-    float *sPr = sV + C * VT, *sRhs = sPr + C * VT, *sdP = sRhs + C * VT;
+    float *sLam = lds, *sdO = sLam + D * VT, *sdP = sdO + C * VT, *sM = sdP + C * VT;
+    float *sE = sM + C * LDM, *sW = sE + C * LDT, *sV = sW + C * LDT, *sPr = sV + C * LDT;
+    float *sRhs = sPr + C * LDT, *sGC = sRhs + C * LDT;
 
     // The value tiles of one head get ids equal mod 8, so they share an XCD and its L2.
     const int id = blockIdx.x;
@@ -414,165 +414,167 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     const int b = bh / H, h = bh % H;
     const int j0 = VT * ct;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
     const size_t HD = size_t(H) * D;
     auto tok_base = [&](int c) { return (size_t(b) * T + size_t(c) * C) * HD + size_t(h) * D + j0; };
+    auto slot_of = [&](int c) { return size_t(bh) * nchunks + c; };
 
-    struct Pre {
-        f32x4_t m[NM4], p[NM4], kb[NK4], qg[NK4], kg[NK4];
-        float dO[NT], e[NT], w[NT], v[NT], pr[NT], gc;
+    // Matrix-core A operands (k = 4 m + kq): K*beta rows and P columns of this wave's tokens;
+    // Q_hat*gamma and K*gamma columns of this wave's channel tiles.
+    float aKB[D / 4], aP[C / 4], aQG[NIT][C / 4], aKG[NIT][C / 4];
+    auto load_rhsA = [&](int c) {
+        const size_t sl = slot_of(c);
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) aKB[m] = kb[(sl * C + 16 * wave + r) * D + 4 * m + kq];
+#pragma unroll
+        for (int m = 0; m < C / 4; ++m) aP[m] = Pw[(sl * C + 4 * m + kq) * C + 16 * wave + r];
     };
-    auto load_pre = [&](int c, Pre &x) {
-        const size_t slot = size_t(bh) * nchunks + c;
-        const f32x4_t *M4 = reinterpret_cast<const f32x4_t *>(Mw + slot * C * C);
-        const f32x4_t *P4 = reinterpret_cast<const f32x4_t *>(Pw + slot * C * C);
-        const f32x4_t *KB4 = reinterpret_cast<const f32x4_t *>(kb + slot * C * D);
-        const f32x4_t *QG4 = reinterpret_cast<const f32x4_t *>(qg + slot * C * D);
-        const f32x4_t *KG4 = reinterpret_cast<const f32x4_t *>(kg + slot * C * D);
+    auto load_lamA = [&](int c) {
+        const size_t sl = slot_of(c);
 #pragma unroll
-        for (int j = 0; j < NM4; ++j) {
-            x.m[j] = M4[tid + kBwdThreads * j];
-            x.p[j] = P4[tid + kBwdThreads * j];
-        }
+        for (int n = 0; n < NIT; ++n)
 #pragma unroll
-        for (int j = 0; j < NK4; ++j) {
-            x.kb[j] = KB4[tid + kBwdThreads * j];
-            x.qg[j] = QG4[tid + kBwdThreads * j];
-            x.kg[j] = KG4[tid + kBwdThreads * j];
-        }
-        const int nval = min(C, T - c * C);
-        const size_t t0 = tok_base(c);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int idx = tid + kBwdThreads * j, t = idx / VT;
-            const bool valid = t < nval;
-            const size_t o = t0 + size_t(t) * HD + idx % VT;
-            x.dO[j] = valid ? ld(dout, o) : 0.f;
-            x.e[j] = valid ? e[o] : 0.f;
-            x.w[j] = valid ? w[o] : 0.f;
-            x.v[j] = valid ? ld(v, o) : 0.f;
-            x.pr[j] = valid ? pred[o] : 0.f;
-        }
-        x.gc = tid < D ? gC[slot * D + tid] : 0.f;
+            for (int m = 0; m < C / 4; ++m) {
+                const size_t o = (sl * C + 4 * m + kq) * D + 16 * (wave + 4 * n) + r;
+                aQG[n][m] = qg[o];
+                aKG[n][m] = kg[o];
+            }
     };
-    auto store_pre = [&](const Pre &x) {
+    // Staged through LDS: M, the per-token tiles (thread: token tid / 4, columns 4 (tid % 4)
+    // .. + 3) and gamma_C.
+    struct Stage {
+        f32x4_t m[C * C / 4 / kBwdThreads];
+        f32x4_t dO, e, w, v, pr;
+        float gc;
+    } st;
+    auto load_stage = [&](int c) {
+        const size_t sl = slot_of(c);
+        const f32x4_t *M4 = reinterpret_cast<const f32x4_t *>(Mw + sl * C * C);
 #pragma unroll
-        for (int j = 0; j < NM4; ++j) {
+        for (int j = 0; j < C * C / 4 / kBwdThreads; ++j) st.m[j] = M4[tid + kBwdThreads * j];
+        const int t = tid >> 2, c4 = 4 * (tid & 3);
+        if (t < min(C, T - c * C)) {
+            const size_t o = tok_base(c) + size_t(t) * HD + c4;
+            st.dO = ld4(dout, o);
+            st.e = ld4(e, o);
+            st.w = ld4(w, o);
+            st.v = ld4(v, o);
+            st.pr = ld4(pred, o);
+        } else {
+            st.dO = st.e = st.w = st.v = st.pr = zero4();
+        }
+        st.gc = tid < D ? gC[sl * D + tid] : 0.f;
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+        for (int j = 0; j < C * C / 4 / kBwdThreads; ++j) {
             const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / C, s = e0 % C;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                sM[t * LDM + s + q4] = x.m[j][q4];
-                sP[t * LDM + s + q4] = x.p[j][q4];
-            }
+            for (int q4 = 0; q4 < 4; ++q4) sM[t * LDM + s + q4] = st.m[j][q4];
         }
+        const int t = tid >> 2, c4 = 4 * (tid & 3);
+        *reinterpret_cast<f32x4_t *>(&sdO[t * VT + c4]) = st.dO;
 #pragma unroll
-        for (int j = 0; j < NK4; ++j) {
-            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, i = e0 % D;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                sKB[t * LDK + i + q4] = x.kb[j][q4];
-                sQG[t * LDK + i + q4] = x.qg[j][q4];
-                sKG[t * LDK + i + q4] = x.kg[j][q4];
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            sE[t * LDT + c4 + q4] = st.e[q4];
+            sW[t * LDT + c4 + q4] = st.w[q4];
+            sV[t * LDT + c4 + q4] = st.v[q4];
+            sPr[t * LDT + c4 + q4] = st.pr[q4];
         }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int idx = tid + kBwdThreads * j;
-            sdO[idx] = x.dO[j];
-            sE[idx] = x.e[j];
-            sW[idx] = x.w[j];
-            sV[idx] = x.v[j];
-            sPr[idx] = x.pr[j];
-        }
-        if (tid < D) sGC[tid] = x.gc;
+        if (tid < D) sGC[tid] = st.gc;
     };
 
     for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
         const int i = idx / VT, j = idx % VT;
         sLam[idx] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
     }
-    Pre pre;
-    if (nchunks > 0) load_pre(nchunks - 1, pre);
+    if (nchunks > 0) {
+        load_stage(nchunks - 1);
+        load_rhsA(nchunks - 1);
+        load_lamA(nchunks - 1);
+    }
     for (int c = nchunks - 1; c >= 0; --c) {
         const int nval = min(C, T - c * C);
         const size_t tok0 = tok_base(c);
-        const size_t slot = size_t(bh) * nchunks + c;
+        const size_t slot = slot_of(c);
         __syncthreads();
-        store_pre(pre);
+        store_stage();
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
             lamC[(slot * D + i) * D + j0 + j] = sLam[idx];
         }
         __syncthreads();
-        if (c > 0) load_pre(c - 1, pre);
-        // Right-hand side: (K*beta) lambda_C + P^T dO, thread (t, column pair).
+        if (c > 0) load_stage(c - 1);
+        // Right-hand side of this wave's 16 tokens.
         {
-            const int t = tid >> 2, j = 2 * (tid & 3);
-            float r0 = 0.f, r1 = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < D; ++i) {
-                const float x = sKB[t * LDK + i];
-                r0 = fmaf(x, sLam[i * VT + j], r0);
-                r1 = fmaf(x, sLam[i * VT + j + 1], r1);
-            }
-#pragma unroll 4
-            for (int tp = t; tp < C; ++tp) {
-                const float pv = sP[tp * LDM + t];
-                r0 = fmaf(pv, sdO[tp * VT + j], r0);
-                r1 = fmaf(pv, sdO[tp * VT + j + 1], r1);
-            }
-            sRhs[t * VT + j] = r0;
-            sRhs[t * VT + j + 1] = r1;
+            f32x4_t y = zero4();
+#pragma unroll
+            for (int m = 0; m < D / 4; ++m)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKB[m], sLam[(4 * m + kq) * VT + r], y, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < C / 4; ++m)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[m], sdO[(4 * m + kq) * VT + r], y, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sRhs[(16 * wave + 4 * kq + i) * LDT + r] = y[i];
         }
+        if (c > 0) load_rhsA(c - 1);
         __syncthreads();
-        // Back substitution, wave w: columns 2w, 2w + 1, lane t. With y = e * dU,
-        // dU_t = rhs_t - sum_{s > t} M_st y_s; lanes t >= s read M_st = 0.
+        // Back substitution. With y = e * dU, dU_t = rhs_t - sum_{s > t} M_st y_s; lanes t >= s
+        // read M_st = 0.
         {
-            const int j = 2 * wave;
-            float x0 = sRhs[lane * VT + j], x1 = sRhs[lane * VT + j + 1];
-            const float e0 = sE[lane * VT + j], e1 = sE[lane * VT + j + 1];
+            const int j = 4 * wave;
+            float x[4], ev[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                x[q4] = sRhs[lane * LDT + j + q4];
+                ev[q4] = sE[lane * LDT + j + q4];
+            }
 #pragma unroll
             for (int s = C - 1; s >= 0; --s) {
                 const float m = sM[s * LDM + lane];
-                const float y0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0 * x0), s));
-                const float y1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1 * x1), s));
-                x0 = fmaf(-m, y0, x0);
-                x1 = fmaf(-m, y1, x1);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float ys = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ev[q4] * x[q4]), s));
+                    x[q4] = fmaf(-m, ys, x[q4]);
+                }
             }
-            sdP[lane * VT + j] = -e0 * x0;
-            sdP[lane * VT + j + 1] = -e1 * x1;
+            f32x4_t xu, xv, xw, xe;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sdP[lane * VT + j + q4] = -ev[q4] * x[q4];
+                xu[q4] = x[q4];
+                xv[q4] = sW[lane * LDT + j + q4] * x[q4];
+                xw[q4] = sV[lane * LDT + j + q4] * x[q4];
+                xe[q4] = -sPr[lane * LDT + j + q4] * x[q4];
+            }
             if (lane < nval) {
                 const size_t o = tok0 + size_t(lane) * HD + j;
-                const int l = lane * VT + j;
-                dU[o] = x0;
-                dU[o + 1] = x1;
-                dv[o] = sW[l] * x0;
-                dv[o + 1] = sW[l + 1] * x1;
-                dw[o] = sV[l] * x0;
-                dw[o + 1] = sV[l + 1] * x1;
-                de[o] = -sPr[l] * x0;
-                de[o + 1] = -sPr[l + 1] * x1;
+                *reinterpret_cast<f32x4_t *>(dU + o) = xu;
+                *reinterpret_cast<f32x4_t *>(dv + o) = xv;
+                *reinterpret_cast<f32x4_t *>(dw + o) = xw;
+                *reinterpret_cast<f32x4_t *>(de + o) = xe;
             }
         }
         __syncthreads();
-        // lambda <- Diag(gamma_C) lambda + (Q_hat*gamma)^T dO + (K*gamma)^T dP.
-        {
-            constexpr int TPI = kBwdThreads / D;  // threads per channel
-            constexpr int NJ = VT / TPI;
-            const int i = tid % D, jb = (tid / D) * NJ;
-            float acc[NJ];
-            const float gc = sGC[i];
+        // Adjoint carry for this wave's channel tiles.
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[j] = gc * sLam[i * VT + jb + j];
-#pragma unroll 4
-            for (int t = 0; t < C; ++t) {
-                const float xq = sQG[t * LDK + i], xk = sKG[t * LDK + i];
+        for (int n = 0; n < NIT; ++n) {
+            const int i0 = 16 * (wave + 4 * n);
+            f32x4_t y;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[j] = fmaf(xq, sdO[t * VT + jb + j], fmaf(xk, sdP[t * VT + jb + j], acc[j]));
+            for (int i = 0; i < 4; ++i) {
+                const int ii = i0 + 4 * kq + i;
+                y[i] = sGC[ii] * sLam[ii * VT + r];
             }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) sLam[i * VT + jb + j] = acc[j];
+            for (int m = 0; m < C / 4; ++m) {
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aQG[n][m], sdO[(4 * m + kq) * VT + r], y, 0, 0, 0);
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKG[n][m], sdP[(4 * m + kq) * VT + r], y, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sLam[(i0 + 4 * kq + i) * VT + r] = y[i];
         }
+        if (c > 0) load_lamA(c - 1);
     }
     __syncthreads();
     if (ds0) {
@@ -910,7 +912,7 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    constexpr int NVT = D / kVT;
+    constexpr int NVT = D / kVTS;
     auto ks = bwd_scan_kernel<QT, D>;
     err = hipFuncSetAttribute(reinterpret_cast<const void *>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
                               int(ScanBwdLds<D>::BYTES));
