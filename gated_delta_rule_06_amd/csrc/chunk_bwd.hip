@@ -26,8 +26,9 @@
 //
 // Kernels, in launch order (after the forward's prepare and its scan, which also writes u and
 // the chunk start states):
-//   bwd_prepare_kernel  one workgroup per (b, h, chunk): K*beta, K*gamma, Q_hat*gamma, gamma_C,
-//                       M and P (fp32 matrix cores for the cross-block tiles), and p.
+//   bwd_prepare_kernel  one workgroup per (b, h, chunk): K*beta, K*gamma and Q_hat*gamma (the
+//                       last two channel-major), gamma_C, M and P transposed (fp32 matrix
+//                       cores for the cross-block tiles), and p.
 //   bwd_scan_kernel     one workgroup per (b, h, 16 value columns), chunks in reverse: the
 //                       transposed triangular solve, the adjoint carry, dv, dw, de.
 //   bwd_grads_kernel    one workgroup per (b, h, chunk): dq, dk, dg and a * dL/da.
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
             for (int t = 0; t < C; ++t) {
                 gm *= sA[t * LDH + ii];
                 const float kt = sK[t * LDH + ii];
-                kg[(slot * C + t) * D + i] = kt * gm;
-                qg[(slot * C + t) * D + i] = sQ[t * LDH + ii] * gm;
+                kg[(slot * D + i) * C + t] = kt * gm;
+                qg[(slot * D + i) * C + t] = sQ[t * LDH + ii] * gm;
                 sKG[t * (D + 4) + i] = kt * gm;
             }
             gC[slot * D + i] = gm;
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
         const int t = idx / C, s = idx % C;
         Mw[slot * C * C + idx] = sM[t * LDM + s];
-        Pw[slot * C * C + idx] = sP[t * LDM + s];
+        Pw[slot * C * C + idx] = sP[s * LDM + t];  // P transposed: row t holds P[., t]
     }
     // p = (K*gamma) S0 + M U, [C x D]: wave w owns value-column tiles w, w + 4, ...
     const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
@@ -379,13 +380,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
 //   solve            back substitution, wave w owns columns 4w .. 4w + 3, lane = token.
 //   adjoint carry    lambda <- Diag(gamma_C) lambda + (Q_hat*gamma)^T dO + (K*gamma)^T dP:
 //                    matrix cores, wave w owns channel tiles w, w + 4, ...
-// LDS: lambda [D][16], dO and dP [C][16], M [C][C + 1], per-token tiles [C][17] of e, w, v, p
+// Matrix-core contraction order: step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi, so
+// a lane's four A values of one mo are adjacent in memory (one 16-byte load) and the B reads
+// from rows of 20 floats fall in distinct LDS banks.
+// LDS: lambda [D][20], dO and dP [C][20], M [C][C + 1], per-token tiles [C][17] of e, w, v, p
 // and the right-hand side, gamma_C [D].
 // ------------------------------------------------------------------------------------------
 constexpr int kVTS = 16;  // value columns per scan workgroup
 template <int D> struct ScanBwdLds {
-    static constexpr int LDM = kC + 1, LDT = kVTS + 1;
-    static constexpr int FLOATS = D * kVTS + 2 * kC * kVTS + kC * LDM + 5 * kC * LDT + D;
+    static constexpr int LDM = kC + 1, LDT = kVTS + 1, LDB = kVTS + 4;
+    static constexpr int FLOATS = D * LDB + 2 * kC * LDB + kC * LDM + 5 * kC * LDT + D;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -399,10 +403,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     float *__restrict__ dw, float *__restrict__ de, float *__restrict__ ds0, int T, int H, int BH,
     int nchunks) {
     using L = ScanBwdLds<D>;
-    constexpr int C = kC, VT = kVTS, NVT = D / VT, LDM = L::LDM, LDT = L::LDT;
+    constexpr int C = kC, VT = kVTS, NVT = D / VT, LDM = L::LDM, LDT = L::LDT, LDB = L::LDB;
     constexpr int NIT = D / 64;  // channel tiles per wave in the adjoint carry
     extern __shared__ float lds[];
-    float *sLam = lds, *sdO = sLam + D * VT, *sdP = sdO + C * VT, *sM = sdP + C * VT;
+    float *sLam = lds, *sdO = sLam + D * LDB, *sdP = sdO + C * LDB, *sM = sdP + C * LDB;
     float *sE = sM + C * LDM, *sW = sE + C * LDT, *sV = sW + C * LDT, *sPr = sV + C * LDT;
     float *sRhs = sPr + C * LDT, *sGC = sRhs + C * LDT;
 
@@ -419,25 +423,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     auto tok_base = [&](int c) { return (size_t(b) * T + size_t(c) * C) * HD + size_t(h) * D + j0; };
     auto slot_of = [&](int c) { return size_t(bh) * nchunks + c; };
 
-    // Matrix-core A operands (k = 4 m + kq): K*beta rows and P columns of this wave's tokens;
-    // Q_hat*gamma and K*gamma columns of this wave's channel tiles.
-    float aKB[D / 4], aP[C / 4], aQG[NIT][C / 4], aKG[NIT][C / 4];
+    // Matrix-core A operands: K*beta and P^T rows of this wave's tokens; Q_hat*gamma and
+    // K*gamma (channel-major) rows of this wave's channel tiles.
+    f32x4_t aKB[D / 16], aP[C / 16], aQG[NIT][C / 16], aKG[NIT][C / 16];
     auto load_rhsA = [&](int c) {
         const size_t sl = slot_of(c);
 #pragma unroll
-        for (int m = 0; m < D / 4; ++m) aKB[m] = kb[(sl * C + 16 * wave + r) * D + 4 * m + kq];
+        for (int mo = 0; mo < D / 16; ++mo) aKB[mo] = ld4(kb, (sl * C + 16 * wave + r) * D + 16 * mo + 4 * kq);
 #pragma unroll
-        for (int m = 0; m < C / 4; ++m) aP[m] = Pw[(sl * C + 4 * m + kq) * C + 16 * wave + r];
+        for (int mo = 0; mo < C / 16; ++mo) aP[mo] = ld4(Pw, (sl * C + 16 * wave + r) * C + 16 * mo + 4 * kq);
     };
     auto load_lamA = [&](int c) {
         const size_t sl = slot_of(c);
 #pragma unroll
         for (int n = 0; n < NIT; ++n)
 #pragma unroll
-            for (int m = 0; m < C / 4; ++m) {
-                const size_t o = (sl * C + 4 * m + kq) * D + 16 * (wave + 4 * n) + r;
-                aQG[n][m] = qg[o];
-                aKG[n][m] = kg[o];
+            for (int mo = 0; mo < C / 16; ++mo) {
+                const size_t o = (sl * D + 16 * (wave + 4 * n) + r) * C + 16 * mo + 4 * kq;
+                aQG[n][mo] = ld4(qg, o);
+                aKG[n][mo] = ld4(kg, o);
             }
     };
     // Staged through LDS: M, the per-token tiles (thread: token tid / 4, columns 4 (tid % 4)
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
             for (int q4 = 0; q4 < 4; ++q4) sM[t * LDM + s + q4] = st.m[j][q4];
         }
         const int t = tid >> 2, c4 = 4 * (tid & 3);
-        *reinterpret_cast<f32x4_t *>(&sdO[t * VT + c4]) = st.dO;
+        *reinterpret_cast<f32x4_t *>(&sdO[t * LDB + c4]) = st.dO;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             sE[t * LDT + c4 + q4] = st.e[q4];
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 
     for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
         const int i = idx / VT, j = idx % VT;
-        sLam[idx] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
+        sLam[i * LDB + j] = dsT ? dsT[(size_t(bh) * D + i) * D + j0 + j] : 0.f;
     }
     if (nchunks > 0) {
         load_stage(nchunks - 1);
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
         store_stage();
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
-            lamC[(slot * D + i) * D + j0 + j] = sLam[idx];
+            lamC[(slot * D + i) * D + j0 + j] = sLam[i * LDB + j];
         }
         __syncthreads();
         if (c > 0) load_stage(c - 1);
@@ -509,11 +513,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
         {
             f32x4_t y = zero4();
 #pragma unroll
-            for (int m = 0; m < D / 4; ++m)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKB[m], sLam[(4 * m + kq) * VT + r], y, 0, 0, 0);
+            for (int mo = 0; mo < D / 16; ++mo)
 #pragma unroll
-            for (int m = 0; m < C / 4; ++m)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[m], sdO[(4 * m + kq) * VT + r], y, 0, 0, 0);
+                for (int mi = 0; mi < 4; ++mi)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKB[mo][mi], sLam[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
+#pragma unroll
+            for (int mo = 0; mo < C / 16; ++mo)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[mo][mi], sdO[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sRhs[(16 * wave + 4 * kq + i) * LDT + r] = y[i];
         }
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
             f32x4_t xu, xv, xw, xe;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                sdP[lane * VT + j + q4] = -ev[q4] * x[q4];
+                sdP[lane * LDB + j + q4] = -ev[q4] * x[q4];
                 xu[q4] = x[q4];
                 xv[q4] = sW[lane * LDT + j + q4] * x[q4];
                 xw[q4] = sV[lane * LDT + j + q4] * x[q4];
@@ -564,15 +572,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ii = i0 + 4 * kq + i;
-                y[i] = sGC[ii] * sLam[ii * VT + r];
+                y[i] = sGC[ii] * sLam[ii * LDB + r];
             }
 #pragma unroll
-            for (int m = 0; m < C / 4; ++m) {
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aQG[n][m], sdO[(4 * m + kq) * VT + r], y, 0, 0, 0);
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKG[n][m], sdP[(4 * m + kq) * VT + r], y, 0, 0, 0);
-            }
+            for (int mo = 0; mo < C / 16; ++mo)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sLam[(i0 + 4 * kq + i) * VT + r] = y[i];
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int tt = 16 * mo + 4 * kq + mi;
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aQG[n][mo][mi], sdO[tt * LDB + r], y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKG[n][mo][mi], sdP[tt * LDB + r], y, 0, 0, 0);
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sLam[(i0 + 4 * kq + i) * LDB + r] = y[i];
         }
         if (c > 0) load_lamA(c - 1);
     }
@@ -580,7 +591,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     if (ds0) {
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
-            ds0[(size_t(bh) * D + i) * D + j0 + j] = sLam[idx];
+            ds0[(size_t(bh) * D + i) * D + j0 + j] = sLam[i * LDB + j];
         }
     }
 }
