@@ -176,50 +176,54 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
             }
         }
         __syncthreads();
-        if (tid < DH) {
-            const int ii = tid;
+        float *sBp = sMid + 6 * DH;  // whole-block decay products per channel
+        {
+            // Thread (channel, 16-token block): prefix F and suffix R inside the block.
+            const int ii = tid % DH, bb = tid / DH;
+            float run = 1.f;
+#pragma unroll
+            for (int tl = 0; tl < 16; ++tl) {
+                run *= sA[(16 * bb + tl) * LDH + ii];
+                sF[(16 * bb + tl) * LDH + ii] = run;
+            }
+            run = 1.f;
+#pragma unroll
+            for (int tl = 15; tl >= 0; --tl) {
+                sR[(16 * bb + tl) * LDH + ii] = run;
+                run *= sA[(16 * bb + tl) * LDH + ii];
+            }
+            sBp[bb * DH + ii] = run;
+        }
+        __syncthreads();
+        {
+            // Thread (channel, block bb): products of the whole blocks between bb and each
+            // earlier block; gamma and beta of its tokens and the scaled operands K*gamma,
+            // Q_hat*gamma, K*beta; gamma_C.
+            const int ii = tid % DH, bb = tid / DH, i = p0 + ii;
             float bp[kNB];
 #pragma unroll
-            for (int bb = 0; bb < kNB; ++bb) {
-                float run = 1.f;
-                for (int tl = 0; tl < 16; ++tl) {
-                    const int t = 16 * bb + tl;
-                    run *= sA[t * LDH + ii];
-                    sF[t * LDH + ii] = run;
-                }
-                run = 1.f;
-                for (int tl = 15; tl >= 0; --tl) {
-                    const int t = 16 * bb + tl;
-                    sR[t * LDH + ii] = run;
-                    run *= sA[t * LDH + ii];
-                }
-                bp[bb] = run;
+            for (int b2 = 0; b2 < kNB; ++b2) bp[b2] = sBp[b2 * DH + ii];
+            float mid = 1.f, before = 1.f, after = 1.f;
+            for (int bs = bb - 1; bs >= 0; --bs) {
+                sMid[(bb * (bb - 1) / 2 + bs) * DH + ii] = mid;
+                mid *= bp[bs];
             }
 #pragma unroll
-            for (int bt = 1; bt < kNB; ++bt) {
-                float mid = 1.f;
-#pragma unroll
-                for (int bs = bt - 1; bs >= 0; --bs) {
-                    sMid[(bt * (bt - 1) / 2 + bs) * DH + ii] = mid;
-                    mid *= bp[bs];
-                }
+            for (int b2 = 0; b2 < kNB; ++b2) {
+                if (b2 < bb) before *= bp[b2];
+                if (b2 > bb) after *= bp[b2];
             }
-            // K*gamma, Q_hat*gamma (gamma through t), K*beta (beta after t), gamma_C.
-            const int i = p0 + ii;
-            float gm = 1.f;
-            for (int t = 0; t < C; ++t) {
-                gm *= sA[t * LDH + ii];
+#pragma unroll
+            for (int tl = 0; tl < 16; ++tl) {
+                const int t = 16 * bb + tl;
+                const float gm = before * sF[t * LDH + ii];
                 const float kt = sK[t * LDH + ii];
                 kg[(slot * D + i) * C + t] = kt * gm;
                 qg[(slot * D + i) * C + t] = sQ[t * LDH + ii] * gm;
                 sKG[t * (D + 4) + i] = kt * gm;
+                kb[(slot * C + t) * D + i] = kt * sR[t * LDH + ii] * after;
             }
-            gC[slot * D + i] = gm;
-            float bt = 1.f;
-            for (int t = C - 1; t >= 0; --t) {
-                kb[(slot * C + t) * D + i] = sK[t * LDH + ii] * bt;
-                bt *= sA[t * LDH + ii];
-            }
+            if (bb == kNB - 1) gC[slot * D + i] = before * bp[kNB - 1];
         }
         __syncthreads();
 #pragma unroll
@@ -239,9 +243,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
         __syncthreads();
         // Sub-block pivots (replacing the block ones): F4, R4 and whole-sub-block products B4.
         float *sB4 = sMid;
-        if (tid < DH) {
-            const int ii = tid;
-            for (int u = 0; u < C / 4; ++u) {
+        {
+            // Thread (channel, block): its four sub-blocks.
+            const int ii = tid % DH, bb = tid / DH;
+#pragma unroll
+            for (int u = 4 * bb; u < 4 * bb + 4; ++u) {
                 float run = 1.f;
 #pragma unroll
                 for (int tl = 0; tl < 4; ++tl) {
@@ -601,10 +607,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 // [C][D + 4] (products) and k, a, q_hat channel-major [D][C + 1] (decayed sums).
 // ------------------------------------------------------------------------------------------
 template <int D> struct GradLds {
-    static constexpr int LDM = kC + 1, LDX = D + 4, LDT = kC + 1;
+    static constexpr int LDM = kC + 1, LDX = D + 4, LDH = 65, DH = 64;
     static constexpr int OUPU = 2 * kC * LDM;
-    static constexpr int P1 = 3 * kC * LDX, P2 = 3 * D * LDT;
-    static constexpr int FLOATS = OUPU + D + (P1 > P2 ? P1 : P2);
+    static constexpr int P1 = 3 * kC * LDX;
+    // Per 64-channel pass: a, k, q_hat, F, R (16-token blocks), F4, R4 (4-token sub-blocks)
+    // [C][65]; products of whole blocks between (6 pairs), of whole sub-blocks (16), of the
+    // blocks before and after each block (4 + 4), per channel.
+    static constexpr int P2 = 7 * kC * LDH + (6 + 16 + 4 + 4) * DH;
+    static constexpr int FLOATS = OUPU + 2 * D + (P1 > P2 ? P1 : P2) + kNB * DH;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -617,13 +627,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg,
     float *__restrict__ dla, float *__restrict__ drp, int T, int H, int nchunks) {
     using L = GradLds<D>;
-    constexpr int C = kC, LDM = L::LDM, LDX = L::LDX, LDT = L::LDT;
+    constexpr int C = kC, LDM = L::LDM, LDX = L::LDX, LDH = L::LDH, DH = L::DH;
     extern __shared__ float lds[];
     float *sOU = lds, *sPU = lds + C * LDM;
     float *sRS = lds + L::OUPU;  // rowsum(S_C * lambda_C) per channel
-    float *un = sRS + D;
+    float *sDr = sRS + D;        // sum over tokens of g * q * dq_hat per channel
+    float *un = sDr + D;
     float *sU = un, *sdO = un + C * LDX, *sdP = un + 2 * C * LDX;
-    float *sKT = un, *sAT = un + D * LDT, *sQT = un + 2 * D * LDT;
+    float *sA = un, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH, *sR = sF + C * LDH,
+          *sF4 = sR + C * LDH, *sR4 = sF4 + C * LDH, *sMid = sR4 + C * LDH, *sB4 = sMid + 6 * DH,
+          *sGb = sB4 + 16 * DH, *sBa = sGb + 4 * DH;
+    float *sBp = lds + L::FLOATS - kNB * DH;  // whole-block decay products per channel
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
@@ -668,6 +682,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         acc = wave_sum(acc);
         if (lane == 0) sRS[i] = acc;
     }
+    for (int i = tid; i < D; i += kBwdThreads) sDr[i] = 0.f;
     __syncthreads();
     // O U^T (s <= t) and dP U^T (s < t), lower 16x16 tiles; job j < 20: matrix j / 10, tile
     // j % 10 = bt (bt + 1) / 2 + bs.
@@ -729,127 +744,300 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     }
     __syncthreads();
     const float *rh = r + size_t(h) * D;
-    {
-        constexpr int N4 = C * D / 4 / kBwdThreads;
-        f32x4_t vk[N4], va[N4], vq[N4];
+    const int rr = lane & 15, kq = lane >> 4;
+    // Decayed sums over token pairs, per 64-channel pass, on the matrix cores. With the pivots
+    // of the prepare kernel, Gamma_ts = F_t * mid * R_s across 16-token blocks and
+    // F4_t * mid4 * R4_s across 4-token sub-blocks of one block; pairs inside one sub-block are
+    // direct products. Jobs: kind 0 (dq_hat and the read part of dk, rows = t) and kind 1 (the
+    // write part of dk, rows = s), 16 tiles each; wave w takes jobs w, w + 4, ...
+    for (int p0 = 0; p0 < D; p0 += DH) {
+        if (p0 > 0) __syncthreads();
+        {
+            constexpr int N4 = C * DH / 4 / kBwdThreads;
+            f32x4_t va[N4], vk[N4], vq[N4];
 #pragma unroll
-        for (int j = 0; j < N4; ++j) {
-            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, ii = e0 % D;
-            const size_t o = tok0 + size_t(t) * HD + ii;
-            if (t < nval) {
-                vk[j] = ld4(k, o);
-                va[j] = ld4(a, o);
-                vq[j] = ld4(g, o) * ld4(q, o) * ld4(rh, ii);
-            } else {
-                vk[j] = vq[j] = zero4();
-                va[j] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+            for (int j = 0; j < N4; ++j) {
+                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
+                const size_t o = tok0 + size_t(t) * HD + p0 + ii;
+                if (t < nval) {
+                    va[j] = ld4(a, o);
+                    vk[j] = ld4(k, o);
+                    vq[j] = ld4(g, o) * ld4(q, o) * ld4(rh, p0 + ii);
+                } else {
+                    va[j] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+                    vk[j] = vq[j] = zero4();
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < N4; ++j) {
+                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    sA[t * LDH + ii + q4] = va[j][q4];
+                    sK[t * LDH + ii + q4] = vk[j][q4];
+                    sQ[t * LDH + ii + q4] = vq[j][q4];
+                }
             }
         }
+        __syncthreads();
+        {
+            // Thread (channel, 16-token block): prefix and suffix products inside the block
+            // and inside its four sub-blocks.
+            const int ii = tid % DH, bb = tid / DH;
+            float run = 1.f;
 #pragma unroll
-        for (int j = 0; j < N4; ++j) {
-            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, ii = e0 % D;
+            for (int tl = 0; tl < 16; ++tl) {
+                run *= sA[(16 * bb + tl) * LDH + ii];
+                sF[(16 * bb + tl) * LDH + ii] = run;
+            }
+            run = 1.f;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                sKT[(ii + q4) * LDT + t] = vk[j][q4];
-                sAT[(ii + q4) * LDT + t] = va[j][q4];
-                sQT[(ii + q4) * LDT + t] = vq[j][q4];
+            for (int tl = 15; tl >= 0; --tl) {
+                sR[(16 * bb + tl) * LDH + ii] = run;
+                run *= sA[(16 * bb + tl) * LDH + ii];
+            }
+            sBp[bb * DH + ii] = run;
+#pragma unroll
+            for (int u = 4 * bb; u < 4 * bb + 4; ++u) {
+                float r4 = 1.f;
+#pragma unroll
+                for (int tl = 0; tl < 4; ++tl) {
+                    r4 *= sA[(4 * u + tl) * LDH + ii];
+                    sF4[(4 * u + tl) * LDH + ii] = r4;
+                }
+                r4 = 1.f;
+#pragma unroll
+                for (int tl = 3; tl >= 0; --tl) {
+                    sR4[(4 * u + tl) * LDH + ii] = r4;
+                    r4 *= sA[(4 * u + tl) * LDH + ii];
+                }
+                sB4[u * DH + ii] = r4;
+            }
+        }
+        __syncthreads();
+        if (tid < DH) {
+            const int ii = tid;
+            float bp[kNB];
+#pragma unroll
+            for (int bb = 0; bb < kNB; ++bb) bp[bb] = sBp[bb * DH + ii];
+#pragma unroll
+            for (int bt = 1; bt < kNB; ++bt) {
+                float mid = 1.f;
+#pragma unroll
+                for (int bs = bt - 1; bs >= 0; --bs) {
+                    sMid[(bt * (bt - 1) / 2 + bs) * DH + ii] = mid;
+                    mid *= bp[bs];
+                }
+            }
+            float before = 1.f;
+#pragma unroll
+            for (int bb = 0; bb < kNB; ++bb) {
+                sGb[bb * DH + ii] = before;
+                before *= bp[bb];
+            }
+            float after = 1.f;
+#pragma unroll
+            for (int bb = kNB - 1; bb >= 0; --bb) {
+                sBa[bb * DH + ii] = after;
+                after *= bp[bb];
+            }
+        }
+        __syncthreads();
+        for (int job = wave; job < 32; job += 4) {
+            const int kind = job / 16, rb = (job % 16) / 4, it = job % 4;
+            const int ic = 16 * it + rr;  // this lane's B / output column, within the pass
+            const size_t ocol = size_t(p0 + ic);
+            if (kind == 0) {
+                // Rows t of block bt = rb. The rows' global operands are loaded first.
+                const int bt = rb;
+                float gx1[4], gx2[4], gg[4], gq[4];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int t = 16 * bt + 4 * kq + e4;
+                    const size_t o = tok0 + size_t(t) * HD + ocol;
+                    const bool ok = t < nval;
+                    gx1[e4] = ok ? dq[o] : 0.f;
+                    gx2[e4] = ok ? dk[o] : 0.f;
+                    gg[e4] = ok ? g[o] : 0.f;
+                    gq[e4] = ok ? ld(q, o) : 0.f;
+                }
+                f32x4_t cq = zero4(), cr = zero4(), dq4 = zero4(), dr4 = zero4();
+                for (int bs = 0; bs < bt; ++bs) {
+                    f32x4_t yq = zero4(), yr = zero4();
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int kk = 4 * m + kq, sg = 16 * bs + kk;
+                        const float b = sK[sg * LDH + ic] * sR[sg * LDH + ic];
+                        yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[(16 * bt + rr) * LDM + sg], b, yq, 0, 0, 0);
+                        yr = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[(16 * bt + rr) * LDM + sg], b, yr, 0, 0, 0);
+                    }
+                    const float md = sMid[(bt * (bt - 1) / 2 + bs) * DH + ic];
+                    cq += md * yq;
+                    cr += md * yr;
+                }
+#pragma unroll
+                for (int gp = 1; gp < 4; ++gp) {
+                    f32x4_t yq = zero4(), yr = zero4();
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int kk = 4 * m + kq, sg = 16 * bt + kk;
+                        const int us = kk >> 2;
+                        const bool on = (rr >> 2) - us == gp;
+                        float mid4 = 1.f;
+                        if (gp >= 2) mid4 = us + 1 < 4 ? sB4[(4 * bt + us + 1) * DH + ic] : 0.f;
+                        if (gp == 3) mid4 *= us + 2 < 4 ? sB4[(4 * bt + us + 2) * DH + ic] : 0.f;
+                        const float b = sK[sg * LDH + ic] * sR4[sg * LDH + ic] * mid4;
+                        const float aq = on ? sOU[(16 * bt + rr) * LDM + sg] : 0.f;
+                        const float ar = on ? sPU[(16 * bt + rr) * LDM + sg] : 0.f;
+                        yq = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, b, yq, 0, 0, 0);
+                        yr = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, b, yr, 0, 0, 0);
+                    }
+                    dq4 += yq;
+                    dr4 += yr;
+                }
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int t = 16 * bt + 4 * kq + e4;
+                    // Pairs inside t's sub-block: s = t, t - 1, ... down to its start.
+                    float sq = 0.f, sr = 0.f, run = 1.f;
+                    for (int s4 = t; s4 >= (t & ~3); --s4) {
+                        const float ks = run * sK[s4 * LDH + ic];
+                        sq = fmaf(sOU[t * LDM + s4], ks, sq);
+                        sr = fmaf(sPU[t * LDM + s4], ks, sr);
+                        run *= sA[s4 * LDH + ic];
+                    }
+                    const float fb = sF[t * LDH + ic], f4 = sF4[t * LDH + ic];
+                    if (t < nval) {
+                        const size_t o = tok0 + size_t(t) * HD + ocol;
+                        const float gam = sGb[bt * DH + ic] * fb;
+                        const float dqh = gam * gx1[e4] + fb * cq[e4] + f4 * dq4[e4] + sq;
+                        const float dkr = gam * gx2[e4] + fb * cr[e4] + f4 * dr4[e4] + sr;
+                        const float gt = gg[e4], qt = gq[e4];
+                        dq[o] = rh[ocol] * gt * dqh;
+                        dg[o] = rh[ocol] * qt * dqh;
+                        dk[o] = dkr;
+                        dla[o] = fmaf(sQ[t * LDH + ic], dqh, sK[t * LDH + ic] * dkr);
+                        atomicAdd(&sDr[ocol], gt * qt * dqh);
+                    }
+                }
+            } else {
+                // Rows s of block bs = rb.
+                const int bs = rb;
+                float gx3[4];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int s4 = 16 * bs + 4 * kq + e4;
+                    gx3[e4] = s4 < nval ? X3[tok0 + size_t(s4) * HD + ocol] : 0.f;
+                }
+                f32x4_t cw = zero4(), dw4 = zero4();
+                for (int bt = bs + 1; bt < kNB; ++bt) {
+                    f32x4_t y = zero4();
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int kk = 4 * m + kq, tg = 16 * bt + kk;
+                        const float f = sF[tg * LDH + ic];
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[tg * LDM + 16 * bs + rr], sQ[tg * LDH + ic] * f, y, 0, 0, 0);
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[tg * LDM + 16 * bs + rr], sK[tg * LDH + ic] * f, y, 0, 0, 0);
+                    }
+                    cw += sMid[(bt * (bt - 1) / 2 + bs) * DH + ic] * y;
+                }
+#pragma unroll
+                for (int gp = 1; gp < 4; ++gp) {
+                    f32x4_t y = zero4();
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int kk = 4 * m + kq, tg = 16 * bs + kk;
+                        const int ut = kk >> 2;
+                        const bool on = ut - (rr >> 2) == gp;
+                        // Products of the gp - 1 whole sub-blocks before t's.
+                        float mid4 = 1.f;
+                        if (gp >= 2) mid4 = ut - 1 >= 0 ? sB4[(4 * bs + ut - 1) * DH + ic] : 0.f;
+                        if (gp == 3) mid4 *= ut - 2 >= 0 ? sB4[(4 * bs + ut - 2) * DH + ic] : 0.f;
+                        const float f = sF4[tg * LDH + ic] * mid4;
+                        const float ao = on ? sOU[tg * LDM + 16 * bs + rr] : 0.f;
+                        const float ap = on ? sPU[tg * LDM + 16 * bs + rr] : 0.f;
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sQ[tg * LDH + ic] * f, y, 0, 0, 0);
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, sK[tg * LDH + ic] * f, y, 0, 0, 0);
+                    }
+                    dw4 += y;
+                }
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int s4 = 16 * bs + 4 * kq + e4;
+                    // Pairs inside s's sub-block: t = s, s + 1, ... up to its end.
+                    float sw = 0.f, run = 1.f;
+                    for (int t = s4; t <= (s4 | 3); ++t) {
+                        sw = fmaf(sOU[t * LDM + s4], run * sQ[t * LDH + ic], sw);
+                        sw = fmaf(sPU[t * LDM + s4], run * sK[t * LDH + ic], sw);
+                        if (t < (s4 | 3)) run *= sA[(t + 1) * LDH + ic];
+                    }
+                    if (s4 < nval) {
+                        const size_t o = tok0 + size_t(s4) * HD + ocol;
+                        const float rb_ = sR[s4 * LDH + ic], r4 = sR4[s4 * LDH + ic];
+                        const float bet = rb_ * sBa[bs * DH + ic];
+                        X3[o] = bet * gx3[e4] + rb_ * cw[e4] + r4 * dw4[e4] + sw;
+                    }
+                }
             }
         }
     }
     __syncthreads();
-    const int i = tid % D, role = tid / D;
-    const float *kT = sKT + i * LDT, *aT = sAT + i * LDT, *qT = sQT + i * LDT;
-    if (role == 0) {
-        // dq_hat and the read part of dk, tokens in order (gamma as a running product). The
-        // token's global operands are loaded one token ahead.
-        float gm = 1.f, dr_acc = 0.f;
-        auto fetch = [&](int t, float (&f)[4]) {
-            if (t < nval) {
-                const size_t o = tok0 + size_t(t) * HD + i;
-                f[0] = dq[o]; f[1] = dk[o]; f[2] = g[o]; f[3] = ld(q, o);
-            } else {
-                f[0] = f[1] = f[2] = f[3] = 0.f;
-            }
-        };
-        float cur[4], nxt[4];
-        fetch(0, cur);
-        for (int t = 0; t < C; ++t) {
-            fetch(t + 1, nxt);
-            gm *= aT[t];
-            float sq = 0.f, sr = 0.f, run = 1.f;
-#pragma unroll 4
-            for (int s = t; s >= 0; --s) {
-                const float ks = run * kT[s];
-                sq = fmaf(sOU[t * LDM + s], ks, sq);
-                sr = fmaf(sPU[t * LDM + s], ks, sr);
-                run *= aT[s];
-            }
-            if (t < nval) {
-                const size_t o = tok0 + size_t(t) * HD + i;
-                const float dqh = fmaf(gm, cur[0], sq);
-                const float dkr = fmaf(gm, cur[1], sr);
-                const float gt = cur[2], qt = cur[3];
-                dq[o] = rh[i] * gt * dqh;
-                dg[o] = rh[i] * qt * dqh;
-                dr_acc = fmaf(gt * qt, dqh, dr_acc);
-                dk[o] = dkr;
-                dla[o] = fmaf(qT[t], dqh, kT[t] * dkr);
-            }
-#pragma unroll
-            for (int f = 0; f < 4; ++f) cur[f] = nxt[f];
-        }
-        drp[slot * D + i] = dr_acc;
-    } else if (role == 1) {
-        // Write part of dk, tokens in reverse (beta as a running product).
-        float bt = 1.f;
-        auto fetch = [&](int s) { return s >= 0 && s < nval ? X3[tok0 + size_t(s) * HD + i] : 0.f; };
-        float cur = fetch(C - 1);
-        for (int s = C - 1; s >= 0; --s) {
-            const float nxt = fetch(s - 1);
-            float sw = 0.f, run = 1.f;
-#pragma unroll 4
-            for (int t = s; t < C; ++t) {
-                sw = fmaf(sOU[t * LDM + s], run * qT[t], sw);
-                sw = fmaf(sPU[t * LDM + s], run * kT[t], sw);
-                run *= aT[t + 1 < C ? t + 1 : t];
-            }
-            if (s < nval) X3[tok0 + size_t(s) * HD + i] = fmaf(bt, cur, sw);
-            bt *= aT[s];
-            cur = nxt;
-        }
-    }
-    __syncthreads();
-    if (role == 0) {
+    if (tid < D) {
+        const int i = tid;
+        drp[slot * D + i] = sDr[i];
         const float rs = sRS[i];
+        // Log-decay gradient: reverse cumulative sum over the chunk, 16 tokens per batch of
+        // loads.
         float cum = 0.f;
-        auto fetch = [&](int t, float (&f)[3]) {
-            if (t >= 0) {
-                const size_t o = tok0 + size_t(t) * HD + i;
-                f[0] = X3[o]; f[1] = dla[o]; f[2] = dk[o];
-            }
-        };
-        float cur[3] = {0.f, 0.f, 0.f}, nxt[3] = {0.f, 0.f, 0.f};
-        fetch(nval - 1, cur);
-        for (int t = nval - 1; t >= 0; --t) {
-            fetch(t - 1, nxt);
-            const size_t o = tok0 + size_t(t) * HD + i;
-            cum += cur[1] - kT[t] * cur[0];
-            dla[o] = cum + rs;
-            dk[o] = cur[2] + cur[0];
+        for (int t1 = C; t1 > 0; t1 -= 16) {
+            float x3[16], la[16], dkv[16], kv[16];
 #pragma unroll
-            for (int f = 0; f < 3; ++f) cur[f] = nxt[f];
+            for (int u = 0; u < 16; ++u) {
+                const int t = t1 - 1 - u;
+                const size_t o = tok0 + size_t(t) * HD + i;
+                const bool ok = t < nval;
+                x3[u] = ok ? X3[o] : 0.f;
+                la[u] = ok ? dla[o] : 0.f;
+                dkv[u] = ok ? dk[o] : 0.f;
+                kv[u] = ok ? ld(k, o) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int t = t1 - 1 - u;
+                cum += la[u] - kv[u] * x3[u];
+                if (t < nval) {
+                    const size_t o = tok0 + size_t(t) * HD + i;
+                    dla[o] = cum + rs;
+                    dk[o] = dkv[u] + x3[u];
+                }
+            }
         }
     }
 }
 
+// dr[h] = sum over (b, chunk) of the per-chunk partials: 1024 threads, thread (group, channel)
+// sums the rows equal to its group mod G, then the G partial sums are added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(D) void bwd_dr_kernel(const float *__restrict__ drp, float *__restrict__ dr,
-                                                   int B, int H, int nchunks) {
-    const int h = blockIdx.x, i = threadIdx.x;
-    float s = 0.f;
-    for (int b = 0; b < B; ++b)
-        for (int c = 0; c < nchunks; ++c) s += drp[((size_t(b) * H + h) * nchunks + c) * D + i];
-    dr[size_t(h) * D + i] = s;
+__global__ __launch_bounds__(1024) void bwd_dr_kernel(const float *__restrict__ drp, float *__restrict__ dr,
+                                                      int B, int H, int nchunks) {
+    constexpr int G = 1024 / D;
+    __shared__ float part[G][D];
+    const int h = blockIdx.x, i = threadIdx.x % D, grp = threadIdx.x / D;
+    const int rows = B * nchunks;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int rw = grp; rw < rows; rw += G) {
+        const int b = rw / nchunks, c = rw % nchunks;
+        acc += drp[((size_t(b) * H + h) * nchunks + c) * D + i];
+    }
+    part[grp][i] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < G; ++g2) sum += part[g2][i];
+        dr[size_t(h) * D + i] = sum;
+    }
 }
 
 // Workspace regions, each 256-byte aligned.
@@ -944,7 +1132,7 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((bwd_dr_kernel<D>), dim3(H), dim3(D), 0, stream, drp, x.dr, B, H, nchunks);
+    hipLaunchKernelGGL((bwd_dr_kernel<D>), dim3(H), dim3(1024), 0, stream, drp, x.dr, B, H, nchunks);
     return hipGetLastError();
 }
 
