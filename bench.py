@@ -242,6 +242,47 @@ def chunk_report(name, inp, chunk, r):
     return out
 
 
+def bwd_bytes(d, qkv_bytes=2):
+    """Algorithmic bytes of the backward pass per token-head: q, k, v, dO read once (qkv dtype),
+    a, g, e, w read once (fp32), dq, dk, dv, a*dL/da, dg, de, dw written once (fp32)."""
+    return 4 * d * qkv_bytes + 4 * d * 4 + 7 * d * 4
+
+
+def time_backward(inp, dev, steps, warmup, name):
+    """Time `steps` backward calls (forward rerun inside, chunks of 64) with HIP events on the
+    stream the library is called on."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_06_amd as muir
+    t = to_dev(inp, dev)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    code = muir.MUIR_BF16 if inp["qkv"] == "bf16" else muir.MUIR_F32
+    rng = np.random.default_rng(7)
+    do = torch.from_numpy(rng.standard_normal((B, T, H, d), dtype=np.float32)).to(dev, t["v"].dtype)
+    ws = torch.empty(muir.chunk_bwd_workspace_size(B, T, H, d, d, 64, code), dtype=torch.uint8,
+                     device=dev)
+    args = [t[n] for n in NAMES]
+    out = muir.chunk_bwd(*args, do=do, workspace=ws)
+    for _ in range(warmup):
+        muir.chunk_bwd(*args, do=do, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        muir.chunk_bwd(*args, do=do, workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert all(torch.isfinite(x).all() for x in out.values())
+    ach = bwd_bytes(d) * B * T * H / (ms * 1e-3)
+    return {"workload": name, "chunk": 64, "ms_per_call": ms,
+            "tokens_per_s_per_layer": B * T / (ms * 1e-3),
+            "workspace_GB": ws.numel() / 1e9,
+            "call_roofline": {"bound": "hbm", "achieved_GBps": ach / 1e9,
+                              "peak_GBps": HBM_PEAK / 1e9, "frac": ach / HBM_PEAK,
+                              "bytes_per_token_head": bwd_bytes(d)}}
+
+
 def time_decode(dev, steps, warmup):
     import numpy as np
     import torch
@@ -301,7 +342,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "scalar", "lowrank", "copy"],
+    ap.add_argument("--only", choices=["all", "main", "t4k", "decode", "scalar", "lowrank", "bwd",
+                                       "copy"],
                     default="all",
                     help="'copy' times a plain 1 GiB device copy: the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -415,6 +457,20 @@ def main():
             del inp, lr
         if "value" not in result:
             first = secondary["long_context_lowrank_gates"]
+            result["value"] = first["tokens_per_s_per_layer"]
+            result["ms_per_step"] = first["ms_per_call"]
+            result["config"] = {"workload": first["workload"]}
+    if args.only in ("all", "bwd"):
+        # The backward pass (gradients of every input), chunks of 64.
+        for cfg, key in ((2, "t4k_backward"), (3, "long_context_backward")):
+            inp = main_inp if (cfg == 3 and main_inp is not None) else workloads.chunk_inputs(cfg)
+            name = (f"chunk_bwd B{inp['B']} H{inp['H']} d{inp['d']} T{inp['T']} C64 bf16, "
+                    f"every input's gradient")
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            secondary[key] = time_backward(inp, dev, max(3, args.steps // 2), args.warmup, name)
+            del inp
+        if "value" not in result:
+            first = secondary["t4k_backward"]
             result["value"] = first["tokens_per_s_per_layer"]
             result["ms_per_step"] = first["ms_per_call"]
             result["config"] = {"workload": first["workload"]}
