@@ -674,13 +674,26 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             *reinterpret_cast<f32x4_t *>(&sdP[t * LDX + jj]) = vp[j];
         }
     }
-    // rowsum(S_C * lambda_C), one wave per row.
-    for (int i = wave; i < D; i += 4) {
+    // rowsum(S_C * lambda_C): thread (row, part) sums a contiguous segment of the row, every
+    // load issued before the first use; the parts meet through LDS atomics.
+    {
+        constexpr int TPR = kBwdThreads / D;  // threads per row
+        constexpr int SEG = D / TPR;          // elements per thread
+        const int i = tid / TPR, part = tid % TPR;
+        f32x4_t xs[SEG / 4], xl[SEG / 4];
+#pragma unroll
+        for (int j = 0; j < SEG / 4; ++j) {
+            xs[j] = ld4(SC, size_t(i) * D + part * SEG + 4 * j);
+            xl[j] = ld4(lam, size_t(i) * D + part * SEG + 4 * j);
+        }
         float acc = 0.f;
 #pragma unroll
-        for (int j = lane; j < D; j += 64) acc = fmaf(SC[size_t(i) * D + j], lam[size_t(i) * D + j], acc);
-        acc = wave_sum(acc);
-        if (lane == 0) sRS[i] = acc;
+        for (int j = 0; j < SEG / 4; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) acc = fmaf(xs[j][q4], xl[j][q4], acc);
+        if (part == 0) sRS[i] = 0.f;
+        __syncthreads();
+        atomicAdd(&sRS[i], acc);
     }
     for (int i = tid; i < D; i += kBwdThreads) sDr[i] = 0.f;
     __syncthreads();
@@ -702,21 +715,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     }
     // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D].
     for (int it = wave; it < D / 16; it += 4) {
-        // This lane's B operands (row 16 it + lane % 16 of S0, then of lambda_C), each loaded
-        // in one batch.
+        // This lane's B operands (row 16 it + lane % 16 of S0, then of lambda_C), 16 bytes per
+        // load: contraction step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi.
         const int rr = lane & 15, kq = lane >> 4;
-        float bv[D / 4];
+        f32x4_t bv[D / 16];
 #pragma unroll
-        for (int m = 0; m < D / 4; ++m) bv[m] = S0[size_t(16 * it + rr) * D + 4 * m + kq];
+        for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(S0, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
             f32x4_t y1 = zero4(), y2 = zero4();
 #pragma unroll
-            for (int m = 0; m < D / 4; ++m) {
-                const int kk = 4 * m + kq;
-                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], bv[m], y1, 0, 0, 0);
-                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], bv[m], y2, 0, 0, 0);
-            }
+            for (int mo = 0; mo < D / 16; ++mo)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int kk = 16 * mo + 4 * kq + mi;
+                    y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], bv[mo][mi], y1, 0, 0, 0);
+                    y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], bv[mo][mi], y2, 0, 0, 0);
+                }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tt + 4 * (lane >> 4) + i;
@@ -728,13 +743,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             }
         }
 #pragma unroll
-        for (int m = 0; m < D / 4; ++m) bv[m] = lam[size_t(16 * it + rr) * D + 4 * m + kq];
+        for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(lam, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
             f32x4_t y3 = zero4();
 #pragma unroll
-            for (int m = 0; m < D / 4; ++m)
-                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + 4 * m + kq], bv[m], y3, 0, 0, 0);
+            for (int mo = 0; mo < D / 16; ++mo)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + 16 * mo + 4 * kq + mi],
+                                                              bv[mo][mi], y3, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tt + 4 * (lane >> 4) + i;
