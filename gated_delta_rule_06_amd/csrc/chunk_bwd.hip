@@ -880,7 +880,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
                     gq[e4] = ok ? ld(q, o) : 0.f;
                 }
                 f32x4_t cq = zero4(), cr = zero4(), dq4 = zero4(), dr4 = zero4();
-                for (int bs = 0; bs < bt; ++bs) {
+#pragma unroll
+                for (int bs = 0; bs < kNB - 1; ++bs) {
+                    if (bs >= bt) break;
                     f32x4_t yq = zero4(), yr = zero4();
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
@@ -916,13 +918,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int t = 16 * bt + 4 * kq + e4;
-                    // Pairs inside t's sub-block: s = t, t - 1, ... down to its start.
+                    // Pairs inside t's sub-block: s = t, t - 1, ... down to its start (a fixed
+                    // four-step loop; steps below the start add nothing).
                     float sq = 0.f, sr = 0.f, run = 1.f;
-                    for (int s4 = t; s4 >= (t & ~3); --s4) {
-                        const float ks = run * sK[s4 * LDH + ic];
-                        sq = fmaf(sOU[t * LDM + s4], ks, sq);
-                        sr = fmaf(sPU[t * LDM + s4], ks, sr);
-                        run *= sA[s4 * LDH + ic];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int s4 = t - u;
+                        const bool on = u <= (t & 3);
+                        const int sc = on ? s4 : t;
+                        const float ks = on ? run * sK[sc * LDH + ic] : 0.f;
+                        sq = fmaf(sOU[t * LDM + sc], ks, sq);
+                        sr = fmaf(sPU[t * LDM + sc], ks, sr);
+                        run *= sA[sc * LDH + ic];
                     }
                     const float fb = sF[t * LDH + ic], f4 = sF4[t * LDH + ic];
                     if (t < nval) {
@@ -948,7 +955,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
                     gx3[e4] = s4 < nval ? X3[tok0 + size_t(s4) * HD + ocol] : 0.f;
                 }
                 f32x4_t cw = zero4(), dw4 = zero4();
-                for (int bt = bs + 1; bt < kNB; ++bt) {
+#pragma unroll
+                for (int bt = 1; bt < kNB; ++bt) {
+                    if (bt <= bs) continue;
                     f32x4_t y = zero4();
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
@@ -982,12 +991,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int s4 = 16 * bs + 4 * kq + e4;
-                    // Pairs inside s's sub-block: t = s, s + 1, ... up to its end.
+                    // Pairs inside s's sub-block: t = s, s + 1, ... up to its end (a fixed
+                    // four-step loop; steps past the end add nothing).
                     float sw = 0.f, run = 1.f;
-                    for (int t = s4; t <= (s4 | 3); ++t) {
-                        sw = fmaf(sOU[t * LDM + s4], run * sQ[t * LDH + ic], sw);
-                        sw = fmaf(sPU[t * LDM + s4], run * sK[t * LDH + ic], sw);
-                        if (t < (s4 | 3)) run *= sA[(t + 1) * LDH + ic];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const bool on = u <= 3 - (s4 & 3);
+                        const int tc = on ? s4 + u : s4;
+                        const float wq = on ? run : 0.f;
+                        sw = fmaf(sOU[tc * LDM + s4], wq * sQ[tc * LDH + ic], sw);
+                        sw = fmaf(sPU[tc * LDM + s4], wq * sK[tc * LDH + ic], sw);
+                        run *= sA[(on && u < 3 - (s4 & 3) ? tc + 1 : tc) * LDH + ic];
                     }
                     if (s4 < nval) {
                         const size_t o = tok0 + size_t(s4) * HD + ocol;
