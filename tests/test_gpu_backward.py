@@ -89,6 +89,21 @@ def test_small_shapes(device, qkv, d, T):
     assert_grad_parity(got, ref, TOL[qkv], f"T={T} d={d} {qkv}")
 
 
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+@pytest.mark.parametrize("B,d", [(2, 128), (4, 64)])
+def test_wide_scan_tiles(device, qkv, B, d):
+    """Enough heads (B * H * d / 16 >= 256) for the reverse scan's 16-column tiles; the other
+    cases here run its 8-column tiles."""
+    T, H = 130, 16
+    inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv=qkv, seed=3000 + d)
+    rng = np.random.default_rng(d)
+    s0 = (rng.standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    do, dS = _cotangents(rng, B, T, H, d, qkv, with_ds=True)
+    got = gpu_bwd(inp, device, s0, do, dS, qkv)
+    ref = ref_bwd(inp, s0, do, dS)
+    assert_grad_parity(got, ref, TOL[qkv], f"B={B} H={H} T={T} d={d} {qkv} (16-column scan tiles)")
+
+
 def test_zero_length(device):
     """T = 0: the initial state's gradient is the final state's cotangent; dr is zero."""
     B, H, d = 2, 3, 64
