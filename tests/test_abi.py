@@ -121,6 +121,48 @@ def test_chunk_fwd_gated_rejects_bad_arguments(over, status):
     assert msg
 
 
+def _bwd_call(**over):
+    lib = muir.lib()
+    names = ["q", "k", "v", "a", "g", "e", "w", "r", "s0", "dout", "ds_out",
+             "dq", "dk", "dv", "dla", "dg", "de", "dw", "dr", "ds0"]
+    args = {n: fake(12 + i) for i, n in enumerate(names)}
+    # Sizes are DK and DV here: dk and dv name gradient buffers.
+    args.update(B=2, T=100, H=3, DK=64, DV=64, chunk=64, qkv=muir.MUIR_BF16, ws=fake(40),
+                wsb=muir.chunk_bwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16),
+                stream=None)
+    args.update(over)
+    st = lib.muir_chunk_bwd(*[args[n] for n in names], args["B"], args["T"], args["H"],
+                            args["DK"], args["DV"], args["chunk"], args["qkv"], args["ws"],
+                            args["wsb"], args["stream"])
+    return st, muir.last_error()
+
+
+def test_chunk_bwd_workspace_size():
+    ws = muir.chunk_bwd_workspace_size
+    assert ws(2, 100, 3, 64, 64, 64, muir.MUIR_BF16) > 0
+    assert ws(2, 100, 3, 64, 64, 64, muir.MUIR_F32) > ws(2, 100, 3, 64, 64, 64, muir.MUIR_BF16)
+    assert ws(2, 0, 3, 64, 64, 64, muir.MUIR_BF16) > 0  # the final-state adjoint still needs room
+    for bad in [(2, 100, 3, 64, 64, 128), (2, 100, 3, 32, 32, 64), (2, 100, 3, 64, 128, 64),
+                (0, 100, 3, 64, 64, 64), (2, -1, 3, 64, 64, 64)]:
+        assert ws(*bad, muir.MUIR_BF16) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(H=0), 2),
+    (dict(chunk=128), 3), (dict(DK=32, DV=32), 3), (dict(DK=64, DV=128), 3), (dict(qkv=5), 3),
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dla=None), 1),
+    (dict(r=None), 1), (dict(dr=None), 1),
+    (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=ctypes.c_void_p(BASE + 40 * STRIDE + 16)), 4),
+    (dict(q=ctypes.c_void_p(BASE + 12 * STRIDE + 8)), 2),
+    (dict(dq=fake(15)), 5), (dict(dq=fake(24)), 5), (dict(ds0=fake(20)), 5),
+    (dict(ws=fake(23)), 5), (dict(dr=fake(19)), 5),
+])
+def test_chunk_bwd_rejects_bad_arguments(over, status):
+    st, msg = _bwd_call(**over)
+    assert st == status, msg
+    assert msg
+
+
 def test_scan_gated_requires_the_gate():
     lib = muir.lib()
     st = lib.muir_chunk_fwd_scan_gated(fake(2), fake(5), fake(6), None, None, fake(9), None, 2,
