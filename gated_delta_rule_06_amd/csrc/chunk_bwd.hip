@@ -20,18 +20,21 @@
 //   a * dL/da at token tau = sum_{t>=tau in chunk} [q_hat*dq_hat + k*dk_read - k*dk_write]_t
 //                            + rowsum(S_C * lambda_C)
 //
-// No decay is ever divided by: cross-block decays are products of factors in (0, 1] split at
-// 16-token block boundaries, and decays inside a block or along one channel are running
-// products.
+// No decay is ever divided by. A pair's decay Gamma_ts is split into factors in (0, 1] at
+// 16-token block boundaries (prefix of t's block, whole blocks between, suffix of s's block),
+// inside one block at 4-token sub-block boundaries the same way, and inside one sub-block it is a
+// direct product of at most three factors. The split forms make every decayed pair sum a
+// product on the fp32 matrix cores, one per block pair or per sub-block gap.
 //
 // Kernels, in launch order (after the forward's prepare and its scan, which also writes u and
 // the chunk start states):
 //   bwd_prepare_kernel  one workgroup per (b, h, chunk): K*beta, K*gamma and Q_hat*gamma (the
-//                       last two channel-major), gamma_C, M and P transposed (fp32 matrix
-//                       cores for the cross-block tiles), and p.
+//                       last two channel-major), gamma_C, M and P transposed, and p.
 //   bwd_scan_kernel     one workgroup per (b, h, 16 value columns), chunks in reverse: the
 //                       transposed triangular solve, the adjoint carry, dv, dw, de.
-//   bwd_grads_kernel    one workgroup per (b, h, chunk): dq, dk, dg and a * dL/da.
+//   bwd_grads_kernel    one workgroup per (b, h, chunk): O U^T, dP U^T and the state products,
+//                       then the decayed pair sums for dq_hat and dk, then dq, dk, dg and
+//                       a * dL/da (a reverse cumulative sum per channel).
 //   bwd_dr_kernel       dr summed over batch and chunks.
 #include <hip/hip_runtime.h>
 
@@ -90,7 +93,6 @@ template <int D> struct PrepBwdLds {
     static constexpr int LDM = kC + 1;
     static constexpr int DH = 64;
     static constexpr int LDH = DH + 1;
-    static constexpr int NPAIR = kNB * (kNB - 1) / 2;
     static constexpr int MP = 2 * kC * LDM;
     static constexpr int PASS = 5 * kC * LDH + 16 * DH;
     static constexpr int KGL = kC * (D + 4);
