@@ -1016,34 +1016,43 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         }
     }
     __syncthreads();
-    if (tid < D) {
-        const int i = tid;
-        drp[slot * D + i] = sDr[i];
-        const float rs = sRS[i];
-        // Log-decay gradient: reverse cumulative sum over the chunk, 16 tokens per batch of
-        // loads.
-        float cum = 0.f;
-        for (int t1 = C; t1 > 0; t1 -= 16) {
-            float x3[16], la[16], dkv[16], kv[16];
+    {
+        // Log-decay gradient: a reverse cumulative sum over the chunk per channel. Thread (part,
+        // channel) takes TP consecutive tokens: suffix sums inside its part, then the totals of
+        // the later parts (through LDS) and rowsum(S_C * lambda_C).
+        constexpr int NP = kBwdThreads / D, TP = C / NP;
+        const int i = tid % D, part = tid / D;
+        if (part == 0) drp[slot * D + i] = sDr[i];
+        float *sTot = un;  // [NP][D]; the pass arrays are no longer read
+        float x3[TP], la[TP], dkv[TP], kv[TP];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int t = t1 - 1 - u;
+        for (int u = 0; u < TP; ++u) {
+            const int t = part * TP + u;
+            const size_t o = tok0 + size_t(t) * HD + i;
+            const bool ok = t < nval;
+            x3[u] = ok ? X3[o] : 0.f;
+            la[u] = ok ? dla[o] : 0.f;
+            dkv[u] = ok ? dk[o] : 0.f;
+            kv[u] = ok ? ld(k, o) : 0.f;
+        }
+        float cum[TP];
+        float run = 0.f;
+#pragma unroll
+        for (int u = TP - 1; u >= 0; --u) {
+            run += la[u] - kv[u] * x3[u];
+            cum[u] = run;
+        }
+        sTot[part * D + i] = run;
+        __syncthreads();
+        float off = sRS[i];
+        for (int p2 = part + 1; p2 < NP; ++p2) off += sTot[p2 * D + i];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const int t = part * TP + u;
+            if (t < nval) {
                 const size_t o = tok0 + size_t(t) * HD + i;
-                const bool ok = t < nval;
-                x3[u] = ok ? X3[o] : 0.f;
-                la[u] = ok ? dla[o] : 0.f;
-                dkv[u] = ok ? dk[o] : 0.f;
-                kv[u] = ok ? ld(k, o) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int t = t1 - 1 - u;
-                cum += la[u] - kv[u] * x3[u];
-                if (t < nval) {
-                    const size_t o = tok0 + size_t(t) * HD + i;
-                    dla[o] = cum + rs;
-                    dk[o] = dkv[u] + x3[u];
-                }
+                dla[o] = cum[u] + off;
+                dk[o] = dkv[u] + x3[u];
             }
         }
     }
