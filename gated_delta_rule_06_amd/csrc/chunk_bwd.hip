@@ -609,14 +609,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 // [C][D + 4] (products) and k, a, q_hat channel-major [D][C + 1] (decayed sums).
 // ------------------------------------------------------------------------------------------
 template <int D> struct GradLds {
-    static constexpr int LDM = kC + 1, LDX = D + 4, LDH = 65, DH = 64;
+    // Rows of DH = 16 floats: a matrix-core step reads 4 rows x 16 channels, one bank each.
+    static constexpr int LDM = kC + 1, DH = 16, LDH = DH;
     static constexpr int OUPU = 2 * kC * LDM;
-    static constexpr int P1 = 3 * kC * LDX;
-    // Per 64-channel pass: a, k, q_hat, F, R (16-token blocks), F4, R4 (4-token sub-blocks)
-    // [C][65]; products of whole blocks between (6 pairs), of whole sub-blocks (16), of the
-    // blocks before and after each block (4 + 4), per channel.
+    // Per 16-channel pass: a, k, q_hat, F, R (16-token blocks), F4, R4 (4-token sub-blocks)
+    // [C][16]; products of whole blocks between (6 pairs), of whole sub-blocks (16), of the
+    // blocks before and after each block (4 + 4), per channel. About 67 KB in all for d = 128,
+    // so two workgroups share a compute unit.
     static constexpr int P2 = 7 * kC * LDH + (6 + 16 + 4 + 4) * DH;
-    static constexpr int FLOATS = OUPU + 2 * D + (P1 > P2 ? P1 : P2) + kNB * DH;
+    static constexpr int FLOATS = OUPU + 2 * D + (P2 > kBwdThreads ? P2 : kBwdThreads) + kNB * DH;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -629,13 +630,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg,
     float *__restrict__ dla, float *__restrict__ drp, int T, int H, int nchunks) {
     using L = GradLds<D>;
-    constexpr int C = kC, LDM = L::LDM, LDX = L::LDX, LDH = L::LDH, DH = L::DH;
+    constexpr int C = kC, LDM = L::LDM, LDH = L::LDH, DH = L::DH;
     extern __shared__ float lds[];
     float *sOU = lds, *sPU = lds + C * LDM;
     float *sRS = lds + L::OUPU;  // rowsum(S_C * lambda_C) per channel
     float *sDr = sRS + D;        // sum over tokens of g * q * dq_hat per channel
     float *un = sDr + D;
-    float *sU = un, *sdO = un + C * LDX, *sdP = un + 2 * C * LDX;
     float *sA = un, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH, *sR = sF + C * LDH,
           *sF4 = sR + C * LDH, *sR4 = sF4 + C * LDH, *sMid = sR4 + C * LDH, *sB4 = sMid + 6 * DH,
           *sGb = sB4 + 16 * DH, *sBa = sGb + 4 * DH;
@@ -653,29 +653,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     const float *SC = S0 + size_t(D) * D;
     const float *lam = lamC + slot * D * D;
 
-    {
-        constexpr int N4 = C * D / 4 / kBwdThreads;
-        f32x4_t vu[N4], vo[N4], vp[N4];
+    // Rows of U, dO and dP = -e * dU as matrix-core operands straight from memory: 16 bytes per
+    // load, contraction step (mo, mi) of lane group kq taking k = 16 mo + 4 kq + mi. Tokens past
+    // the sequence read as zero.
+    const int rr = lane & 15, kq = lane >> 4;
+    auto rowU = [&](int t, f32x4_t (&x)[D / 16]) {
 #pragma unroll
-        for (int j = 0; j < N4; ++j) {
-            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, jj = e0 % D;
-            const size_t o = tok0 + size_t(t) * HD + jj;
-            if (t < nval) {
-                vu[j] = ld4(U, o);
-                vo[j] = ld4(dout, o);
-                vp[j] = -ld4(e, o) * ld4(dU, o);
-            } else {
-                vu[j] = vo[j] = vp[j] = zero4();
-            }
-        }
+        for (int mo = 0; mo < D / 16; ++mo)
+            x[mo] = t < nval ? ld4(U, tok0 + size_t(t) * HD + 16 * mo + 4 * kq) : zero4();
+    };
+    auto rowO = [&](int t, f32x4_t (&x)[D / 16]) {
 #pragma unroll
-        for (int j = 0; j < N4; ++j) {
-            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / D, jj = e0 % D;
-            *reinterpret_cast<f32x4_t *>(&sU[t * LDX + jj]) = vu[j];
-            *reinterpret_cast<f32x4_t *>(&sdO[t * LDX + jj]) = vo[j];
-            *reinterpret_cast<f32x4_t *>(&sdP[t * LDX + jj]) = vp[j];
+        for (int mo = 0; mo < D / 16; ++mo)
+            x[mo] = t < nval ? ld4(dout, tok0 + size_t(t) * HD + 16 * mo + 4 * kq) : zero4();
+    };
+    auto rowP = [&](int t, f32x4_t (&x)[D / 16]) {
+#pragma unroll
+        for (int mo = 0; mo < D / 16; ++mo) {
+            const size_t o = tok0 + size_t(t) * HD + 16 * mo + 4 * kq;
+            x[mo] = t < nval ? -ld4(e, o) * ld4(dU, o) : zero4();
         }
-    }
+    };
     // rowsum(S_C * lambda_C): thread (row, part) sums a contiguous segment of the row, every
     // load issued before the first use; the parts meet through LDS atomics.
     {
@@ -705,9 +703,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         const int mat = job / 10, tl = job % 10;
         const int bt = tl < 1 ? 0 : (tl < 3 ? 1 : (tl < 6 ? 2 : 3));
         const int bs = tl - bt * (bt + 1) / 2;
-        const float *sX = mat == 0 ? sdO : sdP;
-        const f32x4_t y = mm16<D>([&](int rr, int kk) { return sX[(16 * bt + rr) * LDX + kk]; },
-                                  [&](int cc, int kk) { return sU[(16 * bs + cc) * LDX + kk]; }, zero4());
+        f32x4_t xa[D / 16], xb[D / 16];
+        if (mat == 0) rowO(16 * bt + rr, xa);
+        else rowP(16 * bt + rr, xa);
+        rowU(16 * bs + rr, xb);
+        f32x4_t y = zero4();
+#pragma unroll
+        for (int mo = 0; mo < D / 16; ++mo)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) y = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[mo][mi], xb[mo][mi], y, 0, 0, 0);
         float *dst = mat == 0 ? sOU : sPU;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -716,60 +720,64 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         }
     }
     // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D].
-    for (int it = wave; it < D / 16; it += 4) {
-        // This lane's B operands (row 16 it + lane % 16 of S0, then of lambda_C), 16 bytes per
-        // load: contraction step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi.
-        const int rr = lane & 15, kq = lane >> 4;
-        f32x4_t bv[D / 16];
+    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D]; wave w owns the
+    // channel tiles w, w + 4, ... for every token tile.
+#pragma unroll 1
+    for (int tt = 0; tt < kNB; ++tt) {
+        f32x4_t xo[D / 16], xp[D / 16];
+        rowO(16 * tt + rr, xo);
+        rowP(16 * tt + rr, xp);
+        for (int it = wave; it < D / 16; it += 4) {
+            f32x4_t bv[D / 16];
 #pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(S0, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
-#pragma unroll
-        for (int tt = 0; tt < kNB; ++tt) {
+            for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(S0, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
             f32x4_t y1 = zero4(), y2 = zero4();
 #pragma unroll
             for (int mo = 0; mo < D / 16; ++mo)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    const int kk = 16 * mo + 4 * kq + mi;
-                    y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[(16 * tt + rr) * LDX + kk], bv[mo][mi], y1, 0, 0, 0);
-                    y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdP[(16 * tt + rr) * LDX + kk], bv[mo][mi], y2, 0, 0, 0);
+                    y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bv[mo][mi], y1, 0, 0, 0);
+                    y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bv[mo][mi], y2, 0, 0, 0);
                 }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tt + 4 * (lane >> 4) + i;
+                const int t = 16 * tt + 4 * kq + i;
                 if (t < nval) {
-                    const size_t o = tok0 + size_t(t) * HD + 16 * it + (lane & 15);
+                    const size_t o = tok0 + size_t(t) * HD + 16 * it + rr;
                     dq[o] = y1[i];
                     dk[o] = y2[i];
                 }
             }
         }
+    }
+#pragma unroll 1
+    for (int tt = 0; tt < kNB; ++tt) {
+        f32x4_t xu[D / 16];
+        rowU(16 * tt + rr, xu);
+        for (int it = wave; it < D / 16; it += 4) {
+            f32x4_t bv[D / 16];
 #pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(lam, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
-#pragma unroll
-        for (int tt = 0; tt < kNB; ++tt) {
+            for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(lam, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
             f32x4_t y3 = zero4();
 #pragma unroll
             for (int mo = 0; mo < D / 16; ++mo)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
-                    y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * tt + rr) * LDX + 16 * mo + 4 * kq + mi],
-                                                              bv[mo][mi], y3, 0, 0, 0);
+                    y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bv[mo][mi], y3, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tt + 4 * (lane >> 4) + i;
-                if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + (lane & 15)] = y3[i];
+                const int t = 16 * tt + 4 * kq + i;
+                if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + rr] = y3[i];
             }
         }
     }
     __syncthreads();
     const float *rh = r + size_t(h) * D;
-    const int rr = lane & 15, kq = lane >> 4;
-    // Decayed sums over token pairs, per 64-channel pass, on the matrix cores. With the pivots
+    // Decayed sums over token pairs, per 16-channel pass, on the matrix cores. With the pivots
     // of the prepare kernel, Gamma_ts = F_t * mid * R_s across 16-token blocks and
     // F4_t * mid4 * R4_s across 4-token sub-blocks of one block; pairs inside one sub-block are
     // direct products. Jobs: kind 0 (dq_hat and the read part of dk, rows = t) and kind 1 (the
-    // write part of dk, rows = s), 16 tiles each; wave w takes jobs w, w + 4, ...
+    // write part of dk, rows = s), one 16-row block each; wave w takes jobs w and w + 4.
     for (int p0 = 0; p0 < D; p0 += DH) {
         if (p0 > 0) __syncthreads();
         {
@@ -791,16 +799,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
 #pragma unroll
             for (int j = 0; j < N4; ++j) {
                 const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    sA[t * LDH + ii + q4] = va[j][q4];
-                    sK[t * LDH + ii + q4] = vk[j][q4];
-                    sQ[t * LDH + ii + q4] = vq[j][q4];
-                }
+                *reinterpret_cast<f32x4_t *>(&sA[t * LDH + ii]) = va[j];
+                *reinterpret_cast<f32x4_t *>(&sK[t * LDH + ii]) = vk[j];
+                *reinterpret_cast<f32x4_t *>(&sQ[t * LDH + ii]) = vq[j];
             }
         }
         __syncthreads();
-        {
+        if (tid < DH * kNB) {
             // Thread (channel, 16-token block): prefix and suffix products inside the block
             // and inside its four sub-blocks.
             const int ii = tid % DH, bb = tid / DH;
@@ -863,8 +868,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             }
         }
         __syncthreads();
-        for (int job = wave; job < 32; job += 4) {
-            const int kind = job / 16, rb = (job % 16) / 4, it = job % 4;
+        for (int job = wave; job < 2 * kNB; job += 4) {
+            const int kind = job / kNB, rb = job % kNB, it = 0;
             const int ic = 16 * it + rr;  // this lane's B / output column, within the pass
             const size_t ocol = size_t(p0 + ic);
             if (kind == 0) {
