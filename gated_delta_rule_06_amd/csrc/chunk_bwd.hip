@@ -131,21 +131,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     // Cross-block tiles of M and P: pair p = (bt, bs), bs < bt, pair index bt (bt - 1) / 2 + bs;
     // tile job j < 12: matrix j / 6 (0: M, 1: P), pair j % 6. Wave w owns jobs w, w + 4, w + 8.
     f32x4_t acc[3] = {zero4(), zero4(), zero4()};
-    // Diagonal 16x16 tiles, cross-sub-block entries: wave w owns tile jobs w and w + 4 (job:
-    // matrix j / 4, block j % 4), accumulated over the passes.
+    // Diagonal 16x16 tiles: wave w owns tile jobs w and w + 4 (job: matrix j / 4, block j % 4),
+    // accumulated over the passes.
     f32x4_t dacc[2] = {zero4(), zero4()};
-    // Entries (t, s), s <= t, inside one 4-token sub-block: 16 sub-blocks x 10; thread tid < 160
-    // owns one.
-    constexpr int NSUB = (kC / 4) * 10;
-    int st_ = 0, ss_ = 0;
-    if (tid < NSUB) {
-        const int sb = tid / 10;
-        int rem = tid % 10, tl = 0;
-        while (rem > tl) { ++tl; rem -= tl; }
-        st_ = 4 * sb + tl;
-        ss_ = 4 * sb + rem;
-    }
-    float sM_ = 0.f, sP_ = 0.f;
 
     for (int p0 = 0; p0 < D; p0 += DH) {
         __syncthreads();
@@ -275,46 +263,48 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
             const float *sX = mat == 0 ? sK : sQ;
             const int rr = lane & 15, kq = lane >> 4;
             const int us = rr >> 2;  // the B row (column s = 16 bb + rr) sub-block in the block
-            f32x4_t y[3] = {zero4(), zero4(), zero4()};
+            // Inside one sub-block the split repeats at its halves: t in the upper half, s in
+            // the lower takes (a from the half's start through t) x (a after s to the half's
+            // end); t = s + 1 in one half takes a_t; t = s takes 1.
+            const int sub = rr & 3;  // the A row's (and B column's) place in its sub-block
+            f32x4_t y[6] = {zero4(), zero4(), zero4(), zero4(), zero4(), zero4()};
 #pragma unroll 4
             for (int m = 0; m < DH / 4; ++m) {
                 const int kk = 4 * m + kq;
                 const int ta = 16 * bb + rr;
-                const float av = sX[ta * LDH + kk] * sF[ta * LDH + kk];
-                const float b1 = sK[ta * LDH + kk] * sR[ta * LDH + kk];
+                const float xt = sX[ta * LDH + kk], ks = sK[ta * LDH + kk];
+                const float at = sA[ta * LDH + kk];
+                const float aprev = sA[(sub > 0 ? ta - 1 : ta) * LDH + kk];
+                const float anext = sA[(sub < 3 ? ta + 1 : ta) * LDH + kk];
+                const float av = xt * sF[ta * LDH + kk];
+                const float b1 = ks * sR[ta * LDH + kk];
                 const int u0 = 4 * bb + us;  // s's sub-block in the chunk
                 const float m1 = us + 1 < 4 ? sB4[(u0 + 1) * DH + kk] : 0.f;
                 const float m2 = us + 2 < 4 ? sB4[(u0 + 2) * DH + kk] : 0.f;
                 const float b2 = b1 * m1, b3 = b2 * m2;
+                const float f2 = sub == 2 ? at : (sub == 3 ? aprev * at : 0.f);
+                const float r2 = sub == 0 ? anext : (sub == 1 ? 1.f : 0.f);
                 y[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, y[0], 0, 0, 0);
                 y[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b2, y[1], 0, 0, 0);
                 y[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b3, y[2], 0, 0, 0);
+                y[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt * f2, ks * r2, y[3], 0, 0, 0);
+                y[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt * at, ks, y[4], 0, 0, 0);
+                y[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, ks, y[5], 0, 0, 0);
             }
             // Output lane l: rows 4 (l / 16) + i (sub-block l / 16), column l % 16.
-            const int ut = lane >> 4, usc = (lane & 15) >> 2;
+            const int ut = lane >> 4, sc = lane & 15, usc = sc >> 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const int tr = 4 * ut + i;  // row within the block
                 const int gap = ut - usc;
-                dacc[j][i] += gap == 1 ? y[0][i] : (gap == 2 ? y[1][i] : (gap == 3 ? y[2][i] : 0.f));
-            }
-        }
-        // Entries inside one sub-block: decay over s < tau <= t, at most 3 factors.
-        if (tid < NSUB) {
-            const int t = st_, s4 = ss_;
-            float m = 0.f, pp = 0.f;
-            for (int ii = 0; ii < DH; ++ii) {
-                float gm = 1.f;
-#pragma unroll
-                for (int uu = 1; uu < 4; ++uu) {
-                    const float av = sA[((s4 & ~3) + uu) * LDH + ii];
-                    gm *= ((s4 & 3) < uu && uu <= (t & 3)) ? av : 1.f;
+                float add = gap == 1 ? y[0][i] : (gap == 2 ? y[1][i] : (gap == 3 ? y[2][i] : 0.f));
+                if (gap == 0) {
+                    if ((tr & 3) >= 2 && (sc & 3) < 2) add = y[3][i];
+                    else if ((tr & 1) == 1 && sc == tr - 1) add = y[4][i];
+                    else if (sc == tr && mat == 1) add = y[5][i];
                 }
-                const float ks = gm * sK[s4 * LDH + ii];
-                m = fmaf(sK[t * LDH + ii], ks, m);
-                pp = fmaf(sQ[t * LDH + ii], ks, pp);
+                dacc[j][i] += add;
             }
-            if (s4 < t) sM_ += m;
-            sP_ += pp;
         }
     }
     __syncthreads();
@@ -334,15 +324,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
         const int job = wave + 4 * j;
         const int mat = job / 4, bb = job % 4;
         float *dst = mat == 0 ? sM : sP;
-        const int ut = lane >> 4, usc = (lane & 15) >> 2;
-        if (ut > usc) {
+        const int ut = lane >> 4, sc = lane & 15;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * bb + 4 * ut + i) * LDM + 16 * bb + (lane & 15)] = dacc[j][i];
-        }
-    }
-    if (tid < NSUB) {
-        if (ss_ < st_) sM[st_ * LDM + ss_] = sM_;
-        sP[st_ * LDM + ss_] = sP_;
+        for (int i = 0; i < 4; ++i)
+            if (sc <= 4 * ut + i) dst[(16 * bb + 4 * ut + i) * LDM + 16 * bb + sc] = dacc[j][i];
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
