@@ -22,9 +22,10 @@
 //
 // No decay is ever divided by. A pair's decay Gamma_ts is split into factors in (0, 1] at
 // 16-token block boundaries (prefix of t's block, whole blocks between, suffix of s's block),
-// inside one block at 4-token sub-block boundaries the same way, and inside one sub-block it is a
-// direct product of at most three factors. The split forms make every decayed pair sum a
-// product on the fp32 matrix cores, one per block pair or per sub-block gap.
+// inside one block at 4-token sub-block boundaries the same way, and inside one sub-block at its
+// halves (the prepare) or as a direct product of at most three factors (the gradient kernel). The
+// split forms make the decayed pair sums products on the fp32 matrix cores, one per block pair,
+// sub-block gap or half split.
 //
 // Kernels, in launch order (after the forward's prepare and its scan, which also writes u and
 // the chunk start states):
