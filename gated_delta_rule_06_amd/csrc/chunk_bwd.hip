@@ -705,55 +705,70 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             dst[t * LDM + s] = (mat == 0 ? s <= t : s < t) ? y[i] : 0.f;
         }
     }
-    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D].
-    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D]; wave w owns the
-    // channel tiles w, w + 4, ... for every token tile.
-#pragma unroll 1
-    for (int tt = 0; tt < kNB; ++tt) {
-        f32x4_t xo[D / 16], xp[D / 16];
-        rowO(16 * tt + rr, xo);
-        rowP(16 * tt + rr, xp);
-        for (int it = wave; it < D / 16; it += 4) {
-            f32x4_t bv[D / 16];
+    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D]. Wave w owns the
+    // channel tiles w + 4 j; its rows of S0 (then lambda_C) stay in registers over the four
+    // token tiles, so each state is read from memory once per chunk.
+    constexpr int NTW = D / 64;  // channel tiles per wave
+    {
+        f32x4_t bv[NTW][D / 16];
 #pragma unroll
-            for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(S0, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
-            f32x4_t y1 = zero4(), y2 = zero4();
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int mo = 0; mo < D / 16; ++mo)
+                bv[j][mo] = ld4(S0, size_t(16 * (wave + 4 * j) + rr) * D + 16 * mo + 4 * kq);
+#pragma unroll 1
+        for (int tt = 0; tt < kNB; ++tt) {
+            f32x4_t xo[D / 16], xp[D / 16];
+            rowO(16 * tt + rr, xo);
+            rowP(16 * tt + rr, xp);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bv[mo][mi], y1, 0, 0, 0);
-                    y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bv[mo][mi], y2, 0, 0, 0);
-                }
+            for (int j = 0; j < NTW; ++j) {
+                const int it = wave + 4 * j;
+                f32x4_t y1 = zero4(), y2 = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tt + 4 * kq + i;
-                if (t < nval) {
-                    const size_t o = tok0 + size_t(t) * HD + 16 * it + rr;
-                    dq[o] = y1[i];
-                    dk[o] = y2[i];
+                for (int mo = 0; mo < D / 16; ++mo)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bv[j][mo][mi], y1, 0, 0, 0);
+                        y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bv[j][mo][mi], y2, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tt + 4 * kq + i;
+                    if (t < nval) {
+                        const size_t o = tok0 + size_t(t) * HD + 16 * it + rr;
+                        dq[o] = y1[i];
+                        dk[o] = y2[i];
+                    }
                 }
             }
         }
     }
-#pragma unroll 1
-    for (int tt = 0; tt < kNB; ++tt) {
-        f32x4_t xu[D / 16];
-        rowU(16 * tt + rr, xu);
-        for (int it = wave; it < D / 16; it += 4) {
-            f32x4_t bv[D / 16];
+    {
+        f32x4_t bv[NTW][D / 16];
 #pragma unroll
-            for (int mo = 0; mo < D / 16; ++mo) bv[mo] = ld4(lam, size_t(16 * it + rr) * D + 16 * mo + 4 * kq);
-            f32x4_t y3 = zero4();
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int mo = 0; mo < D / 16; ++mo)
+                bv[j][mo] = ld4(lam, size_t(16 * (wave + 4 * j) + rr) * D + 16 * mo + 4 * kq);
+#pragma unroll 1
+        for (int tt = 0; tt < kNB; ++tt) {
+            f32x4_t xu[D / 16];
+            rowU(16 * tt + rr, xu);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bv[mo][mi], y3, 0, 0, 0);
+            for (int j = 0; j < NTW; ++j) {
+                const int it = wave + 4 * j;
+                f32x4_t y3 = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tt + 4 * kq + i;
-                if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + rr] = y3[i];
+                for (int mo = 0; mo < D / 16; ++mo)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi)
+                        y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bv[j][mo][mi], y3, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tt + 4 * kq + i;
+                    if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + rr] = y3[i];
+                }
             }
         }
     }
