@@ -10,6 +10,7 @@ import shutil
 import subprocess
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -34,24 +35,43 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source into ``libmuir.so`` (always recompiles); returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *HIP_FLAGS,
-           *extra_flags, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    t0 = time.time()
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless.
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return res.returncode, err
+
+
+def build(verbose: bool = False, extra_flags=(), jobs: int | None = None) -> str:
+    """Compile every source into ``libmuir.so`` (always recompiles); returns its path.
+
+    Each source is compiled to an object of its own, in parallel, then linked."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *HIP_FLAGS, *extra_flags]
+    cmds, objs = [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *flags, "-c", "-o", obj, os.path.join(CSRC, s)])
+    t0 = time.time()
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), file=sys.stderr)
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, err), c in zip(results, cmds):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) on {c[-1]}:\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)

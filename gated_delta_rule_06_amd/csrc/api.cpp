@@ -409,6 +409,14 @@ muir_status_t muir_chunk_fwd_lowrank(const void *q, const void *k, const void *v
         for (const Range &y : outs)
             if (overlaps(x, y)) return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, y.name, x.name);
     }
+    // validate() checked s0 and r against the base forward's workspace only; the gate kernel
+    // writes e and w past it, up to `need`. s0 may still be s_out (the state in place).
+    const Range rs0 = range("s0", s0, static_cast<size_t>(B) * H * dk * dv * 4);
+    const Range rr = range("r", r, static_cast<size_t>(H) * dk * 4);
+    for (const Range &x : {rs0, rr})
+        for (int i = 0; i < 2; ++i)
+            if (overlaps(x, outs[i]))
+                return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, outs[i].name, x.name);
     if (T == 0) {
         if (!s_out) return ok();
         return check_hip(muir::launch_chunk_scan(v, nullptr, nullptr, nullptr, s0, o, s_out, B, T, H,

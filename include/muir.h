@@ -11,10 +11,11 @@
  *                                       gate e_t, then write under the write gate w_t
  *     o_t <- S^T (r * g_t * q_t)        matched-filter readout: static row scale r
  *                                       times the dynamic query gate g_t
- *   Update order: the Muir abstract ("Full text" on the Astral Feed page): gated
- *   delta-rule models decay the state and erase its prediction for an incoming key
- *   before writing a new value, with channel-wise decay and decoupled erase and write
- *   gates. Readout: openai-hub news page, section on matched-filter readout (a static
+ *   Update order (Muir abstract, "Full text" on the Astral Feed page): each token
+ *   first scales the state down by its per-row decay, then removes what the decayed
+ *   state predicts for the new key (per value channel, under the erase gate), then adds
+ *   the new key's gated value (the write gate is separate from the erase gate), and the
+ *   read comes last. Readout: openai-hub news page, section on matched-filter readout (a static
  *   per-row scale from each row's expected energy plus per-token query modulation),
  *   and the liuch.name summary, first bullet (inverse fractional power law plus
  *   per-token query modulation).

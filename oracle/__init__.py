@@ -70,6 +70,9 @@ def load():
             fn.argtypes = [ctypes.c_int] * 5 + [ptr] * 11 + [ctypes.c_int]
             fn.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_grads_f64.argtypes = [ctypes.c_int] * 5 + [dp] * 21 + [ctypes.c_int]
+        lib.oracle_grads_f64.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 

@@ -44,7 +44,7 @@ import numpy as np
 
 NAMES = ("q", "k", "v", "a", "g", "e", "w")
 
-__all__ = ["grads_autograd", "grads_adjoint", "grads_chunked", "loss"]
+__all__ = ["grads_autograd", "grads_adjoint", "grads_chunked", "grads_c", "loss"]
 
 
 def _heads(x, b, h):
@@ -168,6 +168,28 @@ def grads_adjoint(q, k, v, a, g, e, w, r, s0, do, dS):
                 lam = ab[t][:, None] * dSm
             out["s0"][b, h] = lam
             _finish(out, b, h, qb, gb, rh, dqh)
+    return out
+
+
+def grads_c(q, k, v, a, g, e, w, r, s0, do, dS, *, threads=None):
+    """The token adjoint of ``grads_adjoint`` in C (``oracle_grads_f64`` in recurrence.c),
+    fp64, OpenMP over (b, h), with the forward's states checkpointed every 128 tokens and
+    recomputed per segment, so long sequences fit in memory. Same arguments and result."""
+    import ctypes
+    from . import load, max_threads
+    lib = load()
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    f = lambda x: None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+    ins = [f(x) for x in (q, k, v, a, g, e, w, r, s0, do, dS)]
+    out = _empty(q, v, r, s0)
+    ptr = lambda x: None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    outs = [out[n] for n in ("q", "k", "v", "a", "la", "g", "e", "w", "r", "s0")]
+    nthreads = max_threads() if threads is None else int(threads)
+    rc = lib.oracle_grads_f64(B, T, H, dk, dv, *[ptr(x) for x in ins], *[ptr(x) for x in outs],
+                              nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle backward failed with code {rc}")
     return out
 
 

@@ -273,6 +273,38 @@ def test_lowrank_gates_skips_unrequested_gates():
     assert st == 0, msg
 
 
+def _lowrank_fwd_call(**over):
+    lib = muir.lib()
+    B, T, H, d, C = 2, 100, 3, 64, 64
+    wsb = lib.muir_chunk_fwd_lowrank_workspace_size(B, T, H, d, d, C)
+    args = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), Ua=fake(4), Ue=fake(5), Uw=fake(6),
+                Ug=fake(7), ca=fake(8), ce=fake(9), cw=fake(10), cg=fake(11), r=fake(12),
+                s0=fake(13), o=fake(14), s_out=fake(15), B=B, T=T, H=H, dk=d, dv=d, chunk=C,
+                qkv=muir.MUIR_BF16, ws=fake(16), wsb=wsb, stream=None)
+    args.update(over)
+    st = lib.muir_chunk_fwd_lowrank(*[args[k] for k in (
+        "q", "k", "v", "z", "Ua", "Ue", "Uw", "Ug", "ca", "ce", "cw", "cg", "r", "s0", "o",
+        "s_out", "B", "T", "H", "dk", "dv", "chunk", "qkv", "ws", "wsb", "stream")])
+    return st, muir.last_error()
+
+
+def test_lowrank_fwd_rejects_state_or_scale_in_the_gate_tail():
+    """The low-rank call's workspace is the forward's plus a tail where the gate kernel writes
+    e and w; an s0 or r placed in that tail must be refused, not overwritten."""
+    lib = muir.lib()
+    base = muir.chunk_fwd_workspace_size(2, 100, 3, 64, 64, 64, muir.MUIR_BF16)
+    full = lib.muir_chunk_fwd_lowrank_workspace_size(2, 100, 3, 64, 64, 64)
+    assert full > base
+    tail = ctypes.c_void_p(BASE + 16 * STRIDE + ((base + 255) // 256) * 256)
+    st, msg = _lowrank_fwd_call(s0=tail)
+    assert st == 5 and "s0" in msg, msg
+    st, msg = _lowrank_fwd_call(r=tail)
+    assert st == 5 and "r" in msg, msg
+    # The state updated in place (s0 == s_out) stays allowed.
+    st, msg = _lowrank_fwd_call(s0=fake(15), wsb=1)
+    assert st == 4, msg
+
+
 def _decode_call(**over):
     lib = muir.lib()
     args = dict(q=fake(0), k=fake(1), v=fake(2), a=fake(3), g=fake(4), e=fake(5), w=fake(6),

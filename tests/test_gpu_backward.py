@@ -45,8 +45,9 @@ def gpu_bwd(inp, device, s0, do, dS, qkv):
 
 
 def ref_bwd(inp, s0, do, dS, heads=None):
-    """fp64 oracle gradients (optionally of a subset of heads, which is exact: heads are
-    independent and dr is per head)."""
+    """fp64 oracle gradients, from the C token adjoint (pinned against autograd and finite
+    differences on the CPU); optionally of a subset of heads, which is exact: heads are
+    independent and dr is summed per head."""
     sl = (lambda x: x) if heads is None else (lambda x: x[:, :, heads])
     args = [sl(np.asarray(inp[n], np.float64)) for n in ("q", "k", "v", "a", "g", "e", "w")]
     r = np.asarray(inp["r"], np.float64)
@@ -54,7 +55,7 @@ def ref_bwd(inp, s0, do, dS, heads=None):
     B, T, H, d = args[0].shape
     s0_ = None if s0 is None else (s0 if heads is None else s0[:, heads])
     dS_ = np.zeros((B, H, d, d)) if dS is None else (dS if heads is None else dS[:, heads])
-    return obw.grads_adjoint(*args, r, s0_, sl(do), dS_)
+    return obw.grads_c(*args, r, s0_, sl(do), dS_)
 
 
 def assert_grad_parity(got, ref, tol, what, heads=None):
@@ -92,8 +93,10 @@ def test_small_shapes(device, qkv, d, T):
 @pytest.mark.parametrize("qkv", ["f32", "bf16"])
 @pytest.mark.parametrize("B,d", [(2, 128), (4, 64)])
 def test_wide_scan_tiles(device, qkv, B, d):
-    """Enough heads (B * H * d / 16 >= 256) for the reverse scan's 16-column tiles; the other
-    cases here run its 8-column tiles."""
+    """Enough heads (B * H * d / 8 > 256) that the forward scan the backward reruns (the saving
+    instance) takes 16-column value tiles on the bf16 path; the smaller bf16 cases here rerun it
+    with 8-column tiles. The reverse scan itself runs 16-column tiles in every case; what this
+    case adds to it is H = 16 heads per batch row, two full groups of eight."""
     T, H = 130, 16
     inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv=qkv, seed=3000 + d)
     rng = np.random.default_rng(d)
@@ -101,7 +104,7 @@ def test_wide_scan_tiles(device, qkv, B, d):
     do, dS = _cotangents(rng, B, T, H, d, qkv, with_ds=True)
     got = gpu_bwd(inp, device, s0, do, dS, qkv)
     ref = ref_bwd(inp, s0, do, dS)
-    assert_grad_parity(got, ref, TOL[qkv], f"B={B} H={H} T={T} d={d} {qkv} (16-column scan tiles)")
+    assert_grad_parity(got, ref, TOL[qkv], f"B={B} H={H} T={T} d={d} {qkv} (16-column forward tiles)")
 
 
 def test_zero_length(device):
@@ -128,9 +131,9 @@ def test_errors(device):
         muir.chunk_bwd(*[t[n] for n in NAMES], do=do, out={"q": t["a"]})
 
 
-def test_long_context_sampled_heads(device):
-    """The long-context shape (B=1, T=4096, H=16, d=128, bf16), run whole on the GPU; the
-    first and last heads against the oracle."""
+def test_one_row_t4096_sampled_heads(device):
+    """One batch row of the 1.34B-class shape (B=1, T=4096, H=16, d=128, bf16) with an initial
+    state, run whole on the GPU; the first and last heads against the oracle."""
     B, T, H, d = 1, 4096, 16, 128
     inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv="bf16", seed=4242)
     rng = np.random.default_rng(4242)
@@ -140,3 +143,101 @@ def test_long_context_sampled_heads(device):
     heads = [0, H - 1]
     ref = ref_bwd(inp, s0, do, dS, heads=heads)
     assert_grad_parity(got, ref, TOL["bf16"], "T=4096 H=16 d=128 bf16 heads 0,15", heads=heads)
+
+
+def _extreme_decays(a, seed):
+    """Decays of exactly 0, 1e-30 and 1 mixed into the given ones, plus a run of 40 tokens at
+    a = 1 on head 1 (the same mix as the forward's extreme-decay test)."""
+    rng = np.random.default_rng(seed)
+    pick = rng.uniform(size=a.shape)
+    a = a.copy()
+    a[pick < 0.05] = 0.0
+    a[(pick >= 0.05) & (pick < 0.1)] = 1e-30
+    a[(pick >= 0.1) & (pick < 0.2)] = 1.0
+    a[:, 100:140, 1, :] = 1.0
+    return a
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stress_and_extreme_decays(device, qkv, d):
+    """Long-context stress inputs (heads 0 mod 4 with a ~ U(1e-3, 0.05) per token and row, the
+    others with half-lives up to 1e5 tokens) with exact zeros, 1e-30 and ones mixed in. Every
+    pivot of the backward (16-token blocks, 4-token sub-blocks, their halves) and the reverse
+    cumulative sum of the log-decay gradient meet products that underflow or vanish; every
+    gradient, la included, must stay finite and on the oracle."""
+    B, T, H = 1, 300, 4
+    inp = workloads.chunk_inputs(3, B=B, T=T, H=H, d=d, qkv=qkv, seed=5100 + d)
+    inp["a"] = _extreme_decays(inp["a"], 5200 + d)
+    rng = np.random.default_rng(5300 + d)
+    s0 = (rng.standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    do, dS = _cotangents(rng, B, T, H, d, qkv, with_ds=True)
+    got = gpu_bwd(inp, device, s0, do, dS, qkv)
+    ref = ref_bwd(inp, s0, do, dS)
+    assert_grad_parity(got, ref, TOL[qkv], f"stress + extreme decays T={T} d={d} {qkv}")
+
+
+def test_heads_that_forget_everything(device):
+    """Every decay of head 2 exactly zero (each token sees only its own write) and of head 3
+    at 1e-30, next to a stress head and an ordinary one, on the fp32 path (bar 1e-5). On heads
+    2 and 3 the log-decay gradient a * dL/da is zero or about 1e-30 times the others, so a
+    per-head relative error is undefined there: la is held to the bar relative to its largest
+    value over the whole call instead; every other gradient per head as usual."""
+    B, T, H, d = 1, 200, 4, 64
+    inp = workloads.chunk_inputs(3, B=B, T=T, H=H, d=d, qkv="f32", seed=5400)
+    inp["a"][:, :, 2] = 0.0
+    inp["a"][:, :, 3] = 1e-30
+    rng = np.random.default_rng(5401)
+    do, dS = _cotangents(rng, B, T, H, d, "f32", with_ds=True)
+    got = gpu_bwd(inp, device, None, do, dS, "f32")
+    ref = ref_bwd(inp, None, do, dS)
+    for n, x in got.items():
+        assert np.isfinite(x).all(), f"non-finite d{n}"
+    la_err = np.abs(got["la"] - ref["la"]).max() / np.abs(ref["la"]).max()
+    print(f"la error relative to the call's largest la: {la_err:.2e}; "
+          f"largest |la| on the a = 0 head {np.abs(got['la'][:, :, 2]).max():.2e}", flush=True)
+    assert la_err <= TOL["f32"]
+    got_rest = dict(got, la=ref["la"])
+    assert_grad_parity(got_rest, ref, TOL["f32"], "a = 0 and 1e-30 heads fp32 (la above)")
+
+
+def test_long_context_shape_sampled_heads(device):
+    """The long-context backward shape, B=1 H=16 d=128 T=32768 bf16 with the stress heads
+    (0 mod 4), run whole on the GPU: heads 0 (stress), 1 and 15 against the oracle over the
+    whole sequence, every gradient finite on every head."""
+    B, T, H, d = 1, 32768, 16, 128
+    inp = workloads.chunk_inputs(3, B=B, T=T, H=H, d=d, qkv="bf16", seed=3)
+    rng = np.random.default_rng(5500)
+    do, dS = _cotangents(rng, B, T, H, d, "bf16", with_ds=True)
+    got = gpu_bwd(inp, device, None, do, dS, "bf16")
+    heads = [0, 1, 15]
+    ref = ref_bwd(inp, None, do, dS, heads=heads)
+    assert_grad_parity(got, ref, TOL["bf16"], "T=32768 H=16 d=128 bf16 heads 0,1,15", heads=heads)
+
+
+def test_batch8_shape_sampled_heads(device):
+    """The 1.34B-class backward shape, B=8 H=16 d=128 T=4096 bf16 (the one the bench times),
+    run whole on the GPU: heads 0 and 15 of every batch row against the oracle (dr of those
+    heads summed over all eight rows), every gradient finite everywhere."""
+    B, T, H, d = 8, 4096, 16, 128
+    inp = workloads.chunk_inputs(2, B=B, T=T, H=H, d=d, qkv="bf16", seed=2)
+    rng = np.random.default_rng(5600)
+    s0 = (rng.standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    do, dS = _cotangents(rng, B, T, H, d, "bf16", with_ds=True)
+    got = gpu_bwd(inp, device, s0, do, dS, "bf16")
+    heads = [0, 15]
+    ref = ref_bwd(inp, s0, do, dS, heads=heads)
+    assert_grad_parity(got, ref, TOL["bf16"], "B=8 T=4096 H=16 d=128 bf16 heads 0,15", heads=heads)
+
+
+def test_deterministic(device):
+    """Two identical backward calls give the same bits (no atomics in any reduction)."""
+    B, T, H, d = 2, 333, 4, 128
+    inp = workloads.chunk_inputs(3, B=B, T=T, H=H, d=d, qkv="bf16", seed=5700)
+    rng = np.random.default_rng(5701)
+    s0 = (rng.standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    do, dS = _cotangents(rng, B, T, H, d, "bf16", with_ds=True)
+    g1 = gpu_bwd(inp, device, s0, do, dS, "bf16")
+    g2 = gpu_bwd(inp, device, s0, do, dS, "bf16")
+    for n in g1:
+        assert np.array_equal(g1[n], g2[n]), f"d{n} differs between runs"

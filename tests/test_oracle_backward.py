@@ -179,3 +179,51 @@ def test_some_tokens_forget_everything():
         if n != "a":
             _close(C[n], A[n], 1e-12)
     _close(C["la"], A["la"], 1e-12)
+
+
+def test_c_adjoint_matches_autograd_across_segments():
+    """The C token adjoint (checkpointed every 128 tokens, segments recomputed) against the
+    definition, torch autograd through the fp64 forward: several segments and a ragged last
+    one, an initial state and a final-state cotangent, two batch rows sharing dr."""
+    x = _inputs(np.random.default_rng(11), B=2, T=290, H=2, dk=4, dv=3)
+    A = bw.grads_autograd(*_args(x))
+    G = bw.grads_c(*_args(x))
+    for n in GRADS + ("la",):
+        _close(G[n], A[n], 1e-12)
+
+
+def test_c_adjoint_finite_differences_and_absent_state():
+    """Central differences of the C forward's loss along random directions, with s0 and dS
+    absent (zeros), and with decays of exactly 0 (la finite, equal to a * da)."""
+    rng = np.random.default_rng(12)
+    x = _inputs(rng, T=9, s0=False)
+    x["dS"] = None
+    x["a"][0, 4, 1, :3] = 0.0
+    G = bw.grads_c(*_args(x))
+    assert all(np.isfinite(G[n]).all() for n in G)
+    _close(G["la"], x["a"] * G["a"], 1e-15)
+    h = 1e-5
+    names = [n for n in GRADS if n != "s0"]
+    base = dict(x, s0=None, dS=np.zeros((1, 2, 5, 3)))
+    for trial in range(3):
+        dirs = {n: rng.standard_normal(np.shape(x[n])) for n in names}
+        plus = dict(base, **{n: x[n] + h * dirs[n] for n in names})
+        minus = dict(base, **{n: x[n] - h * dirs[n] for n in names})
+        fd = (_loss_c(plus) - _loss_c(minus)) / (2 * h)
+        an = sum(float(np.sum(G[n] * dirs[n])) for n in names)
+        assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), (trial, an, fd)
+
+
+def test_loss_matches_the_c_forward_and_linear_attention():
+    """oracle.backward.loss (numpy forward) against the C forward recurrence on random
+    inputs, and against causal linear attention written with a library matmul
+    (L = <tril(Q K^T) V, dO> + <K^T V, dS> at unit gates, no decay, no erase)."""
+    x = _inputs(np.random.default_rng(13), B=2, T=10)
+    assert abs(bw.loss(*_args(x)) - _loss_c(x)) <= 1e-12 * max(1.0, abs(_loss_c(x)))
+    T, d = 8, 4
+    y = _inputs(np.random.default_rng(14), T=T, H=1, dk=d, dv=d, s0=False)
+    y.update(a=np.ones((1, T, 1, d)), e=np.zeros((1, T, 1, d)), g=np.ones((1, T, 1, d)),
+             w=np.ones((1, T, 1, d)), r=np.ones((1, d)))
+    Q, K, V, dO = (y[n][0, :, 0] for n in ("q", "k", "v", "do"))
+    want = float(np.sum((np.tril(Q @ K.T) @ V) * dO) + np.sum((K.T @ V) * y["dS"][0, 0]))
+    assert abs(bw.loss(*_args(y)) - want) <= 1e-12 * max(1.0, abs(want))
