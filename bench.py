@@ -43,6 +43,44 @@ def algorithmic(d, chunk, qkv_bytes=2):
     }
 
 
+def flop_tally(C, d, leaf=16):
+    """Flops per token-head of the chunk forward as these kernels organise it, split into the
+    matrix-core products and the vector work around them (algorithmic counts: the useful
+    multiply-adds, 2 flops each, of a chunk of C tokens with 16-token leaves, divided by C).
+
+    Matrix cores: the Gram blocks between leaves and inside them (M strictly lower, P
+    inclusive), the three state products (K*gamma) S0, (Qh*gamma) S0, (K*beta)^T U, the solve's
+    terms between leaves and the readout P U. Vector: decay running products (prefix and
+    suffix), operand scalings, the scaling of every off-diagonal Gram block by the decay of the
+    blocks between, the scalings of the diagonal blocks' four recursion levels, the leaf
+    substitution (a coefficient and an FMA per strictly-lower entry and value column), the
+    right-hand side w*v - e*acc, and the state's pair decay (one multiply per state entry per
+    32-token leaf pair). The pages put 98% of the chunkwise flops on the matrix units (liuch.name
+    summary, third bullet)."""
+    nb = C // leaf
+    lower = leaf * (leaf - 1) // 2            # strictly-lower entries of a leaf
+    pairs = nb * (nb - 1) // 2                # leaf pairs (later, earlier) in a chunk
+    mfma = {
+        "gram_between_leaves": pairs * 2 * leaf * leaf * 2 * d / C,
+        "gram_inside_leaves": nb * (lower + lower + leaf) * 2 * d / C,
+        "state_products": 3 * 2 * d * d,
+        "solve_between_leaves": pairs * leaf * leaf * 2 * d / C,
+        "readout_PU": (C * (C + 1) // 2) * 2 * d / C,
+    }
+    valu = {
+        "decay_products": 2 * d,
+        "operand_scaling": 8 * d,
+        "gram_block_scaling": pairs * leaf * d / C,
+        "diag_level_scaling": 4 * 2 * d,
+        "leaf_substitution": nb * lower * 3 * d / C,
+        "rhs": 3 * d,
+        "state_pair_decay": d * d / 32,
+    }
+    m, v = sum(mfma.values()), sum(valu.values())
+    return {"mfma": mfma, "valu": valu, "mfma_flops": m, "valu_flops": v,
+            "mfma_share": m / (m + v)}
+
+
 CSRC = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc")
 # The sources of the channel-wise chunk kernels: the kernel file and the headers it includes.
 CHUNK_SOURCES = [os.path.join(CSRC, f) for f in
@@ -131,7 +169,16 @@ def time_chunk(inp, chunk, dev, steps, warmup, og=None):
     total = evs[0][0].elapsed_time(evs[-1][2])
     assert torch.isfinite(o.float()).all() and torch.isfinite(s_out).all()
     return {"ms_per_step": total / steps, "wall_ms_per_step": wall / steps,
-            "prepare_ms": sum(prep) / steps, "scan_ms": sum(scan) / steps}
+            "prepare_ms": sum(prep) / steps, "scan_ms": sum(scan) / steps,
+            "o": o, "s_out": s_out}
+
+
+def nonfinite_heads(o, s_out):
+    """Heads (b, h) with any non-finite value in their output or final state."""
+    import torch
+    bad_o = ~torch.isfinite(o.float()).all(dim=3).all(dim=1)     # [B, H]
+    bad_s = ~torch.isfinite(s_out).all(dim=3).all(dim=2)         # [B, H]
+    return int((bad_o | bad_s).sum().item())
 
 
 def time_scalar_erase(inp, es, chunk, dev, steps, warmup):
@@ -314,6 +361,86 @@ def time_decode(dev, steps, warmup):
             "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / HBM_PEAK, "bytes_per_head_step": per_head}
 
 
+def time_decode_workload(dev, steps, warmup):
+    """The decode workload: every step runs the 24 layer calls (B=256 sequences x 16 heads,
+    128x128 fp32 states, 6.4 GB of state in all) on that step's freshly drawn inputs. The
+    24 calls of each step are timed between HIP events on the launch stream; drawing the
+    next step's inputs happens outside them."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_06_amd as muir
+    import workloads
+    cfg = workloads.DECODE_CONFIG
+    B, L, H, d = cfg.B, cfg.L, cfg.H, cfg.d
+    u, r = workloads.decode_base(cfg)
+    u_t = torch.from_numpy(u.astype(np.float32)).to(dev)
+    r_t = torch.from_numpy(r).to(dev)
+    states = torch.zeros(L, B, H, d, d, device=dev)
+    o = torch.empty(L, B, H, d, dtype=torch.bfloat16, device=dev)
+    ms = []
+    for step in range(warmup + steps):
+        x = workloads.decode_step_inputs_torch(step, u_t, dev, B=B, cfg=cfg)
+        args = [x[n] for n in ("q", "k", "v", "a", "g", "e", "w")]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for layer in range(L):
+            muir.decode_step(*[t[layer] for t in args], r_t[layer], states[layer], o=o[layer])
+        e1.record()
+        if step >= warmup:
+            ms.append((e0, e1))
+        del x, args
+    torch.cuda.synchronize()
+    step_ms = sum(a.elapsed_time(b) for a, b in ms) / steps
+    per_head = 2 * d * d * 4 + 3 * d * 2 + 4 * d * 4 + d * 2
+    gbs = per_head * B * H * L / (step_ms * 1e-3) / 1e9
+    assert torch.isfinite(states).all() and torch.isfinite(o.float()).all()
+    return {"workload": f"decode B{B} x {L} layers x H{H} d{d}, fp32 states ({B * L * H * d * d * 4 / 1e9:.2f} GB)",
+            "steps_timed": steps, "ms_per_step_24_layers": step_ms,
+            "tokens_per_s": B / (step_ms * 1e-3), "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / HBM_PEAK,
+            "s_for_1024_steps": step_ms * 1024 / 1e3}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_decode_baseline(dev, steps=4):
+    """The CPU oracle's fp32 token recurrence on a bounded sample of the decode workload: one
+    layer's 256 x 16 states from a random state, `steps` tokens each (the oracle's loop over
+    tokens is the decode step repeated), extrapolated linearly to 24 layers x 1024 steps."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    cfg = workloads.DECODE_CONFIG
+    B, H, d = cfg.B, cfg.H, cfg.d
+    u, r = workloads.decode_base(cfg, L=1)
+    u_t = torch.from_numpy(u.astype(np.float32)).to(dev)
+    xs = [workloads.decode_step_inputs_torch(i, u_t, dev, B=B, cfg=cfg) for i in range(steps)]
+    host = {n: np.stack([x[n][0].float().cpu().numpy() for x in xs], axis=1) for n in xs[0]}
+    del xs
+    s0 = (np.random.default_rng(4).standard_normal((B, H, d, d)) * 0.1).astype(np.float32)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.recurrent(host["q"], host["k"], host["v"], host["a"], host["g"], host["e"], host["w"],
+                     r[0], s0=s0, precision="f32", threads=threads)
+    sec = time.perf_counter() - t0
+    full = sec / steps * cfg.L * 1024
+    per_head = 2 * d * d * 4 + 3 * d * 2 + 4 * d * 4 + d * 2
+    return {"value": cfg.L * 1024 / full, "unit": "decode steps/s (24 layers, 256 sequences)",
+            "cores": threads, "kind": "oracle", "extrapolated": True,
+            "state_GB_per_s": per_head * B * H * steps / sec / 1e9,
+            "s_for_1024_steps": full,
+            "sample": f"fp32 token recurrence in C (OpenMP) over one layer's {B}x{H} states for "
+                      f"{steps} tokens ({sec:.1f} s), extrapolated linearly to {cfg.L} layers x 1024 steps"}
+
+
 def cpu_baseline(inp, budget_s=20.0):
     """The CPU oracle (fp32 token recurrence, as it stands) on a bounded sample of the
     long-context workload: all 16 heads, the first T_s tokens, T_s sized from a short
@@ -331,9 +458,26 @@ def cpu_baseline(inp, budget_s=20.0):
     oracle.recurrent(*[sl(n, T_s) for n in NAMES], precision="f32", threads=threads)
     sec = time.perf_counter() - t0
     return {"value": inp["B"] * T_s / sec, "unit": "tokens/s/layer", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp32 token recurrence in C (OpenMP) on the first {T_s} of {T} tokens, "
                       f"all {inp['H']} heads, B={inp['B']}, d={inp['d']}; {sec:.1f} s"}
+
+
+def sampled_head_errors(inp, o, s_out, heads):
+    """Per-head max relative error (max |x - ref| / max |ref| over the head) of the timed
+    call's output and final state on the given heads, against the oracle's fp64 recurrence
+    over the whole sequence (run beside the CPU baseline, outside any timed region)."""
+    import numpy as np
+    import oracle
+    sl = {n: np.ascontiguousarray(inp[n][:, :, heads]) if n != "r" else inp[n][heads] for n in NAMES}
+    o_ref, s_ref = oracle.recurrent(*[sl[n] for n in NAMES])
+    o_g = o[:, :, heads].float().cpu().numpy()
+    s_g = s_out[:, heads].cpu().numpy()
+    eo = np.abs(o_g - o_ref).max(axis=(0, 1, 3)) / np.abs(o_ref).max(axis=(0, 1, 3))
+    es = np.abs(s_g - s_ref).max(axis=(0, 2, 3)) / np.abs(s_ref).max(axis=(0, 2, 3))
+    return {"heads": list(heads), "o_max_rel_err": [float(x) for x in eo],
+            "state_max_rel_err": [float(x) for x in es],
+            "stress_heads": [h for h in heads if h in inp["stress_heads"]]}
 
 
 def main():
@@ -382,7 +526,7 @@ def main():
               "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
     secondary = {}
-    main_inp = None
+    main_inp = main_out = None
     if args.only in ("all", "main"):
         main_inp = workloads.chunk_inputs(3)
         name = "chunk_fwd long-context B1 H16 d128 T32768 C256 bf16"
@@ -403,7 +547,13 @@ def main():
                               "frac": ach * 1e9 / HBM_PEAK, "traffic": measured_traffic(dom),
                               "avg_ms": dom_ms}
         result["phases_ms"] = {"prepare": r["prepare_ms"], "scan": r["scan_ms"]}
+        result["nan_heads"] = nonfinite_heads(r["o"], r["s_out"])
+        main_out = (r["o"], r["s_out"])
         result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"]}
+        tally = flop_tally(256, 128)
+        result["flop_share"] = {"mfma_share_algorithmic": tally["mfma_share"],
+                                "mfma_flops_per_token_head": tally["mfma_flops"],
+                                "valu_flops_per_token_head": tally["valu_flops"]}
         # The same call with the output-gate epilogue fused into the readout.
         og = workloads.output_gate(1, 32768, 16, 128, seed=3)
         rg = time_chunk(main_inp, 256, dev, args.steps, args.warmup, og=og)
@@ -477,6 +627,11 @@ def main():
     if args.only in ("all", "decode"):
         print("bench: decode step B256 H16 d128", file=sys.stderr, flush=True)
         secondary["decode"] = time_decode(dev, max(50, args.steps * 10), args.warmup * 5)
+        print("bench: decode workload, 24 layers", file=sys.stderr, flush=True)
+        secondary["decode_workload"] = time_decode_workload(dev, max(16, args.steps * 2), 2)
+        if not args.no_cpu:
+            print("bench: CPU oracle decode baseline", file=sys.stderr, flush=True)
+            secondary["decode_workload"]["cpu_baseline"] = cpu_decode_baseline(dev)
         if "value" not in result:
             result["value"] = secondary["decode"]["GB_per_s"]
             result["unit"] = "GB/s"
@@ -486,6 +641,9 @@ def main():
     if main_inp is not None and not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(main_inp)
+        print("bench: sampled heads of the timed output against the oracle", file=sys.stderr,
+              flush=True)
+        result["parity"] = sampled_head_errors(main_inp, *main_out, heads=[0, 1, 15])
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -603,7 +603,8 @@ template <int D> struct GradLds {
     // blocks before and after each block (4 + 4), per channel. About 67 KB in all for d = 128,
     // so two workgroups share a compute unit.
     static constexpr int P2 = 7 * kC * LDH + (6 + 16 + 4 + 4) * DH;
-    static constexpr int FLOATS = OUPU + 2 * D + (P2 > kBwdThreads ? P2 : kBwdThreads) + kNB * DH;
+    static constexpr int FLOATS = OUPU + 2 * D + (P2 > kBwdThreads ? P2 : kBwdThreads) + kNB * DH +
+                                  kNB * 4 * DH;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
@@ -626,6 +627,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
           *sF4 = sR + C * LDH, *sR4 = sF4 + C * LDH, *sMid = sR4 + C * LDH, *sB4 = sMid + 6 * DH,
           *sGb = sB4 + 16 * DH, *sBa = sGb + 4 * DH;
     float *sBp = lds + L::FLOATS - kNB * DH;  // whole-block decay products per channel
+    // dr partials of one pass: [16-token block][lane group][channel], summed in a fixed order.
+    float *sDrP = sBp - kNB * 4 * DH;
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         }
     };
     // rowsum(S_C * lambda_C): thread (row, part) sums a contiguous segment of the row, every
-    // load issued before the first use; the parts meet through LDS atomics.
+    // load issued before the first use; the parts' sums are added in a fixed order.
     {
         constexpr int TPR = kBwdThreads / D;  // threads per row
         constexpr int SEG = D / TPR;          // elements per thread
@@ -677,9 +680,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
         for (int j = 0; j < SEG / 4; ++j)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) acc = fmaf(xs[j][q4], xl[j][q4], acc);
-        if (part == 0) sRS[i] = 0.f;
+        un[part * D + i] = acc;  // the pass arrays are not in use yet
         __syncthreads();
-        atomicAdd(&sRS[i], acc);
+        if (part == 0) {
+            float sum = 0.f;
+#pragma unroll
+            for (int p2 = 0; p2 < TPR; ++p2) sum += un[p2 * D + i];
+            sRS[i] = sum;
+        }
     }
     for (int i = tid; i < D; i += kBwdThreads) sDr[i] = 0.f;
     __syncthreads();
@@ -779,8 +787,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
     // F4_t * mid4 * R4_s across 4-token sub-blocks of one block; pairs inside one sub-block are
     // direct products. Jobs: kind 0 (dq_hat and the read part of dk, rows = t) and kind 1 (the
     // write part of dk, rows = s), one 16-row block each; wave w takes jobs w and w + 4.
+    // The dr partials of the pass before, added in a fixed order (block, then lane group).
+    auto fold_dr = [&](int pp) {
+        if (tid < DH) {
+            float sum = 0.f;
+#pragma unroll
+            for (int x = 0; x < kNB * 4; ++x) sum += sDrP[x * DH + tid];
+            sDr[pp + tid] = sum;
+        }
+    };
     for (int p0 = 0; p0 < D; p0 += DH) {
-        if (p0 > 0) __syncthreads();
+        if (p0 > 0) {
+            __syncthreads();
+            fold_dr(p0 - DH);
+        }
         {
             constexpr int N4 = C * DH / 4 / kBwdThreads;
             f32x4_t va[N4], vk[N4], vq[N4];
@@ -888,6 +908,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
                     gq[e4] = ok ? ld(q, o) : 0.f;
                 }
                 f32x4_t cq = zero4(), cr = zero4(), dq4 = zero4(), dr4 = zero4();
+                float drl = 0.f;  // this lane's share of dr: its four tokens, in order
 #pragma unroll
                 for (int bs = 0; bs < kNB - 1; ++bs) {
                     if (bs >= bt) break;
@@ -950,9 +971,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
                         dg[o] = rh[ocol] * qt * dqh;
                         dk[o] = dkr;
                         dla[o] = fmaf(sQ[t * LDH + ic], dqh, sK[t * LDH + ic] * dkr);
-                        atomicAdd(&sDr[ocol], gt * qt * dqh);
+                        drl += gt * qt * dqh;
                     }
                 }
+                sDrP[(bt * 4 + kq) * DH + ic] = drl;
             } else {
                 // Rows s of block bs = rb.
                 const int bs = rb;
@@ -1021,6 +1043,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             }
         }
     }
+    __syncthreads();
+    fold_dr(D - DH);
     __syncthreads();
     {
         // Log-decay gradient: a reverse cumulative sum over the chunk per channel. Thread (part,
