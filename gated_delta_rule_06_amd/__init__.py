@@ -56,6 +56,10 @@ def lib():
         L.muir_chunk_fwd_workspace_size.restype = sz
         L.muir_chunk_fwd.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
         L.muir_chunk_fwd.restype = i
+        L.muir_chunk_fwd_noalloc.argtypes = [vp] * 11 + [i] * 7 + [vp]
+        L.muir_chunk_fwd_noalloc.restype = i
+        L.muir_chunk_fwd_noalloc_max_workspace.argtypes = []
+        L.muir_chunk_fwd_noalloc_max_workspace.restype = sz
         L.muir_chunk_fwd_prepare.argtypes = [vp] * 5 + [i] * 6 + [vp, sz, vp]
         L.muir_chunk_fwd_prepare.restype = i
         L.muir_chunk_fwd_scan.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp]

@@ -237,6 +237,33 @@ muir_status_t muir_chunk_fwd(const void *q, const void *k, const void *v, const 
                           stream);
 }
 
+muir_status_t muir_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *a,
+                                     const float *g, const float *e, const float *w,
+                                     const float *r, const float *s0, void *o, float *s_out, int B,
+                                     int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+                                     muir_stream_t stream) {
+    const char *fn = "chunk_fwd_noalloc";
+    const size_t need = muir_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, qkv);
+    if (need > muir::kNoAllocScratchBytes)
+        return fail(MUIR_ERR_WORKSPACE,
+                    "%s: these sizes need %zu bytes of workspace; the static scratch holds %zu "
+                    "(call muir_chunk_fwd with a workspace instead)",
+                    fn, need, muir::kNoAllocScratchBytes);
+    void *scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (need > 0) {
+        // Invalid sizes give need == 0 and are reported by the validation below.
+        const muir_status_t st = check_hip(muir::noalloc_scratch(&scratch), fn);
+        if (st != MUIR_OK) return st;
+        scratch_bytes = muir::kNoAllocScratchBytes;
+    }
+    return chunk_fwd_impl(ChunkCall{fn, q, k, v, a, g, e, w, nullptr, r, s0, o, s_out, B, T, H,
+                                    dk, dv, chunk, qkv, scratch, scratch_bytes, true, true, false},
+                          stream);
+}
+
+size_t muir_chunk_fwd_noalloc_max_workspace(void) { return muir::kNoAllocScratchBytes; }
+
 muir_status_t muir_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *a,
                                    const float *g, const float *e, const float *w,
                                    const float *og, const float *r, const float *s0, void *o,

@@ -87,4 +87,9 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d, bool bf16);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &args, int B, int T, int H, int d, bool bf16,
                             void *workspace, hipStream_t stream);
 
+// Size of the static device scratch that muir_chunk_fwd_noalloc uses as its workspace, and
+// its address on the current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace muir

@@ -115,6 +115,31 @@ muir_status_t muir_chunk_fwd(
     void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
+ * muir_chunk_fwd without the workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. The workspace is a static device array inside the library instead, one per
+ * GPU (held from the library's first use on that GPU until the process ends), of
+ * muir_chunk_fwd_noalloc_max_workspace() bytes (128 MiB). The call allocates and frees
+ * nothing; its address on the current device is looked up once per device.
+ *
+ * Arguments, results and errors are those of muir_chunk_fwd (same kernels, same bits),
+ * plus MUIR_ERR_WORKSPACE when muir_chunk_fwd_workspace_size(...) of these sizes exceeds the
+ * static scratch (for example 348 KiB per (batch, head, 256-token chunk) at d = 128 in bf16:
+ * 16 heads x 16 chunks of 256 tokens fit, the long-context shape's 16 x 128 chunks do not).
+ * Every call on one GPU uses the same scratch and leaves its contents there; nothing in it
+ * needs clearing (each call's parallel phase writes every byte its scan reads). Calls that
+ * overlap on one GPU (on different streams, or from several threads) race on the scratch:
+ * order them on one stream or serialise them.
+ */
+muir_status_t muir_chunk_fwd_noalloc(
+    const void *q, const void *k, const void *v,
+    const float *a, const float *g, const float *e, const float *w, const float *r,
+    const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv, muir_stream_t stream);
+
+size_t muir_chunk_fwd_noalloc_max_workspace(void);
+
+/*
  * The two phases of muir_chunk_fwd as separate calls, for callers that schedule or
  * time them on their own. muir_chunk_fwd(...) is exactly muir_chunk_fwd_prepare(...)
  * followed by muir_chunk_fwd_scan(...) on the same stream with the same workspace.

@@ -386,3 +386,15 @@ def test_c_program_builds_and_calls_the_library(tmp_path):
     assert int(version) == lib.muir_version()
     assert int(ws) == muir.chunk_fwd_workspace_size(1, 256, 2, 64, 64, 64, 0)
     assert name == "MUIR_ERR_NULL" and detail == "detail"
+
+
+def test_noalloc_refuses_workspace_beyond_its_scratch():
+    """muir_chunk_fwd_noalloc checks its sizes against the static scratch before touching the
+    device: the long-context shape (712 MiB of workspace) is refused with WORKSPACE."""
+    lib = muir.lib()
+    limit = lib.muir_chunk_fwd_noalloc_max_workspace()
+    assert limit == 128 << 20
+    assert muir.chunk_fwd_workspace_size(1, 32768, 16, 128, 128, 256, muir.MUIR_BF16) > limit
+    st = lib.muir_chunk_fwd_noalloc(*[fake(i) for i in range(11)], 1, 32768, 16, 128, 128, 256,
+                                    muir.MUIR_BF16, None)
+    assert st == 4 and "static scratch" in muir.last_error(), muir.last_error()
