@@ -357,7 +357,9 @@ def time_decode(dev, steps, warmup):
     per_head = 2 * d * d * 4 + 3 * d * 2 + 4 * d * 4 + d * 2   # 134,144 B at d = 128
     gbs = per_head * B * H / (ms * 1e-3) / 1e9
     assert torch.isfinite(state).all()
-    return {"workload": "decode B256 H16 d128 (one layer call)", "ms_per_call": ms,
+    return {"workload": "decode B256 H16 d128, one layer call repeated on the same 268 MB of "
+                        "state (much of it stays in the 256 MB last-level cache; the 24-layer "
+                        "workload below is the HBM figure)", "ms_per_call": ms,
             "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / HBM_PEAK, "bytes_per_head_step": per_head}
 
 
@@ -410,7 +412,7 @@ def cpu_model():
     return None
 
 
-def cpu_decode_baseline(dev, steps=4):
+def cpu_decode_baseline(dev, steps=48):
     """The CPU oracle's fp32 token recurrence on a bounded sample of the decode workload: one
     layer's 256 x 16 states from a random state, `steps` tokens each (the oracle's loop over
     tokens is the decode step repeated), extrapolated linearly to 24 layers x 1024 steps."""

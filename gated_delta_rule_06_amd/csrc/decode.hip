@@ -13,8 +13,17 @@
 //
 // Layout: state [B,H,dk,dv] fp32 with dv contiguous. A thread owns 4 consecutive
 // columns (one float4) of ROWS rows strided by ROW_GROUPS, so each wave reads whole
-// contiguous rows (coalesced 16-byte loads) and all loads are issued up front. The new
-// state is written with non-temporal stores: it is not read again in this step.
+// contiguous rows (coalesced 16-byte loads) and all loads are issued up front. The
+// column sums over rows run first inside each wave (lanes of one column quad, other row
+// groups: butterfly shuffles), then across the waves through LDS.
+//
+// Both the state's loads and its stores are non-temporal: each state is touched once per
+// step and not again until the next step, after every other layer's state has streamed
+// through, so caching it only evicts other data. Over the 24-layer decode workload (6.4 GB
+// of fp32 state) this measured 5.95 TB/s against 5.19 TB/s with cached loads, and against
+// 5.5 TB/s for a plain device copy of the same buffers. 1024-thread workgroups (16 waves,
+// four state rows per thread) beat 512 and 256 threads and splitting a head's columns over
+// several workgroups.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -23,7 +32,7 @@ namespace muir {
 
 namespace {
 
-constexpr int kDecodeThreads = 512;
+constexpr int kDecodeThreads = 1024;
 
 template <typename QT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
@@ -34,12 +43,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     constexpr int TPR = D / 4;                       // threads per row (float4 each)
     constexpr int ROW_GROUPS = kDecodeThreads / TPR;  // rows handled in parallel
     constexpr int ROWS = D / ROW_GROUPS;              // rows per thread
-    static_assert(D % 4 == 0 && kDecodeThreads % TPR == 0 && D % ROW_GROUPS == 0, "shape");
+    constexpr int NW = kDecodeThreads / 64;           // waves
+    static_assert(D % 4 == 0 && kDecodeThreads % TPR == 0 && D % ROW_GROUPS == 0 && 64 % TPR == 0,
+                  "shape");
 
     __shared__ float sh_ak[D], sh_aq[D], sh_k[D], sh_a[D];
-    __shared__ float sh_b[D], sh_e[D], sh_u[D];
-    __shared__ float sh_part[2][ROW_GROUPS][D];
-    __shared__ float sh_qk;
+    __shared__ float sh_part[2][NW][D];
+    __shared__ float sh_u[D];
+    __shared__ float sh_qk[NW];
 
     const int bh = blockIdx.x;              // b * H + h
     const int h = bh % H;
@@ -47,12 +58,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const int c4 = tid % TPR;               // column quad
     const int rg = tid / TPR;               // row group
 
-    float4 *S4 = reinterpret_cast<float4 *>(state + static_cast<size_t>(bh) * D * D);
-    float4 s[ROWS];
+    f32x4_t *S4 = reinterpret_cast<f32x4_t *>(state + static_cast<size_t>(bh) * D * D);
+    f32x4_t s[ROWS];
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m) s[m] = S4[(rg + m * ROW_GROUPS) * TPR + c4];
+    for (int m = 0; m < ROWS; ++m)
+        s[m] = __builtin_nontemporal_load(&S4[(rg + m * ROW_GROUPS) * TPR + c4]);
 
     const size_t vo = static_cast<size_t>(bh) * D;
+    float qk = 0.f;  // q_hat . k over the rows
     if (tid < D) {
         const float ai = a[vo + tid];
         const float ki = elem<QT>::load(k, vo + tid);
@@ -62,57 +75,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
         sh_k[tid] = ki;
         sh_ak[tid] = ai * ki;
         sh_aq[tid] = ai * qh;
-        sh_b[tid] = w[vo + tid] * elem<QT>::load(v, vo + tid);
-        sh_e[tid] = e[vo + tid];
-        // q_hat . k over the D rows: the first D threads are whole waves (D >= 64).
-        float part = wave_sum(qh * ki);
-        if (D == 64) {
-            if (tid == 0) sh_qk = part;
-        } else {
-            if ((tid & 63) == 0) sh_part[0][0][tid >> 6] = part;
-        }
+        qk = qh * ki;
     }
-    __syncthreads();
-    if (D != 64 && tid == 0) {
-        float t = 0.f;
-        for (int i = 0; i < D / 64; ++i) t += sh_part[0][0][i];
-        sh_qk = t;
-    }
+    qk = wave_sum(qk);
+    if ((tid & 63) == 0) sh_qk[tid >> 6] = qk;
     __syncthreads();
 
-    float4 p = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t p = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
         const int i = rg + m * ROW_GROUPS;
-        const float ak = sh_ak[i], aq = sh_aq[i];
-        p.x += ak * s[m].x; p.y += ak * s[m].y; p.z += ak * s[m].z; p.w += ak * s[m].w;
-        y.x += aq * s[m].x; y.y += aq * s[m].y; y.z += aq * s[m].z; y.w += aq * s[m].w;
+        p += sh_ak[i] * s[m];
+        y += sh_aq[i] * s[m];
     }
-    reinterpret_cast<float4 *>(sh_part[0][rg])[c4] = p;
-    reinterpret_cast<float4 *>(sh_part[1][rg])[c4] = y;
+    // Lanes tid, tid ^ TPR, tid ^ 2 TPR, ... of a wave hold the same columns.
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            p[c] += __shfl_xor(p[c], off, 64);
+            y[c] += __shfl_xor(y[c], off, 64);
+        }
+    const int wv = tid >> 6, ln = tid & 63;
+    if (ln < TPR) {
+        reinterpret_cast<f32x4_t *>(sh_part[0][wv])[ln] = p;
+        reinterpret_cast<f32x4_t *>(sh_part[1][wv])[ln] = y;
+    }
     __syncthreads();
 
     if (tid < D) {
-        float pj = 0.f, yj = 0.f;
+        float pj = 0.f, yj = 0.f, qkt = 0.f;
 #pragma unroll
-        for (int i = 0; i < ROW_GROUPS; ++i) {
+        for (int i = 0; i < NW; ++i) {
             pj += sh_part[0][i][tid];
             yj += sh_part[1][i][tid];
+            qkt += sh_qk[i];
         }
-        const float uj = sh_b[tid] - sh_e[tid] * pj;
+        const float uj = w[vo + tid] * elem<QT>::load(v, vo + tid) - e[vo + tid] * pj;
         sh_u[tid] = uj;
-        elem<QT>::store(o, vo + tid, yj + sh_qk * uj);
+        elem<QT>::store(o, vo + tid, yj + qkt * uj);
     }
     __syncthreads();
 
-    const float4 u = reinterpret_cast<const float4 *>(sh_u)[c4];
+    const f32x4_t u = reinterpret_cast<const f32x4_t *>(sh_u)[c4];
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
         const int i = rg + m * ROW_GROUPS;
-        const float ai = sh_a[i], ki = sh_k[i];
-        const f32x4_t t = {ai * s[m].x + ki * u.x, ai * s[m].y + ki * u.y,
-                           ai * s[m].z + ki * u.z, ai * s[m].w + ki * u.w};
-        __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t *>(&S4[i * TPR + c4]));
+        const f32x4_t t = sh_a[i] * s[m] + sh_k[i] * u;
+        __builtin_nontemporal_store(t, &S4[i * TPR + c4]);
     }
 }
 
