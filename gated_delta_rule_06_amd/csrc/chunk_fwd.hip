@@ -41,6 +41,7 @@
 #include <utility>
 
 #include "chunk_layout.hpp"
+#include "scan_leaf.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -344,41 +345,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prepare_kernel(
 // ---------------------------------------------------------------------------------
 // Phase S: sequential chunk scan.
 // ---------------------------------------------------------------------------------
-
-// One step of the leaf's forward substitution for the VC value columns a lane holds (4 or
-// 2): x_c += n_c * x_c(lane S of the 16-lane row), the broadcast done by the DPP row
-// broadcast inside the FMA. A DPP read needs two wait states after a VALU write of its
-// register. With four columns the other columns' instructions provide them (every
-// register is read three instructions after it was written) and only the first step
-// waits; with two columns one more state is waited each step.
-template <int S, int VC>
-__device__ __forceinline__ void subst_step(float &x0, float &x1, float &x2, float &x3, float n0,
-                                           float n1, float n2, float n3) {
-#define MUIR_BCAST_FMA(R, N) \
-    "v_fmac_f32_dpp " R ", " R ", " N " row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
-    if constexpr (VC == 4) {
-        if constexpr (S == 0) {
-            asm("s_nop 1\n\t" MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5")
-                    MUIR_BCAST_FMA("%2", "%6") MUIR_BCAST_FMA("%3", "%7")
-                : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
-                : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
-        } else {
-            asm(MUIR_BCAST_FMA("%0", "%4") MUIR_BCAST_FMA("%1", "%5") MUIR_BCAST_FMA("%2", "%6")
-                    MUIR_BCAST_FMA("%3", "%7")
-                : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
-                : "v"(n0), "v"(n1), "v"(n2), "v"(n3), "i"(S));
-        }
-    } else {
-        static_assert(VC == 2, "VC is 4 or 2");
-        asm("s_nop %5\n\t"
-            "v_fmac_f32_dpp %0, %0, %2 row_newbcast:%4 row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %1, %1, %3 row_newbcast:%4 row_mask:0xf bank_mask:0xf"
-            : "+v"(x0), "+v"(x1)
-            : "v"(n0), "v"(n1), "i"(S), "i"(S == 0 ? 1 : 0));
-    }
-#undef MUIR_BCAST_FMA
-}
-
 
 // ---------------------------------------------------------------------------------
 // Phase P for bf16 operands: the same outputs in one streaming pass over the chunk.
@@ -868,13 +834,6 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     }
     kbt_out(NP - 1);
 }
-
-// Per-leaf inputs of the serial chain, row layout: lane (t, g) holds token t of the
-// leaf and the tile's value columns of lane group g (the first VC values).
-template <typename QT, int VC> struct LeafIn {
-    f32x4_t ev, wv;
-    typename RowV<QT, VC>::raw vv;
-};
 
 // The scan: one workgroup of two wavefronts per (batch, head, 4 VC value columns),
 // sequential over chunks and over the 16-token leaves inside each chunk. Value columns
@@ -1492,6 +1451,8 @@ hipError_t scan_typed(const void *v, const float *e, const float *w, const float
                       const float *s0, void *o, float *s_out, int B, int T, int H,
                       const void *workspace, hipStream_t stream) {
     if constexpr (std::is_same_v<QT, bf16_t>) {
+        if (scan_split_applies(B, H, D))
+            return launch_chunk_scan_split(v, e, w, og, s0, o, s_out, B, T, H, D, C, workspace, stream);
         if (scan_narrow_tiles(B, H, D))
             return scan_vc<QT, OpT, D, C, 2>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
     }

@@ -34,6 +34,14 @@ hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, cons
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                              int chunk, bool bf16, const void *workspace, hipStream_t stream);
 
+// Phase S for bf16 operands split over four wavefronts per workgroup (chain, right-hand
+// side, state carry, readout); runs where scan_split_applies holds (at most one 8-column
+// workgroup per compute unit). Same results as launch_chunk_scan, bit for bit.
+bool scan_split_applies(int B, int H, int d);
+hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
+                                   const float *s0, void *o, float *s_out, int B, int T, int H,
+                                   int d, int chunk, const void *workspace, hipStream_t stream);
+
 // Phase S as above (no output gate), also keeping what the backward pass needs: u_out
 // [B, T, H, d] fp32 (u = w * v - e * p of every token) and states [B * H][nchunks + 1][d][d]
 // fp32 (the state at every chunk start, then the final state). Chunks of 64 only.
