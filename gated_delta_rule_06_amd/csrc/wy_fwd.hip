@@ -18,10 +18,10 @@
 // path's prepare kernel, pivoted at block boundaries so that no cumulative decay is ever
 // divided (the stable large-chunk scheme: liuch.name summary, third bullet; openai-hub
 // news page, section on rewriting the long-sequence parallel algorithm). The inverse is
-// the block recursion of that scheme, one 16-token row block at a time:
-//   T_ii = (I + Diag(e_i) M_ii)^-1                    forward substitution, fp32
-//   T_ij = -T_ii Diag(e_i) sum_{j<=k<i} M_ik T_kj     (j < i) on the matrix cores
-// and it replaces M in the workspace.
+// that scheme's recursive block-Neumann form: 16x16 leaves T_ii = (I + Diag(e_i) M_ii)^-1 by
+// forward substitution in fp32, then log2(C / 16) levels that combine pairs of diagonal blocks,
+//   T21 = -T22 Diag(e2) M21 T11,
+// on the matrix cores; it replaces M in the workspace.
 #include "chunk_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -31,156 +31,216 @@ namespace muir {
 
 namespace {
 
-// LDS of the inverse kernel (bytes). Diagonal blocks are fp32 [16][TDS] (row pitch padded
-// so the 16-lane groups of one wavefront hit different banks).
+// LDS of the inverse kernel (bytes). Every lower 16x16 tile (i, j), i >= j, of T is kept once,
+// as a row fragment in bf16 (lane (x, G): T[16i + x][16j + 4G .. + 3], 8 bytes): the diagonal
+// tiles first (slot i), then the others (slot NB + i (i - 1) / 2 + j), which hold M's tiles
+// until T's replace them. Then the strictly lower triangles of M's fp32 diagonal blocks
+// (element (s, c), c < s, of block i at 120 i + s (s - 1) / 2 + c) and the erase strengths.
+// About 76.5 KB at C = 256: two workgroups share a CU.
 template <int C> struct InvLds {
-    static constexpr int NB = C / 16, NP = NB / 2, TDS = 260;
-    static constexpr size_t E_OFF = 0;                                     // [C] erase strengths
-    static constexpr size_t MD_OFF = E_OFF + size_t(C) * 4;                // [NB][TDS] M_ii
-    static constexpr size_t TD_OFF = MD_OFF + size_t(NB) * TDS * 4;        // [NB][TDS] T_ii
-    static constexpr size_t TA_OFF = TD_OFF + size_t(NB) * TDS * 4;        // [NB][64] T_ii, A operand
-    static constexpr size_t TB_OFF = TA_OFF + size_t(NB) * 64 * 8;         // [NP(NP+1)][64] B operand
-    static constexpr size_t BYTES = TB_OFF + size_t(NP) * (NP + 1) * 64 * 16;
+    static constexpr int NB = C / 16, NTILE = NB * (NB + 1) / 2;
+    static constexpr size_t TILE_OFF = 0;                        // [NTILE][64] x 8 B
+    static constexpr size_t MD_OFF = size_t(NTILE) * 512;        // [NB][120] fp32
+    static constexpr size_t E_OFF = MD_OFF + size_t(NB) * 480;   // [C] fp32
+    static constexpr size_t BYTES = E_OFF + size_t(C) * 4;
 };
 
 // Wavefronts of the inverse kernel: eight for 16 or more row blocks, else four.
 template <int C> constexpr int inv_waves() { return C / 16 >= 16 ? 8 : 4; }
 
-// One workgroup per (chunk, head, batch). T's blocks are kept in LDS as
-// K = 32 operands whose rows are T's columns: slot (m, j) holds blocks (2m, j) and
-// (2m + 1, j), lane (n, G) the elements [4G + r][n] of both. Slots exist for j <= 2m + 1;
-// upper blocks stay zero. Row block i of T is computed from M's row block i (read from the
-// workspace) against the slots of the rows above it; wavefront w takes the column blocks
-// j = w (mod NW). A row's T blocks overwrite its M blocks in the workspace only after every
-// wavefront has finished reading that row (one row later, past a barrier).
+// One workgroup per (chunk, head, batch): T = (I + Diag(e) M)^-1 by the recursive
+// block-Neumann form (openai-hub news page, section on rewriting the long-sequence parallel
+// algorithm for TPU: the unit lower-triangular inverse by recursive block products). For a
+// diagonal block split into halves,
+//   [L11 0; L21 L22]^-1 = [T11 0; -T22 L21 T11  T22],   L21 = Diag(e2) M21,
+// so the 16x16 leaves T_ii = (I + Diag(e_i) M_ii)^-1 are solved first (in fp32, by the first
+// half of the wavefronts while the second half brings M's tiles into LDS), then log2(C / 16)
+// levels each combine pairs of diagonal blocks on the matrix cores: step 1
+// Q = Diag(e2) M21 T11, a barrier, step 2 T21 = -T22 Q over M21's slots, a barrier. A level's
+// work items are (pair, column tile of T11); an item's column strip of Q stays in registers.
+// T goes out once, at the end, over M in the workspace: the kernel streams the M region in
+// and out and the fp32 diagonal blocks in, and touches nothing else in HBM.
 template <int D, int C>
-__global__ __launch_bounds__(64 * inv_waves<C>()) void wy_inverse_kernel(const float *__restrict__ e,
-                                                         unsigned char *__restrict__ ws, int T,
-                                                         int H, int nchunks) {
+__global__ __launch_bounds__(64 * inv_waves<C>()) __attribute__((amdgpu_waves_per_eu(4)))
+void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ ws, int T, int H,
+                       int nchunks) {
     using SL = Slot<bf16_t, D, C>;
     using LY = InvLds<C>;
     using F = Frag<bf16_t>;
     using f4 = F::f4;
     using f8 = F::f8;
-    constexpr int NB = C / 16, NP = NB / 2, TDS = LY::TDS, NW = inv_waves<C>();
-    constexpr int NT = 64 * NW, NJ = (NB + NW - 1) / NW;
+    constexpr int NB = C / 16, NW = inv_waves<C>(), NT = 64 * NW, NPAIR = SL::NPAIR;
+    constexpr int NPW = (NPAIR + NW - 1) / NW;            // pair slots per wavefront, write-out
+    constexpr int NPL = (NPAIR + NW / 2 - 1) / (NW / 2);  // per loading wavefront
+    constexpr int NMD = NB * 64 / NT;  // 16-byte loads of the fp32 diagonal blocks per thread
+    static_assert(NB / 2 <= NW && NB * 16 <= NT / 2 && C <= NT && (NB * 64) % NT == 0,
+                  "work split");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sh_e = reinterpret_cast<float *>(smem + LY::E_OFF);
+    f4 *sh_t = reinterpret_cast<f4 *>(smem + LY::TILE_OFF);
     float *sh_md = reinterpret_cast<float *>(smem + LY::MD_OFF);
-    float *sh_td = reinterpret_cast<float *>(smem + LY::TD_OFF);
-    f4 *sh_ta = reinterpret_cast<f4 *>(smem + LY::TA_OFF);
-    f8 *sh_tb = reinterpret_cast<f8 *>(smem + LY::TB_OFF);
-    auto tb = [&](int m, int j) { return sh_tb + (m * (m + 1) + j) * 64; };
+    float *sh_e = reinterpret_cast<float *>(smem + LY::E_OFF);
+    auto slot_of = [](int i, int j) { return i == j ? i : NB + i * (i - 1) / 2 + j; };
 
     const int ci = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
-    // The wavefront index is uniform: in a scalar register, offsets derived from it are too.
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, x = lane & 15, G = lane >> 4;
     unsigned char *slot = ws + ((size_t(b) * H + hh) * nchunks + ci) * SL::BYTES;
     bf16_t *gT = reinterpret_cast<bf16_t *>(slot + SL::M_OFF);
     const float *gMD = reinterpret_cast<const float *>(slot + SL::MD_OFF);
     const int t0 = ci * C, nreal = min(C, T - t0);
+    const unsigned lo_pair = unsigned((4 * x + G) * 8);  // lane's 8 elements of a pair slot
+    const f4 z4 = {0, 0, 0, 0};
 
-    // Erase strengths (0 past the sequence end: those rows of M are zero, T's are the
-    // identity's), M's fp32 diagonal blocks, zeroed operand slots.
-    for (int t = tid; t < C; t += NT) sh_e[t] = t < nreal ? e[(size_t(b) * T + t0 + t) * H + hh] : 0.f;
-    for (int n = tid; n < NB * 64; n += NT) {
-        const int i = n >> 6, q4 = n & 63;
-        *reinterpret_cast<f32x4_t *>(sh_md + i * TDS + 4 * q4) =
-            *reinterpret_cast<const f32x4_t *>(gMD + i * 256 + 4 * q4);
-    }
+    // Block row and pair index of pair slot ps (wave-uniform).
+    auto pair_rc = [](int ps, int &row, int &m) {
+        int t = 0;
+        while (SL::prow(t + 1) <= ps) ++t;
+        row = t;
+        m = ps - SL::prow(t);
+    };
+
+    // e and the diagonal blocks (unconditional loads, clamped indices), into LDS.
     {
-        const f8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int n = tid; n < NP * (NP + 1) * 64; n += NT) sh_tb[n] = z;
+        const float e_t = e[(size_t(b) * T + t0 + min(tid, nreal - 1)) * H + hh];
+        f32x4_t mdv[NMD];
+#pragma unroll
+        for (int k = 0; k < NMD; ++k) mdv[k] = reinterpret_cast<const f32x4_t *>(gMD)[tid + k * NT];
+        if (tid < C) sh_e[tid] = tid < nreal ? e_t : 0.f;  // 0 past the sequence end
+#pragma unroll
+        for (int k = 0; k < NMD; ++k) {
+            const int n = tid + k * NT, i = n >> 6, s2 = (n >> 2) & 15, c0 = 4 * (n & 3);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c0 + q < s2) sh_md[i * 120 + s2 * (s2 - 1) / 2 + c0 + q] = mdv[k][q];
+        }
     }
     lds_barrier();
 
-    // T_ii, column c: x_t = [t == c] - e_t sum_{s<t} M_ii[t][s] x_s.
-    for (int n = tid; n < NB * 16; n += NT) {
-        const int i = n >> 4, c = n & 15;
-        const float *md = sh_md + i * TDS;
-        const float *ee = sh_e + 16 * i;
-        float xv[16];
+    if (wave < NW / 2) {
+        // Leaves: thread (i, r) solves row r of T_ii from T L = I, right to left:
+        // y_c = [c == r] - sum_{s > c} y_s e_s M_ii[s][c] (y_s = 0 for s > r), in fp32; each
+        // group of four finished values goes to its row fragment at once.
+        const int n = tid;
+        if (n < NB * 16) {
+            const int i = n >> 4, r = n & 15;
+            const float *md = sh_md + i * 120;
+            const float *ee = sh_e + 16 * i;
+            float z[16];
+            f32x4_t y4;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = 0.f;
+            for (int c = 15; c >= 0; --c) {
+                float acc = 0.f;
 #pragma unroll
-            for (int s = 0; s < t; ++s) acc += md[t * 16 + s] * xv[s];
-            xv[t] = (t == c ? 1.f : 0.f) - ee[t] * acc;
+                for (int s2 = c + 1; s2 < 16; ++s2) acc += z[s2] * md[s2 * (s2 - 1) / 2 + c];
+                const float yc = (c == r ? 1.f : 0.f) - acc;
+                z[c] = yc * ee[c];
+                y4[c & 3] = yc;
+                if ((c & 3) == 0) sh_t[slot_of(i, i) * 64 + r + 16 * (c >> 2)] = F::pack(y4);
+            }
         }
+    } else {
+        // M's pair slots into the off-diagonal tile slots. The pair slots holding an off-diagonal
+        // tile are all but the diagonal pair (t, t + 1) of an even row t (an odd row's last pair
+        // holds (t, t - 1) and the diagonal tile); the loads are unconditional (an index past
+        // the last slot reads the last one again).
+        const int wl = wave - NW / 2;
+        f8 mreg[NPL];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) sh_td[i * TDS + t * 16 + c] = xv[t];
+        for (int n = 0; n < NPL; ++n)
+            mreg[n] = F::load8(gT + size_t(min(wl + (NW / 2) * n, NPAIR - 1)) * 512 + lo_pair);
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+            const int ps = wl + (NW / 2) * n;
+            int t, m;
+            if (ps < NPAIR) {
+                pair_rc(ps, t, m);
+                if (2 * m < t) {
+                    sh_t[slot_of(t, 2 * m) * 64 + lane] = F::lo(mreg[n]);
+                    if (2 * m + 1 < t) sh_t[slot_of(t, 2 * m + 1) * 64 + lane] = F::hi(mreg[n]);
+                }
+            }
+        }
     }
     lds_barrier();
 
-    // T_ii in bf16: rows (lane (x, G): T_ii[x][4G..4G+3]) as the A operand, columns
-    // (lane (x, G): T_ii[4G..4G+3][x]) into its operand slot.
-    for (int i = wave; i < NB; i += NW) {
-        const float *td = sh_td + i * TDS;
-        f32x4_t rowv, colv;
+    auto row = [&](int i, int j) { return sh_t[slot_of(i, j) * 64 + lane]; };
+    // Column fragment of tile (i, j) (lane (x, G): T[4G + q][x]) from its row fragment, where
+    // element (row, col) sits in lane row + 16 (col / 4), value col % 4.
+    auto col = [&](int i, int j) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(sh_t + slot_of(i, j) * 64);
+        f4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            rowv[r] = td[x * 16 + 4 * G + r];
-            colv[r] = td[(4 * G + r) * 16 + x];
-        }
-        sh_ta[i * 64 + lane] = F::pack(rowv);
-        reinterpret_cast<f4 *>(tb(i >> 1, i) + lane)[i & 1] = F::pack(colv);
-    }
-    lds_barrier();
-
-    f4 pend[NJ];  // this wavefront's blocks of the previous row, as rows (x, 4G..4G+3)
-    auto flush = [&](int row) {
-#pragma unroll
-        for (int n = 0; n < NJ; ++n) {
-            const int j = wave + NW * n;
-            if (j < row) *reinterpret_cast<f4 *>(gT + SL::blk(row, j, 16 * x + 4 * G)) = pend[n];
-        }
+        for (int q = 0; q < 4; ++q) v[q] = p[(4 * G + q + 16 * (x >> 2)) * 4 + (x & 3)];
+        return v;
     };
-    // M's pairs of row i that this wavefront uses (m >= wave / 2, 2m < i), loaded one row
-    // ahead.
-    const unsigned lo_pair = unsigned((4 * x + G) * 8);
-    f8 mcur[NP], mnext[NP];
-    auto load_row = [&](int i, f8 (&dst)[NP]) {
-        const bf16_t *mrow = gT + size_t(SL::prow(i)) * 512 + lo_pair;
+    static_for<31 - __builtin_clz(NB)>([&](auto Lc) {
+        constexpr int HB = 1 << decltype(Lc)::value;  // tiles per half of a combined block
+        constexpr int NKQ = (HB + 1) / 2;             // K = 32 pairs over a half
+        const int item = wave;                         // NB / 2 items, at most NW
+        const bool active = item < NB / 2;
+        const int p = item / HB;
+        const int base1 = 2 * p * HB, base2 = base1 + HB;  // T11 and T22 tile ranges
+        const int s0 = base1 + item % HB;                  // this item's column tile
+        // Step 1: Q(t, s0) = Diag(e) sum_k M(t, k) T11(k, s0), k over T11's tiles k >= s0; for
+        // HB = 1 the pair's second tile lies outside T11 and is zero.
+        f4 Q[HB];
+        if (active) {
+            f32x4_t acc[HB];
 #pragma unroll
-        for (int m = 0; m < NP; ++m)
-            if (m >= (wave >> 1) && 2 * m < i) dst[m] = F::load8(mrow + size_t(m) * 512);
-    };
-    if (NB > 1) load_row(1, mnext);
-    for (int i = 1; i < NB; ++i) {
-        if (i > 1) flush(i - 1);
+            for (int tt = 0; tt < HB; ++tt) acc[tt] = zero4();
 #pragma unroll
-        for (int m = 0; m < NP; ++m) mcur[m] = mnext[m];
-        if (i + 1 < NB) load_row(i + 1, mnext);
-        const f4 ta = sh_ta[i * 64 + lane];
-        const f32x4_t ev = *reinterpret_cast<const f32x4_t *>(sh_e + 16 * i + 4 * G);
+            for (int kq = 0; kq < NKQ; ++kq) {
+                const int k0 = base1 + 2 * kq;
+                if (k0 + 1 < s0) continue;  // both tiles above T11's diagonal
+                const f8 bt = F::cat(k0 >= s0 ? col(k0, s0) : z4, HB > 1 ? col(k0 + 1, s0) : z4);
 #pragma unroll
-        for (int n = 0; n < NJ; ++n) {
-            const int j = wave + NW * n;
-            if (j < i) {
-                // X = sum over the pairs m holding blocks j .. i - 1 of M(i, pair m) T(pair m, j).
-                // For odd i the last pair's second block is M_ii, stored as zero.
-                f32x4_t X = zero4();
+                for (int tt = 0; tt < HB; ++tt) {
+                    const int t = base2 + tt;
+                    const f8 mt = F::cat(row(t, k0), HB > 1 ? row(t, k0 + 1) : z4);
+                    acc[tt] = F::mma8(mt, bt, acc[tt]);
+                }
+            }
 #pragma unroll
-                for (int m = 0; m < NP; ++m)
-                    if (m >= (j >> 1) && 2 * m < i) X = F::mma8(mcur[m], tb(m, j)[lane], X);
-                const f4 xb = F::pack(X * ev);
-                const f32x4_t y = F::mma16_fresh(ta, xb);   // lane (x, G): (T_ii X)[4G + r][x]
-                const f32x4_t yt = F::mma16_fresh(xb, ta);  // lane (x, G): (T_ii X)[x][4G + r]
-                reinterpret_cast<f4 *>(tb(i >> 1, j) + lane)[i & 1] = F::pack(-y);
-                pend[n] = F::pack(-yt);
+            for (int tt = 0; tt < HB; ++tt) {
+                const f32x4_t ev = *reinterpret_cast<const f32x4_t *>(sh_e + 16 * (base2 + tt) + 4 * G);
+                Q[tt] = F::pack(acc[tt] * ev);
+            }
+        }
+        lds_barrier();  // every read of M21 is done
+        // Step 2: T21(t1, s0) = -sum_t T22(t1, t) Q(t, s0), t over T22's tiles t <= t1; for
+        // HB = 1 the pair is (t1 - 1, t1) and only its second tile is T22's.
+        if (active) {
+#pragma unroll
+            for (int tp = 0; tp < HB; ++tp) {
+                const int t1 = base2 + tp;
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int rq = 0; rq < NKQ; ++rq) {
+                    if (2 * rq > tp) continue;  // tiles above T22's diagonal
+                    const int r0 = HB == 1 ? t1 - 1 : base2 + 2 * rq;
+                    const f4 lo = HB == 1 ? z4 : row(t1, r0);
+                    const f4 hi = r0 + 1 <= t1 ? row(t1, r0 + 1) : z4;
+                    const f8 q = HB == 1 ? F::cat(z4, Q[0])
+                                         : F::cat(Q[2 * rq], Q[2 * rq + 1 < HB ? 2 * rq + 1 : 0]);
+                    acc = F::mma8(q, F::cat(lo, hi), acc);  // lane (x, G): T21[x][4G + q]
+                }
+                sh_t[slot_of(t1, s0) * 64 + lane] = F::pack(-acc);
             }
         }
         lds_barrier();
-    }
-    if (NB > 1) flush(NB - 1);
-    // Diagonal blocks last: for odd i the slot of T_ii is read above as M_ii (zero).
-    for (int i = wave; i < NB; i += NW) {
-        *reinterpret_cast<f4 *>(gT + SL::blk(i, i, 16 * x + 4 * G)) = sh_ta[i * 64 + lane];
-        if ((i & 1) == 0) {
-            const f4 z = {0, 0, 0, 0};
-            *reinterpret_cast<f4 *>(gT + SL::blk(i, i + 1, 16 * x + 4 * G)) = z;
+    });
+
+    // T over M in the workspace, one 16-byte store per lane and pair slot; the second tile of
+    // an even row's diagonal pair is zero.
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+        const int ps = wave + NW * n;
+        int t, m;
+        if (ps < NPAIR) {
+            pair_rc(ps, t, m);
+            const f4 hi = 2 * m + 1 <= t ? row(t, 2 * m + 1) : z4;
+            *reinterpret_cast<f8 *>(gT + size_t(ps) * 512 + lo_pair) = F::cat(row(t, 2 * m), hi);
         }
     }
 }

@@ -43,8 +43,14 @@ def assert_parity(o, s, o_ref, s_ref, what, tol=TOL):
     eo, es = o_err(o, o_ref), s_err(s, s_ref)
     print(f"{what}: max head err o={eo.max():.3e} state={es.max():.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(s).all(), f"{what}: non-finite output"
+    where = ""
+    if eo.max() > tol:
+        b, h = np.unravel_index(np.argmax(eo), eo.shape)
+        diff = np.abs(o[b, :, h].astype(np.float64) - o_ref[b, :, h]).max(axis=-1)
+        bad = np.nonzero(diff > tol * np.abs(o_ref[b, :, h]).max())[0]
+        where = f" worst head (b={b}, h={h}): tokens {bad.min()}..{bad.max()} ({bad.size} rows)"
     assert max(eo.max(), es.max()) <= tol, (f"{what}: o err per head {np.round(eo, 6).tolist()}, "
-                                            f"state err per head {np.round(es, 6).tolist()}")
+                                            f"state err per head {np.round(es, 6).tolist()}{where}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
