@@ -121,6 +121,25 @@ def measured_traffic(kernel):
     return float(m.group(2) if kernel == "prepare" else m.group(3))
 
 
+def measured_mfma():
+    """Matrix-core busy shares of the long-context prepare and scan and the executed-flop share on
+    the matrix cores, from the rocprofv3 counter summary under profiles/, or None when it was
+    taken on different code."""
+    import re
+    path = os.path.join(ROOT, "profiles", "chunk_fwd_mfma_counters.md")
+    try:
+        text = open(path).read()
+        sha = code_sha(*CHUNK_SOURCES)
+    except OSError:
+        return None
+    m = re.search(r"mfma sha=(\w+) prepare_busy=([\d.]+) scan_busy=([\d.]+) mfma_share_executed=([\d.]+)",
+                  text)
+    if not m or m.group(1) != sha:
+        return None
+    return {"prepare_mfma_busy": float(m.group(2)), "scan_mfma_busy": float(m.group(3)),
+            "mfma_share_of_executed_flops": float(m.group(4))}
+
+
 def to_dev(inp, dev):
     import numpy as np
     import torch
@@ -552,7 +571,8 @@ def main():
         result["phases_ms"] = {"prepare": r["prepare_ms"], "scan": r["scan_ms"]}
         result["nan_heads"] = nonfinite_heads(r["o"], r["s_out"])
         main_out = (r["o"], r["s_out"])
-        result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"]}
+        result["call_roofline"] = {"hbm_frac": rep["hbm_frac"], "mfma_frac_bf16": rep["mfma_frac"],
+                                   "counters": measured_mfma()}
         tally = flop_tally(256, 128)
         result["flop_share"] = {"mfma_share_algorithmic": tally["mfma_share"],
                                 "mfma_flops_per_token_head": tally["mfma_flops"],
