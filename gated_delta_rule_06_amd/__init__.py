@@ -94,6 +94,8 @@ def lib():
         L.muir_last_error.restype = ctypes.c_char_p
         L.muir_version.argtypes = []
         L.muir_version.restype = i
+        L.muir_state_bytes.argtypes = [i] * 4
+        L.muir_state_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -108,6 +110,11 @@ def last_error() -> str:
 
 def version() -> int:
     return int(lib().muir_version())
+
+
+def state_bytes(B: int, H: int, dk: int, dv: int) -> int:
+    """Bytes of the fp32 recurrent state of B sequences x H heads (``muir_state_bytes``)."""
+    return int(lib().muir_state_bytes(B, H, dk, dv))
 
 
 def _check(status: int):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmuir.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_fwd.hip", "chunk_bwd.hip", "wy_fwd.hip", "gates_fwd.hip",
+SOURCES = ["api.cpp", "sizes.cpp", "decode.hip", "chunk_fwd.hip", "chunk_bwd.hip", "wy_fwd.hip", "gates_fwd.hip",
            "noalloc.hip", "chunk_scan_split.hip"]
 ARCH = "gfx950"
 

@@ -88,6 +88,15 @@ const char *muir_status_string(muir_status_t s) {
 
 const char *muir_last_error(void) { return g_last_error; }
 
+size_t muir_state_bytes(int B, int H, int dk, int dv) {
+    if (B < 1 || H < 1 || dk < 1 || dv < 1) return 0;
+    size_t n;
+    if (!mul_size(n, {static_cast<size_t>(B), static_cast<size_t>(H), static_cast<size_t>(dk),
+                      static_cast<size_t>(dv), sizeof(float)}))
+        return 0;
+    return n;
+}
+
 size_t muir_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int chunk,
                                      muir_dtype_t qkv) {
     if (B < 1 || T < 0 || H < 1 || dk != dv || !supported_d(dk) || !supported_chunk(chunk))

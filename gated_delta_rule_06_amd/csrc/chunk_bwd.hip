@@ -43,13 +43,14 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "layout.hpp"
 #include "mfma.hpp"
 
 namespace muir {
 
 namespace {
 
-constexpr int kC = 64;        // tokens per chunk
+constexpr int kC = kBwdChunk;  // tokens per chunk
 constexpr int kNB = kC / 16;  // 16-token blocks per chunk
 constexpr int kBwdThreads = 256;
 
@@ -1113,43 +1114,6 @@ __global__ __launch_bounds__(1024) void bwd_dr_kernel(const float *__restrict__ 
     }
 }
 
-// Workspace regions, each 256-byte aligned.
-struct BwdLayout {
-    size_t fwd, o, u, states, kb, kg, qg, gC, M, P, pred, dU, lamC, X3, drp, total;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
-    const size_t fwd = chunk_workspace_bytes(B, T, H, d, kC, bf16);
-    if (fwd == 0 && T > 0) return false;
-    const size_t nc = (size_t(T) + kC - 1) / kC;
-    const size_t BH = size_t(B) * H, tok = size_t(B) * T * H * d;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = off;
-        off += align256(bytes);
-        return at;
-    };
-    L.fwd = take(fwd);
-    L.o = take(tok * (bf16 ? 2 : 4));
-    L.u = take(tok * 4);
-    L.states = take(BH * (nc + 1) * d * d * 4);
-    L.kb = take(BH * nc * kC * d * 4);
-    L.kg = take(BH * nc * kC * d * 4);
-    L.qg = take(BH * nc * kC * d * 4);
-    L.gC = take(BH * nc * d * 4);
-    L.M = take(BH * nc * kC * kC * 4);
-    L.P = take(BH * nc * kC * kC * 4);
-    L.pred = take(tok * 4);
-    L.dU = take(tok * 4);
-    L.lamC = take(BH * nc * d * d * 4);
-    L.X3 = take(tok * 4);
-    L.drp = take(BH * nc * d * 4);
-    L.total = off;
-    return true;
-}
-
 template <typename QT, int D>
 hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *ws, const BwdLayout &L,
                      hipStream_t stream) {
@@ -1210,13 +1174,6 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
 }
 
 }  // namespace
-
-size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d, bool bf16) {
-    if (B < 1 || H < 1 || T < 0 || (d != 64 && d != 128)) return 0;
-    BwdLayout L;
-    if (!bwd_layout(B, T, H, d, bf16, L)) return 0;
-    return L.total;
-}
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &x, int B, int T, int H, int d, bool bf16, void *workspace,
                             hipStream_t stream) {

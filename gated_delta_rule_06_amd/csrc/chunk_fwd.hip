@@ -1371,18 +1371,6 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     if constexpr (SAVE) save_state(nchunks);
 }
 
-template <typename OpT, int D, int C>
-size_t slot_bytes() { return Slot<OpT, D, C>::BYTES; }
-
-size_t slot_bytes_rt(bool bf16, int d, int chunk) {
-#define MUIR_SLOT(D, C) \
-    if (d == D && chunk == C) return bf16 ? slot_bytes<bf16_t, D, C>() : slot_bytes<float, D, C>();
-    MUIR_SLOT(64, 64) MUIR_SLOT(64, 128) MUIR_SLOT(64, 256)
-    MUIR_SLOT(128, 64) MUIR_SLOT(128, 128) MUIR_SLOT(128, 256)
-#undef MUIR_SLOT
-    return 0;
-}
-
 template <typename QT, typename OpT, int D, int C>
 hipError_t prepare_typed(const void *q, const void *k, const float *a, const float *g,
                          const float *r, const LowRankGates &lr, int B, int T, int H,
@@ -1460,15 +1448,6 @@ hipError_t scan_typed(const void *v, const float *e, const float *w, const float
 }
 
 }  // namespace
-
-size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
-    const size_t slot = slot_bytes_rt(bf16, d, chunk);
-    if (slot == 0 || B < 1 || H < 1 || T < 0) return 0;
-    const size_t nchunks = (size_t(T) + chunk - 1) / chunk;
-    const size_t n = size_t(B) * size_t(H) * nchunks;
-    if (n != 0 && slot > SIZE_MAX / n) return 0;
-    return n * slot;
-}
 
 hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, const float *g,
                                 const float *r, int B, int T, int H, int d, int chunk, bool bf16,

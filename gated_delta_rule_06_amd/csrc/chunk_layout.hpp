@@ -7,45 +7,14 @@
 #include <utility>
 
 #include "common.hpp"
+#include "layout.hpp"
 #include "mfma.hpp"
 
 namespace muir {
 
-__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Workspace slot of one (batch, head, chunk). M and P blocks are 16x16 row-major
-// (row = later token t, column = earlier token s), lower-triangular block order; the
-// diagonal blocks of M are kept apart in fp32 (MD) for the leaf solve, and M's own slots
-// for them hold zeros.
-//
-// The matrix-core operands are stored in the order the scan consumes them. Within every
-// group of 32 positions, position 8g + 4h + i holds index 16h + 4g + i of the group
-// (g < 4, h < 2, i < 4): lane group g then finds, in one 8-element load, the indices
-// 4g..4g+3 of both 16-halves. Kg and Qg ([C][D]) are permuted along channels, KbT
-// ([D][C]) along tokens.
-template <typename OpT, int D, int C> struct Slot {
-    static constexpr int NB = C / 16;
-    static constexpr int NPAIR = (NB / 2) * (NB / 2 + 1);  // block-pair slots of M (and of P)
-    static constexpr size_t M_BYTES = size_t(NPAIR) * 512 * sizeof(OpT);
-    static constexpr size_t M_OFF = 0;
-    static constexpr size_t PP_OFF = align256(M_OFF + M_BYTES);       // pair decays [NB/2][D]
-    static constexpr size_t P_OFF = align256(PP_OFF + size_t(NB / 2) * D * 4);
-    static constexpr size_t KG_OFF = align256(P_OFF + M_BYTES);
-    static constexpr size_t QG_OFF = align256(KG_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t KBT_OFF = align256(QG_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t MD_OFF = align256(KBT_OFF + size_t(C) * D * sizeof(OpT));
-    static constexpr size_t BYTES = align256(MD_OFF + size_t(NB) * 256 * 4);
-    // First block-pair slot of block row bt; the row has bt / 2 + 1 of them.
-    static __host__ __device__ constexpr int prow(int bt) {
-        return (bt >> 1) * ((bt >> 1) + 1) + (bt & 1) * ((bt >> 1) + 1);
-    }
-    // Element w = 16 t + s of block (bt, bs). Blocks 2j and 2j + 1 of a row share one
-    // slot, interleaved four elements at a time, so that one 8-element load gives a lane
-    // the same four elements of both (the two halves of a K = 32 operand).
-    static __host__ __device__ constexpr size_t blk(int bt, int bs, int w) {
-        return size_t(prow(bt) + (bs >> 1)) * 512 + ((w >> 2) * 2 + (bs & 1)) * 4 + (w & 3);
-    }
-};
+// Slot<OpT, D, C>: the workspace slot of one (batch, head, chunk) (layout.hpp), for operands of
+// type OpT.
+template <typename OpT, int D, int C> using Slot = SlotLayout<int(sizeof(OpT)), D, C>;
 
 // Storage position of index x under the 32-group permutation described above.
 __host__ __device__ constexpr int pair_perm(int x) {

@@ -255,28 +255,6 @@ __device__ __forceinline__ void buf_store_bf16(rsrc_t r, unsigned voff, unsigned
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, int(voff), int(soff), 0);
 }
 
-// Per (batch, head, chunk) products of the shared-erase form, kept in a workspace region
-// after the prepare kernel's slots (same (b, h, chunk) order). With W = T Diag(e) (K*gamma)
-// and U~ = T (w*v) (never stored):
-//   AT: A~ = (K*beta)^T W as the state scan's A operand (rows = channels i, positions =
-//       channels j in the 32-group order), [D/16][D/32][64 lanes][8] bf16
-//   BC: (K*beta)^T U~ in accumulator layout per (channel tile, value tile), [D/16][D/16][64][4] fp32
-//   GC: gamma_C, the chunk's whole decay per channel, [D] fp32
-//   QT: Q~ = (Qh*gamma) - P W, A operand like Qg (rows = tokens), [C/16][D/32][64][8] bf16
-//   OT: O~ = P U~ in accumulator layout per (leaf, value tile), [C/16][D/16][64][4] bf16
-//   SC: the chunk's start state as B operand per (value tile, channel group), [D/16][D/32][64][8] bf16
-// so that for a chunk with start state S:  S_next = Diag(gamma_C) S - A~ S + BC  and
-// O = Q~ S + O~.
-template <int D, int C> struct XSlot {
-    static constexpr size_t AT_OFF = 0;
-    static constexpr size_t BC_OFF = AT_OFF + size_t(D) * D * 2;
-    static constexpr size_t GC_OFF = BC_OFF + size_t(D) * D * 4;
-    static constexpr size_t QT_OFF = align256(GC_OFF + size_t(D) * 4);
-    static constexpr size_t OT_OFF = QT_OFF + size_t(C) * D * 2;
-    static constexpr size_t SC_OFF = OT_OFF + size_t(C) * D * 2;
-    static constexpr size_t BYTES = align256(SC_OFF + size_t(D) * D * 2);
-};
-
 // Token blocks (16 tokens) a wavefront of an NW-wavefront workgroup takes in the chunk-parallel
 // kernels: blocks w and 2 NW - 1 - w when there are 2 NW of them (equal work under the
 // triangular pair loops), else block w.
@@ -636,9 +614,6 @@ __global__ __launch_bounds__(512) void wy_output_kernel(bf16_t *__restrict__ o,
 }
 
 template <int D, int C>
-size_t wy_bytes() { return Slot<bf16_t, D, C>::BYTES + XSlot<D, C>::BYTES; }
-
-template <int D, int C>
 hipError_t solve_typed(const void *v, const float *e, const float *w, int B, int T, int H,
                        void *workspace, hipStream_t stream) {
     const int nchunks = (T + C - 1) / C;
@@ -684,20 +659,6 @@ hipError_t wy_scan_typed(const float *s0, void *o, float *s_out, int B, int T, i
 }
 
 }  // namespace
-
-size_t wy_workspace_bytes(int B, int T, int H, int d, int chunk) {
-    size_t per = 0;
-#define MUIR_WY(D, C) \
-    if (d == D && chunk == C) per = wy_bytes<D, C>();
-    MUIR_WY(64, 64) MUIR_WY(64, 128) MUIR_WY(64, 256)
-    MUIR_WY(128, 64) MUIR_WY(128, 128) MUIR_WY(128, 256)
-#undef MUIR_WY
-    if (per == 0 || B < 1 || H < 1 || T < 0) return 0;
-    const size_t nchunks = (size_t(T) + chunk - 1) / chunk;
-    const size_t n = size_t(B) * size_t(H) * nchunks;
-    if (n != 0 && per > SIZE_MAX / n) return 0;
-    return n * per;
-}
 
 hipError_t launch_wy_solve(const void *v, const float *e, const float *w, int B, int T, int H,
                            int d, int chunk, void *workspace, hipStream_t stream) {

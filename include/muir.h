@@ -43,8 +43,9 @@
 extern "C" {
 #endif
 
-/* A hipStream_t passed as a plain pointer. */
-typedef void *muir_stream_t;
+/* The HIP stream type itself (hipStream_t is this same pointer type), declared here so that
+ * C callers need no HIP header; NULL is the default stream. */
+typedef struct ihipStream_t *muir_stream_t;
 
 typedef enum {
     MUIR_OK = 0,
@@ -366,6 +367,17 @@ muir_status_t muir_chunk_bwd(
     float *dr, float *ds0,
     int B, int T, int H, int dk_, int dv_, int chunk, muir_dtype_t qkv,
     void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
+ * Bytes of the recurrent state of B sequences x H heads, one dk x dv fp32 matrix per head:
+ * what muir_decode_step reads and writes per layer and what s0 / s_out of the chunk forward
+ * hold. It does not depend on the sequence length: inference runs in constant memory
+ * (openai-hub news page, opening section, and the liuch.name summary, opening paragraph: the
+ * 24 layers of the 1.34B model, 16 heads of d = 128, keep about 25 MB of fp32 state, here
+ * 24 x muir_state_bytes(1, 16, 128, 128) = 25,165,824 bytes per sequence).
+ * 0 when a size is below 1 or the product overflows.
+ */
+size_t muir_state_bytes(int B, int H, int dk, int dv);
 
 /* Static, never-NULL name of a status code ("MUIR_OK", ...). */
 const char *muir_status_string(muir_status_t s);

@@ -134,7 +134,8 @@ int oracle_max_threads(void)
  * operations in the same order, so the same values).
  *
  * Layouts as for the forward; dS may be NULL (zero), s0 may be NULL (zero). Outputs:
- * dq, dk, da, dla, dg [B,T,H,dk]; dv, de, dw [B,T,H,dv]; dr [H,dk]; ds0 [B,H,dk,dv].
+ * dq, dk, da, dla, dg [B,T,H,dk]; dv, de, dw [B,T,H,dv]; dr [H,dk]; ds0 [B,H,dk,dv] (may be
+ * NULL: not written).
  * Work is split over (b, h) with OpenMP; dr is summed over b afterwards in a fixed order.
  */
 #define SEG 128
@@ -239,7 +240,7 @@ int oracle_grads_f64(int B, int T, int H, int dk, int dv,
             }
         }
         #undef FWD_TOKEN
-        memcpy(ds0 + ((size_t)b * H + h) * dd, lam, sizeof(double) * dd);
+        if (ds0) memcpy(ds0 + ((size_t)b * H + h) * dd, lam, sizeof(double) * dd);
         free(ck); free(prev); free(ps); free(us); free(S); free(lam); free(mu); free(vec);
     }
     for (int h = 0; h < H; ++h)

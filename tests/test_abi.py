@@ -380,6 +380,14 @@ def test_c_program_builds_and_calls_the_library(tmp_path):
     if cxx is not None:
         subprocess.run([cxx, "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", f"-I{inc}", "-x", "c++",
                         str(src)], check=True)
+    hip_inc = "/opt/rocm/include"
+    if cxx is not None and os.path.exists(os.path.join(hip_inc, "hip", "hip_runtime_api.h")):
+        # The stream parameter is HIP's own stream type: a hipStream_t passes without a cast.
+        same = tmp_path / "stream_type.cpp"
+        same.write_text('#include <type_traits>\n#include <hip/hip_runtime_api.h>\n#include "muir.h"\n'
+                        "static_assert(std::is_same<muir_stream_t, hipStream_t>::value, \"stream\");\n")
+        subprocess.run([cxx, "-std=c++17", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", f"-I{inc}",
+                        f"-I{hip_inc}", str(same)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
     version, ws, status, name, detail = out.stdout.split()
@@ -398,3 +406,26 @@ def test_noalloc_refuses_workspace_beyond_its_scratch():
     st = lib.muir_chunk_fwd_noalloc(*[fake(i) for i in range(11)], 1, 32768, 16, 128, 128, 256,
                                     muir.MUIR_BF16, None)
     assert st == 4 and "static scratch" in muir.last_error(), muir.last_error()
+
+
+def test_state_bytes_of_the_24_layer_model():
+    """Constant-memory inference (openai-hub news page, opening section; liuch.name summary,
+    opening paragraph): the 24 layers of the 1.34B model, 16 heads of d = 128, keep about
+    25 MB of fp32 state per sequence, exactly 24 x 16 x 128 x 128 x 4 = 25,165,824 bytes,
+    whatever the sequence length (the size takes no T), while the chunk workspace grows
+    with T. The decode step and the chunk forward take state buffers of exactly that size."""
+    per_layer = muir.state_bytes(1, 16, 128, 128)
+    assert 24 * per_layer == 25_165_824
+    assert muir.state_bytes(8, 16, 128, 128) == 8 * per_layer
+    assert muir.state_bytes(1, 16, 64, 64) == 16 * 64 * 64 * 4
+    assert muir.state_bytes(0, 16, 128, 128) == 0 and muir.state_bytes(1, 16, 128, -1) == 0
+    big = 2**31 - 1
+    assert muir.state_bytes(big, big, big, big) == 0  # the product overflows
+    ws = [muir.chunk_fwd_workspace_size(1, t, 16, 128, 128, 256, muir.MUIR_BF16)
+          for t in (4096, 32768)]
+    assert ws[1] == 8 * ws[0]
+    # A state buffer of any other size is refused before anything is launched.
+    import torch
+    x = torch.zeros(1, 16, 128)
+    with pytest.raises(ValueError):
+        muir.decode_step(x, x, x, x, x, x, x, torch.zeros(16, 128), torch.zeros(1, 16, 128, 64))
