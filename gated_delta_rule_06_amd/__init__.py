@@ -82,6 +82,12 @@ def lib():
         L.muir_chunk_fwd_lowrank.restype = i
         L.muir_lowrank_gates.argtypes = [vp] * 13 + [i] * 4 + [vp]
         L.muir_lowrank_gates.restype = i
+        L.muir_lowrank_output_gate.argtypes = [vp] * 4 + [i] * 4 + [vp]
+        L.muir_lowrank_output_gate.restype = i
+        L.muir_chunk_fwd_lowrank_gated_workspace_size.argtypes = [i] * 6
+        L.muir_chunk_fwd_lowrank_gated_workspace_size.restype = sz
+        L.muir_chunk_fwd_lowrank_gated.argtypes = [vp] * 18 + [i] * 7 + [vp, sz, vp]
+        L.muir_chunk_fwd_lowrank_gated.restype = i
         L.muir_chunk_bwd_workspace_size.argtypes = [i] * 7
         L.muir_chunk_bwd_workspace_size.restype = sz
         L.muir_chunk_bwd.argtypes = [vp] * 20 + [i] * 7 + [vp, sz, vp]
@@ -421,11 +427,8 @@ def lowrank_gates(z, U, c, *, H: int, d: int, which=("a", "e", "w", "g"), out=No
     return {k: v for k, v in out.items() if k in which}
 
 
-def chunk_fwd_lowrank(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None, s_out=None,
-                      return_state: bool = True, workspace=None):
-    """Chunk forward with the gates made from the low-rank gate projection inside the call
-    (``muir_chunk_fwd_lowrank``). q, k, v bfloat16 as for :func:`chunk_fwd`; z, U, c as for
-    :func:`lowrank_gates` (all four gates). Returns (o, s_out)."""
+def _chunk_fwd_lowrank(q, k, v, z, U, c, r, s0, chunk, o, s_out, return_state, workspace,
+                       gated: bool):
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -433,8 +436,9 @@ def chunk_fwd_lowrank(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None,
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require(t, name, torch.bfloat16, (B, T, H, dk if name != "v" else dv), dev)
     _require(z, "z", torch.bfloat16, (B, T, 512), dev)
-    for n, rk in (("decay", 64), ("erase", 64), ("write", 128), ("read", 128)):
-        _require(U[n], "U_" + n, torch.bfloat16, (H, dk, rk), dev)
+    names = ("decay", "erase", "write", "read") + (("output",) if gated else ())
+    for n in names:
+        _require(U[n], "U_" + n, torch.bfloat16, (H, dk, 64 if n in ("decay", "erase") else 128), dev)
         _require(c[n], "c_" + n, torch.float32, (H, dk), dev)
     _require(r, "r", torch.float32, (H, dk), dev)
     if s0 is not None:
@@ -443,15 +447,56 @@ def chunk_fwd_lowrank(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None,
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     if s_out is None and return_state:
         s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    need = int(lib().muir_chunk_fwd_lowrank_workspace_size(B, T, H, dk, dv, chunk))
+    size = (lib().muir_chunk_fwd_lowrank_gated_workspace_size if gated
+            else lib().muir_chunk_fwd_lowrank_workspace_size)
+    need = int(size(B, T, H, dk, dv, chunk))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib().muir_chunk_fwd_lowrank(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(U["decay"]), _ptr(U["erase"]), _ptr(U["write"]),
-        _ptr(U["read"]), _ptr(c["decay"]), _ptr(c["erase"]), _ptr(c["write"]), _ptr(c["read"]),
-        _ptr(r), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, MUIR_BF16,
-        _ptr(workspace), workspace.numel(), _stream(dev)))
+    ups = [_ptr(U[n]) for n in ("decay", "erase", "write", "read")]
+    offs = [_ptr(c[n]) for n in ("decay", "erase", "write", "read")]
+    tail = (_ptr(r), _ptr(s0), _ptr(o), _ptr(s_out), B, T, H, dk, dv, chunk, MUIR_BF16,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if gated:
+        _check(lib().muir_chunk_fwd_lowrank_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z), *ups,
+                                                  _ptr(U["output"]), *offs, _ptr(c["output"]), *tail))
+    else:
+        _check(lib().muir_chunk_fwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(z), *ups, *offs, *tail))
     return o, s_out
+
+
+def chunk_fwd_lowrank(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None, s_out=None,
+                      return_state: bool = True, workspace=None):
+    """Chunk forward with the gates made from the low-rank gate projection inside the call
+    (``muir_chunk_fwd_lowrank``). q, k, v bfloat16 as for :func:`chunk_fwd`; z, U, c as for
+    :func:`lowrank_gates` (all four gates). Returns (o, s_out)."""
+    return _chunk_fwd_lowrank(q, k, v, z, U, c, r, s0, chunk, o, s_out, return_state, workspace,
+                              False)
+
+
+def chunk_fwd_lowrank_gated(q, k, v, z, U, c, r, s0=None, *, chunk: int = 256, o=None,
+                            s_out=None, return_state: bool = True, workspace=None):
+    """As :func:`chunk_fwd_lowrank` with the output gate too (``muir_chunk_fwd_lowrank_gated``):
+    U and c also hold "output" ([H, d, 128] bf16, [H, d] fp32); the readout is o * og."""
+    return _chunk_fwd_lowrank(q, k, v, z, U, c, r, s0, chunk, o, s_out, return_state, workspace,
+                              True)
+
+
+def lowrank_output_gate(z, Uo, co, *, out=None):
+    """The output gate og [B, T, H, d] fp32 from z's output slice (``muir_lowrank_output_gate``):
+    z [B, T, 512] bf16, Uo [H, d, 128] bf16, co [H, d] fp32."""
+    import torch
+    B, T, _ = z.shape
+    H, d, _ = Uo.shape
+    dev = z.device
+    _require(z, "z", torch.bfloat16, (B, T, 512), dev)
+    _require(Uo, "Uo", torch.bfloat16, (H, d, 128), dev)
+    _require(co, "co", torch.float32, (H, d), dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    _require(out, "og", torch.float32, (B, T, H, d), dev)
+    _check(lib().muir_lowrank_output_gate(_ptr(z), _ptr(Uo), _ptr(co), _ptr(out), B, T, H, d,
+                                          _stream(dev)))
+    return out
 
 
 def decode_step(q, k, v, a, g, e, w, r, state, *, o=None):

@@ -391,105 +391,29 @@ muir_status_t muir_chunk_fwd_scalar_erase_scan(const float *s0, void *o, float *
                      "chunk_fwd_scalar_erase_scan launch");
 }
 
-size_t muir_chunk_fwd_lowrank_workspace_size(int B, int T, int H, int dk, int dv, int chunk) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of the fused low-rank forward: the plain forward's, then (256-byte aligned) e and
+// w [B, T, H, dv] fp32, and with the output gate og as well.
+size_t lowrank_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, bool gated) {
     const size_t base = muir_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, MUIR_BF16);
     if (base == 0 && T > 0) return 0;
     size_t gates;
     if (!mul_size(gates, {static_cast<size_t>(B), static_cast<size_t>(T), static_cast<size_t>(H),
-                          static_cast<size_t>(dv), 8}))
+                          static_cast<size_t>(dv), gated ? size_t(12) : size_t(8)}))
         return 0;
     const size_t aligned = (base + 255) & ~size_t(255);
     return aligned + gates < aligned ? 0 : aligned + gates;
 }
 
-muir_status_t muir_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const void *z,
-                                     const void *Ua, const void *Ue, const void *Uw,
-                                     const void *Ug, const float *ca, const float *ce,
-                                     const float *cw, const float *cg, const float *r,
-                                     const float *s0, void *o, float *s_out, int B, int T, int H,
-                                     int dk, int dv, int chunk, muir_dtype_t qkv, void *workspace,
-                                     size_t workspace_bytes, muir_stream_t stream) {
-    const char *fn = "chunk_fwd_lowrank";
-    if (qkv != MUIR_BF16)
-        return fail(MUIR_ERR_UNSUPPORTED, "%s: the fused low-rank gates need bf16 q, k, v", fn);
-    // Shape, pointer, alignment and aliasing checks of the plain forward, with the gate
-    // tensors standing in as absent: the gates are made inside the call.
-    const size_t base = muir::chunk_workspace_bytes(B, T, H, dk, chunk, true);
-    const size_t ebase = (base + 255) & ~size_t(255);
-    ChunkCall c{fn, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr, r, s0, o, s_out, B, T, H,
-                dk, dv, chunk, qkv, workspace, workspace_bytes, false, false, false};
-    muir_status_t st = validate(c);
-    if (st != MUIR_OK) return st;
-    if (T > 0 && (!q || !k || !v || !o || !z)) return fail(MUIR_ERR_NULL, "%s: q, k, v, z and o are required", fn);
-    if (!r || !Ua || !Ue || !Uw || !Ug || !ca || !ce || !cw || !cg)
-        return fail(MUIR_ERR_NULL, "%s: r and every up-projection and offset are required", fn);
-    const size_t need = muir_chunk_fwd_lowrank_workspace_size(B, T, H, dk, dv, chunk);
-    if (need == 0 && T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
-    if (T > 0 && (!workspace || workspace_bytes < need))
-        return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
-    if (static_cast<size_t>(T) * 512 * 2 > 0xffffffffu)
-        return fail(MUIR_ERR_UNSUPPORTED, "%s: one batch row of z exceeds 4 GiB", fn);
-    const size_t n_tok = static_cast<size_t>(B) * T * H * dk;
-    const Range ins[] = {range("q", q, n_tok * 2), range("k", k, n_tok * 2), range("v", v, n_tok * 2),
-                         range("z", z, static_cast<size_t>(B) * T * 512 * 2),
-                         range("Ua", Ua, static_cast<size_t>(H) * dk * 64 * 2),
-                         range("Ue", Ue, static_cast<size_t>(H) * dv * 64 * 2),
-                         range("Uw", Uw, static_cast<size_t>(H) * dv * 128 * 2),
-                         range("Ug", Ug, static_cast<size_t>(H) * dk * 128 * 2),
-                         range("ca", ca, static_cast<size_t>(H) * dk * 4), range("ce", ce, static_cast<size_t>(H) * dv * 4),
-                         range("cw", cw, static_cast<size_t>(H) * dv * 4), range("cg", cg, static_cast<size_t>(H) * dk * 4)};
-    const Range outs[] = {range("o", o, n_tok * 2), range("workspace", workspace, need),
-                          range("s_out", s_out, static_cast<size_t>(B) * H * dk * dv * 4)};
-    for (const Range &x : ins) {
-        if (x.lo % 16 != 0) return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
-        for (const Range &y : outs)
-            if (overlaps(x, y)) return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, y.name, x.name);
-    }
-    // validate() checked s0 and r against the base forward's workspace only; the gate kernel
-    // writes e and w past it, up to `need`. s0 may still be s_out (the state in place).
-    const Range rs0 = range("s0", s0, static_cast<size_t>(B) * H * dk * dv * 4);
-    const Range rr = range("r", r, static_cast<size_t>(H) * dk * 4);
-    for (const Range &x : {rs0, rr})
-        for (int i = 0; i < 2; ++i)
-            if (overlaps(x, outs[i]))
-                return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, outs[i].name, x.name);
-    if (T == 0) {
-        if (!s_out) return ok();
-        return check_hip(muir::launch_chunk_scan(v, nullptr, nullptr, nullptr, s0, o, s_out, B, T, H,
-                                                 dk, chunk, true, workspace,
-                                                 static_cast<hipStream_t>(stream)),
-                         fn);
-    }
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    // e and w: made inside the scan where its LDS allows, else by the gate kernel into the
-    // workspace's tail first.
-    const bool in_scan = muir::scan_gates_in_kernel(B, H, dv, chunk);
-    float *e = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ebase);
-    float *w = e + n_tok;
-    if (!in_scan) {
-        st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, nullptr, ce, cw,
-                                                  nullptr, nullptr, e, w, nullptr, B, T, H, dv, hs),
-                       "chunk_fwd_lowrank gates");
-        if (st != MUIR_OK) return st;
-    }
-    st = check_hip(muir::launch_chunk_prepare_lowrank(q, k, z, Ua, Ug, ca, cg, r, B, T, H, dk, chunk,
-                                                      workspace, hs),
-                   "chunk_fwd_lowrank prepare");
-    if (st != MUIR_OK) return st;
-    if (in_scan)
-        return check_hip(muir::launch_chunk_scan_lowrank(v, z, Ue, Uw, ce, cw, s0, o, s_out, B, T, H,
-                                                         dk, chunk, workspace, hs),
-                         "chunk_fwd_lowrank scan");
-    return check_hip(muir::launch_chunk_scan(v, e, w, nullptr, s0, o, s_out, B, T, H, dk, chunk, true,
-                                             workspace, hs),
-                     "chunk_fwd_lowrank scan");
-}
-
-muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
-                                const void *Ug, const float *ca, const float *ce, const float *cw,
-                                const float *cg, float *a, float *e, float *w, float *g, int B,
-                                int T, int H, int d, muir_stream_t stream) {
-    const char *fn = "lowrank_gates";
+// The gate entry points: every requested gate (non-null output) of the five from z.
+muir_status_t lowrank_gates_impl(const char *fn, const void *z, const void *Ua, const void *Ue,
+                                 const void *Uw, const void *Ug, const void *Uo, const float *ca,
+                                 const float *ce, const float *cw, const float *cg,
+                                 const float *co, float *a, float *e, float *w, float *g,
+                                 float *og, int B, int T, int H, int d, muir_stream_t stream) {
     if (B < 1 || T < 0 || H < 1)
         return fail(MUIR_ERR_SHAPE, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
     if (!supported_d(d)) return fail(MUIR_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
@@ -499,7 +423,9 @@ muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, 
         const float *c;
         float *out;
         size_t rank;
-    } gates[] = {{"a", Ua, ca, a, 64}, {"e", Ue, ce, e, 64}, {"w", Uw, cw, w, 128}, {"g", Ug, cg, g, 128}};
+    } gates[] = {{"a", Ua, ca, a, 64}, {"e", Ue, ce, e, 64}, {"w", Uw, cw, w, 128},
+                 {"g", Ug, cg, g, 128}, {"og", Uo, co, og, 128}};
+    constexpr size_t NG = sizeof(gates) / sizeof(gates[0]);
     bool any = false;
     for (const Gate &gt : gates) {
         if (!gt.out) continue;
@@ -515,7 +441,7 @@ muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, 
         return fail(MUIR_ERR_SHAPE, "%s: sizes overflow", fn);
     if (static_cast<size_t>(T) * H * d * 4 > 0xffffffffu || static_cast<size_t>(T) * 512 * 2 > 0xffffffffu)
         return fail(MUIR_ERR_UNSUPPORTED, "%s: one batch row's gates or z exceed 4 GiB", fn);
-    std::initializer_list<const void *> ptrs = {z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g};
+    std::initializer_list<const void *> ptrs = {z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og};
     for (const void *p : ptrs)
         if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
             return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
@@ -524,18 +450,158 @@ muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, 
         ins.push_back(range(gt.name, gt.U, static_cast<size_t>(H) * d * gt.rank * 2));
         ins.push_back(range(gt.name, gt.c, static_cast<size_t>(H) * d * 4));
     }
-    for (size_t i = 0; i < 4; ++i) {
+    for (size_t i = 0; i < NG; ++i) {
         const Range ro = range(gates[i].name, gates[i].out, n_tok * 4);
         for (const Range &x : ins)
             if (overlaps(ro, x)) return fail(MUIR_ERR_ALIAS, "%s: gate %s overlaps an input", fn, gates[i].name);
-        for (size_t j = i + 1; j < 4; ++j)
+        for (size_t j = i + 1; j < NG; ++j)
             if (overlaps(ro, range(gates[j].name, gates[j].out, n_tok * 4)))
                 return fail(MUIR_ERR_ALIAS, "%s: gates %s and %s overlap", fn, gates[i].name, gates[j].name);
     }
     if (!any || T == 0) return ok();
-    return check_hip(muir::launch_lowrank_gates(z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g, B,
-                                                T, H, d, static_cast<hipStream_t>(stream)),
-                     "lowrank_gates launch");
+    return check_hip(muir::launch_lowrank_gates(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g,
+                                                og, B, T, H, d, static_cast<hipStream_t>(stream)),
+                     fn);
+}
+
+// The fused low-rank forward; with Uo the output gate as well (`gated`).
+muir_status_t chunk_fwd_lowrank_impl(const char *fn, const void *q, const void *k, const void *v,
+                                     const void *z, const void *Ua, const void *Ue, const void *Uw,
+                                     const void *Ug, const void *Uo, const float *ca,
+                                     const float *ce, const float *cw, const float *cg,
+                                     const float *co, const float *r, const float *s0, void *o,
+                                     float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+                                     muir_dtype_t qkv, void *workspace, size_t workspace_bytes,
+                                     muir_stream_t stream, bool gated) {
+    if (qkv != MUIR_BF16)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: the fused low-rank gates need bf16 q, k, v", fn);
+    // Shape, pointer, alignment and aliasing checks of the plain forward, with the gate
+    // tensors standing in as absent: the gates are made inside the call.
+    const size_t base = muir::chunk_workspace_bytes(B, T, H, dk, chunk, true);
+    const size_t ebase = (base + 255) & ~size_t(255);
+    ChunkCall c{fn, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr, r, s0, o, s_out, B, T, H,
+                dk, dv, chunk, qkv, workspace, workspace_bytes, false, false, false};
+    muir_status_t st = validate(c);
+    if (st != MUIR_OK) return st;
+    if (T > 0 && (!q || !k || !v || !o || !z)) return fail(MUIR_ERR_NULL, "%s: q, k, v, z and o are required", fn);
+    if (!r || !Ua || !Ue || !Uw || !Ug || !ca || !ce || !cw || !cg || (gated && (!Uo || !co)))
+        return fail(MUIR_ERR_NULL, "%s: r and every up-projection and offset are required", fn);
+    const size_t need = lowrank_workspace_bytes(B, T, H, dk, dv, chunk, gated);
+    if (need == 0 && T > 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (T > 0 && (!workspace || workspace_bytes < need))
+        return fail(MUIR_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+    if (static_cast<size_t>(T) * 512 * 2 > 0xffffffffu)
+        return fail(MUIR_ERR_UNSUPPORTED, "%s: one batch row of z exceeds 4 GiB", fn);
+    const size_t n_tok = static_cast<size_t>(B) * T * H * dk;
+    const Range ins[] = {range("q", q, n_tok * 2), range("k", k, n_tok * 2), range("v", v, n_tok * 2),
+                         range("z", z, static_cast<size_t>(B) * T * 512 * 2),
+                         range("Ua", Ua, static_cast<size_t>(H) * dk * 64 * 2),
+                         range("Ue", Ue, static_cast<size_t>(H) * dv * 64 * 2),
+                         range("Uw", Uw, static_cast<size_t>(H) * dv * 128 * 2),
+                         range("Ug", Ug, static_cast<size_t>(H) * dk * 128 * 2),
+                         range("Uo", gated ? Uo : nullptr, static_cast<size_t>(H) * dv * 128 * 2),
+                         range("ca", ca, static_cast<size_t>(H) * dk * 4), range("ce", ce, static_cast<size_t>(H) * dv * 4),
+                         range("cw", cw, static_cast<size_t>(H) * dv * 4), range("cg", cg, static_cast<size_t>(H) * dk * 4),
+                         range("co", gated ? co : nullptr, static_cast<size_t>(H) * dv * 4)};
+    const Range outs[] = {range("o", o, n_tok * 2), range("workspace", workspace, need),
+                          range("s_out", s_out, static_cast<size_t>(B) * H * dk * dv * 4)};
+    for (const Range &x : ins) {
+        if (x.lo % 16 != 0) return fail(MUIR_ERR_SHAPE, "%s: every buffer must be 16-byte aligned", fn);
+        for (const Range &y : outs)
+            if (overlaps(x, y)) return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, y.name, x.name);
+    }
+    // validate() checked s0 and r against the base forward's workspace only; the gate kernel
+    // writes e and w (and og) past it, up to `need`. s0 may still be s_out (the state in place).
+    const Range rs0 = range("s0", s0, static_cast<size_t>(B) * H * dk * dv * 4);
+    const Range rr = range("r", r, static_cast<size_t>(H) * dk * 4);
+    for (const Range &x : {rs0, rr})
+        for (int i = 0; i < 2; ++i)
+            if (overlaps(x, outs[i]))
+                return fail(MUIR_ERR_ALIAS, "%s: %s overlaps %s", fn, outs[i].name, x.name);
+    if (T == 0) {
+        if (!s_out) return ok();
+        return check_hip(muir::launch_chunk_scan(v, nullptr, nullptr, nullptr, s0, o, s_out, B, T, H,
+                                                 dk, chunk, true, workspace,
+                                                 static_cast<hipStream_t>(stream)),
+                         fn);
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // The gates the scan reads (e, w and og): made inside the scan where its LDS allows, else
+    // by the gate kernel into the workspace's tail first.
+    const bool in_scan = muir::scan_gates_in_kernel(B, H, dv, chunk);
+    float *e = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ebase);
+    float *w = e + n_tok;
+    float *og = gated ? w + n_tok : nullptr;
+    if (!in_scan) {
+        st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, gated ? Uo : nullptr,
+                                                  nullptr, ce, cw, nullptr, gated ? co : nullptr,
+                                                  nullptr, e, w, nullptr, og, B, T, H, dv, hs),
+                       fn);
+        if (st != MUIR_OK) return st;
+    }
+    st = check_hip(muir::launch_chunk_prepare_lowrank(q, k, z, Ua, Ug, ca, cg, r, B, T, H, dk, chunk,
+                                                      workspace, hs),
+                   fn);
+    if (st != MUIR_OK) return st;
+    if (in_scan)
+        return check_hip(muir::launch_chunk_scan_lowrank(v, z, Ue, Uw, ce, cw, gated ? Uo : nullptr,
+                                                         gated ? co : nullptr, s0, o, s_out, B, T,
+                                                         H, dk, chunk, workspace, hs),
+                         fn);
+    return check_hip(muir::launch_chunk_scan(v, e, w, og, s0, o, s_out, B, T, H, dk, chunk, true,
+                                             workspace, hs),
+                     fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muir_chunk_fwd_lowrank_workspace_size(int B, int T, int H, int dk, int dv, int chunk) {
+    return lowrank_workspace_bytes(B, T, H, dk, dv, chunk, false);
+}
+
+size_t muir_chunk_fwd_lowrank_gated_workspace_size(int B, int T, int H, int dk, int dv, int chunk) {
+    return lowrank_workspace_bytes(B, T, H, dk, dv, chunk, true);
+}
+
+muir_status_t muir_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const void *z,
+                                     const void *Ua, const void *Ue, const void *Uw,
+                                     const void *Ug, const float *ca, const float *ce,
+                                     const float *cw, const float *cg, const float *r,
+                                     const float *s0, void *o, float *s_out, int B, int T, int H,
+                                     int dk, int dv, int chunk, muir_dtype_t qkv, void *workspace,
+                                     size_t workspace_bytes, muir_stream_t stream) {
+    return chunk_fwd_lowrank_impl("chunk_fwd_lowrank", q, k, v, z, Ua, Ue, Uw, Ug, nullptr, ca, ce,
+                                  cw, cg, nullptr, r, s0, o, s_out, B, T, H, dk, dv, chunk, qkv,
+                                  workspace, workspace_bytes, stream, false);
+}
+
+muir_status_t muir_chunk_fwd_lowrank_gated(
+    const void *q, const void *k, const void *v, const void *z, const void *Ua, const void *Ue,
+    const void *Uw, const void *Ug, const void *Uo, const float *ca, const float *ce,
+    const float *cw, const float *cg, const float *co, const float *r, const float *s0, void *o,
+    float *s_out, int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream) {
+    return chunk_fwd_lowrank_impl("chunk_fwd_lowrank_gated", q, k, v, z, Ua, Ue, Uw, Ug, Uo, ca, ce,
+                                  cw, cg, co, r, s0, o, s_out, B, T, H, dk, dv, chunk, qkv,
+                                  workspace, workspace_bytes, stream, true);
+}
+
+muir_status_t muir_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
+                                const void *Ug, const float *ca, const float *ce, const float *cw,
+                                const float *cg, float *a, float *e, float *w, float *g, int B,
+                                int T, int H, int d, muir_stream_t stream) {
+    return lowrank_gates_impl("lowrank_gates", z, Ua, Ue, Uw, Ug, nullptr, ca, ce, cw, cg, nullptr,
+                              a, e, w, g, nullptr, B, T, H, d, stream);
+}
+
+muir_status_t muir_lowrank_output_gate(const void *z, const void *Uo, const float *co, float *og,
+                                       int B, int T, int H, int d, muir_stream_t stream) {
+    if (T > 0 && !og) return fail(MUIR_ERR_NULL, "lowrank_output_gate: og is required");
+    return lowrank_gates_impl("lowrank_output_gate", z, nullptr, nullptr, nullptr, nullptr, Uo,
+                              nullptr, nullptr, nullptr, nullptr, co, nullptr, nullptr, nullptr,
+                              nullptr, og, B, T, H, d, stream);
 }
 
 muir_status_t muir_decode_step(const void *q, const void *k, const void *v, const float *a,

@@ -873,13 +873,17 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 // chain into LDS, one matrix-core tile per 16-token leaf and rank step (rows = the tile's
 // value columns, columns = tokens, so its accumulator is the chain's row layout), in the
 // same order of operations as the standalone gate kernel, so the values are the same bits.
+// With GATED, the same wavefront also forms the output gate og = sigmoid(z_output . U_o +
+// c_o) of the chain's current chunk into LDS, where the readout takes it a chunk later.
 // Built for 16-column tiles only.
 struct ScanGates {
     const bf16_t *z;          // [B, T, 512]
     const bf16_t *Ue, *Uw;    // [H, D, 64], [H, D, 128]
     const float *ce, *cw;     // [H, D]
+    const bf16_t *Uo;         // [H, D, 128] (LRS with GATED)
+    const float *co;          // [H, D]
 };
-constexpr int kZOffErase = 64, kZOffWrite = 256;
+constexpr int kZOffErase = 64, kZOffOutput = 128, kZOffWrite = 256;
 // What the forward keeps for the backward pass (SAVE): u = b - e * p of every token in fp32,
 // [B, T, H, D] like v, and the state at every chunk start and at the end, fp32
 // [B * H][nchunks + 1][D][D].
@@ -919,6 +923,10 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     // chunk parity.
     static_assert(!LRS || VC == 4, "the in-kernel gates run with 16-column tiles");
     __shared__ __align__(16) f32x4_t sh_ew[LRS ? 2 : 1][LRS ? NB : 1][2][64];
+    // LRS with GATED: the output gate of every leaf of a chunk in the readout's row layout,
+    // double-buffered by chunk parity.
+    constexpr bool OGL = LRS && GATED;
+    __shared__ __align__(16) f32x4_t sh_og[OGL ? 2 : 1][OGL ? NB : 1][64];
 
     // Workgroups are dealt to the eight XCDs round-robin; the value tiles of one head
     // get ids that are equal mod 8, so they share an XCD and its L2.
@@ -1052,10 +1060,53 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                     make_group(ci, grp, zg[grp & 1]);
                 });
             };
+            // The output gate (GATED): rows of U_o and c_o as for the write gate, z's output
+            // slice (4 rank steps) per leaf.
+            g8 uo[OGL ? 4 : 1];
+            f32x4_t co4 = zero4();
+            if constexpr (OGL) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) uo[s] = F8::load8(sg.Uo + (size_t(h) * D + j0 + x) * 128 + 32 * s + 8 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) co4[i] = sg.co[size_t(h) * D + j0 + 4 * g + i];
+            }
+            struct OGroup {
+                g8 zo[NL][4];
+            };
+            auto load_ogroup = [&](int ci, int grp, OGroup &zg) {
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    const int t = ci * C + 16 * (grp * NL + l) + x;
+                    const unsigned zoff = unsigned(min(t, T)) * (kZRankAll * 2u) + 16u * unsigned(g);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) zg.zo[l][s] = F8::bload8(rz, zoff + unsigned(kZOffOutput + 32 * s) * 2u, 0u);
+                }
+            };
+            auto make_og = [&](int ci) {
+                OGroup zg[2];
+                load_ogroup(ci, 0, zg[0]);
+                static_for<NB / NL>([&](auto Gc) {
+                    constexpr int grp = decltype(Gc)::value;
+                    if constexpr (grp + 1 < NB / NL) load_ogroup(ci, grp + 1, zg[(grp + 1) & 1]);
+#pragma unroll
+                    for (int l = 0; l < NL; ++l) {
+                        f32x4_t yo = co4;
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) yo = F8::mma8(uo[s], zg[grp & 1].zo[l][s], yo);
+                        f32x4_t ov;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ov[i] = gate_sigmoid(yo[i]);
+                        sh_og[ci & 1][grp * NL + l][lane] = ov;
+                    }
+                });
+            };
             make_chunk(0);
             lds_barrier();
             for (int p = 0; p <= nchunks; ++p) {
                 if (p + 1 < nchunks) make_chunk(p + 1);
+                if constexpr (OGL) {
+                    if (p < nchunks) make_og(p);  // read out in phase p + 1
+                }
                 lds_barrier();
             }
             return;
@@ -1065,7 +1116,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     if (wave == 1) {
         // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
         const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * unsigned(sizeof(QT)));
-        const rsrc_t rog = make_rsrc(GATED ? og + tok0 : nullptr, GATED ? tok_elems * 4u : 0u);
+        const rsrc_t rog = make_rsrc(GATED && !OGL ? og + tok0 : nullptr, GATED && !OGL ? tok_elems * 4u : 0u);
         // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L} in block pairs (and the
         // output gate rows), loaded one leaf ahead.
         struct RWin {
@@ -1077,7 +1128,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
             load_kg(ci, L, SL::QG_OFF, wn.qg);
 #pragma unroll
             for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
-            if constexpr (GATED) wn.og = buf_load_fn<VC>(rog, lo_f, trow(ci * C + 16 * L, 4u));
+            if constexpr (GATED && !OGL) wn.og = buf_load_fn<VC>(rog, lo_f, trow(ci * C + 16 * L, 4u));
         };
         RWin rw[2];
         load_rwin(0, 0, rw[0]);
@@ -1139,7 +1190,8 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                     for (int l = 0; l <= L; l += 2) {
                         ro = F::mma8(u_pair(buf, l / 2), cw.pq[l / 2], ro);
                     }
-                    if constexpr (GATED) ro *= cw.og;
+                    if constexpr (OGL) ro *= sh_og[buf][L][lane];
+                    else if constexpr (GATED) ro *= cw.og;
                     RowV<QT, VC>::store(ro_, lo_q, trow(ci * C + 16 * L, unsigned(sizeof(QT))), ro);
                 });
             }
@@ -1411,14 +1463,12 @@ hipError_t scan_vc(const void *v, const float *e, const float *w, const float *o
     const int groups = (BH + 7) / 8;
     const dim3 grid(groups * 8 * (D / (4 * VC)));
     const dim3 block(LRS ? 192 : 128);
-    if constexpr (!LRS) {  // the in-kernel gates come without the output-gate epilogue
-        if (og) {
-            hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true, VC, false>), grid, block, 0,
-                               stream, static_cast<const QT *>(v), e, w, og, s0,
-                               static_cast<QT *>(o), s_out,
-                               static_cast<const unsigned char *>(workspace), sg, T, H, BH, nchunks);
-            return hipGetLastError();
-        }
+    // The output-gate epilogue: og read from memory, or (LRS) formed from z in the kernel.
+    if (LRS ? sg.Uo != nullptr : og != nullptr) {
+        hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, true, VC, LRS>), grid, block, 0,
+                           stream, static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o),
+                           s_out, static_cast<const unsigned char *>(workspace), sg, T, H, BH, nchunks);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((chunk_scan_kernel<QT, OpT, D, C, false, VC, LRS>), grid, block, 0, stream,
                        static_cast<const QT *>(v), e, w, og, s0, static_cast<QT *>(o), s_out,
@@ -1541,12 +1591,13 @@ bool scan_gates_in_kernel(int B, int H, int d, int chunk) {
 }
 
 hipError_t launch_chunk_scan_lowrank(const void *v, const void *z, const void *Ue, const void *Uw,
-                                     const float *ce, const float *cw, const float *s0, void *o,
-                                     float *s_out, int B, int T, int H, int d, int chunk,
-                                     const void *workspace, hipStream_t stream) {
+                                     const float *ce, const float *cw, const void *Uo,
+                                     const float *co, const float *s0, void *o, float *s_out, int B,
+                                     int T, int H, int d, int chunk, const void *workspace,
+                                     hipStream_t stream) {
     if (!scan_gates_in_kernel(B, H, d, chunk)) return hipErrorNotSupported;
     const ScanGates sg{static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ue),
-                       static_cast<const bf16_t *>(Uw), ce, cw};
+                       static_cast<const bf16_t *>(Uw), ce, cw, static_cast<const bf16_t *>(Uo), co};
 #define MUIR_SCAN_LR(D, C)                                                                        \
     if (d == D && chunk == C)                                                                     \
         return scan_vc<bf16_t, bf16_t, D, C, 4, true>(v, nullptr, nullptr, nullptr, s0, o, s_out, \

@@ -6,9 +6,9 @@
 // sensitivity-allocated gating, gate table; liuch.name summary, second bullet). The
 // down-projection's output z [B, T, 512] (rank slices in the table's order) is the input;
 // per gate n, with U_n [H, d, r_n] and an offset c_n [H, d]:
-//   y_n = z[..., slice_n] U_n^T + c_n,   a = exp(-exp(y_decay)),   e, w, g = sigmoid(y)
-// (y_decay is a log decay rate, so a lies in (0, 1]). The output gate's slice feeds none of
-// the four.
+//   y_n = z[..., slice_n] U_n^T + c_n,   a = exp(-exp(y_decay)),   e, w, g, og = sigmoid(y)
+// (y_decay is a log decay rate, so a lies in (0, 1]). The output gate og multiplies the
+// readout; its slice feeds none of the recurrence's four gates.
 //
 // Each product is a 16-token x 16-channel tile with the rank as the contraction, on the
 // matrix cores: the up-projection's rows (channels) are the A operand and z's rows
@@ -24,22 +24,24 @@ namespace muir {
 
 namespace {
 
-// Rank offsets of the four gates' slices of z (their ranks: gate_rank below).
+// Rank offsets of the gates' slices of z (their ranks: gate_rank below), in the order the
+// kernel takes them: decay, erase, write, read, output.
 constexpr int kZRank = 512;
-constexpr int kOffDecay = 0, kOffErase = 64, kOffWrite = 256, kOffRead = 384;
+constexpr int kOffDecay = 0, kOffErase = 64, kOffWrite = 256, kOffRead = 384, kOffOutput = 128;
+constexpr int kGates = 5;
 
 // LDS of the gate kernel: the head's up-projection rows of the requested gates (row pitch
 // padded by 8 elements against bank conflicts) and their offsets; gate n's region starts at
 // the byte offset the host computes (unrequested gates take no room).
 constexpr int kPad = 8;
 struct GateLds {
-    int u_off[4];   // byte offsets of U_n rows, [D][r_n + kPad] bf16
-    int c_off[4];   // byte offsets of c_n, [D] fp32
+    int u_off[kGates];   // byte offsets of U_n rows, [D][r_n + kPad] bf16
+    int c_off[kGates];   // byte offsets of c_n, [D] fp32
     int bytes;
 };
 __host__ __device__ constexpr int gate_rank(int n) { return n < 2 ? 64 : 128; }
 __host__ __device__ constexpr int gate_zoff(int n) {
-    return n == 0 ? kOffDecay : n == 1 ? kOffErase : n == 2 ? kOffWrite : kOffRead;
+    return n == 0 ? kOffDecay : n == 1 ? kOffErase : n == 2 ? kOffWrite : n == 3 ? kOffRead : kOffOutput;
 }
 
 // One workgroup of four wavefronts per (head, batch, token-block group). The head's
@@ -50,9 +52,10 @@ __host__ __device__ constexpr int gate_zoff(int n) {
 template <int D>
 __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const bf16_t *__restrict__ z, const bf16_t *__restrict__ Ua, const bf16_t *__restrict__ Ue,
-    const bf16_t *__restrict__ Uw, const bf16_t *__restrict__ Ug, const float *__restrict__ ca,
-    const float *__restrict__ ce, const float *__restrict__ cw, const float *__restrict__ cg,
-    float *__restrict__ a, float *__restrict__ e, float *__restrict__ w, float *__restrict__ g,
+    const bf16_t *__restrict__ Uw, const bf16_t *__restrict__ Ug, const bf16_t *__restrict__ Uo,
+    const float *__restrict__ ca, const float *__restrict__ ce, const float *__restrict__ cw,
+    const float *__restrict__ cg, const float *__restrict__ co, float *__restrict__ a,
+    float *__restrict__ e, float *__restrict__ w, float *__restrict__ g, float *__restrict__ og,
     int T, int H, GateLds lay) {
     using F = Frag<bf16_t>;
     using f8 = F::f8;
@@ -63,13 +66,13 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const int h = blockIdx.x, b = blockIdx.y;
     const int tw = blockIdx.z * 4 + wave, nw = gridDim.z * 4;
     const int nblk = (T + 15) / 16;
-    const bf16_t *U[4] = {Ua, Ue, Uw, Ug};
-    const float *cc[4] = {ca, ce, cw, cg};
-    float *out[4] = {a, e, w, g};
+    const bf16_t *U[kGates] = {Ua, Ue, Uw, Ug, Uo};
+    const float *cc[kGates] = {ca, ce, cw, cg, co};
+    float *out[kGates] = {a, e, w, g, og};
 
     // The head's rows of every requested gate into LDS.
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kGates; ++n) {
         if (!out[n]) continue;
         const int R = gate_rank(n), pitch = R + kPad, per_row = R / 8;
         bf16_t *su = reinterpret_cast<bf16_t *>(smem + lay.u_off[n]);
@@ -89,14 +92,14 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const unsigned gbytes = unsigned((size_t(T) * HD - size_t(h) * D) * 4);
 
     struct ZRows {
-        f8 r[12];  // decay 2, erase 2, write 4, read 4 K-steps
+        f8 r[16];  // decay 2, erase 2, write 4, read 4, output 4 K-steps
     };
-    constexpr int kStep0[4] = {0, 2, 4, 8};
+    constexpr int kStep0[kGates] = {0, 2, 4, 8, 12};
     auto load_z = [&](int tb, ZRows &zr) {
         const unsigned t = unsigned(min(16 * tb + x, T));
         const unsigned zoff = t * unsigned(kZRank) * 2u + unsigned(8 * G) * 2u;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
+        for (int n = 0; n < kGates; ++n) {
             if (!out[n]) continue;
 #pragma unroll
             for (int s = 0; s < gate_rank(n) / 32; ++s)
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     auto compute = [&](int tb, const ZRows &zr) {
         const unsigned t = unsigned(min(16 * tb + x, T));
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
+        for (int n = 0; n < kGates; ++n) {
             if (!out[n]) continue;
             const int R = gate_rank(n), pitch = R + kPad;
             const bf16_t *su = reinterpret_cast<const bf16_t *>(smem + lay.u_off[n]);
@@ -144,14 +147,14 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
 
 template <int D>
 hipError_t gates_typed(const void *z, const void *Ua, const void *Ue, const void *Uw,
-                       const void *Ug, const float *ca, const float *ce, const float *cw,
-                       const float *cg, float *a, float *e, float *w, float *g, int B, int T,
-                       int H, hipStream_t stream) {
+                       const void *Ug, const void *Uo, const float *ca, const float *ce,
+                       const float *cw, const float *cg, const float *co, float *a, float *e,
+                       float *w, float *g, float *og, int B, int T, int H, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     GateLds lay{};
-    const float *outs[4] = {a, e, w, g};
+    const float *outs[kGates] = {a, e, w, g, og};
     int off = 0;
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kGates; ++n) {
         lay.u_off[n] = lay.c_off[n] = 0;
         if (!outs[n]) continue;
         lay.u_off[n] = off;
@@ -173,18 +176,22 @@ hipError_t gates_typed(const void *z, const void *Ua, const void *Ue, const void
     hipLaunchKernelGGL(kern, dim3(H, B, groups), dim3(256), off, stream,
                        static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(Ua),
                        static_cast<const bf16_t *>(Ue), static_cast<const bf16_t *>(Uw),
-                       static_cast<const bf16_t *>(Ug), ca, ce, cw, cg, a, e, w, g, T, H, lay);
+                       static_cast<const bf16_t *>(Ug), static_cast<const bf16_t *>(Uo), ca, ce, cw,
+                       cg, co, a, e, w, g, og, T, H, lay);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
-                                const void *Ug, const float *ca, const float *ce, const float *cw,
-                                const float *cg, float *a, float *e, float *w, float *g, int B,
-                                int T, int H, int d, hipStream_t stream) {
-    if (d == 64) return gates_typed<64>(z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g, B, T, H, stream);
-    if (d == 128) return gates_typed<128>(z, Ua, Ue, Uw, Ug, ca, ce, cw, cg, a, e, w, g, B, T, H, stream);
+                                const void *Ug, const void *Uo, const float *ca, const float *ce,
+                                const float *cw, const float *cg, const float *co, float *a,
+                                float *e, float *w, float *g, float *og, int B, int T, int H, int d,
+                                hipStream_t stream) {
+    if (d == 64)
+        return gates_typed<64>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H, stream);
+    if (d == 128)
+        return gates_typed<128>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H, stream);
     return hipErrorInvalidValue;
 }
 

@@ -52,13 +52,15 @@ hipError_t launch_chunk_scan_save(const void *v, const float *e, const float *w,
 
 // Phase S with e and w formed inside the kernel from the low-rank gate projection (z,
 // U_e, U_w, c_e, c_w as for launch_lowrank_gates; bf16 operands), bit-identical to
-// launch_lowrank_gates followed by launch_chunk_scan. Only where scan_gates_in_kernel
-// holds; elsewhere it returns hipErrorNotSupported and the caller makes e and w first.
+// launch_lowrank_gates followed by launch_chunk_scan; with a non-null U_o (and c_o) also the
+// output gate and its epilogue. Only where scan_gates_in_kernel holds; elsewhere it returns
+// hipErrorNotSupported and the caller makes the gates first.
 bool scan_gates_in_kernel(int B, int H, int d, int chunk);
 hipError_t launch_chunk_scan_lowrank(const void *v, const void *z, const void *Ue, const void *Uw,
-                                     const float *ce, const float *cw, const float *s0, void *o,
-                                     float *s_out, int B, int T, int H, int d, int chunk,
-                                     const void *workspace, hipStream_t stream);
+                                     const float *ce, const float *cw, const void *Uo,
+                                     const float *co, const float *s0, void *o, float *s_out, int B,
+                                     int T, int H, int d, int chunk, const void *workspace,
+                                     hipStream_t stream);
 
 // Shared-erase variant (one erase strength per token, e [B, T, H]); bf16 operands only. Its
 // workspace is the prepare kernel's slots followed by one region of per-chunk products per
@@ -73,13 +75,14 @@ hipError_t launch_wy_solve(const void *v, const float *e, const float *w, int B,
 hipError_t launch_wy_scan(const float *s0, void *o, float *s_out, int B, int T, int H, int d,
                           int chunk, void *workspace, hipStream_t stream);
 
-// Gates a, e, w, g [B, T, H, d] fp32 from the fused low-rank gate projection: z [B, T, 512]
-// bf16, up-projections U_n [H, d, r_n] bf16, offsets c_n [H, d] fp32. A null gate output
-// is not computed.
+// Gates a, e, w, g and the output gate og [B, T, H, d] fp32 from the fused low-rank gate
+// projection: z [B, T, 512] bf16, up-projections U_n [H, d, r_n] bf16, offsets c_n [H, d]
+// fp32. A null gate output is not computed.
 hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, const void *Uw,
-                                const void *Ug, const float *ca, const float *ce, const float *cw,
-                                const float *cg, float *a, float *e, float *w, float *g, int B,
-                                int T, int H, int d, hipStream_t stream);
+                                const void *Ug, const void *Uo, const float *ca, const float *ce,
+                                const float *cw, const float *cg, const float *co, float *a,
+                                float *e, float *w, float *g, float *og, int B, int T, int H, int d,
+                                hipStream_t stream);
 
 // Backward pass of the chunk forward (chunks of 64). Inputs as for the forward, plus dout
 // (dtype of q) and dsT [B, H, d, d] fp32 (NULL: zero); outputs fp32, [B, T, H, d] except

@@ -264,7 +264,7 @@ muir_status_t muir_chunk_fwd_scalar_erase_scan(
  *
  *   z        [B, T, 512] bf16: the down-projection's output, rank slices in the table's
  *            order: decay 0..63, erase 64..127, output 128..255, write 256..383,
- *            read 384..511 (the output gate's slice is not used here)
+ *            read 384..511 (the output gate's slice is read by muir_lowrank_output_gate)
  *   Ua, Ue   [H, d, 64]  bf16;  Uw, Ug [H, d, 128] bf16  (rank contiguous per channel)
  *   ca .. cg [H, d] fp32 offsets
  *   a, e, w, g  [B, T, H, d] fp32 outputs; a NULL output is not computed (and its U and c
@@ -307,6 +307,46 @@ muir_status_t muir_chunk_fwd_lowrank(
     const void *Ua, const void *Ue, const void *Uw, const void *Ug,
     const float *ca, const float *ce, const float *cw, const float *cg, const float *r,
     const float *s0, void *o, float *s_out,
+    int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
+
+/*
+ * The output gate from the same fused projection (openai-hub page, section on
+ * sensitivity-allocated gating, gate table: the output gate has rank 128 of the 512):
+ *   og[b, t, h, j] = sigmoid(z[b, t, 128:256] . Uo[h, j, :] + co[h, j])
+ * per value channel j; the gated readout is o_t * og_t (as muir_chunk_fwd_gated applies it).
+ *
+ *   z        [B, T, 512] bf16 as for muir_lowrank_gates
+ *   Uo       [H, d, 128] bf16;  co [H, d] fp32
+ *   og       [B, T, H, d] fp32 output
+ *
+ * Errors as for muir_lowrank_gates (og is required when T > 0).
+ */
+muir_status_t muir_lowrank_output_gate(const void *z, const void *Uo, const float *co, float *og,
+                                       int B, int T, int H, int d, muir_stream_t stream);
+
+/*
+ * muir_chunk_fwd_lowrank with the output gate as well: all five gates of the fused
+ * projection are made inside the call and the readout is stored as o_t * og_t. og is made
+ * like e and w: inside the sequential phase's kernel (from z's output slice, one chunk ahead
+ * of the readout) where that kernel makes e and w, otherwise by the gate kernel into the
+ * workspace. Either way the result is muir_chunk_fwd_gated's on the gates that
+ * muir_lowrank_gates and muir_lowrank_output_gate make from the same z, U and c (bit for
+ * bit).
+ *
+ *   arguments as for muir_chunk_fwd_lowrank, plus Uo [H, dv, 128] bf16 and co [H, dv] fp32
+ *   workspace / workspace_bytes: at least muir_chunk_fwd_lowrank_gated_workspace_size(...)
+ *            bytes (muir_chunk_fwd_lowrank's, plus room for og)
+ *
+ * Errors as for muir_chunk_fwd_lowrank (Uo and co are required).
+ */
+size_t muir_chunk_fwd_lowrank_gated_workspace_size(int B, int T, int H, int dk, int dv, int chunk);
+
+muir_status_t muir_chunk_fwd_lowrank_gated(
+    const void *q, const void *k, const void *v, const void *z,
+    const void *Ua, const void *Ue, const void *Uw, const void *Ug, const void *Uo,
+    const float *ca, const float *ce, const float *cw, const float *cg, const float *co,
+    const float *r, const float *s0, void *o, float *s_out,
     int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
     void *workspace, size_t workspace_bytes, muir_stream_t stream);
 

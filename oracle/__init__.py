@@ -27,6 +27,7 @@ Forms provided here:
   * ``naive_unpivoted_nonfinite`` the unpivoted fp32 scheme that divides by cumulative
                            decays, kept only as a negative control (same two passages);
   * ``lowrank_gates``      (``gates.py``) the four gates from the rank-512 gate projection.
+  * ``output_gate``        (``gates.py``) the output gate from the same projection.
   * ``backward``           (``backward.py``) every input's gradient, by autograd, by the
                            token adjoint and by chunk products (no GPU counterpart yet).
 
@@ -45,11 +46,11 @@ import numpy as np
 
 from . import build as _build
 
-from .gates import lowrank_gates  # noqa: E402  (the low-rank gate definition)
+from .gates import lowrank_gates, output_gate  # noqa: E402  (the low-rank gate definition)
 
 __all__ = [
     "recurrent", "recurrent_np", "chunked_np", "bruteforce_np",
-    "naive_unpivoted_nonfinite", "pivot_factors", "max_threads", "load", "lowrank_gates",
+    "naive_unpivoted_nonfinite", "pivot_factors", "max_threads", "load", "lowrank_gates", "output_gate",
 ]
 
 _LIB = None

@@ -11,8 +11,9 @@ order. What the pages leave open, and the reading taken:
     per head and channel and a per-channel offset c_n [H, d];
   * the decay is a = exp(-exp(y_a)): y_a is the log decay rate, as in the workloads'
     decay recipe (base rate plus a per-token jitter), so a stays in (0, 1];
-  * the erase, write and query (dynamic read) gates are sigmoid(y).
-The output gate's slice is part of z but feeds no gate of this recurrence.
+  * the erase, write and query (dynamic read) gates are sigmoid(y);
+  * the output gate is sigmoid(y_output) as well, per value channel, and multiplies the
+    readout o_t elementwise after the read (it feeds none of the recurrence's four gates).
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ for _n, _r in RANKS.items():
     _o += _r
 RANK = _o  # 512
 
-__all__ = ["RANKS", "SLICES", "RANK", "preactivation", "lowrank_gates"]
+__all__ = ["RANKS", "SLICES", "RANK", "preactivation", "lowrank_gates", "output_gate"]
 
 
 def preactivation(z, U, c, name):
@@ -47,3 +48,11 @@ def lowrank_gates(z, Ua, Ue, Uw, Ug, ca, ce, cw, cg):
     w = sig(preactivation(z, Uw, cw, "write"))
     g = sig(preactivation(z, Ug, cg, "read"))
     return a, e, w, g
+
+
+def output_gate(z, Uo, co):
+    """The output gate og [B,T,H,dv] fp64 = sigmoid(z[..., 128:256] Uo^T + co) from the
+    rank-128 output slice of the same projection (Uo [H,dv,128], co [H,dv]); the gated
+    readout is o_t * og_t."""
+    y = preactivation(z, Uo, co, "output")
+    return 1.0 / (1.0 + np.exp(-y))

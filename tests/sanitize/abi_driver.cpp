@@ -142,6 +142,30 @@ void run_shape(const Shape &s) {
                                       s.B, T, s.H, s.d, s.d, s.chunk, s.qkv, lrws, lrn, nullptr),
                s.qkv == MUIR_BF16 ? MUIR_OK : MUIR_ERR_UNSUPPORTED, SHAPE_TAG("lowrank fwd"));
     }
+    // The output gate, alone and in the fused forward.
+    void *Uo = ar.take(size_t(s.H) * s.d * 128 * 2);
+    float *co = ar.take<float>(size_t(s.H) * s.d * 4);
+    float *og2 = ar.take<float>(ntok * 4);
+    expect(muir_lowrank_output_gate(z, Uo, co, og2, s.B, T, s.H, s.d, nullptr), MUIR_OK,
+           SHAPE_TAG("output gate"));
+    if (T > 0)
+        expect(muir_lowrank_output_gate(z, Uo, co, nullptr, s.B, T, s.H, s.d, nullptr), MUIR_ERR_NULL,
+               SHAPE_TAG("output gate without og"));
+    const size_t lgn = muir_chunk_fwd_lowrank_gated_workspace_size(s.B, T, s.H, s.d, s.d, s.chunk);
+    expect_true(T == 0 || lgn > lrn, SHAPE_TAG("gated low-rank workspace"));
+    void *lgws = ar.take(lgn + 256);
+    for (int in_kernel = 0; in_kernel < 2; ++in_kernel) {
+        stub_gates_in_kernel(in_kernel);
+        expect(muir_chunk_fwd_lowrank_gated(q, k, v, z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, r, s0,
+                                            o, s_out, s.B, T, s.H, s.d, s.d, s.chunk, s.qkv, lgws, lgn,
+                                            nullptr),
+               s.qkv == MUIR_BF16 ? MUIR_OK : MUIR_ERR_UNSUPPORTED, SHAPE_TAG("lowrank gated fwd"));
+    }
+    if (T > 0 && s.qkv == MUIR_BF16)
+        expect(muir_chunk_fwd_lowrank_gated(q, k, v, z, Ua, Ue, Uw, Ug, nullptr, ca, ce, cw, cg, co, r,
+                                            s0, o, s_out, s.B, T, s.H, s.d, s.d, s.chunk, s.qkv, lgws,
+                                            lgn, nullptr),
+               MUIR_ERR_NULL, SHAPE_TAG("lowrank gated fwd without Uo"));
     stub_gates_in_kernel(0);
 
     // Decode step on [B, H, d] tokens against a [B, H, d, d] state.

@@ -56,9 +56,9 @@ hipError_t launch_chunk_scan_save(const void *, const float *, const float *, co
 }
 bool scan_gates_in_kernel(int, int, int, int) { return g_gates_in_kernel; }
 hipError_t launch_chunk_scan_lowrank(const void *, const void *, const void *, const void *,
-                                     const float *, const float *, const float *, void *,
-                                     float *, int, int, int, int, int, const void *,
-                                     hipStream_t) {
+                                     const float *, const float *, const void *, const float *,
+                                     const float *, void *, float *, int, int, int, int, int,
+                                     const void *, hipStream_t) {
     return launched();
 }
 hipError_t launch_wy_solve(const void *, const float *, const float *, int, int, int, int, int,
@@ -70,9 +70,9 @@ hipError_t launch_wy_scan(const float *, void *, float *, int, int, int, int, in
     return launched();
 }
 hipError_t launch_lowrank_gates(const void *, const void *, const void *, const void *,
-                                const void *, const float *, const float *, const float *,
-                                const float *, float *, float *, float *, float *, int, int, int,
-                                int, hipStream_t) {
+                                const void *, const void *, const float *, const float *,
+                                const float *, const float *, const float *, float *, float *,
+                                float *, float *, float *, int, int, int, int, hipStream_t) {
     return launched();
 }
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &, int, int, int, int, bool, void *,

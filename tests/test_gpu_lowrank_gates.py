@@ -175,3 +175,99 @@ def test_fused_equals_gate_kernel_then_forward(device, cfg, chunk):
     o2, s2 = muir.chunk_fwd(*[t[n] for n in NAMES], chunk=chunk)
     torch.cuda.synchronize()
     assert np.array_equal(o1, to_numpy(o2)) and np.array_equal(s1, to_numpy(s2))
+
+
+# ---- The output gate from z's output slice (rank 128, z[..., 128:256]) ----
+
+def gpu_output_gate(lr, device):
+    z = torch.from_numpy(lr["z"]).to(device=device, dtype=torch.bfloat16)
+    Uo = torch.from_numpy(lr["U_output"]).to(device=device, dtype=torch.bfloat16)
+    co = torch.from_numpy(lr["c_output"]).to(device)
+    og = muir.lowrank_output_gate(z, Uo, co)
+    torch.cuda.synchronize()
+    return og.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_output_gate_small(device, d, T):
+    """og = sigmoid(z[..., 128:256] U_o^T + c_o) against the oracle, to the sigmoid gates'
+    2e-6 absolute bar."""
+    lr = workloads.lowrank_gate_inputs(0, B=2, T=T, H=3, d=d, seed=800 + T)
+    got = gpu_output_gate(lr, device)
+    ref = oracle.output_gate(lr["z"], lr["U_output"], lr["c_output"])
+    check_gates({"og": got}, {"og": ref}, f"output gate T={T} d={d}")
+
+
+def test_output_gate_long_context_shape_sampled(device):
+    """The long-context shape (B1 T32768 H16 d128): sampled token rows against the oracle."""
+    lr = workloads.lowrank_gate_inputs(3)
+    got = gpu_output_gate(lr, device)
+    rows = np.array([0, 1, 15, 16, 255, 256, 4095, 16384, 32766, 32767])
+    ref = oracle.output_gate(lr["z"][:, rows], lr["U_output"], lr["c_output"])
+    check_gates({"og": got[:, rows]}, {"og": ref}, "output gate long context")
+    assert np.isfinite(got).all() and ((got > 0) & (got < 1)).all()
+
+
+def dev_weights5(lr, device):
+    U, c = dev_weights(lr, device)
+    U["output"] = torch.from_numpy(lr["U_output"]).to(device=device, dtype=torch.bfloat16)
+    c["output"] = torch.from_numpy(lr["c_output"]).to(device)
+    return U, c
+
+
+def lowrank_gated_fwd(inp, lr, device, chunk, s0=None):
+    t = to_device(inp, device, "bf16")
+    z = torch.from_numpy(lr["z"]).to(device=device, dtype=torch.bfloat16)
+    U, c = dev_weights5(lr, device)
+    s0t = None if s0 is None else torch.from_numpy(np.asarray(s0, np.float32)).to(device)
+    o, s = muir.chunk_fwd_lowrank_gated(t["q"], t["k"], t["v"], z, U, c, t["r"], s0t, chunk=chunk)
+    torch.cuda.synchronize()
+    return to_numpy(o), to_numpy(s)
+
+
+def ref_gated(inp, lr, s0=None):
+    ref = ref_gates(lr)
+    full = dict(inp)
+    for k in "aewg":
+        full[k] = ref[k]
+    o_ref, s_ref = oracle.recurrent(*[full[n] for n in NAMES], s0=s0)
+    return o_ref * oracle.output_gate(lr["z"], lr["U_output"], lr["c_output"]), s_ref
+
+
+@pytest.mark.parametrize("d,B,H,chunk", [(64, 2, 2, 64), (128, 2, 2, 256), (128, 2, 16, 128),
+                                         (64, 4, 16, 64)])
+@pytest.mark.parametrize("T", [15, 300])
+def test_fused_lowrank_gated_parity(device, d, B, H, chunk, T):
+    """All five gates made inside the call: the stored output against the fp64 recurrence on
+    the oracle's four gates times the oracle's output gate, with a non-zero initial state.
+    The 16-head cases (B*H*d/8 = 512, chunk <= 128) form og in the scan's gate wavefront;
+    the others take it from the gate kernel."""
+    inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv="bf16", seed=900 + T + d)
+    lr = workloads.lowrank_gate_inputs(0, B=B, T=T, H=H, d=d, seed=900 + T + d)
+    s0 = (np.random.default_rng(900 + T).standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    o, s = lowrank_gated_fwd(inp, lr, device, chunk, s0)
+    o_ref, s_ref = ref_gated(inp, lr, s0)
+    eo, es = o_err(o, o_ref), s_err(s, s_ref)
+    print(f"fused gated T={T} d={d} H={H} C={chunk}: o={eo.max():.3e} state={es.max():.3e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert max(eo.max(), es.max()) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg,chunk", [(2, 128), (2, 256), (3, 256)])
+def test_fused_gated_equals_gate_kernels_then_gated_forward(device, cfg, chunk):
+    """The fused gated call is bit for bit the gate kernel's gates and output gate fed to
+    the output-gated forward: og made in the scan's gate wavefront (C=128), by the gate
+    kernel with 16-column tiles (C=256), and on the long-context shape's split scan."""
+    inp = workloads.chunk_inputs(cfg)
+    lr = workloads.lowrank_gate_inputs(cfg)
+    B, T, H, d = inp["B"], inp["T"], inp["H"], inp["d"]
+    o1, s1 = lowrank_gated_fwd(inp, lr, device, chunk)
+    gates = gpu_gates(lr, H, d, device)
+    og = torch.from_numpy(gpu_output_gate(lr, device)).to(device)
+    t = to_device(inp, device, "bf16")
+    for k in "aewg":
+        t[k] = torch.from_numpy(gates[k]).to(device)
+    o2, s2 = muir.chunk_fwd(*[t[n] for n in NAMES], chunk=chunk, og=og)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, to_numpy(o2)) and np.array_equal(s1, to_numpy(s2))

@@ -1,7 +1,8 @@
 """Pins of the oracle's low-rank gate generation (oracle/gates.py) against closed forms:
 zero up-projections, one-hot ranks (which select one up-projection column, and so pin the
-rank slices and the weight index order), additivity of the pre-activation, and the slice
-of the output gate feeding none of the four gates."""
+rank slices and the weight index order), additivity of the pre-activation, the slice of
+the output gate feeding none of the four gates, and the output gate itself reading its
+slice only."""
 import math
 
 import numpy as np
@@ -95,3 +96,38 @@ def test_ranges():
     assert ((a > 0) & (a <= 1)).all()
     for x in (e, w, g):
         assert ((x > 0) & (x < 1)).all()
+
+
+def test_output_gate_zero_up_projection_and_one_hot_ranks():
+    rng = np.random.default_rng(6)
+    H, d = 2, 3
+    Uo = rng.standard_normal((H, d, 128)) * 0.5
+    co = rng.standard_normal((H, d))
+    og = oracle.output_gate(rng.standard_normal((1, 2, 512)), np.zeros_like(Uo), co)
+    for h in range(H):
+        for i in range(d):
+            assert og[0, 1, h, i] == pytest.approx(sig(co[h, i]), rel=1e-14)
+    for k in (0, 127, 128, 200, 255, 256, 511):
+        z = np.zeros((1, 1, 512))
+        z[0, 0, k] = 1.0
+        og = oracle.output_gate(z, Uo, co)
+        for h in range(H):
+            for i in range(d):
+                y = co[h, i] + (Uo[h, i, k - 128] if 128 <= k < 256 else 0.0)
+                assert og[0, 0, h, i] == pytest.approx(sig(y), rel=1e-13)
+
+
+def test_output_gate_reads_its_slice_only():
+    rng = np.random.default_rng(7)
+    Uo = rng.standard_normal((2, 4, 128)) * 0.5
+    co = rng.standard_normal((2, 4))
+    z = rng.standard_normal((1, 6, 512))
+    og = oracle.output_gate(z, Uo, co)
+    z2 = rng.standard_normal((1, 6, 512)) * 10
+    z2[..., G.SLICES["output"]] = z[..., G.SLICES["output"]]
+    assert np.array_equal(og, oracle.output_gate(z2, Uo, co))
+    assert ((og > 0) & (og < 1)).all()
+    # The pre-activation is the slice times the up-projection, written out.
+    b, t, h, i = 0, 3, 1, 2
+    y = co[h, i] + sum(z[b, t, 128 + r] * Uo[h, i, r] for r in range(128))
+    assert og[b, t, h, i] == pytest.approx(sig(y), rel=1e-13)

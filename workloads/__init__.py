@@ -238,7 +238,7 @@ GATE_RANKS = (("decay", 64), ("erase", 64), ("output", 128), ("write", 128), ("r
 def lowrank_gate_inputs(cfg: ChunkConfig | int, *, B=None, T=None, H=None, d=None,
                         seed=None) -> dict:
     """Inputs of the low-rank gate projection for a chunk workload: z [B,T,512] (the shared
-    down-projection's output) and, per gate n in (decay, erase, write, read), an
+    down-projection's output) and, per gate n in (decay, erase, write, read, output), an
     up-projection U_n [H,d,r_n] and an offset c_n [H,d].
 
     Recipe (one stream each, from ``SeedSequence((seed, 12)).spawn(5)``: z, then U for
@@ -277,6 +277,13 @@ def lowrank_gate_inputs(cfg: ChunkConfig | int, *, B=None, T=None, H=None, d=Non
             c = np.zeros((H, d), np.float32)
         out["U_" + n] = round_bf16(U)
         out["c_" + n] = c
+    # The output gate (rank 128), from a stream of its own (``SeedSequence((seed, 13))``) so
+    # that the other inputs of the same seed are unchanged: U_output ~ N(0, 1/128), zero
+    # offsets, like the erase, write and read gates.
+    Uo = _normal(np.random.SeedSequence((seed, 13)), (H, d, ranks["output"]))
+    Uo *= np.float32(1.0 / math.sqrt(ranks["output"]))
+    out["U_output"] = round_bf16(Uo)
+    out["c_output"] = np.zeros((H, d), np.float32)
     return out
 
 
