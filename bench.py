@@ -85,7 +85,7 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_06_amd", "csrc")
 # The sources of the channel-wise chunk kernels: the kernel file and the headers it includes.
 CHUNK_SOURCES = [os.path.join(CSRC, f) for f in
                  ("chunk_fwd.hip", "chunk_scan_split.hip", "scan_leaf.hpp", "chunk_layout.hpp",
-                  "mfma.hpp", "common.hpp")]
+                  "layout.hpp", "mfma.hpp", "common.hpp")]
 
 
 def code_sha(*paths):
