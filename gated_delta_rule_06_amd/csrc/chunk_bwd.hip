@@ -79,31 +79,32 @@ __device__ __forceinline__ f32x4_t ld4(const bf16_t *p, size_t i) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prepare. LDS: M and P [C][C + 1], K*gamma [C][D + 4] for the prediction, and the pivot
-// pass arrays (per 64-channel pass: a, k, q_hat, prefix F and suffix R [C][65] inside each
-// 16-token block, then inside each 4-token sub-block, and the products of whole blocks,
-// then of whole sub-blocks [16][64]).
+// Prepare. One workgroup per (b, h, chunk), in passes of 32 channels. LDS per pass: a, k,
+// q_hat, and the prefix F and suffix R inside each 16-token block (then inside each 4-token
+// sub-block) [C][33], plus per-channel products of whole blocks (then whole sub-blocks). After
+// the last pass the same space holds M and P [C][C + 1]. About 44 KB, so three workgroups
+// share a compute unit. The K*gamma S0 part of p accumulates in registers pass by pass.
 //
 // Pivots. For s < t in different 16-token blocks, Gamma_ts = F_t * (whole blocks between) *
 // R_s, so each cross-block 16x16 tile of M or P is one matrix-core product over channels with
 // the middle factor folded into the s side. Inside a 16-token block the same split at 4-token
 // sub-blocks gives Gamma_ts = F4_t * (whole sub-blocks between) * R4_s; the middle factor
 // depends only on s's sub-block and the gap (1, 2 or 3 sub-blocks), so each gap is one masked
-// product. Pairs inside one sub-block (at most 3 factors) are direct products.
+// product. Pairs inside one sub-block split once more at its halves (three masked products).
 // ------------------------------------------------------------------------------------------
 template <int D> struct PrepBwdLds {
-    static constexpr int LDM = kC + 1;
-    static constexpr int DH = 64;
+    static constexpr int DH = 32;  // channels per pass
     static constexpr int LDH = DH + 1;
+    static constexpr int LDM = kC + 1;
+    static constexpr int TILE = kC * LDH;  // one [C][DH] pass array
+    static constexpr int PASS = 5 * TILE + 16 * DH;
     static constexpr int MP = 2 * kC * LDM;
-    static constexpr int PASS = 5 * kC * LDH + 16 * DH;
-    static constexpr int KGL = kC * (D + 4);
-    static constexpr int FLOATS = MP + KGL + PASS;
+    static constexpr int FLOATS = PASS > MP ? PASS : MP;
     static constexpr size_t BYTES = size_t(FLOATS) * 4;
 };
 
 template <typename QT, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_prepare_kernel(
     const QT *__restrict__ q, const QT *__restrict__ k, const float *__restrict__ a,
     const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
     const float *__restrict__ u, float *__restrict__ kb, float *__restrict__ kg,
@@ -111,33 +112,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
     float *__restrict__ Pw, float *__restrict__ pred, int T, int H, int nchunks) {
     using L = PrepBwdLds<D>;
     constexpr int C = kC, LDM = L::LDM, DH = L::DH, LDH = L::LDH;
+    constexpr int NJT = D / 64;  // value-column tiles of p per wavefront
+    static_assert(kBwdThreads == 8 * DH && kNB == 4, "thread roles assume 256 threads, 4 blocks");
     extern __shared__ float lds[];
-    float *sM = lds, *sP = lds + kC * LDM;
-    float *sKG = lds + L::MP;
-    float *pass = sKG + L::KGL;
-    float *sA = pass, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH,
-          *sR = sF + C * LDH, *sMid = sR + C * LDH;
+    float *sA = lds, *sK = sA + L::TILE, *sQ = sK + L::TILE, *sF = sQ + L::TILE, *sR = sF + L::TILE;
+    float *sMid = sR + L::TILE;  // [6][DH] whole blocks strictly between a block pair
+    float *sBp = sMid + 6 * DH;  // [4][DH] each whole block
+    float *sBef = sBp + 4 * DH;  // [4][DH] the whole blocks before each block
+    float *sB4 = sMid;           // [16][DH] each whole sub-block (written after the above are read)
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int cc = lane & 15, kq = lane >> 4;
     const size_t HD = size_t(H) * D;
     const int c0 = c * C;
     const int nval = min(C, T - c0);
     const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
     const size_t slot = size_t(bh) * nchunks + c;
     const float *rh = r + size_t(h) * D;
-
-    for (int idx = tid; idx < 2 * C * LDM; idx += kBwdThreads) lds[idx] = 0.f;
+    const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
 
     // Cross-block tiles of M and P: pair p = (bt, bs), bs < bt, pair index bt (bt - 1) / 2 + bs;
     // tile job j < 12: matrix j / 6 (0: M, 1: P), pair j % 6. Wave w owns jobs w, w + 4, w + 8.
     f32x4_t acc[3] = {zero4(), zero4(), zero4()};
-    // Diagonal 16x16 tiles: wave w owns tile jobs w and w + 4 (job: matrix j / 4, block j % 4),
-    // accumulated over the passes.
-    f32x4_t dacc[2] = {zero4(), zero4()};
+    // Diagonal tiles of block w, M and P, accumulated over the passes.
+    f32x4_t dm = zero4(), dp = zero4();
+    // p tiles: value columns 16 (w + 4 jj) .. + 15, tokens 16 tt .. + 15.
+    f32x4_t pacc[NJT][kNB];
+#pragma unroll
+    for (int jj = 0; jj < NJT; ++jj)
+#pragma unroll
+        for (int tt = 0; tt < kNB; ++tt) pacc[jj][tt] = zero4();
 
     for (int p0 = 0; p0 < D; p0 += DH) {
+        // B operands of this pass's (K*gamma) S0 steps: rows p0 .. p0 + DH - 1 of S0.
+        float bS[NJT][DH / 4];
+#pragma unroll
+        for (int jj = 0; jj < NJT; ++jj)
+#pragma unroll
+            for (int m = 0; m < DH / 4; ++m)
+                bS[jj][m] = S0[size_t(p0 + 4 * m + kq) * D + 16 * (wave + 4 * jj) + cc];
         __syncthreads();
         {
             // All of the pass's loads are issued before the first LDS store.
@@ -168,54 +183,67 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
             }
         }
         __syncthreads();
-        float *sBp = sMid + 6 * DH;  // whole-block decay products per channel
         {
-            // Thread (channel, 16-token block): prefix F and suffix R inside the block.
-            const int ii = tid % DH, bb = tid / DH;
+            // Thread (channel, 16-token block): waves 0-1 the prefix F inside the block, waves
+            // 2-3 the suffix R and the whole block's product.
+            const int ii = tid % DH, bb = (tid / DH) % kNB;
             float run = 1.f;
+            if (tid < kBwdThreads / 2) {
 #pragma unroll
-            for (int tl = 0; tl < 16; ++tl) {
-                run *= sA[(16 * bb + tl) * LDH + ii];
-                sF[(16 * bb + tl) * LDH + ii] = run;
-            }
-            run = 1.f;
+                for (int tl = 0; tl < 16; ++tl) {
+                    run *= sA[(16 * bb + tl) * LDH + ii];
+                    sF[(16 * bb + tl) * LDH + ii] = run;
+                }
+            } else {
 #pragma unroll
-            for (int tl = 15; tl >= 0; --tl) {
-                sR[(16 * bb + tl) * LDH + ii] = run;
-                run *= sA[(16 * bb + tl) * LDH + ii];
+                for (int tl = 15; tl >= 0; --tl) {
+                    sR[(16 * bb + tl) * LDH + ii] = run;
+                    run *= sA[(16 * bb + tl) * LDH + ii];
+                }
+                sBp[bb * DH + ii] = run;
             }
-            sBp[bb * DH + ii] = run;
         }
         __syncthreads();
         {
-            // Thread (channel, block bb): products of the whole blocks between bb and each
-            // earlier block; gamma and beta of its tokens and the scaled operands K*gamma,
-            // Q_hat*gamma, K*beta; gamma_C.
-            const int ii = tid % DH, bb = tid / DH, i = p0 + ii;
+            // Thread (channel, block, half of the block): gamma and beta of its eight tokens
+            // and the scaled operands K*gamma, Q_hat*gamma (channel-major, two 16-byte stores
+            // each) and K*beta; the first half also the products of the whole blocks between
+            // its block and each earlier one, and gamma_C.
+            const int ii = tid % DH, bb = (tid / DH) % kNB, half = tid / (DH * kNB), i = p0 + ii;
             float bp[kNB];
 #pragma unroll
             for (int b2 = 0; b2 < kNB; ++b2) bp[b2] = sBp[b2 * DH + ii];
-            float mid = 1.f, before = 1.f, after = 1.f;
-            for (int bs = bb - 1; bs >= 0; --bs) {
-                sMid[(bb * (bb - 1) / 2 + bs) * DH + ii] = mid;
-                mid *= bp[bs];
-            }
+            float before = 1.f, after = 1.f;
 #pragma unroll
             for (int b2 = 0; b2 < kNB; ++b2) {
                 if (b2 < bb) before *= bp[b2];
                 if (b2 > bb) after *= bp[b2];
             }
+            if (half == 0) {
+                float mid = 1.f;
+                for (int bs = bb - 1; bs >= 0; --bs) {
+                    sMid[(bb * (bb - 1) / 2 + bs) * DH + ii] = mid;
+                    mid *= bp[bs];
+                }
+                sBef[bb * DH + ii] = before;
+                if (bb == kNB - 1) gC[slot * D + i] = before * bp[kNB - 1];
+            }
+            f32x4_t vkg[2], vqg[2];
 #pragma unroll
-            for (int tl = 0; tl < 16; ++tl) {
-                const int t = 16 * bb + tl;
+            for (int tl = 0; tl < 8; ++tl) {
+                const int t = 16 * bb + 8 * half + tl;
                 const float gm = before * sF[t * LDH + ii];
                 const float kt = sK[t * LDH + ii];
-                kg[(slot * D + i) * C + t] = kt * gm;
-                qg[(slot * D + i) * C + t] = sQ[t * LDH + ii] * gm;
-                sKG[t * (D + 4) + i] = kt * gm;
+                vkg[tl >> 2][tl & 3] = kt * gm;
+                vqg[tl >> 2][tl & 3] = sQ[t * LDH + ii] * gm;
                 kb[(slot * C + t) * D + i] = kt * sR[t * LDH + ii] * after;
             }
-            if (bb == kNB - 1) gC[slot * D + i] = before * bp[kNB - 1];
+            const size_t row = (slot * D + i) * C + 16 * bb + 8 * half;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                *reinterpret_cast<f32x4_t *>(kg + row + 4 * h2) = vkg[h2];
+                *reinterpret_cast<f32x4_t *>(qg + row + 4 * h2) = vqg[h2];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -227,90 +255,115 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
             const float *sX = mat == 0 ? sK : sQ;
             acc[j] = mm16<DH>(
                 [&](int rr, int kk) { return sX[(16 * bt + rr) * LDH + kk] * sF[(16 * bt + rr) * LDH + kk]; },
-                [&](int cc, int kk) {
-                    return sK[(16 * bs + cc) * LDH + kk] * sR[(16 * bs + cc) * LDH + kk] * sMid[pr * DH + kk];
+                [&](int cc2, int kk) {
+                    return sK[(16 * bs + cc2) * LDH + kk] * sR[(16 * bs + cc2) * LDH + kk] * sMid[pr * DH + kk];
                 },
                 acc[j]);
         }
-        __syncthreads();
-        // Sub-block pivots (replacing the block ones): F4, R4 and whole-sub-block products B4.
-        float *sB4 = sMid;
-        {
-            // Thread (channel, block): its four sub-blocks.
-            const int ii = tid % DH, bb = tid / DH;
+        // (K*gamma) S0 over this pass's channels; the A operand is K*gamma as stored above.
 #pragma unroll
-            for (int u = 4 * bb; u < 4 * bb + 4; ++u) {
+        for (int tt = 0; tt < kNB; ++tt) {
+#pragma unroll
+            for (int m = 0; m < DH / 4; ++m) {
+                const int t = 16 * tt + cc, kk = 4 * m + kq;
+                const float kgv = sK[t * LDH + kk] * (sBef[tt * DH + kk] * sF[t * LDH + kk]);
+#pragma unroll
+                for (int jj = 0; jj < NJT; ++jj)
+                    pacc[jj][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kgv, bS[jj][m], pacc[jj][tt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        {
+            // Thread (channel, block, half): F4, R4 and the whole-sub-block products of two of
+            // the block's sub-blocks (replacing the block pivots).
+            const int ii = tid % DH, bb = (tid / DH) % kNB, half = tid / (DH * kNB);
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int us = 4 * bb + 2 * half + u2;
                 float run = 1.f;
 #pragma unroll
                 for (int tl = 0; tl < 4; ++tl) {
-                    run *= sA[(4 * u + tl) * LDH + ii];
-                    sF[(4 * u + tl) * LDH + ii] = run;
+                    run *= sA[(4 * us + tl) * LDH + ii];
+                    sF[(4 * us + tl) * LDH + ii] = run;
                 }
                 run = 1.f;
 #pragma unroll
                 for (int tl = 3; tl >= 0; --tl) {
-                    sR[(4 * u + tl) * LDH + ii] = run;
-                    run *= sA[(4 * u + tl) * LDH + ii];
+                    sR[(4 * us + tl) * LDH + ii] = run;
+                    run *= sA[(4 * us + tl) * LDH + ii];
                 }
-                sB4[u * DH + ii] = run;
+                sB4[us * DH + ii] = run;
             }
         }
         __syncthreads();
-        // Cross-sub-block entries of the diagonal tiles: for gap g (ut = us + g), the s side
-        // carries K * R4 times the products of the g - 1 whole sub-blocks after s's.
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int job = wave + 4 * j;
-            const int mat = job / 4, bb = job % 4;
-            const float *sX = mat == 0 ? sK : sQ;
-            const int rr = lane & 15, kq = lane >> 4;
-            const int us = rr >> 2;  // the B row (column s = 16 bb + rr) sub-block in the block
-            // Inside one sub-block the split repeats at its halves: t in the upper half, s in
-            // the lower takes (a from the half's start through t) x (a after s to the half's
-            // end); t = s + 1 in one half takes a_t; t = s takes 1.
+        {
+            // Diagonal tiles of block bb = w, M (A rows from K) and P (from Q_hat). For gap g
+            // (t's sub-block = s's + g) the s side carries K * R4 times the g - 1 whole
+            // sub-blocks after s's. Inside one sub-block the split repeats at its halves: t in
+            // the upper half, s in the lower takes (a from the half's start through t) x (a after
+            // s to the half's end); t = s + 1 in one half takes a_t; t = s (P only) takes 1.
+            const int bb = wave, rr = lane & 15;
+            const int us = rr >> 2;  // the B row's (column s = 16 bb + rr) sub-block in the block
             const int sub = rr & 3;  // the A row's (and B column's) place in its sub-block
-            f32x4_t y[6] = {zero4(), zero4(), zero4(), zero4(), zero4(), zero4()};
-#pragma unroll 4
+            const int ta = 16 * bb + rr, u0 = 4 * bb + us;
+            // Partial products per sub-block gap (0-2) and half split (3-5).
+            f32x4_t ym[5], yp[6];
+#pragma unroll
+            for (int j = 0; j < 6; ++j) {
+                if (j < 5) ym[j] = zero4();
+                yp[j] = zero4();
+            }
+#pragma unroll 2
             for (int m = 0; m < DH / 4; ++m) {
                 const int kk = 4 * m + kq;
-                const int ta = 16 * bb + rr;
-                const float xt = sX[ta * LDH + kk], ks = sK[ta * LDH + kk];
+                const float kt = sK[ta * LDH + kk], qt = sQ[ta * LDH + kk];
                 const float at = sA[ta * LDH + kk];
                 const float aprev = sA[(sub > 0 ? ta - 1 : ta) * LDH + kk];
                 const float anext = sA[(sub < 3 ? ta + 1 : ta) * LDH + kk];
-                const float av = xt * sF[ta * LDH + kk];
-                const float b1 = ks * sR[ta * LDH + kk];
-                const int u0 = 4 * bb + us;  // s's sub-block in the chunk
+                const float f4 = sF[ta * LDH + kk];
+                const float b1 = kt * sR[ta * LDH + kk];
                 const float m1 = us + 1 < 4 ? sB4[(u0 + 1) * DH + kk] : 0.f;
                 const float m2 = us + 2 < 4 ? sB4[(u0 + 2) * DH + kk] : 0.f;
                 const float b2 = b1 * m1, b3 = b2 * m2;
                 const float f2 = sub == 2 ? at : (sub == 3 ? aprev * at : 0.f);
                 const float r2 = sub == 0 ? anext : (sub == 1 ? 1.f : 0.f);
-                y[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, y[0], 0, 0, 0);
-                y[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b2, y[1], 0, 0, 0);
-                y[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b3, y[2], 0, 0, 0);
-                y[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt * f2, ks * r2, y[3], 0, 0, 0);
-                y[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt * at, ks, y[4], 0, 0, 0);
-                y[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, ks, y[5], 0, 0, 0);
+                const float avm = kt * f4, avp = qt * f4, bh2 = kt * r2;
+                ym[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(avm, b1, ym[0], 0, 0, 0);
+                ym[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(avm, b2, ym[1], 0, 0, 0);
+                ym[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(avm, b3, ym[2], 0, 0, 0);
+                ym[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt * f2, bh2, ym[3], 0, 0, 0);
+                ym[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt * at, kt, ym[4], 0, 0, 0);
+                yp[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(avp, b1, yp[0], 0, 0, 0);
+                yp[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(avp, b2, yp[1], 0, 0, 0);
+                yp[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(avp, b3, yp[2], 0, 0, 0);
+                yp[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt * f2, bh2, yp[3], 0, 0, 0);
+                yp[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt * at, kt, yp[4], 0, 0, 0);
+                yp[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, kt, yp[5], 0, 0, 0);
             }
             // Output lane l: rows 4 (l / 16) + i (sub-block l / 16), column l % 16.
-            const int ut = lane >> 4, sc = lane & 15, usc = sc >> 2;
+            const int ut = kq, usc = cc >> 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tr = 4 * ut + i;  // row within the block
                 const int gap = ut - usc;
-                float add = gap == 1 ? y[0][i] : (gap == 2 ? y[1][i] : (gap == 3 ? y[2][i] : 0.f));
+                float vm = 0.f, vp = 0.f;
+                if (gap == 1) vm = ym[0][i], vp = yp[0][i];
+                if (gap == 2) vm = ym[1][i], vp = yp[1][i];
+                if (gap == 3) vm = ym[2][i], vp = yp[2][i];
                 if (gap == 0) {
-                    if ((tr & 3) >= 2 && (sc & 3) < 2) add = y[3][i];
-                    else if ((tr & 1) == 1 && sc == tr - 1) add = y[4][i];
-                    else if (sc == tr && mat == 1) add = y[5][i];
+                    if ((tr & 3) >= 2 && (cc & 3) < 2) vm = ym[3][i], vp = yp[3][i];
+                    else if ((tr & 1) == 1 && cc == tr - 1) vm = ym[4][i], vp = yp[4][i];
+                    else if (cc == tr) vp = yp[5][i];
                 }
-                dacc[j][i] += add;
+                dm[i] += vm;
+                dp[i] += vp;
             }
         }
     }
     __syncthreads();
-    // M and P into LDS (the upper parts and M's diagonal stay zero).
+    // M and P into LDS over the pass arrays. Only the strictly lower part of M and the lower
+    // part of P (with its diagonal) are written; every read below masks the rest.
+    float *sM = lds, *sP = lds + C * LDM;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int job = wave + 4 * j;
@@ -319,49 +372,44 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepare_kernel(
         const int bs = pr - bt * (bt - 1) / 2;
         float *dst = mat == 0 ? sM : sP;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * bt + 4 * (lane >> 4) + i) * LDM + 16 * bs + (lane & 15)] = acc[j][i];
+        for (int i = 0; i < 4; ++i) dst[(16 * bt + 4 * kq + i) * LDM + 16 * bs + cc] = acc[j][i];
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int job = wave + 4 * j;
-        const int mat = job / 4, bb = job % 4;
-        float *dst = mat == 0 ? sM : sP;
-        const int ut = lane >> 4, sc = lane & 15;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (sc <= 4 * ut + i) dst[(16 * bb + 4 * ut + i) * LDM + 16 * bb + sc] = dacc[j][i];
+    for (int i = 0; i < 4; ++i) {
+        const int tr = 4 * kq + i;  // row within the diagonal block
+        if (cc <= tr) {
+            sM[(16 * wave + tr) * LDM + 16 * wave + cc] = dm[i];
+            sP[(16 * wave + tr) * LDM + 16 * wave + cc] = dp[i];
+        }
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
         const int t = idx / C, s = idx % C;
-        Mw[slot * C * C + idx] = sM[t * LDM + s];
-        Pw[slot * C * C + idx] = sP[s * LDM + t];  // P transposed: row t holds P[., t]
+        Mw[slot * C * C + idx] = s < t ? sM[t * LDM + s] : 0.f;
+        Pw[slot * C * C + idx] = t <= s ? sP[s * LDM + t] : 0.f;  // P transposed: row t holds P[., t]
     }
-    // p = (K*gamma) S0 + M U, [C x D]: wave w owns value-column tiles w, w + 4, ...
-    const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
+    // p = (K*gamma) S0 + M U: the M U part, then the tokens of the chunk are stored.
     const float *Ub = u + (size_t(b) * T + c0) * HD + size_t(h) * D;
-    for (int jt = wave; jt < D / 16; jt += 4) {
-        // This lane's B operands of every contraction step, loaded together.
-        const int cc = lane & 15, kq = lane >> 4;
-        float bS[D / 4], bU[C / 4];
 #pragma unroll
-        for (int m = 0; m < D / 4; ++m) bS[m] = S0[size_t(4 * m + kq) * D + 16 * jt + cc];
+    for (int jj = 0; jj < NJT; ++jj) {
+        const int jt = wave + 4 * jj;
+        float bU[C / 4];
 #pragma unroll
         for (int m = 0; m < C / 4; ++m)
             bU[m] = 4 * m + kq < nval ? Ub[size_t(4 * m + kq) * HD + 16 * jt + cc] : 0.f;
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
-            f32x4_t y = zero4();
+            const int t = 16 * tt + cc;
 #pragma unroll
-            for (int m = 0; m < D / 4; ++m)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sKG[(16 * tt + cc) * (D + 4) + 4 * m + kq], bS[m], y, 0, 0, 0);
-#pragma unroll
-            for (int m = 0; m < C / 4; ++m)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * tt + cc) * LDM + 4 * m + kq], bU[m], y, 0, 0, 0);
+            for (int m = 0; m < C / 4; ++m) {
+                const int s = 4 * m + kq;
+                const float mv = s < t ? sM[t * LDM + s] : 0.f;
+                pacc[jj][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(mv, bU[m], pacc[jj][tt], 0, 0, 0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tt + 4 * (lane >> 4) + i;
-                if (t < nval) pred[tok0 + size_t(t) * HD + 16 * jt + (lane & 15)] = y[i];
+                const int t2 = 16 * tt + 4 * kq + i;
+                if (t2 < nval) pred[tok0 + size_t(t2) * HD + 16 * jt + cc] = pacc[jj][tt][i];
             }
         }
     }
