@@ -33,9 +33,11 @@
 //                       last two channel-major), gamma_C, M and P transposed, and p.
 //   bwd_scan_kernel     one workgroup per (b, h, 16 value columns), chunks in reverse: the
 //                       transposed triangular solve, the adjoint carry, dv, dw, de.
-//   bwd_grads_kernel    one workgroup per (b, h, chunk): O U^T, dP U^T and the state products,
-//                       then the decayed pair sums for dq_hat and dk, then dq, dk, dg and
-//                       a * dL/da (a reverse cumulative sum per channel).
+//   bwd_products_kernel one workgroup per (b, h, chunk): O U^T, dP U^T and the state terms
+//                       dO S0^T, dP S0^T, U lambda_C^T.
+//   bwd_grads_kernel    one workgroup per (b, h, chunk, 64 key channels): per 16 channels the
+//                       decayed pair sums for dq_hat and dk, then dq, dk, dg and a * dL/da (a
+//                       reverse cumulative sum per channel).
 //   bwd_dr_kernel       dr summed over batch and chunks.
 #include <hip/hip_runtime.h>
 
@@ -640,273 +642,319 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// Chunk-parallel gradients. LDS: O U^T and dP U^T [C][C + 1]; then a union of U, dO, dP
-// [C][D + 4] (products) and k, a, q_hat channel-major [D][C + 1] (decayed sums).
+// Products. One workgroup per (b, h, chunk), four wavefronts, no LDS. Wave w keeps rows
+// 16 w .. 16 w + 15 of dO, dP = -e * dU and U in registers as matrix-core A operands and
+// streams 16-row tiles of S0, lambda_C and U past them (the next tile loads while the current
+// one is multiplied):
+//   Y1 = dO S0^T, Y2 = dP S0^T, Y3 = U lambda_C^T    [C x D], stored [D/16][C][16] per chunk
+//   OU = dO U^T (s <= t), PU = dP U^T (s < t)         [C x C] per chunk, upper parts zero.
+// Y1 and Y2 are the state terms of dq_hat and of the read part of dk, Y3 that of the write
+// part of dk; OU and PU weight the decayed pair sums.
 // ------------------------------------------------------------------------------------------
-template <int D> struct GradLds {
-    // Rows of DH = 16 floats: a matrix-core step reads 4 rows x 16 channels, one bank each.
-    static constexpr int LDM = kC + 1, DH = 16, LDH = DH;
-    static constexpr int OUPU = 2 * kC * LDM;
-    // Per 16-channel pass: a, k, q_hat, F, R (16-token blocks), F4, R4 (4-token sub-blocks)
-    // [C][16]; products of whole blocks between (6 pairs), of whole sub-blocks (16), of the
-    // blocks before and after each block (4 + 4), per channel. About 67 KB in all for d = 128,
-    // so two workgroups share a compute unit.
-    static constexpr int P2 = 7 * kC * LDH + (6 + 16 + 4 + 4) * DH;
-    static constexpr int FLOATS = OUPU + 2 * D + (P2 > kBwdThreads ? P2 : kBwdThreads) + kNB * DH +
-                                  kNB * 4 * DH;
-    static constexpr size_t BYTES = size_t(FLOATS) * 4;
-};
-
 template <typename QT, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
-    const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ dout,
-    const float *__restrict__ a, const float *__restrict__ g, const float *__restrict__ e,
-    const float *__restrict__ r, const float *__restrict__ U, const float *__restrict__ dU,
-    const float *__restrict__ states, const float *__restrict__ lamC, float *__restrict__ X3,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg,
-    float *__restrict__ dla, float *__restrict__ drp, int T, int H, int nchunks) {
-    using L = GradLds<D>;
-    constexpr int C = kC, LDM = L::LDM, LDH = L::LDH, DH = L::DH;
-    extern __shared__ float lds[];
-    float *sOU = lds, *sPU = lds + C * LDM;
-    float *sRS = lds + L::OUPU;  // rowsum(S_C * lambda_C) per channel
-    float *sDr = sRS + D;        // sum over tokens of g * q * dq_hat per channel
-    float *un = sDr + D;
-    float *sA = un, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH, *sR = sF + C * LDH,
-          *sF4 = sR + C * LDH, *sR4 = sF4 + C * LDH, *sMid = sR4 + C * LDH, *sB4 = sMid + 6 * DH,
-          *sGb = sB4 + 16 * DH, *sBa = sGb + 4 * DH;
-    float *sBp = lds + L::FLOATS - kNB * DH;  // whole-block decay products per channel
-    // dr partials of one pass: [16-token block][lane group][channel], summed in a fixed order.
-    float *sDrP = sBp - kNB * 4 * DH;
-
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_products_kernel(
+    const QT *__restrict__ dout, const float *__restrict__ e, const float *__restrict__ U,
+    const float *__restrict__ dU, const float *__restrict__ states, const float *__restrict__ lamC,
+    float *__restrict__ Y1, float *__restrict__ Y2, float *__restrict__ Y3, float *__restrict__ OU,
+    float *__restrict__ PU, int T, int H, int nchunks) {
+    constexpr int C = kC, NT = D / 16;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rr = lane & 15, kq = lane >> 4;
     const size_t HD = size_t(H) * D;
     const int c0 = c * C;
     const int nval = min(C, T - c0);
     const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
     const size_t slot = size_t(bh) * nchunks + c;
     const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
-    const float *SC = S0 + size_t(D) * D;
     const float *lam = lamC + slot * D * D;
 
-    // Rows of U, dO and dP = -e * dU as matrix-core operands straight from memory: 16 bytes per
-    // load, contraction step (mo, mi) of lane group kq taking k = 16 mo + 4 kq + mi. Tokens past
-    // the sequence read as zero.
+    // Contraction step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi: a lane's four
+    // values of one mo are one 16-byte load. Tokens past the sequence read as zero.
+    const int ta = 16 * wave + rr;
+    const bool tok_ok = ta < nval;
+    f32x4_t xo[NT], xp[NT], xu[NT];
+#pragma unroll
+    for (int mo = 0; mo < NT; ++mo) {
+        const size_t o = tok0 + size_t(ta) * HD + 16 * mo + 4 * kq;
+        xo[mo] = tok_ok ? ld4(dout, o) : zero4();
+        xp[mo] = tok_ok ? -ld4(e, o) * ld4(dU, o) : zero4();
+        xu[mo] = tok_ok ? ld4(U, o) : zero4();
+    }
+    auto load_rows = [&](const float *S, int row, f32x4_t (&x)[NT]) {
+#pragma unroll
+        for (int mo = 0; mo < NT; ++mo) x[mo] = ld4(S, size_t(row) * D + 16 * mo + 4 * kq);
+    };
+    // Output lane l: rows 4 (l / 16) + i of the wave's block, column l % 16 of the tile.
+    auto store_y = [&](float *Y, int it, f32x4_t y) {
+        float *dst = Y + ((slot * NT + it) * C + 16 * wave + 4 * kq) * 16 + rr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * i] = y[i];
+    };
+    f32x4_t bS[2][NT], bL[2][NT];
+    load_rows(S0, rr, bS[0]);
+    load_rows(lam, rr, bL[0]);
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+        const int cur = it & 1;
+        if (it + 1 < NT) {
+            load_rows(S0, 16 * (it + 1) + rr, bS[cur ^ 1]);
+            load_rows(lam, 16 * (it + 1) + rr, bL[cur ^ 1]);
+        }
+        f32x4_t y1 = zero4(), y2 = zero4(), y3 = zero4();
+#pragma unroll
+        for (int mo = 0; mo < NT; ++mo)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bS[cur][mo][mi], y1, 0, 0, 0);
+                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bS[cur][mo][mi], y2, 0, 0, 0);
+                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bL[cur][mo][mi], y3, 0, 0, 0);
+            }
+        store_y(Y1, it, y1);
+        store_y(Y2, it, y2);
+        store_y(Y3, it, y3);
+    }
+    // O U^T and dP U^T: the wave's row block against each column block bs <= w (U rows of
+    // block bs, the next loading while the current is multiplied); blocks after w are zero.
+    const float *Ub = U + tok0;
+    auto load_u = [&](int bs, f32x4_t (&x)[NT]) {
+        const int s = 16 * bs + rr;
+#pragma unroll
+        for (int mo = 0; mo < NT; ++mo) x[mo] = s < nval ? ld4(Ub, size_t(s) * HD + 16 * mo + 4 * kq) : zero4();
+    };
+    f32x4_t bu[2][NT];
+    load_u(0, bu[0]);
+#pragma unroll
+    for (int bs = 0; bs < kNB; ++bs) {
+        const int cur = bs & 1;
+        f32x4_t yo = zero4(), yp = zero4();
+        if (bs <= wave) {
+            if (bs + 1 <= wave) load_u(bs + 1, bu[cur ^ 1]);
+#pragma unroll
+            for (int mo = 0; mo < NT; ++mo)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    yo = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bu[cur][mo][mi], yo, 0, 0, 0);
+                    yp = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bu[cur][mo][mi], yp, 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * wave + 4 * kq + i, s = 16 * bs + rr;
+            OU[(slot * C + t) * C + s] = s <= t ? yo[i] : 0.f;
+            PU[(slot * C + t) * C + s] = s < t ? yp[i] : 0.f;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Chunk-parallel gradients. One workgroup per (b, h, chunk, group of 64 key channels); the
+// groups of one chunk take consecutive dispatch slots of one XCD, so they share its L2.
+//   1. rowsum(S_C * lambda_C) of the group's channels; O U^T and dP U^T into LDS.
+//   2. Per 16-channel pass, after the pivots: wave w takes the rows t of block w (dq_hat and the
+//      read part of dk) and the rows s of block w (the write part of dk), each its state term
+//      from the products kernel plus the decayed pair sums on the matrix cores. dq and dg are
+//      stored; the two parts of dk and the log-decay terms meet in LDS.
+//   3. Per pass: dk, and a * dL/da as a reverse cumulative sum over the chunk per channel.
+// The next pass's operands load while the current pass runs.
+// LDS: O U^T and dP U^T [C][C + 1]; per pass a, k, q_hat, F, R (16-token blocks), F4, R4
+// (4-token sub-blocks) [C][16] and the per-channel products of whole blocks and sub-blocks;
+// the read and write parts of dk and the log-decay terms [C][17]. About 78 KB, so two
+// workgroups share a compute unit.
+// ------------------------------------------------------------------------------------------
+template <int D> struct GradLds {
+    static constexpr int DG = 64;     // key channels per workgroup
+    static constexpr int G = D / DG;  // workgroups per chunk
+    static constexpr int LDM = kC + 1, DH = 16, LDH = DH, LDO = DH + 1;
+    static constexpr int OUPU = 2 * kC * LDM;
+    static constexpr int PASS = 7 * kC * LDH + (6 + 16 + 4 + 4) * DH;
+    static constexpr int OUTS = 3 * kC * LDO;
+    static constexpr int SMALL = 2 * DG + kNB * 4 * DH + kNB * DH + 16 * DH;
+    static constexpr int FLOATS = OUPU + PASS + OUTS + SMALL;
+    static constexpr size_t BYTES = size_t(FLOATS) * 4;
+};
+
+template <typename QT, int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_grads_kernel(
+    const QT *__restrict__ q, const QT *__restrict__ k, const float *__restrict__ a,
+    const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
+    const float *__restrict__ lamC, const float *__restrict__ Y1, const float *__restrict__ Y2,
+    const float *__restrict__ Y3, const float *__restrict__ OU, const float *__restrict__ PU,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dla,
+    float *__restrict__ drp, int T, int H, int nchunks, int nwork) {
+    using L = GradLds<D>;
+    constexpr int C = kC, LDM = L::LDM, LDH = L::LDH, DH = L::DH, LDO = L::LDO, G = L::G, DG = L::DG;
+    constexpr int NT = D / 16;
+    static_assert(kBwdThreads == 16 * DH && kNB == 4, "thread roles assume 256 threads, 4 blocks");
+    extern __shared__ float lds[];
+    float *sOU = lds, *sPU = lds + C * LDM;
+    float *pass = lds + L::OUPU;
+    float *sA = pass, *sK = sA + C * LDH, *sQ = sK + C * LDH, *sF = sQ + C * LDH, *sR = sF + C * LDH,
+          *sF4 = sR + C * LDH, *sR4 = sF4 + C * LDH, *sMid = sR4 + C * LDH, *sB4 = sMid + 6 * DH,
+          *sGb = sB4 + 16 * DH, *sBa = sGb + 4 * DH;
+    float *sDkr = pass + L::PASS, *sDkw = sDkr + C * LDO, *sLa = sDkw + C * LDO;
+    float *sRS = sLa + C * LDO;        // rowsum(S_C * lambda_C) per channel of the group
+    float *sDr = sRS + DG;             // sum over tokens of g * q * dq_hat per channel
+    float *sDrP = sDr + DG;            // dr partials of one pass: [block][lane group][channel]
+    float *sBp = sDrP + kNB * 4 * DH;  // whole-block decay products per channel
+    float *sTot = sBp + kNB * DH;      // per-part sums of the reverse cumulative sum
+
+    // Workgroups are dealt to the eight XCDs in turn: slot pos of XCD x is workgroup 8 pos + x.
+    const int wid = blockIdx.x, xcd = wid & 7, pos = wid >> 3;
+    const int work = 8 * (pos / G) + xcd, grp = pos % G;
+    if (work >= nwork) return;
+    const int c = work % nchunks, bh = work / nchunks;
+    const int h = bh % H, b = bh / H;
+    const int gc0 = grp * DG;  // the group's first channel
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rr = lane & 15, kq = lane >> 4;
-    auto rowU = [&](int t, f32x4_t (&x)[D / 16]) {
-#pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo)
-            x[mo] = t < nval ? ld4(U, tok0 + size_t(t) * HD + 16 * mo + 4 * kq) : zero4();
+    const size_t HD = size_t(H) * D;
+    const int c0 = c * C;
+    const int nval = min(C, T - c0);
+    const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
+    const size_t slot = size_t(bh) * nchunks + c;
+    const float *SC = states + (size_t(bh) * (nchunks + 1) + c + 1) * D * D;
+    const float *lam = lamC + slot * D * D;
+    const float *rh = r + size_t(h) * D;
+
+    // A pass's operands from memory: the [C][16] slab of a, k, g, q, r (thread: token tid / 4,
+    // channels 4 (tid % 4) .. + 3) and, for this lane's four rows 16 w + 4 kq + e4 and channel
+    // rr, the state terms and g, q.
+    struct PassIn {
+        f32x4_t a, k, g, q, r;
+        float y1[4], y2[4], y3[4], gg[4], gq[4];
     };
-    auto rowO = [&](int t, f32x4_t (&x)[D / 16]) {
+    auto load_pass = [&](int p0, PassIn &x) {
+        const int t = tid >> 2, ii = 4 * (tid & 3);
+        const size_t o = tok0 + size_t(t) * HD + p0 + ii;
+        if (t < nval) {
+            x.a = ld4(a, o);
+            x.k = ld4(k, o);
+            x.g = ld4(g, o);
+            x.q = ld4(q, o);
+        } else {
+            x.a = f32x4_t{1.f, 1.f, 1.f, 1.f};
+            x.k = x.g = x.q = zero4();
+        }
+        x.r = ld4(rh, p0 + ii);
+        const size_t yo = ((slot * NT + p0 / 16) * C + 16 * wave + 4 * kq) * 16 + rr;
 #pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo)
-            x[mo] = t < nval ? ld4(dout, tok0 + size_t(t) * HD + 16 * mo + 4 * kq) : zero4();
-    };
-    auto rowP = [&](int t, f32x4_t (&x)[D / 16]) {
-#pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo) {
-            const size_t o = tok0 + size_t(t) * HD + 16 * mo + 4 * kq;
-            x[mo] = t < nval ? -ld4(e, o) * ld4(dU, o) : zero4();
+        for (int e4 = 0; e4 < 4; ++e4) {
+            x.y1[e4] = Y1[yo + 16 * e4];
+            x.y2[e4] = Y2[yo + 16 * e4];
+            x.y3[e4] = Y3[yo + 16 * e4];
+            const int t2 = 16 * wave + 4 * kq + e4;
+            const size_t o2 = tok0 + size_t(t2) * HD + p0 + rr;
+            const bool ok = t2 < nval;
+            x.gg[e4] = ok ? g[o2] : 0.f;
+            x.gq[e4] = ok ? ld(q, o2) : 0.f;
         }
     };
-    // rowsum(S_C * lambda_C): thread (row, part) sums a contiguous segment of the row, every
-    // load issued before the first use; the parts' sums are added in a fixed order.
+    PassIn cur;
+    load_pass(gc0, cur);
     {
-        constexpr int TPR = kBwdThreads / D;  // threads per row
-        constexpr int SEG = D / TPR;          // elements per thread
-        const int i = tid / TPR, part = tid % TPR;
+        // O U^T and dP U^T into LDS: thread tid takes 16-byte pieces tid, tid + 256, ...
+        constexpr int N4 = C * C / 4 / kBwdThreads;
+        f32x4_t vo[N4], vp[N4];
+        const f32x4_t *OU4 = reinterpret_cast<const f32x4_t *>(OU + slot * C * C);
+        const f32x4_t *PU4 = reinterpret_cast<const f32x4_t *>(PU + slot * C * C);
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            vo[j] = OU4[tid + kBwdThreads * j];
+            vp[j] = PU4[tid + kBwdThreads * j];
+        }
+        // rowsum(S_C * lambda_C) of the group's channels: thread (row, part) sums a contiguous
+        // segment of the row; the parts' sums are added in a fixed order.
+        constexpr int TPR = kBwdThreads / DG;  // threads per row
+        constexpr int SEG = D / TPR;           // elements per thread
+        const int il = tid / TPR, part = tid % TPR, i = gc0 + il;
         f32x4_t xs[SEG / 4], xl[SEG / 4];
 #pragma unroll
         for (int j = 0; j < SEG / 4; ++j) {
             xs[j] = ld4(SC, size_t(i) * D + part * SEG + 4 * j);
             xl[j] = ld4(lam, size_t(i) * D + part * SEG + 4 * j);
         }
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / C, s = e0 % C;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sOU[t * LDM + s + q4] = vo[j][q4];
+                sPU[t * LDM + s + q4] = vp[j][q4];
+            }
+        }
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < SEG / 4; ++j)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) acc = fmaf(xs[j][q4], xl[j][q4], acc);
-        un[part * D + i] = acc;  // the pass arrays are not in use yet
+        sTot[part * DG + il] = acc;
         __syncthreads();
         if (part == 0) {
             float sum = 0.f;
 #pragma unroll
-            for (int p2 = 0; p2 < TPR; ++p2) sum += un[p2 * D + i];
-            sRS[i] = sum;
+            for (int p2 = 0; p2 < TPR; ++p2) sum += sTot[p2 * DG + il];
+            sRS[il] = sum;
         }
     }
-    for (int i = tid; i < D; i += kBwdThreads) sDr[i] = 0.f;
-    __syncthreads();
-    // O U^T (s <= t) and dP U^T (s < t), lower 16x16 tiles; job j < 20: matrix j / 10, tile
-    // j % 10 = bt (bt + 1) / 2 + bs.
-    for (int job = wave; job < 20; job += 4) {
-        const int mat = job / 10, tl = job % 10;
-        const int bt = tl < 1 ? 0 : (tl < 3 ? 1 : (tl < 6 ? 2 : 3));
-        const int bs = tl - bt * (bt + 1) / 2;
-        f32x4_t xa[D / 16], xb[D / 16];
-        if (mat == 0) rowO(16 * bt + rr, xa);
-        else rowP(16 * bt + rr, xa);
-        rowU(16 * bs + rr, xb);
-        f32x4_t y = zero4();
-#pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) y = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[mo][mi], xb[mo][mi], y, 0, 0, 0);
-        float *dst = mat == 0 ? sOU : sPU;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * bt + 4 * (lane >> 4) + i, s = 16 * bs + (lane & 15);
-            dst[t * LDM + s] = (mat == 0 ? s <= t : s < t) ? y[i] : 0.f;
-        }
-    }
-    // dO S0^T -> dq, dP S0^T -> dk, U lambda_C^T -> X3 (unscaled), [C x D]. Wave w owns the
-    // channel tiles w + 4 j; its rows of S0 (then lambda_C) stay in registers over the four
-    // token tiles, so each state is read from memory once per chunk.
-    constexpr int NTW = D / 64;  // channel tiles per wave
-    {
-        f32x4_t bv[NTW][D / 16];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int mo = 0; mo < D / 16; ++mo)
-                bv[j][mo] = ld4(S0, size_t(16 * (wave + 4 * j) + rr) * D + 16 * mo + 4 * kq);
-#pragma unroll 1
-        for (int tt = 0; tt < kNB; ++tt) {
-            f32x4_t xo[D / 16], xp[D / 16];
-            rowO(16 * tt + rr, xo);
-            rowP(16 * tt + rr, xp);
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int it = wave + 4 * j;
-                f32x4_t y1 = zero4(), y2 = zero4();
-#pragma unroll
-                for (int mo = 0; mo < D / 16; ++mo)
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi) {
-                        y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bv[j][mo][mi], y1, 0, 0, 0);
-                        y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bv[j][mo][mi], y2, 0, 0, 0);
-                    }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tt + 4 * kq + i;
-                    if (t < nval) {
-                        const size_t o = tok0 + size_t(t) * HD + 16 * it + rr;
-                        dq[o] = y1[i];
-                        dk[o] = y2[i];
-                    }
-                }
-            }
-        }
-    }
-    {
-        f32x4_t bv[NTW][D / 16];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int mo = 0; mo < D / 16; ++mo)
-                bv[j][mo] = ld4(lam, size_t(16 * (wave + 4 * j) + rr) * D + 16 * mo + 4 * kq);
-#pragma unroll 1
-        for (int tt = 0; tt < kNB; ++tt) {
-            f32x4_t xu[D / 16];
-            rowU(16 * tt + rr, xu);
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int it = wave + 4 * j;
-                f32x4_t y3 = zero4();
-#pragma unroll
-                for (int mo = 0; mo < D / 16; ++mo)
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi)
-                        y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bv[j][mo][mi], y3, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tt + 4 * kq + i;
-                    if (t < nval) X3[tok0 + size_t(t) * HD + 16 * it + rr] = y3[i];
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const float *rh = r + size_t(h) * D;
+    for (int i = tid; i < DG; i += kBwdThreads) sDr[i] = 0.f;
     // Decayed sums over token pairs, per 16-channel pass, on the matrix cores. With the pivots
     // of the prepare kernel, Gamma_ts = F_t * mid * R_s across 16-token blocks and
     // F4_t * mid4 * R4_s across 4-token sub-blocks of one block; pairs inside one sub-block are
-    // direct products. Jobs: kind 0 (dq_hat and the read part of dk, rows = t) and kind 1 (the
-    // write part of dk, rows = s), one 16-row block each; wave w takes jobs w and w + 4.
-    // The dr partials of the pass before, added in a fixed order (block, then lane group).
-    auto fold_dr = [&](int pp) {
-        if (tid < DH) {
-            float sum = 0.f;
-#pragma unroll
-            for (int x = 0; x < kNB * 4; ++x) sum += sDrP[x * DH + tid];
-            sDr[pp + tid] = sum;
-        }
-    };
-    for (int p0 = 0; p0 < D; p0 += DH) {
-        if (p0 > 0) {
-            __syncthreads();
-            fold_dr(p0 - DH);
-        }
+    // direct products.
+    for (int pp = 0; pp < DG / DH; ++pp) {
+        const int p0 = gc0 + pp * DH;  // the pass's first channel
+        const int ic = rr;             // this lane's B / output column, within the pass
+        const size_t ocol = size_t(p0 + ic);
+        __syncthreads();  // the previous pass is finished with the pass arrays
         {
-            constexpr int N4 = C * DH / 4 / kBwdThreads;
-            f32x4_t va[N4], vk[N4], vq[N4];
-#pragma unroll
-            for (int j = 0; j < N4; ++j) {
-                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
-                const size_t o = tok0 + size_t(t) * HD + p0 + ii;
-                if (t < nval) {
-                    va[j] = ld4(a, o);
-                    vk[j] = ld4(k, o);
-                    vq[j] = ld4(g, o) * ld4(q, o) * ld4(rh, p0 + ii);
-                } else {
-                    va[j] = f32x4_t{1.f, 1.f, 1.f, 1.f};
-                    vk[j] = vq[j] = zero4();
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < N4; ++j) {
-                const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / DH, ii = e0 % DH;
-                *reinterpret_cast<f32x4_t *>(&sA[t * LDH + ii]) = va[j];
-                *reinterpret_cast<f32x4_t *>(&sK[t * LDH + ii]) = vk[j];
-                *reinterpret_cast<f32x4_t *>(&sQ[t * LDH + ii]) = vq[j];
-            }
+            const int t = tid >> 2, ii = 4 * (tid & 3);
+            *reinterpret_cast<f32x4_t *>(&sA[t * LDH + ii]) = cur.a;
+            *reinterpret_cast<f32x4_t *>(&sK[t * LDH + ii]) = cur.k;
+            *reinterpret_cast<f32x4_t *>(&sQ[t * LDH + ii]) = cur.g * cur.q * cur.r;
         }
+        PassIn nxt;
+        if (pp + 1 < DG / DH) load_pass(p0 + DH, nxt);
         __syncthreads();
-        if (tid < DH * kNB) {
-            // Thread (channel, 16-token block): prefix and suffix products inside the block
-            // and inside its four sub-blocks.
-            const int ii = tid % DH, bb = tid / DH;
-            float run = 1.f;
+        {
+            // Pivots, thread (channel, 16-token block, role = wave): 0 the prefix F inside the
+            // block, 1 the suffix R and the block's product, 2 and 3 the prefix F4, suffix R4
+            // and product of two sub-blocks each.
+            const int ii = tid % DH, bb = (tid / DH) % kNB;
+            if (wave == 0) {
+                float run = 1.f;
 #pragma unroll
-            for (int tl = 0; tl < 16; ++tl) {
-                run *= sA[(16 * bb + tl) * LDH + ii];
-                sF[(16 * bb + tl) * LDH + ii] = run;
-            }
-            run = 1.f;
-#pragma unroll
-            for (int tl = 15; tl >= 0; --tl) {
-                sR[(16 * bb + tl) * LDH + ii] = run;
-                run *= sA[(16 * bb + tl) * LDH + ii];
-            }
-            sBp[bb * DH + ii] = run;
-#pragma unroll
-            for (int u = 4 * bb; u < 4 * bb + 4; ++u) {
-                float r4 = 1.f;
-#pragma unroll
-                for (int tl = 0; tl < 4; ++tl) {
-                    r4 *= sA[(4 * u + tl) * LDH + ii];
-                    sF4[(4 * u + tl) * LDH + ii] = r4;
+                for (int tl = 0; tl < 16; ++tl) {
+                    run *= sA[(16 * bb + tl) * LDH + ii];
+                    sF[(16 * bb + tl) * LDH + ii] = run;
                 }
-                r4 = 1.f;
+            } else if (wave == 1) {
+                float run = 1.f;
 #pragma unroll
-                for (int tl = 3; tl >= 0; --tl) {
-                    sR4[(4 * u + tl) * LDH + ii] = r4;
-                    r4 *= sA[(4 * u + tl) * LDH + ii];
+                for (int tl = 15; tl >= 0; --tl) {
+                    sR[(16 * bb + tl) * LDH + ii] = run;
+                    run *= sA[(16 * bb + tl) * LDH + ii];
                 }
-                sB4[u * DH + ii] = r4;
+                sBp[bb * DH + ii] = run;
+            } else {
+#pragma unroll
+                for (int u2 = 0; u2 < 2; ++u2) {
+                    const int u = 4 * bb + 2 * (wave - 2) + u2;
+                    float r4 = 1.f;
+#pragma unroll
+                    for (int tl = 0; tl < 4; ++tl) {
+                        r4 *= sA[(4 * u + tl) * LDH + ii];
+                        sF4[(4 * u + tl) * LDH + ii] = r4;
+                    }
+                    r4 = 1.f;
+#pragma unroll
+                    for (int tl = 3; tl >= 0; --tl) {
+                        sR4[(4 * u + tl) * LDH + ii] = r4;
+                        r4 *= sA[(4 * u + tl) * LDH + ii];
+                    }
+                    sB4[u * DH + ii] = r4;
+                }
             }
         }
         __syncthreads();
@@ -938,203 +986,173 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(
             }
         }
         __syncthreads();
-        for (int job = wave; job < 2 * kNB; job += 4) {
-            const int kind = job / kNB, rb = job % kNB, it = 0;
-            const int ic = 16 * it + rr;  // this lane's B / output column, within the pass
-            const size_t ocol = size_t(p0 + ic);
-            if (kind == 0) {
-                // Rows t of block bt = rb. The rows' global operands are loaded first.
-                const int bt = rb;
-                float gx1[4], gx2[4], gg[4], gq[4];
+        {
+            // Rows t of block bt = w: dq_hat and the read part of dk.
+            const int bt = wave;
+            f32x4_t cq = zero4(), cr = zero4(), dq4 = zero4(), dr4 = zero4();
+            float drl = 0.f;  // this lane's share of dr: its four tokens, in order
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int t = 16 * bt + 4 * kq + e4;
+            for (int bs = 0; bs < kNB - 1; ++bs) {
+                if (bs >= bt) break;
+                f32x4_t yq = zero4(), yr = zero4();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int kk = 4 * m + kq, sg = 16 * bs + kk;
+                    const float bv = sK[sg * LDH + ic] * sR[sg * LDH + ic];
+                    yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[(16 * bt + rr) * LDM + sg], bv, yq, 0, 0, 0);
+                    yr = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[(16 * bt + rr) * LDM + sg], bv, yr, 0, 0, 0);
+                }
+                const float md = sMid[(bt * (bt - 1) / 2 + bs) * DH + ic];
+                cq += md * yq;
+                cr += md * yr;
+            }
+#pragma unroll
+            for (int gp = 1; gp < 4; ++gp) {
+                f32x4_t yq = zero4(), yr = zero4();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int kk = 4 * m + kq, sg = 16 * bt + kk;
+                    const int us = kk >> 2;
+                    const bool on = (rr >> 2) - us == gp;
+                    float mid4 = 1.f;
+                    if (gp >= 2) mid4 = us + 1 < 4 ? sB4[(4 * bt + us + 1) * DH + ic] : 0.f;
+                    if (gp == 3) mid4 *= us + 2 < 4 ? sB4[(4 * bt + us + 2) * DH + ic] : 0.f;
+                    const float bv = sK[sg * LDH + ic] * sR4[sg * LDH + ic] * mid4;
+                    const float aq = on ? sOU[(16 * bt + rr) * LDM + sg] : 0.f;
+                    const float ar = on ? sPU[(16 * bt + rr) * LDM + sg] : 0.f;
+                    yq = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bv, yq, 0, 0, 0);
+                    yr = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, bv, yr, 0, 0, 0);
+                }
+                dq4 += yq;
+                dr4 += yr;
+            }
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int t = 16 * bt + 4 * kq + e4;
+                // Pairs inside t's sub-block: s = t, t - 1, ... down to its start (a fixed
+                // four-step loop; steps below the start add nothing).
+                float sq = 0.f, sr = 0.f, run = 1.f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s4 = t - u;
+                    const bool on = u <= (t & 3);
+                    const int sc = on ? s4 : t;
+                    const float ks = on ? run * sK[sc * LDH + ic] : 0.f;
+                    sq = fmaf(sOU[t * LDM + sc], ks, sq);
+                    sr = fmaf(sPU[t * LDM + sc], ks, sr);
+                    run *= sA[sc * LDH + ic];
+                }
+                const float fb = sF[t * LDH + ic], f4 = sF4[t * LDH + ic];
+                const float gam = sGb[bt * DH + ic] * fb;
+                const float dqh = gam * cur.y1[e4] + fb * cq[e4] + f4 * dq4[e4] + sq;
+                const float dkr = gam * cur.y2[e4] + fb * cr[e4] + f4 * dr4[e4] + sr;
+                sDkr[t * LDO + ic] = dkr;
+                sLa[t * LDO + ic] = fmaf(sQ[t * LDH + ic], dqh, sK[t * LDH + ic] * dkr);
+                if (t < nval) {
                     const size_t o = tok0 + size_t(t) * HD + ocol;
-                    const bool ok = t < nval;
-                    gx1[e4] = ok ? dq[o] : 0.f;
-                    gx2[e4] = ok ? dk[o] : 0.f;
-                    gg[e4] = ok ? g[o] : 0.f;
-                    gq[e4] = ok ? ld(q, o) : 0.f;
-                }
-                f32x4_t cq = zero4(), cr = zero4(), dq4 = zero4(), dr4 = zero4();
-                float drl = 0.f;  // this lane's share of dr: its four tokens, in order
-#pragma unroll
-                for (int bs = 0; bs < kNB - 1; ++bs) {
-                    if (bs >= bt) break;
-                    f32x4_t yq = zero4(), yr = zero4();
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int kk = 4 * m + kq, sg = 16 * bs + kk;
-                        const float b = sK[sg * LDH + ic] * sR[sg * LDH + ic];
-                        yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[(16 * bt + rr) * LDM + sg], b, yq, 0, 0, 0);
-                        yr = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[(16 * bt + rr) * LDM + sg], b, yr, 0, 0, 0);
-                    }
-                    const float md = sMid[(bt * (bt - 1) / 2 + bs) * DH + ic];
-                    cq += md * yq;
-                    cr += md * yr;
-                }
-#pragma unroll
-                for (int gp = 1; gp < 4; ++gp) {
-                    f32x4_t yq = zero4(), yr = zero4();
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int kk = 4 * m + kq, sg = 16 * bt + kk;
-                        const int us = kk >> 2;
-                        const bool on = (rr >> 2) - us == gp;
-                        float mid4 = 1.f;
-                        if (gp >= 2) mid4 = us + 1 < 4 ? sB4[(4 * bt + us + 1) * DH + ic] : 0.f;
-                        if (gp == 3) mid4 *= us + 2 < 4 ? sB4[(4 * bt + us + 2) * DH + ic] : 0.f;
-                        const float b = sK[sg * LDH + ic] * sR4[sg * LDH + ic] * mid4;
-                        const float aq = on ? sOU[(16 * bt + rr) * LDM + sg] : 0.f;
-                        const float ar = on ? sPU[(16 * bt + rr) * LDM + sg] : 0.f;
-                        yq = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, b, yq, 0, 0, 0);
-                        yr = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, b, yr, 0, 0, 0);
-                    }
-                    dq4 += yq;
-                    dr4 += yr;
-                }
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int t = 16 * bt + 4 * kq + e4;
-                    // Pairs inside t's sub-block: s = t, t - 1, ... down to its start (a fixed
-                    // four-step loop; steps below the start add nothing).
-                    float sq = 0.f, sr = 0.f, run = 1.f;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int s4 = t - u;
-                        const bool on = u <= (t & 3);
-                        const int sc = on ? s4 : t;
-                        const float ks = on ? run * sK[sc * LDH + ic] : 0.f;
-                        sq = fmaf(sOU[t * LDM + sc], ks, sq);
-                        sr = fmaf(sPU[t * LDM + sc], ks, sr);
-                        run *= sA[sc * LDH + ic];
-                    }
-                    const float fb = sF[t * LDH + ic], f4 = sF4[t * LDH + ic];
-                    if (t < nval) {
-                        const size_t o = tok0 + size_t(t) * HD + ocol;
-                        const float gam = sGb[bt * DH + ic] * fb;
-                        const float dqh = gam * gx1[e4] + fb * cq[e4] + f4 * dq4[e4] + sq;
-                        const float dkr = gam * gx2[e4] + fb * cr[e4] + f4 * dr4[e4] + sr;
-                        const float gt = gg[e4], qt = gq[e4];
-                        dq[o] = rh[ocol] * gt * dqh;
-                        dg[o] = rh[ocol] * qt * dqh;
-                        dk[o] = dkr;
-                        dla[o] = fmaf(sQ[t * LDH + ic], dqh, sK[t * LDH + ic] * dkr);
-                        drl += gt * qt * dqh;
-                    }
-                }
-                sDrP[(bt * 4 + kq) * DH + ic] = drl;
-            } else {
-                // Rows s of block bs = rb.
-                const int bs = rb;
-                float gx3[4];
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int s4 = 16 * bs + 4 * kq + e4;
-                    gx3[e4] = s4 < nval ? X3[tok0 + size_t(s4) * HD + ocol] : 0.f;
-                }
-                f32x4_t cw = zero4(), dw4 = zero4();
-#pragma unroll
-                for (int bt = 1; bt < kNB; ++bt) {
-                    if (bt <= bs) continue;
-                    f32x4_t y = zero4();
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int kk = 4 * m + kq, tg = 16 * bt + kk;
-                        const float f = sF[tg * LDH + ic];
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[tg * LDM + 16 * bs + rr], sQ[tg * LDH + ic] * f, y, 0, 0, 0);
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[tg * LDM + 16 * bs + rr], sK[tg * LDH + ic] * f, y, 0, 0, 0);
-                    }
-                    cw += sMid[(bt * (bt - 1) / 2 + bs) * DH + ic] * y;
-                }
-#pragma unroll
-                for (int gp = 1; gp < 4; ++gp) {
-                    f32x4_t y = zero4();
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int kk = 4 * m + kq, tg = 16 * bs + kk;
-                        const int ut = kk >> 2;
-                        const bool on = ut - (rr >> 2) == gp;
-                        // Products of the gp - 1 whole sub-blocks before t's.
-                        float mid4 = 1.f;
-                        if (gp >= 2) mid4 = ut - 1 >= 0 ? sB4[(4 * bs + ut - 1) * DH + ic] : 0.f;
-                        if (gp == 3) mid4 *= ut - 2 >= 0 ? sB4[(4 * bs + ut - 2) * DH + ic] : 0.f;
-                        const float f = sF4[tg * LDH + ic] * mid4;
-                        const float ao = on ? sOU[tg * LDM + 16 * bs + rr] : 0.f;
-                        const float ap = on ? sPU[tg * LDM + 16 * bs + rr] : 0.f;
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sQ[tg * LDH + ic] * f, y, 0, 0, 0);
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, sK[tg * LDH + ic] * f, y, 0, 0, 0);
-                    }
-                    dw4 += y;
-                }
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int s4 = 16 * bs + 4 * kq + e4;
-                    // Pairs inside s's sub-block: t = s, s + 1, ... up to its end (a fixed
-                    // four-step loop; steps past the end add nothing).
-                    float sw = 0.f, run = 1.f;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const bool on = u <= 3 - (s4 & 3);
-                        const int tc = on ? s4 + u : s4;
-                        const float wq = on ? run : 0.f;
-                        sw = fmaf(sOU[tc * LDM + s4], wq * sQ[tc * LDH + ic], sw);
-                        sw = fmaf(sPU[tc * LDM + s4], wq * sK[tc * LDH + ic], sw);
-                        run *= sA[(on && u < 3 - (s4 & 3) ? tc + 1 : tc) * LDH + ic];
-                    }
-                    if (s4 < nval) {
-                        const size_t o = tok0 + size_t(s4) * HD + ocol;
-                        const float rb_ = sR[s4 * LDH + ic], r4 = sR4[s4 * LDH + ic];
-                        const float bet = rb_ * sBa[bs * DH + ic];
-                        X3[o] = bet * gx3[e4] + rb_ * cw[e4] + r4 * dw4[e4] + sw;
-                    }
+                    const float gt = cur.gg[e4], qt = cur.gq[e4];
+                    dq[o] = rh[ocol] * gt * dqh;
+                    dg[o] = rh[ocol] * qt * dqh;
+                    drl += gt * qt * dqh;
                 }
             }
+            sDrP[(bt * 4 + kq) * DH + ic] = drl;
         }
-    }
-    __syncthreads();
-    fold_dr(D - DH);
-    __syncthreads();
-    {
-        // Log-decay gradient: a reverse cumulative sum over the chunk per channel. Thread (part,
-        // channel) takes TP consecutive tokens: suffix sums inside its part, then the totals of
-        // the later parts (through LDS) and rowsum(S_C * lambda_C).
-        constexpr int NP = kBwdThreads / D, TP = C / NP;
-        const int i = tid % D, part = tid / D;
-        if (part == 0) drp[slot * D + i] = sDr[i];
-        float *sTot = un;  // [NP][D]; the pass arrays are no longer read
-        float x3[TP], la[TP], dkv[TP], kv[TP];
+        {
+            // Rows s of block bs = w: the write part of dk.
+            const int bs = wave;
+            f32x4_t cw = zero4(), dw4 = zero4();
 #pragma unroll
-        for (int u = 0; u < TP; ++u) {
-            const int t = part * TP + u;
-            const size_t o = tok0 + size_t(t) * HD + i;
-            const bool ok = t < nval;
-            x3[u] = ok ? X3[o] : 0.f;
-            la[u] = ok ? dla[o] : 0.f;
-            dkv[u] = ok ? dk[o] : 0.f;
-            kv[u] = ok ? ld(k, o) : 0.f;
-        }
-        float cum[TP];
-        float run = 0.f;
+            for (int bt = 1; bt < kNB; ++bt) {
+                if (bt <= bs) continue;
+                f32x4_t y = zero4();
 #pragma unroll
-        for (int u = TP - 1; u >= 0; --u) {
-            run += la[u] - kv[u] * x3[u];
-            cum[u] = run;
+                for (int m = 0; m < 4; ++m) {
+                    const int kk = 4 * m + kq, tg = 16 * bt + kk;
+                    const float f = sF[tg * LDH + ic];
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sOU[tg * LDM + 16 * bs + rr], sQ[tg * LDH + ic] * f, y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sPU[tg * LDM + 16 * bs + rr], sK[tg * LDH + ic] * f, y, 0, 0, 0);
+                }
+                cw += sMid[(bt * (bt - 1) / 2 + bs) * DH + ic] * y;
+            }
+#pragma unroll
+            for (int gp = 1; gp < 4; ++gp) {
+                f32x4_t y = zero4();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int kk = 4 * m + kq, tg = 16 * bs + kk;
+                    const int ut = kk >> 2;
+                    const bool on = ut - (rr >> 2) == gp;
+                    // Products of the gp - 1 whole sub-blocks before t's.
+                    float mid4 = 1.f;
+                    if (gp >= 2) mid4 = ut - 1 >= 0 ? sB4[(4 * bs + ut - 1) * DH + ic] : 0.f;
+                    if (gp == 3) mid4 *= ut - 2 >= 0 ? sB4[(4 * bs + ut - 2) * DH + ic] : 0.f;
+                    const float f = sF4[tg * LDH + ic] * mid4;
+                    const float ao = on ? sOU[tg * LDM + 16 * bs + rr] : 0.f;
+                    const float ap = on ? sPU[tg * LDM + 16 * bs + rr] : 0.f;
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sQ[tg * LDH + ic] * f, y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, sK[tg * LDH + ic] * f, y, 0, 0, 0);
+                }
+                dw4 += y;
+            }
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int s4 = 16 * bs + 4 * kq + e4;
+                // Pairs inside s's sub-block: t = s, s + 1, ... up to its end (a fixed
+                // four-step loop; steps past the end add nothing).
+                float sw = 0.f, run = 1.f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool on = u <= 3 - (s4 & 3);
+                    const int tc = on ? s4 + u : s4;
+                    const float wq = on ? run : 0.f;
+                    sw = fmaf(sOU[tc * LDM + s4], wq * sQ[tc * LDH + ic], sw);
+                    sw = fmaf(sPU[tc * LDM + s4], wq * sK[tc * LDH + ic], sw);
+                    run *= sA[(on && u < 3 - (s4 & 3) ? tc + 1 : tc) * LDH + ic];
+                }
+                const float rb_ = sR[s4 * LDH + ic], r4 = sR4[s4 * LDH + ic];
+                const float bet = rb_ * sBa[bs * DH + ic];
+                sDkw[s4 * LDO + ic] = bet * cur.y3[e4] + rb_ * cw[e4] + r4 * dw4[e4] + sw;
+            }
         }
-        sTot[part * D + i] = run;
         __syncthreads();
-        float off = sRS[i];
-        for (int p2 = part + 1; p2 < NP; ++p2) off += sTot[p2 * D + i];
+        {
+            // dk = read part + write part, and the log-decay gradient: a reverse cumulative sum
+            // over the chunk per channel of q_hat dq_hat + k dk_read - k dk_write, plus
+            // rowsum(S_C * lambda_C). Thread (channel, part) takes four consecutive tokens.
+            const int ii = tid % DH, part = tid / DH;
+            float cum[4], run = 0.f;
 #pragma unroll
-        for (int u = 0; u < TP; ++u) {
-            const int t = part * TP + u;
-            if (t < nval) {
-                const size_t o = tok0 + size_t(t) * HD + i;
-                dla[o] = cum[u] + off;
-                dk[o] = dkv[u] + x3[u];
+            for (int u = 3; u >= 0; --u) {
+                const int t = 4 * part + u;
+                run += sLa[t * LDO + ii] - sK[t * LDH + ii] * sDkw[t * LDO + ii];
+                cum[u] = run;
+            }
+            sTot[part * DH + ii] = run;
+            if (tid < DH) {
+                // The dr partials of the pass, added in a fixed order (block, then lane group).
+                float sum = 0.f;
+#pragma unroll
+                for (int x = 0; x < kNB * 4; ++x) sum += sDrP[x * DH + tid];
+                sDr[pp * DH + tid] = sum;
+            }
+            __syncthreads();
+            float off = sRS[pp * DH + ii];
+            for (int p2 = part + 1; p2 < C / 4; ++p2) off += sTot[p2 * DH + ii];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = 4 * part + u;
+                if (t < nval) {
+                    const size_t o = tok0 + size_t(t) * HD + p0 + ii;
+                    dla[o] = cum[u] + off;
+                    dk[o] = sDkr[t * LDO + ii] + sDkw[t * LDO + ii];
+                }
             }
         }
+        if (pp + 1 < DG / DH) cur = nxt;
     }
+    __syncthreads();
+    for (int i = tid; i < DG; i += kBwdThreads) drp[slot * D + gc0 + i] = sDr[i];
 }
 
 // dr[h] = sum over (b, chunk) of the per-chunk partials: 1024 threads, thread (group, channel)
@@ -1173,7 +1191,7 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     float *qg = reinterpret_cast<float *>(ws + L.qg), *gC = reinterpret_cast<float *>(ws + L.gC);
     float *Mw = reinterpret_cast<float *>(ws + L.M), *Pw = reinterpret_cast<float *>(ws + L.P);
     float *pred = reinterpret_cast<float *>(ws + L.pred), *dUw = reinterpret_cast<float *>(ws + L.dU);
-    float *lamC = reinterpret_cast<float *>(ws + L.lamC), *X3 = reinterpret_cast<float *>(ws + L.X3);
+    float *lamC = reinterpret_cast<float *>(ws + L.lamC);
     float *drp = reinterpret_cast<float *>(ws + L.drp);
     const bool bf16 = std::is_same_v<QT, bf16_t>;
     hipError_t err;
@@ -1207,13 +1225,21 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (nchunks > 0) {
+        // The products go where the scan's operands were (K*beta, K*gamma, Q_hat*gamma, M and P
+        // are not read again): Y1, Y2, Y3 over kb, kg, qg, and OU, PU over M, P.
+        float *Y1 = kb, *Y2 = kg, *Y3 = qg, *OU = Mw, *PU = Pw;
+        hipLaunchKernelGGL((bwd_products_kernel<QT, D>), dim3(nchunks, H, B), dim3(kBwdThreads), 0, stream, dout,
+                           x.e, u, dUw, states, lamC, Y1, Y2, Y3, OU, PU, T, H, nchunks);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
         auto kgk = bwd_grads_kernel<QT, D>;
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(kgk), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   int(GradLds<D>::BYTES));
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(kgk, dim3(nchunks, H, B), dim3(kBwdThreads), GradLds<D>::BYTES, stream, q, k, dout,
-                           x.a, x.g, x.e, x.r, u, dUw, states, lamC, X3, x.dq, x.dk, x.dg, x.dla, drp, T, H,
-                           nchunks);
+        const int nwork = BH * nchunks;
+        const int nwg = (nwork + 7) / 8 * 8 * GradLds<D>::G;
+        hipLaunchKernelGGL(kgk, dim3(nwg), dim3(kBwdThreads), GradLds<D>::BYTES, stream, q, k, x.a, x.g, x.r,
+                           states, lamC, Y1, Y2, Y3, OU, PU, x.dq, x.dk, x.dg, x.dla, drp, T, H, nchunks, nwork);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -76,7 +76,6 @@ bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
     L.pred = take(tok * 4);
     L.dU = take(tok * 4);
     L.lamC = take(BH * nc * d * d * 4);
-    L.X3 = take(tok * 4);
     L.drp = take(BH * nc * d * 4);
     L.total = off;
     return true;
