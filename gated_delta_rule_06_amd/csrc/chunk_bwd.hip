@@ -80,6 +80,21 @@ __device__ __forceinline__ f32x4_t ld4(const bf16_t *p, size_t i) {
     return f32x4_t{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])};
 }
 
+// Loads whose conversion to fp32 waits until the value is used: a prefetch of bf16 data that
+// converted at once would make the wave wait for the load right there.
+template <typename QT> struct Raw4 { using type = f32x4_t; };
+template <> struct Raw4<bf16_t> { using type = u16x4_t; };
+__device__ __forceinline__ f32x4_t raw4(const float *p, size_t i) {
+    return *reinterpret_cast<const f32x4_t *>(p + i);
+}
+__device__ __forceinline__ u16x4_t raw4(const bf16_t *p, size_t i) {
+    return *reinterpret_cast<const u16x4_t *>(p + i);
+}
+__device__ __forceinline__ f32x4_t cvt4(f32x4_t x) { return x; }
+__device__ __forceinline__ f32x4_t cvt4(u16x4_t u) {
+    return f32x4_t{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])};
+}
+
 // ------------------------------------------------------------------------------------------
 // Prepare. One workgroup per (b, h, chunk), in passes of 32 channels. LDS per pass: a, k,
 // q_hat, and the prefix F and suffix R inside each 16-token block (then inside each 4-token
@@ -490,10 +505,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
             }
     };
     // Staged through LDS: M, the per-token tiles (thread: token tid / 4, columns 4 (tid % 4)
-    // .. + 3) and gamma_C.
+    // .. + 3) and gamma_C. Every load is unconditional (rows past the sequence read the chunk's
+    // first row and are zeroed when stored), so the next chunk's loads stay in flight.
     struct Stage {
         f32x4_t m[C * C / 4 / kBwdThreads];
-        f32x4_t dO, e, w, v, pr;
+        typename Raw4<QT>::type dO, v;
+        f32x4_t e, w, pr;
         float gc;
     } st;
     auto load_stage = [&](int c) {
@@ -502,19 +519,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 #pragma unroll
         for (int j = 0; j < C * C / 4 / kBwdThreads; ++j) st.m[j] = M4[tid + kBwdThreads * j];
         const int t = tid >> 2, c4 = 4 * (tid & 3);
-        if (t < min(C, T - c * C)) {
-            const size_t o = tok_base(c) + size_t(t) * HD + c4;
-            st.dO = ld4(dout, o);
-            st.e = ld4(e, o);
-            st.w = ld4(w, o);
-            st.v = ld4(v, o);
-            st.pr = ld4(pred, o);
-        } else {
-            st.dO = st.e = st.w = st.v = st.pr = zero4();
-        }
-        st.gc = tid < D ? gC[sl * D + tid] : 0.f;
+        const int tc = t < T - c * C ? t : 0;
+        const size_t o = tok_base(c) + size_t(tc) * HD + c4;
+        st.dO = raw4(dout, o);
+        st.e = ld4(e, o);
+        st.w = ld4(w, o);
+        st.v = raw4(v, o);
+        st.pr = ld4(pred, o);
+        st.gc = gC[sl * D + (tid < D ? tid : 0)];
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](int c) {
+        const bool ok = (tid >> 2) < T - c * C;
 #pragma unroll
         for (int j = 0; j < C * C / 4 / kBwdThreads; ++j) {
             const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / C, s = e0 % C;
@@ -522,13 +537,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
             for (int q4 = 0; q4 < 4; ++q4) sM[t * LDM + s + q4] = st.m[j][q4];
         }
         const int t = tid >> 2, c4 = 4 * (tid & 3);
-        *reinterpret_cast<f32x4_t *>(&sdO[t * LDB + c4]) = st.dO;
+        const f32x4_t dO4 = ok ? cvt4(st.dO) : zero4(), v4 = ok ? cvt4(st.v) : zero4();
+        *reinterpret_cast<f32x4_t *>(&sdO[t * LDB + c4]) = dO4;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            sE[t * LDT + c4 + q4] = st.e[q4];
-            sW[t * LDT + c4 + q4] = st.w[q4];
-            sV[t * LDT + c4 + q4] = st.v[q4];
-            sPr[t * LDT + c4 + q4] = st.pr[q4];
+            sE[t * LDT + c4 + q4] = ok ? st.e[q4] : 0.f;
+            sW[t * LDT + c4 + q4] = ok ? st.w[q4] : 0.f;
+            sV[t * LDT + c4 + q4] = v4[q4];
+            sPr[t * LDT + c4 + q4] = ok ? st.pr[q4] : 0.f;
         }
         if (tid < D) sGC[tid] = st.gc;
     };
@@ -547,13 +563,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
         const size_t tok0 = tok_base(c);
         const size_t slot = slot_of(c);
         __syncthreads();
-        store_stage();
+        store_stage(c);
         for (int idx = tid; idx < D * VT; idx += kBwdThreads) {
             const int i = idx / VT, j = idx % VT;
             lamC[(slot * D + i) * D + j0 + j] = sLam[i * LDB + j];
         }
         __syncthreads();
-        if (c > 0) load_stage(c - 1);
+        load_stage(c > 0 ? c - 1 : 0);
         // Right-hand side of this wave's 16 tokens.
         {
             f32x4_t y = zero4();
@@ -570,7 +586,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sRhs[(16 * wave + 4 * kq + i) * LDT + r] = y[i];
         }
-        if (c > 0) load_rhsA(c - 1);
+        load_rhsA(c > 0 ? c - 1 : 0);
         __syncthreads();
         // Back substitution. With y = e * dU, dU_t = rhs_t - sum_{s > t} M_st y_s; lanes t >= s
         // read M_st = 0.
@@ -630,7 +646,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sLam[(i0 + 4 * kq + i) * LDB + r] = y[i];
         }
-        if (c > 0) load_lamA(c - 1);
+        load_lamA(c > 0 ? c - 1 : 0);
     }
     __syncthreads();
     if (ds0) {
@@ -643,16 +659,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Products. One workgroup per (b, h, chunk), four wavefronts, no LDS. Wave w keeps rows
-// 16 w .. 16 w + 15 of dO, dP = -e * dU and U in registers as matrix-core A operands and
-// streams 16-row tiles of S0, lambda_C and U past them (the next tile loads while the current
-// one is multiplied):
+// 16 w .. 16 w + 15 of U, then of dO and dP = -e * dU, in registers as matrix-core A operands
+// and streams 16-row tiles of lambda_C, U and S0 past them (the next tile loads while the
+// current one is multiplied):
 //   Y1 = dO S0^T, Y2 = dP S0^T, Y3 = U lambda_C^T    [C x D], stored [D/16][C][16] per chunk
 //   OU = dO U^T (s <= t), PU = dP U^T (s < t)         [C x C] per chunk, upper parts zero.
 // Y1 and Y2 are the state terms of dq_hat and of the read part of dk, Y3 that of the write
 // part of dk; OU and PU weight the decayed pair sums.
 // ------------------------------------------------------------------------------------------
 template <typename QT, int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_products_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_products_kernel(
     const QT *__restrict__ dout, const float *__restrict__ e, const float *__restrict__ U,
     const float *__restrict__ dU, const float *__restrict__ states, const float *__restrict__ lamC,
     float *__restrict__ Y1, float *__restrict__ Y2, float *__restrict__ Y3, float *__restrict__ OU,
@@ -671,17 +687,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float *lam = lamC + slot * D * D;
 
     // Contraction step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi: a lane's four
-    // values of one mo are one 16-byte load. Tokens past the sequence read as zero.
-    const int ta = 16 * wave + rr;
-    const bool tok_ok = ta < nval;
-    f32x4_t xo[NT], xp[NT], xu[NT];
+    // values of one mo are one 16-byte load. Token rows past the sequence load the chunk's first
+    // row (every load unconditional, so none waits on another). Only the dO and dP rows are
+    // zeroed there: that makes every O U^T, dP U^T, Y1 and Y2 entry of such a row zero, and the
+    // U rows past the sequence meet only rows whose results are not used.
+    auto load_tok = [&](const float *X, int t, f32x4_t (&x)[NT]) {
 #pragma unroll
-    for (int mo = 0; mo < NT; ++mo) {
-        const size_t o = tok0 + size_t(ta) * HD + 16 * mo + 4 * kq;
-        xo[mo] = tok_ok ? ld4(dout, o) : zero4();
-        xp[mo] = tok_ok ? -ld4(e, o) * ld4(dU, o) : zero4();
-        xu[mo] = tok_ok ? ld4(U, o) : zero4();
-    }
+        for (int mo = 0; mo < NT; ++mo) x[mo] = ld4(X, tok0 + size_t(t < nval ? t : 0) * HD + 16 * mo + 4 * kq);
+    };
+    auto zero_past = [&](int t, f32x4_t (&x)[NT]) {
+#pragma unroll
+        for (int mo = 0; mo < NT; ++mo) x[mo] = t < nval ? x[mo] : zero4();
+    };
     auto load_rows = [&](const float *S, int row, f32x4_t (&x)[NT]) {
 #pragma unroll
         for (int mo = 0; mo < NT; ++mo) x[mo] = ld4(S, size_t(row) * D + 16 * mo + 4 * kq);
@@ -692,58 +709,79 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[16 * i] = y[i];
     };
-    f32x4_t bS[2][NT], bL[2][NT];
-    load_rows(S0, rr, bS[0]);
-    load_rows(lam, rr, bL[0]);
+    const int ta = 16 * wave + rr;  // this lane's A row
+    // 1. Y3 = U lambda_C^T, the tiles of lambda_C streaming past the wave's U rows.
+    {
+        f32x4_t xu[NT], bL[2][NT];
+        load_tok(U, ta, xu);
+        load_rows(lam, rr, bL[0]);
 #pragma unroll
-    for (int it = 0; it < NT; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < NT) {
-            load_rows(S0, 16 * (it + 1) + rr, bS[cur ^ 1]);
-            load_rows(lam, 16 * (it + 1) + rr, bL[cur ^ 1]);
+        for (int it = 0; it < NT; ++it) {
+            const int cur = it & 1;
+            if (it + 1 < NT) load_rows(lam, 16 * (it + 1) + rr, bL[cur ^ 1]);
+            f32x4_t y3 = zero4();
+#pragma unroll
+            for (int mo = 0; mo < NT; ++mo)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bL[cur][mo][mi], y3, 0, 0, 0);
+            store_y(Y3, it, y3);
         }
-        f32x4_t y1 = zero4(), y2 = zero4(), y3 = zero4();
-#pragma unroll
-        for (int mo = 0; mo < NT; ++mo)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bS[cur][mo][mi], y1, 0, 0, 0);
-                y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bS[cur][mo][mi], y2, 0, 0, 0);
-                y3 = __builtin_amdgcn_mfma_f32_16x16x4f32(xu[mo][mi], bL[cur][mo][mi], y3, 0, 0, 0);
-            }
-        store_y(Y1, it, y1);
-        store_y(Y2, it, y2);
-        store_y(Y3, it, y3);
     }
-    // O U^T and dP U^T: the wave's row block against each column block bs <= w (U rows of
+    // 2. O U^T and dP U^T: the wave's row block against each column block bs <= w (U rows of
     // block bs, the next loading while the current is multiplied); blocks after w are zero.
-    const float *Ub = U + tok0;
-    auto load_u = [&](int bs, f32x4_t (&x)[NT]) {
-        const int s = 16 * bs + rr;
+    f32x4_t xo[NT], xp[NT];
+    {
+        f32x4_t bu[2][NT];
+        load_tok(U, rr, bu[0]);
 #pragma unroll
-        for (int mo = 0; mo < NT; ++mo) x[mo] = s < nval ? ld4(Ub, size_t(s) * HD + 16 * mo + 4 * kq) : zero4();
-    };
-    f32x4_t bu[2][NT];
-    load_u(0, bu[0]);
+        for (int mo = 0; mo < NT; ++mo) {
+            const size_t o = tok0 + size_t(ta < nval ? ta : 0) * HD + 16 * mo + 4 * kq;
+            xo[mo] = ld4(dout, o);
+            xp[mo] = -ld4(e, o) * ld4(dU, o);
+        }
+        zero_past(ta, xo);
+        zero_past(ta, xp);
 #pragma unroll
-    for (int bs = 0; bs < kNB; ++bs) {
-        const int cur = bs & 1;
-        f32x4_t yo = zero4(), yp = zero4();
-        if (bs <= wave) {
-            if (bs + 1 <= wave) load_u(bs + 1, bu[cur ^ 1]);
+        for (int bs = 0; bs < kNB; ++bs) {
+            const int cur = bs & 1;
+            f32x4_t yo = zero4(), yp = zero4();
+            if (bs <= wave) {
+                if (bs + 1 <= wave) load_tok(U, 16 * (bs + 1) + rr, bu[cur ^ 1]);
+#pragma unroll
+                for (int mo = 0; mo < NT; ++mo)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        yo = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bu[cur][mo][mi], yo, 0, 0, 0);
+                        yp = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bu[cur][mo][mi], yp, 0, 0, 0);
+                    }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * wave + 4 * kq + i, s = 16 * bs + rr;
+                OU[(slot * C + t) * C + s] = s <= t ? yo[i] : 0.f;
+                PU[(slot * C + t) * C + s] = s < t ? yp[i] : 0.f;
+            }
+        }
+    }
+    // 3. Y1 = dO S0^T and Y2 = dP S0^T, the tiles of S0 streaming past the wave's rows.
+    {
+        f32x4_t bS[2][NT];
+        load_rows(S0, rr, bS[0]);
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+            const int cur = it & 1;
+            if (it + 1 < NT) load_rows(S0, 16 * (it + 1) + rr, bS[cur ^ 1]);
+            f32x4_t y1 = zero4(), y2 = zero4();
 #pragma unroll
             for (int mo = 0; mo < NT; ++mo)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    yo = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bu[cur][mo][mi], yo, 0, 0, 0);
-                    yp = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bu[cur][mo][mi], yp, 0, 0, 0);
+                    y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[mo][mi], bS[cur][mo][mi], y1, 0, 0, 0);
+                    y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[mo][mi], bS[cur][mo][mi], y2, 0, 0, 0);
                 }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * wave + 4 * kq + i, s = 16 * bs + rr;
-            OU[(slot * C + t) * C + s] = s <= t ? yo[i] : 0.f;
-            PU[(slot * C + t) * C + s] = s < t ? yp[i] : 0.f;
+            store_y(Y1, it, y1);
+            store_y(Y2, it, y2);
         }
     }
 }
@@ -820,23 +858,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
     // A pass's operands from memory: the [C][16] slab of a, k, g, q, r (thread: token tid / 4,
     // channels 4 (tid % 4) .. + 3) and, for this lane's four rows 16 w + 4 kq + e4 and channel
-    // rr, the state terms and g, q.
+    // rr, the state terms and g, q. Every load is unconditional (rows past the sequence read the
+    // chunk's first row and are masked where used) and k, q stay in their stored precision until
+    // used, so the next pass's loads stay in flight while the current pass runs.
     struct PassIn {
-        f32x4_t a, k, g, q, r;
-        float y1[4], y2[4], y3[4], gg[4], gq[4];
+        f32x4_t a, g, r;
+        typename Raw4<QT>::type k, q;
+        float y1[4], y2[4], y3[4], gg[4];
+        QT gq[4];
     };
     auto load_pass = [&](int p0, PassIn &x) {
         const int t = tid >> 2, ii = 4 * (tid & 3);
-        const size_t o = tok0 + size_t(t) * HD + p0 + ii;
-        if (t < nval) {
-            x.a = ld4(a, o);
-            x.k = ld4(k, o);
-            x.g = ld4(g, o);
-            x.q = ld4(q, o);
-        } else {
-            x.a = f32x4_t{1.f, 1.f, 1.f, 1.f};
-            x.k = x.g = x.q = zero4();
-        }
+        const size_t o = tok0 + size_t(t < nval ? t : 0) * HD + p0 + ii;
+        x.a = ld4(a, o);
+        x.k = raw4(k, o);
+        x.g = ld4(g, o);
+        x.q = raw4(q, o);
         x.r = ld4(rh, p0 + ii);
         const size_t yo = ((slot * NT + p0 / 16) * C + 16 * wave + 4 * kq) * 16 + rr;
 #pragma unroll
@@ -845,10 +882,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             x.y2[e4] = Y2[yo + 16 * e4];
             x.y3[e4] = Y3[yo + 16 * e4];
             const int t2 = 16 * wave + 4 * kq + e4;
-            const size_t o2 = tok0 + size_t(t2) * HD + p0 + rr;
-            const bool ok = t2 < nval;
-            x.gg[e4] = ok ? g[o2] : 0.f;
-            x.gq[e4] = ok ? ld(q, o2) : 0.f;
+            const size_t o2 = tok0 + size_t(t2 < nval ? t2 : 0) * HD + p0 + rr;
+            x.gg[e4] = g[o2];
+            x.gq[e4] = q[o2];
         }
     };
     PassIn cur;
@@ -910,12 +946,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         __syncthreads();  // the previous pass is finished with the pass arrays
         {
             const int t = tid >> 2, ii = 4 * (tid & 3);
-            *reinterpret_cast<f32x4_t *>(&sA[t * LDH + ii]) = cur.a;
-            *reinterpret_cast<f32x4_t *>(&sK[t * LDH + ii]) = cur.k;
-            *reinterpret_cast<f32x4_t *>(&sQ[t * LDH + ii]) = cur.g * cur.q * cur.r;
+            const bool ok = t < nval;
+            *reinterpret_cast<f32x4_t *>(&sA[t * LDH + ii]) = ok ? cur.a : f32x4_t{1.f, 1.f, 1.f, 1.f};
+            *reinterpret_cast<f32x4_t *>(&sK[t * LDH + ii]) = ok ? cvt4(cur.k) : zero4();
+            *reinterpret_cast<f32x4_t *>(&sQ[t * LDH + ii]) = ok ? cur.g * cvt4(cur.q) * cur.r : zero4();
         }
+        // The next pass's operands (the last pass reloads its own, unused).
         PassIn nxt;
-        if (pp + 1 < DG / DH) load_pass(p0 + DH, nxt);
+        load_pass(pp + 1 < DG / DH ? p0 + DH : p0, nxt);
         __syncthreads();
         {
             // Pivots, thread (channel, 16-token block, role = wave): 0 the prefix F inside the
@@ -1050,7 +1088,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 sLa[t * LDO + ic] = fmaf(sQ[t * LDH + ic], dqh, sK[t * LDH + ic] * dkr);
                 if (t < nval) {
                     const size_t o = tok0 + size_t(t) * HD + ocol;
-                    const float gt = cur.gg[e4], qt = cur.gq[e4];
+                    const float gt = cur.gg[e4], qt = to_f32(cur.gq[e4]);
                     dq[o] = rh[ocol] * gt * dqh;
                     dg[o] = rh[ocol] * qt * dqh;
                     drl += gt * qt * dqh;
@@ -1149,7 +1187,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 }
             }
         }
-        if (pp + 1 < DG / DH) cur = nxt;
+        cur = nxt;
     }
     __syncthreads();
     for (int i = tid; i < DG; i += kBwdThreads) drp[slot * D + gc0 + i] = sDr[i];
