@@ -124,9 +124,9 @@ template <typename QT, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_prepare_kernel(
     const QT *__restrict__ q, const QT *__restrict__ k, const float *__restrict__ a,
     const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
-    const float *__restrict__ u, float *__restrict__ kb, float *__restrict__ kg,
-    float *__restrict__ qg, float *__restrict__ gC, float *__restrict__ Mw,
-    float *__restrict__ Pw, float *__restrict__ pred, int T, int H, int nchunks) {
+    const float *__restrict__ u, QT *__restrict__ kb, QT *__restrict__ kg,
+    QT *__restrict__ qg, float *__restrict__ gC, float *__restrict__ Mw,
+    QT *__restrict__ Pw, float *__restrict__ pred, int T, int H, int nchunks) {
     using L = PrepBwdLds<D>;
     constexpr int C = kC, LDM = L::LDM, DH = L::DH, LDH = L::LDH;
     constexpr int NJT = D / 64;  // value-column tiles of p per wavefront
@@ -253,13 +253,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 const float kt = sK[t * LDH + ii];
                 vkg[tl >> 2][tl & 3] = kt * gm;
                 vqg[tl >> 2][tl & 3] = sQ[t * LDH + ii] * gm;
-                kb[(slot * C + t) * D + i] = kt * sR[t * LDH + ii] * after;
+                elem<QT>::store(kb, (slot * C + t) * D + i, kt * sR[t * LDH + ii] * after);
             }
             const size_t row = (slot * D + i) * C + 16 * bb + 8 * half;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                *reinterpret_cast<f32x4_t *>(kg + row + 4 * h2) = vkg[h2];
-                *reinterpret_cast<f32x4_t *>(qg + row + 4 * h2) = vqg[h2];
+                store4(kg + row + 4 * h2, vkg[h2]);
+                store4(qg + row + 4 * h2, vqg[h2]);
             }
         }
         __syncthreads();
@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
         const int t = idx / C, s = idx % C;
         Mw[slot * C * C + idx] = s < t ? sM[t * LDM + s] : 0.f;
-        Pw[slot * C * C + idx] = t <= s ? sP[s * LDM + t] : 0.f;  // P transposed: row t holds P[., t]
+        // P transposed: row t holds P[., t].
+        elem<QT>::store(Pw, slot * C * C + idx, t <= s ? sP[s * LDM + t] : 0.f);
     }
     // p = (K*gamma) S0 + M U: the M U part, then the tokens of the chunk are stored.
     const float *Ub = u + (size_t(b) * T + c0) * HD + size_t(h) * D;
@@ -456,9 +457,9 @@ template <int D> struct ScanBwdLds {
 template <typename QT, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     const QT *__restrict__ dout, const QT *__restrict__ v, const float *__restrict__ e,
-    const float *__restrict__ w, const float *__restrict__ kb, const float *__restrict__ kg,
-    const float *__restrict__ qg, const float *__restrict__ gC, const float *__restrict__ Mw,
-    const float *__restrict__ Pw, const float *__restrict__ pred, const float *__restrict__ dsT,
+    const float *__restrict__ w, const QT *__restrict__ kb, const QT *__restrict__ kg,
+    const QT *__restrict__ qg, const float *__restrict__ gC, const float *__restrict__ Mw,
+    const QT *__restrict__ Pw, const float *__restrict__ pred, const float *__restrict__ dsT,
     float *__restrict__ dU, float *__restrict__ lamC, float *__restrict__ dv,
     float *__restrict__ dw, float *__restrict__ de, float *__restrict__ ds0, int T, int H, int BH,
     int nchunks) {
@@ -484,25 +485,56 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
     auto slot_of = [&](int c) { return size_t(bh) * nchunks + c; };
 
     // Matrix-core A operands: K*beta and P^T rows of this wave's tokens; Q_hat*gamma and
-    // K*gamma (channel-major) rows of this wave's channel tiles.
-    f32x4_t aKB[D / 16], aP[C / 16], aQG[NIT][C / 16], aKG[NIT][C / 16];
+    // K*gamma (channel-major) rows of this wave's channel tiles. fp32 operands take 16-byte
+    // pieces of four fp32 steps (k = 16 mo + 4 kq + mi); bf16 operands one bf16 step's
+    // fragment (k = 32 s + 8 kq + j).
+    using M16 = Mma<bf16_t>;
+    constexpr bool BF = std::is_same_v<QT, bf16_t>;
+    constexpr int KD = BF ? D / 32 : D / 16, KC = BF ? C / 32 : C / 16;
+    using AF = std::conditional_t<BF, M16::frag, f32x4_t>;
+    AF aKB[KD], aP[KC], aQG[NIT][KC], aKG[NIT][KC];
+    auto ldA = [&](const QT *p, size_t o) {
+        if constexpr (BF) return M16::load(p + o);
+        else return ld4(p, o);
+    };
+    constexpr int KW = BF ? 32 : 16, KL = BF ? 8 : 4;  // k of step m, lane group kq: KW m + KL kq
     auto load_rhsA = [&](int c) {
         const size_t sl = slot_of(c);
 #pragma unroll
-        for (int mo = 0; mo < D / 16; ++mo) aKB[mo] = ld4(kb, (sl * C + 16 * wave + r) * D + 16 * mo + 4 * kq);
+        for (int m = 0; m < KD; ++m) aKB[m] = ldA(kb, (sl * C + 16 * wave + r) * D + KW * m + KL * kq);
 #pragma unroll
-        for (int mo = 0; mo < C / 16; ++mo) aP[mo] = ld4(Pw, (sl * C + 16 * wave + r) * C + 16 * mo + 4 * kq);
+        for (int m = 0; m < KC; ++m) aP[m] = ldA(Pw, (sl * C + 16 * wave + r) * C + KW * m + KL * kq);
     };
     auto load_lamA = [&](int c) {
         const size_t sl = slot_of(c);
 #pragma unroll
         for (int n = 0; n < NIT; ++n)
 #pragma unroll
-            for (int mo = 0; mo < C / 16; ++mo) {
-                const size_t o = (sl * D + 16 * (wave + 4 * n) + r) * C + 16 * mo + 4 * kq;
-                aQG[n][mo] = ld4(qg, o);
-                aKG[n][mo] = ld4(kg, o);
+            for (int m = 0; m < KC; ++m) {
+                const size_t o = (sl * D + 16 * (wave + 4 * n) + r) * C + KW * m + KL * kq;
+                aQG[n][m] = ldA(qg, o);
+                aKG[n][m] = ldA(kg, o);
             }
+    };
+    // B fragment of a bf16 step: rows 32 m + 8 kq .. + 7 of an fp32 LDS array, column r;
+    // ldsB2 also gives the rounding remainder as a second fragment (hi + lo carries the fp32
+    // value to about 2^-17), for the operands that carry the adjoint along the sequence.
+    auto ldsB = [&](const float *X, int m, int ld) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = X[(32 * m + 8 * kq + j) * ld + r];
+        return M16::pack(x);
+    };
+    auto ldsB2 = [&](const float *X, int m, int ld, M16::frag &lo) {
+        float x[8], rem[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = X[(32 * m + 8 * kq + j) * ld + r];
+        const M16::frag hi = M16::pack(x);
+        const u16x8_t hb = __builtin_bit_cast(u16x8_t, hi);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rem[j] = x[j] - bf16_to_f32(hb[j]);
+        lo = M16::pack(rem);
+        return hi;
     };
     // Staged through LDS: M, the per-token tiles (thread: token tid / 4, columns 4 (tid % 4)
     // .. + 3) and gamma_C. Every load is unconditional (rows past the sequence read the chunk's
@@ -573,16 +605,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
         // Right-hand side of this wave's 16 tokens.
         {
             f32x4_t y = zero4();
+            if constexpr (BF) {
 #pragma unroll
-            for (int mo = 0; mo < D / 16; ++mo)
+                for (int m = 0; m < KD; ++m) {
+                    M16::frag lo;
+                    const M16::frag hi = ldsB2(sLam, m, LDB, lo);
+                    y = M16::mma(aKB[m], hi, y);
+                    y = M16::mma(aKB[m], lo, y);
+                }
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKB[mo][mi], sLam[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
+                for (int m = 0; m < KC; ++m) y = M16::mma(aP[m], ldsB(sdO, m, LDB), y);
+            } else {
 #pragma unroll
-            for (int mo = 0; mo < C / 16; ++mo)
+                for (int mo = 0; mo < D / 16; ++mo)
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[mo][mi], sdO[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
+                    for (int mi = 0; mi < 4; ++mi)
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKB[mo][mi], sLam[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
+#pragma unroll
+                for (int mo = 0; mo < C / 16; ++mo)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi)
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[mo][mi], sdO[(16 * mo + 4 * kq + mi) * LDB + r], y, 0, 0, 0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) sRhs[(16 * wave + 4 * kq + i) * LDT + r] = y[i];
         }
@@ -635,14 +679,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
                 const int ii = i0 + 4 * kq + i;
                 y[i] = sGC[ii] * sLam[ii * LDB + r];
             }
+            if constexpr (BF) {
 #pragma unroll
-            for (int mo = 0; mo < C / 16; ++mo)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    const int tt = 16 * mo + 4 * kq + mi;
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aQG[n][mo][mi], sdO[tt * LDB + r], y, 0, 0, 0);
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKG[n][mo][mi], sdP[tt * LDB + r], y, 0, 0, 0);
+                for (int m = 0; m < KC; ++m) {
+                    M16::frag lo;
+                    const M16::frag hi = ldsB2(sdP, m, LDB, lo);
+                    y = M16::mma(aQG[n][m], ldsB(sdO, m, LDB), y);
+                    y = M16::mma(aKG[n][m], hi, y);
+                    y = M16::mma(aKG[n][m], lo, y);
                 }
+            } else {
+#pragma unroll
+                for (int mo = 0; mo < C / 16; ++mo)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        const int tt = 16 * mo + 4 * kq + mi;
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aQG[n][mo][mi], sdO[tt * LDB + r], y, 0, 0, 0);
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aKG[n][mo][mi], sdP[tt * LDB + r], y, 0, 0, 0);
+                    }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) sLam[(i0 + 4 * kq + i) * LDB + r] = y[i];
         }
@@ -1225,9 +1280,12 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     const int BH = B * H;
     float *u = reinterpret_cast<float *>(ws + L.u);
     float *states = reinterpret_cast<float *>(ws + L.states);
-    float *kb = reinterpret_cast<float *>(ws + L.kb), *kg = reinterpret_cast<float *>(ws + L.kg);
-    float *qg = reinterpret_cast<float *>(ws + L.qg), *gC = reinterpret_cast<float *>(ws + L.gC);
-    float *Mw = reinterpret_cast<float *>(ws + L.M), *Pw = reinterpret_cast<float *>(ws + L.P);
+    // The scan's operands K*beta, K*gamma, Q_hat*gamma and P^T are stored in the operand
+    // precision (bf16 on the bf16 path); their regions are sized for fp32 because the products
+    // kernel reuses them afterwards.
+    QT *kb = reinterpret_cast<QT *>(ws + L.kb), *kg = reinterpret_cast<QT *>(ws + L.kg);
+    QT *qg = reinterpret_cast<QT *>(ws + L.qg), *Pw = reinterpret_cast<QT *>(ws + L.P);
+    float *gC = reinterpret_cast<float *>(ws + L.gC), *Mw = reinterpret_cast<float *>(ws + L.M);
     float *pred = reinterpret_cast<float *>(ws + L.pred), *dUw = reinterpret_cast<float *>(ws + L.dU);
     float *lamC = reinterpret_cast<float *>(ws + L.lamC);
     float *drp = reinterpret_cast<float *>(ws + L.drp);
@@ -1265,7 +1323,8 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     if (nchunks > 0) {
         // The products go where the scan's operands were (K*beta, K*gamma, Q_hat*gamma, M and P
         // are not read again): Y1, Y2, Y3 over kb, kg, qg, and OU, PU over M, P.
-        float *Y1 = kb, *Y2 = kg, *Y3 = qg, *OU = Mw, *PU = Pw;
+        float *Y1 = reinterpret_cast<float *>(ws + L.kb), *Y2 = reinterpret_cast<float *>(ws + L.kg);
+        float *Y3 = reinterpret_cast<float *>(ws + L.qg), *OU = Mw, *PU = reinterpret_cast<float *>(ws + L.P);
         hipLaunchKernelGGL((bwd_products_kernel<QT, D>), dim3(nchunks, H, B), dim3(kBwdThreads), 0, stream, dout,
                            x.e, u, dUw, states, lamC, Y1, Y2, Y3, OU, PU, T, H, nchunks);
         err = hipGetLastError();

@@ -3,11 +3,14 @@ itself pinned against autograd, finite differences and closed forms on the CPU).
 
 Bar: per-head max relative error (max |x - ref| / max |ref| over the head's slice) of every
 gradient <= 1e-5 for fp32 q/k/v and <= 2e-2 for bf16, with every value finite. Why these
-bounds: the backward's own arithmetic is fp32 throughout (about 1e-6 measured), but it starts
-from the forward's u, which the bf16 path forms with bf16 matrix-core operands (relative
-error about 2^-8 per operand; the forward's own bar is 2e-2). The gradients are sums of
-products of u with fp32 terms and inherit that error; measured, at most 5.3e-3 (the
-log-decay gradient, a cumulative sum).
+bounds: on the fp32 path the backward's arithmetic is fp32 throughout (about 1e-6 measured).
+The bf16 path starts from the forward's u, formed with bf16 matrix-core operands (relative
+error about 2^-8 per operand; the forward's own bar is 2e-2), and its reverse scan multiplies
+K*beta, P, Q_hat*gamma and K*gamma as bf16 operands (the adjoint and dP as exact hi + lo
+pairs). Measured, the largest error is 1.4e-2, the log-decay gradient of the long-context
+shape (a cumulative sum over the sequence); it is the same with fp32 scan operands, so it
+comes from u. The scan's bf16 operands bring dv, dw, de and ds0 from about 1e-6 to at most
+5e-3.
 Calls go through the C ABI via the Python binding.
 """
 import numpy as np
