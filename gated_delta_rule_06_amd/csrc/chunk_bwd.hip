@@ -1291,11 +1291,13 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     float *drp = reinterpret_cast<float *>(ws + L.drp);
     const bool bf16 = std::is_same_v<QT, bf16_t>;
     hipError_t err;
+    // The forward rerun, at its own chunk size, keeping u and the state every 64 tokens.
+    const int cf = bwd_fwd_chunk(B, T, H, D);
     if (T > 0) {
-        err = launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, kC, bf16, ws + L.fwd, stream);
+        err = launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, cf, bf16, ws + L.fwd, stream);
         if (err != hipSuccess) return err;
     }
-    err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, ws + L.o, nullptr, u, states, B, T, H, D, kC, bf16,
+    err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, ws + L.o, nullptr, u, states, B, T, H, D, cf, bf16,
                                  ws + L.fwd, stream);
     if (err != hipSuccess) return err;
     const QT *q = static_cast<const QT *>(x.q), *k = static_cast<const QT *>(x.k);

@@ -885,8 +885,8 @@ struct ScanGates {
 };
 constexpr int kZOffErase = 64, kZOffOutput = 128, kZOffWrite = 256;
 // What the forward keeps for the backward pass (SAVE): u = b - e * p of every token in fp32,
-// [B, T, H, D] like v, and the state at every chunk start and at the end, fp32
-// [B * H][nchunks + 1][D][D].
+// [B, T, H, D] like v, and the state at the start of every 64-token block and at the end,
+// fp32 [B * H][ceil(T / 64) + 1][D][D], whatever the forward's own chunk size.
 struct ScanSave {
     float *u;
     float *states;
@@ -950,8 +950,10 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
 
-    // SAVE: the state at every chunk start and at the end, [BH][nchunks + 1][D][D].
-    float *svst = SAVE ? sv.states + size_t(bh) * (nchunks + 1) * D * D + j0 : nullptr;
+    // SAVE: the state at every 64-token block start and at the end, [BH][n64 + 1][D][D].
+    static_assert(!SAVE || C % 64 == 0, "saved states are 64 tokens apart");
+    const int n64 = (T + 63) / 64;
+    float *svst = SAVE ? sv.states + size_t(bh) * (n64 + 1) * D * D + j0 : nullptr;
     if (nchunks == 0) {
         if (wave == 0 && col_ok) {
 #pragma unroll
@@ -1296,7 +1298,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                 fS[c] = F::pack(S[c]);
                 sh_fS[buf][c][lane] = fS[c];
             }
-            if constexpr (SAVE) save_state(ci);
+            if constexpr (SAVE) save_state(ci * (C / 64));
             f32x4_t acc = zero4();  // right-hand-side accumulator of the current leaf
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) acc = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgH[kk], acc);
@@ -1387,6 +1389,15 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                         S[c + off] = F::mma8(cw.kbt[c], u2, S[c + off] * lds_pp(ci, p0 / 2, c + off));
                     }
                 }
+                // SAVE inside a chunk: after this update of leaf 4 q + 1 every tile has taken
+                // the leaf pairs of tokens 0 .. 64 q - 1 and no later one (the lower tiles take
+                // pair 2 q at leaf 4 q + 2), so S is the state at the chunk's 64 q-th token. A
+                // boundary past the sequence goes to the final state's slot, which the final
+                // state overwrites.
+                if constexpr (SAVE && L % 4 == 1 && L >= 5) {
+                    constexpr int q = (L - 1) / 4;
+                    save_state(ci * C + 64 * q < T ? ci * (C / 64) + q : n64);
+                }
                 if constexpr (!more) {
 #pragma unroll
                     for (int c = 0; c < NCT; ++c) kbtLast[c] = load_kbt(ci, NB / 2 - 1, c);
@@ -1420,7 +1431,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) south[size_t(16 * c + i) * D + lo_st] = S[c][i];
     }
-    if constexpr (SAVE) save_state(nchunks);
+    if constexpr (SAVE) save_state(n64);
 }
 
 template <typename QT, typename OpT, int D, int C>
@@ -1581,7 +1592,8 @@ hipError_t launch_chunk_scan_save(const void *v, const float *e, const float *w,
                                                     stream)                                       \
                     : scan_save_typed<float, D, C>(v, e, w, s0, o, s_out, sv, B, T, H, workspace,  \
                                                    stream);
-    MUIR_SCAN_SV(64, 64) MUIR_SCAN_SV(128, 64)
+    MUIR_SCAN_SV(64, 64) MUIR_SCAN_SV(64, 128) MUIR_SCAN_SV(64, 256)
+    MUIR_SCAN_SV(128, 64) MUIR_SCAN_SV(128, 128) MUIR_SCAN_SV(128, 256)
 #undef MUIR_SCAN_SV
     return hipErrorInvalidValue;
 }

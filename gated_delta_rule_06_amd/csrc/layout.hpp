@@ -74,5 +74,8 @@ struct BwdLayout {
 // Offsets of the backward workspace for these sizes; false when the forward's workspace size
 // is invalid.
 bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L);
+// Chunk size of the forward that the backward pass reruns (it saves the state every 64
+// tokens whatever its own chunk size).
+int bwd_fwd_chunk(int B, int T, int H, int d);
 
 }  // namespace muir

@@ -51,9 +51,11 @@ size_t wy_workspace_bytes(int B, int T, int H, int d, int chunk) {
     return n * per;
 }
 
+int bwd_fwd_chunk(int, int T, int, int) { return T >= 256 ? 128 : kBwdChunk; }
+
 bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
     constexpr int kC = kBwdChunk;
-    const size_t fwd = chunk_workspace_bytes(B, T, H, d, kC, bf16);
+    const size_t fwd = chunk_workspace_bytes(B, T, H, d, bwd_fwd_chunk(B, T, H, d), bf16);
     if (fwd == 0 && T > 0) return false;
     const size_t nc = (size_t(T) + kC - 1) / kC;
     const size_t BH = size_t(B) * H, tok = size_t(B) * T * H * d;
