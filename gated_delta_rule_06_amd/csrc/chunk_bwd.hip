@@ -722,6 +722,145 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 // Y1 and Y2 are the state terms of dq_hat and of the read part of dk, Y3 that of the write
 // part of dk; OU and PU weight the decayed pair sums.
 // ------------------------------------------------------------------------------------------
+// Products of fp32 operands on the bf16 matrix cores (bf16 path): each fp32 value is carried as
+// a bf16 pair hi + lo (hi the nearest bf16, lo the nearest bf16 to the remainder, which is exact
+// in fp32), and a product takes hi*hi + hi*lo + lo*hi, leaving out only lo*lo (relative size
+// about 2^-16). Per K = 32 step that is three v_mfma_f32_16x16x32_bf16 (16 cycles each) in place
+// of eight v_mfma_f32_16x16x4_f32 (32 cycles each). A bf16 input (dO) needs only its hi part.
+struct Split {
+    Mma<bf16_t>::frag hi, lo;
+};
+__device__ __forceinline__ Split split8(f32x4_t a, f32x4_t b) {
+    using M16 = Mma<bf16_t>;
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    Split sp;
+    sp.hi = M16::pack(x);
+    const u16x8_t hb = __builtin_bit_cast(u16x8_t, sp.hi);
+    float rem[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rem[j] = x[j] - bf16_to_f32(hb[j]);
+    sp.lo = M16::pack(rem);
+    return sp;
+}
+__device__ __forceinline__ f32x4_t mma3(const Split &a, const Split &b, f32x4_t y) {
+    using M16 = Mma<bf16_t>;
+    y = M16::mma(a.hi, b.hi, y);
+    y = M16::mma(a.hi, b.lo, y);
+    return M16::mma(a.lo, b.hi, y);
+}
+__device__ __forceinline__ f32x4_t mma2(Mma<bf16_t>::frag a, const Split &b, f32x4_t y) {
+    y = Mma<bf16_t>::mma(a, b.hi, y);
+    return Mma<bf16_t>::mma(a, b.lo, y);
+}
+
+// The products kernel's body on the bf16 path: the same three phases and outputs, contraction
+// step s of lane group kq taking k = 32 s + 8 kq .. + 7 (two 16-byte loads per fp32 operand).
+template <int D>
+__device__ __forceinline__ void products_split(const bf16_t *__restrict__ dout, const float *__restrict__ e,
+                                               const float *__restrict__ U, const float *__restrict__ dU,
+                                               const float *__restrict__ S0, const float *__restrict__ lam,
+                                               float *__restrict__ Y1, float *__restrict__ Y2,
+                                               float *__restrict__ Y3, float *__restrict__ OU,
+                                               float *__restrict__ PU, size_t tok0, size_t HD, size_t slot,
+                                               int nval, int wave, int rr, int kq) {
+    using M16 = Mma<bf16_t>;
+    constexpr int C = kC, NT = D / 16, NS = D / 32;
+    const int ta = 16 * wave + rr;  // this lane's A row
+    const bool ok = ta < nval;
+    auto tokrow = [&](int t) { return tok0 + size_t(t < nval ? t : 0) * HD; };
+    using Raw = f32x4_t[NS][2];
+    auto ld8 = [&](const float *X, size_t row0, Raw &x) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            x[st][0] = ld4(X, row0 + 32 * st + 8 * kq);
+            x[st][1] = ld4(X, row0 + 32 * st + 8 * kq + 4);
+        }
+    };
+    auto store_y = [&](float *Y, int it, f32x4_t y) {
+        float *dst = Y + ((slot * NT + it) * C + 16 * wave + 4 * kq) * 16 + rr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * i] = y[i];
+    };
+    // 1. Y3 = U lambda_C^T.
+    {
+        Raw ru, bl[2];
+        ld8(U, tokrow(ta), ru);
+        ld8(lam, size_t(rr) * D, bl[0]);
+        Split xu[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) xu[st] = split8(ru[st][0], ru[st][1]);
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+            const int cur = it & 1;
+            if (it + 1 < NT) ld8(lam, size_t(16 * (it + 1) + rr) * D, bl[cur ^ 1]);
+            f32x4_t y3 = zero4();
+#pragma unroll
+            for (int st = 0; st < NS; ++st) y3 = mma3(xu[st], split8(bl[cur][st][0], bl[cur][st][1]), y3);
+            store_y(Y3, it, y3);
+        }
+    }
+    // The wave's rows of dO (exact in bf16) and dP = -e * dU (split), zero past the sequence.
+    M16::frag xo[NS];
+    Split xp[NS];
+    Raw bu[2];
+    ld8(U, tokrow(rr), bu[0]);
+    {
+        Raw re, rd;
+        ld8(e, tokrow(ta), re);
+        ld8(dU, tokrow(ta), rd);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) xo[st] = M16::load(dout + tokrow(ta) + 32 * st + 8 * kq);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            xp[st] = split8(-re[st][0] * rd[st][0], -re[st][1] * rd[st][1]);
+            if (!ok) {
+                xo[st] = M16::zero();
+                xp[st].hi = xp[st].lo = M16::zero();
+            }
+        }
+    }
+    // 2. O U^T and dP U^T against the column blocks bs <= w; blocks after w are zero.
+#pragma unroll
+    for (int bs = 0; bs < kNB; ++bs) {
+        const int cur = bs & 1;
+        f32x4_t yo = zero4(), yp = zero4();
+        if (bs <= wave) {
+            if (bs + 1 <= wave) ld8(U, tokrow(16 * (bs + 1) + rr), bu[cur ^ 1]);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const Split b = split8(bu[cur][st][0], bu[cur][st][1]);
+                yo = mma2(xo[st], b, yo);
+                yp = mma3(xp[st], b, yp);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * wave + 4 * kq + i, sc = 16 * bs + rr;
+            OU[(slot * C + t) * C + sc] = sc <= t ? yo[i] : 0.f;
+            PU[(slot * C + t) * C + sc] = sc < t ? yp[i] : 0.f;
+        }
+    }
+    // 3. Y1 = dO S0^T and Y2 = dP S0^T.
+    {
+        Raw bS[2];
+        ld8(S0, size_t(rr) * D, bS[0]);
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+            const int cur = it & 1;
+            if (it + 1 < NT) ld8(S0, size_t(16 * (it + 1) + rr) * D, bS[cur ^ 1]);
+            f32x4_t y1 = zero4(), y2 = zero4();
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const Split b = split8(bS[cur][st][0], bS[cur][st][1]);
+                y1 = mma2(xo[st], b, y1);
+                y2 = mma3(xp[st], b, y2);
+            }
+            store_y(Y1, it, y1);
+            store_y(Y2, it, y2);
+        }
+    }
+}
+
 template <typename QT, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_products_kernel(
     const QT *__restrict__ dout, const float *__restrict__ e, const float *__restrict__ U,
@@ -740,6 +879,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const size_t slot = size_t(bh) * nchunks + c;
     const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
     const float *lam = lamC + slot * D * D;
+    if constexpr (std::is_same_v<QT, bf16_t>) {
+        products_split<D>(dout, e, U, dU, S0, lam, Y1, Y2, Y3, OU, PU, tok0, HD, slot, nval, wave, lane & 15,
+                          lane >> 4);
+        return;
+    }
 
     // Contraction step (mo, mi) of lane group kq takes k = 16 mo + 4 kq + mi: a lane's four
     // values of one mo are one 16-byte load. Token rows past the sequence load the chunk's first
