@@ -95,6 +95,41 @@ __device__ __forceinline__ f32x4_t cvt4(u16x4_t u) {
     return f32x4_t{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])};
 }
 
+// Products of fp32 operands on the bf16 matrix cores (bf16 path): each fp32 value is carried as
+// a bf16 pair hi + lo (hi the nearest bf16, lo the nearest bf16 to the remainder, which is exact
+// in fp32), and a product takes hi*hi + hi*lo + lo*hi, leaving out only lo*lo (relative size
+// about 2^-16). Per K = 32 step that is three v_mfma_f32_16x16x32_bf16 (16 cycles each) in place
+// of eight v_mfma_f32_16x16x4_f32 (32 cycles each). A bf16 input (dO) needs only its hi part.
+struct Split {
+    Mma<bf16_t>::frag hi, lo;
+};
+__device__ __forceinline__ Split split8(f32x4_t a, f32x4_t b) {
+    using M16 = Mma<bf16_t>;
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    Split sp;
+    sp.hi = M16::pack(x);
+    const u16x8_t hb = __builtin_bit_cast(u16x8_t, sp.hi);
+    float rem[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rem[j] = x[j] - bf16_to_f32(hb[j]);
+    sp.lo = M16::pack(rem);
+    return sp;
+}
+__device__ __forceinline__ Split split8(const float (&x)[8]) {
+    return split8(f32x4_t{x[0], x[1], x[2], x[3]}, f32x4_t{x[4], x[5], x[6], x[7]});
+}
+__device__ __forceinline__ f32x4_t mma3(const Split &a, const Split &b, f32x4_t y) {
+    using M16 = Mma<bf16_t>;
+    y = M16::mma(a.hi, b.hi, y);
+    y = M16::mma(a.hi, b.lo, y);
+    return M16::mma(a.lo, b.hi, y);
+}
+__device__ __forceinline__ f32x4_t mma2(Mma<bf16_t>::frag a, const Split &b, f32x4_t y) {
+    y = Mma<bf16_t>::mma(a, b.hi, y);
+    return Mma<bf16_t>::mma(a, b.lo, y);
+}
+
+
 // ------------------------------------------------------------------------------------------
 // Prepare. One workgroup per (b, h, chunk), in passes of 32 channels. LDS per pass: a, k,
 // q_hat, and the prefix F and suffix R inside each 16-token block (then inside each 4-token
@@ -121,7 +156,7 @@ template <int D> struct PrepBwdLds {
 };
 
 template <typename QT, int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_prepare_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(std::is_same_v<QT, bf16_t> ? 2 : 3))) void bwd_prepare_kernel(
     const QT *__restrict__ q, const QT *__restrict__ k, const float *__restrict__ a,
     const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
     const float *__restrict__ u, QT *__restrict__ kb, QT *__restrict__ kg,
@@ -130,6 +165,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     using L = PrepBwdLds<D>;
     constexpr int C = kC, LDM = L::LDM, DH = L::DH, LDH = L::LDH;
     constexpr int NJT = D / 64;  // value-column tiles of p per wavefront
+    // The bf16 path multiplies on the bf16 matrix cores with split fp32 operands: one K = 32
+    // step per pass, lane group kq taking channels 8 kq .. + 7. The fp32 path takes eight K = 4
+    // steps, lane group kq taking channel 4 m + kq of step m.
+    constexpr bool BF = std::is_same_v<QT, bf16_t>;
+    static_assert(DH == 32, "one bf16 step per pass");
     static_assert(kBwdThreads == 8 * DH && kNB == 4, "thread roles assume 256 threads, 4 blocks");
     extern __shared__ float lds[];
     float *sA = lds, *sK = sA + L::TILE, *sQ = sK + L::TILE, *sF = sQ + L::TILE, *sR = sF + L::TILE;
@@ -169,7 +209,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         for (int jj = 0; jj < NJT; ++jj)
 #pragma unroll
             for (int m = 0; m < DH / 4; ++m)
-                bS[jj][m] = S0[size_t(p0 + 4 * m + kq) * D + 16 * (wave + 4 * jj) + cc];
+                bS[jj][m] = S0[size_t(p0 + (BF ? 8 * kq + m : 4 * m + kq)) * D + 16 * (wave + 4 * jj) + cc];
         __syncthreads();
         {
             // All of the pass's loads are issued before the first LDS store.
@@ -270,6 +310,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
             const int bt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
             const int bs = pr - bt * (bt - 1) / 2;
             const float *sX = mat == 0 ? sK : sQ;
+            if constexpr (BF) {
+                float av[8], bv[8];
+#pragma unroll
+                for (int j8 = 0; j8 < 8; ++j8) {
+                    const int kk = 8 * kq + j8;
+                    av[j8] = sX[(16 * bt + cc) * LDH + kk] * sF[(16 * bt + cc) * LDH + kk];
+                    bv[j8] = sK[(16 * bs + cc) * LDH + kk] * sR[(16 * bs + cc) * LDH + kk] * sMid[pr * DH + kk];
+                }
+                acc[j] = mma3(split8(av), split8(bv), acc[j]);
+                continue;
+            }
             acc[j] = mm16<DH>(
                 [&](int rr, int kk) { return sX[(16 * bt + rr) * LDH + kk] * sF[(16 * bt + rr) * LDH + kk]; },
                 [&](int cc2, int kk) {
@@ -278,8 +329,26 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 acc[j]);
         }
         // (K*gamma) S0 over this pass's channels; the A operand is K*gamma as stored above.
+        if constexpr (BF) {
+            Split sS[NJT];
 #pragma unroll
-        for (int tt = 0; tt < kNB; ++tt) {
+            for (int jj = 0; jj < NJT; ++jj) sS[jj] = split8(bS[jj]);
+#pragma unroll
+            for (int tt = 0; tt < kNB; ++tt) {
+                const int t = 16 * tt + cc;
+                float kv[8];
+#pragma unroll
+                for (int j8 = 0; j8 < 8; ++j8) {
+                    const int kk = 8 * kq + j8;
+                    kv[j8] = sK[t * LDH + kk] * (sBef[tt * DH + kk] * sF[t * LDH + kk]);
+                }
+                const Split ks = split8(kv);
+#pragma unroll
+                for (int jj = 0; jj < NJT; ++jj) pacc[jj][tt] = mma3(ks, sS[jj], pacc[jj][tt]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < (BF ? 0 : kNB); ++tt) {
 #pragma unroll
             for (int m = 0; m < DH / 4; ++m) {
                 const int t = 16 * tt + cc, kk = 4 * m + kq;
@@ -330,8 +399,76 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 if (j < 5) ym[j] = zero4();
                 yp[j] = zero4();
             }
+            if constexpr (BF) {
+                // One K = 32 step: the same factors for channels 8 kq .. + 7, split.
+                float kt[8], qt[8], v1[8], v2[8], v3[8];
+#pragma unroll
+                for (int j8 = 0; j8 < 8; ++j8) {
+                    const int kk = 8 * kq + j8;
+                    kt[j8] = sK[ta * LDH + kk];
+                    qt[j8] = sQ[ta * LDH + kk];
+                }
+                {
+                    // Gaps 1-3: A = X * F4, B = K * R4 times the whole sub-blocks between.
+                    float fa[8];
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        const int kk = 8 * kq + j8;
+                        fa[j8] = sF[ta * LDH + kk];
+                        v1[j8] = kt[j8] * sR[ta * LDH + kk];
+                        const float m1 = us + 1 < 4 ? sB4[(u0 + 1) * DH + kk] : 0.f;
+                        const float m2 = us + 2 < 4 ? sB4[(u0 + 2) * DH + kk] : 0.f;
+                        v2[j8] = v1[j8] * m1;
+                        v3[j8] = v2[j8] * m2;
+                    }
+                    const Split b1 = split8(v1), b2 = split8(v2), b3 = split8(v3);
+                    float am[8], ap[8];
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        am[j8] = kt[j8] * fa[j8];
+                        ap[j8] = qt[j8] * fa[j8];
+                    }
+                    const Split sm = split8(am), sp = split8(ap);
+                    ym[0] = mma3(sm, b1, ym[0]);
+                    ym[1] = mma3(sm, b2, ym[1]);
+                    ym[2] = mma3(sm, b3, ym[2]);
+                    yp[0] = mma3(sp, b1, yp[0]);
+                    yp[1] = mma3(sp, b2, yp[1]);
+                    yp[2] = mma3(sp, b3, yp[2]);
+                }
+                {
+                    // Inside one sub-block: the half split, adjacent tokens, the diagonal.
+                    float af[8], bf[8], at[8];
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        const int kk = 8 * kq + j8;
+                        const float a0 = sA[ta * LDH + kk];
+                        const float aprev = sA[(sub > 0 ? ta - 1 : ta) * LDH + kk];
+                        const float anext = sA[(sub < 3 ? ta + 1 : ta) * LDH + kk];
+                        af[j8] = sub == 2 ? a0 : (sub == 3 ? aprev * a0 : 0.f);
+                        bf[j8] = kt[j8] * (sub == 0 ? anext : (sub == 1 ? 1.f : 0.f));
+                        at[j8] = a0;
+                    }
+                    const Split bh = split8(bf), sk = split8(kt);
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        v1[j8] = kt[j8] * af[j8];
+                        v2[j8] = qt[j8] * af[j8];
+                    }
+                    ym[3] = mma3(split8(v1), bh, ym[3]);
+                    yp[3] = mma3(split8(v2), bh, yp[3]);
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        v1[j8] = kt[j8] * at[j8];
+                        v2[j8] = qt[j8] * at[j8];
+                    }
+                    ym[4] = mma3(split8(v1), sk, ym[4]);
+                    yp[4] = mma3(split8(v2), sk, yp[4]);
+                    yp[5] = mma3(split8(qt), sk, yp[5]);
+                }
+            }
 #pragma unroll 2
-            for (int m = 0; m < DH / 4; ++m) {
+            for (int m = 0; m < (BF ? 0 : DH / 4); ++m) {
                 const int kk = 4 * m + kq;
                 const float kt = sK[ta * LDH + kk], qt = sQ[ta * LDH + kk];
                 const float at = sA[ta * LDH + kk];
@@ -411,10 +548,44 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int jj = 0; jj < NJT; ++jj) {
         const int jt = wave + 4 * jj;
+        // B operands: token s of step m is 4 m + kq (fp32 path) or, for the two K = 32 steps
+        // st of the bf16 path, 32 st + 8 kq + j.
         float bU[C / 4];
 #pragma unroll
-        for (int m = 0; m < C / 4; ++m)
-            bU[m] = 4 * m + kq < nval ? Ub[size_t(4 * m + kq) * HD + 16 * jt + cc] : 0.f;
+        for (int m = 0; m < C / 4; ++m) {
+            const int sb = BF ? 32 * (m / 8) + 8 * kq + m % 8 : 4 * m + kq;
+            bU[m] = sb < nval ? Ub[size_t(sb) * HD + 16 * jt + cc] : 0.f;
+        }
+        if constexpr (BF) {
+            Split sU[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                float x8[8];
+#pragma unroll
+                for (int j8 = 0; j8 < 8; ++j8) x8[j8] = bU[8 * st + j8];
+                sU[st] = split8(x8);
+            }
+#pragma unroll
+            for (int tt = 0; tt < kNB; ++tt) {
+                const int t = 16 * tt + cc;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    float mv[8];
+#pragma unroll
+                    for (int j8 = 0; j8 < 8; ++j8) {
+                        const int s2 = 32 * st + 8 * kq + j8;
+                        mv[j8] = s2 < t ? sM[t * LDM + s2] : 0.f;
+                    }
+                    pacc[jj][tt] = mma3(split8(mv), sU[st], pacc[jj][tt]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t2 = 16 * tt + 4 * kq + i;
+                    if (t2 < nval) pred[tok0 + size_t(t2) * HD + 16 * jt + cc] = pacc[jj][tt][i];
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int tt = 0; tt < kNB; ++tt) {
             const int t = 16 * tt + cc;
@@ -722,37 +893,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 // Y1 and Y2 are the state terms of dq_hat and of the read part of dk, Y3 that of the write
 // part of dk; OU and PU weight the decayed pair sums.
 // ------------------------------------------------------------------------------------------
-// Products of fp32 operands on the bf16 matrix cores (bf16 path): each fp32 value is carried as
-// a bf16 pair hi + lo (hi the nearest bf16, lo the nearest bf16 to the remainder, which is exact
-// in fp32), and a product takes hi*hi + hi*lo + lo*hi, leaving out only lo*lo (relative size
-// about 2^-16). Per K = 32 step that is three v_mfma_f32_16x16x32_bf16 (16 cycles each) in place
-// of eight v_mfma_f32_16x16x4_f32 (32 cycles each). A bf16 input (dO) needs only its hi part.
-struct Split {
-    Mma<bf16_t>::frag hi, lo;
-};
-__device__ __forceinline__ Split split8(f32x4_t a, f32x4_t b) {
-    using M16 = Mma<bf16_t>;
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    Split sp;
-    sp.hi = M16::pack(x);
-    const u16x8_t hb = __builtin_bit_cast(u16x8_t, sp.hi);
-    float rem[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rem[j] = x[j] - bf16_to_f32(hb[j]);
-    sp.lo = M16::pack(rem);
-    return sp;
-}
-__device__ __forceinline__ f32x4_t mma3(const Split &a, const Split &b, f32x4_t y) {
-    using M16 = Mma<bf16_t>;
-    y = M16::mma(a.hi, b.hi, y);
-    y = M16::mma(a.hi, b.lo, y);
-    return M16::mma(a.lo, b.hi, y);
-}
-__device__ __forceinline__ f32x4_t mma2(Mma<bf16_t>::frag a, const Split &b, f32x4_t y) {
-    y = Mma<bf16_t>::mma(a, b.hi, y);
-    return Mma<bf16_t>::mma(a, b.lo, y);
-}
-
 // The products kernel's body on the bf16 path: the same three phases and outputs, contraction
 // step s of lane group kq taking k = 32 s + 8 kq .. + 7 (two 16-byte loads per fp32 operand).
 template <int D>
