@@ -891,8 +891,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_scan_kernel(
 //   Y1 = dO S0^T, Y2 = dP S0^T, Y3 = U lambda_C^T    [C x D], stored [D/16][C][16] per chunk
 //   OU = dO U^T (s <= t), PU = dP U^T (s < t)         [C x C] per chunk, upper parts zero.
 // Y1 and Y2 are the state terms of dq_hat and of the read part of dk, Y3 that of the write
-// part of dk; OU and PU weight the decayed pair sums.
+// part of dk; OU and PU weight the decayed pair sums. Also rowsum(S_C * lambda_C) per channel,
+// the log-decay gradient's chunk-end term, [D] per chunk.
 // ------------------------------------------------------------------------------------------
+// rowsum(S_C * lambda_C) of rows 16 (w + 4 jj) + rr, the log-decay gradient's chunk-end term:
+// lane group kq sums its 32 columns (k = 32 st + 8 kq + j) in order, and the four groups are
+// added with two lane exchanges, in a fixed order.
+template <int D>
+__device__ __forceinline__ void rowsum_sc_lam(const float *__restrict__ SC, const float *__restrict__ lam,
+                                              float *__restrict__ rs, int wave, int rr, int kq) {
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj) {
+        const size_t row = size_t(16 * (wave + 4 * jj) + rr);
+        f32x4_t xs[D / 16], xl[D / 16];
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                xs[2 * st + h2] = ld4(SC, row * D + 32 * st + 8 * kq + 4 * h2);
+                xl[2 * st + h2] = ld4(lam, row * D + 32 * st + 8 * kq + 4 * h2);
+            }
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < D / 16; ++x)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) acc = fmaf(xs[x][q4], xl[x][q4], acc);
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (kq == 0) rs[row] = acc;
+    }
+}
+
 // The products kernel's body on the bf16 path: the same three phases and outputs, contraction
 // step s of lane group kq taking k = 32 s + 8 kq .. + 7 (two 16-byte loads per fp32 operand).
 template <int D>
@@ -1006,7 +1035,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const QT *__restrict__ dout, const float *__restrict__ e, const float *__restrict__ U,
     const float *__restrict__ dU, const float *__restrict__ states, const float *__restrict__ lamC,
     float *__restrict__ Y1, float *__restrict__ Y2, float *__restrict__ Y3, float *__restrict__ OU,
-    float *__restrict__ PU, int T, int H, int nchunks) {
+    float *__restrict__ PU, float *__restrict__ rs, int T, int H, int nchunks) {
     constexpr int C = kC, NT = D / 16;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int bh = b * H + h;
@@ -1019,6 +1048,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const size_t slot = size_t(bh) * nchunks + c;
     const float *S0 = states + (size_t(bh) * (nchunks + 1) + c) * D * D;
     const float *lam = lamC + slot * D * D;
+    // The chunk-end state is the next 64-token block's start state.
+    rowsum_sc_lam<D>(S0 + size_t(D) * D, lam, rs + slot * D, wave, lane & 15, lane >> 4);
     if constexpr (std::is_same_v<QT, bf16_t>) {
         products_split<D>(dout, e, U, dU, S0, lam, Y1, Y2, Y3, OU, PU, tok0, HD, slot, nval, wave, lane & 15,
                           lane >> 4);
@@ -1128,7 +1159,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 // ------------------------------------------------------------------------------------------
 // Chunk-parallel gradients. One workgroup per (b, h, chunk, group of 64 key channels); the
 // groups of one chunk take consecutive dispatch slots of one XCD, so they share its L2.
-//   1. rowsum(S_C * lambda_C) of the group's channels; O U^T and dP U^T into LDS.
+//   1. O U^T and dP U^T into LDS, with rowsum(S_C * lambda_C) of the group's channels (both from
+//      the products kernel).
 //   2. Per 16-channel pass, after the pivots: wave w takes the rows t of block w (dq_hat and the
 //      read part of dk) and the rows s of block w (the write part of dk), each its state term
 //      from the products kernel plus the decayed pair sums on the matrix cores. dq and dg are
@@ -1158,8 +1190,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float *__restrict__ g, const float *__restrict__ r, const float *__restrict__ states,
     const float *__restrict__ lamC, const float *__restrict__ Y1, const float *__restrict__ Y2,
     const float *__restrict__ Y3, const float *__restrict__ OU, const float *__restrict__ PU,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dla,
-    float *__restrict__ drp, int T, int H, int nchunks, int nwork) {
+    const float *__restrict__ rs, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg,
+    float *__restrict__ dla, float *__restrict__ drp, int T, int H, int nchunks, int nwork) {
     using L = GradLds<D>;
     constexpr int C = kC, LDM = L::LDM, LDH = L::LDH, DH = L::DH, LDO = L::LDO, G = L::G, DG = L::DG;
     constexpr int NT = D / 16;
@@ -1191,8 +1223,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int nval = min(C, T - c0);
     const size_t tok0 = (size_t(b) * T + c0) * HD + size_t(h) * D;
     const size_t slot = size_t(bh) * nchunks + c;
-    const float *SC = states + (size_t(bh) * (nchunks + 1) + c + 1) * D * D;
-    const float *lam = lamC + slot * D * D;
     const float *rh = r + size_t(h) * D;
 
     // A pass's operands from memory: the [C][16] slab of a, k, g, q, r (thread: token tid / 4,
@@ -1239,17 +1269,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             vo[j] = OU4[tid + kBwdThreads * j];
             vp[j] = PU4[tid + kBwdThreads * j];
         }
-        // rowsum(S_C * lambda_C) of the group's channels: thread (row, part) sums a contiguous
-        // segment of the row; the parts' sums are added in a fixed order.
-        constexpr int TPR = kBwdThreads / DG;  // threads per row
-        constexpr int SEG = D / TPR;           // elements per thread
-        const int il = tid / TPR, part = tid % TPR, i = gc0 + il;
-        f32x4_t xs[SEG / 4], xl[SEG / 4];
-#pragma unroll
-        for (int j = 0; j < SEG / 4; ++j) {
-            xs[j] = ld4(SC, size_t(i) * D + part * SEG + 4 * j);
-            xl[j] = ld4(lam, size_t(i) * D + part * SEG + 4 * j);
-        }
 #pragma unroll
         for (int j = 0; j < N4; ++j) {
             const int e0 = 4 * (tid + kBwdThreads * j), t = e0 / C, s = e0 % C;
@@ -1259,19 +1278,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 sPU[t * LDM + s + q4] = vp[j][q4];
             }
         }
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < SEG / 4; ++j)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) acc = fmaf(xs[j][q4], xl[j][q4], acc);
-        sTot[part * DG + il] = acc;
-        __syncthreads();
-        if (part == 0) {
-            float sum = 0.f;
-#pragma unroll
-            for (int p2 = 0; p2 < TPR; ++p2) sum += sTot[p2 * DG + il];
-            sRS[il] = sum;
-        }
+        if (tid < DG) sRS[tid] = rs[slot * D + gc0 + tid];
     }
     for (int i = tid; i < DG; i += kBwdThreads) sDr[i] = 0.f;
     // Decayed sums over token pairs, per 16-channel pass, on the matrix cores. With the pivots
@@ -1607,12 +1614,13 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (nchunks > 0) {
-        // The products go where the scan's operands were (K*beta, K*gamma, Q_hat*gamma, M and P
-        // are not read again): Y1, Y2, Y3 over kb, kg, qg, and OU, PU over M, P.
+        // The products go where the scan's operands were (K*beta, K*gamma, Q_hat*gamma, M, P and
+        // gamma_C are not read again): Y1, Y2, Y3 over kb, kg, qg, OU, PU over M, P, and the
+        // rowsums over gamma_C.
         float *Y1 = reinterpret_cast<float *>(ws + L.kb), *Y2 = reinterpret_cast<float *>(ws + L.kg);
         float *Y3 = reinterpret_cast<float *>(ws + L.qg), *OU = Mw, *PU = reinterpret_cast<float *>(ws + L.P);
         hipLaunchKernelGGL((bwd_products_kernel<QT, D>), dim3(nchunks, H, B), dim3(kBwdThreads), 0, stream, dout,
-                           x.e, u, dUw, states, lamC, Y1, Y2, Y3, OU, PU, T, H, nchunks);
+                           x.e, u, dUw, states, lamC, Y1, Y2, Y3, OU, PU, gC, T, H, nchunks);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
         auto kgk = bwd_grads_kernel<QT, D>;
@@ -1622,7 +1630,7 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
         const int nwork = BH * nchunks;
         const int nwg = (nwork + 7) / 8 * 8 * GradLds<D>::G;
         hipLaunchKernelGGL(kgk, dim3(nwg), dim3(kBwdThreads), GradLds<D>::BYTES, stream, q, k, x.a, x.g, x.r,
-                           states, lamC, Y1, Y2, Y3, OU, PU, x.dq, x.dk, x.dg, x.dla, drp, T, H, nchunks, nwork);
+                           states, lamC, Y1, Y2, Y3, OU, PU, gC, x.dq, x.dk, x.dg, x.dla, drp, T, H, nchunks, nwork);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
