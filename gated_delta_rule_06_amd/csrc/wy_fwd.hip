@@ -70,8 +70,7 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
     using f4 = F::f4;
     using f8 = F::f8;
     constexpr int NB = C / 16, NW = inv_waves<C>(), NT = 64 * NW, NPAIR = SL::NPAIR;
-    constexpr int NPW = (NPAIR + NW - 1) / NW;            // pair slots per wavefront, write-out
-    constexpr int NPL = (NPAIR + NW / 2 - 1) / (NW / 2);  // per loading wavefront
+    constexpr int NPW = (NPAIR + NW - 1) / NW;  // pair slots per wavefront (load and write-out)
     constexpr int NMD = NB * 64 / NT;  // 16-byte loads of the fp32 diagonal blocks per thread
     static_assert(NB / 2 <= NW && NB * 16 <= NT / 2 && C <= NT && (NB * 64) % NT == 0,
                   "work split");
@@ -100,12 +99,20 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
         m = ps - SL::prow(t);
     };
 
-    // e and the diagonal blocks (unconditional loads, clamped indices), into LDS.
+    // e and the diagonal blocks (unconditional loads, clamped indices), into LDS. Every wavefront
+    // then issues its share of M's pair slots, so that they are in flight during the wait for
+    // e and the diagonal blocks and during the leaves (each load unconditional: an index past the
+    // last slot reads the last one again; the loads come after e's and the blocks', so waiting
+    // for those does not wait for them).
+    f8 mreg[NPW];
     {
         const float e_t = e[(size_t(b) * T + t0 + min(tid, nreal - 1)) * H + hh];
         f32x4_t mdv[NMD];
 #pragma unroll
         for (int k = 0; k < NMD; ++k) mdv[k] = reinterpret_cast<const f32x4_t *>(gMD)[tid + k * NT];
+#pragma unroll
+        for (int n = 0; n < NPW; ++n)
+            mreg[n] = F::load8(gT + size_t(min(wave + NW * n, NPAIR - 1)) * 512 + lo_pair);
         if (tid < C) sh_e[tid] = tid < nreal ? e_t : 0.f;  // 0 past the sequence end
 #pragma unroll
         for (int k = 0; k < NMD; ++k) {
@@ -139,26 +146,19 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
                 if ((c & 3) == 0) sh_t[slot_of(i, i) * 64 + r + 16 * (c >> 2)] = F::pack(y4);
             }
         }
-    } else {
-        // M's pair slots into the off-diagonal tile slots. The pair slots holding an off-diagonal
-        // tile are all but the diagonal pair (t, t + 1) of an even row t (an odd row's last pair
-        // holds (t, t - 1) and the diagonal tile); the loads are unconditional (an index past
-        // the last slot reads the last one again).
-        const int wl = wave - NW / 2;
-        f8 mreg[NPL];
+    }
+    // M's pair slots into the off-diagonal tile slots. The pair slots holding an off-diagonal
+    // tile are all but the diagonal pair (t, t + 1) of an even row t (an odd row's last pair
+    // holds (t, t - 1) and the diagonal tile).
 #pragma unroll
-        for (int n = 0; n < NPL; ++n)
-            mreg[n] = F::load8(gT + size_t(min(wl + (NW / 2) * n, NPAIR - 1)) * 512 + lo_pair);
-#pragma unroll
-        for (int n = 0; n < NPL; ++n) {
-            const int ps = wl + (NW / 2) * n;
-            int t, m;
-            if (ps < NPAIR) {
-                pair_rc(ps, t, m);
-                if (2 * m < t) {
-                    sh_t[slot_of(t, 2 * m) * 64 + lane] = F::lo(mreg[n]);
-                    if (2 * m + 1 < t) sh_t[slot_of(t, 2 * m + 1) * 64 + lane] = F::hi(mreg[n]);
-                }
+    for (int n = 0; n < NPW; ++n) {
+        const int ps = wave + NW * n;
+        int t, m;
+        if (ps < NPAIR) {
+            pair_rc(ps, t, m);
+            if (2 * m < t) {
+                sh_t[slot_of(t, 2 * m) * 64 + lane] = F::lo(mreg[n]);
+                if (2 * m + 1 < t) sh_t[slot_of(t, 2 * m + 1) * 64 + lane] = F::hi(mreg[n]);
             }
         }
     }
@@ -334,6 +334,7 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
         for (int p = 0; p < NP; ++p) gc *= gPP[p * D + tid];
         reinterpret_cast<float *>(xslot + XS::GC_OFF)[tid] = gc;
     }
+    lds_barrier();  // e is in LDS for every wavefront's e * (K*gamma) below
     {
         // w*v of token 16L + x, value columns 16c + 4G .. + 3 (row layout), tokens past the
         // end zero; then its transpose.
