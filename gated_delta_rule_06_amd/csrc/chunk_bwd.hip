@@ -1588,7 +1588,7 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
         err = launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, cf, bf16, ws + L.fwd, stream);
         if (err != hipSuccess) return err;
     }
-    err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, ws + L.o, nullptr, u, states, B, T, H, D, cf, bf16,
+    err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, nullptr, nullptr, u, states, B, T, H, D, cf, bf16,
                                  ws + L.fwd, stream);
     if (err != hipSuccess) return err;
     const QT *q = static_cast<const QT *>(x.q), *k = static_cast<const QT *>(x.k);

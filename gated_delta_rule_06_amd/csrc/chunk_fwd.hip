@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
 
     if (wave == 1) {
         // ---------------- readout wavefront: O of chunk p - 1 in phase p ----------------
-        const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * unsigned(sizeof(QT)));
+        const rsrc_t ro_ = make_rsrc(SAVE ? nullptr : o + tok0, SAVE ? 0u : tok_elems * unsigned(sizeof(QT)));
         const rsrc_t rog = make_rsrc(GATED && !OGL ? og + tok0 : nullptr, GATED && !OGL ? tok_elems * 4u : 0u);
         // Operands of leaf L's readout: (Qh*gamma)_L and P_{L,0..L} in block pairs (and the
         // output gate rows), loaded one leaf ahead.
@@ -1132,8 +1132,10 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
             for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
             if constexpr (GATED && !OGL) wn.og = buf_load_fn<VC>(rog, lo_f, trow(ci * C + 16 * L, 4u));
         };
+        // SAVE (the backward's rerun) keeps u and the states and does not read out: the
+        // wavefront only stages the chain's pair decays and diagonal blocks.
         RWin rw[2];
-        load_rwin(0, 0, rw[0]);
+        if constexpr (!SAVE) load_rwin(0, 0, rw[0]);
         // Pair decays of chunk ci into sh_pp[ci & 1] (NP * D floats, four per lane and
         // step).
         constexpr int PP4 = NP * D / 4;
@@ -1171,7 +1173,7 @@ __global__ __launch_bounds__(LRS ? 192 : 128) void chunk_scan_kernel(
                 load_ppt(p + 1, ppt);
                 load_mdt(p + 1);
             }
-            if (p >= 1) {
+            if (!SAVE && p >= 1) {
                 const int ci = p - 1;
                 const int buf = ci & 1;
                 f4 fS[NCT];

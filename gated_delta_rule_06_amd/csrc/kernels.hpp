@@ -42,10 +42,10 @@ hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w
                                    const float *s0, void *o, float *s_out, int B, int T, int H,
                                    int d, int chunk, const void *workspace, hipStream_t stream);
 
-// Phase S as above (no output gate), also keeping what the backward pass needs: u_out
-// [B, T, H, d] fp32 (u = w * v - e * p of every token) and states [B * H][ceil(T / 64) + 1]
-// [d][d] fp32 (the state at every 64-token block start, then the final state). Chunks of 64,
-// 128 or 256.
+// Phase S for the backward pass: keeps u_out [B, T, H, d] fp32 (u = w * v - e * p of every
+// token) and states [B * H][ceil(T / 64) + 1][d][d] fp32 (the state at every 64-token block
+// start, then the final state), and reads nothing out (o is not written and may be null).
+// Chunks of 64, 128 or 256.
 hipError_t launch_chunk_scan_save(const void *v, const float *e, const float *w, const float *s0,
                                   void *o, float *s_out, float *u_out, float *states, int B,
                                   int T, int H, int d, int chunk, bool bf16,

@@ -69,7 +69,7 @@ template <int D, int C> struct XSlot {
 // operand-precision regions, each 256-byte aligned.
 constexpr int kBwdChunk = 64;
 struct BwdLayout {
-    size_t fwd, o, u, states, kb, kg, qg, gC, M, P, pred, dU, lamC, drp, total;
+    size_t fwd, u, states, kb, kg, qg, gC, M, P, pred, dU, lamC, drp, total;
 };
 // Offsets of the backward workspace for these sizes; false when the forward's workspace size
 // is invalid.

@@ -66,7 +66,6 @@ bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
         return at;
     };
     L.fwd = take(fwd);
-    L.o = take(tok * (bf16 ? 2 : 4));
     L.u = take(tok * 4);
     L.states = take(BH * (nc + 1) * d * d * 4);
     L.kb = take(BH * nc * kC * d * 4);
