@@ -1585,7 +1585,8 @@ hipError_t bwd_typed(const ChunkBwdArgs &x, int B, int T, int H, unsigned char *
     // The forward rerun, at its own chunk size, keeping u and the state every 64 tokens.
     const int cf = bwd_fwd_chunk(B, T, H, D);
     if (T > 0) {
-        err = launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, cf, bf16, ws + L.fwd, stream);
+        err = bf16 ? launch_chunk_prepare_state(x.k, x.a, x.g, x.r, B, T, H, D, cf, ws + L.fwd, stream)
+                   : launch_chunk_prepare(x.q, x.k, x.a, x.g, x.r, B, T, H, D, cf, bf16, ws + L.fwd, stream);
         if (err != hipSuccess) return err;
     }
     err = launch_chunk_scan_save(x.v, x.e, x.w, x.s0, nullptr, nullptr, u, states, B, T, H, D, cf, bf16,

@@ -425,7 +425,9 @@ template <int D, int C> struct LrLds {
     static_assert(UA_OFF <= 160 * 1024 - 1024, "LDS budget");
 };
 
-template <int D, int C, bool LR>
+// NORD: for a forward that keeps the state and does not read out (the backward pass's rerun):
+// neither P nor Qh*gamma is formed, and q is not read.
+template <int D, int C, bool LR, bool NORD = false>
 __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const float *__restrict__ a,
     const float *__restrict__ g, const float *__restrict__ r, LowRankGates lr,
@@ -467,7 +469,8 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     const size_t HD = size_t(H) * D;
     const size_t base = (size_t(b) * T + t0) * HD + size_t(hh) * D;
     const unsigned span = unsigned((size_t(nreal - 1) * HD + D));
-    const rsrc_t rk = make_rsrc(k + base, span * 2u), rq = make_rsrc(q + base, span * 2u);
+    const rsrc_t rk = make_rsrc(k + base, span * 2u);
+    const rsrc_t rq = make_rsrc(NORD ? nullptr : q + base, NORD ? 0u : span * 2u);
     const unsigned vo = unsigned(size_t(t) * HD + chl);
     // Gate rows: fp32 a and g, or (LR) the z rows of the decay and read slices, K = 32 rank
     // steps of 8 values per lane (lane (t, G): token t, ranks 32s + 8G .. + 7).
@@ -501,8 +504,12 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
         }
         in.k0 = Row4<bf16_t>::load(rk, vo * 2u, row * 2u);
         in.k1 = Row4<bf16_t>::load(rk, vo * 2u + 32u, row * 2u);
-        in.q0 = Row4<bf16_t>::load(rq, vo * 2u, row * 2u);
-        in.q1 = Row4<bf16_t>::load(rq, vo * 2u + 32u, row * 2u);
+        if constexpr (!NORD) {
+            in.q0 = Row4<bf16_t>::load(rq, vo * 2u, row * 2u);
+            in.q1 = Row4<bf16_t>::load(rq, vo * 2u + 32u, row * 2u);
+        } else {
+            in.q0 = in.q1 = u16x4_t{0, 0, 0, 0};
+        }
     };
     float rr[8];
 #pragma unroll
@@ -691,7 +698,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 #pragma unroll
             for (int j = 0; j < 8; ++j) { x[j] = kv[j] * pi[j]; y[j] = qh[j] * pi[j]; }
             *reinterpret_cast<f8 *>(sh_A + (hb * 2 + 0) * 16 * D + swz<D>(t, 4 * cg + G)) = pack8(x);
-            *reinterpret_cast<f8 *>(sh_A + (hb * 2 + 1) * 16 * D + swz<D>(t, 4 * cg + G)) = pack8(y);
+            if constexpr (!NORD) *reinterpret_cast<f8 *>(sh_A + (hb * 2 + 1) * 16 * D + swz<D>(t, 4 * cg + G)) = pack8(y);
             if (t == 15) st8f(sh_pi + bt * D + pos0, pi);
         }
         // This wavefront's share (its 32 channels) of the diagonal blocks of M and P: one
@@ -704,7 +711,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 for (int j = 0; j < 8; ++j) { x[j] = kv[j] * f[j]; y[j] = qh[j] * f[j]; }
                 const f8 fk = pack8(x), fq = pack8(y);
                 const f32x4_t am = F::mma8(fk, fk, zero4());
-                const f32x4_t ap = F::mma8(fk, fq, zero4());
+                const f32x4_t ap = NORD ? zero4() : F::mma8(fk, fq, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = 4 * G + i;
@@ -717,9 +724,11 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
             level(f4t, 4);
             level(f2t, 2);
             level(f1t, 1);
-            const f32x4_t ad = F::mma8(pack8(kv), pack8(qh), zero4());
+            if constexpr (!NORD) {
+                const f32x4_t ad = F::mma8(pack8(kv), pack8(qh), zero4());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lp[i] += (4 * G + i == t) ? ad[i] : 0.f;
+                for (int i = 0; i < 4; ++i) lp[i] += (4 * G + i == t) ? ad[i] : 0.f;
+            }
             sh_dg[((hb * NG + cg) * 2 + 0) * 64 + lane] = lm;
             sh_dg[((hb * NG + cg) * 2 + 1) * 64 + lane] = lp;
         }
@@ -739,7 +748,7 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
             }
             const size_t row = frag_idx(16 * bt + t, pos0, D);
             *reinterpret_cast<f8 *>(gKg + row) = pack8(x);
-            *reinterpret_cast<f8 *>(gQg + row) = pack8(y);
+            if constexpr (!NORD) *reinterpret_cast<f8 *>(gQg + row) = pack8(y);
             // (K*beta')^T into LDS: channel row, position 8 (t / 4) + 4 hb + t % 4 of the
             // pair (the 32-group order), 16-byte chunks rotated by (channel / 4) mod 4.
             const int pp = 8 * (t >> 2) + 4 * hb + (t & 3);
@@ -767,12 +776,12 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 lp += sh_dg[((hb * NG + c) * 2 + 1) * 64 + lane];
             }
             *reinterpret_cast<f32x4_t *>(gMD + size_t(bt) * 256 + blk_lo) = lm;
-            store4(gP + SL::blk(bt, bt, blk_lo), lp);
+            if constexpr (!NORD) store4(gP + SL::blk(bt, bt, blk_lo), lp);
             // The pair slots the scan reads whole: M's diagonal block (its products use
             // the fp32 copy above) and, for even bt, P's block (bt, bt + 1) above the
             // diagonal hold zeros.
             store4(gM + SL::blk(bt, bt, blk_lo), zero4());
-            if ((bt & 1) == 0) store4(gP + SL::blk(bt, bt + 1, blk_lo), zero4());
+            if (!NORD && (bt & 1) == 0) store4(gP + SL::blk(bt, bt + 1, blk_lo), zero4());
         }
         // Off-diagonal blocks of the pair: (2p, bs < 2p) and (2p + 1, bs <= 2p). Rows s:
         // K*sigma of block bs times the decay of the whole blocks between bs and bt;
@@ -786,7 +795,8 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     ak[h2][kk] = *reinterpret_cast<const f8 *>(sh_A + (h2 * 2 + 0) * 16 * D + swz<D>(t, 4 * kk + G));
-                    aq[h2][kk] = *reinterpret_cast<const f8 *>(sh_A + (h2 * 2 + 1) * 16 * D + swz<D>(t, 4 * kk + G));
+                    if constexpr (!NORD)
+                        aq[h2][kk] = *reinterpret_cast<const f8 *>(sh_A + (h2 * 2 + 1) * 16 * D + swz<D>(t, 4 * kk + G));
                 }
                 ld8f(sh_pi + (2 * p) * D + 32 * kk + 8 * G, pb0[kk]);
             }
@@ -806,14 +816,18 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                     }
                     const f8 fb0 = pack8(x0), fb1 = pack8(x1);
                     am0 = F::mma8(fb0, ak[0][kk], am0);
-                    ap0 = F::mma8(fb0, aq[0][kk], ap0);
                     am1 = F::mma8(fb1, ak[1][kk], am1);
-                    ap1 = F::mma8(fb1, aq[1][kk], ap1);
+                    if constexpr (!NORD) {
+                        ap0 = F::mma8(fb0, aq[0][kk], ap0);
+                        ap1 = F::mma8(fb1, aq[1][kk], ap1);
+                    }
                 }
                 store4(gM + SL::blk(2 * p, bs, blk_lo), am0);
-                store4(gP + SL::blk(2 * p, bs, blk_lo), ap0);
                 store4(gM + SL::blk(2 * p + 1, bs, blk_lo), am1);
-                store4(gP + SL::blk(2 * p + 1, bs, blk_lo), ap1);
+                if constexpr (!NORD) {
+                    store4(gP + SL::blk(2 * p, bs, blk_lo), ap0);
+                    store4(gP + SL::blk(2 * p + 1, bs, blk_lo), ap1);
+                }
             };
             // Block (2p + 1, 2p): no whole block in between.
             auto block_adjacent = [&]() {
@@ -822,10 +836,10 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
                 for (int kk = 0; kk < NG; ++kk) {
                     const f8 xb = *reinterpret_cast<const f8 *>(sh_bb + swz<D>(16 * (2 * p) + t, 4 * kk + G));
                     am = F::mma8(xb, ak[1][kk], am);
-                    ap = F::mma8(xb, aq[1][kk], ap);
+                    if constexpr (!NORD) ap = F::mma8(xb, aq[1][kk], ap);
                 }
                 store4(gM + SL::blk(2 * p + 1, 2 * p, blk_lo), am);
-                store4(gP + SL::blk(2 * p + 1, 2 * p, blk_lo), ap);
+                if constexpr (!NORD) store4(gP + SL::blk(2 * p + 1, 2 * p, blk_lo), ap);
             };
             for (int n = wave; n < 2 * p; n += NW) block_pair(n);
             if (2 * p % NW == wave) block_adjacent();
@@ -1525,6 +1539,36 @@ hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, co
     MUIR_PREP(64, 64) MUIR_PREP(64, 128) MUIR_PREP(64, 256)
     MUIR_PREP(128, 64) MUIR_PREP(128, 128) MUIR_PREP(128, 256)
 #undef MUIR_PREP
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_prepare_state(const void *k, const float *a, const float *g, const float *r,
+                                      int B, int T, int H, int d, int chunk, void *workspace,
+                                      hipStream_t stream) {
+    const LowRankGates none{nullptr, nullptr, nullptr, nullptr, nullptr};
+    const int nchunks = (T + chunk - 1) / chunk;
+    if (nchunks == 0) return hipSuccess;
+    auto run = [&](auto dc, auto cc) {
+        constexpr int D = decltype(dc)::value, C = decltype(cc)::value;
+        auto kern = chunk_prepare_bf16_kernel<D, C, false, true>;
+        constexpr size_t lds = Prep2Lds<D, C>::BYTES;
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(nchunks, H, B), dim3(4 * D), lds, stream,
+                           static_cast<const bf16_t *>(nullptr), static_cast<const bf16_t *>(k), a, g, r,
+                           none, static_cast<unsigned char *>(workspace), T, H, nchunks);
+        return hipGetLastError();
+    };
+    using I = std::integral_constant<int, 64>;
+    using J = std::integral_constant<int, 128>;
+    using K = std::integral_constant<int, 256>;
+    if (d == 64 && chunk == 64) return run(I{}, I{});
+    if (d == 64 && chunk == 128) return run(I{}, J{});
+    if (d == 64 && chunk == 256) return run(I{}, K{});
+    if (d == 128 && chunk == 64) return run(J{}, I{});
+    if (d == 128 && chunk == 128) return run(J{}, J{});
+    if (d == 128 && chunk == 256) return run(J{}, K{});
     return hipErrorInvalidValue;
 }
 

@@ -20,6 +20,13 @@ hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, co
                                 const float *r, int B, int T, int H, int d, int chunk, bool bf16,
                                 void *workspace, hipStream_t stream);
 
+// Phase P for a forward that keeps the state and does not read out (bf16 k): M, its fp32
+// diagonal blocks, K*gamma, (K*beta')^T and the pair decays, without P and Qh*gamma (q and g are
+// not needed; g may still be passed).
+hipError_t launch_chunk_prepare_state(const void *k, const float *a, const float *g, const float *r,
+                                      int B, int T, int H, int d, int chunk, void *workspace,
+                                      hipStream_t stream);
+
 // Phase P with the decay a and the query gate g formed in the kernel from the low-rank gate
 // projection (z [B, T, 512], U_a [H, d, 64], U_g [H, d, 128] bf16; c_a, c_g [H, d] fp32),
 // bf16 q and k only.
