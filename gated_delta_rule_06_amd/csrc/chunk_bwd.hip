@@ -950,29 +950,50 @@ __device__ __forceinline__ void products_split(const bf16_t *__restrict__ dout, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[16 * i] = y[i];
     };
-    // 1. Y3 = U lambda_C^T.
+    // The B operands stream through LDS, one 16-row tile at a time, double-buffered, loaded
+    // once per workgroup (every wavefront multiplies every tile): the NT tiles of lambda_C
+    // (phase 1), the kNB row blocks of U (phase 2), the NT tiles of S0 (phase 3). Thread tid
+    // moves 16-byte pieces tid, tid + 256, ... of a tile.
+    constexpr int LDT = D + 4, N4 = 16 * D / 4 / kBwdThreads, NQ = 2 * NT + kNB;
+    __shared__ __align__(16) float sh_b[2][16][LDT];
+    const int tid = 64 * wave + 16 * kq + rr;
+    auto tile_src = [&](int q, int r) -> const float * {
+        if (q < NT) return lam + size_t(16 * q + r) * D;
+        if (q < NT + kNB) return U + tokrow(16 * (q - NT) + r);
+        return S0 + size_t(16 * (q - NT - kNB) + r) * D;
+    };
+    f32x4_t nx[N4];
+    auto load_tile = [&](int q) {
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int i = tid + kBwdThreads * j, r = i / (D / 4), c4 = i % (D / 4);
+            nx[j] = ld4(tile_src(q, r), 4 * c4);
+        }
+    };
+    auto put_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            const int i = tid + kBwdThreads * j, r = i / (D / 4), c4 = i % (D / 4);
+            *reinterpret_cast<f32x4_t *>(&sh_b[buf][r][4 * c4]) = nx[j];
+        }
+    };
+    // B fragment of step st: row rr of the tile, k = 32 st + 8 kq .. + 7, split.
+    auto tileB = [&](int buf, int st) {
+        const f32x4_t *p = reinterpret_cast<const f32x4_t *>(&sh_b[buf][rr][32 * st + 8 * kq]);
+        return split8(p[0], p[1]);
+    };
+    load_tile(0);
+    Split xu[NS];
     {
-        Raw ru, bl[2];
+        Raw ru;
         ld8(U, tokrow(ta), ru);
-        ld8(lam, size_t(rr) * D, bl[0]);
-        Split xu[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) xu[st] = split8(ru[st][0], ru[st][1]);
-#pragma unroll
-        for (int it = 0; it < NT; ++it) {
-            const int cur = it & 1;
-            if (it + 1 < NT) ld8(lam, size_t(16 * (it + 1) + rr) * D, bl[cur ^ 1]);
-            f32x4_t y3 = zero4();
-#pragma unroll
-            for (int st = 0; st < NS; ++st) y3 = mma3(xu[st], split8(bl[cur][st][0], bl[cur][st][1]), y3);
-            store_y(Y3, it, y3);
-        }
     }
+    put_tile(0);
     // The wave's rows of dO (exact in bf16) and dP = -e * dU (split), zero past the sequence.
     M16::frag xo[NS];
     Split xp[NS];
-    Raw bu[2];
-    ld8(U, tokrow(rr), bu[0]);
     {
         Raw re, rd;
         ld8(e, tokrow(ta), re);
@@ -988,45 +1009,50 @@ __device__ __forceinline__ void products_split(const bf16_t *__restrict__ dout, 
             }
         }
     }
-    // 2. O U^T and dP U^T against the column blocks bs <= w; blocks after w are zero.
+    __syncthreads();
 #pragma unroll
-    for (int bs = 0; bs < kNB; ++bs) {
-        const int cur = bs & 1;
-        f32x4_t yo = zero4(), yp = zero4();
-        if (bs <= wave) {
-            if (bs + 1 <= wave) ld8(U, tokrow(16 * (bs + 1) + rr), bu[cur ^ 1]);
+    for (int q = 0; q < NQ; ++q) {
+        const int buf = q & 1;
+        if (q + 1 < NQ) load_tile(q + 1);
+        if (q < NT) {
+            // 1. Y3 = U lambda_C^T.
+            f32x4_t y3 = zero4();
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const Split b = split8(bu[cur][st][0], bu[cur][st][1]);
-                yo = mma2(xo[st], b, yo);
-                yp = mma3(xp[st], b, yp);
+            for (int st = 0; st < NS; ++st) y3 = mma3(xu[st], tileB(buf, st), y3);
+            store_y(Y3, q, y3);
+        } else if (q < NT + kNB) {
+            // 2. O U^T and dP U^T against column block bs <= w; blocks after w are zero.
+            const int bs = q - NT;
+            f32x4_t yo = zero4(), yp = zero4();
+            if (bs <= wave) {
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    const Split b = tileB(buf, st);
+                    yo = mma2(xo[st], b, yo);
+                    yp = mma3(xp[st], b, yp);
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * wave + 4 * kq + i, sc = 16 * bs + rr;
-            OU[(slot * C + t) * C + sc] = sc <= t ? yo[i] : 0.f;
-            PU[(slot * C + t) * C + sc] = sc < t ? yp[i] : 0.f;
-        }
-    }
-    // 3. Y1 = dO S0^T and Y2 = dP S0^T.
-    {
-        Raw bS[2];
-        ld8(S0, size_t(rr) * D, bS[0]);
-#pragma unroll
-        for (int it = 0; it < NT; ++it) {
-            const int cur = it & 1;
-            if (it + 1 < NT) ld8(S0, size_t(16 * (it + 1) + rr) * D, bS[cur ^ 1]);
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * wave + 4 * kq + i, sc = 16 * bs + rr;
+                OU[(slot * C + t) * C + sc] = sc <= t ? yo[i] : 0.f;
+                PU[(slot * C + t) * C + sc] = sc < t ? yp[i] : 0.f;
+            }
+        } else {
+            // 3. Y1 = dO S0^T and Y2 = dP S0^T.
+            const int it = q - NT - kNB;
             f32x4_t y1 = zero4(), y2 = zero4();
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const Split b = split8(bS[cur][st][0], bS[cur][st][1]);
+                const Split b = tileB(buf, st);
                 y1 = mma2(xo[st], b, y1);
                 y2 = mma3(xp[st], b, y2);
             }
             store_y(Y1, it, y1);
             store_y(Y2, it, y2);
         }
+        if (q + 1 < NQ) put_tile(buf ^ 1);
+        __syncthreads();
     }
 }
 
