@@ -220,3 +220,40 @@ def test_head_offsets_past_2_gib(device):
     o_ref, s_ref = oracle.recurrent(*[head[n] for n in NAMES])
     assert_parity(to_numpy(o[:, :, h:h + 1]), to_numpy(s[:, h:h + 1]), o_ref, s_ref, TOL["bf16"],
                   f"T={T} head {h}")
+
+
+def test_linear_in_state_and_values(device):
+    """With q, k and every gate fixed the recurrence is linear in (S0, v) jointly:
+    o(x S0 + y S0', x v + y v') = x o(S0, v) + y o(S0', v'), and the same for the final state,
+    up to fp32 rounding (fp32 q/k/v, so the combined v is passed exactly)."""
+    inp = workloads.chunk_inputs(2, B=1, T=300, H=2, qkv="f32", seed=51)
+    rng = np.random.default_rng(51)
+    s0a, s0b = state_like(rng, 1, 2, 128), state_like(rng, 1, 2, 128)
+    vb = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    x, y = 0.75, -1.25
+    oa, sa = gpu_fwd(inp, device, 128, s0a)
+    ob, sb = gpu_fwd(dict(inp, v=vb), device, 128, s0b)
+    vc = (x * inp["v"].astype(np.float64) + y * vb).astype(np.float32)
+    s0c = (x * s0a.astype(np.float64) + y * s0b).astype(np.float32)
+    oc, sc = gpu_fwd(dict(inp, v=vc), device, 128, s0c)
+    assert_parity(oc, sc, x * oa.astype(np.float64) + y * ob, x * sa.astype(np.float64) + y * sb,
+                  1e-4, "linearity in (S0, v)")
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_value_column_permutation(device, qkv):
+    """Value columns never interact: permuting the columns of v, e, w and S0 permutes those
+    of o and of the final state, bit for bit (every column takes the same arithmetic,
+    whichever tile and lane hold it)."""
+    inp = workloads.chunk_inputs(2, B=1, T=300, H=2, qkv=qkv, seed=52)
+    rng = np.random.default_rng(52)
+    s0 = state_like(rng, 1, 2, 128)
+    perm = rng.permutation(128)
+    permuted = dict(inp)
+    for n in ("v", "e", "w"):
+        permuted[n] = np.ascontiguousarray(inp[n][..., perm])
+    o, s = gpu_fwd(inp, device, 128, s0)
+    op, sp = gpu_fwd(permuted, device, 128, np.ascontiguousarray(s0[..., perm]))
+    do = np.abs(op - o[..., perm]).max()
+    ds = np.abs(sp - s[..., perm]).max()
+    assert do == 0 and ds == 0, f"permuted columns differ: o by {do:.3e}, state by {ds:.3e}"
