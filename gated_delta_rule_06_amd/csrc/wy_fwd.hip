@@ -70,9 +70,11 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
     using f4 = F::f4;
     using f8 = F::f8;
     constexpr int NB = C / 16, NW = inv_waves<C>(), NT = 64 * NW, NPAIR = SL::NPAIR;
-    constexpr int NPW = (NPAIR + NW - 1) / NW;  // pair slots per wavefront (load and write-out)
-    constexpr int NMD = NB * 64 / NT;  // 16-byte loads of the fp32 diagonal blocks per thread
-    static_assert(NB / 2 <= NW && NB * 16 <= NT / 2 && C <= NT && (NB * 64) % NT == 0,
+    constexpr int NW2 = NW / 2, NT2 = NT / 2;     // wavefronts and threads per half
+    constexpr int NPW = (NPAIR + NW - 1) / NW;    // pair slots per wavefront in the write-out
+    constexpr int NPL = (NPAIR + NW2 - 1) / NW2;  // pair slots per wavefront of the M half
+    constexpr int NMD = NB * 64 / NT2;  // 16-byte loads of the fp32 diagonal blocks per thread
+    static_assert(NB / 2 <= NW && NB * 16 <= NT2 && C <= NT2 && (NB * 64) % NT2 == 0,
                   "work split");
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -91,46 +93,46 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
     const unsigned lo_pair = unsigned((4 * x + G) * 8);  // lane's 8 elements of a pair slot
     const f4 z4 = {0, 0, 0, 0};
 
-    // Block row and pair index of pair slot ps (wave-uniform).
+    // Block row and pair index of pair slot ps (wave-uniform): the row is the number of rows
+    // after the first whose first slot is at or below ps, a sum of compile-time comparisons
+    // (a search loop here cost more scalar instructions than the kernel's vector ones).
     auto pair_rc = [](int ps, int &row, int &m) {
         int t = 0;
-        while (SL::prow(t + 1) <= ps) ++t;
+#pragma unroll
+        for (int k = 1; k < NB; ++k) t += SL::prow(k) <= ps ? 1 : 0;
         row = t;
         m = ps - SL::prow(t);
     };
 
-    // e and the diagonal blocks (unconditional loads, clamped indices), into LDS. Every wavefront
-    // then issues its share of M's pair slots, so that they are in flight during the wait for
-    // e and the diagonal blocks and during the leaves (each load unconditional: an index past the
-    // last slot reads the last one again; the loads come after e's and the blocks', so waiting
-    // for those does not wait for them).
-    f8 mreg[NPW];
-    {
+    // Inputs. The two halves of the workgroup take different parts, so that each half's
+    // waits cover only its own loads and no wavefront holds M's tiles in registers through the
+    // leaves' substitution:
+    //   leaf half (wavefronts 0 .. NW/2 - 1): e (0 past the sequence end) and the strict lower
+    //     triangles of the fp32 diagonal blocks into LDS, a barrier, then the leaves;
+    //   M half: its share of M's pair slots, in flight over that barrier, then into the
+    //     off-diagonal tile slots. The pair slots holding an off-diagonal tile are all but the
+    //     diagonal pair (t, t + 1) of an even row t (an odd row's last pair holds (t, t - 1) and
+    //     the diagonal tile).
+    // Every load is unconditional; an index past the end is clamped and reads valid, unused data.
+    if (wave < NW2) {
         const float e_t = e[(size_t(b) * T + t0 + min(tid, nreal - 1)) * H + hh];
         f32x4_t mdv[NMD];
 #pragma unroll
-        for (int k = 0; k < NMD; ++k) mdv[k] = reinterpret_cast<const f32x4_t *>(gMD)[tid + k * NT];
-#pragma unroll
-        for (int n = 0; n < NPW; ++n)
-            mreg[n] = F::load8(gT + size_t(min(wave + NW * n, NPAIR - 1)) * 512 + lo_pair);
-        if (tid < C) sh_e[tid] = tid < nreal ? e_t : 0.f;  // 0 past the sequence end
+        for (int k = 0; k < NMD; ++k) mdv[k] = reinterpret_cast<const f32x4_t *>(gMD)[tid + k * NT2];
+        if (tid < C) sh_e[tid] = tid < nreal ? e_t : 0.f;
 #pragma unroll
         for (int k = 0; k < NMD; ++k) {
-            const int n = tid + k * NT, i = n >> 6, s2 = (n >> 2) & 15, c0 = 4 * (n & 3);
+            const int n = tid + k * NT2, i = n >> 6, s2 = (n >> 2) & 15, c0 = 4 * (n & 3);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (c0 + q < s2) sh_md[i * 120 + s2 * (s2 - 1) / 2 + c0 + q] = mdv[k][q];
         }
-    }
-    lds_barrier();
-
-    if (wave < NW / 2) {
+        lds_barrier();
         // Leaves: thread (i, r) solves row r of T_ii from T L = I, right to left:
         // y_c = [c == r] - sum_{s > c} y_s e_s M_ii[s][c] (y_s = 0 for s > r), in fp32; each
         // group of four finished values goes to its row fragment at once.
-        const int n = tid;
-        if (n < NB * 16) {
-            const int i = n >> 4, r = n & 15;
+        if (tid < NB * 16) {
+            const int i = tid >> 4, r = tid & 15;
             const float *md = sh_md + i * 120;
             const float *ee = sh_e + 16 * i;
             float z[16];
@@ -146,19 +148,23 @@ void wy_inverse_kernel(const float *__restrict__ e, unsigned char *__restrict__ 
                 if ((c & 3) == 0) sh_t[slot_of(i, i) * 64 + r + 16 * (c >> 2)] = F::pack(y4);
             }
         }
-    }
-    // M's pair slots into the off-diagonal tile slots. The pair slots holding an off-diagonal
-    // tile are all but the diagonal pair (t, t + 1) of an even row t (an odd row's last pair
-    // holds (t, t - 1) and the diagonal tile).
+    } else {
+        const int mw = wave - NW2;
+        f8 mreg[NPL];
 #pragma unroll
-    for (int n = 0; n < NPW; ++n) {
-        const int ps = wave + NW * n;
-        int t, m;
-        if (ps < NPAIR) {
-            pair_rc(ps, t, m);
-            if (2 * m < t) {
-                sh_t[slot_of(t, 2 * m) * 64 + lane] = F::lo(mreg[n]);
-                if (2 * m + 1 < t) sh_t[slot_of(t, 2 * m + 1) * 64 + lane] = F::hi(mreg[n]);
+        for (int n = 0; n < NPL; ++n)
+            mreg[n] = F::load8(gT + size_t(min(mw + NW2 * n, NPAIR - 1)) * 512 + lo_pair);
+        lds_barrier();
+#pragma unroll
+        for (int n = 0; n < NPL; ++n) {
+            const int ps = mw + NW2 * n;
+            int t, m;
+            if (ps < NPAIR) {
+                pair_rc(ps, t, m);
+                if (2 * m < t) {
+                    sh_t[slot_of(t, 2 * m) * 64 + lane] = F::lo(mreg[n]);
+                    if (2 * m + 1 < t) sh_t[slot_of(t, 2 * m + 1) * 64 + lane] = F::hi(mreg[n]);
+                }
             }
         }
     }
