@@ -332,41 +332,85 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
         return F::load8(base + size_t(SL::prow(bt) + m) * 512 + lo_pair);
     };
 
+    // Every phase issues its global loads ahead of the work that waits for them (a wavefront's
+    // loads complete in order, so a load used at once makes every later one wait): phase 1's at
+    // the start, phase 2's T pairs when phase 1's work begins, phase 3's (K*beta)^T fragments and
+    // P pairs when phase 2's products are done. All are unconditional: a pair index past a block
+    // row's last is clamped to it and its product skipped.
+    constexpr int NU1 = NB * NCT / NW;  // w*v tiles per wavefront
+    constexpr int NU2 = NB * NKD / NW;  // e*(K*gamma) fragments per wavefront
+    static_assert(NU1 * NW == NB * NCT && NU2 * NW == NB * NKD, "work split");
+    // Pair slots of the k-th block a wavefront takes: at most this many.
+    constexpr auto maxm = [](int k) {
+        return (NB >= 2 * NW ? 2 * NW * (k >> 1) + ((k & 1) ? 2 * NW - 1 : NW - 1) : NB - 1) / 2 + 1;
+    };
+
     // ---- 1: operands in accumulator layout; pair decays, e and gamma_C ----
-    for (int t = tid; t < C; t += 64 * NW) sh_e[t] = t < nreal ? e[(size_t(b) * T + t0 + t) * H + hh] : 0.f;
-    for (int n = tid; n < NP * D; n += 64 * NW) sh_pp[n] = gPP[n];
+    const float e_t = e[(size_t(b) * T + t0 + min(tid, nreal - 1)) * H + hh];
+    constexpr int NPPL = (NP * D + 64 * NW - 1) / (64 * NW);
+    float ppl[NPPL], gcl[NP];
+#pragma unroll
+    for (int n = 0; n < NPPL; ++n) ppl[n] = gPP[min(tid + n * 64 * NW, NP * D - 1)];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) gcl[q] = gPP[q * D + (tid & (D - 1))];
+    // w*v of token 16L + x, value columns 16c + 4G .. + 3 (row layout), tokens past the end zero;
+    // e*(K*gamma): one fragment gives both 16-channel halves of a channel group.
+    const rsrc_t rv = make_rsrc(v + (size_t(b) * T + t0) * HD + size_t(hh) * D,
+                                unsigned((size_t(nreal - 1) * HD + D) * 2));
+    const rsrc_t rw = make_rsrc(w + (size_t(b) * T + t0) * HD + size_t(hh) * D,
+                                unsigned((size_t(nreal - 1) * HD + D) * 4));
+    u16x4_t vv[NU1];
+    f32x4_t wv[NU1];
+    f8 kg[NU2];
+#pragma unroll
+    for (int k = 0; k < NU1; ++k) {
+        const int u = wave + NW * k, L = u / NCT, c = u % NCT;
+        const unsigned off = unsigned(16 * L + x) * unsigned(HD) + unsigned(16 * c + 4 * G);
+        vv[k] = Row4<bf16_t>::load(rv, off * 2u, 0u);
+        wv[k] = buf_load_f4(rw, off * 4u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < NU2; ++k) {
+        const int u = wave + NW * k, L = u / NKD, kk = u % NKD;
+        kg[k] = F::load8(gKg + frag_idx(16 * L, 32 * kk, D) + lo_frag);
+    }
+    if (tid < C) sh_e[tid] = tid < nreal ? e_t : 0.f;
+#pragma unroll
+    for (int n = 0; n < NPPL; ++n)
+        if (tid + n * 64 * NW < NP * D) sh_pp[tid + n * 64 * NW] = ppl[n];
     if (tid < D) {
         float gc = 1.f;
-        for (int p = 0; p < NP; ++p) gc *= gPP[p * D + tid];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) gc *= gcl[q];
         reinterpret_cast<float *>(xslot + XS::GC_OFF)[tid] = gc;
     }
     lds_barrier();  // e is in LDS for every wavefront's e * (K*gamma) below
+
+    // Phase 2's T pairs, in flight during phase 1's work.
+    f8 tpr[BD::NPW][maxm(BD::NPW - 1)];
+    static_for<BD::NPW>([&](auto Kc) {
+        constexpr int k = decltype(Kc)::value;
+        const int i = BD::block(wave, k);
+#pragma unroll
+        for (int m = 0; m < maxm(k); ++m) tpr[k][m] = pair(gT, i, min(m, i / 2));
+    });
     {
-        // w*v of token 16L + x, value columns 16c + 4G .. + 3 (row layout), tokens past the
-        // end zero; then its transpose.
-        const rsrc_t rv = make_rsrc(v + (size_t(b) * T + t0) * HD + size_t(hh) * D,
-                                    unsigned((size_t(nreal - 1) * HD + D) * 2));
-        const rsrc_t rw = make_rsrc(w + (size_t(b) * T + t0) * HD + size_t(hh) * D,
-                                    unsigned((size_t(nreal - 1) * HD + D) * 4));
         const f4 unit = F::unit(x, G);
-        for (int u = wave; u < NB * NCT; u += NW) {
-            const int L = u / NCT, c = u % NCT;
-            const unsigned off = unsigned(16 * L + x) * unsigned(HD) + unsigned(16 * c + 4 * G);
-            const u16x4_t vv = Row4<bf16_t>::load(rv, off * 2u, 0u);
-            const f32x4_t wv = buf_load_f4(rw, off * 4u, 0u);
+#pragma unroll
+        for (int k = 0; k < NU1; ++k) {
+            const int u = wave + NW * k, L = u / NCT, c = u % NCT;
             f32x4_t p;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = wv[r] * bf16_to_f32(vv[r]);
+            for (int r = 0; r < 4; ++r) p[r] = wv[k][r] * bf16_to_f32(vv[k][r]);
             reinterpret_cast<f4 *>(b2(L >> 1, c) + lane)[L & 1] = F::pack(F::mma16_fresh(F::pack(p), unit));
         }
-        // e * (K*gamma): one fragment gives both 16-channel halves of a channel group.
-        for (int u = wave; u < NB * NKD; u += NW) {
-            const int L = u / NKD, kk = u % NKD;
-            const f8 kg = F::load8(gKg + frag_idx(16 * L, 32 * kk, D) + lo_frag);
+#pragma unroll
+        for (int k = 0; k < NU2; ++k) {
+            const int u = wave + NW * k, L = u / NKD, kk = u % NKD;
             const f32x4_t ev = *reinterpret_cast<const f32x4_t *>(sh_e + 16 * L + 4 * G);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const f32x4_t t = F::mma16_fresh(hf ? F::hi(kg) : F::lo(kg), unit);
+                const f32x4_t t = F::mma16_fresh(hf ? F::hi(kg[k]) : F::lo(kg[k]), unit);
                 reinterpret_cast<f4 *>(b1(L >> 1, 2 * kk + hf) + lane)[L & 1] = F::pack(t * ev);
             }
         }
@@ -374,6 +418,8 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
     lds_barrier();
 
     // ---- 2: W = T e*Kg and U~ = T w*v per token block ----
+    f8 kbt[NP];
+    f8 ppr[BD::NPW][maxm(BD::NPW - 1)];
     {
         f32x4_t aw[BD::NPW][NCT], au[BD::NPW][NCT];
 #pragma unroll
@@ -381,19 +427,32 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
 #pragma unroll
             for (int c = 0; c < NCT; ++c) aw[k][c] = au[k][c] = zero4();
         if (BD::active(wave)) {
-#pragma unroll
-            for (int k = 0; k < BD::NPW; ++k) {
+            static_for<BD::NPW>([&](auto Kc) {
+                constexpr int k = decltype(Kc)::value;
                 const int i = BD::block(wave, k);
-                for (int m = 0; m <= i / 2; ++m) {
-                    const f8 tp = pair(gT, i, m);
+#pragma unroll
+                for (int m = 0; m < maxm(k); ++m) {
+                    if (m > i / 2) continue;
 #pragma unroll
                     for (int c = 0; c < NCT; ++c) {
-                        aw[k][c] = F::mma8(tp, b1(m, c)[lane], aw[k][c]);
-                        au[k][c] = F::mma8(tp, b2(m, c)[lane], au[k][c]);
+                        aw[k][c] = F::mma8(tpr[k][m], b1(m, c)[lane], aw[k][c]);
+                        au[k][c] = F::mma8(tpr[k][m], b2(m, c)[lane], au[k][c]);
                     }
                 }
-            }
+            });
         }
+        // Phase 3's operands, in flight over the barriers below.
+        {
+            const int c = wave < NCT ? wave : 0;
+#pragma unroll
+            for (int q = 0; q < NP; ++q) kbt[q] = F::load8(gKbT + frag_idx(16 * c, 32 * q, C) + lo_frag);
+        }
+        static_for<BD::NPW>([&](auto Kc) {
+            constexpr int k = decltype(Kc)::value;
+            const int i = BD::block(wave, k);
+#pragma unroll
+            for (int m = 0; m < maxm(k); ++m) ppr[k][m] = pair(gP, i, min(m, i / 2));
+        });
         lds_barrier();
         if (BD::active(wave)) {
 #pragma unroll
@@ -415,14 +474,14 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
         f32x4_t at[NCT], bc[NCT];
 #pragma unroll
         for (int j = 0; j < NCT; ++j) at[j] = bc[j] = zero4();
-        for (int p = 0; p < NP; ++p) {
-            const f8 kb = F::load8(gKbT + frag_idx(16 * c, 32 * p, C) + lo_frag);
-            const float pcol = sh_pp[p * D + 16 * c + x];  // A~^T: column = channel 16c + x
-            const f32x4_t prow = *reinterpret_cast<const f32x4_t *>(sh_pp + p * D + 16 * c + 4 * G);
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const float pcol = sh_pp[q * D + 16 * c + x];  // A~^T: column = channel 16c + x
+            const f32x4_t prow = *reinterpret_cast<const f32x4_t *>(sh_pp + q * D + 16 * c + 4 * G);
 #pragma unroll
             for (int j = 0; j < NCT; ++j) {
-                at[j] = F::mma8(b1(p, j)[lane], kb, at[j] * pcol);  // rows j (W), columns i
-                bc[j] = F::mma8(kb, b2(p, j)[lane], bc[j] * prow);  // rows i, columns value j
+                at[j] = F::mma8(b1(q, j)[lane], kbt[q], at[j] * pcol);  // rows j (W), columns i
+                bc[j] = F::mma8(kbt[q], b2(q, j)[lane], bc[j] * prow);  // rows i, columns value j
             }
         }
         bf16_t *gAT = reinterpret_cast<bf16_t *>(xslot + XS::AT_OFF);
@@ -439,35 +498,38 @@ __global__ __launch_bounds__(512) void wy_precompute_kernel(
     if (BD::active(wave)) {
         bf16_t *gQT = reinterpret_cast<bf16_t *>(xslot + XS::QT_OFF);
         bf16_t *gOT = reinterpret_cast<bf16_t *>(xslot + XS::OT_OFF);
-#pragma unroll
-        for (int k = 0; k < BD::NPW; ++k) {
+        static_for<BD::NPW>([&](auto Kc) {
+            constexpr int k = decltype(Kc)::value;
             const int i = BD::block(wave, k);
+            f8 qg[NKD];
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) qg[kk] = F::load8(gQg + frag_idx(16 * i, 32 * kk, D) + lo_frag);
             f32x4_t pw[NCT], ou[NCT];
 #pragma unroll
             for (int j = 0; j < NCT; ++j) pw[j] = ou[j] = zero4();
-            for (int m = 0; m <= i / 2; ++m) {
-                const f8 pp = pair(gP, i, m);
+#pragma unroll
+            for (int m = 0; m < maxm(k); ++m) {
+                if (m > i / 2) continue;
 #pragma unroll
                 for (int j = 0; j < NCT; ++j) {
-                    pw[j] = F::mma8(b1(m, j)[lane], pp, pw[j]);  // (P W)^T: lane (t, G) row t
-                    ou[j] = F::mma8(pp, b2(m, j)[lane], ou[j]);  // P U~: accumulator layout
+                    pw[j] = F::mma8(b1(m, j)[lane], ppr[k][m], pw[j]);  // (P W)^T: lane (t, G) row t
+                    ou[j] = F::mma8(ppr[k][m], b2(m, j)[lane], ou[j]);  // P U~: accumulator layout
                 }
             }
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
                 const size_t fo = frag_idx(16 * i, 32 * kk, D) + lo_frag;
-                const f8 qg = F::load8(gQg + fo);
                 f32x4_t lo, hi;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    lo[r] = bf16_to_f32(qg[r]) - pw[2 * kk][r];
-                    hi[r] = bf16_to_f32(qg[4 + r]) - pw[2 * kk + 1][r];
+                    lo[r] = bf16_to_f32(qg[kk][r]) - pw[2 * kk][r];
+                    hi[r] = bf16_to_f32(qg[kk][4 + r]) - pw[2 * kk + 1][r];
                 }
                 *reinterpret_cast<f8 *>(gQT + fo) = F::cat(F::pack(lo), F::pack(hi));
             }
 #pragma unroll
             for (int j = 0; j < NCT; ++j) *reinterpret_cast<f4 *>(gOT + ((i * NCT + j) * 64 + lane) * 4) = F::pack(ou[j]);
-        }
+        });
     }
 }
 
