@@ -447,7 +447,9 @@ __global__ __launch_bounds__(4 * D) void chunk_prepare_bf16_kernel(
     f32x4_t *sh_dg = reinterpret_cast<f32x4_t *>(smem + LY::DG_OFF);
 
     const int ci = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // The wavefront index is made visibly uniform: the row offsets of the buffer loads derive
+    // from it and must be scalar (else every load becomes a loop over lanes' offsets).
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int hb = wave / NG, cg = wave % NG;  // block of the pair, channel group
     const int G = lane >> 4, t = lane & 15;
     const int pos0 = 32 * cg + 8 * G;          // operand positions of the thread
