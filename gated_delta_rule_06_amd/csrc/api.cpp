@@ -213,7 +213,8 @@ muir_status_t chunk_scan_impl(const ChunkCall &c, muir_stream_t stream) {
     if (c.T == 0 && !c.s_out) return ok();
     return check_hip(muir::launch_chunk_scan(c.v, c.e, c.w, c.og, c.s0, c.o, c.s_out, c.B, c.T,
                                              c.H, c.dk, c.chunk, c.qkv == MUIR_BF16,
-                                             c.workspace, static_cast<hipStream_t>(stream)),
+                                             const_cast<void *>(c.workspace),
+                                             static_cast<hipStream_t>(stream)),
                      c.fn);
 }
 
@@ -303,7 +304,7 @@ muir_status_t muir_chunk_fwd_prepare(const void *q, const void *k, const float *
 
 muir_status_t muir_chunk_fwd_scan(const void *v, const float *e, const float *w, const float *s0,
                                   void *o, float *s_out, int B, int T, int H, int dk, int dv,
-                                  int chunk, muir_dtype_t qkv, const void *workspace,
+                                  int chunk, muir_dtype_t qkv, void *workspace,
                                   size_t workspace_bytes, muir_stream_t stream) {
     return chunk_scan_impl(ChunkCall{"chunk_fwd_scan", nullptr, nullptr, v, nullptr, nullptr, e,
                                      w, nullptr, nullptr, s0, o, s_out, B, T, H, dk, dv, chunk,
@@ -314,7 +315,7 @@ muir_status_t muir_chunk_fwd_scan(const void *v, const float *e, const float *w,
 muir_status_t muir_chunk_fwd_scan_gated(const void *v, const float *e, const float *w,
                                         const float *og, const float *s0, void *o, float *s_out,
                                         int B, int T, int H, int dk, int dv, int chunk,
-                                        muir_dtype_t qkv, const void *workspace,
+                                        muir_dtype_t qkv, void *workspace,
                                         size_t workspace_bytes, muir_stream_t stream) {
     return chunk_scan_impl(ChunkCall{"chunk_fwd_scan_gated", nullptr, nullptr, v, nullptr,
                                      nullptr, e, w, og, nullptr, s0, o, s_out, B, T, H, dk, dv,
@@ -690,7 +691,7 @@ muir_status_t muir_chunk_bwd(const void *q, const void *k, const void *v, const 
         return fail(MUIR_ERR_UNSUPPORTED, "%s: T*H*d*4 = %zu bytes exceeds 4 GiB", fn, head_span);
     const size_t need = muir::chunk_bwd_workspace_bytes(B, T, H, d, qkv == MUIR_BF16);
     if (need == 0) return fail(MUIR_ERR_SHAPE, "%s: workspace size overflows", fn);
-    if (muir::chunk_workspace_bytes(B, T, H, d, 64, qkv == MUIR_BF16) /
+    if (muir::chunk_slots_bytes(B, T, H, d, 64, qkv == MUIR_BF16) /
             (static_cast<size_t>(B) * H) > 0xffffffffu)
         return fail(MUIR_ERR_UNSUPPORTED, "%s: the forward workspace of one head exceeds 4 GiB",
                     fn);

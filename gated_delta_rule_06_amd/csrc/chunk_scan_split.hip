@@ -21,8 +21,14 @@
 //   state (wave 2)   the state carry in Horner form, one leaf pair at a time as soon as its
 //                    U is in LDS: S <- Diag(pair decay) S + (K*beta')^T U, and at each chunk
 //                    start the state's bf16 operand copy for the helper and the readout.
-//   readout (wave 3) O = (Qh*gamma) S0 + P U of the chunk before, one leaf per phase, and the
-//                    staging of the next chunk's pair decays and diagonal blocks into LDS.
+//   hand-over (wave 3) U of the chunk before, one leaf pair per phase, into the readout
+//                    region of the workspace (the state wavefront puts each chunk's S0
+//                    there), for the readout kernel below.
+//
+// The readout O = (Qh*gamma) S0 + P U needs nothing from the next chunk, and inside the scan
+// its operand loads (Qh*gamma and P, the same for all of a head's workgroups) compete with the
+// chain's for the compute unit's load path; as a kernel of its own it runs over all chunks at
+// once, at the rate of its memory traffic.
 //
 // Which leaf pairs go where: the chain multiplies the pair that holds leaf L - 1 (for odd L
 // that is leaf L - 1 and the zero diagonal block), and for odd L also the pair before, into
@@ -55,12 +61,11 @@ constexpr int help_pairs(int L) { return L < 2 ? 0 : (L - 2 - (L & 1)) / 2; }
 // The pair of row L >= 1 holding leaf L - 1 (for odd L, leaf L - 1 and the zero diagonal).
 constexpr int ser_pair(int L) { return (L - 1) / 2; }
 
-template <int D, int C, bool GATED, int VC>
+template <int D, int C, int VC>
 __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     const bf16_t *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
-    const float *__restrict__ og, const float *__restrict__ s0, bf16_t *__restrict__ o,
-    float *__restrict__ s_out, const unsigned char *__restrict__ ws, int T, int H, int BH,
-    int nchunks) {
+    const float *__restrict__ s0, float *__restrict__ s_out, const unsigned char *__restrict__ ws,
+    unsigned char *__restrict__ rd, int T, int H, int BH, int nchunks) {
     using SL = Slot<bf16_t, D, C>;
     using F = Frag<bf16_t>;
     using f4 = F::f4;
@@ -134,53 +139,31 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     auto u_put = [&](int buf, int L, f4 u) {
         reinterpret_cast<f4 *>(&sh_U[buf][L >> 1][lane])[L & 1] = u;
     };
+    // The readout region of this head's 16-column tile ct / 2: fragment row x + 2 (ct % 2)
+    // holds what lane row x holds here (lanes with x % 4 >= 2 hold padding and store nothing).
+    constexpr size_t TB = readout_tile_bytes(D, C), RCB = readout_chunk_bytes(D, C);
+    const rsrc_t rrd = make_rsrc(rd + size_t(bh) * nchunks * RCB + size_t(ct >> 1) * TB,
+                                 unsigned(size_t(nchunks) * RCB - size_t(ct >> 1) * TB));
+    const unsigned lo_rd = unsigned(16 * (16 * g + x + 2 * (ct & 1)));
+    auto rd_put = [&](int ci, int frag, f8 val) {
+        if (col_ok)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rrd, int(lo_rd),
+                                                   int(size_t(ci) * RCB + size_t(frag) * 1024), 0);
+    };
 
     // ------------------------------------------------------------------------------------
     if (wave == 3) {
-        // Readout of the chunk before.
-        const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * 2u);
-        const rsrc_t rog = make_rsrc(GATED ? og + tok0 : nullptr, GATED ? tok_elems * 4u : 0u);
-        struct RWin {
-            f8 qg[NKD];
-            f8 pq[NB / 2];
-            f32x4_t og;
-        };
-        auto load_rwin = [&](int ci, int L, RWin &wn) {
-            load_kg(ci, L, SL::QG_OFF, wn.qg);
-#pragma unroll
-            for (int j = 0; j <= L / 2; ++j) wn.pq[j] = load_pair(ci, SL::P_OFF, L, j);
-            if constexpr (GATED) wn.og = buf_load_fn<VC>(rog, lo_f, trow(ci * C + 16 * L, 4u));
-        };
-        // No leaf phase holds a runtime branch: at a join, the wait-count pass waits for every
-        // load in flight, prefetches included. Each leaf's operands load RR - 1 phases ahead,
-        // the first leaves' in phase Z1.
-        constexpr int RR = 4;
+        // Hands U of the chunk before to the readout region, one leaf pair per phase (the
+        // chain fills the other parity's buffer meanwhile).
         lds_barrier();
-        RWin rw[RR];
-        f4 fS[NCT];
-        // Iteration 0: no chunk to read out yet.
-        for (int k = 0; k < NB + 2; ++k) lds_barrier();
+        for (int k = 0; k < NB + 2; ++k) lds_barrier();  // iteration 0: no chunk solved yet
         for (int c = 1; c <= nchunks; ++c) {
-            const int cr = c - 1;  // chunk read out in this iteration
-#pragma unroll
-            for (int t = 0; t < NCT; ++t) fS[t] = sh_fS[cr & 1][t][lane];
-            static_for<RR - 1>([&](auto Ic) {
-                constexpr int L = decltype(Ic)::value;
-                if constexpr (L < NB) load_rwin(cr, L, rw[L % RR]);
-            });
+            const int cr = c - 1;
             lds_barrier();  // phase Z1
             lds_barrier();  // phase Z2
             static_for<NB>([&](auto Lc) {
                 constexpr int L = decltype(Lc)::value;
-                if constexpr (L + RR - 1 < NB) load_rwin(cr, L + RR - 1, rw[(L + RR - 1) % RR]);
-                RWin &cw = rw[L % RR];
-                f32x4_t ro = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) ro = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.qg[kk], ro);
-#pragma unroll
-                for (int j = 0; j <= L / 2; ++j) ro = F::mma8(sh_U[cr & 1][j][lane], cw.pq[j], ro);
-                if constexpr (GATED) ro *= cw.og;
-                RowV<bf16_t, VC>::store(ro_, lo_q, trow(cr * C + 16 * L, 2u), ro);
+                if constexpr (L < NP) rd_put(cr, NKD + L, sh_U[cr & 1][L][lane]);
                 lds_barrier();  // end of leaf phase L
             });
         }
@@ -257,8 +240,14 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                 if constexpr (L < NB) load_half(c, L, kbt[L % RS]);
             });
             if (c >= 1) carry_last(c - 1);
+            f4 pk[NCT];
 #pragma unroll
-            for (int t = 0; t < NCT; ++t) sh_fS[c & 1][t][lane] = F::pack(S[t]);
+            for (int t = 0; t < NCT; ++t) {
+                pk[t] = F::pack(S[t]);
+                sh_fS[c & 1][t][lane] = pk[t];
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) rd_put(c, kk, F::cat(pk[2 * kk], pk[2 * kk + 1]));
             lds_barrier();  // phase Z1
             lds_barrier();  // phase Z2
             static_for<NB>([&](auto Lc) {
@@ -465,15 +454,135 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     for (int k = 0; k < NB + 2; ++k) lds_barrier();  // the iteration after the last chunk
 }
 
-}  // namespace
+// The readout of the split scan, O = (Qh*gamma) S0 + P U and the output gate, for every chunk
+// at once. One workgroup per (batch*head, chunk, half of the value columns) stages the S0 and
+// U fragments of its value tiles from the readout region into LDS; each of its four
+// wavefronts then takes a quarter of the chunk's leaves (mirrored, so that every wavefront
+// has about the same number of P blocks), loads each leaf's Qh*gamma and P operands once and
+// applies them to every tile. Each output element takes the same products in the same order
+// as the in-scan readout of the other scan (S0 first, then the leaf pairs in order), so the
+// two give the same bits.
+template <int D, int C, bool GATED>
+__global__ __launch_bounds__(256) void chunk_readout_kernel(
+    const float *__restrict__ og, bf16_t *__restrict__ o, const unsigned char *__restrict__ ws,
+    const unsigned char *__restrict__ rd, int T, int H, int BH, int nchunks) {
+    using SL = Slot<bf16_t, D, C>;
+    using F = Frag<bf16_t>;
+    using f8 = F::f8;
+    constexpr int NB = C / 16, NKD = D / 32, NP = NB / 2;
+    constexpr int NF = NKD + NP;   // fragments per 16-column tile
+    constexpr int NQ = D / 32;     // tiles per workgroup (half of the head's D / 16)
+    constexpr int NLW = NB / 4;    // leaves per wavefront
+    constexpr unsigned OB = 2;
+    constexpr size_t TB = readout_tile_bytes(D, C), RCB = readout_chunk_bytes(D, C);
+    static_assert(TB == size_t(NF) * 1024 && (NQ * NF) % 4 == 0, "readout layout");
+    __shared__ f8 sh[NQ * NF][64];
 
-// Whether the split scan runs: bf16 operands with at most one 8-column workgroup per compute
-// unit (the 1.34B-class long-context shape), where a leaf's serial path sets the time.
-bool scan_split_applies(int B, int H, int d) { return size_t(B) * H * (d / 8) <= 256; }
+    // Workgroups go to the eight XCDs round-robin: ids 16n + x and 16n + 8 + x, the two halves
+    // of one (batch*head, chunk), share XCD x and so the L2 that serves both their Qh*gamma and
+    // P loads.
+    const int id = blockIdx.x;
+    const int hf = (id >> 3) & 1;
+    const int unit = (id >> 4) * 8 + (id & 7);
+    if (unit >= BH * nchunks) return;  // the whole workgroup, before any barrier
+    const int bh = unit / nchunks, c = unit % nchunks;
+    const int b = bh / H, h = bh % H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+    const size_t HD = size_t(H) * D;
+    const size_t ci = size_t(bh) * nchunks + c;
+    const rsrc_t rws = make_rsrc(ws + ci * SL::BYTES, unsigned(SL::BYTES));
+    const rsrc_t rrd = make_rsrc(rd + ci * RCB + size_t(hf) * NQ * TB, unsigned(NQ * TB));
+#pragma unroll
+    for (int n = 0; n < NQ * NF / 4; ++n) {
+        const int f = n * 4 + wave;
+        sh[f][lane] = F::bload8(rrd, unsigned(lane * 16), unsigned(f * 1024));
+    }
+    __syncthreads();
+
+    // This head's tokens, from column 0; rows at or past T read zero, stores there are dropped.
+    // Output lane (token x, group g) of tile p holds its rows 4g + i: columns 16p + 2g + i
+    // (i < 2) and 16p + 8 + 2g + (i - 2) (i >= 2).
+    const size_t tok0 = size_t(b) * T * HD + size_t(h) * D;
+    const unsigned tok_elems = unsigned(size_t(T) * HD - size_t(h) * D);
+    const rsrc_t ro_ = make_rsrc(o + tok0, tok_elems * 2u);
+    const rsrc_t rog = make_rsrc(GATED ? og + tok0 : nullptr, GATED ? tok_elems * 4u : 0u);
+    const unsigned lo_x = unsigned(x * HD + 2 * g);
+    auto trow = [&](int t, unsigned es) { return unsigned(min(t, T)) * unsigned(HD) * es; };
+    const unsigned lo_frag = unsigned(lane * 8) * OB;
+    const unsigned lo_pair = unsigned((4 * x + g) * 8) * OB;
+
+    struct Win {
+        f8 qg[NKD];
+        f8 pq[NP];
+        f32x2_t oa[NQ], ob[NQ];  // output gate (GATED)
+    };
+    // Wavefront W takes leaves 4m + W (m even) and 4m + 3 - W (m odd). Its code is made for
+    // its own leaves, so that no loop bound or load is a runtime branch (at a join the
+    // wait-count pass would wait for every load in flight, the prefetches included).
+    auto body = [&](auto Wc) {
+        constexpr int W = decltype(Wc)::value;
+        auto load_win = [&](auto Lc, Win &wn) {
+            constexpr int L = decltype(Lc)::value;
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+                wn.qg[kk] = F::bload8(rws, lo_frag, unsigned(SL::QG_OFF + frag_idx(16 * L, 32 * kk, D) * OB));
+#pragma unroll
+            for (int j = 0; j <= L / 2; ++j)
+                wn.pq[j] = F::bload8(rws, lo_pair, unsigned(SL::P_OFF + size_t(SL::prow(L) + j) * 512 * OB));
+            if constexpr (GATED) {
+                const unsigned row = trow(c * C + 16 * L, 4u);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const unsigned col = unsigned(16 * (hf * NQ + q));
+                    wn.oa[q] = __builtin_bit_cast(f32x2_t, buf_load8(rog, (lo_x + col) * 4u, row));
+                    wn.ob[q] = __builtin_bit_cast(f32x2_t, buf_load8(rog, (lo_x + col + 8u) * 4u, row));
+                }
+            }
+        };
+        constexpr auto leaf = [](int m) { return (m & 1) ? 4 * m + 3 - W : 4 * m + W; };
+        Win win[2];
+        load_win(std::integral_constant<int, leaf(0)>{}, win[0]);
+        static_for<NLW>([&](auto Mc) {
+            constexpr int m = decltype(Mc)::value;
+            constexpr int L = leaf(m);
+            if constexpr (m + 1 < NLW) load_win(std::integral_constant<int, leaf(m + 1)>{}, win[(m + 1) & 1]);
+            const Win &cw = win[m & 1];
+            const unsigned row = trow(c * C + 16 * L, 1u);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const unsigned col = unsigned(16 * (hf * NQ + q));
+                f32x4_t ro = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) ro = F::mma8(sh[q * NF + kk][lane], cw.qg[kk], ro);
+#pragma unroll
+                for (int j = 0; j <= L / 2; ++j) ro = F::mma8(sh[q * NF + NKD + j][lane], cw.pq[j], ro);
+                f32x4_t va = {ro[0], ro[1], 0.f, 0.f}, vb = {ro[2], ro[3], 0.f, 0.f};
+                if constexpr (GATED) {
+                    va *= f32x4_t{cw.oa[q][0], cw.oa[q][1], 0.f, 0.f};
+                    vb *= f32x4_t{cw.ob[q][0], cw.ob[q][1], 0.f, 0.f};
+                }
+                RowV<bf16_t, 2>::store(ro_, (lo_x + col) * 2u, row * 2u, va);
+                RowV<bf16_t, 2>::store(ro_, (lo_x + col + 8u) * 2u, row * 2u, vb);
+                // One tile's LDS operands in registers at a time: without this the scheduler
+                // hoists every tile's reads and runs out of registers.
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+    switch (wave) {
+        case 0: body(std::integral_constant<int, 0>{}); break;
+        case 1: body(std::integral_constant<int, 1>{}); break;
+        case 2: body(std::integral_constant<int, 2>{}); break;
+        default: body(std::integral_constant<int, 3>{}); break;
+    }
+}
+
+}  // namespace
 
 hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
                                    const float *s0, void *o, float *s_out, int B, int T, int H,
-                                   int d, int chunk, const void *workspace, hipStream_t stream) {
+                                   int d, int chunk, void *workspace, hipStream_t stream) {
     const int nchunks = (T + chunk - 1) / chunk;
     const int BH = B * H;
     const int groups = (BH + 7) / 8;
@@ -481,20 +590,27 @@ hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w
     // chain's substitution then having twice the steps' instructions.
     constexpr int VC = 2;
     const dim3 block(256);
-    auto run = [&](auto dc, auto cc, auto gated) {
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    unsigned char *rd = ws + chunk_slots_bytes(B, T, H, d, chunk, true);
+    auto run = [&](auto dc, auto cc) {
         constexpr int D = decltype(dc)::value, C = decltype(cc)::value;
-        constexpr bool G = decltype(gated)::value;
         const dim3 grid(groups * 8 * (D / (4 * VC)));
-        hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, G, VC>), grid, block, 0, stream,
-                           static_cast<const bf16_t *>(v), e, w, og, s0, static_cast<bf16_t *>(o),
-                           s_out, static_cast<const unsigned char *>(workspace), T, H, BH, nchunks);
+        hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, VC>), grid, block, 0, stream,
+                           static_cast<const bf16_t *>(v), e, w, s0, s_out, ws, rd, T, H, BH,
+                           nchunks);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess || nchunks == 0) return err;
+        const dim3 rgrid(unsigned((size_t(BH) * nchunks + 7) / 8 * 16));
+        if (og)
+            hipLaunchKernelGGL((chunk_readout_kernel<D, C, true>), rgrid, block, 0, stream, og,
+                               static_cast<bf16_t *>(o), ws, rd, T, H, BH, nchunks);
+        else
+            hipLaunchKernelGGL((chunk_readout_kernel<D, C, false>), rgrid, block, 0, stream, og,
+                               static_cast<bf16_t *>(o), ws, rd, T, H, BH, nchunks);
         return hipGetLastError();
     };
-    auto by_gate = [&](auto dc, auto cc) {
-        return og ? run(dc, cc, std::true_type{}) : run(dc, cc, std::false_type{});
-    };
 #define MUIR_SPLIT(D, C) \
-    if (d == D && chunk == C) return by_gate(std::integral_constant<int, D>{}, std::integral_constant<int, C>{});
+    if (d == D && chunk == C) return run(std::integral_constant<int, D>{}, std::integral_constant<int, C>{});
     MUIR_SPLIT(64, 64) MUIR_SPLIT(64, 128) MUIR_SPLIT(64, 256)
     MUIR_SPLIT(128, 64) MUIR_SPLIT(128, 128) MUIR_SPLIT(128, 256)
 #undef MUIR_SPLIT

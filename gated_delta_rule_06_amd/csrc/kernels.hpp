@@ -12,8 +12,11 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
                               float *state, void *o, int B, int H, int d, bool bf16,
                               hipStream_t stream);
 
-// Bytes of the chunk-forward workspace for these sizes (0 when they overflow).
+// Bytes of the chunk-forward workspace for these sizes (0 when they overflow): the slots the
+// prepare writes and, where the split scan runs, its readout region after them.
 size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16);
+// Bytes of the slots alone (what a scan that reads nothing out needs).
+size_t chunk_slots_bytes(int B, int T, int H, int d, int chunk, bool bf16);
 
 // Phase P: decay products, pivoted operands and intra-chunk Gram blocks -> workspace.
 hipError_t launch_chunk_prepare(const void *q, const void *k, const float *a, const float *g,
@@ -36,18 +39,20 @@ hipError_t launch_chunk_prepare_lowrank(const void *q, const void *k, const void
                                         int d, int chunk, void *workspace, hipStream_t stream);
 
 // Phase S: sequential chunk scan (solve, readout, state carry) from the workspace. A
-// non-null og applies the output-gate epilogue o <- o * og.
+// non-null og applies the output-gate epilogue o <- o * og. The slots are only read; where
+// the split scan runs it writes the readout region after them.
 hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
-                             int chunk, bool bf16, const void *workspace, hipStream_t stream);
+                             int chunk, bool bf16, void *workspace, hipStream_t stream);
 
-// Phase S for bf16 operands split over four wavefronts per workgroup (chain, right-hand
-// side, state carry, readout); runs where scan_split_applies holds (at most one 8-column
-// workgroup per compute unit). Same results as launch_chunk_scan, bit for bit.
-bool scan_split_applies(int B, int H, int d);
+// Phase S for bf16 operands where split_scan_applies holds (at most one 8-column workgroup
+// per compute unit): the sequential part split over four wavefronts per workgroup (chain,
+// right-hand side, state carry, hand-over of S0 and U to the readout region), then the
+// readout O = (Qh*gamma) S0 + P U (and the output gate) as a parallel kernel over chunks.
+// Same results as the other scan, bit for bit.
 hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
                                    const float *s0, void *o, float *s_out, int B, int T, int H,
-                                   int d, int chunk, const void *workspace, hipStream_t stream);
+                                   int d, int chunk, void *workspace, hipStream_t stream);
 
 // Phase S for the backward pass: keeps u_out [B, T, H, d] fp32 (u = w * v - e * p of every
 // token) and states [B * H][ceil(T / 64) + 1][d][d] fp32 (the state at every 64-token block

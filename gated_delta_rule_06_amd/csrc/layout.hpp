@@ -43,6 +43,20 @@ template <int OB, int D, int C> struct SlotLayout {
     }
 };
 
+// The split scan (bf16 operands, at most one 8-column scan workgroup per compute unit, so
+// B * H * d / 8 <= 256) leaves the readout to a kernel of its own. It hands over, in a region
+// after the slots, per (batch, head, chunk) and per 16-column value tile:
+//   S0: the chunk's start state as d/32 K = 32 operand fragments (rows = the tile's value
+//       columns, contraction = channels), [d/32][64 lanes][8] bf16;
+//   U:  the chunk's solved values as C/32 leaf-pair fragments (rows = value columns,
+//       contraction = the pair's 32 tokens), [C/32][64 lanes][8] bf16.
+// Fragment lane 16 G + x holds row x: value column 2 (x / 4) + (x % 4) of the tile's first
+// eight for x % 4 < 2, column 8 + 2 (x / 4) + (x % 4 - 2) for x % 4 >= 2 (the two 8-column scan
+// tiles of a 16-column tile each fill half of the rows).
+constexpr bool split_scan_applies(int B, int H, int d) { return size_t(B) * H * (d / 8) <= 256; }
+constexpr size_t readout_tile_bytes(int d, int chunk) { return size_t(d / 32 + chunk / 32) * 1024; }
+constexpr size_t readout_chunk_bytes(int d, int chunk) { return size_t(d / 16) * readout_tile_bytes(d, chunk); }
+
 // Per (batch, head, chunk) products of the shared-erase form, kept in a workspace region
 // after the prepare kernel's slots (same (b, h, chunk) order). With W = T Diag(e) (K*gamma)
 // and U~ = T (w*v) (never stored):

@@ -28,13 +28,23 @@ size_t wy_bytes() { return SlotLayout<2, D, C>::BYTES + XSlot<D, C>::BYTES; }
 
 }  // namespace
 
-size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
+size_t chunk_slots_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
     const size_t slot = slot_bytes_rt(bf16, d, chunk);
     if (slot == 0 || B < 1 || H < 1 || T < 0) return 0;
     const size_t nchunks = (size_t(T) + chunk - 1) / chunk;
     const size_t n = size_t(B) * size_t(H) * nchunks;
     if (n != 0 && slot > SIZE_MAX / n) return 0;
     return n * slot;
+}
+
+size_t chunk_workspace_bytes(int B, int T, int H, int d, int chunk, bool bf16) {
+    const size_t slots = chunk_slots_bytes(B, T, H, d, chunk, bf16);
+    if (slots == 0 || !bf16 || !split_scan_applies(B, H, d)) return slots;
+    // The split scan's readout region (bf16 only), after the slots (a multiple of 256 bytes).
+    const size_t n = size_t(B) * size_t(H) * ((size_t(T) + chunk - 1) / chunk);
+    const size_t per = readout_chunk_bytes(d, chunk);
+    if (per > (SIZE_MAX - slots) / n) return 0;
+    return slots + n * per;
 }
 
 size_t wy_workspace_bytes(int B, int T, int H, int d, int chunk) {
@@ -55,7 +65,7 @@ int bwd_fwd_chunk(int, int T, int, int) { return T >= 256 ? 128 : kBwdChunk; }
 
 bool bwd_layout(int B, int T, int H, int d, bool bf16, BwdLayout &L) {
     constexpr int kC = kBwdChunk;
-    const size_t fwd = chunk_workspace_bytes(B, T, H, d, bwd_fwd_chunk(B, T, H, d), bf16);
+    const size_t fwd = chunk_slots_bytes(B, T, H, d, bwd_fwd_chunk(B, T, H, d), bf16);
     if (fwd == 0 && T > 0) return false;
     const size_t nc = (size_t(T) + kC - 1) / kC;
     const size_t BH = size_t(B) * H, tok = size_t(B) * T * H * d;

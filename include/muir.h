@@ -159,9 +159,12 @@ size_t muir_chunk_fwd_noalloc_max_workspace(void);
  *   block-Neumann solve of every value column's triangular system, the readout
  *   o = (r*g*q*gamma) S0 + P U and the state carry S = Diag(gamma_C) S0 + (K*beta)^T U,
  *   evaluated pair by pair as S <- Diag(pair decay) S + (K*beta')^T U.
- *   Reads `workspace` as left by muir_chunk_fwd_prepare for the same sizes and inputs;
- *   the workspace must not be modified between the two calls. T == 0 copies s0 (or
- *   zeros) into s_out.
+ *   Reads the slots of `workspace` as left by muir_chunk_fwd_prepare for the same sizes
+ *   and inputs; they must not be modified between the two calls. With bf16 q, k, v and
+ *   B*H*dk/8 <= 256 (at most one 8-column scan work item per compute unit) the scan hands
+ *   S0 and U of every chunk to a parallel readout kernel through a region of `workspace`
+ *   after the slots, which it writes (muir_chunk_fwd_workspace_size counts it). T == 0
+ *   copies s0 (or zeros) into s_out.
  *
  * Errors as for muir_chunk_fwd, restricted to the arguments each phase takes.
  */
@@ -173,7 +176,7 @@ muir_status_t muir_chunk_fwd_prepare(
 muir_status_t muir_chunk_fwd_scan(
     const void *v, const float *e, const float *w, const float *s0, void *o, float *s_out,
     int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
-    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
  * The chunk forward with the output-gate epilogue fused into the readout: the stored
@@ -198,7 +201,7 @@ muir_status_t muir_chunk_fwd_gated(
 muir_status_t muir_chunk_fwd_scan_gated(
     const void *v, const float *e, const float *w, const float *og, const float *s0,
     void *o, float *s_out, int B, int T, int H, int dk, int dv, int chunk, muir_dtype_t qkv,
-    const void *workspace, size_t workspace_bytes, muir_stream_t stream);
+    void *workspace, size_t workspace_bytes, muir_stream_t stream);
 
 /*
  * The chunk forward with ONE erase strength per token, shared by every value channel:

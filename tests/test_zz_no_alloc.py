@@ -28,7 +28,7 @@ def _noalloc(t, s0, B, T, H, d, chunk):
 
 def test_noalloc_matches_the_workspace_call_twice(device):
     cases = [
-        # 16 heads x 16 chunks of 256 tokens at d = 128: 89 MiB of the 128 MiB scratch.
+        # 16 heads x 16 chunks of 256 tokens at d = 128: 113 MiB of the 128 MiB scratch.
         dict(cfg=2, B=1, T=4096, H=16, d=128, chunk=256, seed=71, s0=False),
         # Smaller, ragged, with an initial state: runs on the first call's leftovers.
         dict(cfg=1, B=2, T=300, H=3, d=64, chunk=64, seed=72, s0=True),
@@ -53,7 +53,7 @@ def test_noalloc_matches_the_workspace_call_twice(device):
 
 
 def test_noalloc_refuses_sizes_beyond_the_scratch(device):
-    """The long-context shape needs 712 MiB of workspace: refused before any launch."""
+    """The long-context shape needs 904 MiB of workspace: refused before any launch."""
     B, T, H, d = 1, 32768, 16, 128
     v = torch.zeros(1, dtype=torch.bfloat16, device=device)
     p = ctypes.c_void_p(v.data_ptr())
