@@ -17,13 +17,15 @@
 //                    of leaf L + 1 from what the helper left in LDS.
 //   helper (wave 1)  during leaf L, the part of leaf L + 2's right-hand side that does not
 //                    need the last leaves' U: (K*gamma)_{L+2} S0 + sum M_{L+2,l} U_l over the
-//                    leaf pairs l that are solved by then.
+//                    leaf pairs l that are solved by then (the first term from wave 3).
 //   state (wave 2)   the state carry in Horner form, one leaf pair at a time as soon as its
 //                    U is in LDS: S <- Diag(pair decay) S + (K*beta')^T U, and at each chunk
-//                    start the state's bf16 operand copy for the helper and the readout.
-//   hand-over (wave 3) U of the chunk before, one leaf pair per phase, into the readout
-//                    region of the workspace (the state wavefront puts each chunk's S0
-//                    there), for the readout kernel below.
+//                    start the state's bf16 operand copy for the helper (and, through the
+//                    readout region of the workspace, for the readout kernel below).
+//   hand-over (wave 3) H_L = (K*gamma)_L S0 of leaves L >= 2 a phase before the helper
+//                    needs it; U of the chunk before, one leaf pair per phase, into the
+//                    readout region; the staging of the next chunk's pair decays and
+//                    diagonal blocks into LDS and its L2 warm-up.
 //
 // The readout O = (Qh*gamma) S0 + P U needs nothing from the next chunk, and inside the scan
 // its operand loads (Qh*gamma and P, the same for all of a head's workgroups) compete with the
@@ -82,11 +84,14 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     // U of every leaf, by chunk parity, leaves 2j and 2j + 1 of a lane as one K = 32 operand.
     __shared__ f8 sh_U[2][NP][64];
     // Pair decays per channel and the fp32 diagonal blocks of M, by chunk parity (staged by
-    // the readout wavefront one chunk ahead).
+    // the hand-over wavefront one chunk ahead).
     __shared__ __align__(16) float sh_pp[2][NP][D];
     __shared__ __align__(16) f32x4_t sh_md[2][NB][64];
     // acc_pre parts from the helper, a ring over leaves (written two leaves ahead).
     __shared__ __align__(16) f32x4_t sh_acc[4][64];
+    // H_L = (K*gamma)_L S0 of leaves L >= 2 from the hand-over wavefront, a ring over leaves
+    // (written three leaves ahead, one phase before the helper adds the leaf pairs to it).
+    __shared__ __align__(16) f32x4_t sh_h[4][64];
 
     // Workgroups go to the eight XCDs round-robin; a head's value tiles share one XCD.
     constexpr int NVT = D / (4 * VC);
@@ -154,46 +159,8 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     // ------------------------------------------------------------------------------------
     if (wave == 3) {
         // Hands U of the chunk before to the readout region, one leaf pair per phase (the
-        // chain fills the other parity's buffer meanwhile).
-        lds_barrier();
-        for (int k = 0; k < NB + 2; ++k) lds_barrier();  // iteration 0: no chunk solved yet
-        for (int c = 1; c <= nchunks; ++c) {
-            const int cr = c - 1;
-            lds_barrier();  // phase Z1
-            lds_barrier();  // phase Z2
-            static_for<NB>([&](auto Lc) {
-                constexpr int L = decltype(Lc)::value;
-                if constexpr (L < NP) rd_put(cr, NKD + L, sh_U[cr & 1][L][lane]);
-                lds_barrier();  // end of leaf phase L
-            });
-        }
-        return;
-    }
-
-    // ------------------------------------------------------------------------------------
-    if (wave == 2) {
-        // The state: S[t][i] = state[16t + 4g + i][j0 + x], fp32 accumulators, carried in
-        // Horner form over leaf pairs.
-        f32x4_t S[NCT];
-#pragma unroll
-        for (int t = 0; t < NCT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[t][i] = s0h && col_ok ? s0h[size_t(16 * t + i) * D + lo_st] : 0.f;
-        auto load_kbt = [&](int ci, int pair, int t) {
-            return F::bload8(rws, lo_frag, wsoff(ci, SL::KBT_OFF + frag_idx(16 * t, 32 * pair, C) * OB));
-        };
-        auto lds_pp = [&](int ci, int pair, int t) {
-            return *reinterpret_cast<const f32x4_t *>(&sh_pp[ci & 1][pair][16 * t + 4 * g]);
-        };
-        // Tiles of phase L >= 2: pair (L - 2) / 2, tiles (L & 1) * HALF + [0, HALF); loaded RS - 1
-        // phases ahead, those of phases 2 .. RS in phase Z1.
-        constexpr int RS = 4;
-        f8 kbt[RS][HALF], kbtLast[NCT];
-        auto load_half = [&](int ci, int L, f8 (&dst)[HALF]) {
-#pragma unroll
-            for (int t = 0; t < HALF; ++t) dst[t] = load_kbt(ci, (L - 2) / 2, t + (L & 1) * HALF);
-        };
+        // chain fills the other parity's buffer meanwhile), and stages the next chunk's pair
+        // decays and diagonal blocks into LDS.
         constexpr int PP4 = NP * D / 4;
         constexpr int PPN = (PP4 + 63) / 64;
         f32x4_t ppt[PPN], mdt[NB];
@@ -225,14 +192,101 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
             const unsigned off = unsigned(min(line, LINES - 1)) * 128u;
             touched += __builtin_amdgcn_raw_buffer_load_b32(rws, int(off), int(wsoff(ci, 0)), 0);
         };
+        // The next chunk's staging goes to the buffers of the other parity: nobody reads them
+        // during this chunk (the state wavefront's carry of the chunk before's last pair comes
+        // before phase 2). A clamped chunk index past the end reads valid, unused data.
+        auto stage_phase = [&](int cn, auto Lc) {
+            constexpr int L = decltype(Lc)::value;
+            if constexpr (L == 0) load_stage(cn);
+            if constexpr (L == 2) put_stage(cn);
+            if constexpr (L < NTOUCH) touch(cn, L);
+        };
+        // H_L = (K*gamma)_L S0 of leaves 2 .. NB - 1: H_2 in phase Z2, H_{L+3} in leaf phase L,
+        // each from K*gamma rows loaded two phases ahead (leaves 2 .. 4 of the next chunk in
+        // the last phases of a chunk), in a ring over leaves.
+        constexpr int RK = 4;
+        f8 kgr[RK][NKD];
+        f4 fS[NCT];
+        auto h_make = [&](auto Lc) {
+            constexpr int L = decltype(Lc)::value;
+            f32x4_t a = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) a = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), kgr[L % RK][kk], a);
+            sh_h[L & 3][lane] = a;
+        };
+        auto load_next = [&](int cn, auto Lc) {
+            constexpr int L = decltype(Lc)::value;
+            if constexpr (L == (NB > 3 ? NB - 3 : 0)) {
+                if constexpr (2 < NB) load_kg(cn, 2, SL::KG_OFF, kgr[2 % RK]);
+                if constexpr (3 < NB) load_kg(cn, 3, SL::KG_OFF, kgr[3 % RK]);
+            }
+            if constexpr (L == (NB > 3 ? NB - 2 : 0) && 4 < NB) load_kg(cn, 4, SL::KG_OFF, kgr[4 % RK]);
+        };
+        // Iteration k: H of chunk k (WH), U of chunk k - 1 (WU), staging of chunk k + 1.
+        auto iter = [&](int k, auto wh, auto wu) {
+            constexpr bool WH = decltype(wh)::value, WU = decltype(wu)::value;
+            lds_barrier();  // phase Z1: the state wavefront publishes S0
+            if constexpr (WH) {
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) fS[t] = sh_fS[k & 1][t][lane];
+                if constexpr (2 < NB) h_make(std::integral_constant<int, 2>{});
+            }
+            lds_barrier();  // phase Z2
+            static_for<NB>([&](auto Lc) {
+                constexpr int L = decltype(Lc)::value;
+                stage_phase(k + 1, Lc);
+                if constexpr (WU && L < NP) rd_put(k - 1, NKD + L, sh_U[(k - 1) & 1][L][lane]);
+                if constexpr (WH) {
+                    if constexpr (L + 5 < NB) load_kg(k, L + 5, SL::KG_OFF, kgr[(L + 5) % RK]);
+                    if constexpr (L + 3 < NB) h_make(std::integral_constant<int, L + 3>{});
+                    load_next(k + 1, Lc);
+                }
+                lds_barrier();  // end of leaf phase L
+            });
+        };
+        load_stage(0);
+        put_stage(0);
+        load_next(0, std::integral_constant<int, (NB > 3 ? NB - 3 : 0)>{});
+        load_next(0, std::integral_constant<int, (NB > 3 ? NB - 2 : 0)>{});
+        lds_barrier();
+        iter(0, std::true_type{}, std::false_type{});
+        for (int k = 1; k < nchunks; ++k) iter(k, std::true_type{}, std::true_type{});
+        iter(nchunks, std::false_type{}, std::true_type{});
+        // The touched words are not needed; this keeps their loads.
+        asm volatile("" ::"v"(touched));
+        return;
+    }
+
+    // ------------------------------------------------------------------------------------
+    if (wave == 2) {
+        // The state: S[t][i] = state[16t + 4g + i][j0 + x], fp32 accumulators, carried in
+        // Horner form over leaf pairs.
+        f32x4_t S[NCT];
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[t][i] = s0h && col_ok ? s0h[size_t(16 * t + i) * D + lo_st] : 0.f;
+        auto load_kbt = [&](int ci, int pair, int t) {
+            return F::bload8(rws, lo_frag, wsoff(ci, SL::KBT_OFF + frag_idx(16 * t, 32 * pair, C) * OB));
+        };
+        auto lds_pp = [&](int ci, int pair, int t) {
+            return *reinterpret_cast<const f32x4_t *>(&sh_pp[ci & 1][pair][16 * t + 4 * g]);
+        };
+        // Tiles of phase L >= 2: pair (L - 2) / 2, tiles (L & 1) * HALF + [0, HALF); loaded RS - 1
+        // phases ahead, those of phases 2 .. RS in phase Z1.
+        constexpr int RS = 4;
+        f8 kbt[RS][HALF], kbtLast[NCT];
+        auto load_half = [&](int ci, int L, f8 (&dst)[HALF]) {
+#pragma unroll
+            for (int t = 0; t < HALF; ++t) dst[t] = load_kbt(ci, (L - 2) / 2, t + (L & 1) * HALF);
+        };
         // The chunk before's last leaf pair (all tiles), into the state.
         auto carry_last = [&](int cp) {
             const f8 u2 = sh_U[cp & 1][NP - 1][lane];
 #pragma unroll
             for (int t = 0; t < NCT; ++t) S[t] = F::mma8(kbtLast[t], u2, S[t] * lds_pp(cp, NP - 1, t));
         };
-        load_stage(0);
-        put_stage(0);
         lds_barrier();
         for (int c = 0; c < nchunks; ++c) {
             static_for<RS - 1>([&](auto Ic) {
@@ -252,12 +306,6 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
             lds_barrier();  // phase Z2
             static_for<NB>([&](auto Lc) {
                 constexpr int L = decltype(Lc)::value;
-                // The next chunk's pair decays and diagonal blocks into LDS (the buffers of the
-                // other parity: nobody reads them during this chunk); a clamped chunk index
-                // past the end reads valid, unused data.
-                if constexpr (L == 0) load_stage(c + 1);
-                if constexpr (L == 2) put_stage(c + 1);
-                if constexpr (L < NTOUCH) touch(c + 1, L);
                 if constexpr (L >= 2 && L + RS - 1 < NB) load_half(c, L + RS - 1, kbt[(L + RS - 1) % RS]);
                 if constexpr (L == (NB > 4 ? NB - 4 : 1)) {
 #pragma unroll
@@ -284,30 +332,24 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) south[size_t(16 * t + i) * D + lo_st] = S[t][i];
         }
-        // The touched words are not needed; this keeps their loads (T is never negative).
-        if (T < 0 && touched == 0x7fc00001u) south[lane] = 0.f;
         return;
     }
 
     // ------------------------------------------------------------------------------------
     if (wave == 1) {
-        // Helper: during leaf phase L, the part of leaf L + 2's right-hand side from S0 and
-        // from the leaf pairs below help_pairs(L + 2); at phase Z2, leaves 0 and 1 (S0 only).
-        struct HWin {
-            f8 kg[NKD];
-            f8 mp[NP];
-        };
-        auto load_hwin = [&](int ci, auto ltc, HWin &wn) {
+        // Helper: during leaf phase L, leaf L + 2's right-hand side part: H_{L+2} from the
+        // hand-over wavefront plus the leaf pairs below help_pairs(L + 2); at phase Z2, H of
+        // leaves 0 and 1 (S0 only).
+        auto load_mp = [&](int ci, auto ltc, f8 (&dst)[NP]) {
             constexpr int Lt = decltype(ltc)::value;
-            load_kg(ci, Lt, SL::KG_OFF, wn.kg);
 #pragma unroll
-            for (int j = 0; j < help_pairs(Lt); ++j) wn.mp[j] = load_pair(ci, SL::M_OFF, Lt, j);
+            for (int j = 0; j < help_pairs(Lt); ++j) dst[j] = load_pair(ci, SL::M_OFF, Lt, j);
         };
-        // Leaf Lt's operands load RH - 1 phases ahead, those of leaves 2 .. RH in phase Z1;
+        // Leaf Lt's pairs load RH - 1 phases ahead, those of leaves 2 .. RH in phase Z1;
         // kg0, kg1 (leaves 0 and 1 of the next chunk) a few phases before the chunk ends.
         constexpr int RH = 3;
         f8 kg0[NKD], kg1[NKD];
-        HWin hw[RH];
+        f8 mp[RH][NP];
         f4 fS[NCT];
         load_kg(0, 0, SL::KG_OFF, kg0);
         load_kg(0, 1, SL::KG_OFF, kg1);
@@ -315,7 +357,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
         for (int c = 0; c < nchunks; ++c) {
             static_for<RH - 1>([&](auto Ic) {
                 constexpr int Lt = 2 + decltype(Ic)::value;
-                if constexpr (Lt < NB) load_hwin(c, std::integral_constant<int, Lt>{}, hw[Lt % RH]);
+                if constexpr (Lt < NB) load_mp(c, std::integral_constant<int, Lt>{}, mp[Lt % RH]);
             });
             lds_barrier();  // phase Z1: the state wavefront publishes S0
 #pragma unroll
@@ -335,16 +377,13 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                 constexpr int L = decltype(Lc)::value;
                 constexpr int Lt = L + 2;
                 if constexpr (Lt + RH - 1 < NB)
-                    load_hwin(c, std::integral_constant<int, Lt + RH - 1>{}, hw[(Lt + RH - 1) % RH]);
+                    load_mp(c, std::integral_constant<int, Lt + RH - 1>{}, mp[(Lt + RH - 1) % RH]);
                 if constexpr (L == (NB > 4 ? NB - 5 : 0)) load_kg(c + 1, 0, SL::KG_OFF, kg0);
                 if constexpr (L == (NB > 4 ? NB - 4 : 1)) load_kg(c + 1, 1, SL::KG_OFF, kg1);
                 if constexpr (Lt < NB) {
-                    const HWin &cw = hw[Lt % RH];
-                    f32x4_t a = zero4();
+                    f32x4_t a = sh_h[Lt & 3][lane];
 #pragma unroll
-                    for (int kk = 0; kk < NKD; ++kk) a = F::mma8(F::cat(fS[2 * kk], fS[2 * kk + 1]), cw.kg[kk], a);
-#pragma unroll
-                    for (int j = 0; j < help_pairs(Lt); ++j) a = F::mma8(sh_U[c & 1][j][lane], cw.mp[j], a);
+                    for (int j = 0; j < help_pairs(Lt); ++j) a = F::mma8(sh_U[c & 1][j][lane], mp[Lt % RH][j], a);
                     sh_acc[Lt & 3][lane] = a;
                 }
                 lds_barrier();
