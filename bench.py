@@ -104,7 +104,8 @@ def code_sha(*paths):
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` ('prepare' or 'scan') on the long-context workload,
+    """HBM bytes per call of `kernel` ('prepare', or 'scan': the split scan and its readout kernel)
+    on the long-context workload,
     from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/ (scaled by the copy
     calibration recorded there). None when the summary is missing or was taken on
     different code (its code_sha differs from the current source's)."""
@@ -564,7 +565,11 @@ def main():
         dom = "scan" if r["scan_ms"] >= r["prepare_ms"] else "prepare"
         dom_ms = r[f"{dom}_ms"]
         ach = alg[dom]["bytes"] * tok_heads / (dom_ms * 1e-3) / 1e9
-        result["roofline"] = {"bound": "hbm", "kernel": f"chunk_{dom}", "achieved": ach,
+        # The sequential phase is two launches: the split scan and the readout kernel it hands
+        # S0 and U to; its HIP-event time and its counter traffic cover both.
+        kname = ("chunk_scan (chunk_scan_split_kernel + chunk_readout_kernel)" if dom == "scan"
+                 else "chunk_prepare")
+        result["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": ach,
                               "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                               "frac": ach * 1e9 / HBM_PEAK, "traffic": measured_traffic(dom),
                               "avg_ms": dom_ms}
