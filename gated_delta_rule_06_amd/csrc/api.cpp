@@ -12,6 +12,7 @@
 
 #include "muir.h"
 #include "kernels.hpp"
+#include "layout.hpp"
 
 namespace {
 
@@ -528,15 +529,18 @@ muir_status_t chunk_fwd_lowrank_impl(const char *fn, const void *q, const void *
     }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     // The gates the scan reads (e, w and og): made inside the scan where its LDS allows, else
-    // by the gate kernel into the workspace's tail first.
+    // by the gate kernel into the workspace's tail first, e and w tile-packed where the split
+    // scan reads them (whole cache lines per leaf instead of 32-byte row pieces).
     const bool in_scan = muir::scan_gates_in_kernel(B, H, dv, chunk);
+    const bool packed = !in_scan && muir::split_scan_applies(B, H, dv);
     float *e = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ebase);
     float *w = e + n_tok;
     float *og = gated ? w + n_tok : nullptr;
     if (!in_scan) {
         st = check_hip(muir::launch_lowrank_gates(z, nullptr, Ue, Uw, nullptr, gated ? Uo : nullptr,
                                                   nullptr, ce, cw, nullptr, gated ? co : nullptr,
-                                                  nullptr, e, w, nullptr, og, B, T, H, dv, hs),
+                                                  nullptr, e, w, nullptr, og, B, T, H, dv, hs,
+                                                  packed),
                        fn);
         if (st != MUIR_OK) return st;
     }
@@ -550,7 +554,7 @@ muir_status_t chunk_fwd_lowrank_impl(const char *fn, const void *q, const void *
                                                          H, dk, chunk, workspace, hs),
                          fn);
     return check_hip(muir::launch_chunk_scan(v, e, w, og, s0, o, s_out, B, T, H, dk, chunk, true,
-                                             workspace, hs),
+                                             workspace, hs, packed),
                      fn);
 }
 

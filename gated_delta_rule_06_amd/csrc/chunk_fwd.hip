@@ -1516,10 +1516,14 @@ bool scan_narrow_tiles(int B, int H, int d) { return size_t(B) * H * (d / 8) <= 
 template <typename QT, typename OpT, int D, int C>
 hipError_t scan_typed(const void *v, const float *e, const float *w, const float *og,
                       const float *s0, void *o, float *s_out, int B, int T, int H,
-                      void *workspace, hipStream_t stream) {
+                      void *workspace, hipStream_t stream, bool packed_ew) {
     if constexpr (std::is_same_v<QT, bf16_t>) {
         if (split_scan_applies(B, H, D))
-            return launch_chunk_scan_split(v, e, w, og, s0, o, s_out, B, T, H, D, C, workspace, stream);
+            return launch_chunk_scan_split(v, e, w, og, s0, o, s_out, B, T, H, D, C, workspace, stream,
+                                           packed_ew);
+    }
+    if (packed_ew) return hipErrorInvalidValue;  // only the split scan reads packed gates
+    if constexpr (std::is_same_v<QT, bf16_t>) {
         if (scan_narrow_tiles(B, H, D))
             return scan_vc<QT, OpT, D, C, 2>(v, e, w, og, s0, o, s_out, B, T, H, workspace, stream);
     }
@@ -1592,13 +1596,14 @@ hipError_t launch_chunk_prepare_lowrank(const void *q, const void *k, const void
 
 hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
-                             int chunk, bool bf16, void *workspace, hipStream_t stream) {
+                             int chunk, bool bf16, void *workspace, hipStream_t stream,
+                             bool packed_ew) {
 #define MUIR_SCAN(D, C)                                                                        \
     if (d == D && chunk == C)                                                                  \
         return bf16 ? scan_typed<bf16_t, bf16_t, D, C>(v, e, w, og, s0, o, s_out, B, T, H,      \
-                                                       workspace, stream)                      \
+                                                       workspace, stream, packed_ew)           \
                     : scan_typed<float, float, D, C>(v, e, w, og, s0, o, s_out, B, T, H,        \
-                                                     workspace, stream);
+                                                     workspace, stream, packed_ew);
     MUIR_SCAN(64, 64) MUIR_SCAN(64, 128) MUIR_SCAN(64, 256)
     MUIR_SCAN(128, 64) MUIR_SCAN(128, 128) MUIR_SCAN(128, 256)
 #undef MUIR_SCAN

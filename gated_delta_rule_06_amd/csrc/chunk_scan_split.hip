@@ -63,7 +63,10 @@ constexpr int help_pairs(int L) { return L < 2 ? 0 : (L - 2 - (L & 1)) / 2; }
 // The pair of row L >= 1 holding leaf L - 1 (for odd L, leaf L - 1 and the zero diagonal).
 constexpr int ser_pair(int L) { return (L - 1) / 2; }
 
-template <int D, int C, int VC>
+// PK: e and w tile-packed, [B*H][D/8][T][8] fp32, so that a leaf's rows of this workgroup's eight
+// columns are one contiguous 512-byte run each (with the [B, T, H, D] layout they are sixteen
+// 32-byte pieces of sixteen cache lines).
+template <int D, int C, int VC, bool PK>
 __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     const bf16_t *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ s0, float *__restrict__ s_out, const unsigned char *__restrict__ ws,
@@ -78,6 +81,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     constexpr int HALF = NCT / 2; // state tiles carried per phase
     constexpr int NP = NB / 2;    // leaf pairs per chunk
     constexpr unsigned OB = 2;    // operand bytes
+    static_assert(!PK || VC == 2, "packed e and w come in 8-column tiles");
 
     // S0 of a chunk as bf16 operands, by chunk parity (state -> helper, readout).
     __shared__ f4 sh_fS[2][NCT][64];
@@ -397,13 +401,22 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     // Chain. Where several workgroups share a SIMD it wins instruction arbitration.
     __builtin_amdgcn_s_setprio(1);
     const f4 unit = F::unit(x, g);
-    const rsrc_t re = make_rsrc(e + tok0, tok_elems * 4u);
-    const rsrc_t rwt = make_rsrc(w + tok0, tok_elems * 4u);
+    // Packed e and w: this tile's T rows of 8 values; rows at or past T read zero as well.
+    const size_t pk0 = (size_t(bh) * (D / 8) + size_t(ct)) * size_t(T) * 8;
+    const rsrc_t re = PK ? make_rsrc(e + pk0, unsigned(T) * 32u) : make_rsrc(e + tok0, tok_elems * 4u);
+    const rsrc_t rwt = PK ? make_rsrc(w + pk0, unsigned(T) * 32u) : make_rsrc(w + tok0, tok_elems * 4u);
     const rsrc_t rv = make_rsrc(v + tok0, tok_elems * 2u);
+    const unsigned lo_pk = unsigned(8 * x + VC * g) * 4u;  // packed e, w: token x, group g
     auto load_leaf = [&](int ci, int L, LeafIn<bf16_t, VC> &in) {
-        const unsigned so = trow(ci * C + 16 * L, 4u);
-        in.ev = buf_load_fn<VC>(re, lo_f, so);
-        in.wv = buf_load_fn<VC>(rwt, lo_f, so);
+        if constexpr (PK) {
+            const unsigned so = unsigned(min(ci * C + 16 * L, T)) * 32u;
+            in.ev = buf_load_fn<VC>(re, lo_pk, so);
+            in.wv = buf_load_fn<VC>(rwt, lo_pk, so);
+        } else {
+            const unsigned so = trow(ci * C + 16 * L, 4u);
+            in.ev = buf_load_fn<VC>(re, lo_f, so);
+            in.wv = buf_load_fn<VC>(rwt, lo_f, so);
+        }
         in.vv = RowV<bf16_t, VC>::load(rv, lo_q, trow(ci * C + 16 * L, 2u));
     };
     // Rings over leaves: the leaf inputs (slot = leaf mod RT, which divides the leaves per
@@ -621,7 +634,8 @@ __global__ __launch_bounds__(256) void chunk_readout_kernel(
 
 hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
                                    const float *s0, void *o, float *s_out, int B, int T, int H,
-                                   int d, int chunk, void *workspace, hipStream_t stream) {
+                                   int d, int chunk, void *workspace, hipStream_t stream,
+                                   bool packed_ew) {
     const int nchunks = (T + chunk - 1) / chunk;
     const int BH = B * H;
     const int groups = (BH + 7) / 8;
@@ -634,9 +648,14 @@ hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w
     auto run = [&](auto dc, auto cc) {
         constexpr int D = decltype(dc)::value, C = decltype(cc)::value;
         const dim3 grid(groups * 8 * (D / (4 * VC)));
-        hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, VC>), grid, block, 0, stream,
-                           static_cast<const bf16_t *>(v), e, w, s0, s_out, ws, rd, T, H, BH,
-                           nchunks);
+        if (packed_ew)
+            hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, VC, true>), grid, block, 0, stream,
+                               static_cast<const bf16_t *>(v), e, w, s0, s_out, ws, rd, T, H, BH,
+                               nchunks);
+        else
+            hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, VC, false>), grid, block, 0, stream,
+                               static_cast<const bf16_t *>(v), e, w, s0, s_out, ws, rd, T, H, BH,
+                               nchunks);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || nchunks == 0) return err;
         const dim3 rgrid(unsigned((size_t(BH) * nchunks + 7) / 8 * 16));

@@ -44,12 +44,14 @@ __host__ __device__ constexpr int gate_zoff(int n) {
     return n == 0 ? kOffDecay : n == 1 ? kOffErase : n == 2 ? kOffWrite : n == 3 ? kOffRead : kOffOutput;
 }
 
+// PK: e and w are stored tile-packed for the split scan, [B*H][D/8][T][8] fp32 (eight value
+// columns of one token contiguous, a tile's tokens consecutive), the other gates as [B, T, H, D].
 // One workgroup of four wavefronts per (head, batch, token-block group). The head's
 // up-projection rows sit in LDS, so each z row a wavefront loads serves every channel tile
 // of the head: per token block, z's four slices are loaded once (the next block's while the
 // current one computes), then for each 16-channel tile every requested gate is one short
 // chain of K = 32 products. Gates whose output pointer is null are skipped.
-template <int D>
+template <int D, bool PK>
 __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const bf16_t *__restrict__ z, const bf16_t *__restrict__ Ua, const bf16_t *__restrict__ Ue,
     const bf16_t *__restrict__ Uw, const bf16_t *__restrict__ Ug, const bf16_t *__restrict__ Uo,
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
     const size_t HD = size_t(H) * D;
     const size_t gbase = size_t(b) * T * HD + size_t(h) * D;  // uniform
     const unsigned gbytes = unsigned((size_t(T) * HD - size_t(h) * D) * 4);
+    const size_t pbase = (size_t(b) * H + h) * D * T;  // packed e, w of this head (PK)
+    const unsigned pbytes = unsigned(size_t(D) * T * 4);
 
     struct ZRows {
         f8 r[16];  // decay 2, erase 2, write 4, read 4, output 4 K-steps
@@ -114,7 +118,8 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
             const int R = gate_rank(n), pitch = R + kPad;
             const bf16_t *su = reinterpret_cast<const bf16_t *>(smem + lay.u_off[n]);
             const float *sc = reinterpret_cast<const float *>(smem + lay.c_off[n]);
-            const rsrc_t ro = make_rsrc(out[n] + gbase, gbytes);
+            const bool pk = PK && (n == 1 || n == 2);
+            const rsrc_t ro = pk ? make_rsrc(out[n] + pbase, pbytes) : make_rsrc(out[n] + gbase, gbytes);
 #pragma unroll 2
             for (int c = 0; c < NCT; ++c) {
                 f32x4_t y = *reinterpret_cast<const f32x4_t *>(sc + 16 * c + 4 * G);
@@ -125,7 +130,12 @@ __global__ __launch_bounds__(256) void lowrank_gates_kernel(
                                     zr.r[kStep0[n] + s], y);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) y[r] = n == 0 ? gate_decay(y[r]) : gate_sigmoid(y[r]);
-                const unsigned off = (t * unsigned(HD) + unsigned(16 * c + 4 * G)) * 4u;
+                // Tokens past T (t == T here) are dropped: [B, T, H, D] offsets lie past the
+                // buffer's end, packed ones are moved there.
+                const unsigned off = pk ? (t < unsigned(T) ? ((unsigned(2 * c + (G >> 1)) * unsigned(T) + t) * 8u +
+                                                              4u * unsigned(G & 1)) * 4u
+                                                           : 0xfffffff0u)
+                                        : (t * unsigned(HD) + unsigned(16 * c + 4 * G)) * 4u;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, y), ro, int(off), 0, 0);
             }
         }
@@ -149,7 +159,8 @@ template <int D>
 hipError_t gates_typed(const void *z, const void *Ua, const void *Ue, const void *Uw,
                        const void *Ug, const void *Uo, const float *ca, const float *ce,
                        const float *cw, const float *cg, const float *co, float *a, float *e,
-                       float *w, float *g, float *og, int B, int T, int H, hipStream_t stream) {
+                       float *w, float *g, float *og, int B, int T, int H, bool packed_ew,
+                       hipStream_t stream) {
     if (T == 0) return hipSuccess;
     GateLds lay{};
     const float *outs[kGates] = {a, e, w, g, og};
@@ -164,7 +175,7 @@ hipError_t gates_typed(const void *z, const void *Ua, const void *Ue, const void
     }
     lay.bytes = off;
     if (off == 0) return hipSuccess;
-    auto kern = lowrank_gates_kernel<D>;
+    auto kern = packed_ew ? lowrank_gates_kernel<D, true> : lowrank_gates_kernel<D, false>;
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, off);
     if (err != hipSuccess) return err;
@@ -187,11 +198,13 @@ hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, c
                                 const void *Ug, const void *Uo, const float *ca, const float *ce,
                                 const float *cw, const float *cg, const float *co, float *a,
                                 float *e, float *w, float *g, float *og, int B, int T, int H, int d,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool packed_ew) {
     if (d == 64)
-        return gates_typed<64>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H, stream);
+        return gates_typed<64>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H,
+                               packed_ew, stream);
     if (d == 128)
-        return gates_typed<128>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H, stream);
+        return gates_typed<128>(z, Ua, Ue, Uw, Ug, Uo, ca, ce, cw, cg, co, a, e, w, g, og, B, T, H,
+                                packed_ew, stream);
     return hipErrorInvalidValue;
 }
 

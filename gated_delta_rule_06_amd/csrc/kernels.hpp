@@ -43,16 +43,21 @@ hipError_t launch_chunk_prepare_lowrank(const void *q, const void *k, const void
 // the split scan runs it writes the readout region after them.
 hipError_t launch_chunk_scan(const void *v, const float *e, const float *w, const float *og,
                              const float *s0, void *o, float *s_out, int B, int T, int H, int d,
-                             int chunk, bool bf16, void *workspace, hipStream_t stream);
+                             int chunk, bool bf16, void *workspace, hipStream_t stream,
+                             bool packed_ew = false);
 
 // Phase S for bf16 operands where split_scan_applies holds (at most one 8-column workgroup
 // per compute unit): the sequential part split over four wavefronts per workgroup (chain,
 // right-hand side, state carry, hand-over of S0 and U to the readout region), then the
 // readout O = (Qh*gamma) S0 + P U (and the output gate) as a parallel kernel over chunks.
 // Same results as the other scan, bit for bit.
+// packed_ew: e and w come tile-packed, [B*H][d/8][T][8] fp32 (as launch_lowrank_gates writes them
+// with packed_ew), which the split scan reads as whole cache lines; only where the split scan runs
+// (elsewhere launch_chunk_scan returns hipErrorInvalidValue).
 hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
                                    const float *s0, void *o, float *s_out, int B, int T, int H,
-                                   int d, int chunk, void *workspace, hipStream_t stream);
+                                   int d, int chunk, void *workspace, hipStream_t stream,
+                                   bool packed_ew = false);
 
 // Phase S for the backward pass: keeps u_out [B, T, H, d] fp32 (u = w * v - e * p of every
 // token) and states [B * H][ceil(T / 64) + 1][d][d] fp32 (the state at every 64-token block
@@ -95,7 +100,7 @@ hipError_t launch_lowrank_gates(const void *z, const void *Ua, const void *Ue, c
                                 const void *Ug, const void *Uo, const float *ca, const float *ce,
                                 const float *cw, const float *cg, const float *co, float *a,
                                 float *e, float *w, float *g, float *og, int B, int T, int H, int d,
-                                hipStream_t stream);
+                                hipStream_t stream, bool packed_ew = false);
 
 // Backward pass of the chunk forward (chunks of 64). Inputs as for the forward, plus dout
 // (dtype of q) and dsT [B, H, d, d] fp32 (NULL: zero); outputs fp32, [B, T, H, d] except

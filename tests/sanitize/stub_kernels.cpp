@@ -40,10 +40,9 @@ hipError_t launch_chunk_prepare_lowrank(const void *, const void *, const void *
 }
 hipError_t launch_chunk_scan(const void *, const float *, const float *, const float *,
                              const float *, void *, float *, int, int, int, int, int, bool,
-                             void *, hipStream_t) {
+                             void *, hipStream_t, bool) {
     return launched();
 }
-bool scan_split_applies(int B, int H, int d) { return size_t(B) * H * (d / 8) <= 256; }
 hipError_t launch_chunk_scan_split(const void *, const float *, const float *, const float *,
                                    const float *, void *, float *, int, int, int, int, int,
                                    const void *, hipStream_t) {
@@ -72,7 +71,7 @@ hipError_t launch_wy_scan(const float *, void *, float *, int, int, int, int, in
 hipError_t launch_lowrank_gates(const void *, const void *, const void *, const void *,
                                 const void *, const void *, const float *, const float *,
                                 const float *, const float *, const float *, float *, float *,
-                                float *, float *, float *, int, int, int, int, hipStream_t) {
+                                float *, float *, float *, int, int, int, int, hipStream_t, bool) {
     return launched();
 }
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &, int, int, int, int, bool, void *,
