@@ -1630,6 +1630,9 @@ hipError_t scan_save_typed(const void *v, const float *e, const float *w, const 
                            H, BH, nchunks, sv);
         return hipGetLastError();
     };
+    if (std::is_same_v<QT, bf16_t> && split_scan_applies(B, H, D))
+        return launch_chunk_scan_split_save(v, e, w, s0, s_out, sv.u, sv.states, B, T, H, D, C,
+                                            workspace, stream);
     if (std::is_same_v<QT, bf16_t> && scan_narrow_tiles(B, H, D)) return run(std::integral_constant<int, 2>{});
     return run(std::integral_constant<int, 4>{});
 }

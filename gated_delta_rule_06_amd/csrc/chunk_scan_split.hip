@@ -66,11 +66,16 @@ constexpr int ser_pair(int L) { return (L - 1) / 2; }
 // PK: e and w tile-packed, [B*H][D/8][T][8] fp32, so that a leaf's rows of this workgroup's eight
 // columns are one contiguous 512-byte run each (with the [B, T, H, D] layout they are sixteen
 // 32-byte pieces of sixteen cache lines).
-template <int D, int C, int VC, bool PK>
+// SAVE (the backward pass's rerun of the forward): no readout; the chain keeps u = w*v - e*p of
+// every token in fp32 ([B, T, H, D], u_save) and the state wavefront the state at every 64-token
+// block start and at the end ([B*H][ceil(T/64) + 1][D][D] fp32, st_save), as the two-wavefront
+// scan's saving instance does, bit for bit.
+template <int D, int C, int VC, bool PK, bool SAVE = false>
 __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     const bf16_t *__restrict__ v, const float *__restrict__ e, const float *__restrict__ w,
     const float *__restrict__ s0, float *__restrict__ s_out, const unsigned char *__restrict__ ws,
-    unsigned char *__restrict__ rd, int T, int H, int BH, int nchunks) {
+    unsigned char *__restrict__ rd, int T, int H, int BH, int nchunks,
+    float *__restrict__ u_save = nullptr, float *__restrict__ st_save = nullptr) {
     using SL = Slot<bf16_t, D, C>;
     using F = Frag<bf16_t>;
     using f4 = F::f4;
@@ -82,6 +87,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     constexpr int NP = NB / 2;    // leaf pairs per chunk
     constexpr unsigned OB = 2;    // operand bytes
     static_assert(!PK || VC == 2, "packed e and w come in 8-column tiles");
+    static_assert(!SAVE || C % 64 == 0, "saved states are 64 tokens apart");
 
     // S0 of a chunk as bf16 operands, by chunk parity (state -> helper, readout).
     __shared__ f4 sh_fS[2][NCT][64];
@@ -113,13 +119,19 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     const float *s0h = s0 ? s0 + size_t(bh) * D * D + j0 : nullptr;
     float *south = s_out ? s_out + size_t(bh) * D * D + j0 : nullptr;
 
+    // SAVE: this head's saved states, from this tile's first column.
+    const int n64 = (T + 63) / 64;
+    float *svst = SAVE ? st_save + size_t(bh) * (n64 + 1) * D * D + j0 : nullptr;
     if (nchunks == 0) {
-        if (wave == 0 && col_ok && south) {
+        if (wave == 0 && col_ok) {
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    south[size_t(16 * c + i) * D + lo_st] = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = s0h ? s0h[size_t(16 * c + i) * D + lo_st] : 0.f;
+                    if (south) south[size_t(16 * c + i) * D + lo_st] = x0;
+                    if constexpr (SAVE) svst[size_t(16 * c + i) * D + lo_st] = x0;
+                }
         }
         return;
     }
@@ -155,6 +167,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                                  unsigned(size_t(nchunks) * RCB - size_t(ct >> 1) * TB));
     const unsigned lo_rd = unsigned(16 * (16 * g + x + 2 * (ct & 1)));
     auto rd_put = [&](int ci, int frag, f8 val) {
+        if constexpr (SAVE) return;  // no readout: nothing to hand over
         if (col_ok)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rrd, int(lo_rd),
                                                    int(size_t(ci) * RCB + size_t(frag) * 1024), 0);
@@ -285,6 +298,15 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
 #pragma unroll
             for (int t = 0; t < HALF; ++t) dst[t] = load_kbt(ci, (L - 2) / 2, t + (L & 1) * HALF);
         };
+        auto save_state = [&](int slot) {
+            if (col_ok) {
+                float *dst = svst + size_t(slot) * D * D;
+#pragma unroll
+                for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[size_t(16 * t + i) * D + lo_st] = S[t][i];
+            }
+        };
         // The chunk before's last leaf pair (all tiles), into the state.
         auto carry_last = [&](int cp) {
             const f8 u2 = sh_U[cp & 1][NP - 1][lane];
@@ -298,6 +320,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                 if constexpr (L < NB) load_half(c, L, kbt[L % RS]);
             });
             if (c >= 1) carry_last(c - 1);
+            if constexpr (SAVE) save_state(c * (C / 64));
             f4 pk[NCT];
 #pragma unroll
             for (int t = 0; t < NCT; ++t) {
@@ -322,6 +345,14 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                     for (int t = 0; t < HALF; ++t)
                         S[t + off] = F::mma8(kbt[L % RS][t], u2, S[t + off] * lds_pp(c, p, t + off));
                 }
+                // SAVE inside a chunk: after phase 4q + 1 every tile has taken the leaf pairs of
+                // tokens 0 .. 64q - 1 and no later one, so S is the state at the chunk's 64q-th
+                // token. A boundary past the sequence goes to the final state's slot, which the
+                // final state overwrites.
+                if constexpr (SAVE && L % 4 == 1 && L >= 5) {
+                    constexpr int q = (L - 1) / 4;
+                    save_state(c * C + 64 * q < T ? c * (C / 64) + q : n64);
+                }
                 lds_barrier();
             });
         }
@@ -336,6 +367,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) south[size_t(16 * t + i) * D + lo_st] = S[t][i];
         }
+        if constexpr (SAVE) save_state(n64);
         return;
     }
 
@@ -406,6 +438,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
     const rsrc_t re = PK ? make_rsrc(e + pk0, unsigned(T) * 32u) : make_rsrc(e + tok0, tok_elems * 4u);
     const rsrc_t rwt = PK ? make_rsrc(w + pk0, unsigned(T) * 32u) : make_rsrc(w + tok0, tok_elems * 4u);
     const rsrc_t rv = make_rsrc(v + tok0, tok_elems * 2u);
+    const rsrc_t rus = make_rsrc(SAVE ? u_save + tok0 : nullptr, SAVE ? tok_elems * 4u : 0u);
     const unsigned lo_pk = unsigned(8 * x + VC * g) * 4u;  // packed e, w: token x, group g
     auto load_leaf = [&](int ci, int L, LeafIn<bf16_t, VC> &in) {
         if constexpr (PK) {
@@ -494,6 +527,8 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
             };
             // Step 15 would update no token (M is strictly lower triangular): left out.
             static_for<15>([&](auto Sc) { step(std::integral_constant<int, decltype(Sc)::value>{}); });
+            if constexpr (SAVE)
+                RowV<float, VC>::store(rus, lo_f, trow(c * C + 16 * L, 4u), f32x4_t{x0, x1, x2, x3});
             const f4 U = F::pack(F::mma16_fresh(F::pack(f32x4_t{x0, x1, x2, x3}), unit));
             u_put(buf, L, U);
             U2 = U1;
@@ -631,6 +666,31 @@ __global__ __launch_bounds__(256) void chunk_readout_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_chunk_scan_split_save(const void *v, const float *e, const float *w,
+                                        const float *s0, float *s_out, float *u_out, float *states,
+                                        int B, int T, int H, int d, int chunk, const void *workspace,
+                                        hipStream_t stream) {
+    const int nchunks = (T + chunk - 1) / chunk;
+    const int BH = B * H;
+    const int groups = (BH + 7) / 8;
+    constexpr int VC = 2;
+    unsigned char *ws = static_cast<unsigned char *>(const_cast<void *>(workspace));
+    auto run = [&](auto dc, auto cc) {
+        constexpr int D = decltype(dc)::value, C = decltype(cc)::value;
+        hipLaunchKernelGGL((chunk_scan_split_kernel<D, C, VC, false, true>),
+                           dim3(groups * 8 * (D / (4 * VC))), dim3(256), 0, stream,
+                           static_cast<const bf16_t *>(v), e, w, s0, s_out, ws, nullptr, T, H, BH,
+                           nchunks, u_out, states);
+        return hipGetLastError();
+    };
+#define MUIR_SPLIT(D, C) \
+    if (d == D && chunk == C) return run(std::integral_constant<int, D>{}, std::integral_constant<int, C>{});
+    MUIR_SPLIT(64, 64) MUIR_SPLIT(64, 128) MUIR_SPLIT(64, 256)
+    MUIR_SPLIT(128, 64) MUIR_SPLIT(128, 128) MUIR_SPLIT(128, 256)
+#undef MUIR_SPLIT
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w, const float *og,
                                    const float *s0, void *o, float *s_out, int B, int T, int H,

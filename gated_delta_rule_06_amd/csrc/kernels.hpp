@@ -59,6 +59,13 @@ hipError_t launch_chunk_scan_split(const void *v, const float *e, const float *w
                                    int d, int chunk, void *workspace, hipStream_t stream,
                                    bool packed_ew = false);
 
+// The split scan's saving instance (bf16, where split_scan_applies holds): what
+// launch_chunk_scan_save keeps, bit for bit, and no readout; reads only the workspace's slots.
+hipError_t launch_chunk_scan_split_save(const void *v, const float *e, const float *w,
+                                        const float *s0, float *s_out, float *u_out, float *states,
+                                        int B, int T, int H, int d, int chunk, const void *workspace,
+                                        hipStream_t stream);
+
 // Phase S for the backward pass: keeps u_out [B, T, H, d] fp32 (u = w * v - e * p of every
 // token) and states [B * H][ceil(T / 64) + 1][d][d] fp32 (the state at every 64-token block
 // start, then the final state), and reads nothing out (o is not written and may be null).
