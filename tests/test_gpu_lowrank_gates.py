@@ -177,6 +177,26 @@ def test_fused_equals_gate_kernel_then_forward(device, cfg, chunk):
     assert np.array_equal(o1, to_numpy(o2)) and np.array_equal(s1, to_numpy(s2))
 
 
+@pytest.mark.parametrize("B,T,H,d,chunk", [(1, 300, 2, 128, 256), (2, 77, 3, 64, 64), (1, 15, 4, 128, 128)])
+def test_fused_packed_gates_ragged_tail(device, B, T, H, d, chunk):
+    """Few heads (one 8-column scan workgroup per compute unit at most), so the gate kernel
+    stores e and w tile-packed and the split scan reads them so; with a ragged tail (rows past
+    T read zero) and a non-zero initial state the fused call is still bit for bit the gate
+    kernel's four gates, stored as [B, T, H, d], fed to the plain forward."""
+    inp = workloads.chunk_inputs(1, B=B, T=T, H=H, d=d, qkv="bf16", seed=800 + T)
+    lr = workloads.lowrank_gate_inputs(1, B=B, T=T, H=H, d=d, seed=800 + T)
+    s0 = (np.random.default_rng(T).standard_normal((B, H, d, d)) * 0.3).astype(np.float32)
+    print(f"packed gates B{B} T{T} H{H} d{d} C{chunk}", flush=True)
+    o1, s1 = lowrank_fwd(inp, lr, device, chunk, s0)
+    gates = gpu_gates(lr, H, d, device)
+    t = to_device(inp, device, "bf16")
+    for k in "aewg":
+        t[k] = torch.from_numpy(gates[k]).to(device)
+    o2, s2 = muir.chunk_fwd(*[t[n] for n in NAMES], s0=torch.from_numpy(s0).to(device), chunk=chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, to_numpy(o2)) and np.array_equal(s1, to_numpy(s2))
+
+
 # ---- The output gate from z's output slice (rank 128, z[..., 128:256]) ----
 
 def gpu_output_gate(lr, device):
