@@ -97,9 +97,10 @@ def test_small_shapes(device, qkv, d, T):
 @pytest.mark.parametrize("B,d", [(2, 128), (4, 64)])
 def test_wide_scan_tiles(device, qkv, B, d):
     """Enough heads (B * H * d / 8 > 256) that the forward scan the backward reruns (the saving
-    instance) takes 16-column value tiles on the bf16 path; the smaller bf16 cases here rerun it
-    with 8-column tiles. The reverse scan itself runs 16-column tiles in every case; what this
-    case adds to it is H = 16 heads per batch row, two full groups of eight."""
+    instance) is the two-wavefront scan with 16-column value tiles on the bf16 path; the smaller
+    bf16 cases here rerun it on the split scan (8-column tiles, four wavefronts). The reverse scan
+    itself runs 16-column tiles in every case; what this case adds to it is H = 16 heads per
+    batch row, two full groups of eight."""
     T, H = 130, 16
     inp = workloads.chunk_inputs(0, B=B, T=T, H=H, d=d, qkv=qkv, seed=3000 + d)
     rng = np.random.default_rng(d)
