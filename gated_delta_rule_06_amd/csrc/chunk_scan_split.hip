@@ -41,9 +41,9 @@
 //
 // Per chunk there are NB leaf phases and two more: in the first the state wavefront applies
 // the chunk before's last leaf pair and publishes the new chunk's start state; in the
-// second the helper makes the first two leaves' right-hand sides from it. One extra
-// iteration after the last chunk lets the state and readout wavefronts finish. Every
-// wavefront passes the same barriers in the same order.
+// second the helper makes the first two leaves' right-hand sides from it (and the hand-over
+// wavefront H_2). One extra iteration after the last chunk lets the state and hand-over
+// wavefronts finish. Every wavefront passes the same barriers in the same order.
 #include <type_traits>
 #include <utility>
 
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
                 lds_barrier();
             });
         }
-        // The iteration after the last chunk: its last pair, then the readout's phases.
+        // The iteration after the last chunk: its last pair, then the hand-over wavefront's phases.
         carry_last(nchunks - 1);
         lds_barrier();  // phase Z1
         lds_barrier();  // phase Z2
