@@ -200,13 +200,21 @@ __global__ __launch_bounds__(256) void chunk_scan_split_kernel(
         // Every workgroup of a head reads the same chunk slots in step, so each touches its
         // share of the next chunk's slot a chunk ahead (one word per 128-byte line), and the
         // head's other workgroups then find those lines in the L2 they share.
-        constexpr int LINES = int(SL::BYTES / 128);
+        // Only the slot's parts the scan reads: M and the pair decays, K*gamma, and (K*beta')^T
+        // with the diagonal blocks (Qh*gamma and P are the readout kernel's; touching them cost
+        // the scan 2-3%).
+        constexpr int LA = int(SL::P_OFF / 128), LB = int((SL::QG_OFF - SL::KG_OFF) / 128),
+                      LC = int((SL::BYTES - SL::KBT_OFF) / 128);
+        constexpr int LINES = LA + LB + LC;
         constexpr int LINES_WG = (LINES + NVT - 1) / NVT;
         constexpr int NTOUCH = (LINES_WG + 63) / 64;
         unsigned touched = 0;
         auto touch = [&](int ci, int n) {
-            const int line = ct * LINES_WG + n * 64 + lane;
-            const unsigned off = unsigned(min(line, LINES - 1)) * 128u;
+            const int v = min(ct * LINES_WG + n * 64 + lane, LINES - 1);
+            const int line = v < LA ? v
+                           : v < LA + LB ? int(SL::KG_OFF / 128) + (v - LA)
+                                         : int(SL::KBT_OFF / 128) + (v - LA - LB);
+            const unsigned off = unsigned(line) * 128u;
             touched += __builtin_amdgcn_raw_buffer_load_b32(rws, int(off), int(wsoff(ci, 0)), 0);
         };
         // The next chunk's staging goes to the buffers of the other parity: nobody reads them
