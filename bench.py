@@ -31,7 +31,7 @@ NAMES = "q k v a g e w r".split()
 
 
 def algorithmic(d, chunk, qkv_bytes=2):
-    """Per token-head algorithmic bytes and MFMA flops of each phase (see DESIGN.md).
+    """Per token-head algorithmic bytes and MFMA flops of each phase.
 
     prepare: reads q, k (qkv dtype) and a, g (fp32); Gram M and P: 2*C*d flops.
     scan:    reads v (qkv dtype), e, w (fp32), writes o (qkv dtype);

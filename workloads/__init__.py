@@ -11,7 +11,7 @@ Sensitivity-Allocated Gating and Matched-Filter Readout", arXiv 2611.08376): a
 decay with slow rows carrying ~100x the energy of fast rows, and a decode step
 against the fixed 25 MB fp32 state.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open (this recipe takes the plainest one for each):
   * decay a = exp(-exp(u + eps)), eps ~ N(0, 0.1) per token and row; u is the
     log of the decay rate, so a stays in (0, 1];
   * half-life workloads: h = 10**U(0, log10 Hmax), u = ln(ln 2 / h), i.e. the
